@@ -1,0 +1,336 @@
+"""CPU oracle for the INT8 KV-cache hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+module.  The product library never routes through it, and it shares no code
+with the HIP kernels: it takes plain NumPy arrays and computes, slowly and
+step by step, what the pages define.
+
+Precision contract
+  * quantization is emulated in IEEE fp32 (NumPy float32 division rounds to
+    nearest; denormals are kept on x86 SSE), because the method produces
+    integer codes from fp32 arithmetic and both sides must take that decision
+    in the same precision;
+  * rounding of the quotient is "half away from zero" and is evaluated in fp64
+    on the fp32 quotient (``|y| + 0.5`` in fp32 would mis-round 0.49999997);
+  * dequantization for attention is exact in fp64 ((code-128) * scale fits in
+    31 significant bits);
+  * attention is fp64 over those exact values, by its plain definition:
+    scores, max-subtracted softmax, probability-weighted sum.
+
+Sources (docs.rs source pages; a citation names the page and the Rust item):
+  [P1] abaddon 0.2.0-rc.1, src/kv_cache_quant_cuda.rs
+  [P2] realizar 0.8.5, src/cuda/executor/kv_cache_q8_init.rs
+  [P3] abaddon 0.2.0-rc.2, src/kv_cache_quant.rs
+  [P4] combs-models 0.2.2, src/kv.rs
+  [P5] llama-gguf 0.14.0, src/model/kv_quantized.rs
+
+Every function below is pinned by a ``-m "not gpu"`` test against a value the
+pages fix, a closed form, or brute force; none is marked "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+# Smallest absmax the per-token quantizer allows (P1 `quantize_tensor`, the
+# `.max(1e-8)` on the row's absolute maximum; P3 `QuantizedKvCache::quantize`,
+# the `eps` tensor).  Applied identically for group-32 (reading documented in
+# the P1 rule for both scale modes).
+ABSMAX_FLOOR = np.float32(1e-8)
+QMAX = np.float32(127.0)
+CODE_OFFSET = 128
+GROUP = 32
+PAGE_SIZE = 16
+
+
+# ----------------------------------------------------------------------------
+# bf16 helpers (output rounding; [P1] kernel-source helpers `bf16_to_f32`,
+# `f32_to_bf16`, which define bf16 as the upper half of an fp32 word rounded
+# to nearest, ties to even)
+# ----------------------------------------------------------------------------
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp32 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 -> bf16, nearest with ties to even, as uint16 bit patterns.
+
+    Written from the definition: the 16 dropped low bits are compared with the
+    half-way point 0x8000; above it rounds up, below it truncates, and exactly
+    at it the kept part is made even.  Finite inputs only.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    hi = u >> np.uint64(16)
+    lo = u & np.uint64(0xFFFF)
+    up = (lo > 0x8000) | ((lo == 0x8000) & ((hi & np.uint64(1)) == 1))
+    return (hi + up.astype(np.uint64)).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# Quantizer
+# ----------------------------------------------------------------------------
+
+def round_half_away_from_zero(y: np.ndarray) -> np.ndarray:
+    """Nearest integer, ties away from zero, of fp32 values, as int64.
+
+    Rust's `f32::round`, used by the per-token quantizer of [P1]
+    `CudaQuantizedKvCache::quantize_tensor` and by [P5] `quantize_int8`.
+    """
+    y64 = np.asarray(y, dtype=np.float32).astype(np.float64)
+    return (np.sign(y64) * np.floor(np.abs(y64) + 0.5)).astype(np.int64)
+
+
+def quantize(x: np.ndarray, group: int = 0):
+    """Symmetric absmax/127 quantization to u8 codes with a +128 offset.
+
+    ``x``: float32 array ``[..., D]``.  ``group``: 0 for one scale per row
+    (per token and KV head) or 32 for one scale per 32 consecutive elements
+    along the last axis.  Returns ``(codes uint8 [..., D], scales float32
+    [..., G])`` with G = 1 or D/32.
+
+    Steps, in the order [P1] `CudaQuantizedKvCache::quantize_tensor` takes
+    them (group-32 granularity and fp32 scale storage from [P4] `kv_quantize`
+    and [P2] `init_kv_cache_q8_gpu`):
+      1. m = max(max_i |x_i|, 1e-8)            (exact in fp32)
+      2. s = fl32(m / 127)                     (IEEE fp32 division)
+      3. y = fl32(x_i / s)                     (IEEE fp32 division, not x*(1/s))
+      4. q = round half away from zero (y), clamped to [-127, 127]
+      5. code = q + 128                        (in [1, 255] for finite input)
+    """
+    x = np.asarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    gsize = d if group == 0 else group
+    if d % gsize != 0:
+        raise ValueError("head_dim must be a multiple of the group size")
+    g = x.reshape(x.shape[:-1] + (d // gsize, gsize))
+    m = np.max(np.abs(g), axis=-1)
+    m = np.maximum(m, ABSMAX_FLOOR).astype(np.float32)
+    s = (m / QMAX).astype(np.float32)
+    y = (g / s[..., None]).astype(np.float32)
+    q = np.clip(round_half_away_from_zero(y), -127, 127)
+    codes = (q + CODE_OFFSET).astype(np.uint8).reshape(x.shape)
+    return codes, s
+
+
+def _expand_scales(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    d = codes.shape[-1]
+    gcount = scales.shape[-1]
+    return np.repeat(scales.astype(np.float64), d // gcount, axis=-1)
+
+
+def dequantize_exact(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_hat = (code - 128) * s, exact in fp64.
+
+    [P1] module doc ("Dequantize K: (K_u8 - 128) * scale"), [P3]
+    `QuantizedKvCache::dequantize`.  The group count is read from the trailing
+    dimension of ``scales`` (1 = per token, D/32 = group-32).
+    """
+    c = np.asarray(codes).astype(np.float64) - CODE_OFFSET
+    return c * _expand_scales(codes, scales)
+
+
+def dequantize_f32(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fl32((code - 128) * s): the exact product rounded once to fp32."""
+    return dequantize_exact(codes, scales).astype(np.float32)
+
+
+def dequantize_bf16_bits(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """bf16 (RNE) of the fp32 dequantized value, as uint16 bit patterns."""
+    return f32_to_bf16_bits(dequantize_f32(codes, scales))
+
+
+# ----------------------------------------------------------------------------
+# Cache layouts
+# ----------------------------------------------------------------------------
+
+def contiguous_append(k_codes, k_scales, v_codes, v_scales, k_new, v_new, start_pos, group):
+    """Quantize ``[B, KVH, n, D]`` new rows and store them at positions
+    ``start_pos[b] + i`` of a contiguous cache ``[B, KVH, max_len, D]``.
+
+    Fixed-capacity slot write with a per-head ``max_len`` stride, as in [P2]
+    `write_kv_q8` (offset head*max_len*head_dim + position*head_dim).
+    Arrays are modified in place.
+    """
+    kc, ks = quantize(k_new, group)
+    vc, vs = quantize(v_new, group)
+    bsz, _, n, _ = k_new.shape
+    max_len = k_codes.shape[2]
+    for b in range(bsz):
+        p0 = int(start_pos[b])
+        if p0 < 0 or p0 + n > max_len:
+            raise IndexError("append beyond capacity")
+        k_codes[b, :, p0:p0 + n] = kc[b]
+        k_scales[b, :, p0:p0 + n] = ks[b]
+        v_codes[b, :, p0:p0 + n] = vc[b]
+        v_scales[b, :, p0:p0 + n] = vs[b]
+
+
+def page_slot(block_table: np.ndarray, b: int, p: int, page_size: int = PAGE_SIZE):
+    """Logical position p of sequence b -> (physical page, slot).
+
+    [P4] `PagedKVCache::attention_opts` write loop: slot = pos % page_size,
+    phys = table[pos / page_size]; generalised to one table row per sequence.
+    """
+    return int(block_table[b, p // page_size]), p % page_size
+
+
+def paged_append(k_codes, k_scales, v_codes, v_scales, block_table, k_new, v_new, start_pos, group):
+    """Quantize new rows and write them into a paged arena
+    ``[P, KVH, 16, D]`` (scales ``[P, KVH, 16, G]``) through the block table.
+
+    [P4] `PagedKVCache::attention_opts` (quantized arena branch): quantize the
+    incoming chunk once, then place each token with the page-slot arithmetic.
+    """
+    kc, ks = quantize(k_new, group)
+    vc, vs = quantize(v_new, group)
+    bsz, _, n, _ = k_new.shape
+    for b in range(bsz):
+        for i in range(n):
+            phys, slot = page_slot(block_table, b, int(start_pos[b]) + i)
+            k_codes[phys, :, slot] = kc[b, :, i]
+            k_scales[phys, :, slot] = ks[b, :, i]
+            v_codes[phys, :, slot] = vc[b, :, i]
+            v_scales[phys, :, slot] = vs[b, :, i]
+
+
+def paged_gather(arena, block_table, b, length, page_size=PAGE_SIZE):
+    """Materialise sequence b's logical window ``[KVH, length, last]`` from a
+    paged arena ``[P, KVH, page_size, last]``.
+
+    [P4] `PagedKVCache::gather_window`: select the table's pages, put the
+    head axis first, flatten pages x slots, keep the first ``length``.
+    """
+    npages = -(-length // page_size)
+    pages = arena[block_table[b, :npages]]            # [npages, KVH, PS, last]
+    win = np.swapaxes(pages, 0, 1)                   # [KVH, npages, PS, last]
+    win = win.reshape(win.shape[0], npages * page_size, win.shape[-1])
+    return win[:, :length]
+
+
+# ----------------------------------------------------------------------------
+# Attention (fp64, plain definition)
+# ----------------------------------------------------------------------------
+
+def kv_head_of(h: int, num_heads: int, num_kv_heads: int) -> int:
+    """GQA mapping: query head h reads KV head h // (H / KVH).
+
+    [P4] `repeat_kv` repeats each KV head n_rep times consecutively; [P1]
+    kernels use h * num_kv_heads / num_heads, the same when H % KVH == 0.
+    """
+    return h // (num_heads // num_kv_heads)
+
+
+def softmax_attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, attn_scale: float,
+                   visible: np.ndarray | None = None) -> np.ndarray:
+    """One query row: fp64 scaled dot-product attention.
+
+    ``q`` [D], ``k``/``v`` [T, D] (fp64), ``visible`` optional bool [T].
+    Scores q.k * scale; masked keys drop out (the [P1] causal branch fills
+    -inf, [P4] `attend` fills -1e30: both vanish after exp); max-subtracted
+    softmax; probability-weighted sum of values ([P4] `attend`, manual path;
+    [P1] `forward_attention` softmax).
+    """
+    s = (k @ q) * float(attn_scale)
+    if visible is not None:
+        s = np.where(visible, s, -np.inf)
+    m = np.max(s)
+    p = np.exp(s - m)
+    p = p / np.sum(p)
+    return p @ v
+
+
+def attention_decode(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray,
+                     seq_lens, attn_scale: float) -> np.ndarray:
+    """Decode attention, one query token per sequence.
+
+    ``q`` [B, H, D] (exact bf16 values as floats), ``k_hat``/``v_hat``
+    [B, KVH, >=L, D] dequantized (fp64), ``seq_lens`` [B] attended lengths.
+    A single query at the end of the window sees every cached token, so no
+    mask applies ([P4] `attend`, the decode comment).  Returns [B, H, D] fp64.
+    """
+    bsz, nh, d = q.shape
+    nkv = k_hat.shape[1]
+    out = np.zeros((bsz, nh, d), dtype=np.float64)
+    for b in range(bsz):
+        length = int(seq_lens[b])
+        for h in range(nh):
+            g = kv_head_of(h, nh, nkv)
+            out[b, h] = softmax_attend(q[b, h].astype(np.float64), k_hat[b, g, :length],
+                                       v_hat[b, g, :length], attn_scale)
+    return out
+
+
+def attention_chunk(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, ctx_lens,
+                    causal: bool, attn_scale: float) -> np.ndarray:
+    """Chunked-prefill attention for n new queries per sequence.
+
+    ``q`` [B, H, n, D]; ``k_hat``/``v_hat`` [B, KVH, >=L0+n, D] with the chunk
+    already appended after ``ctx_lens[b] = L0`` cached tokens.  Query i sits at
+    absolute position L0 + i and, when causal, sees keys t <= L0 + i
+    (bottom-right alignment: [P1] `forward_attention`, cache_offset = seq_len
+    - q_len; [P4] `attend`, keys > pos forbidden).  Non-causal queries see all
+    L0 + n keys.  Returns [B, H, n, D] fp64.
+    """
+    bsz, nh, n, d = q.shape
+    nkv = k_hat.shape[1]
+    out = np.zeros((bsz, nh, n, d), dtype=np.float64)
+    for b in range(bsz):
+        l0 = int(ctx_lens[b])
+        total = l0 + n
+        t = np.arange(total)
+        for h in range(nh):
+            g = kv_head_of(h, nh, nkv)
+            kk = k_hat[b, g, :total]
+            vv = v_hat[b, g, :total]
+            for i in range(n):
+                vis = (t <= l0 + i) if causal else None
+                out[b, h, i] = softmax_attend(q[b, h, i].astype(np.float64), kk, vv,
+                                              attn_scale, vis)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Sizing
+# ----------------------------------------------------------------------------
+
+def cache_bytes(num_kv_heads: int, max_len: int, head_dim: int, group: int,
+                batch: int = 1, layers: int = 1) -> int:
+    """Bytes of u8 codes plus fp32 scales for K and V.
+
+    [P2] `init_kv_cache_q8_gpu` / `kv_cache_q8_memory_bytes`:
+    layers * 2 * (values + 4 * scales), with values = kvh*max_len*dim and
+    scales = kvh*max_len*(dim/32) for group-32 (dim/dim = 1 per token).
+    """
+    per_row_scales = 1 if group == 0 else head_dim // group
+    values = num_kv_heads * max_len * head_dim
+    scales = num_kv_heads * max_len * per_row_scales
+    return layers * batch * 2 * (values + 4 * scales)
+
+
+def fp32_equivalent_bytes(num_kv_heads: int, max_len: int, head_dim: int,
+                          batch: int = 1, layers: int = 1) -> int:
+    """[P2] `kv_cache_fp32_equivalent_bytes`: layers*2*kvh*max_len*dim*4."""
+    return layers * batch * 2 * num_kv_heads * max_len * head_dim * 4
+
+
+def codes_bytes(num_kv_heads: int, max_len: int, head_dim: int,
+                batch: int = 1, layers: int = 1) -> int:
+    """u8 code bytes alone for K and V."""
+    return layers * batch * 2 * num_kv_heads * max_len * head_dim
+
+
+def reference_attention_fp(q, k, v, attn_scale):
+    """Unquantized fp64 decode attention on raw K/V (used to check the
+    quantized path against the [P4] test tolerance); same definition as
+    :func:`attention_decode` with K/V taken as given."""
+    return attention_decode(q, np.asarray(k, np.float64), np.asarray(v, np.float64),
+                            [k.shape[2]] * q.shape[0], attn_scale)
+
+
+__all__ = [name for name in dir() if not name.startswith("_") and name not in ("math", "np", "annotations")]

@@ -1,0 +1,473 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, brute force.
+
+None of these tests retype the oracle's formulas: each checks it against
+something fixed independently (a page's worked example and threshold, exact
+rational arithmetic, an exhaustive search, a library cast, or a closed-form
+attention result).
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_examples.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# quantizer: page examples
+# ----------------------------------------------------------------------------
+
+def _grid_input():
+    n = 2 * 3 * 64
+    i = np.arange(n)
+    q = (i * 37) % 255 - 127
+    x = (q * 0.5).astype(np.float32)
+    x[::32] = np.float32(63.5)
+    return x.reshape(1, 2, 3, 64), q
+
+
+@pytest.mark.parametrize("group", [32, 0])
+def test_grid_roundtrip_exact(golden, group):
+    """combs-models kv.rs `kv_quant_roundtrip_exact_on_grid_values`: absmax
+    63.5 per group (and per row) forces scale 0.5, so codes are 2x+128 and the
+    round trip is exact."""
+    x, qgrid = _grid_input()
+    codes, scales = orc.quantize(x, group)
+    assert np.all(scales == np.float32(0.5))
+    expect = (qgrid + 128).astype(np.uint8)
+    expect[::32] = 255
+    assert np.array_equal(codes.reshape(-1), expect)
+    back = orc.dequantize_exact(codes, scales)
+    assert np.max(np.abs(back - x)) < golden["grid_roundtrip"]["tolerance"]
+    assert np.array_equal(orc.dequantize_f32(codes, scales), x)
+
+
+def test_tie_rounding_half_away_from_zero():
+    """Ties of x/s round away from zero (Rust `f32::round` in abaddon
+    kv_cache_quant_cuda.rs `quantize_tensor`), and the rounding happens before
+    the +128 offset: -0.5 -> -1 -> code 127 (rounding after the offset would
+    give 128)."""
+    row = np.zeros(32, np.float32)
+    row[0] = 63.5                                   # s = 0.5 exactly
+    row[1:9] = [0.25, -0.25, 0.75, -0.75, 1.25, -1.25, 0.0, -0.0]
+    codes, s = orc.quantize(row[None], 32)
+    assert s[0, 0] == np.float32(0.5)
+    assert list(codes[0, :9]) == [255, 129, 127, 130, 126, 131, 125, 128, 128]
+
+
+def test_half_step_bound(golden):
+    """combs-models kv.rs `kv_quant_error_bounded_by_half_step`: error at
+    most absmax/254 + 1e-6 per 32-group; also the tighter fp32 bound
+    (s/2)(1 + 2^-15) per element."""
+    n = 2 * 5 * 64
+    i = np.arange(n, dtype=np.int64)
+    x = (((i * 7919) % 1000).astype(np.float32) / np.float32(250.0) - np.float32(2.0)).astype(np.float32)
+    x = x.reshape(1, 2, 5, 64)
+    codes, scales = orc.quantize(x, 32)
+    back = orc.dequantize_f32(codes, scales).astype(np.float64)
+    xf = x.astype(np.float64).reshape(-1, 32)
+    bf = back.reshape(-1, 32)
+    absmax = np.max(np.abs(xf), axis=1, keepdims=True)
+    assert np.all(np.abs(xf - bf) <= absmax / 254.0 + golden["half_step_bound"]["slack"])
+    s = np.repeat(scales.reshape(-1, 1).astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(xf - bf) <= (s / 2) * (1 + 2.0 ** -15))
+
+
+def test_candle_roundtrip(golden):
+    """abaddon 0.2.0-rc.2 kv_cache_quant.rs roundtrip test: (1,2,8,8), x=(i-64)/64."""
+    x = ((np.arange(128, dtype=np.float32) - np.float32(64)) / np.float32(64)).reshape(1, 2, 8, 8)
+    codes, scales = orc.quantize(x, 0)
+    assert scales.shape == (1, 2, 8, 1)
+    err = np.abs(orc.dequantize_f32(codes, scales) - x)
+    assert np.max(err) < golden["candle_roundtrip"]["tolerance"]
+
+
+def test_int8_roundtrip_relative(golden):
+    """llama-gguf kv_quantized.rs `test_int8_roundtrip`: 128 values 0.1 i - 6.4."""
+    x = (np.arange(128, dtype=np.float32) * np.float32(0.1) - np.float32(6.4)).astype(np.float32)
+    codes, scales = orc.quantize(x[None], 0)
+    dec = orc.dequantize_f32(codes, scales)[0]
+    for o, d in zip(x, dec):
+        err = abs(float(o) - float(d))
+        rel = err / abs(float(o)) if abs(float(o)) > 1e-6 else err
+        assert rel < golden["int8_roundtrip"]["tolerance"]
+
+
+def test_constant_tokens(golden):
+    """llama-gguf kv_quantized.rs `test_shift_left` writes tokens whose
+    elements all equal their position: codes are all 255 (128 at pos 0) and
+    the read-back is within 0.01."""
+    for pos in range(5):
+        x = np.full((2, 4), pos, np.float32)
+        codes, s = orc.quantize(x, 0)
+        assert np.all(codes == (128 if pos == 0 else 255))
+        assert np.max(np.abs(orc.dequantize_f32(codes, s) - x)) < golden["constant_tokens"]["tolerance"]
+
+
+def test_zero_row():
+    """All-zero row: absmax floor 1e-8 gives s = fl32(1e-8/127), codes 128, deq 0."""
+    codes, s = orc.quantize(np.zeros((1, 64), np.float32), 0)
+    assert np.all(codes == 128)
+    assert s[0, 0] == np.float32(np.float32(1e-8) / np.float32(127))
+    assert np.all(orc.dequantize_f32(codes, s) == 0)
+
+
+# ----------------------------------------------------------------------------
+# quantizer: exact-arithmetic and brute-force pins
+# ----------------------------------------------------------------------------
+
+def _is_nearest_f32(result: np.float32, exact: Fraction) -> bool:
+    """True when ``result`` is a float32 nearest to ``exact`` (ties: even)."""
+    r = Fraction(float(result))
+    up = Fraction(float(np.nextafter(result, np.float32(np.inf), dtype=np.float32)))
+    dn = Fraction(float(np.nextafter(result, np.float32(-np.inf), dtype=np.float32)))
+    d = abs(r - exact)
+    if d > abs(up - exact) or d > abs(dn - exact):
+        return False
+    if d == abs(up - exact) or d == abs(dn - exact):        # tie: mantissa even
+        return (np.float32(result).view(np.uint32) & 1) == 0
+    return True
+
+
+def test_scale_and_quotient_are_correctly_rounded():
+    """s and x/s are the fp32 values nearest to the exact rationals m/127 and
+    x/s (IEEE division), checked with exact rational arithmetic."""
+    rng = np.random.default_rng(123)
+    x = (rng.standard_normal((40, 64)) * rng.choice([1e-3, 1.0, 37.0], size=(40, 1))).astype(np.float32)
+    codes, s = orc.quantize(x, 0)
+    for r in range(x.shape[0]):
+        m = max(float(abs(v)) for v in x[r])
+        assert _is_nearest_f32(s[r, 0], Fraction(m) / 127)
+        for j in range(0, 64, 7):
+            y = np.float32(x[r, j] / s[r, 0])
+            assert _is_nearest_f32(y, Fraction(float(x[r, j])) / Fraction(float(s[r, 0])))
+
+
+def test_rounding_brute_force():
+    """Each code is the integer nearest the fp32 quotient (ties away from
+    zero), found by exhaustive search over [-127, 127]."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 32)).astype(np.float32)
+    # plant exact ties: quotients k + 1/2 need s with a short mantissa
+    x[:8, 0] = np.float32(63.5)
+    x[:8, 1:6] = np.float32([0.25, -0.75, 12.25, -30.75, 0.5])
+    codes, s = orc.quantize(x, 32)
+    cand = np.arange(-127, 128)
+    for r in range(x.shape[0]):
+        for j in range(32):
+            y = float(np.float32(x[r, j] / s[r, 0]))
+            dist = np.abs(cand - y)
+            best = np.flatnonzero(dist == dist.min())
+            q = cand[best[np.argmax(np.abs(cand[best]))]]
+            assert codes[r, j] == q + 128, (r, j, y)
+
+
+def _nearest_f32_of(exact: Fraction) -> np.float32:
+    """The fp32 value nearest to an exact rational (ties to even), found by
+    exact comparison among the neighbours of a first guess."""
+    c = np.float32(float(exact))
+    cands = [c]
+    for _ in range(2):
+        cands.append(np.nextafter(cands[-1], np.float32(np.inf), dtype=np.float32))
+    dn = c
+    for _ in range(2):
+        dn = np.nextafter(dn, np.float32(-np.inf), dtype=np.float32)
+        cands.append(dn)
+    best = [v for v in cands if _is_nearest_f32(v, exact)]
+    assert len(best) == 1
+    return best[0]
+
+
+def _round_away(y: float) -> int:
+    return int(math.copysign(math.floor(abs(y) + 0.5), y))
+
+
+def test_division_not_reciprocal_multiply():
+    """Codes come from the correctly rounded quotient x/s.  With s = 3
+    (absmax 381) some x just below (k + 1/2) * 3 round one way through x/s and
+    the other way through x * fl32(1/s); expected codes are derived with exact
+    rational arithmetic."""
+    s = np.float32(3.0)
+    recip = np.float32(1) / s
+    picks = []
+    for k in range(0, 126):
+        x = np.float32((k + 0.5) * 3)
+        for _ in range(30):
+            x = np.nextafter(x, np.float32(-np.inf), dtype=np.float32)
+        for _ in range(60):
+            if _round_away(np.float32(x / s)) != _round_away(np.float32(x * recip)):
+                picks.append(x)
+            x = np.nextafter(x, np.float32(np.inf), dtype=np.float32)
+    assert len(picks) >= 8
+    row = np.zeros(len(picks) + 1 + (-(len(picks) + 1)) % 32, np.float32)
+    row[0] = np.float32(381.0)
+    row[1:len(picks) + 1] = picks
+    row[len(picks) + 1:] = -np.float32(picks[0])
+    codes, sc = orc.quantize(row[None], 0)
+    assert sc[0, 0] == s
+    for j, x in enumerate(row):
+        y = _nearest_f32_of(Fraction(float(x)) / 3)
+        assert codes[0, j] == _round_away(float(y)) + 128, (j, float(x))
+
+
+def test_code_range_and_absmax_code():
+    """Codes lie in [1, 255]; each row's absmax element maps to 1 or 255."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((256, 128)).astype(np.float32)
+    codes, _ = orc.quantize(x, 0)
+    assert codes.min() >= 1 and codes.max() <= 255
+    am = np.argmax(np.abs(x), axis=1)
+    assert np.all(np.isin(codes[np.arange(256), am], [1, 255]))
+    codes32, _ = orc.quantize(x, 32)
+    assert codes32.min() >= 1
+
+
+def test_group_scales_independent():
+    """Group-32 scales see only their own 32 elements (the [P4] group rule):
+    changing one group leaves the others' codes and scales untouched."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 128)).astype(np.float32)
+    c1, s1 = orc.quantize(x, 32)
+    x2 = x.copy()
+    x2[:, 32:64] *= np.float32(50.0)
+    c2, s2 = orc.quantize(x2, 32)
+    keep = np.r_[0:32, 64:128]
+    assert np.array_equal(c1[:, keep], c2[:, keep])
+    assert np.array_equal(s1[:, [0, 2, 3]], s2[:, [0, 2, 3]])
+    assert np.all(s2[:, 1] > s1[:, 1])
+
+
+def test_bf16_rounding_matches_library_cast():
+    """The oracle's fp32->bf16 rounding equals torch's CPU cast (RNE),
+    including exact ties on both parities."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(100000).astype(np.float32) * np.float32(100)
+    ties = (np.arange(0, 4096, dtype=np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+    x = np.concatenate([x, ties.view(np.float32)[10:2000], np.float32([0.0, -0.0, 1.0, -3.5])])
+    ours = orc.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(orc.bf16_bits_to_f32(ours), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+# ----------------------------------------------------------------------------
+# attention: closed forms and brute force
+# ----------------------------------------------------------------------------
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_single_token_gives_v():
+    q = _rand((2, 4, 16), 0)
+    k = _rand((2, 2, 1, 16), 1)
+    v = _rand((2, 2, 1, 16), 2)
+    out = orc.attention_decode(q, k, v, [1, 1], 0.25)
+    for h in range(4):
+        assert np.allclose(out[:, h], v[:, h // 2, 0], rtol=0, atol=1e-15)
+
+
+def test_constant_keys_give_mean_v():
+    k = np.repeat(_rand((1, 2, 1, 8), 3), 9, axis=2)
+    v = _rand((1, 2, 9, 8), 4)
+    q = _rand((1, 6, 8), 5)
+    out = orc.attention_decode(q, k, v, [9], 0.7)
+    for h in range(6):
+        assert np.allclose(out[0, h], v[0, h // 3].mean(axis=0), atol=1e-14)
+
+
+def test_zero_query_and_zero_scale_give_mean_v():
+    k = _rand((1, 1, 5, 8), 6)
+    v = _rand((1, 1, 5, 8), 7)
+    q = np.zeros((1, 1, 8))
+    assert np.allclose(orc.attention_decode(q, k, v, [5], 1.0)[0, 0], v[0, 0].mean(0), atol=1e-14)
+    q = _rand((1, 1, 8), 8)
+    assert np.allclose(orc.attention_decode(q, k, v, [5], 0.0)[0, 0], v[0, 0].mean(0), atol=1e-14)
+
+
+def test_two_token_closed_form():
+    q = _rand((1, 1, 4), 9)
+    k = _rand((1, 1, 2, 4), 10)
+    v = _rand((1, 1, 2, 4), 11)
+    sc = 0.3
+    s0 = sc * sum(q[0, 0, d] * k[0, 0, 0, d] for d in range(4))
+    s1 = sc * sum(q[0, 0, d] * k[0, 0, 1, d] for d in range(4))
+    p0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    expect = p0 * v[0, 0, 0] + (1 - p0) * v[0, 0, 1]
+    assert np.allclose(orc.attention_decode(q, k, v, [2], sc)[0, 0], expect, atol=1e-14)
+
+
+def test_gqa_head_mapping():
+    """Query head h reads KV head h // (H/KVH): with V constant per KV head,
+    each output equals its group's constant (h % KVH would fail)."""
+    H, KVH, L, D = 8, 2, 5, 4
+    v = np.zeros((1, KVH, L, D))
+    v[0, 0] = 1.0
+    v[0, 1] = -2.0
+    out = orc.attention_decode(_rand((1, H, D), 12), _rand((1, KVH, L, D), 13), v, [L], 0.5)
+    assert np.allclose(out[0, :4], 1.0) and np.allclose(out[0, 4:], -2.0)
+
+
+def test_dominant_key_and_length_limit():
+    """A key with a huge score takes all the weight; keys at t >= L are ignored."""
+    D = 8
+    q = np.ones((1, 1, D))
+    k = np.zeros((1, 1, 6, D))
+    k[0, 0, 2] = 100.0
+    k[0, 0, 5] = 1000.0                       # beyond L = 4: must not matter
+    v = _rand((1, 1, 6, D), 14)
+    out = orc.attention_decode(q, k, v, [4], 1.0)
+    assert np.allclose(out[0, 0], v[0, 0, 2], atol=1e-12)
+
+
+def test_token_permutation_invariance():
+    q = _rand((1, 2, 8), 15)
+    k = _rand((1, 1, 11, 8), 16)
+    v = _rand((1, 1, 11, 8), 17)
+    perm = np.random.default_rng(0).permutation(11)
+    a = orc.attention_decode(q, k, v, [11], 0.4)
+    b = orc.attention_decode(q, k[:, :, perm], v[:, :, perm], [11], 0.4)
+    assert np.allclose(a, b, atol=1e-13)
+
+
+def _loop_attention(q, k, v, scale):
+    """Brute force, scalar loops with math.exp (no NumPy reductions)."""
+    scores = [scale * sum(q[d] * k[t][d] for d in range(len(q))) for t in range(len(k))]
+    m = max(scores)
+    w = [math.exp(s - m) for s in scores]
+    z = sum(w)
+    return [sum(w[t] * v[t][d] for t in range(len(k))) / z for d in range(len(q))]
+
+
+def test_brute_force_tiny_decode_and_chunk():
+    rng = np.random.default_rng(21)
+    B, H, KVH, D, L0, n = 2, 4, 2, 5, 3, 4
+    q = rng.standard_normal((B, H, n, D))
+    k = rng.standard_normal((B, KVH, L0 + n, D))
+    v = rng.standard_normal((B, KVH, L0 + n, D))
+    out = orc.attention_chunk(q, k, v, [L0, L0], True, 0.37)
+    for b in range(B):
+        for h in range(H):
+            g = h // 2
+            for i in range(n):
+                vis = L0 + i + 1
+                ref = _loop_attention(list(q[b, h, i]), [list(r) for r in k[b, g, :vis]],
+                                      [list(r) for r in v[b, g, :vis]], 0.37)
+                assert np.allclose(out[b, h, i], ref, atol=1e-13)
+    dec = orc.attention_decode(q[:, :, 0], k, v, [2, 5], 0.37)
+    for b, length in enumerate([2, 5]):
+        for h in range(H):
+            ref = _loop_attention(list(q[b, h, 0]), [list(r) for r in k[b, h // 2, :length]],
+                                  [list(r) for r in v[b, h // 2, :length]], 0.37)
+            assert np.allclose(dec[b, h], ref, atol=1e-13)
+
+
+def test_chunk_rows_equal_decode_and_noncausal():
+    rng = np.random.default_rng(22)
+    B, H, KVH, D, L0, n = 1, 2, 1, 8, 6, 5
+    q = rng.standard_normal((B, H, n, D))
+    k = rng.standard_normal((B, KVH, L0 + n, D))
+    v = rng.standard_normal((B, KVH, L0 + n, D))
+    ch = orc.attention_chunk(q, k, v, [L0], True, 0.5)
+    for i in range(n):
+        assert np.allclose(ch[:, :, i], orc.attention_decode(q[:, :, i], k, v, [L0 + i + 1], 0.5), atol=1e-14)
+    nc = orc.attention_chunk(q, k, v, [L0], False, 0.5)
+    for i in range(n):
+        assert np.allclose(nc[:, :, i], orc.attention_decode(q[:, :, i], k, v, [L0 + n], 0.5), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# cache layouts and the page's end-to-end tolerance
+# ----------------------------------------------------------------------------
+
+def _kv_tok(i, n_kv, d, salt):
+    j = np.arange(n_kv * d)
+    return ((((i * 7 + j * 3 + salt) % 13) / 13.0) - 0.5).astype(np.float32).reshape(n_kv, d)
+
+
+def _q_tok(i, n_q, d):
+    j = np.arange(n_q * d)
+    return ((((i * 11 + j * 5) % 17) / 17.0) - 0.5).astype(np.float32).reshape(n_q, d)
+
+
+def test_quantized_paged_matches_fp(golden):
+    """combs-models kv.rs `quantized_paged_cache_matches_fp_within_tolerance`:
+    prefill 20 tokens (crossing the 16-token page boundary), then decode
+    20..29; quantized (group-32) paged attention stays within 1e-2 of fp
+    attention.  The paged arena, written through a scattered block table,
+    also holds exactly the codes a contiguous cache holds."""
+    g = golden["quantized_paged_vs_fp"]
+    n_kv, n_q, d = g["n_kv"], g["n_q"], g["head_dim"]
+    scale = 0.9 / math.sqrt(d)
+    total = g["decode_to"]
+    K = np.stack([_kv_tok(i, n_kv, d, 0) for i in range(total)], axis=1)[None]   # [1,KVH,T,D]
+    V = np.stack([_kv_tok(i, n_kv, d, 5) for i in range(total)], axis=1)[None]
+    Q = np.stack([_q_tok(i, n_q, d) for i in range(total)], axis=1)[None]        # [1,H,T,D]
+    nblocks = 4
+    table = np.array([[7, 2, 5, 0]], np.int32)
+    arena = [np.zeros((8, n_kv, 16, d), np.uint8), np.zeros((8, n_kv, 16, 1), np.float32),
+             np.zeros((8, n_kv, 16, d), np.uint8), np.zeros((8, n_kv, 16, 1), np.float32)]
+    cont = [np.zeros((1, n_kv, nblocks * 16, d), np.uint8), np.zeros((1, n_kv, nblocks * 16, 1), np.float32),
+            np.zeros((1, n_kv, nblocks * 16, d), np.uint8), np.zeros((1, n_kv, nblocks * 16, 1), np.float32)]
+    # prefill chunk
+    orc.paged_append(*arena, table, K[:, :, :20], V[:, :, :20], [0], 32)
+    orc.contiguous_append(*cont, K[:, :, :20], V[:, :, :20], [0], 32)
+    for pos in range(20, total):
+        orc.paged_append(*arena, table, K[:, :, pos:pos + 1], V[:, :, pos:pos + 1], [pos], 32)
+        orc.contiguous_append(*cont, K[:, :, pos:pos + 1], V[:, :, pos:pos + 1], [pos], 32)
+    L = total
+    kc = orc.paged_gather(arena[0], table, 0, L)
+    ks = orc.paged_gather(arena[1], table, 0, L)
+    vc = orc.paged_gather(arena[2], table, 0, L)
+    vs = orc.paged_gather(arena[3], table, 0, L)
+    assert np.array_equal(kc, cont[0][0, :, :L]) and np.array_equal(vs, cont[3][0, :, :L])
+    k_hat = orc.dequantize_exact(kc, ks)[None]
+    v_hat = orc.dequantize_exact(vc, vs)[None]
+    # prefill rows 0..19 (causal chunk at ctx 0), then each decode step
+    qp = Q[:, :, :20].astype(np.float64)
+    a = orc.attention_chunk(qp, k_hat[:, :, :20], v_hat[:, :, :20], [0], True, scale)
+    b = orc.attention_chunk(qp, K[:, :, :20].astype(np.float64), V[:, :, :20].astype(np.float64), [0], True, scale)
+    assert np.max(np.abs(a - b)) < g["tolerance"]
+    for pos in range(20, total):
+        a = orc.attention_decode(Q[:, :, pos].astype(np.float64), k_hat, v_hat, [pos + 1], scale)
+        b = orc.attention_decode(Q[:, :, pos].astype(np.float64), K.astype(np.float64), V.astype(np.float64),
+                                 [pos + 1], scale)
+        assert np.max(np.abs(a - b)) < g["tolerance"]
+
+
+def test_page_slot_arithmetic():
+    table = np.array([[3, 9, 1], [0, 2, 4]], np.int32)
+    assert orc.page_slot(table, 0, 0) == (3, 0)
+    assert orc.page_slot(table, 0, 15) == (3, 15)
+    assert orc.page_slot(table, 0, 16) == (9, 0)
+    assert orc.page_slot(table, 1, 47) == (4, 15)
+
+
+def test_sizing_matches_printed_figures(golden):
+    """realizar kv_cache_q8_init.rs: the byte formulas, and the printed
+    "8.59 GB" / "2.15 GB" read as batch 8 (codes only for the Q8 figure)."""
+    s = golden["sizing"]
+    kw = dict(num_kv_heads=s["num_kv_heads"], max_len=s["max_len"], head_dim=s["head_dim"],
+              layers=s["layers"])
+    assert orc.fp32_equivalent_bytes(**kw) == s["per_sequence_fp32_bytes"]
+    assert orc.cache_bytes(group=32, **kw) == s["per_sequence_q8_bytes"]
+    assert orc.fp32_equivalent_bytes(batch=8, **kw) == s["batch8_fp32_bytes"]
+    assert orc.codes_bytes(batch=8, **kw) == s["batch8_codes_bytes"]
+    assert orc.cache_bytes(group=32, batch=8, **kw) == s["batch8_q8_total_bytes"]
+    assert f"{s['batch8_fp32_bytes'] / 1e9:.2f} GB" == s["printed_fp32"]
+    assert f"{s['batch8_codes_bytes'] / 1e9:.2f} GB" == s["printed_q8"]
+    # the page's own product, evaluated, is 1.07e9 (garbled figure)
+    assert 32 * 2 * 4096 * 8 * 128 * 4 == s["per_sequence_fp32_bytes"]
