@@ -1,0 +1,189 @@
+/*
+ * kvq.h — C ABI of libkvq: an INT8-quantized KV cache for AMD MI355X (gfx950).
+ *
+ * What the library computes (sources are docs.rs source pages, cited by page
+ * title and Rust item):
+ *   - quantize-on-append: symmetric absmax/127 codes stored as u8 with a +128
+ *     offset, one fp32 scale per token row or per 32 elements along head_dim
+ *     (abaddon 0.2.0-rc.1 src/kv_cache_quant_cuda.rs, `quantize_tensor`;
+ *     combs-models 0.2.2 src/kv.rs, `kv_quantize`; realizar 0.8.5
+ *     src/cuda/executor/kv_cache_q8_init.rs, `init_kv_cache_q8_gpu`);
+ *   - attention directly on those codes, dequantizing in registers
+ *     (abaddon kv_cache_quant_cuda.rs module doc, "fused approach"), over GQA
+ *     heads, in a contiguous or a paged (16-token pages) layout (combs-models
+ *     kv.rs, `PagedKVCache`, `attend`).
+ *
+ * Conventions (every entry point):
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no global mutable state besides a thread-local
+ *     error message, never synchronizes and never reads device memory on the
+ *     host.  Work is enqueued on `stream` (a hipStream_t; NULL = null stream).
+ *   - Return value: KVQ_OK, or an error code with a message available from
+ *     kvq_last_error() on the calling thread.  On error nothing is enqueued.
+ *   - Layouts (row-major, last index fastest):
+ *       new K/V rows       [batch, num_kv_heads, n_new, head_dim]
+ *       queries / outputs  [batch, num_heads, n, head_dim]   (n = 1: [B, H, D])
+ *       contiguous cache   codes [batch, num_kv_heads, max_len, head_dim] u8,
+ *                          scales [batch, num_kv_heads, max_len, G] fp32
+ *       paged arena        codes [num_pages, num_kv_heads, 16, head_dim] u8,
+ *                          scales [num_pages, num_kv_heads, 16, G] fp32,
+ *                          block_table [batch, max_blocks_per_seq] int32
+ *     with G = 1 (KVQ_SCALE_PER_TOKEN) or head_dim/32 (KVQ_SCALE_GROUP32).
+ *   - GQA: query head h reads KV head h / (num_heads / num_kv_heads)
+ *     (combs-models kv.rs, `repeat_kv`).
+ *   - Host-checkable argument errors return KVQ_ERR_INVALID_ARG (null
+ *     pointer, num_heads % num_kv_heads != 0, head_dim not a multiple of 32 or
+ *     above 256, paged page_size != 16, n_new <= 0, ...).  Device-side values
+ *     (positions, lengths, page ids) are the caller's contract; kernels clamp
+ *     or skip out-of-range ones so that no access leaves the buffers described
+ *     by the descriptor.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1,  /* bad descriptor or argument (host-checkable)        */
+  KVQ_ERR_OUT_OF_RANGE = 2, /* host-known size beyond the cache capacity          */
+  KVQ_ERR_UNSUPPORTED = 3,  /* valid but not implemented (e.g. head_dim 96 decode) */
+  KVQ_ERR_HIP = 4,          /* kernel launch failed (hipGetLastError)             */
+  KVQ_ERR_WORKSPACE = 5     /* workspace missing or smaller than required          */
+} kvq_status;
+
+enum { KVQ_SCALE_PER_TOKEN = 0, KVQ_SCALE_GROUP32 = 1 };
+enum { KVQ_LAYOUT_CONTIGUOUS = 0, KVQ_LAYOUT_PAGED = 1 };
+enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 };
+
+/* One layer's K/V cache (the pages keep one cache per layer: realizar
+ * kv_cache_q8_init.rs per-layer buffers; combs-models kv.rs per-layer arena). */
+typedef struct kvq_cache {
+  int32_t batch;               /* sequences                                       */
+  int32_t num_heads;           /* query heads H                                   */
+  int32_t num_kv_heads;        /* KV heads KVH, H % KVH == 0                      */
+  int32_t head_dim;            /* D: multiple of 32, at most 256                  */
+  int32_t layout;              /* KVQ_LAYOUT_*                                    */
+  int32_t scale_mode;          /* KVQ_SCALE_*                                     */
+  int32_t max_len;             /* contiguous: per-sequence capacity (tokens)      */
+  int32_t page_size;           /* paged: must be 16                               */
+  int32_t num_pages;           /* paged: arena pages P                            */
+  int32_t max_blocks_per_seq;  /* paged: block-table row length                   */
+  const int32_t* block_table;  /* paged: device [batch, max_blocks_per_seq]       */
+  uint8_t* k_codes;            /* device, layout above                            */
+  uint8_t* v_codes;
+  float* k_scales;
+  float* v_scales;
+} kvq_cache;
+
+/*
+ * kvq_append — quantize n_new new K and V rows per (sequence, KV head) and
+ * write them at logical positions start_pos[b] .. start_pos[b] + n_new - 1.
+ *
+ * Follows abaddon kv_cache_quant_cuda.rs `CudaQuantizedKvCache::quantize_tensor`
+ * step by step in IEEE fp32: m = max(max|x|, 1e-8); s = m / 127 (correctly
+ * rounded); q = round-half-away-from-zero(x / s) (correctly rounded quotient);
+ * code = q + 128 in [1, 255].  Group-32 scales take the max over 32 elements
+ * (combs-models kv.rs `kv_quantize`); scales are stored as fp32 (realizar
+ * kv_cache_q8_init.rs).  The slot write is a fixed-capacity store: contiguous
+ * row (b, h, p) sits at ((b*KVH + h)*max_len + p); paged position p of
+ * sequence b sits in page block_table[b][p/16], slot p%16 (combs-models kv.rs
+ * `PagedKVCache::attention_opts` write loop).
+ *
+ *   k_new, v_new : device [B, KVH, n_new, D], fp32 or bf16 (in_dtype)
+ *   start_pos    : device int32 [B]
+ * Errors: INVALID_ARG (nulls, bad descriptor, n_new <= 0, bad dtype),
+ * OUT_OF_RANGE (n_new larger than the per-sequence capacity).  Rows whose
+ * device position or page id falls outside the cache are not written.
+ */
+kvq_status kvq_append(const kvq_cache* cache, const void* k_new, const void* v_new,
+                      int32_t in_dtype, int32_t n_new, const int32_t* start_pos,
+                      void* stream);
+
+/*
+ * kvq_attention_decode — one query token per sequence attends to the first
+ * seq_lens[b] cached tokens (the tokens appended for this step included; a
+ * decode query at the end of the window needs no mask: combs-models kv.rs
+ * `attend`).  out[b,h,:] = softmax_t(attn_scale * q.k_hat_t) . v_hat_t with
+ * k_hat = (code - 128) * scale dequantized in registers (abaddon
+ * kv_cache_quant_cuda.rs module doc, fused approach).  Computed as split-K
+ * partials (m, l, o) per token range, merged with a log-sum-exp combine; the
+ * result is rounded to bf16 (nearest even).
+ *
+ *   q         : device bf16 [B, H, D]
+ *   seq_lens  : device int32 [B]; each in [1, max_seq_len_hint] (values are
+ *               clamped to [0, min(hint, capacity)]; a length of 0 gives zeros)
+ *   out       : device bf16 [B, H, D]
+ *   workspace : device scratch of at least kvq_workspace_size(cache,
+ *               max_seq_len_hint, 1) bytes (split partials); may be NULL when
+ *               that size is 0.  Contents need no initialisation.
+ * Errors: INVALID_ARG, OUT_OF_RANGE (hint beyond capacity or < 1),
+ * WORKSPACE, UNSUPPORTED (head_dim not in {32, 64, 128, 256}), HIP.
+ */
+kvq_status kvq_attention_decode(const kvq_cache* cache, const uint16_t* q,
+                                const int32_t* seq_lens, float attn_scale, uint16_t* out,
+                                void* workspace, size_t workspace_bytes,
+                                int32_t max_seq_len_hint, void* stream);
+
+/*
+ * kvq_attention_chunk — chunked prefill: n queries per sequence, already
+ * appended at positions ctx_lens[b] .. ctx_lens[b] + n - 1, attend to the
+ * cache.  With causal != 0 query i sees keys t <= ctx_lens[b] + i
+ * (bottom-right alignment: abaddon kv_cache_quant_cuda.rs
+ * `forward_attention`, cache_offset = seq_len - q_len; combs-models kv.rs
+ * `attend`); otherwise all ctx_lens[b] + n keys.  bf16 MFMA on dequantized
+ * tiles, fp32 accumulation, bf16 output.
+ *
+ *   q        : device bf16 [B, H, n, D];  out : device bf16 [B, H, n, D]
+ *   ctx_lens : device int32 [B], tokens cached before the chunk
+ *   max_ctx_len_hint : host upper bound on ctx_lens (sizes the launch)
+ *   workspace: kvq_workspace_size(cache, max_ctx_len_hint + n, n) bytes
+ * Errors: INVALID_ARG, OUT_OF_RANGE, WORKSPACE, UNSUPPORTED (head_dim != 128
+ * or 64), HIP.
+ */
+kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_t n,
+                               const int32_t* ctx_lens, int32_t causal, float attn_scale,
+                               uint16_t* out, void* workspace, size_t workspace_bytes,
+                               int32_t max_ctx_len_hint, void* stream);
+
+/*
+ * kvq_dequant — materialise one cache side as values: out[b,h,t,d] =
+ * fl32((code - 128) * scale) (abaddon kv_cache_quant_cuda.rs
+ * `int8_dequant_bf16`; abaddon 0.2.0-rc.2 kv_cache_quant.rs `dequantize`),
+ * optionally rounded to bf16 (nearest even).  Positions t >= seq_lens[b]
+ * (clamped to capacity) are written as 0.
+ *
+ *   which   : 0 = K, 1 = V
+ *   out     : device [B, KVH, out_len, D] of out_dtype
+ * Errors: INVALID_ARG, OUT_OF_RANGE (out_len beyond capacity), HIP.
+ */
+kvq_status kvq_dequant(const kvq_cache* cache, int32_t which, const int32_t* seq_lens,
+                       int32_t out_dtype, void* out, int32_t out_len, void* stream);
+
+/* Workspace bytes needed by kvq_attention_decode (n_query = 1) or
+ * kvq_attention_chunk (n_query = chunk length) for lengths up to
+ * max_seq_len.  0 on an invalid descriptor (see kvq_last_error). */
+size_t kvq_workspace_size(const kvq_cache* cache, int32_t max_seq_len, int32_t n_query);
+
+/* Bytes of codes plus scales the descriptor addresses, K and V together
+ * (realizar kv_cache_q8_init.rs `kv_cache_q8_memory_bytes`: 2 * (values +
+ * 4 * scales) per layer).  Contiguous: batch*KVH*max_len rows; paged:
+ * num_pages*KVH*16 rows.  0 on an invalid descriptor. */
+uint64_t kvq_cache_bytes(const kvq_cache* cache);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Library version string. */
+const char* kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

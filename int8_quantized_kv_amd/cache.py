@@ -1,0 +1,103 @@
+"""Torch-owned storage for one layer's INT8 KV cache, driven through libkvq.
+
+PyTorch only allocates device memory and provides the stream; every step of
+quantization, append, attention and dequantization runs in libkvq's kernels.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import kvq as _k
+
+
+class Int8KVCache:
+    """One layer's cache: u8 codes + fp32 scales, contiguous or paged.
+
+    Contiguous: codes ``[B, KVH, max_len, D]``, scales ``[B, KVH, max_len, G]``.
+    Paged: arena codes ``[P, KVH, 16, D]``, scales ``[P, KVH, 16, G]``, with a
+    caller-provided int32 ``block_table [B, max_blocks_per_seq]``.
+    """
+
+    def __init__(self, batch: int, num_heads: int, num_kv_heads: int, head_dim: int, *,
+                 max_len: int = 0, group32: bool = False, num_pages: int = 0,
+                 block_table: torch.Tensor | None = None, device="cuda", fill: int | None = None):
+        self.batch, self.num_heads, self.num_kv_heads, self.head_dim = batch, num_heads, num_kv_heads, head_dim
+        self.groups = head_dim // 32 if group32 else 1
+        self.paged = block_table is not None
+        if self.paged:
+            rows = (num_pages, num_kv_heads, 16)
+            self.block_table = block_table.to(device=device, dtype=torch.int32).contiguous()
+            self.max_blocks = self.block_table.shape[1]
+            self.capacity = self.max_blocks * 16
+        else:
+            rows = (batch, num_kv_heads, max_len)
+            self.block_table = None
+            self.max_blocks = 0
+            self.capacity = max_len
+        shape_c = rows + (head_dim,)
+        shape_s = rows + (self.groups,)
+        if fill is None:
+            self.k_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
+            self.v_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
+        else:
+            self.k_codes = torch.full(shape_c, fill, dtype=torch.uint8, device=device)
+            self.v_codes = torch.full(shape_c, fill, dtype=torch.uint8, device=device)
+        self.k_scales = torch.zeros(shape_s, dtype=torch.float32, device=device)
+        self.v_scales = torch.zeros(shape_s, dtype=torch.float32, device=device)
+        self.desc = _k.make_cache(
+            batch, num_heads, num_kv_heads, head_dim, self.k_codes, self.v_codes, self.k_scales,
+            self.v_scales,
+            layout=_k.KVQ_LAYOUT_PAGED if self.paged else _k.KVQ_LAYOUT_CONTIGUOUS,
+            scale_mode=_k.KVQ_SCALE_GROUP32 if group32 else _k.KVQ_SCALE_PER_TOKEN,
+            max_len=0 if self.paged else max_len, num_pages=num_pages,
+            max_blocks_per_seq=self.max_blocks, block_table=self.block_table)
+
+    # -- entry points -----------------------------------------------------------
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor, start_pos: torch.Tensor, stream=None):
+        """k_new/v_new: [B, KVH, n, D] fp32 or bf16 on the device; start_pos int32 [B]."""
+        dt = _k.KVQ_DT_BF16 if k_new.dtype == torch.bfloat16 else _k.KVQ_DT_F32
+        if k_new.dtype not in (torch.float32, torch.bfloat16) or v_new.dtype != k_new.dtype:
+            raise TypeError("k_new and v_new must both be float32 or both bfloat16")
+        if not (k_new.is_contiguous() and v_new.is_contiguous()):
+            raise ValueError("k_new and v_new must be contiguous")
+        _k.kvq_append(self.desc, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
+
+    def workspace(self, max_seq_len: int, n_query: int = 1) -> torch.Tensor:
+        n = _k.kvq_workspace_size(self.desc, max_seq_len, n_query)
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.k_codes.device)
+
+    def decode(self, q: torch.Tensor, seq_lens: torch.Tensor, attn_scale: float, max_seq_len_hint: int,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+        """q: bf16 [B, H, D]; returns bf16 [B, H, D]."""
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace(max_seq_len_hint, 1)
+        _k.kvq_attention_decode(self.desc, q, seq_lens, attn_scale, out, workspace, workspace.numel(),
+                                max_seq_len_hint, stream)
+        return out
+
+    def chunk(self, q: torch.Tensor, ctx_lens: torch.Tensor, causal: bool, attn_scale: float,
+              max_ctx_len_hint: int, out: torch.Tensor | None = None,
+              workspace: torch.Tensor | None = None, stream=None):
+        """q: bf16 [B, H, n, D]; returns bf16 [B, H, n, D]."""
+        n = q.shape[2]
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace(max_ctx_len_hint + n, n)
+        _k.kvq_attention_chunk(self.desc, q, n, ctx_lens, causal, attn_scale, out, workspace,
+                               workspace.numel(), max_ctx_len_hint, stream)
+        return out
+
+    def dequant(self, which: int, seq_lens: torch.Tensor, out_len: int, bf16: bool = False, stream=None):
+        dt = torch.bfloat16 if bf16 else torch.float32
+        out = torch.empty((self.batch, self.num_kv_heads, out_len, self.head_dim), dtype=dt,
+                          device=self.k_codes.device)
+        _k.kvq_dequant(self.desc, which, seq_lens, _k.KVQ_DT_BF16 if bf16 else _k.KVQ_DT_F32, out, out_len,
+                       stream)
+        return out
+
+    def nbytes(self) -> int:
+        return _k.kvq_cache_bytes(self.desc)

@@ -1,0 +1,167 @@
+// C ABI entry points of libkvq: argument validation, launch planning and the
+// thread-local error message.  No allocation, no synchronisation, no device
+// reads on the host.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <cmath>
+
+#include "kvq_internal.hpp"
+
+#define KVQ_API extern "C" __attribute__((visibility("default")))
+
+namespace kvq {
+
+thread_local char g_err[512] = "";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+namespace {
+
+// Descriptor checks common to every entry point.
+kvq_status check_cache(const kvq_cache* c, const char* who) {
+  if (!c) return fail(KVQ_ERR_INVALID_ARG, "%s: cache descriptor is NULL", who);
+  if (c->batch <= 0 || c->num_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: batch, num_heads, num_kv_heads and head_dim must be positive", who);
+  if (c->num_heads % c->num_kv_heads != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: num_heads (%d) must be a multiple of num_kv_heads (%d)", who,
+                c->num_heads, c->num_kv_heads);
+  if (c->head_dim % 32 != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be a multiple of 32", who, c->head_dim);
+  if (c->head_dim > 256)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be at most 256", who, c->head_dim);
+  if (c->scale_mode != KVQ_SCALE_PER_TOKEN && c->scale_mode != KVQ_SCALE_GROUP32)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: unknown scale_mode %d", who, c->scale_mode);
+  if (c->layout == KVQ_LAYOUT_CONTIGUOUS) {
+    if (c->max_len <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: contiguous cache needs max_len > 0", who);
+  } else if (c->layout == KVQ_LAYOUT_PAGED) {
+    if (c->page_size != kPageSize)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: page_size must be %d (got %d)", who, kPageSize, c->page_size);
+    if (c->num_pages <= 0 || c->max_blocks_per_seq <= 0)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: paged cache needs num_pages > 0 and max_blocks_per_seq > 0", who);
+    if (!c->block_table) return fail(KVQ_ERR_INVALID_ARG, "%s: paged cache needs a block_table", who);
+    if (static_cast<int64_t>(c->max_blocks_per_seq) * kPageSize > 0x7fffffffLL)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: max_blocks_per_seq too large", who);
+  } else {
+    return fail(KVQ_ERR_INVALID_ARG, "%s: unknown layout %d", who, c->layout);
+  }
+  if (!c->k_codes || !c->v_codes || !c->k_scales || !c->v_scales)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: cache code and scale pointers must be non-NULL", who);
+  return KVQ_OK;
+}
+
+kvq_status check_split_workspace(size_t need, void* ws, size_t ws_bytes, const char* who) {
+  if (need == 0) return KVQ_OK;
+  if (!ws) return fail(KVQ_ERR_WORKSPACE, "%s: workspace is NULL but %zu bytes are needed", who, need);
+  if (ws_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE, "%s: workspace of %zu bytes is smaller than the %zu bytes needed", who,
+                ws_bytes, need);
+  return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+KVQ_API const char* kvq_last_error(void) { return g_err; }
+
+KVQ_API const char* kvq_version(void) { return "kvq 0.1.0 (gfx950)"; }
+
+KVQ_API uint64_t kvq_cache_bytes(const kvq_cache* c) {
+  g_err[0] = '\0';
+  if (check_cache(c, "kvq_cache_bytes") != KVQ_OK) return 0;
+  const uint64_t rows = c->layout == KVQ_LAYOUT_PAGED
+                            ? static_cast<uint64_t>(c->num_pages) * c->num_kv_heads * kPageSize
+                            : static_cast<uint64_t>(c->batch) * c->num_kv_heads * c->max_len;
+  const uint64_t per_row = static_cast<uint64_t>(c->head_dim) + 4ull * scales_per_row(*c);
+  return 2ull * rows * per_row;
+}
+
+KVQ_API size_t kvq_workspace_size(const kvq_cache* c, int32_t max_seq_len, int32_t n_query) {
+  g_err[0] = '\0';
+  if (check_cache(c, "kvq_workspace_size") != KVQ_OK) return 0;
+  if (max_seq_len <= 0 || n_query <= 0) {
+    fail(KVQ_ERR_INVALID_ARG, "kvq_workspace_size: max_seq_len and n_query must be positive");
+    return 0;
+  }
+  if (n_query == 1) return plan_decode(*c, max_seq_len).workspace;
+  return chunk_workspace(*c, max_seq_len, n_query);
+}
+
+KVQ_API kvq_status kvq_append(const kvq_cache* c, const void* k_new, const void* v_new, int32_t in_dtype,
+                              int32_t n_new, const int32_t* start_pos, void* stream) {
+  const char* who = "kvq_append";
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new || !start_pos) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new, v_new and start_pos must be non-NULL", who);
+  if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
+  if (n_new <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: n_new must be positive (got %d)", who, n_new);
+  if (n_new > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: n_new (%d) exceeds the per-sequence capacity (%d)", who, n_new,
+                capacity_of(*c));
+  return launch_append(*c, k_new, v_new, in_dtype, n_new, start_pos, static_cast<hipStream_t>(stream));
+}
+
+KVQ_API kvq_status kvq_attention_decode(const kvq_cache* c, const uint16_t* q, const int32_t* seq_lens,
+                                        float attn_scale, uint16_t* out, void* workspace,
+                                        size_t workspace_bytes, int32_t max_seq_len_hint, void* stream) {
+  const char* who = "kvq_attention_decode";
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (!q || !seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, seq_lens and out must be non-NULL", who);
+  if (!(attn_scale == attn_scale) || attn_scale == INFINITY || attn_scale == -INFINITY)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
+  if (max_seq_len_hint < 1 || max_seq_len_hint > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
+                capacity_of(*c));
+  if (!decode_supported(c->head_dim))
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
+  const DecodePlan plan = plan_decode(*c, max_seq_len_hint);
+  st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
+  if (st != KVQ_OK) return st;
+  return launch_decode(*c, plan, q, seq_lens, attn_scale, out, workspace, max_seq_len_hint,
+                       static_cast<hipStream_t>(stream));
+}
+
+KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens,
+                                       int32_t causal, float attn_scale, uint16_t* out, void* workspace,
+                                       size_t workspace_bytes, int32_t max_ctx_len_hint, void* stream) {
+  const char* who = "kvq_attention_chunk";
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (!q || !ctx_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, ctx_lens and out must be non-NULL", who);
+  if (n <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: n must be positive (got %d)", who, n);
+  if (!(attn_scale == attn_scale) || attn_scale == INFINITY || attn_scale == -INFINITY)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
+  if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
+                static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
+  if (!chunk_supported(c->head_dim))
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported", who, c->head_dim);
+  st = check_split_workspace(chunk_workspace(*c, max_ctx_len_hint + n, n), workspace, workspace_bytes, who);
+  if (st != KVQ_OK) return st;
+  return launch_chunk(*c, q, n, ctx_lens, causal, attn_scale, out, workspace, max_ctx_len_hint,
+                      static_cast<hipStream_t>(stream));
+}
+
+KVQ_API kvq_status kvq_dequant(const kvq_cache* c, int32_t which, const int32_t* seq_lens, int32_t out_dtype,
+                               void* out, int32_t out_len, void* stream) {
+  const char* who = "kvq_dequant";
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "%s: which must be 0 (K) or 1 (V)", who);
+  if (!seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: seq_lens and out must be non-NULL", who);
+  if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: out_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
+  if (out_len <= 0 || out_len > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: out_len (%d) must be in [1, %d]", who, out_len, capacity_of(*c));
+  return launch_dequant(*c, which, seq_lens, out_dtype, out, out_len, static_cast<hipStream_t>(stream));
+}

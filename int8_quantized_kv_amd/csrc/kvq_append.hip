@@ -1,0 +1,244 @@
+// Quantize-on-append and dequantization kernels.
+//
+// One wave64 per token row (b, kv head, token) of K or V: the lanes load the
+// row with one vector load each, reduce |x| to the row (or 32-element group)
+// maximum across lanes, and emit codes with a correctly rounded fp32
+// division and round-half-away-from-zero (abaddon 0.2.0-rc.1
+// src/kv_cache_quant_cuda.rs, `CudaQuantizedKvCache::quantize_tensor`;
+// group-32 from combs-models 0.2.2 src/kv.rs, `kv_quantize`).  The maximum is
+// exact, so the reduction order cannot change a code.
+#include "kvq_internal.hpp"
+
+namespace kvq {
+namespace {
+
+struct AppendParams {
+  const void* src[2];        // K, V new rows [B, KVH, n, D]
+  uint8_t* codes[2];
+  float* scales[2];
+  const int32_t* start_pos;  // [B]
+  CacheGeom geom;
+  int32_t batch, n, head_dim, groups;  // groups = scales per row
+  int32_t rows_per_side;               // B * KVH * n
+};
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<float> {
+  template <int N>
+  __device__ static void load(const float* p, float (&x)[N]) {
+    if constexpr (N == 1) {
+      x[0] = p[0];
+    } else if constexpr (N == 2) {
+      float2 v = *reinterpret_cast<const float2*>(p);
+      x[0] = v.x; x[1] = v.y;
+    } else {
+      float4 v = *reinterpret_cast<const float4*>(p);
+      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    }
+  }
+};
+template <>
+struct Vec<uint16_t> {
+  template <int N>
+  __device__ static void load(const uint16_t* p, float (&x)[N]) {
+    if constexpr (N == 1) {
+      x[0] = bf16_to_f32(p[0]);
+    } else if constexpr (N == 2) {
+      uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+      x[0] = __uint_as_float(v << 16);
+      x[1] = __uint_as_float(v & 0xffff0000u);
+    } else {
+      uint2 v = *reinterpret_cast<const uint2*>(p);
+      x[0] = __uint_as_float(v.x << 16);
+      x[1] = __uint_as_float(v.x & 0xffff0000u);
+      x[2] = __uint_as_float(v.y << 16);
+      x[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+  }
+};
+
+// EPL: elements per lane (1, 2 or 4); a row of D elements uses D/EPL <= 64
+// lanes.  GROUP32: one scale per 32 elements (32/EPL lanes) instead of one
+// per row.
+template <int EPL, typename TIn, bool GROUP32>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (r >= 2 * p.rows_per_side) return;
+  const int side = r >= p.rows_per_side ? 1 : 0;
+  const int row = r - side * p.rows_per_side;
+  const int i = row % p.n;
+  const int bh = row / p.n;
+  const int h = bh % p.geom.kvh;
+  const int b = bh / p.geom.kvh;
+  const int pos = p.start_pos[b] + i;
+  const int64_t dst = cache_row(p.geom, b, h, pos);
+  if (dst < 0) return;  // outside the cache: not written
+
+  const int D = p.head_dim;
+  const int active = D / EPL;
+  const bool on = lane < active;
+  float x[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] = 0.0f;
+  const TIn* src = static_cast<const TIn*>(p.src[side]) + static_cast<int64_t>(row) * D;
+  if (on) Vec<TIn>::template load<EPL>(src + lane * EPL, x);
+
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
+  // Maximum over the row, or over the 32/EPL lanes of one group.
+  constexpr int kGroupLanes = 32 / EPL;
+  const int span = GROUP32 ? kGroupLanes : kWave;
+  for (int off = span / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
+
+  const float m = fmaxf(a, 1e-8f);
+  const float s = m / 127.0f;  // IEEE division (correctly rounded)
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    float y = x[e] / s;        // IEEE division, not a reciprocal multiply
+    float q = roundf(y);       // half away from zero
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    packed |= static_cast<uint32_t>(static_cast<int>(q) + 128) << (8 * e);
+  }
+  if (on) {
+    uint8_t* out = p.codes[side] + dst * D + lane * EPL;
+    if constexpr (EPL == 1) {
+      *out = static_cast<uint8_t>(packed);
+    } else if constexpr (EPL == 2) {
+      *reinterpret_cast<uint16_t*>(out) = static_cast<uint16_t>(packed);
+    } else {
+      *reinterpret_cast<uint32_t*>(out) = packed;
+    }
+    float* sc = p.scales[side] + dst * p.groups;
+    if (GROUP32) {
+      if ((lane % kGroupLanes) == 0) sc[lane / kGroupLanes] = s;
+    } else if (lane == 0) {
+      sc[0] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantization: out = fl32((code - 128) * s) (abaddon kv_cache_quant_cuda.rs
+// `int8_dequant_bf16`; abaddon 0.2.0-rc.2 src/kv_cache_quant.rs
+// `dequantize`), optionally rounded to bf16.  One thread per 4 elements.
+// ---------------------------------------------------------------------------
+struct DequantParams {
+  const uint8_t* codes;
+  const float* scales;
+  const int32_t* seq_lens;
+  void* out;
+  CacheGeom geom;
+  int32_t batch, head_dim, groups, out_len, out_bf16;
+  int64_t quads;  // B * KVH * out_len * D / 4
+};
+
+__global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= p.quads) return;
+  const int D = p.head_dim;
+  const int64_t e0 = idx * 4;
+  const int d = static_cast<int>(e0 % D);
+  const int64_t trow = e0 / D;  // (b*KVH + h)*out_len + t
+  const int t = static_cast<int>(trow % p.out_len);
+  const int64_t bh = trow / p.out_len;
+  const int h = static_cast<int>(bh % p.geom.kvh);
+  const int b = static_cast<int>(bh / p.geom.kvh);
+  int len = p.seq_lens[b];
+  len = len < 0 ? 0 : (len > capacity(p.geom) ? capacity(p.geom) : len);
+  float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t row = t < len ? cache_row(p.geom, b, h, t) : -1;
+  if (row >= 0) {
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
+    const float s = p.scales[row * p.groups + (p.groups == 1 ? 0 : d / 32)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = static_cast<float>(static_cast<int>((c >> (8 * e)) & 0xffu) - 128) * s;
+  }
+  if (p.out_bf16) {
+    ushort4 o;
+    o.x = f32_to_bf16_rne(v[0]);
+    o.y = f32_to_bf16_rne(v[1]);
+    o.z = f32_to_bf16_rne(v[2]);
+    o.w = f32_to_bf16_rne(v[3]);
+    reinterpret_cast<ushort4*>(p.out)[idx] = o;
+  } else {
+    reinterpret_cast<float4*>(p.out)[idx] = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <typename TIn, bool G32>
+void dispatch_epl(int epl, dim3 grid, hipStream_t st, const AppendParams& p) {
+  if (epl == 1)
+    hipLaunchKernelGGL((append_kernel<1, TIn, G32>), grid, dim3(256), 0, st, p);
+  else if (epl == 2)
+    hipLaunchKernelGGL((append_kernel<2, TIn, G32>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((append_kernel<4, TIn, G32>), grid, dim3(256), 0, st, p);
+}
+
+}  // namespace
+
+kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_new, int in_dtype,
+                         int n_new, const int32_t* start_pos, hipStream_t stream) {
+  AppendParams p;
+  p.src[0] = k_new;
+  p.src[1] = v_new;
+  p.codes[0] = c.k_codes;
+  p.codes[1] = c.v_codes;
+  p.scales[0] = c.k_scales;
+  p.scales[1] = c.v_scales;
+  p.start_pos = start_pos;
+  p.geom = geom_of(c);
+  p.batch = c.batch;
+  p.n = n_new;
+  p.head_dim = c.head_dim;
+  p.groups = scales_per_row(c);
+  const int64_t rows = static_cast<int64_t>(c.batch) * c.num_kv_heads * n_new;
+  if (rows * 2 > 0x7fffffffLL) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_append: too many rows (%lld)", (long long)rows);
+  p.rows_per_side = static_cast<int32_t>(rows);
+  // Elements per lane: smallest power of two with D/EPL <= 64.
+  const int epl = c.head_dim <= 64 ? 1 : (c.head_dim <= 128 ? 2 : 4);
+  const int64_t waves = rows * 2;
+  dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+  const bool g32 = c.scale_mode == KVQ_SCALE_GROUP32;
+  if (in_dtype == KVQ_DT_F32) {
+    if (g32) dispatch_epl<float, true>(epl, grid, stream, p);
+    else dispatch_epl<float, false>(epl, grid, stream, p);
+  } else {
+    if (g32) dispatch_epl<uint16_t, true>(epl, grid, stream, p);
+    else dispatch_epl<uint16_t, false>(epl, grid, stream, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_append: launch failed: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens, int out_dtype,
+                          void* out, int out_len, hipStream_t stream) {
+  DequantParams p;
+  p.codes = which ? c.v_codes : c.k_codes;
+  p.scales = which ? c.v_scales : c.k_scales;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.geom = geom_of(c);
+  p.batch = c.batch;
+  p.head_dim = c.head_dim;
+  p.groups = scales_per_row(c);
+  p.out_len = out_len;
+  p.out_bf16 = out_dtype == KVQ_DT_BF16 ? 1 : 0;
+  p.quads = static_cast<int64_t>(c.batch) * c.num_kv_heads * out_len * c.head_dim / 4;
+  if (p.quads == 0) return KVQ_OK;
+  const int64_t blocks = (p.quads + 255) / 256;
+  if (blocks > 0x7fffffffLL) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_dequant: output too large");
+  hipLaunchKernelGGL(dequant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_dequant: launch failed: %s", hipGetErrorString(e));
+  return KVQ_OK;
+}
+
+}  // namespace kvq

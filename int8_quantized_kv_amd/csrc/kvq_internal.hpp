@@ -1,0 +1,61 @@
+// Host-side declarations shared by the libkvq translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+#include "kvq_device.hpp"
+
+namespace kvq {
+
+// Records `msg` as this thread's last error and returns `st`.
+kvq_status fail(kvq_status st, const char* fmt, ...);
+
+inline CacheGeom geom_of(const kvq_cache& c) {
+  CacheGeom g;
+  g.kvh = c.num_kv_heads;
+  g.max_len = c.max_len;
+  g.paged = c.layout == KVQ_LAYOUT_PAGED ? 1 : 0;
+  g.num_pages = c.num_pages;
+  g.max_blocks = c.max_blocks_per_seq;
+  g.block_table = c.block_table;
+  return g;
+}
+
+inline int scales_per_row(const kvq_cache& c) {
+  return c.scale_mode == KVQ_SCALE_GROUP32 ? c.head_dim / 32 : 1;
+}
+
+inline int capacity_of(const kvq_cache& c) {
+  return c.layout == KVQ_LAYOUT_PAGED ? c.max_blocks_per_seq * kPageSize : c.max_len;
+}
+
+// ---- append / dequant -------------------------------------------------------
+kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_new, int in_dtype,
+                         int n_new, const int32_t* start_pos, hipStream_t stream);
+kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens, int out_dtype,
+                          void* out, int out_len, hipStream_t stream);
+
+// ---- decode -----------------------------------------------------------------
+struct DecodePlan {
+  int heads_per_wg;   // query heads sharing one K/V read (a divisor of H/KVH)
+  int split_len;      // tokens per split (multiple of the kernel's pass size)
+  int num_splits;     // splits per sequence for the hinted length
+  size_t workspace;   // bytes of split partials
+};
+bool decode_supported(int head_dim);
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len);
+kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
+                         const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
+                         int max_seq_len, hipStream_t stream);
+
+// ---- chunked prefill --------------------------------------------------------
+bool chunk_supported(int head_dim);
+size_t chunk_workspace(const kvq_cache& c, int max_total_len, int n);
+kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens,
+                        int causal, float attn_scale, uint16_t* out, void* ws, int max_ctx_len,
+                        hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: exported symbols, struct layout, sizing and
+every host-checkable error path (each returns before any HIP call)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+kvq = pytest.importorskip("int8_quantized_kv_amd.kvq")
+
+FAKE = 0x10000  # never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(kvq.EXPORTED)
+    lib = kvq.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kvq_[a-z_]+)", out))
+    assert exported == set(names), exported ^ set(names)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """sizeof/offsetof of kvq_cache from the C compiler equal the ctypes mirror."""
+    fields = [f for f, _ in kvq.kvq_cache._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvq.h"\nint main(void){\n'
+                   '  printf("%zu\\n", sizeof(kvq_cache));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof(kvq_cache, {f}));\n' for f in fields) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(kvq.kvq_cache)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(kvq.kvq_cache, f).offset == off, f
+
+
+def _desc(**kw):
+    base = dict(batch=2, num_heads=8, num_kv_heads=2, head_dim=128, max_len=64)
+    base.update(kw)
+    layout = base.pop("layout", kvq.KVQ_LAYOUT_CONTIGUOUS)
+    scale = base.pop("scale_mode", kvq.KVQ_SCALE_PER_TOKEN)
+    ptrs = base.pop("ptrs", (FAKE, FAKE, FAKE, FAKE))
+    return kvq.make_cache(base.pop("batch"), base.pop("num_heads"), base.pop("num_kv_heads"),
+                          base.pop("head_dim"), *ptrs, layout=layout, scale_mode=scale, **base)
+
+
+def test_cache_bytes_pins_the_q8_sizing():
+    """realizar kv_cache_q8_init.rs sizing: 32 layers x 8 KV heads x 128 dim x
+    4096 positions with group-32 fp32 scales; batch 8 gives the printed
+    "2.15 GB" of codes and 8.59 GB fp32-equivalent."""
+    d = _desc(batch=8, num_heads=32, num_kv_heads=8, head_dim=128, max_len=4096,
+              scale_mode=kvq.KVQ_SCALE_GROUP32)
+    per_layer = kvq.kvq_cache_bytes(d)
+    assert per_layer * 32 == orc.cache_bytes(8, 4096, 128, 32, batch=8, layers=32) == 2_415_919_104
+    codes = 8 * 8 * 4096 * 128 * 2 * 32
+    assert codes == orc.codes_bytes(8, 4096, 128, batch=8, layers=32) == 2_147_483_648
+    assert per_layer * 32 - codes == 268_435_456
+    d1 = _desc(batch=1, num_heads=32, num_kv_heads=8, head_dim=128, max_len=4096,
+               scale_mode=kvq.KVQ_SCALE_GROUP32)
+    assert kvq.kvq_cache_bytes(d1) * 32 == 301_989_888
+    # per-token, paged
+    dp = _desc(batch=4, num_heads=32, num_kv_heads=8, head_dim=128, max_len=0, layout=kvq.KVQ_LAYOUT_PAGED,
+               num_pages=100, max_blocks_per_seq=10, block_table=FAKE)
+    assert kvq.kvq_cache_bytes(dp) == 2 * 100 * 8 * 16 * (128 + 4)
+
+
+def test_workspace_size_positive_and_monotone():
+    d = _desc(batch=16, num_heads=32, num_kv_heads=8, head_dim=128, max_len=4096)
+    a = kvq.kvq_workspace_size(d, 512, 1)
+    b = kvq.kvq_workspace_size(d, 4096, 1)
+    assert 0 < a <= b
+    assert b % (16 * 32 * (128 + 2) * 4) == 0
+
+
+def _status(fn, *args):
+    lib = kvq.library()
+    st = getattr(lib, fn)(*args)
+    return st, kvq.kvq_last_error()
+
+
+INVALID_DESCRIPTORS = [
+    ("heads_not_multiple", dict(num_heads=6, num_kv_heads=4)),
+    ("head_dim_not_32", dict(head_dim=48)),
+    ("head_dim_too_big", dict(head_dim=288)),
+    ("zero_batch", dict(batch=0)),
+    ("bad_scale_mode", dict(scale_mode=7)),
+    ("bad_layout", dict(layout=5)),
+    ("contiguous_no_len", dict(max_len=0)),
+    ("paged_page_size", dict(layout=kvq.KVQ_LAYOUT_PAGED, page_size=8, num_pages=4, max_blocks_per_seq=2,
+                             block_table=FAKE)),
+    ("paged_no_table", dict(layout=kvq.KVQ_LAYOUT_PAGED, num_pages=4, max_blocks_per_seq=2)),
+    ("null_codes", dict(ptrs=(0, FAKE, FAKE, FAKE))),
+    ("null_scales", dict(ptrs=(FAKE, FAKE, FAKE, 0))),
+]
+
+
+@pytest.mark.parametrize("name,kw", INVALID_DESCRIPTORS, ids=[n for n, _ in INVALID_DESCRIPTORS])
+def test_invalid_descriptor_rejected_everywhere(name, kw):
+    d = ctypes.byref(_desc(**kw))
+    calls = [
+        ("kvq_append", (d, FAKE, FAKE, 0, 1, FAKE, None)),
+        ("kvq_attention_decode", (d, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 8, None)),
+        ("kvq_attention_chunk", (d, FAKE, 4, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)),
+        ("kvq_dequant", (d, 0, FAKE, 0, FAKE, 8, None)),
+    ]
+    for fn, args in calls:
+        st, msg = _status(fn, *args)
+        assert st == kvq.KVQ_ERR_INVALID_ARG, (fn, st, msg)
+        assert msg
+    assert kvq.library().kvq_cache_bytes(d) == 0
+    assert kvq.library().kvq_workspace_size(d, 16, 1) == 0
+
+
+def test_null_descriptor():
+    st, msg = _status("kvq_append", None, FAKE, FAKE, 0, 1, FAKE, None)
+    assert st == kvq.KVQ_ERR_INVALID_ARG and "NULL" in msg
+
+
+def test_append_argument_errors():
+    d = ctypes.byref(_desc())
+    assert _status("kvq_append", d, FAKE, FAKE, 0, 0, FAKE, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_append", d, FAKE, FAKE, 0, -3, FAKE, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_append", d, None, FAKE, 0, 1, FAKE, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_append", d, FAKE, FAKE, 0, 1, None, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_append", d, FAKE, FAKE, 9, 1, FAKE, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    st, msg = _status("kvq_append", d, FAKE, FAKE, 0, 65, FAKE, None)
+    assert st == kvq.KVQ_ERR_OUT_OF_RANGE and "capacity" in msg
+
+
+def test_decode_argument_errors():
+    d = ctypes.byref(_desc())
+    ws = kvq.kvq_workspace_size(_desc(), 64, 1)
+    assert _status("kvq_attention_decode", d, None, FAKE, 0.1, FAKE, FAKE, ws, 64, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_attention_decode", d, FAKE, FAKE, float("nan"), FAKE, FAKE, ws, 64, None)[0] == \
+        kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_attention_decode", d, FAKE, FAKE, 0.1, FAKE, FAKE, ws, 65, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
+    assert _status("kvq_attention_decode", d, FAKE, FAKE, 0.1, FAKE, FAKE, ws, 0, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
+    st, msg = _status("kvq_attention_decode", d, FAKE, FAKE, 0.1, FAKE, FAKE, ws - 1, 64, None)
+    assert st == kvq.KVQ_ERR_WORKSPACE and "workspace" in msg
+    assert _status("kvq_attention_decode", d, FAKE, FAKE, 0.1, FAKE, None, ws, 64, None)[0] == kvq.KVQ_ERR_WORKSPACE
+    d96 = ctypes.byref(_desc(head_dim=96))
+    assert _status("kvq_attention_decode", d96, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)[0] == \
+        kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_chunk_and_dequant_argument_errors():
+    d = ctypes.byref(_desc())
+    assert _status("kvq_attention_chunk", d, FAKE, 0, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
+        kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_attention_chunk", d, FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 60, None)[0] == \
+        kvq.KVQ_ERR_OUT_OF_RANGE
+    assert _status("kvq_dequant", d, 2, FAKE, 0, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_dequant", d, 0, FAKE, 3, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_dequant", d, 0, FAKE, 0, FAKE, 65, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
+    assert _status("kvq_dequant", d, 0, None, 0, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+
+
+def test_python_binding_raises():
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_append(_desc(head_dim=48), FAKE, FAKE, 0, 1, FAKE, stream=0)
+    assert e.value.status == kvq.KVQ_ERR_INVALID_ARG
