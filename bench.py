@@ -1,0 +1,300 @@
+"""Benchmark of the INT8-KV decode hot path on one MI355X.
+
+One step = for every layer of the 8B-shaped decode workload (batch 16, 32 query
+/ 8 KV heads, head_dim 128, per-token fp32 scales, 4 outlier channels x10 per
+KV head, 32 layers each with its own cache): quantize-append the new token at
+position 4095 (kvq_append) and run decode attention over 4096 tokens
+(kvq_attention_decode).  The 32 caches (4.44 GB) are visited in order, as a
+model does, so no K/V byte is re-read from the 256 MB Infinity Cache within a
+step.  Inputs are seeded synthetic data, already resident in HBM when timing
+starts.
+
+Prints one JSON line (see --help).  ``--gpus N`` with N > 1 is refused: this
+path is measured on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(w: wl.Workload, L: int) -> dict:
+    """Algorithmic bytes of one layer-step (each byte the step must move once)."""
+    B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    G = 1 if w.group == 0 else D // 32
+    in_bytes = 4 if w.kv_dtype == "f32" else 2
+    codes = 2 * B * KVH * L * D
+    scales = 2 * B * KVH * L * G * 4
+    q = B * H * D * 2
+    out = B * H * D * 2
+    app_in = 2 * B * KVH * D * in_bytes
+    app_codes = 2 * B * KVH * D
+    app_scales = 2 * B * KVH * G * 4
+    decode = codes + scales + q + out
+    return {"decode": decode, "append": app_in + app_codes + app_scales,
+            "step": decode + app_in + app_codes + app_scales}
+
+
+# ----------------------------------------------------------------------------
+# GPU setup
+# ----------------------------------------------------------------------------
+
+def build_layers(w: wl.Workload, kvq, torch, stream, threads: int):
+    """Allocate and prefill every layer's cache through kvq_append."""
+    T = w.ctx + w.n_new
+    dev = torch.device("cuda")
+    layers = []
+
+    def gen(layer):
+        return wl.layer_inputs(w, layer)
+
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        futs = {ex.submit(gen, l): l for l in range(min(w.layers, threads))}
+        nxt = len(futs)
+        done_layers = {}
+        while futs:
+            fut = next(cf.as_completed(futs))
+            l = futs.pop(fut)
+            done_layers[l] = fut.result()
+            if nxt < w.layers:
+                futs[ex.submit(gen, nxt)] = nxt
+                nxt += 1
+            while len(layers) in done_layers:
+                li = len(layers)
+                x = done_layers.pop(li)
+                cache = kvq.Int8KVCache(w.batch, w.num_heads, w.num_kv_heads, w.head_dim, max_len=w.max_len,
+                                        group32=(w.group == 32))
+                k_raw, v_raw = x["k_raw"], x["v_raw"]
+                tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+
+                def up(a):
+                    t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
+                    return t.to(dev, non_blocking=False).view(tdt)
+
+                with torch.cuda.stream(stream):
+                    chunk = 1024
+                    for p0 in range(0, w.ctx, chunk):
+                        n = min(chunk, w.ctx - p0)
+                        cache.append(up(k_raw[:, :, p0:p0 + n]), up(v_raw[:, :, p0:p0 + n]),
+                                     torch.full((w.batch,), p0, dtype=torch.int32, device=dev), stream=stream)
+                    k_new = up(k_raw[:, :, w.ctx:T])
+                    v_new = up(v_raw[:, :, w.ctx:T])
+                    q = torch.from_numpy(x["q_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+                stream.synchronize()
+                layers.append({"cache": cache, "k_new": k_new, "v_new": v_new, "q": q,
+                               "out": torch.empty_like(q)})
+                if len(layers) % 8 == 0 or len(layers) == w.layers:
+                    log(f"prefilled {len(layers)}/{w.layers} layers ({time.time() - t0:.1f}s)")
+    return layers
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the same workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    T = w.ctx + w.n_new
+    # one sequence's worth of the step per call: quantize the new K/V rows,
+    # then fp64 attention over the dequantized cache for all its heads
+    x = wl.layer_inputs(w, 0)
+    nb = w.batch
+    caches = []
+    for b in range(nb):
+        kc, ks = orc.quantize(x["k"][b:b + 1, :, :w.ctx], w.group)
+        vc, vs = orc.quantize(x["v"][b:b + 1, :, :w.ctx], w.group)
+        caches.append((kc, ks, vc, vs))
+
+    def one_seq(b):
+        kc, ks, vc, vs = caches[b]
+        nk, nks = orc.quantize(x["k"][b:b + 1, :, w.ctx:T], w.group)
+        nv, nvs = orc.quantize(x["v"][b:b + 1, :, w.ctx:T], w.group)
+        kcat = np.concatenate([kc, nk], axis=2)
+        kscat = np.concatenate([ks, nks], axis=2)
+        vcat = np.concatenate([vc, nv], axis=2)
+        vscat = np.concatenate([vs, nvs], axis=2)
+        return orc.attention_decode(x["q"][b:b + 1], orc.dequantize_exact(kcat, kscat),
+                                    orc.dequantize_exact(vcat, vscat), [T], w.attn_scale)
+
+    per_seq_bytes = step_bytes(w, T)["step"] / w.batch
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        one_seq(done % nb)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    rate = per_seq_bytes * done / el / 1e12
+    return {"value": rate, "unit": "TB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{done} sequences of layer 0 ({done / w.batch:.2f} layer-steps: quantize 1 new token "
+                      f"+ fp64 attention over {T} tokens, 32 heads), {el:.1f}s wall; numpy elementwise "
+                      f"single-threaded, BLAS threads {blas_threads}; host {platform.processor() or 'x86_64'} "
+                      f"nproc {os.cpu_count()}",
+            "seconds": el}
+
+
+# ----------------------------------------------------------------------------
+# main
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=10,
+                    help="passes over all layers when timing the decode kernel alone")
+    ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures the INT8-KV decode path on one GPU; --gpus {args.gpus} is not supported "
+              "(sequences and KV heads shard with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int8_quantized_kv_amd as kvq
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        with torch.cuda.stream(stream):
+            for _ in range(5):
+                b.copy_(a)
+        stream.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    w = wl.ALL[args.workload]
+    T = w.ctx + w.n_new
+    log(f"workload {w.name}: B={w.batch} H={w.num_heads} KVH={w.num_kv_heads} D={w.head_dim} "
+        f"L={T} layers={w.layers} group={w.group}")
+    layers = build_layers(w, kvq, torch, stream, args.threads)
+    dev = torch.device("cuda")
+    start_pos = torch.full((w.batch,), w.ctx, dtype=torch.int32, device=dev)
+    seq_lens = torch.full((w.batch,), T, dtype=torch.int32, device=dev)
+    ws = layers[0]["cache"].workspace(T, 1)
+
+    def step():
+        for ly in layers:
+            c = ly["cache"]
+            c.append(ly["k_new"], ly["v_new"], start_pos, stream=stream)
+            c.decode(ly["q"], seq_lens, w.attn_scale, T, out=ly["out"], workspace=ws, stream=stream)
+
+    def decode_only():
+        for ly in layers:
+            ly["cache"].decode(ly["q"], seq_lens, w.attn_scale, T, out=ly["out"], workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        torch.cuda.synchronize()
+        log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        step_ms = e0.elapsed_time(e1) / args.steps
+        log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
+
+        # the dominant kernel alone (decode attention), same launch configuration
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.kernel_reps):
+            decode_only()
+        d1.record(stream)
+        stream.synchronize()
+        dec_us = d0.elapsed_time(d1) * 1e3 / (args.kernel_reps * w.layers)
+
+    nbytes = step_bytes(w, T)
+    total_bytes = nbytes["step"] * w.layers
+    tbps = total_bytes / (step_ms * 1e-3) / 1e12
+    us_layer = step_ms * 1e3 / w.layers
+    dec_gbs = nbytes["decode"] / (dec_us * 1e-6) / 1e9
+    log(f"{us_layer:.2f} us/layer-step, {tbps:.3f} TB/s ({tbps * 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s); "
+        f"decode kernel {dec_us:.2f} us/launch = {dec_gbs:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w)
+        cpu.pop("seconds", None)
+
+    result = {
+        "metric": "INT8-KV decode attention: us/layer-step and achieved HBM TB/s (% of peak)",
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "us_per_layer_step": round(us_layer, 3),
+        "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {w.batch}, {w.num_heads} q / {w.num_kv_heads} kv heads, "
+                               f"head_dim {w.head_dim}, context {T}, "
+                               f"{'per-token' if w.group == 0 else 'group-32'} fp32 scales, {w.layers} layers, "
+                               "append 1 token + decode per layer",
+                   "batch": w.batch, "seq_len": T, "layers": w.layers, "bytes_per_step": total_bytes},
+        "roofline": {"bound": "hbm", "kernel": "kvq_attention_decode",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": nbytes["decode"], "us_per_launch": round(dec_us, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

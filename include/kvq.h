@@ -120,8 +120,11 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k_new, const void* v_n
  *               clamped to [0, min(hint, capacity)]; a length of 0 gives zeros)
  *   out       : device bf16 [B, H, D]
  *   workspace : device scratch of at least kvq_workspace_size(cache,
- *               max_seq_len_hint, 1) bytes (split partials); may be NULL when
- *               that size is 0.  Contents need no initialisation.
+ *               max_seq_len_hint, 1) bytes: split counters followed by split
+ *               partials.  Zero-fill it once after allocation; every call
+ *               returns the counters to zero, so it can be reused by later
+ *               calls on the same stream.  Calls that overlap in time (other
+ *               streams) must not share a workspace.
  * Errors: INVALID_ARG, OUT_OF_RANGE (hint beyond capacity or < 1),
  * WORKSPACE, UNSUPPORTED (head_dim not in {32, 64, 128, 256}), HIP.
  */

@@ -64,8 +64,10 @@ class Int8KVCache:
         _k.kvq_append(self.desc, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
 
     def workspace(self, max_seq_len: int, n_query: int = 1) -> torch.Tensor:
+        """Zero-filled scratch for the attention calls (the split counters at
+        its start must be zero before the first call; calls leave them zero)."""
         n = _k.kvq_workspace_size(self.desc, max_seq_len, n_query)
-        return torch.empty(max(n, 1), dtype=torch.uint8, device=self.k_codes.device)
+        return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.k_codes.device)
 
     def decode(self, q: torch.Tensor, seq_lens: torch.Tensor, attn_scale: float, max_seq_len_hint: int,
                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):

@@ -5,30 +5,48 @@
 // head h of KV group g = h / (H/KVH):
 //     S_t = scale * sum_d q_d (cK_td - 128) sK_t(d)
 //     o   = sum_t softmax(S)_t (cV_td - 128) sV_t(d)
-// Design for gfx950:
-//   * one workgroup per (sequence, KV head, token split): its 4 waves stream
-//     the split's K and V rows once with 16-byte loads, and every byte feeds
-//     all query heads of the GQA group handled by the workgroup;
-//   * a token row of D bytes is spread over D/16 lanes; codes become floats
-//     in registers; the -128 offset is folded out of the inner loop
-//     (sum q (c-128) = sum q c - 128 sum q) and per-row scales multiply the
-//     partial dot, so no dequantized tile is ever materialised;
-//   * softmax is online per lane with a lazy rescale (only when a score
-//     exceeds the running max by more than 2^8 in probability);
-//   * each split writes (m, l, o) partials; a second kernel merges splits
-//     with the log-sum-exp identity and rounds to bf16.
+//
+// gfx950 design of the streaming kernel (head_dim 32, 64, 128):
+//   * one workgroup = (sequence, KV head, token split); its 4 waves take
+//     64-token blocks in turn.  A token row of D code bytes is read by D/16
+//     lanes with one 16-byte load each, and every loaded byte serves all the
+//     query heads of the GQA group (one K/V read per group).
+//   * codes are never widened to fp32: v_perm_b32 places two code bytes into
+//     the low bytes of two f16 halves (the f16 values c * 2^-24, exact) and
+//     v_dot2_f32_f16 multiplies them with f16 queries (QK: pairs along D) or
+//     f16 softmax weights (PV: pairs of tokens), accumulating in fp32.  The
+//     -128 offset is folded out: sum x (c - 128) = sum x c - 128 sum x.
+//     Queries are scaled by a power of two into [2^14, 2^15) first, which is
+//     exact for bf16 inputs.
+//   * the softmax of each token is computed once, by one lane, from partial
+//     dot products exchanged through LDS; per-token V scales are folded into
+//     the exponent (w = 2^(S + log2 sV - m)), so the weights stay in f16
+//     range; the running maximum is wave-uniform and only rescales the
+//     accumulators when a score exceeds it by more than 2^8.
+//   * the next block's K (and V) rows are loaded while the current block is
+//     computed;
+//   * each split leaves (m, l, o) partials; the last workgroup of a (sequence,
+//     KV head) to finish merges them with the log-sum-exp identity and writes
+//     bf16 (a counter in the workspace elects it and is reset for the next
+//     call).
+// head_dim 256 uses the generic kernel below (fp32 FMAs, separate merge).
 #include "kvq_internal.hpp"
 
 #include <cmath>
 #include <cstdlib>
+#include <type_traits>
 
 namespace kvq {
 namespace {
 
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kThreads = kWaves * kWave;
+constexpr int kBlock = 64;         // tokens per wave block (streaming kernel)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;      // log2 headroom before a rescale
+constexpr int kWeightShift = 7;    // weights carry 2^7 so they fill f16 range
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 struct DecodeParams {
   const uint8_t* k_codes;
@@ -37,8 +55,9 @@ struct DecodeParams {
   const float* v_scales;
   const uint16_t* q;         // [B, H, D] bf16
   const int32_t* seq_lens;   // [B]
-  float* part_o;             // [B, H, S, D]
-  float* part_ml;            // [B, H, S, 2]
+  int32_t* counters;         // [B, KVH * wg_per_kvh], zero between calls
+  float* part_ml;            // [B, H, S, 2]  (m, l) per split
+  float* part_o;             // [B, H, S, D]  unnormalised outputs
   uint16_t* out;             // [B, H, D] bf16
   CacheGeom geom;
   int32_t num_heads;
@@ -63,8 +82,547 @@ __device__ __forceinline__ float byte_f32(uint32_t w, int e) {
   return static_cast<float>((w >> (8 * e)) & 0xffu);  // v_cvt_f32_ubyteN
 }
 
-template <int D, int HPW, bool G32>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+
+__device__ __forceinline__ float f16_value(uint32_t bits) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+}
+
+// Maximum over aligned groups of N consecutive lanes (N in {1,2,4,8,16}).
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (N >= 2) x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return x;
+}
+
+// {x_i, x_(i^32)} and {x_i, x_(i^16)} for every lane i, without LDS
+// (v_permlane32_swap / v_permlane16_swap on the same register).
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  float a, b;
+  x = group_max<16>(x);
+  swap16(x, a, b);
+  x = fmaxf(a, b);
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  float a, b;
+  x = group_sum<16>(x);
+  swap16(x, a, b);
+  x = a + b;
+  swap32(x, a, b);
+  return a + b;
+}
+
+// Sum over the lanes that share (lane % LPT): the token slots of a wave.
+template <int LPT>
+__device__ __forceinline__ float slot_sum(float x) {
+  float a, b;
+  if constexpr (LPT <= 1) x += dpp_f32<0x121>(x);  // row_ror:1
+  if constexpr (LPT <= 2) x += dpp_f32<0x122>(x);  // row_ror:2
+  if constexpr (LPT <= 4) x += dpp_f32<0x124>(x);  // row_ror:4
+  if constexpr (LPT <= 8) x += dpp_f32<0x128>(x);  // row_ror:8
+  if constexpr (LPT <= 16) {
+    swap16(x, a, b);
+    x = a + b;
+  }
+  swap32(x, a, b);
+  return a + b;
+}
+
+// Value of lane (i + N) for lanes whose partner lies in the same 32-lane half.
+template <int N>
+__device__ __forceinline__ uint32_t lane_up(uint32_t x) {
+  if constexpr (N < 16) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x100 + N, 0xF, 0xF, false));
+  } else {
+    static_assert(N == 16, "partner distance");
+    return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+  }
+}
+
+// A value every lane holds equally, moved to a scalar register.
+__device__ __forceinline__ float uniform(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Orders this wave's LDS writes before its following LDS reads (lanes of one
+// wave exchange data through LDS; no other wave takes part).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
+  int L = p.seq_lens[b];
+  return L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+}
+
+// ---------------------------------------------------------------------------
+// Final output of HPW heads from the workgroup's own combined partial, or,
+// when several splits exist, by the last workgroup to arrive.  `acc` / `msum`
+// hold, for this thread's (head j, dim d) pairs, the workgroup's combined
+// unnormalised output and (m, l).
+// ---------------------------------------------------------------------------
+template <int D, int HPW>
+__device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int split, int ns,
+                             const float (*sm_o)[D], const float (*sm_ml)[2]) {
+  const int H = p.num_heads;
+  __shared__ int sm_last;
+  if (ns == 1) {
+    for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+      const int j = idx / D, d = idx % D;
+      const float l = sm_ml[j][1];
+      const float v = l > 0.0f ? sm_o[j][d] / l : 0.0f;
+      p.out[(static_cast<int64_t>(b) * H + h0 + j) * D + d] = f32_to_bf16_rne(v);
+    }
+    return;
+  }
+  // Partials go out as agent-scope stores, which bypass the per-XCD L2, so the
+  // workgroup that merges them (possibly on another XCD) reads them back with
+  // agent-scope loads; no L2 write-back or invalidate is needed.
+  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+    const int j = idx / D, d = idx % D;
+    const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + split;
+    __hip_atomic_store(&p.part_o[pidx * D + d], sm_o[j][d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(&p.part_ml[pidx * 2], sm_ml[j][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.part_ml[pidx * 2 + 1], sm_ml[j][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // every wave's stores have completed before the split is counted
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* cnt = p.counters + static_cast<int64_t>(b) * gridDim.y + hg;
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = old == ns - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all splits counted
+    sm_last = last;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+    const int j = idx / D, d = idx % D;
+    const int64_t base = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits;
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s)
+      M = fmaxf(M, __hip_atomic_load(&p.part_ml[(base + s) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    float num = 0.0f, den = 0.0f;
+    for (int s = 0; s < ns; ++s) {
+      const float ms = __hip_atomic_load(&p.part_ml[(base + s) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (ms == -INFINITY) continue;
+      const float f = exp2f(ms - M);
+      den = fmaf(__hip_atomic_load(&p.part_ml[(base + s) * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), f,
+                 den);
+      num = fmaf(__hip_atomic_load(&p.part_o[(base + s) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), f,
+                 num);
+    }
+    const float v = den > 0.0f ? num / den : 0.0f;
+    p.out[(static_cast<int64_t>(b) * H + h0 + j) * D + d] = f32_to_bf16_rne(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel (head_dim 32, 64, 128).
+// ---------------------------------------------------------------------------
+template <int D, int HPW, bool G32, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams p) {
+  // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
+  // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
+  // so a lane accumulates 8 output dims per head.
+  constexpr int LK = D / 16, TK = kWave / LK, NPK = kBlock / TK;
+  constexpr int LV = D / 8, TV = kWave / LV, NPV = kBlock / TV;
+  constexpr int NPAIR = NPV / 2;             // token pairs per lane per block
+  constexpr int NG = G32 ? D / 32 : 1;       // scales per row
+  static_assert(NPV % 2 == 0 && LV <= 16, "block shape");
+  static_assert(HPW >= 1 && HPW <= 4, "at most four heads per workgroup");
+
+  __shared__ float4 sm_part[kWaves][kBlock * LK];    // partial scores [token][k-lane] x 4 heads
+  __shared__ uint4 sm_w[kWaves][NPAIR * TV * NG];    // f16 weight pairs [pair][slot][group] x 4 heads
+  __shared__ float sm_fo[kWaves][HPW][D];            // per-wave outputs
+  __shared__ float sm_fml[kWaves][HPW][2];           // per-wave (m, l)
+  __shared__ float sm_o[HPW][D];                     // workgroup outputs
+  __shared__ float sm_ml[HPW][2];
+
+  const int split = blockIdx.x;
+  const int hg = blockIdx.y;
+  const int b = blockIdx.z;
+  const int H = p.num_heads;
+  const int kvh = hg / p.wg_per_kvh;
+  const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
+  const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
+
+  const int L = clamp_len(p, b);
+  const int t_begin = split * p.split_len;
+  if (L == 0 && split == 0) {  // empty window: the output is zero
+    for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads)
+      p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
+  }
+  if (t_begin >= L) return;  // this split has no tokens (and is not counted)
+  const int t_end = min(L, t_begin + p.split_len);
+  const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
+  const int ns = (L + p.split_len - 1) / p.split_len;
+
+  // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
+  uint32_t qp[HPW][8];
+  float fold[HPW];      // group-32: 128 * 2^-24 * (sum of this lane's scaled queries)
+  float fold_row[HPW];  // per-token: the same over the whole row (wave-uniform)
+  float cst[HPW];       // scale_log2 * 2^24 * 2^-kq (wave-uniform)
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    float qf[16];
+    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
+    bf16x8_to_f32(qptr[0], &qf[0]);
+    bf16x8_to_f32(qptr[1], &qf[8]);
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(qf[e]));
+    a = group_max<LK>(a);
+    const int kq = a > 0.0f ? 14 - ilogbf(a) : 0;
+    float qs = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b0 = f16_bits(ldexpf(qf[2 * k], kq)), b1 = f16_bits(ldexpf(qf[2 * k + 1], kq));
+      qs += f16_value(b0) + f16_value(b1);
+      qp[j][k] = b0 | (b1 << 16);
+    }
+    fold[j] = qs * (128.0f * 0x1p-24f);
+    fold_row[j] = uniform(group_sum<LK>(fold[j]));
+    cst[j] = uniform(ldexpf(p.scale_log2, 24 - kq));
+  }
+
+  // ---- state -------------------------------------------------------------------
+  float o[HPW][8];
+  float m[HPW], l[HPW], ws[HPW][NG];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) ws[j][g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = 0.0f;
+  }
+
+  uint4 kb[NPK];
+  uint2 vb[NPV];
+  float ksc[NPK];       // group-32: this lane's K group scale per pass
+  float s_k;            // per-token mode: K scale of this lane's softmax token
+  float s_v[NG];        // V scales of this lane's softmax token
+  const int kgroup = G32 ? ksub / 2 : 0;
+  const int vgroup = G32 ? vsub / 4 : 0;
+  const int64_t seq_row0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.geom.max_len;
+  const uint32_t koff = static_cast<uint32_t>(kslot * D + ksub * 16);   // lane's byte offset in a K pass
+  const uint32_t voff = static_cast<uint32_t>(vslot * D + vsub * 8);    // lane's byte offset in a V pass
+
+  // ---- loads --------------------------------------------------------------------
+  // A block whose 64 tokens all lie before t_end takes the fast path: the rows of
+  // one pass are consecutive (contiguous layout) or lie in one 16-token page
+  // (paged layout, page ids read once per block as scalars), so a load is a
+  // uniform base plus a per-lane constant.  The last, partial block clamps every
+  // row into [t_begin, t_end) instead; its extra tokens are discarded through
+  // their -inf score and zero weight.  No load sits under a per-lane branch.
+  constexpr bool kPassInPage = TK <= kPageSize && TV <= kPageSize;
+  auto page_row0 = [&](int s0, int tok) -> int64_t {   // row of token s0+tok's page slot 0 (uniform)
+    int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + ((s0 + tok) >> 4)];
+    phys = min(max(phys, 0), p.geom.num_pages - 1);
+    return (static_cast<int64_t>(phys) * p.geom.kvh + kvh) * kPageSize;
+  };
+  auto row_of = [&](int t) -> int64_t {                  // clamped per-lane row
+    t = min(t, t_end - 1);
+    if constexpr (PAGED) {
+      int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (t >> 4)];
+      phys = min(max(phys, 0), p.geom.num_pages - 1);
+      return (static_cast<int64_t>(phys) * p.geom.kvh + kvh) * kPageSize + (t & (kPageSize - 1));
+    } else {
+      return seq_row0 + t;
+    }
+  };
+  auto load_scales = [&](int64_t srow) {
+    if constexpr (G32) {
+      if constexpr (NG == 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(p.v_scales + srow * NG);
+        s_v[0] = v4.x; s_v[1] = v4.y; s_v[2] = v4.z; s_v[3] = v4.w;
+      } else {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) s_v[g] = p.v_scales[srow * NG + g];
+      }
+    } else {
+      s_k = p.k_scales[srow];
+      s_v[0] = p.v_scales[srow];
+    }
+  };
+  auto load_k = [&](int bi) {
+    const int s0 = t_begin + bi * kBlock;
+    if (s0 + kBlock <= t_end && (!PAGED || kPassInPage)) {
+      if constexpr (PAGED) {
+        int64_t r0[kBlock / kPageSize];
+#pragma unroll
+        for (int pg = 0; pg < kBlock / kPageSize; ++pg) r0[pg] = page_row0(s0, pg * kPageSize);
+#pragma unroll
+        for (int i = 0; i < NPK; ++i) {
+          const int tok = i * TK;                          // first token of the pass
+          const uint8_t* base = p.k_codes + (r0[tok >> 4] + (tok & 15)) * D;
+          kb[i] = *reinterpret_cast<const uint4*>(base + koff);
+          if constexpr (G32) ksc[i] = p.k_scales[(r0[tok >> 4] + (tok & 15) + kslot) * NG + kgroup];
+        }
+        int64_t srow = r0[0];
+#pragma unroll
+        for (int pg = 1; pg < kBlock / kPageSize; ++pg) srow = (lane >> 4) == pg ? r0[pg] : srow;
+        load_scales(srow + (lane & 15));
+      } else {
+        const int64_t r = seq_row0 + s0;
+        const uint8_t* base = p.k_codes + r * D;
+#pragma unroll
+        for (int i = 0; i < NPK; ++i) {
+          kb[i] = *reinterpret_cast<const uint4*>(base + i * TK * D + koff);
+          if constexpr (G32) ksc[i] = p.k_scales[(r + i * TK + kslot) * NG + kgroup];
+        }
+        load_scales(r + lane);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPK; ++i) {
+        const int64_t row = row_of(s0 + i * TK + kslot);
+        kb[i] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + ksub * 16);
+        if constexpr (G32) ksc[i] = p.k_scales[row * NG + kgroup];
+      }
+      load_scales(row_of(s0 + lane));
+    }
+  };
+  auto load_v = [&](int bi) {
+    const int s0 = t_begin + bi * kBlock;
+    if (s0 + kBlock <= t_end && (!PAGED || kPassInPage)) {
+      if constexpr (PAGED) {
+        int64_t r0[kBlock / kPageSize];
+#pragma unroll
+        for (int pg = 0; pg < kBlock / kPageSize; ++pg) r0[pg] = page_row0(s0, pg * kPageSize);
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+          const int tok = i * TV;
+          const uint8_t* base = p.v_codes + (r0[tok >> 4] + (tok & 15)) * D;
+          vb[i] = *reinterpret_cast<const uint2*>(base + voff);
+        }
+      } else {
+        const uint8_t* base = p.v_codes + (seq_row0 + s0) * D;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) vb[i] = *reinterpret_cast<const uint2*>(base + i * TV * D + voff);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int64_t row = row_of(s0 + i * TV + vslot);
+        vb[i] = *reinterpret_cast<const uint2*>(p.v_codes + row * D + vsub * 8);
+      }
+    }
+  };
+
+  // ---- one 64-token block; PREFETCH issues the next block's loads early ----------
+  auto run_block = [&](int blk, auto prefetch) {
+    constexpr bool PREFETCH = decltype(prefetch)::value;
+    // QK: partial dots of this lane's 16 dims, all heads
+#pragma unroll
+    for (int i = 0; i < NPK; ++i) {
+      const uint32_t kw[4] = {kb[i].x, kb[i].y, kb[i].z, kb[i].w};
+      float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w4 = 0; w4 < 4; ++w4) {
+        const uint32_t c01 = __builtin_amdgcn_perm(0u, kw[w4], 0x0C010C00u);
+        const uint32_t c23 = __builtin_amdgcn_perm(0u, kw[w4], 0x0C030C02u);
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          P[j] = dot2(qp[j][2 * w4], c01, P[j]);
+          P[j] = dot2(qp[j][2 * w4 + 1], c23, P[j]);
+        }
+      }
+      if constexpr (G32) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) P[j] = (P[j] - fold[j]) * ksc[i];
+      }
+      sm_part[wave][(i * TK + kslot) * LK + ksub] = make_float4(P[0], P[1], P[2], P[3]);
+    }
+    const float sk_cur = G32 ? 0.0f : s_k;
+    float sv_cur[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) sv_cur[g] = s_v[g];
+    if constexpr (PREFETCH) load_k(blk + kWaves);
+    wave_lds_sync();
+
+    // softmax: this lane owns token `lane` of the block
+    const int t = t_begin + blk * kBlock + lane;
+    const bool valid = t < t_end;
+    float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < LK; ++r) {
+      const float4 v = sm_part[wave][lane * LK + ((r + lane) & (LK - 1))];
+      S[0] += v.x; S[1] += v.y; S[2] += v.z; S[3] += v.w;
+    }
+    float lsv[NG];
+    float lsv_max = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      lsv[g] = __log2f(sv_cur[g]);
+      lsv_max = fmaxf(lsv_max, lsv[g]);
+    }
+    float Sh[HPW];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      // per-token scales fold the offset once for the whole row, then scale
+      const float dotv = G32 ? S[j] : (S[j] - fold_row[j]) * sk_cur;
+      Sh[j] = valid ? dotv * cst[j] : -INFINITY;
+    }
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const float bm = uniform(wave_max(Sh[j] + lsv_max));
+      if (bm > m[j] + kLazy) {  // wave-uniform: raise the running maximum
+        const float alpha = exp2f(m[j] - bm);
+        m[j] = bm;
+        l[j] *= alpha;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) ws[j][g] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[j][e] *= alpha;
+      }
+    }
+    uint32_t wbits[HPW][NG];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      l[j] += valid ? exp2f(Sh[j] - m[j]) : 0.0f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float wv = valid ? exp2f(Sh[j] + lsv[g] - m[j] + static_cast<float>(kWeightShift)) : 0.0f;
+        wbits[j][g] = f16_bits(wv);
+        ws[j][g] += f16_value(wbits[j][g]);
+      }
+    }
+    // token lane = V pass * TV + V slot; pair V passes (2k, 2k+1) of one slot:
+    // the partner token sits TV lanes higher
+    const bool even_pass = ((lane / TV) & 1) == 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) word[j] = wbits[j][g] | (lane_up<TV>(wbits[j][g]) << 16);
+      if (even_pass) {
+        const int pair = (lane / TV) >> 1;
+        sm_w[wave][(pair * TV + lane % TV) * NG + g] = make_uint4(word[0], word[1], word[2], word[3]);
+      }
+    }
+    wave_lds_sync();
+
+    // PV: token pairs, this lane's 8 dims, all heads
+#pragma unroll
+    for (int k = 0; k < NPAIR; ++k) {
+      const uint4 wq = sm_w[wave][(k * TV + vslot) * NG + vgroup];
+      const uint32_t wv[4] = {wq.x, wq.y, wq.z, wq.w};
+      const uint32_t a2[2] = {vb[2 * k].x, vb[2 * k].y};
+      const uint32_t b2[2] = {vb[2 * k + 1].x, vb[2 * k + 1].y};
+#pragma unroll
+      for (int w2 = 0; w2 < 2; ++w2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t cp = __builtin_amdgcn_perm(b2[w2], a2[w2], 0x0C040C00u + 0x00010001u * e);
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) o[j][4 * w2 + e] = dot2(wv[j], cp, o[j][4 * w2 + e]);
+        }
+      }
+    }
+    if constexpr (PREFETCH) load_v(blk + kWaves);
+  };
+
+  // the wave index is uniform, so every block condition below is a scalar branch
+  int blk = wave;
+  if (blk < nblk) {
+    load_k(blk);
+    load_v(blk);
+  }
+  for (; blk + kWaves < nblk; blk += kWaves) run_block(blk, std::true_type{});
+  if (blk < nblk) run_block(blk, std::false_type{});
+
+  // ---- combine the wave: l and weight sums over lanes, o over token slots ------
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    l[j] = wave_sum(l[j]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) ws[j][g] = wave_sum(ws[j][g]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[j][e] = slot_sum<LV>(o[j][e]);
+  }
+  if (vslot == 0) {
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      // U = sum_t 2^(S + log2 sV - m) (c - 128) = 2^-7 (2^24 o - 128 sum w)
+      float wsum = ws[j][0];
+#pragma unroll
+      for (int g = 1; g < NG; ++g) wsum = (g == vgroup) ? ws[j][g] : wsum;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sm_fo[wave][j][vsub * 8 + e] = o[j][e] * 0x1p17f - wsum * (128.0f * 0x1p-7f);
+      if (vsub == 0) {
+        sm_fml[wave][j][0] = m[j];
+        sm_fml[wave][j][1] = l[j];
+      }
+    }
+  }
+  __syncthreads();
+  // ---- combine the four waves -----------------------------------------------------
+  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+    const int j = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_fml[w][j][0]);
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_fml[w][j][0];
+      if (mw == -INFINITY) continue;
+      const float f = exp2f(mw - M);
+      acc = fmaf(sm_fo[w][j][d], f, acc);
+      lsum = fmaf(sm_fml[w][j][1], f, lsum);
+    }
+    sm_o[j][d] = acc;
+    if (d == 0) {
+      sm_ml[j][0] = M;
+      sm_ml[j][1] = lsum;
+    }
+  }
+  __syncthreads();
+  finish_split<D, HPW>(p, b, h0, hg, split, ns, sm_o, sm_ml);
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernel (any supported head_dim, used for 256): fp32 FMAs on codes
+// widened in registers, per-lane online softmax, partials merged by
+// decode_merge_kernel.
+// ---------------------------------------------------------------------------
+template <int D, int HPW, bool G32, bool PAGED>
+__global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p) {
   constexpr int LPT = D / 16;          // lanes per token row (16 bytes each)
   constexpr int TPW = kWave / LPT;     // token rows per wave pass
   constexpr int TPP = TPW * kWaves;    // token rows per workgroup pass
@@ -85,14 +643,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int sub = lane % LPT;
   const int slot = lane / LPT;
 
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+  const int L = clamp_len(p, b);
   const int t_begin = split * p.split_len;
-  if (t_begin >= L) return;  // the merge reads only ceil(L / split_len) splits
+  if (t_begin >= L) return;
   const int t_end = min(L, t_begin + p.split_len);
   const int npass = (t_end - t_begin + TPP - 1) / TPP;
 
-  // Query slice of this lane: 16 consecutive dims per head, as fp32.
   float q[HPW][16];
   float qsum[HPW];
 #pragma unroll
@@ -105,7 +661,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     for (int e = 0; e < 16; ++e) s += q[j][e];
     qsum[j] = s;
   }
-  const int grp = G32 ? (sub * 16) / 32 : 0;  // scale group of this lane's slice
+  const int grp = G32 ? (sub * 16) / 32 : 0;
 
   float m[HPW], l[HPW], ws[HPW], o[HPW][16];
 #pragma unroll
@@ -123,21 +679,23 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // unconditional loads from a clamped row; out-of-range tokens are
+      // discarded through their -inf score
       const int t = t_begin + (ip + u) * TPP + wave * TPW + slot;
-      int64_t row = -1;
-      if (ip + u < npass && t < t_end) row = cache_row(p.geom, b, kvh, t);
-      ok[u] = row >= 0;
-      if (ok[u]) {
-        kb[u] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + sub * 16);
-        vb[u] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + sub * 16);
-        ks[u] = p.k_scales[row * p.groups + grp];
-        vs[u] = p.v_scales[row * p.groups + grp];
+      ok[u] = t < t_end;
+      const int tc = min(t, t_end - 1);
+      int64_t row;
+      if constexpr (PAGED) {
+        int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (tc >> 4)];
+        phys = min(max(phys, 0), p.geom.num_pages - 1);
+        row = (static_cast<int64_t>(phys) * p.geom.kvh + kvh) * kPageSize + (tc & (kPageSize - 1));
       } else {
-        kb[u] = make_uint4(0, 0, 0, 0);
-        vb[u] = make_uint4(0, 0, 0, 0);
-        ks[u] = 0.0f;
-        vs[u] = 0.0f;
+        row = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.geom.max_len + tc;
       }
+      kb[u] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + sub * 16);
+      vb[u] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + sub * 16);
+      ks[u] = p.k_scales[row * p.groups + grp];
+      vs[u] = p.v_scales[row * p.groups + grp];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -147,14 +705,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
       for (int j = 0; j < HPW; ++j) part[j] = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float c = byte_f32(kw[i], e);
 #pragma unroll
           for (int j = 0; j < HPW; ++j) part[j] = fmaf(q[j][4 * i + e], c, part[j]);
         }
-      }
       float cv[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -165,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         float sc = (part[j] - 128.0f * qsum[j]) * ks[u];
         sc = group_sum<LPT>(sc) * p.scale_log2;
         const float sj = ok[u] ? sc : -INFINITY;
-        if (sj > m[j] + kLazy) {  // rare: raise the running max
+        if (sj > m[j] + kLazy) {
           const float alpha = exp2f(m[j] - sj);
           l[j] *= alpha;
           ws[j] *= alpha;
@@ -175,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         }
         const float pj = ok[u] ? exp2f(sj - m[j]) : 0.0f;
         l[j] += pj;
-        const float w = pj * vs[u];
+        const float w = ok[u] ? pj * vs[u] : 0.0f;
         ws[j] += w;
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[j][e] = fmaf(w, cv[e], o[j][e]);
@@ -183,23 +740,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     }
   }
 
-  // Fold the +128 offset back in, then combine the token slots of the wave.
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[j][e] = fmaf(-128.0f, ws[j], o[j][e]);
     float M = m[j];
-#pragma unroll
-    for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, shfl_xor_f32(M, off));
+    for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
     const float f = (m[j] == -INFINITY) ? 0.0f : exp2f(m[j] - M);
     l[j] *= f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[j][e] *= f;
-#pragma unroll
     for (int off = LPT; off < kWave; off <<= 1) {
-      l[j] += shfl_xor_f32(l[j], off);
+      l[j] += __shfl_xor(l[j], off, kWave);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[j][e] += shfl_xor_f32(o[j][e], off);
+      for (int e = 0; e < 16; ++e) o[j][e] += __shfl_xor(o[j][e], off, kWave);
     }
     m[j] = M;
   }
@@ -242,8 +796,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int H = p.num_heads;
-  int L = p.seq_lens[b];
-  L = L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+  const int L = clamp_len(p, b);
   const int ns = (L + p.split_len - 1) / p.split_len;
   const int64_t base = (static_cast<int64_t>(b) * H + h) * p.num_splits;
   float M = -INFINITY;
@@ -270,21 +823,41 @@ int heads_per_wg(int gqa) {
   return 1;
 }
 
-int lanes_per_token(int D) { return D / 16; }
+bool use_stream(int head_dim) { return head_dim <= 128; }
+
+int pass_tokens(int head_dim) {
+  // tokens a workgroup consumes per step: whole 64-token wave blocks for the
+  // streaming kernel, one pass of all waves for the generic kernel
+  return use_stream(head_dim) ? kBlock * kWaves : (kWave / (head_dim / 16)) * kWaves;
+}
+
+template <int D, int HPW, bool G32, bool PAGED>
+void launch_kernel(bool stream_kernel, const DecodeParams& p, dim3 grid, hipStream_t st) {
+  if (stream_kernel) {
+    if constexpr (D <= 128)
+      hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED>), grid, dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((decode_generic_kernel<D, HPW, G32, PAGED>), grid, dim3(kThreads), 0, st, p);
+  }
+}
 
 template <int D, int HPW>
-void launch_split(const DecodeParams& p, bool g32, dim3 grid, hipStream_t st) {
-  if (g32)
-    hipLaunchKernelGGL((decode_split_kernel<D, HPW, true>), grid, dim3(kThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<D, HPW, false>), grid, dim3(kThreads), 0, st, p);
+void launch_modes(bool stream_kernel, bool g32, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
+  if (g32) {
+    if (paged) launch_kernel<D, HPW, true, true>(stream_kernel, p, grid, st);
+    else launch_kernel<D, HPW, true, false>(stream_kernel, p, grid, st);
+  } else {
+    if (paged) launch_kernel<D, HPW, false, true>(stream_kernel, p, grid, st);
+    else launch_kernel<D, HPW, false, false>(stream_kernel, p, grid, st);
+  }
 }
 
 template <int D>
-void launch_split_d(const DecodeParams& p, int hpw, bool g32, dim3 grid, hipStream_t st) {
-  if (hpw == 4) launch_split<D, 4>(p, g32, grid, st);
-  else if (hpw == 2) launch_split<D, 2>(p, g32, grid, st);
-  else launch_split<D, 1>(p, g32, grid, st);
+void launch_d(bool stream_kernel, int hpw, bool g32, bool paged, const DecodeParams& p, dim3 grid,
+              hipStream_t st) {
+  if (hpw == 4) launch_modes<D, 4>(stream_kernel, g32, paged, p, grid, st);
+  else if (hpw == 2) launch_modes<D, 2>(stream_kernel, g32, paged, p, grid, st);
+  else launch_modes<D, 1>(stream_kernel, g32, paged, p, grid, st);
 }
 
 int env_int(const char* name, int dflt) {
@@ -292,6 +865,8 @@ int env_int(const char* name, int dflt) {
   if (!v || !*v) return dflt;
   return std::atoi(v);
 }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
@@ -303,19 +878,22 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   DecodePlan pl;
   const int gqa = c.num_heads / c.num_kv_heads;
   pl.heads_per_wg = heads_per_wg(gqa);
-  const int tpp = (kWave / lanes_per_token(c.head_dim)) * kWaves;
+  const int step = pass_tokens(c.head_dim);
   int split = 512;
   const int forced_splits = env_int("KVQ_NUM_SPLITS", 0);
   const int forced_len = env_int("KVQ_SPLIT_LEN", 0);
   if (forced_splits > 0) split = (max_seq_len + forced_splits - 1) / forced_splits;
   else if (forced_len > 0) split = forced_len;
-  split = ((split + tpp - 1) / tpp) * tpp;
-  if (split < tpp) split = tpp;
+  split = ((split + step - 1) / step) * step;
+  if (split < step) split = step;
   pl.split_len = split;
   pl.num_splits = (max_seq_len + split - 1) / split;
   if (pl.num_splits < 1) pl.num_splits = 1;
-  pl.workspace = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits *
-                 (static_cast<size_t>(c.head_dim) + 2) * sizeof(float);
+  const size_t groups = static_cast<size_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
+  const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
+  pl.counter_bytes = align_up(groups * sizeof(int32_t), 256);
+  pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
+                 partials * static_cast<size_t>(c.head_dim) * sizeof(float);
   return pl;
 }
 
@@ -329,8 +907,11 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   p.v_scales = c.v_scales;
   p.q = q;
   p.seq_lens = seq_lens;
-  p.part_o = static_cast<float*>(ws);
-  p.part_ml = p.part_o + static_cast<size_t>(c.batch) * c.num_heads * plan.num_splits * c.head_dim;
+  const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * plan.num_splits;
+  char* w = static_cast<char*>(ws);
+  p.counters = reinterpret_cast<int32_t*>(w);
+  p.part_ml = reinterpret_cast<float*>(w + plan.counter_bytes);
+  p.part_o = reinterpret_cast<float*>(w + plan.counter_bytes + align_up(partials * 2 * sizeof(float), 256));
   p.out = out;
   p.geom = geom_of(c);
   p.num_heads = c.num_heads;
@@ -346,18 +927,23 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   if (grid.y > 65535 || grid.z > 65535)
     return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_decode: grid too large");
   const bool g32 = c.scale_mode == KVQ_SCALE_GROUP32;
+  const bool stream_kernel = use_stream(c.head_dim);
+  const bool paged = c.layout == KVQ_LAYOUT_PAGED;
   switch (c.head_dim) {
-    case 32: launch_split_d<32>(p, plan.heads_per_wg, g32, grid, stream); break;
-    case 64: launch_split_d<64>(p, plan.heads_per_wg, g32, grid, stream); break;
-    case 128: launch_split_d<128>(p, plan.heads_per_wg, g32, grid, stream); break;
-    default: launch_split_d<256>(p, plan.heads_per_wg, g32, grid, stream); break;
+    case 32: launch_d<32>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    case 64: launch_d<64>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    case 128: launch_d<128>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    default: launch_d<256>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: split launch failed: %s", hipGetErrorString(e));
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(c.num_heads, c.batch), dim3(c.head_dim < 256 ? c.head_dim : 256), 0,
-                     stream, p, c.head_dim);
-  e = hipGetLastError();
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: merge launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: launch failed: %s", hipGetErrorString(e));
+  if (!stream_kernel) {
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(c.num_heads, c.batch), dim3(c.head_dim < 256 ? c.head_dim : 256),
+                       0, stream, p, c.head_dim);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(KVQ_ERR_HIP, "kvq_attention_decode: merge launch failed: %s", hipGetErrorString(e));
+  }
   return KVQ_OK;
 }
 

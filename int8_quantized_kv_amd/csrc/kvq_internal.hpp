@@ -43,7 +43,8 @@ struct DecodePlan {
   int heads_per_wg;   // query heads sharing one K/V read (a divisor of H/KVH)
   int split_len;      // tokens per split (multiple of the kernel's pass size)
   int num_splits;     // splits per sequence for the hinted length
-  size_t workspace;   // bytes of split partials
+  size_t counter_bytes;  // leading bytes of the workspace holding split counters
+  size_t workspace;   // bytes of counters + split partials
 };
 bool decode_supported(int head_dim);
 DecodePlan plan_decode(const kvq_cache& c, int max_seq_len);

@@ -139,9 +139,12 @@ def test_split_count_invariance(kvq, monkeypatch):
         monkeypatch.setenv("KVQ_NUM_SPLITS", str(ns))
         outs.append(orc.bf16_bits_to_f32(_decode(cache, qb, [L, 1234], 0.088, L)).astype(np.float64))
     monkeypatch.delenv("KVQ_NUM_SPLITS")
-    for o in outs[1:]:
-        # equal up to one bf16 rounding step of the fp32 result
-        assert np.all(np.abs(o - outs[0]) <= 2.0 ** -7 * np.abs(outs[0]) + 1e-6)
+    for ns, o in zip((2, 7, 64), outs[1:]):
+        # equal up to one bf16 rounding step of the fp32 result, plus fp32
+        # association noise near zero (100x below the attention tolerance)
+        dev = np.abs(o - outs[0])
+        log(f"  splits={ns}: max |diff| {dev.max():.3e}")
+        assert np.all(dev <= 2.0 ** -7 * np.abs(outs[0]) + 1e-4)
     ref = _oracle_decode(x["k"], x["v"], qv, [L, 1234], 0.088, 0)
     assert_attention_close(to_bits(outs[0]), ref, "split invariance")
 
