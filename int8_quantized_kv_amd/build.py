@@ -18,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -29,6 +30,7 @@ COMMON = [
     "-fPIC",
     "-fvisibility=hidden",
     "-Wall",
+    f"-I{INCLUDE}",
     # fp32 division and sqrt stay IEEE correctly rounded (quantization codes
     # depend on it); no fast-math, no denormal flushing.
     "-fhip-fp32-correctly-rounded-divide-sqrt",

@@ -39,8 +39,11 @@
 namespace kvq {
 namespace {
 
-constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kWaves = 4;          // waves per workgroup (generic kernel)
 constexpr int kThreads = kWaves * kWave;
+constexpr int kStreamWaves = 8;    // waves per workgroup (streaming kernel): 2 per SIMD
+constexpr int kStreamThreads = kStreamWaves * kWave;
+constexpr int kCUs = 256;          // MI355X compute units: the split heuristic aims at one workgroup each
 constexpr int kBlock = 64;         // tokens per wave block (streaming kernel)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;      // log2 headroom before a rescale
@@ -162,6 +165,13 @@ __device__ __forceinline__ uint32_t lane_up(uint32_t x) {
   }
 }
 
+// 2^x with the hardware instruction (results below the normal range flush to
+// zero, which only drops weights that could not change a bf16 output).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// True when the condition holds in any lane of the wave (scalar result).
+__device__ __forceinline__ bool any_lane(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
 // A value every lane holds equally, moved to a scalar register.
 __device__ __forceinline__ float uniform(float x) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -186,13 +196,13 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
 // hold, for this thread's (head j, dim d) pairs, the workgroup's combined
 // unnormalised output and (m, l).
 // ---------------------------------------------------------------------------
-template <int D, int HPW>
+template <int D, int HPW, int NT>
 __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int split, int ns,
                              const float (*sm_o)[D], const float (*sm_ml)[2]) {
   const int H = p.num_heads;
   __shared__ int sm_last;
   if (ns == 1) {
-    for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
       const int j = idx / D, d = idx % D;
       const float l = sm_ml[j][1];
       const float v = l > 0.0f ? sm_o[j][d] / l : 0.0f;
@@ -203,7 +213,7 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
   // Partials go out as agent-scope stores, which bypass the per-XCD L2, so the
   // workgroup that merges them (possibly on another XCD) reads them back with
   // agent-scope loads; no L2 write-back or invalidate is needed.
-  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
     const int j = idx / D, d = idx % D;
     const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + split;
     __hip_atomic_store(&p.part_o[pidx * D + d], sm_o[j][d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -224,23 +234,71 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
   }
   __syncthreads();
   if (!sm_last) return;
-  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
-    const int j = idx / D, d = idx % D;
-    const int64_t base = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-      M = fmaxf(M, __hip_atomic_load(&p.part_ml[(base + s) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-      const float ms = __hip_atomic_load(&p.part_ml[(base + s) * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (ms == -INFINITY) continue;
-      const float f = exp2f(ms - M);
-      den = fmaf(__hip_atomic_load(&p.part_ml[(base + s) * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), f,
-                 den);
-      num = fmaf(__hip_atomic_load(&p.part_o[(base + s) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), f,
-                 num);
+
+  // Merge.  All loads of one round are independent and unconditional
+  // (indices clamped, surplus entries masked), so they are in flight together.
+  constexpr int kChunk = NT / HPW;   // splits whose (m, l) one round stages in LDS
+  constexpr int kItems = (HPW * D + NT - 1) / NT;
+  __shared__ float sm_sm[HPW][kChunk];
+  __shared__ float sm_sl[HPW][kChunk];
+  float run_m[kItems], num[kItems], den[kItems];
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    run_m[it] = -INFINITY;
+    num[it] = 0.0f;
+    den[it] = 0.0f;
+  }
+  for (int c0 = 0; c0 < ns; c0 += kChunk) {
+    const int cnt = min(kChunk, ns - c0);
+    {
+      const int j = threadIdx.x / kChunk, u = threadIdx.x % kChunk;
+      const int sidx = min(c0 + u, ns - 1);
+      const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + sidx;
+      const float mv = __hip_atomic_load(&p.part_ml[pidx * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float lv = __hip_atomic_load(&p.part_ml[pidx * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm_sm[j][u] = u < cnt ? mv : -INFINITY;
+      sm_sl[j][u] = u < cnt ? lv : 0.0f;
     }
-    const float v = den > 0.0f ? num / den : 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int idx = threadIdx.x + it * NT;
+      if (idx >= HPW * D) break;
+      const int j = idx / D, d = idx % D;
+      float cm = -INFINITY;
+      for (int u = 0; u < cnt; ++u) cm = fmaxf(cm, sm_sm[j][u]);
+      const float newm = fmaxf(run_m[it], cm);
+      if (newm == -INFINITY) continue;
+      const float f_old = run_m[it] == -INFINITY ? 0.0f : exp2f(run_m[it] - newm);
+      num[it] *= f_old;
+      den[it] *= f_old;
+      run_m[it] = newm;
+      const int64_t base = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + c0;
+      for (int u0 = 0; u0 < cnt; u0 += 8) {
+        float ov[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int uu = min(u0 + u, cnt - 1);
+          ov[u] = __hip_atomic_load(&p.part_o[(base + uu) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int uu = u0 + u;
+          const float ms = uu < cnt ? sm_sm[j][uu] : -INFINITY;
+          const float f = ms == -INFINITY ? 0.0f : exp2f(ms - newm);
+          num[it] = fmaf(ov[u], f, num[it]);
+          den[it] = fmaf(uu < cnt ? sm_sl[j][uu] : 0.0f, f, den[it]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int idx = threadIdx.x + it * NT;
+    if (idx >= HPW * D) break;
+    const int j = idx / D, d = idx % D;
+    const float v = den[it] > 0.0f ? num[it] / den[it] : 0.0f;
     p.out[(static_cast<int64_t>(b) * H + h0 + j) * D + d] = f32_to_bf16_rne(v);
   }
 }
@@ -249,7 +307,7 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
 // Streaming kernel (head_dim 32, 64, 128).
 // ---------------------------------------------------------------------------
 template <int D, int HPW, bool G32, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(DecodeParams p) {
   // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
   // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
   // so a lane accumulates 8 output dims per head.
@@ -257,13 +315,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
   constexpr int LV = D / 8, TV = kWave / LV, NPV = kBlock / TV;
   constexpr int NPAIR = NPV / 2;             // token pairs per lane per block
   constexpr int NG = G32 ? D / 32 : 1;       // scales per row
+  constexpr int kSwz = 16 / LK;              // partial-score swizzle
   static_assert(NPV % 2 == 0 && LV <= 16, "block shape");
   static_assert(HPW >= 1 && HPW <= 4, "at most four heads per workgroup");
 
-  __shared__ float4 sm_part[kWaves][kBlock * LK];    // partial scores [token][k-lane] x 4 heads
-  __shared__ uint4 sm_w[kWaves][NPAIR * TV * NG];    // f16 weight pairs [pair][slot][group] x 4 heads
-  __shared__ float sm_fo[kWaves][HPW][D];            // per-wave outputs
-  __shared__ float sm_fml[kWaves][HPW][2];           // per-wave (m, l)
+  // partial scores, [k-lane][token ^ (k-lane * 16/LK)] x 4 heads: the writes of
+  // one pass and the reads of one k-lane both touch distinct banks
+  __shared__ float4 sm_part[kStreamWaves][kBlock * LK];
+  __shared__ uint4 sm_w[kStreamWaves][NPAIR * TV * NG];    // f16 weight pairs [pair][slot][group] x 4 heads
+  __shared__ float sm_fo[kStreamWaves][HPW][D];            // per-wave outputs
+  __shared__ float sm_fml[kStreamWaves][HPW][2];           // per-wave (m, l)
   __shared__ float sm_o[HPW][D];                     // workgroup outputs
   __shared__ float sm_ml[HPW][2];
 
@@ -278,44 +339,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
   const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
 
-  const int L = clamp_len(p, b);
   const int t_begin = split * p.split_len;
-  if (L == 0 && split == 0) {  // empty window: the output is zero
-    for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads)
-      p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
-  }
-  if (t_begin >= L) return;  // this split has no tokens (and is not counted)
-  const int t_end = min(L, t_begin + p.split_len);
-  const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
-  const int ns = (L + p.split_len - 1) / p.split_len;
+  // Until seq_lens[b] arrives, t_end is only bounded by the launch: the first
+  // block's loads go out against that bound (rows past the real end are valid
+  // memory and are masked later), overlapping the length and query loads.
+  int t_end = min(p.len_cap, t_begin + p.split_len);
 
-  // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
   uint32_t qp[HPW][8];
   float fold[HPW];      // group-32: 128 * 2^-24 * (sum of this lane's scaled queries)
   float fold_row[HPW];  // per-token: the same over the whole row (wave-uniform)
   float cst[HPW];       // scale_log2 * 2^24 * 2^-kq (wave-uniform)
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    float qf[16];
-    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
-    bf16x8_to_f32(qptr[0], &qf[0]);
-    bf16x8_to_f32(qptr[1], &qf[8]);
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(qf[e]));
-    a = group_max<LK>(a);
-    const int kq = a > 0.0f ? 14 - ilogbf(a) : 0;
-    float qs = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t b0 = f16_bits(ldexpf(qf[2 * k], kq)), b1 = f16_bits(ldexpf(qf[2 * k + 1], kq));
-      qs += f16_value(b0) + f16_value(b1);
-      qp[j][k] = b0 | (b1 << 16);
-    }
-    fold[j] = qs * (128.0f * 0x1p-24f);
-    fold_row[j] = uniform(group_sum<LK>(fold[j]));
-    cst[j] = uniform(ldexpf(p.scale_log2, 24 - kq));
-  }
 
   // ---- state -------------------------------------------------------------------
   float o[HPW][8];
@@ -465,24 +498,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
 #pragma unroll
         for (int j = 0; j < HPW; ++j) P[j] = (P[j] - fold[j]) * ksc[i];
       }
-      sm_part[wave][(i * TK + kslot) * LK + ksub] = make_float4(P[0], P[1], P[2], P[3]);
+      sm_part[wave][ksub * kBlock + ((i * TK + kslot) ^ (ksub * kSwz))] = make_float4(P[0], P[1], P[2], P[3]);
     }
     const float sk_cur = G32 ? 0.0f : s_k;
     float sv_cur[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) sv_cur[g] = s_v[g];
-    if constexpr (PREFETCH) load_k(blk + kWaves);
+    if constexpr (PREFETCH) load_k(blk + kStreamWaves);
     wave_lds_sync();
 
     // softmax: this lane owns token `lane` of the block
     const int t = t_begin + blk * kBlock + lane;
     const bool valid = t < t_end;
-    float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float4 acc4 = sm_part[wave][lane ^ 0];
 #pragma unroll
-    for (int r = 0; r < LK; ++r) {
-      const float4 v = sm_part[wave][lane * LK + ((r + lane) & (LK - 1))];
-      S[0] += v.x; S[1] += v.y; S[2] += v.z; S[3] += v.w;
+    for (int r = 1; r < LK; ++r) {
+      const float4 v = sm_part[wave][r * kBlock + (lane ^ (r * kSwz))];
+      acc4.x += v.x; acc4.y += v.y; acc4.z += v.z; acc4.w += v.w;
     }
+    const float S[4] = {acc4.x, acc4.y, acc4.z, acc4.w};
     float lsv[NG];
     float lsv_max = -INFINITY;
 #pragma unroll
@@ -499,9 +533,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
     }
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      const float bm = uniform(wave_max(Sh[j] + lsv_max));
-      if (bm > m[j] + kLazy) {  // wave-uniform: raise the running maximum
-        const float alpha = exp2f(m[j] - bm);
+      // raise the (wave-uniform) reference only when some score exceeds it by
+      // more than 2^8; the exact block maximum is needed only then
+      if (any_lane(Sh[j] + lsv_max > m[j] + kLazy)) {
+        const float bm = uniform(wave_max(Sh[j] + lsv_max));
+        const float alpha = fast_exp2(m[j] - bm);
         m[j] = bm;
         l[j] *= alpha;
 #pragma unroll
@@ -513,11 +549,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
     uint32_t wbits[HPW][NG];
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      l[j] += valid ? exp2f(Sh[j] - m[j]) : 0.0f;
+      l[j] += fast_exp2(Sh[j] - m[j]);  // -inf score: exactly 0
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float wv = valid ? exp2f(Sh[j] + lsv[g] - m[j] + static_cast<float>(kWeightShift)) : 0.0f;
-        wbits[j][g] = f16_bits(wv);
+        wbits[j][g] = f16_bits(fast_exp2(Sh[j] + lsv[g] - m[j] + static_cast<float>(kWeightShift)));
         ws[j][g] += f16_value(wbits[j][g]);
       }
     }
@@ -553,16 +588,50 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
         }
       }
     }
-    if constexpr (PREFETCH) load_v(blk + kWaves);
+    if constexpr (PREFETCH) load_v(blk + kStreamWaves);
   };
 
   // the wave index is uniform, so every block condition below is a scalar branch
   int blk = wave;
-  if (blk < nblk) {
+  if (t_begin + blk * kBlock < t_end) {  // speculative first block
     load_k(blk);
     load_v(blk);
   }
-  for (; blk + kWaves < nblk; blk += kWaves) run_block(blk, std::true_type{});
+  const int L = clamp_len(p, b);
+  if (L == 0 && split == 0) {  // empty window: the output is zero
+    for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads)
+      p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
+  }
+  if (t_begin >= L) return;  // this split has no tokens (and is not counted)
+  t_end = min(L, t_begin + p.split_len);
+  const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
+  const int ns = (L + p.split_len - 1) / p.split_len;
+
+  // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    float qf[16];
+    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
+    bf16x8_to_f32(qptr[0], &qf[0]);
+    bf16x8_to_f32(qptr[1], &qf[8]);
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(qf[e]));
+    a = group_max<LK>(a);
+    const int kq = a > 0.0f ? 14 - ilogbf(a) : 0;
+    float qs = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b0 = f16_bits(ldexpf(qf[2 * k], kq)), b1 = f16_bits(ldexpf(qf[2 * k + 1], kq));
+      qs += f16_value(b0) + f16_value(b1);
+      qp[j][k] = b0 | (b1 << 16);
+    }
+    fold[j] = qs * (128.0f * 0x1p-24f);
+    fold_row[j] = uniform(group_sum<LK>(fold[j]));
+    cst[j] = uniform(ldexpf(p.scale_log2, 24 - kq));
+  }
+
+  for (; blk + kStreamWaves < nblk; blk += kStreamWaves) run_block(blk, std::true_type{});
   if (blk < nblk) run_block(blk, std::false_type{});
 
   // ---- combine the wave: l and weight sums over lanes, o over token slots ------
@@ -592,14 +661,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
   }
   __syncthreads();
   // ---- combine the four waves -----------------------------------------------------
-  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads) {
     const int j = idx / D, d = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_fml[w][j][0]);
+    for (int w = 0; w < kStreamWaves; ++w) M = fmaxf(M, sm_fml[w][j][0]);
     float acc = 0.0f, lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kStreamWaves; ++w) {
       const float mw = sm_fml[w][j][0];
       if (mw == -INFINITY) continue;
       const float f = exp2f(mw - M);
@@ -613,7 +682,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_stream_kernel(DecodeParams
     }
   }
   __syncthreads();
-  finish_split<D, HPW>(p, b, h0, hg, split, ns, sm_o, sm_ml);
+  finish_split<D, HPW, kStreamThreads>(p, b, h0, hg, split, ns, sm_o, sm_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -828,14 +897,14 @@ bool use_stream(int head_dim) { return head_dim <= 128; }
 int pass_tokens(int head_dim) {
   // tokens a workgroup consumes per step: whole 64-token wave blocks for the
   // streaming kernel, one pass of all waves for the generic kernel
-  return use_stream(head_dim) ? kBlock * kWaves : (kWave / (head_dim / 16)) * kWaves;
+  return use_stream(head_dim) ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
 }
 
 template <int D, int HPW, bool G32, bool PAGED>
 void launch_kernel(bool stream_kernel, const DecodeParams& p, dim3 grid, hipStream_t st) {
   if (stream_kernel) {
     if constexpr (D <= 128)
-      hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED>), grid, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED>), grid, dim3(kStreamThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL((decode_generic_kernel<D, HPW, G32, PAGED>), grid, dim3(kThreads), 0, st, p);
   }
@@ -879,7 +948,12 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   const int gqa = c.num_heads / c.num_kv_heads;
   pl.heads_per_wg = heads_per_wg(gqa);
   const int step = pass_tokens(c.head_dim);
-  int split = 512;
+  // Aim at about one workgroup per compute unit, in whole workgroup passes,
+  // at most 2048 tokens per split so that ragged batches stay balanced.
+  const int64_t groups = static_cast<int64_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
+  int64_t want = (static_cast<int64_t>(max_seq_len) * groups + kCUs - 1) / kCUs;
+  want = want < 512 ? 512 : (want > 2048 ? 2048 : want);
+  int split = static_cast<int>(want);
   const int forced_splits = env_int("KVQ_NUM_SPLITS", 0);
   const int forced_len = env_int("KVQ_SPLIT_LEN", 0);
   if (forced_splits > 0) split = (max_seq_len + forced_splits - 1) / forced_splits;
@@ -889,9 +963,8 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   pl.split_len = split;
   pl.num_splits = (max_seq_len + split - 1) / split;
   if (pl.num_splits < 1) pl.num_splits = 1;
-  const size_t groups = static_cast<size_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
-  pl.counter_bytes = align_up(groups * sizeof(int32_t), 256);
+  pl.counter_bytes = align_up(static_cast<size_t>(groups) * sizeof(int32_t), 256);
   pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
                  partials * static_cast<size_t>(c.head_dim) * sizeof(float);
   return pl;
