@@ -172,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
     ap.add_argument("--kernel-reps", type=int, default=10,
                     help="passes over all layers when timing the decode kernel alone")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
@@ -214,15 +216,24 @@ def main():
     seq_lens = torch.full((w.batch,), T, dtype=torch.int32, device=dev)
     ws = layers[0]["cache"].workspace(T, 1)
 
-    def step():
-        for ly in layers:
-            c = ly["cache"]
-            c.append(ly["k_new"], ly["v_new"], start_pos, stream=stream)
-            c.decode(ly["q"], seq_lens, w.attn_scale, T, out=ly["out"], workspace=ws, stream=stream)
+    if args.separate:
+        def step():
+            for ly in layers:
+                c = ly["cache"]
+                c.append(ly["k_new"], ly["v_new"], start_pos, stream=stream)
+                c.decode(ly["q"], seq_lens, w.attn_scale, T, out=ly["out"], workspace=ws, stream=stream)
 
-    def decode_only():
-        for ly in layers:
-            ly["cache"].decode(ly["q"], seq_lens, w.attn_scale, T, out=ly["out"], workspace=ws, stream=stream)
+        def kernel_pass():  # the dominant kernel alone: decode attention
+            for ly in layers:
+                ly["cache"].decode(ly["q"], seq_lens, w.attn_scale, T, out=ly["out"], workspace=ws, stream=stream)
+        kernel_name, kernel_bytes = "kvq_attention_decode", "decode"
+    else:
+        def step():  # one launch per layer: quantize-append at position 4095, then decode over 4096
+            for ly in layers:
+                ly["cache"].append_decode(ly["k_new"], ly["v_new"], ly["q"], seq_lens, w.attn_scale, T,
+                                          out=ly["out"], workspace=ws, stream=stream)
+        kernel_pass = step
+        kernel_name, kernel_bytes = "kvq_append_decode", "step"
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -243,12 +254,12 @@ def main():
         step_ms = e0.elapsed_time(e1) / args.steps
         log(f"timed {args.steps} steps: {step_ms:.3f} ms/step (events), wall {wall * 1e3 / args.steps:.3f} ms/step")
 
-        # the dominant kernel alone (decode attention), same launch configuration
+        # the dominant kernel alone, same launch configuration
         d0 = torch.cuda.Event(enable_timing=True)
         d1 = torch.cuda.Event(enable_timing=True)
         d0.record(stream)
         for _ in range(args.kernel_reps):
-            decode_only()
+            kernel_pass()
         d1.record(stream)
         stream.synchronize()
         dec_us = d0.elapsed_time(d1) * 1e3 / (args.kernel_reps * w.layers)
@@ -257,9 +268,9 @@ def main():
     total_bytes = nbytes["step"] * w.layers
     tbps = total_bytes / (step_ms * 1e-3) / 1e12
     us_layer = step_ms * 1e3 / w.layers
-    dec_gbs = nbytes["decode"] / (dec_us * 1e-6) / 1e9
+    dec_gbs = nbytes[kernel_bytes] / (dec_us * 1e-6) / 1e9
     log(f"{us_layer:.2f} us/layer-step, {tbps:.3f} TB/s ({tbps * 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s); "
-        f"decode kernel {dec_us:.2f} us/launch = {dec_gbs:.0f} GB/s")
+        f"{kernel_name} {dec_us:.2f} us/launch = {dec_gbs:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -285,12 +296,13 @@ def main():
         "config": {"workload": f"{w.name}: batch {w.batch}, {w.num_heads} q / {w.num_kv_heads} kv heads, "
                                f"head_dim {w.head_dim}, context {T}, "
                                f"{'per-token' if w.group == 0 else 'group-32'} fp32 scales, {w.layers} layers, "
-                               "append 1 token + decode per layer",
+                               f"append 1 token + decode per layer "
+                               f"({'two launches' if args.separate else 'one fused launch'})",
                    "batch": w.batch, "seq_len": T, "layers": w.layers, "bytes_per_step": total_bytes},
-        "roofline": {"bound": "hbm", "kernel": "kvq_attention_decode",
+        "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": nbytes["decode"], "us_per_launch": round(dec_us, 3)},
+                     "bytes_per_launch": nbytes[kernel_bytes], "us_per_launch": round(dec_us, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -134,6 +134,25 @@ kvq_status kvq_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                 int32_t max_seq_len_hint, void* stream);
 
 /*
+ * kvq_append_decode — one decode step in a single launch: the new K and V
+ * rows of every sequence are quantized into position seq_lens[b] - 1 (exactly
+ * as kvq_append with start_pos = seq_lens - 1 and n_new = 1 would), then the
+ * query attends to the first seq_lens[b] tokens, that row included (exactly
+ * as kvq_attention_decode).  The workgroup whose token range holds the new
+ * position quantizes the rows and uses them directly, so no separate append
+ * pass runs first.
+ *
+ *   k_new, v_new : device [B, KVH, 1, D] of in_dtype (fp32 or bf16)
+ *   other arguments and the workspace as for kvq_attention_decode; a
+ *   sequence with seq_lens[b] <= 0 writes no row and gives zeros.
+ * Errors: those of kvq_append and kvq_attention_decode.
+ */
+kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const void* v_new,
+                             int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens,
+                             float attn_scale, uint16_t* out, void* workspace,
+                             size_t workspace_bytes, int32_t max_seq_len_hint, void* stream);
+
+/*
  * kvq_attention_chunk — chunked prefill: n queries per sequence, already
  * appended at positions ctx_lens[b] .. ctx_lens[b] + n - 1, attend to the
  * cache.  With causal != 0 query i sees keys t <= ctx_lens[b] + i

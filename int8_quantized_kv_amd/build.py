@@ -2,7 +2,8 @@
 
 Compiles every ``csrc/*.hip`` translation unit with hipcc and links them into
 ``int8_quantized_kv_amd/libkvq.so`` (in-tree, so the built library travels
-with the source tree).  Usage: ``python -m int8_quantized_kv_amd.build``.
+with the source tree).  Usage: ``python int8_quantized_kv_amd/build.py`` (run
+as a file: importing the package would load the library being rebuilt).
 """
 
 from __future__ import annotations

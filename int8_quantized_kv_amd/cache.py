@@ -80,6 +80,23 @@ class Int8KVCache:
                                 max_seq_len_hint, stream)
         return out
 
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, seq_lens: torch.Tensor,
+                      attn_scale: float, max_seq_len_hint: int, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+        """Append one K/V row per sequence at seq_lens - 1 and decode, in one launch."""
+        if k_new.dtype not in (torch.float32, torch.bfloat16) or v_new.dtype != k_new.dtype:
+            raise TypeError("k_new and v_new must both be float32 or both bfloat16")
+        if not (k_new.is_contiguous() and v_new.is_contiguous()):
+            raise ValueError("k_new and v_new must be contiguous")
+        dt = _k.KVQ_DT_BF16 if k_new.dtype == torch.bfloat16 else _k.KVQ_DT_F32
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = self.workspace(max_seq_len_hint, 1)
+        _k.kvq_append_decode(self.desc, k_new, v_new, dt, q, seq_lens, attn_scale, out, workspace,
+                             workspace.numel(), max_seq_len_hint, stream)
+        return out
+
     def chunk(self, q: torch.Tensor, ctx_lens: torch.Tensor, causal: bool, attn_scale: float,
               max_ctx_len_hint: int, out: torch.Tensor | None = None,
               workspace: torch.Tensor | None = None, stream=None):

@@ -131,6 +131,31 @@ KVQ_API kvq_status kvq_attention_decode(const kvq_cache* c, const uint16_t* q, c
                        static_cast<hipStream_t>(stream));
 }
 
+KVQ_API kvq_status kvq_append_decode(const kvq_cache* c, const void* k_new, const void* v_new, int32_t in_dtype,
+                                     const uint16_t* q, const int32_t* seq_lens, float attn_scale, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, int32_t max_seq_len_hint,
+                                     void* stream) {
+  const char* who = "kvq_append_decode";
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
+  if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
+  if (!q || !seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, seq_lens and out must be non-NULL", who);
+  if (!(attn_scale == attn_scale) || attn_scale == INFINITY || attn_scale == -INFINITY)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
+  if (max_seq_len_hint < 1 || max_seq_len_hint > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
+                capacity_of(*c));
+  if (!decode_supported(c->head_dim))
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
+  const DecodePlan plan = plan_decode(*c, max_seq_len_hint);
+  st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
+  if (st != KVQ_OK) return st;
+  return launch_decode(*c, plan, q, seq_lens, attn_scale, out, workspace, max_seq_len_hint,
+                       static_cast<hipStream_t>(stream), k_new, v_new, in_dtype);
+}
+
 KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens,
                                        int32_t causal, float attn_scale, uint16_t* out, void* workspace,
                                        size_t workspace_bytes, int32_t max_ctx_len_hint, void* stream) {

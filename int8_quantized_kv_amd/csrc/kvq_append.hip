@@ -8,6 +8,7 @@
 // group-32 from combs-models 0.2.2 src/kv.rs, `kv_quantize`).  The maximum is
 // exact, so the reduction order cannot change a code.
 #include "kvq_internal.hpp"
+#include "kvq_quant.hpp"
 
 namespace kvq {
 namespace {
@@ -16,53 +17,17 @@ struct AppendParams {
   const void* src[2];        // K, V new rows [B, KVH, n, D]
   uint8_t* codes[2];
   float* scales[2];
-  const int32_t* start_pos;  // [B]
+  const int32_t* start_pos;  // [B]; with pos_from_lens, seq_lens [B]
   CacheGeom geom;
   int32_t batch, n, head_dim, groups;  // groups = scales per row
   int32_t rows_per_side;               // B * KVH * n
+  int32_t pos_from_lens;               // 1: the row goes to position seq_lens[b] - 1
+  int32_t in_bf16;
 };
 
-template <typename T>
-struct Vec;
-template <>
-struct Vec<float> {
-  template <int N>
-  __device__ static void load(const float* p, float (&x)[N]) {
-    if constexpr (N == 1) {
-      x[0] = p[0];
-    } else if constexpr (N == 2) {
-      float2 v = *reinterpret_cast<const float2*>(p);
-      x[0] = v.x; x[1] = v.y;
-    } else {
-      float4 v = *reinterpret_cast<const float4*>(p);
-      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    }
-  }
-};
-template <>
-struct Vec<uint16_t> {
-  template <int N>
-  __device__ static void load(const uint16_t* p, float (&x)[N]) {
-    if constexpr (N == 1) {
-      x[0] = bf16_to_f32(p[0]);
-    } else if constexpr (N == 2) {
-      uint32_t v = *reinterpret_cast<const uint32_t*>(p);
-      x[0] = __uint_as_float(v << 16);
-      x[1] = __uint_as_float(v & 0xffff0000u);
-    } else {
-      uint2 v = *reinterpret_cast<const uint2*>(p);
-      x[0] = __uint_as_float(v.x << 16);
-      x[1] = __uint_as_float(v.x & 0xffff0000u);
-      x[2] = __uint_as_float(v.y << 16);
-      x[3] = __uint_as_float(v.y & 0xffff0000u);
-    }
-  }
-};
-
-// EPL: elements per lane (1, 2 or 4); a row of D elements uses D/EPL <= 64
-// lanes.  GROUP32: one scale per 32 elements (32/EPL lanes) instead of one
-// per row.
-template <int EPL, typename TIn, bool GROUP32>
+// One wave per row; EPL elements per lane (row_epl(D)); GROUP32: one scale
+// per 32 elements (32/EPL lanes) instead of one per row.
+template <int EPL, bool GROUP32>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int lane = threadIdx.x & (kWave - 1);
   const int r = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
@@ -73,46 +38,21 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int bh = row / p.n;
   const int h = bh % p.geom.kvh;
   const int b = bh / p.geom.kvh;
-  const int pos = p.start_pos[b] + i;
+  const int pos = p.pos_from_lens ? p.start_pos[b] - 1 : p.start_pos[b] + i;
   const int64_t dst = cache_row(p.geom, b, h, pos);
   if (dst < 0) return;  // outside the cache: not written
 
   const int D = p.head_dim;
-  const int active = D / EPL;
-  const bool on = lane < active;
+  const bool on = lane < D / EPL;
   float x[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) x[e] = 0.0f;
-  const TIn* src = static_cast<const TIn*>(p.src[side]) + static_cast<int64_t>(row) * D;
-  if (on) Vec<TIn>::template load<EPL>(src + lane * EPL, x);
-
-  float a = 0.0f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) a = fmaxf(a, fabsf(x[e]));
-  // Maximum over the row, or over the 32/EPL lanes of one group.
-  constexpr int kGroupLanes = 32 / EPL;
-  const int span = GROUP32 ? kGroupLanes : kWave;
-  for (int off = span / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
-
-  const float m = fmaxf(a, 1e-8f);
-  const float s = m / 127.0f;  // IEEE division (correctly rounded)
-  uint32_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    float y = x[e] / s;        // IEEE division, not a reciprocal multiply
-    float q = roundf(y);       // half away from zero
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    packed |= static_cast<uint32_t>(static_cast<int>(q) + 128) << (8 * e);
-  }
+  const size_t esize = p.in_bf16 ? 2 : 4;
+  load_row_values<EPL>(static_cast<const char*>(p.src[side]) + static_cast<int64_t>(row) * D * esize, lane, on,
+                       p.in_bf16 != 0, x);
+  float s;
+  const uint32_t packed = quantize_lane<EPL, GROUP32>(x, s);
   if (on) {
-    uint8_t* out = p.codes[side] + dst * D + lane * EPL;
-    if constexpr (EPL == 1) {
-      *out = static_cast<uint8_t>(packed);
-    } else if constexpr (EPL == 2) {
-      *reinterpret_cast<uint16_t*>(out) = static_cast<uint16_t>(packed);
-    } else {
-      *reinterpret_cast<uint32_t*>(out) = packed;
-    }
+    store_lane_codes<EPL>(p.codes[side] + dst * D, lane, packed);
+    constexpr int kGroupLanes = 32 / EPL;
     float* sc = p.scales[side] + dst * p.groups;
     if (GROUP32) {
       if ((lane % kGroupLanes) == 0) sc[lane / kGroupLanes] = s;
@@ -171,20 +111,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   }
 }
 
-template <typename TIn, bool G32>
+template <bool G32>
 void dispatch_epl(int epl, dim3 grid, hipStream_t st, const AppendParams& p) {
   if (epl == 1)
-    hipLaunchKernelGGL((append_kernel<1, TIn, G32>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((append_kernel<1, G32>), grid, dim3(256), 0, st, p);
   else if (epl == 2)
-    hipLaunchKernelGGL((append_kernel<2, TIn, G32>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((append_kernel<2, G32>), grid, dim3(256), 0, st, p);
   else
-    hipLaunchKernelGGL((append_kernel<4, TIn, G32>), grid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL((append_kernel<4, G32>), grid, dim3(256), 0, st, p);
 }
 
 }  // namespace
 
 kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_new, int in_dtype,
-                         int n_new, const int32_t* start_pos, hipStream_t stream) {
+                         int n_new, const int32_t* start_pos, hipStream_t stream, bool pos_from_lens) {
   AppendParams p;
   p.src[0] = k_new;
   p.src[1] = v_new;
@@ -198,21 +138,15 @@ kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_ne
   p.n = n_new;
   p.head_dim = c.head_dim;
   p.groups = scales_per_row(c);
+  p.pos_from_lens = pos_from_lens ? 1 : 0;
+  p.in_bf16 = in_dtype == KVQ_DT_BF16 ? 1 : 0;
   const int64_t rows = static_cast<int64_t>(c.batch) * c.num_kv_heads * n_new;
   if (rows * 2 > 0x7fffffffLL) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_append: too many rows (%lld)", (long long)rows);
   p.rows_per_side = static_cast<int32_t>(rows);
-  // Elements per lane: smallest power of two with D/EPL <= 64.
-  const int epl = c.head_dim <= 64 ? 1 : (c.head_dim <= 128 ? 2 : 4);
   const int64_t waves = rows * 2;
   dim3 grid(static_cast<unsigned>((waves + 3) / 4));
-  const bool g32 = c.scale_mode == KVQ_SCALE_GROUP32;
-  if (in_dtype == KVQ_DT_F32) {
-    if (g32) dispatch_epl<float, true>(epl, grid, stream, p);
-    else dispatch_epl<float, false>(epl, grid, stream, p);
-  } else {
-    if (g32) dispatch_epl<uint16_t, true>(epl, grid, stream, p);
-    else dispatch_epl<uint16_t, false>(epl, grid, stream, p);
-  }
+  if (c.scale_mode == KVQ_SCALE_GROUP32) dispatch_epl<true>(row_epl(c.head_dim), grid, stream, p);
+  else dispatch_epl<false>(row_epl(c.head_dim), grid, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_append: launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;

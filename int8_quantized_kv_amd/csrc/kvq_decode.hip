@@ -31,6 +31,7 @@
 //     call).
 // head_dim 256 uses the generic kernel below (fp32 FMAs, separate merge).
 #include "kvq_internal.hpp"
+#include "kvq_quant.hpp"
 
 #include <cmath>
 #include <cstdlib>
@@ -52,16 +53,19 @@ constexpr int kWeightShift = 7;    // weights carry 2^7 so they fill f16 range
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 struct DecodeParams {
-  const uint8_t* k_codes;
-  const uint8_t* v_codes;
-  const float* k_scales;
-  const float* v_scales;
+  uint8_t* k_codes;          // written only by the fused append
+  uint8_t* v_codes;
+  float* k_scales;
+  float* v_scales;
   const uint16_t* q;         // [B, H, D] bf16
   const int32_t* seq_lens;   // [B]
   int32_t* counters;         // [B, KVH * wg_per_kvh], zero between calls
   float* part_ml;            // [B, H, S, 2]  (m, l) per split
   float* part_o;             // [B, H, S, D]  unnormalised outputs
   uint16_t* out;             // [B, H, D] bf16
+  const void* new_k;         // fused append: K/V rows [B, KVH, 1, D] for position seq_lens[b] - 1
+  const void* new_v;
+  int32_t new_bf16;          // fused append: rows are bf16 (else fp32)
   CacheGeom geom;
   int32_t num_heads;
   int32_t groups;            // scales per row
@@ -306,7 +310,7 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
 // ---------------------------------------------------------------------------
 // Streaming kernel (head_dim 32, 64, 128).
 // ---------------------------------------------------------------------------
-template <int D, int HPW, bool G32, bool PAGED>
+template <int D, int HPW, bool G32, bool PAGED, bool APPEND>
 __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(DecodeParams p) {
   // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
   // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
@@ -327,6 +331,9 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   __shared__ float sm_fml[kStreamWaves][HPW][2];           // per-wave (m, l)
   __shared__ float sm_o[HPW][D];                     // workgroup outputs
   __shared__ float sm_ml[HPW][2];
+  __shared__ uint4 sm_nk[D / 16];                    // fused append: new K codes
+  __shared__ uint2 sm_nv[D / 8];                     // fused append: new V codes
+  __shared__ float sm_ns[2][NG];                     // fused append: new K / V scales
 
   const int split = blockIdx.x;
   const int hg = blockIdx.y;
@@ -344,6 +351,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // block's loads go out against that bound (rows past the real end are valid
   // memory and are masked later), overlapping the length and query loads.
   int t_end = min(p.len_cap, t_begin + p.split_len);
+  int pn = -1;            // fused append: position of the new row (set once the length is known)
+  bool owns_new = false;  // fused append: this workgroup's split holds it
 
   uint32_t qp[HPW][8];
   float fold[HPW];      // group-32: 128 * 2^-24 * (sum of this lane's scaled queries)
@@ -479,6 +488,29 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // ---- one 64-token block; PREFETCH issues the next block's loads early ----------
   auto run_block = [&](int blk, auto prefetch) {
     constexpr bool PREFETCH = decltype(prefetch)::value;
+    if constexpr (APPEND) {
+      // the block holding the freshly appended token uses the codes just
+      // computed (its loads may have been issued before they were stored)
+      const int s0 = t_begin + blk * kBlock;
+      if (owns_new && pn >= s0 && pn < s0 + kBlock) {
+        const int rel = pn - s0;
+#pragma unroll
+        for (int i = 0; i < NPK; ++i) {
+          if (i * TK + kslot == rel) {
+            kb[i] = sm_nk[ksub];
+            if constexpr (G32) ksc[i] = sm_ns[0][kgroup];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NPV; ++i)
+          if (i * TV + vslot == rel) vb[i] = sm_nv[vsub];
+        if (lane == rel) {
+          if constexpr (!G32) s_k = sm_ns[0][0];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) s_v[g] = sm_ns[1][g];
+        }
+      }
+    }
     // QK: partial dots of this lane's 16 dims, all heads
 #pragma unroll
     for (int i = 0; i < NPK; ++i) {
@@ -597,6 +629,15 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     load_k(blk);
     load_v(blk);
   }
+  // fused append: waves 0 and 1 fetch the new K and V rows of this KV head
+  constexpr int kEpl = row_epl(D);
+  float xnew[kEpl];
+  if constexpr (APPEND) {
+    const size_t esz = p.new_bf16 ? 2 : 4;
+    const char* src = static_cast<const char*>(wave == 0 ? p.new_k : p.new_v) +
+                      (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * esz;
+    load_row_values<kEpl>(src, lane, wave < 2 && lane < D / kEpl, p.new_bf16 != 0, xnew);
+  }
   const int L = clamp_len(p, b);
   if (L == 0 && split == 0) {  // empty window: the output is zero
     for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads)
@@ -606,6 +647,38 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   t_end = min(L, t_begin + p.split_len);
   const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
   const int ns = (L + p.split_len - 1) / p.split_len;
+  // fused append: the workgroup whose split holds position L-1 quantizes the
+  // new rows (abaddon kv_cache_quant_cuda.rs `quantize_tensor` steps), stores
+  // them in the cache, and keeps a copy in LDS for its own attention
+  pn = L - 1;
+  owns_new = APPEND && pn >= t_begin && pn < t_end;
+
+  if constexpr (APPEND) {
+    if (owns_new) {
+      if (wave < 2) {
+        float sc;
+        const uint32_t packed = quantize_lane<kEpl, G32>(xnew, sc);
+        const int64_t row = row_of(pn);
+        if (lane < D / kEpl) {
+          store_lane_codes<kEpl>((wave == 0 ? p.k_codes : p.v_codes) + row * D, lane, packed);
+          store_lane_codes<kEpl>(wave == 0 ? reinterpret_cast<uint8_t*>(sm_nk) : reinterpret_cast<uint8_t*>(sm_nv),
+                                 lane, packed);
+          constexpr int kGroupLanes = 32 / kEpl;
+          float* gs = (wave == 0 ? p.k_scales : p.v_scales) + row * NG;
+          if (G32) {
+            if (lane % kGroupLanes == 0) {
+              gs[lane / kGroupLanes] = sc;
+              sm_ns[wave][lane / kGroupLanes] = sc;
+            }
+          } else if (lane == 0) {
+            gs[0] = sc;
+            sm_ns[wave][0] = sc;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
 
   // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
 #pragma unroll
@@ -901,32 +974,37 @@ int pass_tokens(int head_dim) {
 }
 
 template <int D, int HPW, bool G32, bool PAGED>
-void launch_kernel(bool stream_kernel, const DecodeParams& p, dim3 grid, hipStream_t st) {
+void launch_kernel(bool stream_kernel, bool append, const DecodeParams& p, dim3 grid, hipStream_t st) {
   if (stream_kernel) {
-    if constexpr (D <= 128)
-      hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED>), grid, dim3(kStreamThreads), 0, st, p);
+    if constexpr (D <= 128) {
+      if (append)
+        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED, true>), grid, dim3(kStreamThreads), 0, st, p);
+      else
+        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED, false>), grid, dim3(kStreamThreads), 0, st, p);
+    }
   } else {
     hipLaunchKernelGGL((decode_generic_kernel<D, HPW, G32, PAGED>), grid, dim3(kThreads), 0, st, p);
   }
 }
 
 template <int D, int HPW>
-void launch_modes(bool stream_kernel, bool g32, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
+void launch_modes(bool stream_kernel, bool append, bool g32, bool paged, const DecodeParams& p, dim3 grid,
+                  hipStream_t st) {
   if (g32) {
-    if (paged) launch_kernel<D, HPW, true, true>(stream_kernel, p, grid, st);
-    else launch_kernel<D, HPW, true, false>(stream_kernel, p, grid, st);
+    if (paged) launch_kernel<D, HPW, true, true>(stream_kernel, append, p, grid, st);
+    else launch_kernel<D, HPW, true, false>(stream_kernel, append, p, grid, st);
   } else {
-    if (paged) launch_kernel<D, HPW, false, true>(stream_kernel, p, grid, st);
-    else launch_kernel<D, HPW, false, false>(stream_kernel, p, grid, st);
+    if (paged) launch_kernel<D, HPW, false, true>(stream_kernel, append, p, grid, st);
+    else launch_kernel<D, HPW, false, false>(stream_kernel, append, p, grid, st);
   }
 }
 
 template <int D>
-void launch_d(bool stream_kernel, int hpw, bool g32, bool paged, const DecodeParams& p, dim3 grid,
+void launch_d(bool stream_kernel, bool append, int hpw, bool g32, bool paged, const DecodeParams& p, dim3 grid,
               hipStream_t st) {
-  if (hpw == 4) launch_modes<D, 4>(stream_kernel, g32, paged, p, grid, st);
-  else if (hpw == 2) launch_modes<D, 2>(stream_kernel, g32, paged, p, grid, st);
-  else launch_modes<D, 1>(stream_kernel, g32, paged, p, grid, st);
+  if (hpw == 4) launch_modes<D, 4>(stream_kernel, append, g32, paged, p, grid, st);
+  else if (hpw == 2) launch_modes<D, 2>(stream_kernel, append, g32, paged, p, grid, st);
+  else launch_modes<D, 1>(stream_kernel, append, g32, paged, p, grid, st);
 }
 
 int env_int(const char* name, int dflt) {
@@ -972,7 +1050,15 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
 
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
                          const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
-                         int max_seq_len, hipStream_t stream) {
+                         int max_seq_len, hipStream_t stream, const void* new_k, const void* new_v,
+                         int new_dtype) {
+  const bool append = new_k != nullptr;
+  const bool stream_kernel = use_stream(c.head_dim);
+  if (append && !stream_kernel) {
+    // the generic kernel has no fused path: append the row first
+    kvq_status st = launch_append(c, new_k, new_v, new_dtype, 1, seq_lens, stream, true);
+    if (st != KVQ_OK) return st;
+  }
   DecodeParams p;
   p.k_codes = c.k_codes;
   p.v_codes = c.v_codes;
@@ -986,6 +1072,9 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   p.part_ml = reinterpret_cast<float*>(w + plan.counter_bytes);
   p.part_o = reinterpret_cast<float*>(w + plan.counter_bytes + align_up(partials * 2 * sizeof(float), 256));
   p.out = out;
+  p.new_k = new_k;
+  p.new_v = new_v;
+  p.new_bf16 = new_dtype == KVQ_DT_BF16 ? 1 : 0;
   p.geom = geom_of(c);
   p.num_heads = c.num_heads;
   p.groups = scales_per_row(c);
@@ -1000,13 +1089,13 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   if (grid.y > 65535 || grid.z > 65535)
     return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_decode: grid too large");
   const bool g32 = c.scale_mode == KVQ_SCALE_GROUP32;
-  const bool stream_kernel = use_stream(c.head_dim);
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
+  const bool fused = append && stream_kernel;
   switch (c.head_dim) {
-    case 32: launch_d<32>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
-    case 64: launch_d<64>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
-    case 128: launch_d<128>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
-    default: launch_d<256>(stream_kernel, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    case 32: launch_d<32>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    case 64: launch_d<64>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    case 128: launch_d<128>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    default: launch_d<256>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: launch failed: %s", hipGetErrorString(e));

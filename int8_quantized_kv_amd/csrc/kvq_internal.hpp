@@ -33,8 +33,10 @@ inline int capacity_of(const kvq_cache& c) {
 }
 
 // ---- append / dequant -------------------------------------------------------
+// pos_from_lens: start_pos holds seq_lens and the single new row goes to
+// position seq_lens[b] - 1.
 kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_new, int in_dtype,
-                         int n_new, const int32_t* start_pos, hipStream_t stream);
+                         int n_new, const int32_t* start_pos, hipStream_t stream, bool pos_from_lens = false);
 kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens, int out_dtype,
                           void* out, int out_len, hipStream_t stream);
 
@@ -48,9 +50,12 @@ struct DecodePlan {
 };
 bool decode_supported(int head_dim);
 DecodePlan plan_decode(const kvq_cache& c, int max_seq_len);
+// new_k / new_v non-null: fused append of one row per sequence at position
+// seq_lens[b] - 1 before the attention.
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
                          const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
-                         int max_seq_len, hipStream_t stream);
+                         int max_seq_len, hipStream_t stream, const void* new_k = nullptr,
+                         const void* new_v = nullptr, int new_dtype = KVQ_DT_BF16);
 
 // ---- chunked prefill --------------------------------------------------------
 bool chunk_supported(int head_dim);

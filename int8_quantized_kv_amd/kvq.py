@@ -30,7 +30,7 @@ KVQ_DT_BF16 = 1
 
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_RANGE", 3: "UNSUPPORTED", 4: "HIP", 5: "WORKSPACE"}
 
-EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_attention_chunk", "kvq_dequant",
+EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_append_decode", "kvq_attention_chunk", "kvq_dequant",
             "kvq_workspace_size", "kvq_cache_bytes", "kvq_last_error", "kvq_version")
 
 
@@ -86,7 +86,7 @@ def _load():
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libkvq.so not found at {LIB_PATH}; build it with "
-                          "`python -m int8_quantized_kv_amd.build`")
+                          "`python int8_quantized_kv_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     runtimes = _hip_runtimes()
     if len(runtimes) > 1:
@@ -99,6 +99,8 @@ def _load():
     lib.kvq_append.restype = I
     lib.kvq_attention_decode.argtypes = [CP, P, P, ctypes.c_float, P, P, ctypes.c_size_t, I, P]
     lib.kvq_attention_decode.restype = I
+    lib.kvq_append_decode.argtypes = [CP, P, P, I, P, P, ctypes.c_float, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_append_decode.restype = I
     lib.kvq_attention_chunk.argtypes = [CP, P, I, P, I, ctypes.c_float, P, P, ctypes.c_size_t, I, P]
     lib.kvq_attention_chunk.restype = I
     lib.kvq_dequant.argtypes = [CP, I, P, I, P, I, P]
@@ -174,6 +176,13 @@ def kvq_attention_decode(cache: kvq_cache, q, seq_lens, attn_scale: float, out, 
                          workspace_bytes: int, max_seq_len_hint: int, stream=None):
     _check(_lib.kvq_attention_decode(ctypes.byref(cache), _ptr(q), _ptr(seq_lens), attn_scale, _ptr(out),
                                      _ptr(workspace), workspace_bytes, max_seq_len_hint, _stream(stream)))
+
+
+def kvq_append_decode(cache: kvq_cache, k_new, v_new, in_dtype: int, q, seq_lens, attn_scale: float, out,
+                      workspace, workspace_bytes: int, max_seq_len_hint: int, stream=None):
+    _check(_lib.kvq_append_decode(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), in_dtype, _ptr(q), _ptr(seq_lens),
+                                  attn_scale, _ptr(out), _ptr(workspace), workspace_bytes, max_seq_len_hint,
+                                  _stream(stream)))
 
 
 def kvq_attention_chunk(cache: kvq_cache, q, n: int, ctx_lens, causal: bool, attn_scale: float, out,
