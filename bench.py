@@ -1,14 +1,19 @@
-"""Benchmark of the INT8-KV decode hot path on one MI355X.
+"""Benchmark of the INT8-KV hot path on one MI355X.
 
-One step = for every layer of the 8B-shaped decode workload (batch 16, 32 query
-/ 8 KV heads, head_dim 128, per-token fp32 scales, 4 outlier channels x10 per
-KV head, 32 layers each with its own cache): quantize-append the new token at
-position 4095 (kvq_append) and run decode attention over 4096 tokens
-(kvq_attention_decode).  The 32 caches (4.44 GB) are visited in order, as a
-model does, so no K/V byte is re-read from the 256 MB Infinity Cache within a
-step.  Inputs are seeded synthetic data, already resident in HBM when timing
-starts.
+Default workload (decode_8b): one step = for every layer of the 8B-shaped
+decode workload (batch 16, 32 query / 8 KV heads, head_dim 128, per-token fp32
+scales, 4 outlier channels x10 per KV head, 32 layers each with its own cache):
+quantize-append the new token at position 4095 and run decode attention over
+4096 tokens (kvq_append_decode, one launch per layer).  The 32 caches (4.44 GB)
+are visited in order, as a model does, so no K/V byte is re-read from the
+256 MB Infinity Cache within a step.
 
+``--workload chunked_prefill``: one step = quantize-append 512 new tokens
+after 8192 cached ones (batch 4, 32/8 heads, head_dim 128) and run causal
+chunked-prefill attention for the 512 queries (kvq_attention_chunk); the
+figure is TFLOP/s over the visible keys only.
+
+Inputs are seeded synthetic data, already resident in HBM when timing starts.
 Prints one JSON line (see --help).  ``--gpus N`` with N > 1 is refused: this
 path is measured on one GPU.
 """
@@ -33,6 +38,7 @@ if ROOT not in sys.path:
 import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, AMD published peak
 
 
 def log(msg):
@@ -54,6 +60,20 @@ def step_bytes(w: wl.Workload, L: int) -> dict:
     decode = codes + scales + q + out
     return {"decode": decode, "append": app_in + app_codes + app_scales,
             "step": decode + app_in + app_codes + app_scales}
+
+
+def chunk_counts(w: wl.Workload) -> dict:
+    """Chunked-prefill step: MFMA flops over visible keys (QK and PV, 2 flops
+    per multiply-add each) and algorithmic bytes."""
+    B, H, KVH, D, n, L0 = w.batch, w.num_heads, w.num_kv_heads, w.head_dim, w.n_new, w.ctx
+    visible = n * (L0 + 1) + n * (n - 1) // 2          # sum over i < n of L0 + i + 1
+    flops = 4 * B * H * D * visible
+    L = L0 + n
+    codes = 2 * B * KVH * L * D
+    scales = 2 * B * KVH * L * 4
+    qo = 2 * B * H * n * D * 2
+    append = 2 * B * KVH * n * (D * 2 + D + 4)
+    return {"flops": flops, "chunk_bytes": codes + scales + qo, "step_bytes": codes + scales + qo + append}
 
 
 # ----------------------------------------------------------------------------
@@ -161,6 +181,131 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
             "seconds": el}
 
 
+def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
+    """The oracle on whole query rows of the chunk step: quantize the cache of
+    one (sequence, KV head), then fp64 attention for sampled query rows."""
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    hpg = w.num_heads // w.num_kv_heads
+    rng = np.random.default_rng(7)
+    flops = 0
+    rows = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        b = int(rng.integers(w.batch))
+        g = int(rng.integers(w.num_kv_heads))
+        kc, ks = orc.quantize(x["k"][b, g], 0)
+        vc, vs = orc.quantize(x["v"][b, g], 0)
+        kh, vh = orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs)
+        for _ in range(64):
+            h = g * hpg + int(rng.integers(hpg))
+            i = int(rng.integers(w.n_new))
+            total = w.ctx + i + 1
+            orc.softmax_attend(x["q"][b, h, i].astype(np.float64), kh[:total], vh[:total], w.attn_scale, None)
+            flops += 4 * w.head_dim * total
+            rows += 1
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{rows} query rows (random sequence, head, position) of the chunk step, each fp64 "
+                      f"attention over its visible keys, plus the oracle quantization of the K/V of their "
+                      f"(sequence, KV head); {el:.1f}s wall; numpy, BLAS threads {blas_threads}; host "
+                      f"{platform.processor() or 'x86_64'} nproc {os.cpu_count()}"}
+
+
+def time_calls(fn, reps: int, stream, torch) -> float:
+    """Average milliseconds of fn() over reps calls, HIP events on `stream`."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    stream.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_chunk(args, w: wl.Workload, kvq, torch, stream):
+    x = wl.layer_inputs(w, 0)
+    B, KVH, T, D = x["k"].shape
+    dev = torch.device("cuda")
+    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len)
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
+        return t.to(dev).view(torch.bfloat16 if a.dtype == np.uint16 else torch.float32)
+
+    with torch.cuda.stream(stream):
+        for p0 in range(0, w.ctx, 1024):
+            n = min(1024, w.ctx - p0)
+            cache.append(up(x["k_raw"][:, :, p0:p0 + n]), up(x["v_raw"][:, :, p0:p0 + n]),
+                         torch.full((B,), p0, dtype=torch.int32, device=dev), stream=stream)
+        k_new = up(x["k_raw"][:, :, w.ctx:])
+        v_new = up(x["v_raw"][:, :, w.ctx:])
+        q = up(x["q_bits"])
+        out = torch.empty_like(q)
+        ctx = torch.full((B,), w.ctx, dtype=torch.int32, device=dev)
+        ws = cache.workspace(T, w.n_new)
+    stream.synchronize()
+    log(f"prefilled {w.ctx} tokens")
+
+    def step():  # quantize-append the chunk's rows, then attention for its queries
+        cache.append(k_new, v_new, ctx, stream=stream)
+        cache.chunk(q, ctx, True, w.attn_scale, w.ctx, out=out, workspace=ws, stream=stream)
+
+    def kernel_pass():
+        cache.chunk(q, ctx, True, w.attn_scale, w.ctx, out=out, workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        torch.cuda.synchronize()
+        log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+        t0 = time.perf_counter()
+        step_ms = time_calls(step, args.steps, stream, torch)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        k_ms = time_calls(kernel_pass, args.kernel_reps, stream, torch)
+    cnt = chunk_counts(w)
+    tflops = cnt["flops"] / (step_ms * 1e-3) / 1e12
+    k_tflops = cnt["flops"] / (k_ms * 1e-3) / 1e12
+    log(f"step {step_ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), wall {wall * 1e3 / args.steps:.3f} ms/step; "
+        f"kvq_attention_chunk {k_ms * 1e3:.1f} us = {k_tflops:.1f} TFLOP/s "
+        f"({k_tflops / MFMA_F16_PEAK_TFLOPS * 100:.1f}% of {MFMA_F16_PEAK_TFLOPS:.0f})")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_chunk(w, x)
+    result = {
+        "metric": "INT8-KV chunked-prefill attention: MFMA TFLOP/s over visible keys",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {B}, {w.num_heads} q / {KVH} kv heads, head_dim {D}, "
+                               f"{w.ctx} cached + {w.n_new} new tokens, causal, per-token fp32 scales; "
+                               f"append the {w.n_new} rows + chunk attention",
+                   "batch": B, "seq_len": T, "flops_per_step": cnt["flops"], "bytes_per_step": cnt["step_bytes"]},
+        "roofline": {"bound": "mfma", "kernel": "kvq_attention_chunk",
+                     "achieved": round(k_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": cnt["flops"], "us_per_launch": round(k_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
@@ -170,7 +315,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32"])
+    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -207,6 +352,9 @@ def main():
         return
 
     w = wl.ALL[args.workload]
+    if w.name == "chunked_prefill":
+        run_chunk(args, w, kvq, torch, stream)
+        return
     T = w.ctx + w.n_new
     log(f"workload {w.name}: B={w.batch} H={w.num_heads} KVH={w.num_kv_heads} D={w.head_dim} "
         f"L={T} layers={w.layers} group={w.group}")

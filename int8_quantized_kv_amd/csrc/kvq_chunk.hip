@@ -7,26 +7,34 @@
 // q_len; combs-models 0.2.2 src/kv.rs, `attend`, keys after the query position
 // forbidden).  Scores and the weighted value sum are dense contractions and run
 // on v_mfma_f32_32x32x16_f16:
-//   * K and V codes become exact f16 values c - 128 (v_perm_b32 puts a code
-//     under the f16 exponent of 1024, v_pk_add_f16 subtracts 1152).  Queries
-//     are scaled by a power of two into f16 range, exact for bf16 inputs.  The
-//     per-token K scale multiplies the fp32 score; the per-token V scale is
-//     folded into the exponent of the weight, w_t = 2^(S_t log2 e + log2 sV_t
-//     - m), and the normaliser sums w_t / sV_t.  Only the f16 weights are
-//     rounded before the fp32 accumulation.
 //   * S^T = K Q^T gives each lane one query column; in the 32x32 C layout a
 //     lane's 16 token rows are exactly the k-slots the B operand of the
 //     second product O^T = V^T P^T needs, so the weights never leave their
-//     lanes.  V^T comes out of a row-major LDS tile through ds_read_b64_tr_b8
-//     (each lane of a 16-lane group names one 8-byte row piece; lane j gets
-//     byte j % 8 of the pieces named by lanes 2b + j / 8, b = 0..7).
+//     lanes.
+//   * K codes are widened once per workgroup, while staging the tile in LDS,
+//     to exact f16 values c - 128 (v_perm_b32 puts a code under the f16
+//     exponent of 1024, v_pk_add_f16 subtracts 1152).  V stays as codes in
+//     LDS; V^T comes out through ds_read_b64_tr_b8 (each lane of a 16-lane
+//     group names one 8-byte row piece; lane j gets byte j % 8 of the pieces
+//     named by lanes 2b + j / 8, b = 0..7) and v_perm_b32 makes each code the
+//     f16 value c * 2^-24 (exact), so sum_t w_t (c_t - 128) =
+//     2^24 sum_t w_t c_t 2^-24 - 128 sum_t w_t, the last sum taken from the
+//     same f16 weights with v_dot2.
+//   * queries are scaled by one power of two per workgroup into f16 range
+//     (exact for bf16 inputs); the per-token K scale, the attention scale,
+//     log2 e and that power of two form one staged factor per token, so a
+//     score is one FMA: z_t = acc * kc_t + log2 sV_t.  The V scale rides in
+//     the exponent of the weight, w_t = 2^(z_t - m), and the normaliser sums
+//     w_t / sV_t.
 //   * one workgroup = 4 waves = 4 (query head, 32-position block) items of
-//     one KV head; the 64-token K/V tile is staged once in LDS (double
-//     buffered, XOR-swizzled in 8-byte units) and serves all four.  With
-//     H / KVH a multiple of 4 the four items share their positions.
+//     one KV head; the 64-token tile is staged once in LDS (double buffered,
+//     XOR-swizzled) and serves all four.  With H / KVH a multiple of 4 the
+//     four items share their positions.
 //   * the running maximum per query is lazy: accumulators are rescaled only
 //     when a score exceeds it by more than 2^8, so weights stay below 2^8.
 #include "kvq_internal.hpp"
+
+#include <type_traits>
 
 namespace kvq {
 namespace {
@@ -39,7 +47,6 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 
 constexpr int kCkWaves = 4;
 constexpr int kCkThreads = kCkWaves * kWave;
-constexpr int kCkTile = 64;   // tokens per pipeline stage
 constexpr int kQBlock = 32;   // query positions per wave
 constexpr float kCkLog2e = 1.4426950408889634f;
 constexpr float kCkLazy = 8.0f;
@@ -64,47 +71,58 @@ struct ChunkParams {
   float scale_log2;     // attn_scale * log2(e)
 };
 
-// 8-byte unit permutation of a D-byte code row, chosen so that the 32 lanes
-// of one K read (32 rows, one unit) and of one V transpose read (8 rows x 4
-// units) fall on distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int t) {
-  if constexpr (D == 128) {
-    const int s = (t >> 1) & 15;
-    return ((s & 1) << 2) | (((s >> 2) & 1) << 3) | ((s >> 1) & 1) | (((s >> 3) & 1) << 1);
-  } else {
-    const int s = (t >> 2) & 7;
-    return (((s >> 1) & 1) << 2) | ((s & 1) << 1) | ((s >> 2) & 1);
+// LDS tile geometry for TOK tokens.  K rows hold D f16 values and are padded
+// by 16 bytes, so the 16 lanes of one K read (16 consecutive rows, one
+// 16-byte unit) fall on distinct banks.  V rows hold D codes in 8-byte units,
+// XOR-permuted so the 32 lanes of one V transpose read (8 rows x 4 units) do.
+template <int D, int TOK>
+struct Tile {
+  static constexpr int kKRow = 2 * D + 16;
+  static constexpr int kKBytes = TOK * kKRow;
+  static constexpr int kVBytes = TOK * D;
+  static constexpr int kBytes = kKBytes + kVBytes + 3 * TOK * 4;
+  static __device__ __forceinline__ int vswz(int t) {
+    if constexpr (D == 128) {
+      const int s = (t >> 1) & 15;
+      return ((s & 1) << 2) | (((s >> 2) & 1) << 3) | ((s >> 1) & 1) | (((s >> 3) & 1) << 1);
+    } else {
+      const int s = (t >> 2) & 7;
+      return (((s >> 1) & 1) << 2) | ((s & 1) << 1) | ((s >> 2) & 1);
+    }
   }
-}
+  // byte offsets inside one buffer
+  static __device__ __forceinline__ int k_off(int t, int u16) { return t * kKRow + 16 * u16; }
+  static __device__ __forceinline__ int v_off(int t, int u8) { return kKBytes + t * D + 8 * (u8 ^ vswz(t)); }
+  static constexpr int kKc = kKBytes + kVBytes;
+  static constexpr int kLsv = kKc + TOK * 4;
+  static constexpr int kRsv = kLsv + TOK * 4;
+};
 
-// Byte offset of 8-byte unit u of tile row t.
-template <int D>
-__device__ __forceinline__ int tile_off(int t, int u) {
-  return t * D + 8 * (u ^ swz<D>(t));
-}
-
-// Eight codes -> eight exact f16 values c - 128.
-__device__ __forceinline__ f16x8 codes_f16(uint32_t lo, uint32_t hi) {
+// Four codes -> two f16 pairs holding the exact values c - 128.
+__device__ __forceinline__ uint2 codes_exact_f16(uint32_t w) {
   const uint32_t e = 0x64646464u;  // high byte of f16 1024 + c
-  uint4 w;
-  w.x = __builtin_amdgcn_perm(e, lo, 0x04010400u);
-  w.y = __builtin_amdgcn_perm(e, lo, 0x04030402u);
-  w.z = __builtin_amdgcn_perm(e, hi, 0x04010400u);
-  w.w = __builtin_amdgcn_perm(e, hi, 0x04030402u);
   const f16x2 off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
-  f16x2 p0 = __builtin_bit_cast(f16x2, w.x) + off;
-  f16x2 p1 = __builtin_bit_cast(f16x2, w.y) + off;
-  f16x2 p2 = __builtin_bit_cast(f16x2, w.z) + off;
-  f16x2 p3 = __builtin_bit_cast(f16x2, w.w) + off;
-  f16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  return r;
+  const f16x2 a = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e, w, 0x04010400u)) + off;
+  const f16x2 b = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(e, w, 0x04030402u)) + off;
+  return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+// Eight codes -> eight f16 values c * 2^-24 (subnormal, exact).
+__device__ __forceinline__ f16x8 codes_tiny_f16(uint32_t lo, uint32_t hi) {
+  uint4 w;
+  w.x = __builtin_amdgcn_perm(0u, lo, 0x0C010C00u);
+  w.y = __builtin_amdgcn_perm(0u, lo, 0x0C030C02u);
+  w.z = __builtin_amdgcn_perm(0u, hi, 0x0C010C00u);
+  w.w = __builtin_amdgcn_perm(0u, hi, 0x0C030C02u);
+  return __builtin_bit_cast(f16x8, w);
 }
 
 __device__ __forceinline__ f16x2 pack2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_convertvector(v, f16x2);
 }
+
+__device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
 
 __device__ __forceinline__ float other_half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -116,7 +134,16 @@ __device__ __forceinline__ float other_half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool PAGED>
+__device__ __forceinline__ float wave_max64(float x) {
+  x = fmaxf(x, __shfl_xor(x, 1, kWave));
+  x = fmaxf(x, __shfl_xor(x, 2, kWave));
+  x = fmaxf(x, __shfl_xor(x, 4, kWave));
+  x = fmaxf(x, __shfl_xor(x, 8, kWave));
+  x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  return other_half_max(x);
+}
+
+template <bool PAGED>
 __device__ __forceinline__ int64_t row_of(const ChunkParams& p, int b, int g, int t) {
   if constexpr (PAGED) {
     int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (t >> 4)];
@@ -129,18 +156,17 @@ __device__ __forceinline__ int64_t row_of(const ChunkParams& p, int b, int g, in
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
-  constexpr int kTileBytes = kCkTile * D;
-  constexpr int kChunksPerRow = D / 16;                          // 16-byte pieces
+  constexpr int kTT = D == 128 ? 1 : 2;     // 32-token S tiles per pipeline stage
+  constexpr int kCkTile = 32 * kTT;         // tokens per pipeline stage
+  using TL = Tile<D, kCkTile>;
+  constexpr int kChunksPerRow = D / 16;                          // 16-code pieces per row
   constexpr int kLoads = kCkTile * kChunksPerRow / kCkThreads;   // per side per thread
   constexpr int kKK = D / 16;                                    // MFMA k-steps for S
   constexpr int kDT = D / 32;                                    // 32-wide d tiles of O
   static_assert(kLoads >= 1, "tile loader");
 
-  __shared__ __attribute__((aligned(16))) uint8_t sm_k[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sm_v[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sm_sk[2][kCkTile];
-  __shared__ __attribute__((aligned(16))) float sm_lsv[2][kCkTile];
-  __shared__ __attribute__((aligned(16))) float sm_rsv[2][kCkTile];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * TL::kBytes];
+  __shared__ float sm_qmax[kCkWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -179,230 +205,283 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
   const int qi = pos0 + col;
   const bool q_ok = active && qi < p.n;
 
-  // ---- query operand: B of S^T = K Q^T (k-slot 8*half + e <-> d = 16kk + 8*half + e)
-  f16x8 qop[kKK];
-  float cq;
+  // ---- queries: one power-of-two scale for the workgroup
+  uint4 qraw[kKK];
   {
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.heads + head) * p.n + (q_ok ? qi : 0)) * D;
-    uint4 raw[kKK];
     float amax = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < kKK; ++kk) {
-      raw[kk] = q_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
+      qraw[kk] = q_ok ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * half) : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {qraw[kk].x, qraw[kk].y, qraw[kk].z, qraw[kk].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         amax = fmaxf(amax, fabsf(__uint_as_float(w[e] << 16)));
         amax = fmaxf(amax, fabsf(__uint_as_float(w[e] & 0xffff0000u)));
       }
     }
-    amax = other_half_max(amax);
-    int kq = 0;
-    if (amax > 0.0f && amax <= 3.0e38f) {
-      int ex;
-      (void)frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
-      kq = min(max(15 - ex, -120), 120);
-    }
-#pragma unroll
-    for (int kk = 0; kk < kKK; ++kk) {
-      const uint32_t w[4] = {raw[kk].x, raw[kk].y, raw[kk].z, raw[kk].w};
-      f16x8 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 h2 = pack2(ldexpf(__uint_as_float(w[e] << 16), kq), ldexpf(__uint_as_float(w[e] & 0xffff0000u), kq));
-        v[2 * e] = h2[0];
-        v[2 * e + 1] = h2[1];
-      }
-      qop[kk] = v;
-    }
-    cq = ldexpf(p.scale_log2, -kq);
+    amax = wave_max64(amax);
+    if (lane == 0) sm_qmax[wave] = amax;
   }
 
-  // ---- tile loader: 16-byte pieces of K and V rows plus per-token scales
+  // ---- tile loader: 16-code pieces of K and V rows plus per-token scales
   uint4 kreg[kLoads], vreg[kLoads];
   float sreg = 0.0f;
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int id = tid + i * kCkThreads;
-      const int r = id / kChunksPerRow;
-      const int c = id % kChunksPerRow;
-      int t = t0 + r;
+      int t = t0 + id / kChunksPerRow;
       t = t < Ltot ? t : Ltot - 1;
-      const int64_t row = row_of<D, PAGED>(p, b, g, t);
-      kreg[i] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + 16 * c);
-      vreg[i] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + 16 * c);
+      const int64_t row = row_of<PAGED>(p, b, g, t);
+      kreg[i] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + 16 * (id % kChunksPerRow));
+      vreg[i] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + 16 * (id % kChunksPerRow));
     }
     if (tid < 2 * kCkTile) {
       const int t = t0 + (tid & (kCkTile - 1));
       if (t < Ltot) {
-        const int64_t row = row_of<D, PAGED>(p, b, g, t);
+        const int64_t row = row_of<PAGED>(p, b, g, t);
         sreg = tid < kCkTile ? p.k_scales[row] : p.v_scales[row];
       }
     }
   };
-  auto store_tile = [&](int buf, int t0) {
+  auto store_tile = [&](uint8_t* buf, int t0, float kfac) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int id = tid + i * kCkThreads;
       const int r = id / kChunksPerRow;
       const int c = id % kChunksPerRow;
-      const int f = swz<D>(r);
-      const int off = r * D + 8 * ((2 * c) ^ (f & ~1));
-      uint4 kv = kreg[i], vv = vreg[i];
-      if (f & 1) {
-        kv = make_uint4(kv.z, kv.w, kv.x, kv.y);
-        vv = make_uint4(vv.z, vv.w, vv.x, vv.y);
-      }
-      *reinterpret_cast<uint4*>(&sm_k[buf][off]) = kv;
-      *reinterpret_cast<uint4*>(&sm_v[buf][off]) = vv;
+      // K: 16 codes -> 16 exact f16 values = units 2c and 2c + 1
+      const uint2 k0 = codes_exact_f16(kreg[i].x), k1 = codes_exact_f16(kreg[i].y);
+      const uint2 k2 = codes_exact_f16(kreg[i].z), k3 = codes_exact_f16(kreg[i].w);
+      *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+      *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c + 1)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
+      // V: codes, 8-byte units 2c and 2c + 1 (one 16-byte store; halves
+      // swap when the permutation flips the low unit bit)
+      const int f = TL::vswz(r);
+      uint4 vv = vreg[i];
+      if (f & 1) vv = make_uint4(vv.z, vv.w, vv.x, vv.y);
+      *reinterpret_cast<uint4*>(buf + TL::kKBytes + r * D + 8 * ((2 * c) ^ (f & ~1))) = vv;
     }
     if (tid < 2 * kCkTile) {
       const int tl = tid & (kCkTile - 1);
       const bool ok = t0 + tl < Ltot;
+      float* kc = reinterpret_cast<float*>(buf + TL::kKc);
+      float* lsv = reinterpret_cast<float*>(buf + TL::kLsv);
+      float* rsv = reinterpret_cast<float*>(buf + TL::kRsv);
       if (tid < kCkTile) {
-        sm_sk[buf][tl] = ok ? sreg : 0.0f;
+        kc[tl] = ok ? sreg * kfac : 0.0f;
       } else {
-        sm_lsv[buf][tl] = ok ? __builtin_amdgcn_logf(sreg) : -INFINITY;
-        sm_rsv[buf][tl] = ok ? 1.0f / sreg : 0.0f;
+        lsv[tl] = ok ? __builtin_amdgcn_logf(sreg) : -INFINITY;
+        rsv[tl] = ok ? 1.0f / sreg : 0.0f;
       }
     }
   };
 
-  // ---- per-lane LDS addresses (loop invariant)
-  // K operand: row 32tt + col, unit 2kk + half.
-  // V operand (transpose read): lane 16*grp + r names token 16ks + pi(grp/2, r/2)
-  // and unit 4dt + 2(grp%2) + r%2, where pi(h, e) = 8(e/4) + 4h + e%4 is the
+  load_tile(0);
+  __syncthreads();  // sm_qmax
+
+  int kq = 0;
+  {
+    const float amax = fmaxf(fmaxf(sm_qmax[0], sm_qmax[1]), fmaxf(sm_qmax[2], sm_qmax[3]));
+    if (amax > 0.0f && amax <= 3.0e38f) {
+      int ex;
+      (void)frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+      kq = min(max(15 - ex, -120), 120);
+    }
+  }
+  const float kfac = ldexpf(p.scale_log2, -kq);
+  f16x8 qop[kKK];  // B of S^T = K Q^T: k-slot 8*half + e <-> d = 16kk + 8*half + e
+#pragma unroll
+  for (int kk = 0; kk < kKK; ++kk) {
+    const uint32_t w[4] = {qraw[kk].x, qraw[kk].y, qraw[kk].z, qraw[kk].w};
+    f16x8 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f16x2 h2 = pack2(ldexpf(__uint_as_float(w[e] << 16), kq), ldexpf(__uint_as_float(w[e] & 0xffff0000u), kq));
+      v[2 * e] = h2[0];
+      v[2 * e + 1] = h2[1];
+    }
+    qop[kk] = v;
+  }
+
+  // Pipeline: tiles j and j + 1 are in LDS when iteration j starts; it loads
+  // tile j + 2, multiplies S for tile j + 1 while it turns the scores of tile j
+  // into weights, accumulates tile j's values, then stores tile j + 2.  Three
+  // LDS buffers rotate.  Waves past their last visible key still run: every
+  // key they see there is masked, so nothing is added.
+  store_tile(smem, 0, kfac);
+  if (ntiles > 1) {
+    load_tile(kCkTile);
+    store_tile(smem + TL::kBytes, kCkTile, kfac);
+  }
+  __syncthreads();
+
+  // V transpose read: lane 16*grp + r names token 16ks + pi(grp/2, r/2) and
+  // unit 4dt + 2(grp%2) + r%2, where pi(h, e) = 8(e/4) + 4h + e%4 is the
   // token of k-slot 8h + e in the S^T C layout.
   const int grp = lane >> 4;
   const int r16 = lane & 15;
   const int vtok = 8 * ((r16 >> 1) >> 2) + 4 * (grp >> 1) + ((r16 >> 1) & 3);
   const int vunit = 2 * (grp & 1) + (r16 & 1);
+  const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
   f32x16 oacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x16{};
   float m_run = kMinusBig;
-  float l_run = 0.0f;
+  float l_run = 0.0f;   // sum of w / sV over this lane's tokens
+  float w_run = 0.0f;   // sum of the f16 weights over this lane's tokens
 
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
+  // S^T for the tile in `buf` (rows = tokens 32tt + 8(r/4) + 4*half + r%4,
+  // column = query), k-steps [K0, K1).
+  auto qk = [&](const uint8_t* buf, f32x16 (&s)[kTT], auto k0c, auto k1c) {
+    constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
+    f16x8 ka[kTT];
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) ka[tt] = *reinterpret_cast<const f16x8*>(buf + TL::k_off(32 * tt + col, 2 * K0 + half));
+#pragma unroll
+    for (int kk = K0; kk < K1; ++kk) {
+      f16x8 na[kTT];
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt)
+        na[tt] = kk + 1 < K1 ? *reinterpret_cast<const f16x8*>(buf + TL::k_off(32 * tt + col, 2 * (kk + 1) + half))
+                             : ka[tt];
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[tt], qop[kk], s[tt], 0, 0, 0);
+        ka[tt] = na[tt];
+      }
+    }
+  };
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
+  f32x16 s_cur[kTT];
+#pragma unroll
+  for (int tt = 0; tt < kTT; ++tt) s_cur[tt] = f32x16{};
+  qk(smem, s_cur, std::integral_constant<int, 0>{}, std::integral_constant<int, kKK>{});
+
+  auto iter = [&](auto curc, int it) {
+    constexpr int CUR = decltype(curc)::value;
+    constexpr int NXT = (CUR + 1) % 3, FUT = (CUR + 2) % 3;
+    const uint8_t* bc = smem + CUR * TL::kBytes;
+    const uint8_t* bn = smem + NXT * TL::kBytes;
     const int t0 = it * kCkTile;
-    const bool more = it + 1 < ntiles;
-    if (more) load_tile(t0 + kCkTile);
+    const bool fut = it + 2 < ntiles;
+    if (fut) load_tile(t0 + 2 * kCkTile);
 
-    if (active && t0 < my_end) {
-      const uint8_t* smk = sm_k[buf];
-      const uint8_t* smv = sm_v[buf];
-      // S^T tiles: rows = tokens 32tt + (8(r/4) + 4*half + r%4), column = query
-      f32x16 s[2];
+    // S for tile j + 1 (first half of the k-steps) beside the scores of tile j
+    f32x16 s_nxt[kTT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        s[tt] = f32x16{};
-        const int trow = 32 * tt + col;
+    for (int tt = 0; tt < kTT; ++tt) s_nxt[tt] = f32x16{};
+    qk(bn, s_nxt, std::integral_constant<int, 0>{}, std::integral_constant<int, kKK / 2>{});
+
+    const float* kc = reinterpret_cast<const float*>(bc + TL::kKc);
+    const float* lsv = reinterpret_cast<const float*>(bc + TL::kLsv);
+    const float* rsv = reinterpret_cast<const float*>(bc + TL::kRsv);
+    float z[kTT][16];
 #pragma unroll
-        for (int kk = 0; kk < kKK; ++kk) {
-          const uint2 c8 = *reinterpret_cast<const uint2*>(smk + tile_off<D>(trow, 2 * kk + half));
-          s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(codes_f16(c8.x, c8.y), qop[kk], s[tt], 0, 0, 0);
+    for (int tt = 0; tt < kTT; ++tt) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int tl = 32 * tt + 8 * q4 + 4 * half;
+        const float4 a = *reinterpret_cast<const float4*>(kc + tl);
+        const float4 c = *reinterpret_cast<const float4*>(lsv + tl);
+        z[tt][4 * q4 + 0] = fmaf(s_cur[tt][4 * q4 + 0], a.x, c.x);
+        z[tt][4 * q4 + 1] = fmaf(s_cur[tt][4 * q4 + 1], a.y, c.y);
+        z[tt][4 * q4 + 2] = fmaf(s_cur[tt][4 * q4 + 2], a.z, c.z);
+        z[tt][4 * q4 + 3] = fmaf(s_cur[tt][4 * q4 + 3], a.w, c.w);
+      }
+    }
+    if (p.causal && t0 + kCkTile - 1 > L0 + pos0) {  // tile reaches the diagonal
+      const int limit = L0 + qi - t0;
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * tt + 8 * (r >> 2) + 4 * half + (r & 3) > limit) z[tt][r] = -INFINITY;
+    }
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, z[tt][r]);
+    zmax = other_half_max(zmax);
+    const bool need = zmax > m_run + kCkLazy;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? zmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      w_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
+    }
+
+    // rest of S for tile j + 1, beside the weights and values of tile j
+    qk(bn, s_nxt, std::integral_constant<int, kKK / 2>{}, std::integral_constant<int, kKK>{});
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) {
+      float w[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 rv = *reinterpret_cast<const float4*>(rsv + 32 * tt + 8 * q4 + 4 * half);
+        const float rvv[4] = {rv.x, rv.y, rv.z, rv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[4 * q4 + e] = __builtin_amdgcn_exp2f(z[tt][4 * q4 + e] - m_run);
+          l_run = fmaf(w[4 * q4 + e], rvv[e], l_run);
         }
       }
-      // z = S log2 e + log2 sV (per token), masked to -inf where not visible
-      const bool diag = p.causal && (t0 + kCkTile - 1 > L0 + pos0);
-      const int limit = L0 + qi;
-      float z[2][16];
-      float zmax = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int ks = 0; ks < 2; ++ks) {
+        f16x8 pw;
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tl = 32 * tt + 8 * q4 + 4 * half;
-          const float4 sk = *reinterpret_cast<const float4*>(&sm_sk[buf][tl]);
-          const float4 lv = *reinterpret_cast<const float4*>(&sm_lsv[buf][tl]);
-          const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
-          const float lvv[4] = {lv.x, lv.y, lv.z, lv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) z[tt][4 * q4 + e] = fmaf(s[tt][4 * q4 + e], skv[e] * cq, lvv[e]);
+        for (int e = 0; e < 4; ++e) {
+          const f16x2 h2 = pack2(w[8 * ks + 2 * e], w[8 * ks + 2 * e + 1]);
+          w_run = dot2(h2, ones, w_run);
+          pw[2 * e] = h2[0];
+          pw[2 * e + 1] = h2[1];
         }
-      }
-      if (diag) {
+        const int tok = 32 * tt + 16 * ks + vtok;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (t0 + 32 * tt + 8 * (r >> 2) + 4 * half + (r & 3) > limit) z[tt][r] = -INFINITY;
-      }
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, z[tt][r]);
-      zmax = other_half_max(zmax);
-      const bool need = zmax > m_run + kCkLazy;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_new = need ? zmax : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
-      }
-      // weights, normaliser, and O^T += V^T P^T
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        float w[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int tl = 32 * tt + 8 * q4 + 4 * half;
-          const float4 rv = *reinterpret_cast<const float4*>(&sm_rsv[buf][tl]);
-          const float rvv[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w[4 * q4 + e] = __builtin_amdgcn_exp2f(z[tt][4 * q4 + e] - m_run);
-            l_run = fmaf(w[4 * q4 + e], rvv[e], l_run);
-          }
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f16x8 pw;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const f16x2 h2 = pack2(w[8 * ks + 2 * e], w[8 * ks + 2 * e + 1]);
-            pw[2 * e] = h2[0];
-            pw[2 * e + 1] = h2[1];
-          }
-          const int tok = 32 * tt + 16 * ks + vtok;
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt) {
-            const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (v2i __attribute__((address_space(3)))*)(smv + tile_off<D>(tok, 4 * dt + vunit)));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                codes_f16(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)), pw, oacc[dt], 0, 0, 0);
-          }
+        for (int dt = 0; dt < kDT; ++dt) {
+          const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (v2i __attribute__((address_space(3)))*)(bc + TL::v_off(tok, 4 * dt + vunit)));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              codes_tiny_f16(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)), pw, oacc[dt], 0, 0, 0);
         }
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt) s_cur[tt] = s_nxt[tt];
 
-    if (more) store_tile(buf ^ 1, t0 + kCkTile);
+    if (fut) store_tile(smem + FUT * TL::kBytes, t0 + 2 * kCkTile, kfac);
     __syncthreads();
+  };
+
+  for (int it = 0; it < ntiles; it += 3) {
+    iter(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < ntiles) iter(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 < ntiles) iter(std::integral_constant<int, 2>{}, it + 2);
   }
 
   // ---- normalise and store: lane holds query qi, d = 32dt + 8(r/4) + 4*half + r%4
   if (!q_ok) return;
   const float l_tot = other_half_sum(l_run);
+  const float w_tot = other_half_sum(w_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float big = 16777216.0f;  // 2^24: the V operands carry c * 2^-24
+  const float off = 128.0f * w_tot;
   uint16_t* orow = p.out + ((static_cast<int64_t>(b) * p.heads + head) * p.n + qi) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       ushort4 o;
-      o.x = f32_to_bf16_rne(oacc[dt][4 * q4 + 0] * inv);
-      o.y = f32_to_bf16_rne(oacc[dt][4 * q4 + 1] * inv);
-      o.z = f32_to_bf16_rne(oacc[dt][4 * q4 + 2] * inv);
-      o.w = f32_to_bf16_rne(oacc[dt][4 * q4 + 3] * inv);
+      o.x = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 0], big, -off) * inv);
+      o.y = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 1], big, -off) * inv);
+      o.z = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 2], big, -off) * inv);
+      o.w = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 3], big, -off) * inv);
       *reinterpret_cast<ushort4*>(orow + 32 * dt + 8 * q4 + 4 * half) = o;
     }
   }
