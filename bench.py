@@ -45,6 +45,24 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    summarised in profiles/, or None when they were taken on another workload
+    or the kernel's sources have changed since."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
+        if rec["workload"] != workload:
+            return None
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def step_bytes(w: wl.Workload, L: int) -> dict:
     """Algorithmic bytes of one layer-step (each byte the step must move once)."""
     B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
@@ -134,13 +152,19 @@ def build_layers(w: wl.Workload, kvq, torch, stream, threads: int):
 # CPU baseline: the oracle on a bounded sample of the same workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
-    import oracle as orc
+def blas_thread_count() -> int:
+    """Threads numpy's BLAS may use (the oracle's matrix products); its
+    elementwise work is single-threaded."""
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
-        blas_threads = 1
+        return 1
+
+
+def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
+    import oracle as orc
+    blas_threads = blas_thread_count()
     T = w.ctx + w.n_new
     # one sequence's worth of the step per call: quantize the new K/V rows,
     # then fp64 attention over the dequantized cache for all its heads
@@ -185,11 +209,7 @@ def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
     """The oracle on whole query rows of the chunk step: quantize the cache of
     one (sequence, KV head), then fp64 attention for sampled query rows."""
     import oracle as orc
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
+    blas_threads = blas_thread_count()
     hpg = w.num_heads // w.num_kv_heads
     rng = np.random.default_rng(7)
     flops = 0
@@ -306,6 +326,127 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     print(json.dumps(result), flush=True)
 
 
+def paged_bytes(w: wl.Workload, lens) -> dict:
+    """Algorithmic bytes of one paged step: every cached code and scale once,
+    queries, outputs, and the appended rows (input, codes, scales)."""
+    H, KVH, D = w.num_heads, w.num_kv_heads, w.head_dim
+    total = int(np.sum(lens))
+    B = len(lens)
+    decode = 2 * total * KVH * (D + 4) + 2 * B * H * D * 2 + B * w.max_blocks_read * 4
+    append = 2 * B * KVH * (D * 2 + D + 4)
+    return {"decode": decode, "step": decode + append}
+
+
+def run_paged(args, w: wl.Workload, kvq, torch, stream):
+    """Paged decode: 64 sequences with lengths U[512, 32768] over a shared
+    arena of 16-token pages dealt out in random order; one step appends one
+    token per sequence and runs decode attention (kvq_append_decode)."""
+    lens, table, num_pages = wl.paged_layout(w)
+    B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    Lmax = int(lens.max())
+    w.max_blocks_read = int(((lens + 15) // 16).sum())  # block-table entries the step reads
+    dev = torch.device("cuda")
+    cache = kvq.Int8KVCache(B, H, KVH, D, num_pages=num_pages,
+                            block_table=torch.from_numpy(table).to(dev))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    t0 = time.time()
+    with torch.cuda.stream(stream):
+        zero = torch.zeros(B, dtype=torch.int32, device=dev)
+        step = 1024
+        for p0 in range(0, Lmax - 1, step):
+            n = min(step, Lmax - 1 - p0)
+            k = torch.randn((B, KVH, n, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            v = torch.randn((B, KVH, n, D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            cache.append(k, v, zero + p0, stream=stream)
+        k_new = torch.randn((B, KVH, 1, D), generator=gen, device=dev).to(torch.bfloat16)
+        v_new = torch.randn((B, KVH, 1, D), generator=gen, device=dev).to(torch.bfloat16)
+        q_bits, _ = wl.paged_q(w)
+        q = torch.from_numpy(q_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        out = torch.empty_like(q)
+        seq_lens = torch.from_numpy(lens).to(dev)
+        ws = cache.workspace(Lmax, 1)
+    stream.synchronize()
+    log(f"paged arena: {num_pages} pages, {int(lens.sum())} tokens, lengths {int(lens.min())}..{Lmax}; "
+        f"prefilled in {time.time() - t0:.1f}s")
+
+    def step_fn():  # rows at position seq_lens[b] - 1, then attention over seq_lens[b] tokens
+        cache.append_decode(k_new, v_new, q, seq_lens, w.attn_scale, Lmax, out=out, workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step_fn()
+        stream.synchronize()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        step_ms = time_calls(step_fn, args.steps, stream, torch)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t1
+    nb = paged_bytes(w, lens)
+    tbps = nb["step"] / (step_ms * 1e-3) / 1e12
+    k_gbs = nb["step"] / (step_ms * 1e-3) / 1e9
+    log(f"step {step_ms * 1e3:.1f} us, {tbps:.3f} TB/s ({tbps * 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s), "
+        f"wall {wall * 1e3 / args.steps:.3f} ms/step")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_paged(w, lens)
+    result = {
+        "metric": "INT8-KV paged decode attention: achieved HBM TB/s (% of peak)",
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {B}, {H} q / {KVH} kv heads, head_dim {D}, page size 16, "
+                               f"lengths U[512, 32768] (seed {w.seed}: {int(lens.sum())} tokens), pages dealt "
+                               f"from a shared arena in random order, per-token fp32 scales; append 1 token + "
+                               f"decode (one fused launch)",
+                   "batch": B, "seq_len": Lmax, "bytes_per_step": nb["step"]},
+        "roofline": {"bound": "hbm", "kernel": "kvq_append_decode",
+                     "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": nb["step"], "us_per_launch": round(step_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_paged(w: wl.Workload, lens, target_s: float = 12.0):
+    """The oracle on whole sequences of the paged step (quantize the sequence's
+    K/V, fp64 attention for its heads), on a bounded sample of sequences."""
+    import oracle as orc
+    blas_threads = blas_thread_count()
+    q_bits, q = wl.paged_q(w)
+    done_bytes = 0
+    seqs = 0
+    t0 = time.perf_counter()
+    b = 0
+    while time.perf_counter() - t0 < target_s:
+        L = int(lens[b])
+        x = wl.sequence_kv(w, b, L)
+        kc, ks = orc.quantize(x["k"], 0)
+        vc, vs = orc.quantize(x["v"], 0)
+        orc.attention_decode(q[b:b + 1], orc.dequantize_exact(kc, ks)[None], orc.dequantize_exact(vc, vs)[None],
+                             [L], w.attn_scale)
+        done_bytes += 2 * L * w.num_kv_heads * (w.head_dim + 4)
+        seqs += 1
+        b = (b + 1) % len(lens)
+    el = time.perf_counter() - t0
+    return {"value": done_bytes / el / 1e12, "unit": "TB/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"{seqs} sequences of the paged step in order (quantize the sequence's K/V, fp64 attention "
+                      f"for its 32 heads), {el:.1f}s wall; bytes counted as the cache codes and scales those "
+                      f"sequences occupy; numpy elementwise single-threaded, BLAS threads {blas_threads}; host "
+                      f"{platform.processor() or 'x86_64'} nproc {os.cpu_count()}"}
+
+
 # ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
@@ -315,7 +456,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill"])
+    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -354,6 +495,9 @@ def main():
     w = wl.ALL[args.workload]
     if w.name == "chunked_prefill":
         run_chunk(args, w, kvq, torch, stream)
+        return
+    if w.name == "paged_decode":
+        run_paged(args, w, kvq, torch, stream)
         return
     T = w.ctx + w.n_new
     log(f"workload {w.name}: B={w.batch} H={w.num_heads} KVH={w.num_kv_heads} D={w.head_dim} "
@@ -449,7 +593,7 @@ def main():
                    "batch": w.batch, "seq_len": T, "layers": w.layers, "bytes_per_step": total_bytes},
         "roofline": {"bound": "hbm", "kernel": kernel_name,
                      "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(kernel_name, w.name),
                      "bytes_per_launch": nbytes[kernel_bytes], "us_per_launch": round(dec_us, 3)},
         "cpu_baseline": cpu,
     }
