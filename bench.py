@@ -370,8 +370,16 @@ def run_paged(args, w: wl.Workload, kvq, torch, stream):
     log(f"paged arena: {num_pages} pages, {int(lens.sum())} tokens, lengths {int(lens.min())}..{Lmax}; "
         f"prefilled in {time.time() - t0:.1f}s")
 
-    def step_fn():  # rows at position seq_lens[b] - 1, then attention over seq_lens[b] tokens
-        cache.append_decode(k_new, v_new, q, seq_lens, w.attn_scale, Lmax, out=out, workspace=ws, stream=stream)
+    if args.separate:
+        last = seq_lens - 1
+
+        def step_fn():  # two launches: append at seq_lens[b] - 1, then decode
+            cache.append(k_new, v_new, last, stream=stream)
+            cache.decode(q, seq_lens, w.attn_scale, Lmax, out=out, workspace=ws, stream=stream)
+    else:
+        def step_fn():  # rows at position seq_lens[b] - 1, then attention over seq_lens[b] tokens
+            cache.append_decode(k_new, v_new, q, seq_lens, w.attn_scale, Lmax, out=out, workspace=ws,
+                                stream=stream)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -408,9 +416,10 @@ def run_paged(args, w: wl.Workload, kvq, torch, stream):
         "config": {"workload": f"{w.name}: batch {B}, {H} q / {KVH} kv heads, head_dim {D}, page size 16, "
                                f"lengths U[512, 32768] (seed {w.seed}: {int(lens.sum())} tokens), pages dealt "
                                f"from a shared arena in random order, per-token fp32 scales; append 1 token + "
-                               f"decode (one fused launch)",
+                               f"decode ({'two launches' if args.separate else 'one fused launch'})",
                    "batch": B, "seq_len": Lmax, "bytes_per_step": nb["step"]},
-        "roofline": {"bound": "hbm", "kernel": "kvq_append_decode",
+        "roofline": {"bound": "hbm", "kernel": "kvq_append + kvq_attention_decode" if args.separate
+                     else "kvq_append_decode",
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": nb["step"], "us_per_launch": round(step_ms * 1e3, 3)},

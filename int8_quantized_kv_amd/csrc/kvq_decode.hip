@@ -93,6 +93,12 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// f16 pair (1024 + c0, 1024 + c1) -> (c0 - 128, c1 - 128), exact.
+__device__ __forceinline__ uint32_t exact_pair(uint32_t w) {
+  const half2_t off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, w) + off);
+}
+
 __device__ __forceinline__ uint32_t f16_bits(float x) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
 }
@@ -355,29 +361,27 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   bool owns_new = false;  // fused append: this workgroup's split holds it
 
   uint32_t qp[HPW][8];
-  float fold[HPW];      // group-32: 128 * 2^-24 * (sum of this lane's scaled queries)
-  float fold_row[HPW];  // per-token: the same over the whole row (wave-uniform)
+  float fold_row[HPW];  // per-token: 128 * 2^-24 * (sum of the scaled queries), wave-uniform
   float cst[HPW];       // scale_log2 * 2^24 * 2^-kq (wave-uniform)
 
   // ---- state -------------------------------------------------------------------
   float o[HPW][8];
-  float m[HPW], l[HPW], ws[HPW][NG];
+  float m[HPW], l[HPW], ws[HPW][1];   // weight sums (for the -128 fold)
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.0f;
-#pragma unroll
-    for (int g = 0; g < NG; ++g) ws[j][g] = 0.0f;
+    ws[j][0] = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = 0.0f;
   }
 
   uint4 kb[NPK];
   uint2 vb[NPV];
-  float ksc[NPK];       // group-32: this lane's K group scale per pass
-  float s_k;            // per-token mode: K scale of this lane's softmax token
+  constexpr int kPidAhead = 4;  // paged: blocks of page ids held ahead (covers a 2048-token split)
+  int32_t pq[kPidAhead][kBlock / kPageSize] = {};
+  float s_k[NG];        // K scales of this lane's softmax token (per token or per group)
   float s_v[NG];        // V scales of this lane's softmax token
-  const int kgroup = G32 ? ksub / 2 : 0;
   const int vgroup = G32 ? vsub / 4 : 0;
   const int64_t seq_row0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.geom.max_len;
   const uint32_t koff = static_cast<uint32_t>(kslot * D + ksub * 16);   // lane's byte offset in a K pass
@@ -386,17 +390,44 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // ---- loads --------------------------------------------------------------------
   // A block whose 64 tokens all lie before t_end takes the fast path: the rows of
   // one pass are consecutive (contiguous layout) or lie in one 16-token page
-  // (paged layout, page ids read once per block as scalars), so a load is a
-  // uniform base plus a per-lane constant.  The last, partial block clamps every
-  // row into [t_begin, t_end) instead; its extra tokens are discarded through
-  // their -inf score and zero weight.  No load sits under a per-lane branch.
+  // (paged layout), so a load is a uniform base plus a per-lane constant.
+  // Page ids come from a queue of scalar registers filled kPidAhead blocks
+  // ahead with s_load (counted by lgkmcnt, so waiting for them never drains
+  // the vector loads in flight).  The last, partial block clamps every
+  // row into [t_begin, t_end) instead (paged layouts need no clamp: rows past
+  // the end still lie in the block's pages); the extra tokens are discarded
+  // through their -inf score and zero weight.  No load sits under a per-lane
+  // branch.
   constexpr bool kPassInPage = TK <= kPageSize && TV <= kPageSize;
-  auto page_row0 = [&](int s0, int tok) -> int64_t {   // row of token s0+tok's page slot 0 (uniform)
-    int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + ((s0 + tok) >> 4)];
+  constexpr int kPages = kBlock / kPageSize;          // pages per block
+  typedef const int32_t __attribute__((address_space(4))) const_i32;
+  const const_i32* bt_s = (const const_i32*)(p.geom.block_table);  // scalar loads
+  // page ids of block bi (uniform; ids past the table read as 0)
+  auto fetch_pids = [&](int bi, int32_t (&pid)[kPages]) {
+    const int blk0 = (t_begin + bi * kBlock) >> 4;
+#pragma unroll
+    for (int pg = 0; pg < kPages; ++pg)
+      pid[pg] = blk0 + pg < p.geom.max_blocks ? bt_s[static_cast<int64_t>(b) * p.geom.max_blocks + blk0 + pg] : 0;
+  };
+  auto page_row0 = [&](int32_t phys) -> int64_t {     // row of a page's slot 0 (uniform)
     phys = min(max(phys, 0), p.geom.num_pages - 1);
     return (static_cast<int64_t>(phys) * p.geom.kvh + kvh) * kPageSize;
   };
-  auto row_of = [&](int t) -> int64_t {                  // clamped per-lane row
+  // clamped per-lane row of token t of the block starting at s0 (whose page ids
+  // are pid): the clamp keeps t inside the block, so no table read is needed
+  auto block_row = [&](int s0, int t, const int32_t (&pid)[kPages]) -> int64_t {
+    t = min(t, t_end - 1);
+    if constexpr (PAGED) {
+      const int pg = (t - s0) >> 4;
+      int32_t my = pid[0];
+#pragma unroll
+      for (int k = 1; k < kPages; ++k) my = pg == k ? pid[k] : my;
+      return page_row0(my) + (t & (kPageSize - 1));
+    } else {
+      return seq_row0 + t;
+    }
+  };
+  auto row_of = [&](int t) -> int64_t {                  // clamped per-lane row (table read)
     t = min(t, t_end - 1);
     if constexpr (PAGED) {
       int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (t >> 4)];
@@ -407,64 +438,61 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     }
   };
   auto load_scales = [&](int64_t srow) {
-    if constexpr (G32) {
-      if constexpr (NG == 4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(p.v_scales + srow * NG);
-        s_v[0] = v4.x; s_v[1] = v4.y; s_v[2] = v4.z; s_v[3] = v4.w;
-      } else {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) s_v[g] = p.v_scales[srow * NG + g];
-      }
+    if constexpr (NG == 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(p.k_scales + srow * NG);
+      const float4 v4 = *reinterpret_cast<const float4*>(p.v_scales + srow * NG);
+      s_k[0] = k4.x; s_k[1] = k4.y; s_k[2] = k4.z; s_k[3] = k4.w;
+      s_v[0] = v4.x; s_v[1] = v4.y; s_v[2] = v4.z; s_v[3] = v4.w;
     } else {
-      s_k = p.k_scales[srow];
-      s_v[0] = p.v_scales[srow];
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        s_k[g] = p.k_scales[srow * NG + g];
+        s_v[g] = p.v_scales[srow * NG + g];
+      }
     }
   };
-  auto load_k = [&](int bi) {
+  // scales of the softmax token (token `lane`) of block bi
+  // (scales of rows past the end could be any bits, so their rows are clamped)
+  auto load_block_scales = [&](int bi, const int32_t (&pid)[kPages]) {
     const int s0 = t_begin + bi * kBlock;
-    if (s0 + kBlock <= t_end && (!PAGED || kPassInPage)) {
+    load_scales(block_row(s0, s0 + lane, pid));
+  };
+  auto load_k = [&](int bi, const int32_t (&pid)[kPages]) {
+    const int s0 = t_begin + bi * kBlock;
+    if (PAGED ? kPassInPage : s0 + kBlock <= t_end) {
       if constexpr (PAGED) {
-        int64_t r0[kBlock / kPageSize];
+        int64_t r0[kPages];
 #pragma unroll
-        for (int pg = 0; pg < kBlock / kPageSize; ++pg) r0[pg] = page_row0(s0, pg * kPageSize);
+        for (int pg = 0; pg < kPages; ++pg) r0[pg] = page_row0(pid[pg]);
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
           const int tok = i * TK;                          // first token of the pass
           const uint8_t* base = p.k_codes + (r0[tok >> 4] + (tok & 15)) * D;
           kb[i] = *reinterpret_cast<const uint4*>(base + koff);
-          if constexpr (G32) ksc[i] = p.k_scales[(r0[tok >> 4] + (tok & 15) + kslot) * NG + kgroup];
         }
-        int64_t srow = r0[0];
-#pragma unroll
-        for (int pg = 1; pg < kBlock / kPageSize; ++pg) srow = (lane >> 4) == pg ? r0[pg] : srow;
-        load_scales(srow + (lane & 15));
       } else {
         const int64_t r = seq_row0 + s0;
         const uint8_t* base = p.k_codes + r * D;
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
           kb[i] = *reinterpret_cast<const uint4*>(base + i * TK * D + koff);
-          if constexpr (G32) ksc[i] = p.k_scales[(r + i * TK + kslot) * NG + kgroup];
         }
-        load_scales(r + lane);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NPK; ++i) {
         const int64_t row = row_of(s0 + i * TK + kslot);
         kb[i] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + ksub * 16);
-        if constexpr (G32) ksc[i] = p.k_scales[row * NG + kgroup];
       }
-      load_scales(row_of(s0 + lane));
     }
   };
-  auto load_v = [&](int bi) {
+  auto load_v = [&](int bi, const int32_t (&pid)[kPages]) {
     const int s0 = t_begin + bi * kBlock;
-    if (s0 + kBlock <= t_end && (!PAGED || kPassInPage)) {
+    if (PAGED ? kPassInPage : s0 + kBlock <= t_end) {
       if constexpr (PAGED) {
-        int64_t r0[kBlock / kPageSize];
+        int64_t r0[kPages];
 #pragma unroll
-        for (int pg = 0; pg < kBlock / kPageSize; ++pg) r0[pg] = page_row0(s0, pg * kPageSize);
+        for (int pg = 0; pg < kPages; ++pg) r0[pg] = page_row0(pid[pg]);
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
           const int tok = i * TV;
@@ -498,16 +526,17 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         for (int i = 0; i < NPK; ++i) {
           if (i * TK + kslot == rel) {
             kb[i] = sm_nk[ksub];
-            if constexpr (G32) ksc[i] = sm_ns[0][kgroup];
           }
         }
 #pragma unroll
         for (int i = 0; i < NPV; ++i)
           if (i * TV + vslot == rel) vb[i] = sm_nv[vsub];
         if (lane == rel) {
-          if constexpr (!G32) s_k = sm_ns[0][0];
 #pragma unroll
-          for (int g = 0; g < NG; ++g) s_v[g] = sm_ns[1][g];
+          for (int g = 0; g < NG; ++g) {
+            s_k[g] = sm_ns[0][g];
+            s_v[g] = sm_ns[1][g];
+          }
         }
       }
     }
@@ -518,49 +547,53 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int w4 = 0; w4 < 4; ++w4) {
-        const uint32_t c01 = __builtin_amdgcn_perm(0u, kw[w4], 0x0C010C00u);
-        const uint32_t c23 = __builtin_amdgcn_perm(0u, kw[w4], 0x0C030C02u);
+        uint32_t c01, c23;
+        if constexpr (G32) {
+          // exact f16 c - 128: the group scale multiplies the partial later
+          c01 = exact_pair(__builtin_amdgcn_perm(0x64646464u, kw[w4], 0x04010400u));
+          c23 = exact_pair(__builtin_amdgcn_perm(0x64646464u, kw[w4], 0x04030402u));
+        } else {
+          c01 = __builtin_amdgcn_perm(0u, kw[w4], 0x0C010C00u);
+          c23 = __builtin_amdgcn_perm(0u, kw[w4], 0x0C030C02u);
+        }
 #pragma unroll
         for (int j = 0; j < HPW; ++j) {
           P[j] = dot2(qp[j][2 * w4], c01, P[j]);
           P[j] = dot2(qp[j][2 * w4 + 1], c23, P[j]);
         }
       }
-      if constexpr (G32) {
-#pragma unroll
-        for (int j = 0; j < HPW; ++j) P[j] = (P[j] - fold[j]) * ksc[i];
-      }
       sm_part[wave][ksub * kBlock + ((i * TK + kslot) ^ (ksub * kSwz))] = make_float4(P[0], P[1], P[2], P[3]);
     }
-    const float sk_cur = G32 ? 0.0f : s_k;
-    float sv_cur[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) sv_cur[g] = s_v[g];
-    if constexpr (PREFETCH) load_k(blk + kStreamWaves);
+    if constexpr (PREFETCH) load_k(blk + kStreamWaves, pq[1]);
     wave_lds_sync();
 
     // softmax: this lane owns token `lane` of the block
     const int t = t_begin + blk * kBlock + lane;
     const bool valid = t < t_end;
     float4 acc4 = sm_part[wave][lane ^ 0];
+    if constexpr (G32) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
 #pragma unroll
     for (int r = 1; r < LK; ++r) {
       const float4 v = sm_part[wave][r * kBlock + (lane ^ (r * kSwz))];
-      acc4.x += v.x; acc4.y += v.y; acc4.z += v.z; acc4.w += v.w;
+      if constexpr (G32) {
+        const float sg = s_k[r >> 1];  // k-lane r holds dims 16r..16r+15: group r / 2
+        acc4.x = fmaf(v.x, sg, acc4.x); acc4.y = fmaf(v.y, sg, acc4.y);
+        acc4.z = fmaf(v.z, sg, acc4.z); acc4.w = fmaf(v.w, sg, acc4.w);
+      } else {
+        acc4.x += v.x; acc4.y += v.y; acc4.z += v.z; acc4.w += v.w;
+      }
     }
     const float S[4] = {acc4.x, acc4.y, acc4.z, acc4.w};
-    float lsv[NG];
-    float lsv_max = -INFINITY;
+    // V scale of the token: per-token, or the largest of its groups (group-32)
+    float sv_top = s_v[0];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      lsv[g] = __log2f(sv_cur[g]);
-      lsv_max = fmaxf(lsv_max, lsv[g]);
-    }
+    for (int g = 1; g < NG; ++g) sv_top = fmaxf(sv_top, s_v[g]);
+    const float lsv_max = __log2f(sv_top);
     float Sh[HPW];
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
       // per-token scales fold the offset once for the whole row, then scale
-      const float dotv = G32 ? S[j] : (S[j] - fold_row[j]) * sk_cur;
+      const float dotv = G32 ? S[j] : (S[j] - fold_row[j]) * s_k[0];
       Sh[j] = valid ? dotv * cst[j] : -INFINITY;
     }
 #pragma unroll
@@ -572,35 +605,50 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         const float alpha = fast_exp2(m[j] - bm);
         m[j] = bm;
         l[j] *= alpha;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) ws[j][g] *= alpha;
+        ws[j][0] *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[j][e] *= alpha;
-      }
-    }
-    uint32_t wbits[HPW][NG];
-#pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-      l[j] += fast_exp2(Sh[j] - m[j]);  // -inf score: exactly 0
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        wbits[j][g] = f16_bits(fast_exp2(Sh[j] + lsv[g] - m[j] + static_cast<float>(kWeightShift)));
-        ws[j][g] += f16_value(wbits[j][g]);
       }
     }
     // token lane = V pass * TV + V slot; pair V passes (2k, 2k+1) of one slot:
     // the partner token sits TV lanes higher
     const bool even_pass = ((lane / TV) & 1) == 0;
+    const int wslot = ((lane / TV) >> 1) * TV + lane % TV;
+    if constexpr (G32) {
+      // w_g = 2^(S + log2 sV_g - m + 7) = E * (sV_g / sV_top) with
+      // E = 2^(S + log2 sV_top - m + 7) <= 2^15; the normaliser takes
+      // 2^(S - m) = E / (128 sV_top).  One exponential per head.
+      const float inv = 1.0f / sv_top;
+      float E[HPW];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
+      for (int j = 0; j < HPW; ++j) {
+        E[j] = fast_exp2(Sh[j] + lsv_max - m[j] + static_cast<float>(kWeightShift));  // -inf score: 0
+        l[j] = fmaf(E[j], inv * 0x1p-7f, l[j]);
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float r = s_v[g] * inv;
+        uint32_t word[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const uint32_t wb = f16_bits(E[j] * r);
+          word[j] = wb | (lane_up<TV>(wb) << 16);
+        }
+        if (even_pass) sm_w[wave][wslot * NG + g] = make_uint4(word[0], word[1], word[2], word[3]);
+      }
+    } else {
       uint32_t word[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) word[j] = wbits[j][g] | (lane_up<TV>(wbits[j][g]) << 16);
-      if (even_pass) {
-        const int pair = (lane / TV) >> 1;
-        sm_w[wave][(pair * TV + lane % TV) * NG + g] = make_uint4(word[0], word[1], word[2], word[3]);
+      for (int j = 0; j < HPW; ++j) {
+        l[j] += fast_exp2(Sh[j] - m[j]);  // -inf score: exactly 0
+        const uint32_t wb = f16_bits(fast_exp2(Sh[j] + lsv_max - m[j] + static_cast<float>(kWeightShift)));
+        ws[j][0] += f16_value(wb);
+        word[j] = wb | (lane_up<TV>(wb) << 16);
       }
+      if (even_pass) sm_w[wave][wslot] = make_uint4(word[0], word[1], word[2], word[3]);
     }
+    // the scales of this block are used up: fetch the next block's
+    if constexpr (PREFETCH) load_block_scales(blk + kStreamWaves, pq[1]);
     wave_lds_sync();
 
     // PV: token pairs, this lane's 8 dims, all heads
@@ -608,6 +656,10 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     for (int k = 0; k < NPAIR; ++k) {
       const uint4 wq = sm_w[wave][(k * TV + vslot) * NG + vgroup];
       const uint32_t wv[4] = {wq.x, wq.y, wq.z, wq.w};
+      if constexpr (G32) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) ws[j][0] = dot2(wv[j], 0x3C003C00u, ws[j][0]);  // f16 pair (1, 1)
+      }
       const uint32_t a2[2] = {vb[2 * k].x, vb[2 * k].y};
       const uint32_t b2[2] = {vb[2 * k + 1].x, vb[2 * k + 1].y};
 #pragma unroll
@@ -620,14 +672,37 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         }
       }
     }
-    if constexpr (PREFETCH) load_v(blk + kStreamWaves);
+    if constexpr (PREFETCH) load_v(blk + kStreamWaves, pq[1]);
+    if constexpr (PAGED) {  // advance the page-id queue
+#pragma unroll
+      for (int k = 0; k + 1 < kPidAhead; ++k)
+#pragma unroll
+        for (int pg = 0; pg < kPages; ++pg) pq[k][pg] = pq[k + 1][pg];
+      if (t_begin + (blk + kPidAhead * kStreamWaves) * kBlock < t_end) fetch_pids(blk + kPidAhead * kStreamWaves, pq[kPidAhead - 1]);
+    }
   };
 
   // the wave index is uniform, so every block condition below is a scalar branch
   int blk = wave;
+  // the length and the queries go out before the first block's K/V loads, so
+  // they do not queue behind the bulk traffic every workgroup starts with
+  const int len_raw = p.seq_lens[b];
+  uint4 qraw[HPW][2];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
+    qraw[j][0] = qptr[0];
+    qraw[j][1] = qptr[1];
+  }
+  if constexpr (PAGED) {
+#pragma unroll
+    for (int k = 0; k < kPidAhead; ++k)
+      if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
+  }
   if (t_begin + blk * kBlock < t_end) {  // speculative first block
-    load_k(blk);
-    load_v(blk);
+    load_k(blk, pq[0]);
+    load_v(blk, pq[0]);
+    load_block_scales(blk, pq[0]);
   }
   // fused append: waves 0 and 1 fetch the new K and V rows of this KV head
   constexpr int kEpl = row_epl(D);
@@ -638,7 +713,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
                       (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * esz;
     load_row_values<kEpl>(src, lane, wave < 2 && lane < D / kEpl, p.new_bf16 != 0, xnew);
   }
-  const int L = clamp_len(p, b);
+  const int L = len_raw < 0 ? 0 : (len_raw > p.len_cap ? p.len_cap : len_raw);
   if (L == 0 && split == 0) {  // empty window: the output is zero
     for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads)
       p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
@@ -684,9 +759,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     float qf[16];
-    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
-    bf16x8_to_f32(qptr[0], &qf[0]);
-    bf16x8_to_f32(qptr[1], &qf[8]);
+    bf16x8_to_f32(qraw[j][0], &qf[0]);
+    bf16x8_to_f32(qraw[j][1], &qf[8]);
     float a = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(qf[e]));
@@ -699,9 +773,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       qs += f16_value(b0) + f16_value(b1);
       qp[j][k] = b0 | (b1 << 16);
     }
-    fold[j] = qs * (128.0f * 0x1p-24f);
-    fold_row[j] = uniform(group_sum<LK>(fold[j]));
-    cst[j] = uniform(ldexpf(p.scale_log2, 24 - kq));
+    fold_row[j] = uniform(group_sum<LK>(qs * (128.0f * 0x1p-24f)));
+    cst[j] = uniform(ldexpf(p.scale_log2, (G32 ? 0 : 24) - kq));
   }
 
   for (; blk + kStreamWaves < nblk; blk += kStreamWaves) run_block(blk, std::true_type{});
@@ -711,21 +784,25 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     l[j] = wave_sum(l[j]);
+    // U = sum_t 2^(S + log2 sV - m) (c - 128) = 2^-7 (2^24 o - 128 sum w).
+    // Group-32: each V lane folds the weights it used (its group, its token
+    // slot) before the slot sum; per-token: the softmax lanes' sum, folded
+    // after it.
+    if constexpr (G32) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) ws[j][g] = wave_sum(ws[j][g]);
+      for (int e = 0; e < 8; ++e) o[j][e] = fmaf(o[j][e], 0x1p17f, -ws[j][0]);
+    } else {
+      ws[j][0] = wave_sum(ws[j][0]);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[j][e] = slot_sum<LV>(o[j][e]);
   }
   if (vslot == 0) {
 #pragma unroll
     for (int j = 0; j < HPW; ++j) {
-      // U = sum_t 2^(S + log2 sV - m) (c - 128) = 2^-7 (2^24 o - 128 sum w)
-      float wsum = ws[j][0];
-#pragma unroll
-      for (int g = 1; g < NG; ++g) wsum = (g == vgroup) ? ws[j][g] : wsum;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        sm_fo[wave][j][vsub * 8 + e] = o[j][e] * 0x1p17f - wsum * (128.0f * 0x1p-7f);
+        sm_fo[wave][j][vsub * 8 + e] = G32 ? o[j][e] : o[j][e] * 0x1p17f - ws[j][0];
       if (vsub == 0) {
         sm_fml[wave][j][0] = m[j];
         sm_fml[wave][j][1] = l[j];
@@ -1026,11 +1103,19 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   const int gqa = c.num_heads / c.num_kv_heads;
   pl.heads_per_wg = heads_per_wg(gqa);
   const int step = pass_tokens(c.head_dim);
-  // Aim at about one workgroup per compute unit, in whole workgroup passes,
-  // at most 2048 tokens per split so that ragged batches stay balanced.
+  // Aim at about one workgroup per compute unit (one round), in whole
+  // workgroup passes.  When one round would need splits longer than 2048
+  // tokens (large batches of long windows), take about four rounds instead,
+  // with splits of at most 16384 tokens: each workgroup spends a fixed few
+  // microseconds filling its pipeline and combining its waves, which long
+  // splits amortise, while ragged batches stay balanced across rounds.
   const int64_t groups = static_cast<int64_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
   int64_t want = (static_cast<int64_t>(max_seq_len) * groups + kCUs - 1) / kCUs;
-  want = want < 512 ? 512 : (want > 2048 ? 2048 : want);
+  if (want > 2048) {
+    want = (static_cast<int64_t>(max_seq_len) * groups + 4 * kCUs - 1) / (4 * kCUs);
+    want = want < 2048 ? 2048 : (want > 16384 ? 16384 : want);
+  }
+  want = want < 512 ? 512 : want;
   int split = static_cast<int>(want);
   const int forced_splits = env_int("KVQ_NUM_SPLITS", 0);
   const int forced_len = env_int("KVQ_SPLIT_LEN", 0);
