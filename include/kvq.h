@@ -158,15 +158,20 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const vo
  * cache.  With causal != 0 query i sees keys t <= ctx_lens[b] + i
  * (bottom-right alignment: abaddon kv_cache_quant_cuda.rs
  * `forward_attention`, cache_offset = seq_len - q_len; combs-models kv.rs
- * `attend`); otherwise all ctx_lens[b] + n keys.  bf16 MFMA on dequantized
- * tiles, fp32 accumulation, bf16 output.
+ * `attend`); otherwise all ctx_lens[b] + n keys.  Both products run on
+ * f16 MFMA with the codes as exact f16 values and the scales applied to the
+ * fp32 scores and weights; bf16 output.
  *
  *   q        : device bf16 [B, H, n, D];  out : device bf16 [B, H, n, D]
  *   ctx_lens : device int32 [B], tokens cached before the chunk
- *   max_ctx_len_hint : host upper bound on ctx_lens (sizes the launch)
- *   workspace: kvq_workspace_size(cache, max_ctx_len_hint + n, n) bytes
- * Errors: INVALID_ARG, OUT_OF_RANGE, WORKSPACE, UNSUPPORTED (head_dim != 128
- * or 64), HIP.
+ *   max_ctx_len_hint : host upper bound on ctx_lens; hint + n must fit the
+ *              capacity
+ *   workspace: kvq_workspace_size(cache, max_ctx_len_hint + n, n) bytes (the
+ *              current kernel needs none: the size is 0 and NULL is accepted)
+ * Keys beyond the cache capacity do not exist: a query sees at most
+ * min(ctx_lens[b] + n, capacity) keys.
+ * Errors: INVALID_ARG, OUT_OF_RANGE, WORKSPACE, UNSUPPORTED (head_dim other
+ * than 64 or 128, or group-32 scales), HIP.
  */
 kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_t n,
                                const int32_t* ctx_lens, int32_t causal, float attn_scale,
