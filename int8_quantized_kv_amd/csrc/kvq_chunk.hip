@@ -26,10 +26,15 @@
 //     score is one FMA: z_t = acc * kc_t + log2 sV_t.  The V scale rides in
 //     the exponent of the weight, w_t = 2^(z_t - m), and the normaliser sums
 //     w_t / sV_t.
-//   * one workgroup = 4 waves = 4 (query head, 32-position block) items of
-//     one KV head; the 64-token tile is staged once in LDS (double buffered,
-//     XOR-swizzled) and serves all four.  With H / KVH a multiple of 4 the
-//     four items share their positions.
+//   * one workgroup = 8 waves = 8 (query head, 32-position block) items of
+//     one KV head, in two groups of four; each 64-token tile is staged once in
+//     LDS (four buffers in rotation) and serves all eight.  With H / KVH a
+//     multiple of 4 each group's items share their positions.
+//   * the groups ping-pong: each wave alternates an MFMA step (the values of
+//     the previous tile, S of this one) and a vector step (this tile's
+//     softmax), with a workgroup barrier after each; group 1 runs one step
+//     behind, so the two waves that share a SIMD always do opposite kinds of
+//     work and the matrix cores overlap the exponentials.
 //   * the running maximum per query is lazy: accumulators are rescaled only
 //     when a score exceeds it by more than 2^8, so weights stay below 2^8.
 #include "kvq_internal.hpp"
@@ -45,9 +50,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 
-constexpr int kCkWaves = 4;
+constexpr int kCkWaves = 8;      // two groups of four, one wave of each per SIMD
+constexpr int kGroupWaves = 4;
 constexpr int kCkThreads = kCkWaves * kWave;
-constexpr int kQBlock = 32;   // query positions per wave
+constexpr int kCkTile = 64;     // tokens per tile
+constexpr int kCkBufs = 4;      // LDS tile buffers in rotation
+constexpr int kQBlock = 32;     // query positions per wave
 constexpr float kCkLog2e = 1.4426950408889634f;
 constexpr float kCkLazy = 8.0f;
 constexpr float kMinusBig = -1.0e30f;  // running-max start: finite, below any score
@@ -155,24 +163,24 @@ __device__ __forceinline__ int64_t row_of(const ChunkParams& p, int b, int g, in
 }
 
 template <int D, bool PAGED>
-__global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
-  constexpr int kTT = D == 128 ? 1 : 2;     // 32-token S tiles per pipeline stage
-  constexpr int kCkTile = 32 * kTT;         // tokens per pipeline stage
+__global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   using TL = Tile<D, kCkTile>;
-  constexpr int kChunksPerRow = D / 16;                          // 16-code pieces per row
-  constexpr int kLoads = kCkTile * kChunksPerRow / kCkThreads;   // per side per thread
-  constexpr int kKK = D / 16;                                    // MFMA k-steps for S
-  constexpr int kDT = D / 32;                                    // 32-wide d tiles of O
-  static_assert(kLoads >= 1, "tile loader");
+  constexpr int kTT = kCkTile / 32;                        // 32-token S tiles per tile
+  constexpr int kChunksPerRow = D / 16;                    // 16-code pieces per row
+  constexpr int kChunks = kCkTile * kChunksPerRow;         // per side per tile
+  constexpr int kLoads = (2 * kChunks + kCkThreads - 1) / kCkThreads;  // pieces per thread
+  constexpr int kKK = D / 16;                              // MFMA k-steps for S
+  constexpr int kDT = D / 32;                              // 32-wide d tiles of O
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[3 * TL::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kCkBufs * TL::kBytes];
   __shared__ float sm_qmax[kCkWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int col = lane & 31;   // query column of this lane
-  const int half = lane >> 5;  // which 8 of each 16 k-slots
+  const int grp = wave / kGroupWaves;   // 0: leads, 1: one phase behind
+  const int col = lane & 31;            // query column of this lane
+  const int half = lane >> 5;           // which 8 of each 16 k-slots
 
   // Consecutive blockIdx land on different XCDs; give each XCD a contiguous
   // range of logical ids so the workgroups of one KV head share an L2.
@@ -188,20 +196,21 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
   const int Ltot = min(L0 + p.n, cap);   // keys that exist
   const int items = p.hpg * p.nblk;
 
-  auto wave_end = [&](int w) -> int {
+  int wg_end = 0;
+#pragma unroll
+  for (int w = 0; w < kCkWaves; ++w) {
     const int it = wg * kCkWaves + w;
-    if (it >= items) return 0;
-    const int pb = (it / p.hpg) * kQBlock;
-    return p.causal ? min(L0 + pb + kQBlock, Ltot) : Ltot;
-  };
-  const int wg_end = max(max(wave_end(0), wave_end(1)), max(wave_end(2), wave_end(3)));
+    if (it < items) {
+      const int pb = (it / p.hpg) * kQBlock;
+      wg_end = max(wg_end, p.causal ? min(L0 + pb + kQBlock, Ltot) : Ltot);
+    }
+  }
   const int ntiles = (wg_end + kCkTile - 1) / kCkTile;
 
   const int item = wg * kCkWaves + wave;
   const bool active = item < items;
   const int head = g * p.hpg + (active ? item % p.hpg : 0);
   const int pos0 = active ? (item / p.hpg) * kQBlock : 0;
-  const int my_end = wave_end(wave);
   const int qi = pos0 + col;
   const bool q_ok = active && qi < p.n;
 
@@ -224,20 +233,26 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
     if (lane == 0) sm_qmax[wave] = amax;
   }
 
-  // ---- tile loader: 16-code pieces of K and V rows plus per-token scales
-  uint4 kreg[kLoads], vreg[kLoads];
+  // ---- tile loader: piece j of a tile (j < kChunks: K, else V) is held by
+  // thread j % kCkThreads; threads 0..2*kCkTile-1 also hold the per-token
+  // scales (first half K, second half V)
+  const bool ld_s = tid < 2 * kCkTile;
+  uint4 lreg[kLoads];
   float sreg = 0.0f;
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int id = tid + i * kCkThreads;
-      int t = t0 + id / kChunksPerRow;
-      t = t < Ltot ? t : Ltot - 1;
-      const int64_t row = row_of<PAGED>(p, b, g, t);
-      kreg[i] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + 16 * (id % kChunksPerRow));
-      vreg[i] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + 16 * (id % kChunksPerRow));
+      const int j = tid + i * kCkThreads;
+      if (j < 2 * kChunks) {
+        const bool kside = j < kChunks;
+        const int id = kside ? j : j - kChunks;
+        int t = t0 + id / kChunksPerRow;
+        t = t < Ltot ? t : Ltot - 1;
+        const int64_t row = row_of<PAGED>(p, b, g, t);
+        lreg[i] = *reinterpret_cast<const uint4*>((kside ? p.k_codes : p.v_codes) + row * D + 16 * (id % kChunksPerRow));
+      }
     }
-    if (tid < 2 * kCkTile) {
+    if (ld_s) {
       const int t = t0 + (tid & (kCkTile - 1));
       if (t < Ltot) {
         const int64_t row = row_of<PAGED>(p, b, g, t);
@@ -248,32 +263,30 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
   auto store_tile = [&](uint8_t* buf, int t0, float kfac) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int id = tid + i * kCkThreads;
-      const int r = id / kChunksPerRow;
-      const int c = id % kChunksPerRow;
-      // K: 16 codes -> 16 exact f16 values = units 2c and 2c + 1
-      const uint2 k0 = codes_exact_f16(kreg[i].x), k1 = codes_exact_f16(kreg[i].y);
-      const uint2 k2 = codes_exact_f16(kreg[i].z), k3 = codes_exact_f16(kreg[i].w);
-      *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
-      *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c + 1)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
-      // V: codes, 8-byte units 2c and 2c + 1 (one 16-byte store; halves
-      // swap when the permutation flips the low unit bit)
-      const int f = TL::vswz(r);
-      uint4 vv = vreg[i];
-      if (f & 1) vv = make_uint4(vv.z, vv.w, vv.x, vv.y);
-      *reinterpret_cast<uint4*>(buf + TL::kKBytes + r * D + 8 * ((2 * c) ^ (f & ~1))) = vv;
+      const int j = tid + i * kCkThreads;
+      if (j < kChunks) {  // K: 16 codes -> 16 exact f16 values = units 2c and 2c + 1
+        const int r = j / kChunksPerRow, c = j % kChunksPerRow;
+        const uint2 k0 = codes_exact_f16(lreg[i].x), k1 = codes_exact_f16(lreg[i].y);
+        const uint2 k2 = codes_exact_f16(lreg[i].z), k3 = codes_exact_f16(lreg[i].w);
+        *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c + 1)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
+      } else if (j < 2 * kChunks) {  // V: codes, 8-byte units 2c and 2c + 1 (halves swap with the low unit bit)
+        const int id = j - kChunks;
+        const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+        const int f = TL::vswz(r);
+        uint4 vv = lreg[i];
+        if (f & 1) vv = make_uint4(vv.z, vv.w, vv.x, vv.y);
+        *reinterpret_cast<uint4*>(buf + TL::kKBytes + r * D + 8 * ((2 * c) ^ (f & ~1))) = vv;
+      }
     }
-    if (tid < 2 * kCkTile) {
+    if (ld_s) {
       const int tl = tid & (kCkTile - 1);
       const bool ok = t0 + tl < Ltot;
-      float* kc = reinterpret_cast<float*>(buf + TL::kKc);
-      float* lsv = reinterpret_cast<float*>(buf + TL::kLsv);
-      float* rsv = reinterpret_cast<float*>(buf + TL::kRsv);
       if (tid < kCkTile) {
-        kc[tl] = ok ? sreg * kfac : 0.0f;
+        reinterpret_cast<float*>(buf + TL::kKc)[tl] = ok ? sreg * kfac : 0.0f;
       } else {
-        lsv[tl] = ok ? __builtin_amdgcn_logf(sreg) : -INFINITY;
-        rsv[tl] = ok ? 1.0f / sreg : 0.0f;
+        reinterpret_cast<float*>(buf + TL::kLsv)[tl] = ok ? __builtin_amdgcn_logf(sreg) : -INFINITY;
+        reinterpret_cast<float*>(buf + TL::kRsv)[tl] = ok ? 1.0f / sreg : 0.0f;
       }
     }
   };
@@ -283,7 +296,9 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
 
   int kq = 0;
   {
-    const float amax = fmaxf(fmaxf(sm_qmax[0], sm_qmax[1]), fmaxf(sm_qmax[2], sm_qmax[3]));
+    float amax = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kCkWaves; ++w) amax = fmaxf(amax, sm_qmax[w]);
     if (amax > 0.0f && amax <= 3.0e38f) {
       int ex;
       (void)frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
@@ -305,25 +320,22 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
     qop[kk] = v;
   }
 
-  // Pipeline: tiles j and j + 1 are in LDS when iteration j starts; it loads
-  // tile j + 2, multiplies S for tile j + 1 while it turns the scores of tile j
-  // into weights, accumulates tile j's values, then stores tile j + 2.  Three
-  // LDS buffers rotate.  Waves past their last visible key still run: every
-  // key they see there is masked, so nothing is added.
+  // Prologue: tiles 0 and 1 in LDS, tile 2 in flight.
   store_tile(smem, 0, kfac);
   if (ntiles > 1) {
     load_tile(kCkTile);
     store_tile(smem + TL::kBytes, kCkTile, kfac);
   }
+  if (ntiles > 2) load_tile(2 * kCkTile);
   __syncthreads();
 
-  // V transpose read: lane 16*grp + r names token 16ks + pi(grp/2, r/2) and
-  // unit 4dt + 2(grp%2) + r%2, where pi(h, e) = 8(e/4) + 4h + e%4 is the
+  // V transpose read: lane 16*r4 + r names token 16ks + pi(r4/2, r/2) and
+  // unit 4dt + 2(r4%2) + r%2, where pi(h, e) = 8(e/4) + 4h + e%4 is the
   // token of k-slot 8h + e in the S^T C layout.
-  const int grp = lane >> 4;
+  const int r4 = lane >> 4;
   const int r16 = lane & 15;
-  const int vtok = 8 * ((r16 >> 1) >> 2) + 4 * (grp >> 1) + ((r16 >> 1) & 3);
-  const int vunit = 2 * (grp & 1) + (r16 & 1);
+  const int vtok = 8 * ((r16 >> 1) >> 2) + 4 * (r4 >> 1) + ((r16 >> 1) & 3);
+  const int vunit = 2 * (r4 & 1) + (r16 & 1);
   const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
 
   f32x16 oacc[kDT];
@@ -332,49 +344,70 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
   float m_run = kMinusBig;
   float l_run = 0.0f;   // sum of w / sV over this lane's tokens
   float w_run = 0.0f;   // sum of the f16 weights over this lane's tokens
+  f32x16 s[kTT];        // S^T of the tile whose softmax comes next
+  f16x8 pw[kTT][2];     // weights of the tile whose values come next
+#pragma unroll
+  for (int tt = 0; tt < kTT; ++tt) {
+    s[tt] = f32x16{};
+    pw[tt][0] = f16x8{};
+    pw[tt][1] = f16x8{};
+  }
 
-  // S^T for the tile in `buf` (rows = tokens 32tt + 8(r/4) + 4*half + r%4,
-  // column = query), k-steps [K0, K1).
-  auto qk = [&](const uint8_t* buf, f32x16 (&s)[kTT], auto k0c, auto k1c) {
-    constexpr int K0 = decltype(k0c)::value, K1 = decltype(k1c)::value;
-    f16x8 ka[kTT];
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) ka[tt] = *reinterpret_cast<const f16x8*>(buf + TL::k_off(32 * tt + col, 2 * K0 + half));
-#pragma unroll
-    for (int kk = K0; kk < K1; ++kk) {
-      f16x8 na[kTT];
-#pragma unroll
-      for (int tt = 0; tt < kTT; ++tt)
-        na[tt] = kk + 1 < K1 ? *reinterpret_cast<const f16x8*>(buf + TL::k_off(32 * tt + col, 2 * (kk + 1) + half))
-                             : ka[tt];
+  // Ping-pong.  Each wave runs, per tile t, an MFMA step (the values of tile
+  // t - 1 and S for tile t) and a vector step (the softmax of tile t), each
+  // closed by a workgroup barrier.  Group 1 starts one barrier later, so the
+  // two waves sharing a SIMD always run opposite kinds of work.  In global
+  // phase 2t + 1 (group 0's vector step, group 1's MFMA step) the loader
+  // stores tile t + 2 and fetches tile t + 3: tile t + 2's buffer last held
+  // tile t - 2, whose last reader (group 1's values, phase 2t - 1) is past.
+  // Waves past their last visible key still run: every key they see there is
+  // masked, so nothing is added.
+  auto mfma_step = [&](int t) {
+    __builtin_amdgcn_s_setprio(1);
+    {  // values of tile t - 1 (all-zero weights before the first tile)
+      const uint8_t* bv = smem + ((t + kCkBufs - 1) % kCkBufs) * TL::kBytes;
 #pragma unroll
       for (int tt = 0; tt < kTT; ++tt) {
-        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[tt], qop[kk], s[tt], 0, 0, 0);
-        ka[tt] = na[tt];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int tok = 32 * tt + 16 * ks + vtok;
+#pragma unroll
+          for (int dt = 0; dt < kDT; ++dt) {
+            const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (v2i __attribute__((address_space(3)))*)(bv + TL::v_off(tok, 4 * dt + vunit)));
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                codes_tiny_f16(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)), pw[tt][ks], oacc[dt], 0, 0, 0);
+          }
+        }
       }
     }
+    {  // S^T of tile t: rows = tokens 32tt + 8(r/4) + 4*half + r%4, column = query
+      const uint8_t* bk = smem + (t % kCkBufs) * TL::kBytes;
+      f16x8 ka[kTT];
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        s[tt] = f32x16{};
+        ka[tt] = *reinterpret_cast<const f16x8*>(bk + TL::k_off(32 * tt + col, half));
+      }
+#pragma unroll
+      for (int kk = 0; kk < kKK; ++kk) {
+        f16x8 na[kTT];
+#pragma unroll
+        for (int tt = 0; tt < kTT; ++tt)
+          na[tt] = kk + 1 < kKK ? *reinterpret_cast<const f16x8*>(bk + TL::k_off(32 * tt + col, 2 * (kk + 1) + half))
+                                : ka[tt];
+#pragma unroll
+        for (int tt = 0; tt < kTT; ++tt) {
+          s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[tt], qop[kk], s[tt], 0, 0, 0);
+          ka[tt] = na[tt];
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
-
-  f32x16 s_cur[kTT];
-#pragma unroll
-  for (int tt = 0; tt < kTT; ++tt) s_cur[tt] = f32x16{};
-  qk(smem, s_cur, std::integral_constant<int, 0>{}, std::integral_constant<int, kKK>{});
-
-  auto iter = [&](auto curc, int it) {
-    constexpr int CUR = decltype(curc)::value;
-    constexpr int NXT = (CUR + 1) % 3, FUT = (CUR + 2) % 3;
-    const uint8_t* bc = smem + CUR * TL::kBytes;
-    const uint8_t* bn = smem + NXT * TL::kBytes;
-    const int t0 = it * kCkTile;
-    const bool fut = it + 2 < ntiles;
-    if (fut) load_tile(t0 + 2 * kCkTile);
-
-    // S for tile j + 1 (first half of the k-steps) beside the scores of tile j
-    f32x16 s_nxt[kTT];
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) s_nxt[tt] = f32x16{};
-    qk(bn, s_nxt, std::integral_constant<int, 0>{}, std::integral_constant<int, kKK / 2>{});
-
+  auto softmax_step = [&](int t) {
+    const int t0 = t * kCkTile;
+    const uint8_t* bc = smem + (t % kCkBufs) * TL::kBytes;
     const float* kc = reinterpret_cast<const float*>(bc + TL::kKc);
     const float* lsv = reinterpret_cast<const float*>(bc + TL::kLsv);
     const float* rsv = reinterpret_cast<const float*>(bc + TL::kRsv);
@@ -386,10 +419,10 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
         const int tl = 32 * tt + 8 * q4 + 4 * half;
         const float4 a = *reinterpret_cast<const float4*>(kc + tl);
         const float4 c = *reinterpret_cast<const float4*>(lsv + tl);
-        z[tt][4 * q4 + 0] = fmaf(s_cur[tt][4 * q4 + 0], a.x, c.x);
-        z[tt][4 * q4 + 1] = fmaf(s_cur[tt][4 * q4 + 1], a.y, c.y);
-        z[tt][4 * q4 + 2] = fmaf(s_cur[tt][4 * q4 + 2], a.z, c.z);
-        z[tt][4 * q4 + 3] = fmaf(s_cur[tt][4 * q4 + 3], a.w, c.w);
+        z[tt][4 * q4 + 0] = fmaf(s[tt][4 * q4 + 0], a.x, c.x);
+        z[tt][4 * q4 + 1] = fmaf(s[tt][4 * q4 + 1], a.y, c.y);
+        z[tt][4 * q4 + 2] = fmaf(s[tt][4 * q4 + 2], a.z, c.z);
+        z[tt][4 * q4 + 3] = fmaf(s[tt][4 * q4 + 3], a.w, c.w);
       }
     }
     if (p.causal && t0 + kCkTile - 1 > L0 + pos0) {  // tile reaches the diagonal
@@ -416,54 +449,46 @@ __global__ __launch_bounds__(kCkThreads, 2) void chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
     }
-
-    // rest of S for tile j + 1, beside the weights and values of tile j
-    qk(bn, s_nxt, std::integral_constant<int, kKK / 2>{}, std::integral_constant<int, kKK>{});
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
-      float w[16];
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 rv = *reinterpret_cast<const float4*>(rsv + 32 * tt + 8 * q4 + 4 * half);
-        const float rvv[4] = {rv.x, rv.y, rv.z, rv.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[4 * q4 + e] = __builtin_amdgcn_exp2f(z[tt][4 * q4 + e] - m_run);
-          l_run = fmaf(w[4 * q4 + e], rvv[e], l_run);
-        }
-      }
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        f16x8 pw;
+        const float4 r0 = *reinterpret_cast<const float4*>(rsv + 32 * tt + 16 * ks + 4 * half);
+        const float4 r1 = *reinterpret_cast<const float4*>(rsv + 32 * tt + 16 * ks + 8 + 4 * half);
+        const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          w[e] = __builtin_amdgcn_exp2f(z[tt][8 * ks + e] - m_run);
+          l_run = fmaf(w[e], rv[e], l_run);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const f16x2 h2 = pack2(w[8 * ks + 2 * e], w[8 * ks + 2 * e + 1]);
+          const f16x2 h2 = pack2(w[2 * e], w[2 * e + 1]);
           w_run = dot2(h2, ones, w_run);
-          pw[2 * e] = h2[0];
-          pw[2 * e + 1] = h2[1];
-        }
-        const int tok = 32 * tt + 16 * ks + vtok;
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (v2i __attribute__((address_space(3)))*)(bc + TL::v_off(tok, 4 * dt + vunit)));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              codes_tiny_f16(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)), pw, oacc[dt], 0, 0, 0);
+          pw[tt][ks][2 * e] = h2[0];
+          pw[tt][ks][2 * e + 1] = h2[1];
         }
       }
     }
-#pragma unroll
-    for (int tt = 0; tt < kTT; ++tt) s_cur[tt] = s_nxt[tt];
-
-    if (fut) store_tile(smem + FUT * TL::kBytes, t0 + 2 * kCkTile, kfac);
-    __syncthreads();
+  };
+  auto loader_step = [&](int t) {
+    if (t + 2 < ntiles) store_tile(smem + ((t + 2) % kCkBufs) * TL::kBytes, (t + 2) * kCkTile, kfac);
+    if (t + 3 < ntiles) load_tile((t + 3) * kCkTile);
   };
 
-  for (int it = 0; it < ntiles; it += 3) {
-    iter(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < ntiles) iter(std::integral_constant<int, 1>{}, it + 1);
-    if (it + 2 < ntiles) iter(std::integral_constant<int, 2>{}, it + 2);
+  if (grp == 1) __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    mfma_step(t);
+    if (grp == 1) loader_step(t);
+    __syncthreads();
+    softmax_step(t);
+    if (grp == 0) loader_step(t);
+    __syncthreads();
   }
+  mfma_step(ntiles);  // values of the last tile (its S product is unused)
+  __syncthreads();
+  if (grp == 0) __syncthreads();
 
   // ---- normalise and store: lane holds query qi, d = 32dt + 8(r/4) + 4*half + r%4
   if (!q_ok) return;
