@@ -47,12 +47,12 @@ def log(msg):
 
 def recorded_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-    summarised in profiles/, or None when they were taken on another workload
-    or the kernel's sources have changed since."""
+    summarised in profiles/ (one record per workload), or None when none was
+    taken for this kernel on this workload or its sources have changed since."""
     import hashlib
     try:
-        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[kernel]
-        if rec["workload"] != workload:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))[workload]
+        if rec["kernel"] != kernel:
             return None
         h = hashlib.sha256()
         for src in rec["sources"]:
@@ -319,7 +319,8 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
                    "batch": B, "seq_len": T, "flops_per_step": cnt["flops"], "bytes_per_step": cnt["step_bytes"]},
         "roofline": {"bound": "mfma", "kernel": "kvq_attention_chunk",
                      "achieved": round(k_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic("kvq_attention_chunk", w.name),
                      "flops_per_launch": cnt["flops"], "us_per_launch": round(k_ms * 1e3, 3)},
         "cpu_baseline": cpu,
     }
@@ -421,7 +422,8 @@ def run_paged(args, w: wl.Workload, kvq, torch, stream):
         "roofline": {"bound": "hbm", "kernel": "kvq_append + kvq_attention_decode" if args.separate
                      else "kvq_append_decode",
                      "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if args.separate else recorded_traffic("kvq_append_decode", w.name),
                      "bytes_per_launch": nb["step"], "us_per_launch": round(step_ms * 1e3, 3)},
         "cpu_baseline": cpu,
     }

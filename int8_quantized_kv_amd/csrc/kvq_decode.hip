@@ -46,6 +46,7 @@ constexpr int kStreamWaves = 8;    // waves per workgroup (streaming kernel): 2 
 constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kCUs = 256;          // MI355X compute units: the split heuristic aims at one workgroup each
 constexpr int kBlock = 64;         // tokens per wave block (streaming kernel)
+constexpr int kLongestFirstMax = kStreamThreads;  // largest batch ranked by length in a workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazy = 8.0f;      // log2 headroom before a rescale
 constexpr int kWeightShift = 7;    // weights carry 2^7 so they fill f16 range
@@ -73,6 +74,7 @@ struct DecodeParams {
   int32_t num_splits;
   int32_t len_cap;           // min(hint, capacity)
   int32_t wg_per_kvh;        // workgroups sharing one KV head (GQA group / HPW)
+  int32_t longest_first;     // workgroup z takes the z-th longest sequence (batch <= kLongestFirstMax)
   float scale_log2;          // attn_scale * log2(e)
 };
 
@@ -200,6 +202,38 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   return L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
 }
 
+// The sequence a workgroup serves.  With longest_first set (batch at most NT),
+// workgroup z takes the z-th longest sequence, ties in index order: when the
+// grid runs in several rounds the long sequences start first and the ragged
+// end of the launch is made of short ones.  Each (sequence, head) result is
+// the same whichever workgroup computes it.  `scratch` is NT ints of LDS
+// that no wave writes before it has returned from here.  `len` receives the
+// sequence's clamped length when the ranking has read it, else -1.
+template <int NT>
+__device__ __forceinline__ int sequence_of(const DecodeParams& p, int* scratch, int& len) {
+  const int z = blockIdx.z;
+  len = -1;
+  if (!p.longest_first) return z;
+  __shared__ int sm_seq;
+  const int nb = gridDim.z;
+  const int t = threadIdx.x;
+  const int lt = t < nb ? clamp_len(p, t) : 0;
+  scratch[t] = lt;
+  __syncthreads();
+  if (t < nb) {
+    int r = 0;  // sequences ahead of t
+    for (int j = 0; j < nb; ++j) {
+      const int lj = scratch[j];
+      r += (lj > lt) | ((lj == lt) & (j < t));
+    }
+    if (r == z) sm_seq = t;  // the ranks are a permutation of 0..nb-1
+  }
+  __syncthreads();
+  const int b = __builtin_amdgcn_readfirstlane(sm_seq);
+  len = __builtin_amdgcn_readfirstlane(scratch[b]);
+  return b;
+}
+
 // ---------------------------------------------------------------------------
 // Final output of HPW heads from the workgroup's own combined partial, or,
 // when several splits exist, by the last workgroup to arrive.  `acc` / `msum`
@@ -232,11 +266,16 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
       __hip_atomic_store(&p.part_ml[pidx * 2 + 1], sm_ml[j][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  // every wave's stores have completed before the split is counted
+  // Every wave's partial stores have completed before the split is counted.
+  // A workgroup-scope release emits no wait for global stores, and an
+  // agent-scope one adds a write-back of the whole L2; the partials are
+  // agent-scope (write-through) stores, so waiting for their acknowledgement
+  // (vmcnt 0; expcnt and lgkmcnt left at their maxima) is what is needed.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int32_t* cnt = p.counters + static_cast<int64_t>(b) * gridDim.y + hg;
+    int32_t* cnt = p.counters + static_cast<int64_t>(b) * gridDim.x + hg;  // grid x = head groups
     const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = old == ns - 1;
     if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all splits counted
@@ -341,9 +380,13 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   __shared__ uint2 sm_nv[D / 8];                     // fused append: new V codes
   __shared__ float sm_ns[2][NG];                     // fused append: new K / V scales
 
-  const int split = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+  // Consecutive workgroup ids go to consecutive XCDs, so the head group varies
+  // fastest: each XCD then receives one head group of every (sequence, split),
+  // the same token count whatever the mix of lengths.
+  const int hg = blockIdx.x;
+  const int split = blockIdx.y;
+  int known_len;  // (the ranking's scratch lies in wave 0's score staging)
+  const int b = sequence_of<kStreamThreads>(p, reinterpret_cast<int*>(&sm_part[0][0]), known_len);
   const int H = p.num_heads;
   const int kvh = hg / p.wg_per_kvh;
   const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
@@ -356,7 +399,9 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // Until seq_lens[b] arrives, t_end is only bounded by the launch: the first
   // block's loads go out against that bound (rows past the real end are valid
   // memory and are masked later), overlapping the length and query loads.
-  int t_end = min(p.len_cap, t_begin + p.split_len);
+  // A length already read by the ranking bounds them (an empty split loads
+  // nothing).
+  int t_end = min(known_len >= 0 ? known_len : p.len_cap, t_begin + p.split_len);
   int pn = -1;            // fused append: position of the new row (set once the length is known)
   bool owns_new = false;  // fused append: this workgroup's split holds it
 
@@ -418,10 +463,13 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   auto block_row = [&](int s0, int t, const int32_t (&pid)[kPages]) -> int64_t {
     t = min(t, t_end - 1);
     if constexpr (PAGED) {
+      // the ids are uniform: reading them through readfirstlane makes the
+      // per-lane choice a select of values, which the optimiser would otherwise
+      // turn into a load at a per-lane index (forcing the queue out of registers)
       const int pg = (t - s0) >> 4;
-      int32_t my = pid[0];
+      int32_t my = __builtin_amdgcn_readfirstlane(pid[0]);
 #pragma unroll
-      for (int k = 1; k < kPages; ++k) my = pg == k ? pid[k] : my;
+      for (int k = 1; k < kPages; ++k) my = pg == k ? __builtin_amdgcn_readfirstlane(pid[k]) : my;
       return page_row0(my) + (t & (kPageSize - 1));
     } else {
       return seq_row0 + t;
@@ -851,9 +899,9 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   __shared__ float sm_m[kWaves][HPW];
   __shared__ float sm_l[kWaves][HPW];
 
-  const int split = blockIdx.x;
-  const int hg = blockIdx.y;
-  const int b = blockIdx.z;
+  const int hg = blockIdx.x;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;  // the launch never sets longest_first for this kernel
   const int kvh = hg / p.wg_per_kvh;
   const int H = p.num_heads;
   const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
@@ -1111,7 +1159,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   // splits amortise, while ragged batches stay balanced across rounds.
   const int64_t groups = static_cast<int64_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
   int64_t want = (static_cast<int64_t>(max_seq_len) * groups + kCUs - 1) / kCUs;
-  if (want > 2048) {
+  if (want > 2048) {  // several rounds
     want = (static_cast<int64_t>(max_seq_len) * groups + 4 * kCUs - 1) / (4 * kCUs);
     want = want < 2048 ? 2048 : (want > 16384 ? 16384 : want);
   }
@@ -1126,6 +1174,12 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   pl.split_len = split;
   pl.num_splits = (max_seq_len + split - 1) / split;
   if (pl.num_splits < 1) pl.num_splits = 1;
+  // Longest sequence first pays when workgroups are long (several rounds of
+  // splits of 4096 tokens or more): ranking the lengths costs each workgroup
+  // a read of the batch's lengths and about batch compare steps up front.
+  pl.longest_first = use_stream(c.head_dim) && c.batch > 1 && c.batch <= kLongestFirstMax && split >= 4096;
+  const int forced_lf = env_int("KVQ_LONGEST_FIRST", -1);
+  if (forced_lf >= 0) pl.longest_first = forced_lf != 0 && use_stream(c.head_dim) && c.batch <= kLongestFirstMax;
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
   pl.counter_bytes = align_up(static_cast<size_t>(groups) * sizeof(int32_t), 256);
   pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
@@ -1169,8 +1223,9 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   p.len_cap = max_seq_len < cap ? max_seq_len : cap;
   const int gqa = c.num_heads / c.num_kv_heads;
   p.wg_per_kvh = gqa / plan.heads_per_wg;
+  p.longest_first = plan.longest_first && stream_kernel ? 1 : 0;
   p.scale_log2 = attn_scale * kLog2e;
-  dim3 grid(plan.num_splits, c.num_kv_heads * p.wg_per_kvh, c.batch);
+  dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, c.batch);
   if (grid.y > 65535 || grid.z > 65535)
     return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_decode: grid too large");
   const bool g32 = c.scale_mode == KVQ_SCALE_GROUP32;

@@ -45,6 +45,7 @@ struct DecodePlan {
   int heads_per_wg;   // query heads sharing one K/V read (a divisor of H/KVH)
   int split_len;      // tokens per split (multiple of the kernel's pass size)
   int num_splits;     // splits per sequence for the hinted length
+  bool longest_first; // workgroups take sequences in order of decreasing length
   size_t counter_bytes;  // leading bytes of the workspace holding split counters
   size_t workspace;   // bytes of counters + split partials
 };

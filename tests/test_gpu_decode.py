@@ -181,3 +181,39 @@ def test_large_scores_lazy_rescale(kvq):
     got = _decode(cache, qb, [L], 1.0 / np.sqrt(D), L)
     ref = _oracle_decode(k, v, qv, [L], 1.0 / np.sqrt(D), 0)
     assert_attention_close(got, ref, "growing scores")
+
+
+@pytest.mark.parametrize("paged,fused", [(False, False), (True, False), (False, True), (True, True)])
+def test_longest_first_order(kvq, monkeypatch, paged, fused):
+    """Workgroups that take sequences longest first (ties, an empty sequence
+    and several splits per sequence included) give the same bits as the
+    natural order, and match the oracle."""
+    import torch
+    log(f"decode: longest-first order paged={paged} fused={fused}")
+    lens = [700, 3, 1500, 700, 0, 1499, 64, 1500, 65]
+    B, H, KVH, D = len(lens), 32, 8, 128
+    T = max(lens)
+    rng = np.random.default_rng(21 + 2 * paged + fused)
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "bf16")
+    qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, D))
+    scale = 1.0 / np.sqrt(D)
+    lens_np = np.asarray(lens, np.int32)
+    idx = np.maximum(lens_np - 1, 0)
+    k_new = np.ascontiguousarray(x["k_raw"][np.arange(B), :, idx][:, :, None, :])
+    v_new = np.ascontiguousarray(x["v_raw"][np.arange(B), :, idx][:, :, None, :])
+    monkeypatch.setenv("KVQ_SPLIT_LEN", "512")
+    outs = {}
+    for lf in ("0", "1"):
+        monkeypatch.setenv("KVQ_LONGEST_FIRST", lf)
+        cache = _build(kvq, x["k_raw"], x["v_raw"], H, 0, paged=paged, rng=np.random.default_rng(5))
+        if fused:
+            out = cache.append_decode(kv_dev(k_new), kv_dev(v_new), bf16_dev(qb), dev_tensor(lens_np), scale, T)
+            torch.cuda.synchronize()
+            outs[lf] = to_host_bits(out)
+        else:
+            outs[lf] = _decode(cache, qb, lens, scale, T)
+    assert np.array_equal(outs["0"], outs["1"])
+    live = lens_np > 0
+    assert np.all(outs["1"][~live] == 0)
+    ref = _oracle_decode(x["k"][live], x["v"][live], qv[live], lens_np[live], scale, 0)
+    assert_attention_close(outs["1"][live], ref, "longest first")
