@@ -296,6 +296,110 @@ def attention_chunk(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, ctx_len
 
 
 # ----------------------------------------------------------------------------
+# Recent-window hybrid cache ([P1] `OptimizedQuantizedKvCache`): the last W
+# tokens of a sequence stay unquantized (bf16), older tokens are INT8.
+# ----------------------------------------------------------------------------
+
+def to_bf16_values(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to bf16 (nearest even), returned as fp32."""
+    return bf16_bits_to_f32(f32_to_bf16_bits(x))
+
+
+class RecentWindowCache:
+    """One sequence's hybrid cache, updated by the steps of [P1]
+    `OptimizedQuantizedKvCache::append`:
+
+      1. the new rows join the unquantized recent part (held as bf16 values:
+         the page keeps its recent tensors in BF16, so an fp32 input row is
+         rounded once, to nearest even, when it enters);
+      2. if the recent part is longer than the window W, its oldest
+         len - W rows are quantized (one row at a time, with this cache's
+         quantizer and scale mode) and appended to the quantized part;
+      3. the newest W rows stay recent.
+
+    Arrays are ``[KVH, tokens, D]``.  ``window`` 0 quantizes every row on
+    arrival (a plain INT8 cache).
+    """
+
+    def __init__(self, num_kv_heads: int, head_dim: int, window: int, group: int = 0):
+        self.window = int(window)
+        self.group = int(group)
+        g = 1 if group == 0 else head_dim // group
+        self.k_codes = np.zeros((num_kv_heads, 0, head_dim), np.uint8)
+        self.v_codes = np.zeros((num_kv_heads, 0, head_dim), np.uint8)
+        self.k_scales = np.zeros((num_kv_heads, 0, g), np.float32)
+        self.v_scales = np.zeros((num_kv_heads, 0, g), np.float32)
+        self.k_recent = np.zeros((num_kv_heads, 0, head_dim), np.float32)
+        self.v_recent = np.zeros((num_kv_heads, 0, head_dim), np.float32)
+
+    def append(self, k_new: np.ndarray, v_new: np.ndarray) -> None:
+        k_rec = np.concatenate([self.k_recent, to_bf16_values(k_new)], axis=1)
+        v_rec = np.concatenate([self.v_recent, to_bf16_values(v_new)], axis=1)
+        n_old = k_rec.shape[1] - self.window
+        if n_old > 0:
+            kc, ks = quantize(k_rec[:, :n_old], self.group)
+            vc, vs = quantize(v_rec[:, :n_old], self.group)
+            self.k_codes = np.concatenate([self.k_codes, kc], axis=1)
+            self.k_scales = np.concatenate([self.k_scales, ks], axis=1)
+            self.v_codes = np.concatenate([self.v_codes, vc], axis=1)
+            self.v_scales = np.concatenate([self.v_scales, vs], axis=1)
+            k_rec, v_rec = k_rec[:, n_old:], v_rec[:, n_old:]
+        self.k_recent, self.v_recent = k_rec, v_rec
+
+    def quantized_len(self) -> int:
+        return self.k_codes.shape[1]
+
+    def recent_len(self) -> int:
+        return self.k_recent.shape[1]
+
+    def seq_len(self) -> int:
+        return self.quantized_len() + self.recent_len()
+
+    def kv(self):
+        """[P1] `get_kv`: the dequantized old rows followed by the recent rows,
+        as exact fp64 ``[KVH, L, D]`` K and V."""
+        k = np.concatenate([dequantize_exact(self.k_codes, self.k_scales),
+                            self.k_recent.astype(np.float64)], axis=1)
+        v = np.concatenate([dequantize_exact(self.v_codes, self.v_scales),
+                            self.v_recent.astype(np.float64)], axis=1)
+        return k, v
+
+
+def attention_decode_recent(q: np.ndarray, caches, attn_scale: float) -> np.ndarray:
+    """Decode attention over hybrid caches: ``q`` [B, H, D], ``caches`` one
+    :class:`RecentWindowCache` per sequence; each query sees its sequence's
+    `get_kv` view (all tokens, old ones dequantized).  Returns [B, H, D] fp64."""
+    bsz, nh, d = q.shape
+    out = np.zeros((bsz, nh, d), dtype=np.float64)
+    for b, c in enumerate(caches):
+        if c.seq_len() == 0:
+            continue
+        k, v = c.kv()
+        for h in range(nh):
+            g = kv_head_of(h, nh, k.shape[0])
+            out[b, h] = softmax_attend(q[b, h].astype(np.float64), k[g], v[g], attn_scale)
+    return out
+
+
+def recent_memory_bytes(num_kv_heads: int, head_dim: int, length: int, window: int,
+                        group: int = 0, scale_bytes: int = 2) -> int:
+    """[P1] `OptimizedQuantizedKvCache::memory_bytes` for one sequence: one
+    byte per quantized element, ``scale_bytes`` per scale (the page stores
+    them as BF16, 2 bytes), two bytes per recent element; K and V."""
+    nq = recent_split(length, window)
+    nr = length - nq
+    g = 1 if group == 0 else head_dim // group
+    return 2 * (num_kv_heads * nq * head_dim + scale_bytes * num_kv_heads * nq * g
+                + 2 * num_kv_heads * nr * head_dim)
+
+
+def recent_split(length: int, window: int) -> int:
+    """Number of INT8 rows of a hybrid sequence of ``length`` tokens: every
+    position below length - W is quantized, the rest are recent."""
+    return max(0, int(length) - int(window))
+
+
+# ----------------------------------------------------------------------------
 # Sizing
 # ----------------------------------------------------------------------------
 

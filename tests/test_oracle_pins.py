@@ -471,3 +471,123 @@ def test_sizing_matches_printed_figures(golden):
     assert f"{s['batch8_codes_bytes'] / 1e9:.2f} GB" == s["printed_q8"]
     # the page's own product, evaluated, is 1.07e9 (garbled figure)
     assert 32 * 2 * 4096 * 8 * 128 * 4 == s["per_sequence_fp32_bytes"]
+
+
+# ----------------------------------------------------------------------------
+# recent-window hybrid cache (abaddon 0.2.0-rc.1 kv_cache_quant_cuda.rs,
+# OptimizedQuantizedKvCache)
+# ----------------------------------------------------------------------------
+
+def _bf16_values_torch(x):
+    """bf16 rounding by the library cast (independent of the oracle's)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def test_recent_window_counts(golden):
+    """The quantized / recent split that the page's tests print."""
+    for case in golden["recent_window_counts"]["cases"]:
+        c = orc.RecentWindowCache(case["kv_heads"], case["head_dim"], case["window"])
+        rng = np.random.default_rng(0)
+        for n in case["appends"]:
+            x = rng.standard_normal((case["kv_heads"], n, case["head_dim"])).astype(np.float32)
+            c.append(x, x)
+        assert (c.seq_len(), c.quantized_len(), c.recent_len()) == (case["seq_len"], case["quantized"],
+                                                                     case["recent"])
+        assert orc.recent_split(c.seq_len(), case["window"]) == case["quantized"]
+
+
+@pytest.mark.parametrize("group", [0, 32])
+def test_recent_window_state_is_path_independent(group):
+    """Over random append sequences (chunks shorter and longer than the
+    window), rows below L - W always hold the codes of their bf16-rounded
+    values and the last W rows hold those bf16 values.  The fp32 inputs are
+    chosen so that quantizing the raw value would give other codes."""
+    rng = np.random.default_rng(1)
+    W, KVH, D, T = 5, 2, 64, 41
+    k = (rng.standard_normal((KVH, T, D)) * 3).astype(np.float32)
+    v = (rng.standard_normal((KVH, T, D)) * 0.3).astype(np.float32)
+    kb, vb = _bf16_values_torch(k), _bf16_values_torch(v)
+    assert not np.array_equal(orc.quantize(k, group)[0], orc.quantize(kb, group)[0])
+    for _ in range(10):
+        c = orc.RecentWindowCache(KVH, D, W, group)
+        L = 0
+        while L < T:
+            n = min(int(rng.integers(1, 13)), T - L)
+            c.append(k[:, L:L + n], v[:, L:L + n])
+            L += n
+            nq = max(0, L - W)
+            kc, ks = orc.quantize(kb[:, :nq], group)
+            vc, vs = orc.quantize(vb[:, :nq], group)
+            assert np.array_equal(c.k_codes, kc) and np.array_equal(c.v_codes, vc)
+            assert np.array_equal(c.k_scales, ks) and np.array_equal(c.v_scales, vs)
+            assert np.array_equal(c.k_recent, kb[:, nq:L]) and np.array_equal(c.v_recent, vb[:, nq:L])
+
+
+def test_recent_window_zero_is_plain_int8():
+    """W = 0 quantizes every row on arrival: the plain INT8 cache."""
+    rng = np.random.default_rng(2)
+    x = _bf16_values_torch(rng.standard_normal((2, 9, 32)))
+    c = orc.RecentWindowCache(2, 32, 0)
+    c.append(x[:, :4], x[:, :4])
+    c.append(x[:, 4:], x[:, 4:])
+    assert c.recent_len() == 0
+    assert np.array_equal(c.k_codes, orc.quantize(x, 0)[0])
+
+
+def test_recent_attention_all_recent_brute_force():
+    """L <= W: attention over the bf16 rows, computed here with Python floats."""
+    rng = np.random.default_rng(3)
+    KVH, H, D, L = 1, 2, 8, 5
+    k = rng.standard_normal((KVH, L, D)).astype(np.float32)
+    v = rng.standard_normal((KVH, L, D)).astype(np.float32)
+    q = _bf16_values_torch(rng.standard_normal((1, H, D)))
+    c = orc.RecentWindowCache(KVH, D, 8)
+    c.append(k, v)
+    got = orc.attention_decode_recent(q, [c], 0.3)
+    kb, vb = _bf16_values_torch(k)[0], _bf16_values_torch(v)[0]
+    for h in range(H):
+        s = [0.3 * sum(float(q[0, h, d]) * float(kb[t, d]) for d in range(D)) for t in range(L)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = sum(w)
+        for d in range(D):
+            ref = sum(w[t] * float(vb[t, d]) for t in range(L)) / z
+            assert abs(got[0, h, d] - ref) < 1e-12
+
+
+def test_recent_attention_equal_keys_give_mean_v():
+    """Keys on the quantization grid and bf16-exact (integers, absmax 127)
+    dequantize to themselves, so old and recent keys are equal, the weights
+    are uniform, and the output is the mean of the old (dequantized) and
+    recent (bf16) value rows."""
+    rng = np.random.default_rng(4)
+    KVH, D, L, W = 1, 32, 11, 4
+    row = rng.integers(-127, 128, size=D).astype(np.float32)
+    row[0] = 127.0
+    k = np.repeat(row[None, None, :], L, axis=1)
+    v = rng.standard_normal((KVH, L, D)).astype(np.float32)
+    c = orc.RecentWindowCache(KVH, D, W)
+    c.append(k[:, :6], v[:, :6])
+    c.append(k[:, 6:], v[:, 6:])
+    assert c.quantized_len() == L - W
+    assert np.array_equal(orc.dequantize_exact(c.k_codes, c.k_scales)[0], k[0, :L - W].astype(np.float64))
+    vb = _bf16_values_torch(v)[0]
+    vc, vs = orc.quantize(vb[:L - W], 0)
+    rows = np.concatenate([orc.dequantize_exact(vc, vs), vb[L - W:].astype(np.float64)])
+    q = rng.standard_normal((1, 3, D))
+    out = orc.attention_decode_recent(q, [c], 0.05)
+    for h in range(3):
+        assert np.allclose(out[0, h], rows.mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_recent_memory_savings(golden):
+    """test_memory_savings: W = 16, 8 KV heads, D = 128, 1000 tokens in BF16
+    save more than 1.5x; by hand: 984 quantized rows (1 byte per element, a
+    2-byte scale per row) and 16 recent rows (2 bytes per element), K and V."""
+    g = golden["recent_window_savings"]
+    got = orc.recent_memory_bytes(g["kv_heads"], g["head_dim"], g["tokens"], g["window"])
+    by_hand = 2 * (8 * 984 * 128 + 2 * 8 * 984 + 2 * 8 * 16 * 128)
+    assert got == by_hand == 2_112_256
+    full = g["tokens"] * g["kv_heads"] * g["head_dim"] * 2 * 2
+    assert full / got > g["min_savings"]
