@@ -192,6 +192,88 @@ kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_
 kvq_status kvq_dequant(const kvq_cache* cache, int32_t which, const int32_t* seq_lens,
                        int32_t out_dtype, void* out, int32_t out_len, void* stream);
 
+/*
+ * Recent-window hybrid cache (abaddon 0.2.0-rc.1 src/kv_cache_quant_cuda.rs,
+ * `OptimizedQuantizedKvCache` with `DynamicQuantConfig::unquantized_window`):
+ * the last `window` positions of every sequence stay unquantized, as bf16,
+ * in a ring beside the INT8 cache; older positions are INT8 in the cache
+ * that the kvq_cache describes.  For a sequence of length L, position p is
+ *   INT8, at its usual cache row,        if p <  L - window,
+ *   bf16, in ring slot p % capacity,     if p >= L - window.
+ * A row is quantized from its bf16 value: fp32 input rows are rounded to
+ * bf16 (nearest even) when they enter, whichever call later moves them out
+ * of the window.  capacity > window keeps the slot a fused step writes apart
+ * from the slot it quantizes.
+ */
+typedef struct kvq_recent {
+  int32_t window;    /* W >= 1 positions kept in bf16                         */
+  int32_t capacity;  /* ring slots R per (sequence, KV head), R > W           */
+  uint16_t* k;       /* device bf16 [batch, num_kv_heads, capacity, head_dim] */
+  uint16_t* v;
+} kvq_recent;
+
+/*
+ * kvq_append_recent — append n_new rows per sequence at the end of a hybrid
+ * cache: start_pos[b] must be sequence b's current length (the caller's
+ * contract).  With L' = start_pos[b] + n_new, the rows that leave the window
+ * (old ring rows and new rows below L' - W) are quantized into the INT8
+ * cache exactly as kvq_append would quantize their bf16 values, and the
+ * rows at L' - W and above are stored, as bf16, in their ring slots
+ * (`OptimizedQuantizedKvCache::append` steps).  Two launches: the rows
+ * leaving the ring are quantized before any ring slot is overwritten.
+ *
+ *   k_new, v_new : device [B, KVH, n_new, D], fp32 or bf16 (in_dtype)
+ * Errors: those of kvq_append, plus INVALID_ARG for a bad recent descriptor
+ * (NULL, window < 1, capacity <= window, NULL ring pointers).
+ */
+kvq_status kvq_append_recent(const kvq_cache* cache, const kvq_recent* recent, const void* k_new,
+                             const void* v_new, int32_t in_dtype, int32_t n_new,
+                             const int32_t* start_pos, void* stream);
+
+/*
+ * kvq_attention_decode_recent — kvq_attention_decode over a hybrid cache:
+ * each query attends to all seq_lens[b] tokens, the INT8 ones dequantized in
+ * registers and the recent ones read as bf16 (the `get_kv` view: old rows
+ * dequantized, then the recent rows).  The ring is one more split of the
+ * split-K launch.  seq_lens[b] is clamped to [0, min(hint, capacity of the
+ * INT8 cache)].  Workspace: kvq_workspace_size_recent(cache, recent, hint).
+ * Errors: those of kvq_attention_decode; UNSUPPORTED for head_dim 256.
+ */
+kvq_status kvq_attention_decode_recent(const kvq_cache* cache, const kvq_recent* recent,
+                                       const uint16_t* q, const int32_t* seq_lens, float attn_scale,
+                                       uint16_t* out, void* workspace, size_t workspace_bytes,
+                                       int32_t max_seq_len_hint, void* stream);
+
+/*
+ * kvq_append_decode_recent — one decode step on a hybrid cache in a single
+ * launch: the new row of every sequence goes to position seq_lens[b] - 1
+ * (its ring slot), the row leaving the window (position seq_lens[b] - 1 -
+ * window, if any) is quantized into the INT8 cache, and the query attends
+ * to all seq_lens[b] tokens: exactly kvq_append_recent (start_pos =
+ * seq_lens - 1, n_new = 1) followed by kvq_attention_decode_recent.
+ * Errors: those of both.
+ */
+kvq_status kvq_append_decode_recent(const kvq_cache* cache, const kvq_recent* recent,
+                                    const void* k_new, const void* v_new, int32_t in_dtype,
+                                    const uint16_t* q, const int32_t* seq_lens, float attn_scale,
+                                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    int32_t max_seq_len_hint, void* stream);
+
+/*
+ * kvq_dequant_recent — the `get_kv` view of one side of a hybrid cache:
+ * out[b,h,t,:] is the dequantized INT8 row for t < L - W and the bf16 ring
+ * row for L - W <= t < L (L = seq_lens[b] clamped to the INT8 capacity),
+ * as fp32 or bf16; positions t >= L are 0.
+ */
+kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, int32_t which,
+                              const int32_t* seq_lens, int32_t out_dtype, void* out, int32_t out_len,
+                              void* stream);
+
+/* Workspace bytes needed by kvq_attention_decode_recent and
+ * kvq_append_decode_recent for lengths up to max_seq_len (0 on an invalid
+ * descriptor). */
+size_t kvq_workspace_size_recent(const kvq_cache* cache, const kvq_recent* recent, int32_t max_seq_len);
+
 /* Workspace bytes needed by kvq_attention_decode (n_query = 1) or
  * kvq_attention_chunk (n_query = chunk length) for lengths up to
  * max_seq_len.  0 on an invalid descriptor (see kvq_last_error). */

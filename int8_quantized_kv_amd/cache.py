@@ -21,7 +21,8 @@ class Int8KVCache:
 
     def __init__(self, batch: int, num_heads: int, num_kv_heads: int, head_dim: int, *,
                  max_len: int = 0, group32: bool = False, num_pages: int = 0,
-                 block_table: torch.Tensor | None = None, device="cuda", fill: int | None = None):
+                 block_table: torch.Tensor | None = None, device="cuda", fill: int | None = None,
+                 recent_window: int = 0, recent_capacity: int | None = None):
         self.batch, self.num_heads, self.num_kv_heads, self.head_dim = batch, num_heads, num_kv_heads, head_dim
         self.groups = head_dim // 32 if group32 else 1
         self.paged = block_table is not None
@@ -52,6 +53,15 @@ class Int8KVCache:
             scale_mode=_k.KVQ_SCALE_GROUP32 if group32 else _k.KVQ_SCALE_PER_TOKEN,
             max_len=0 if self.paged else max_len, num_pages=num_pages,
             max_blocks_per_seq=self.max_blocks, block_table=self.block_table)
+        # recent-window hybrid: the last W positions of each sequence stay bf16
+        # in a ring of R > W slots per (sequence, KV head)
+        self.recent = None
+        if recent_window > 0:
+            cap = recent_capacity or recent_window + 1
+            ring = (batch, num_kv_heads, cap, head_dim)
+            self.k_recent = torch.zeros(ring, dtype=torch.bfloat16, device=device)
+            self.v_recent = torch.zeros(ring, dtype=torch.bfloat16, device=device)
+            self.recent = _k.make_recent(recent_window, cap, self.k_recent, self.v_recent)
 
     # -- entry points -----------------------------------------------------------
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, start_pos: torch.Tensor, stream=None):
@@ -61,12 +71,18 @@ class Int8KVCache:
             raise TypeError("k_new and v_new must both be float32 or both bfloat16")
         if not (k_new.is_contiguous() and v_new.is_contiguous()):
             raise ValueError("k_new and v_new must be contiguous")
-        _k.kvq_append(self.desc, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
+        if self.recent is not None:
+            _k.kvq_append_recent(self.desc, self.recent, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
+        else:
+            _k.kvq_append(self.desc, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
 
     def workspace(self, max_seq_len: int, n_query: int = 1) -> torch.Tensor:
         """Zero-filled scratch for the attention calls (the split counters at
         its start must be zero before the first call; calls leave them zero)."""
-        n = _k.kvq_workspace_size(self.desc, max_seq_len, n_query)
+        if self.recent is not None and n_query == 1:
+            n = _k.kvq_workspace_size_recent(self.desc, self.recent, max_seq_len)
+        else:
+            n = _k.kvq_workspace_size(self.desc, max_seq_len, n_query)
         return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.k_codes.device)
 
     def decode(self, q: torch.Tensor, seq_lens: torch.Tensor, attn_scale: float, max_seq_len_hint: int,
@@ -76,8 +92,12 @@ class Int8KVCache:
             out = torch.empty_like(q)
         if workspace is None:
             workspace = self.workspace(max_seq_len_hint, 1)
-        _k.kvq_attention_decode(self.desc, q, seq_lens, attn_scale, out, workspace, workspace.numel(),
-                                max_seq_len_hint, stream)
+        if self.recent is not None:
+            _k.kvq_attention_decode_recent(self.desc, self.recent, q, seq_lens, attn_scale, out, workspace,
+                                           workspace.numel(), max_seq_len_hint, stream)
+        else:
+            _k.kvq_attention_decode(self.desc, q, seq_lens, attn_scale, out, workspace, workspace.numel(),
+                                    max_seq_len_hint, stream)
         return out
 
     def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, seq_lens: torch.Tensor,
@@ -93,14 +113,20 @@ class Int8KVCache:
             out = torch.empty_like(q)
         if workspace is None:
             workspace = self.workspace(max_seq_len_hint, 1)
-        _k.kvq_append_decode(self.desc, k_new, v_new, dt, q, seq_lens, attn_scale, out, workspace,
-                             workspace.numel(), max_seq_len_hint, stream)
+        if self.recent is not None:
+            _k.kvq_append_decode_recent(self.desc, self.recent, k_new, v_new, dt, q, seq_lens, attn_scale, out,
+                                        workspace, workspace.numel(), max_seq_len_hint, stream)
+        else:
+            _k.kvq_append_decode(self.desc, k_new, v_new, dt, q, seq_lens, attn_scale, out, workspace,
+                                 workspace.numel(), max_seq_len_hint, stream)
         return out
 
     def chunk(self, q: torch.Tensor, ctx_lens: torch.Tensor, causal: bool, attn_scale: float,
               max_ctx_len_hint: int, out: torch.Tensor | None = None,
               workspace: torch.Tensor | None = None, stream=None):
         """q: bf16 [B, H, n, D]; returns bf16 [B, H, n, D]."""
+        if self.recent is not None:
+            raise NotImplementedError("chunked attention over a recent-window cache is not provided")
         n = q.shape[2]
         if out is None:
             out = torch.empty_like(q)
@@ -114,8 +140,11 @@ class Int8KVCache:
         dt = torch.bfloat16 if bf16 else torch.float32
         out = torch.empty((self.batch, self.num_kv_heads, out_len, self.head_dim), dtype=dt,
                           device=self.k_codes.device)
-        _k.kvq_dequant(self.desc, which, seq_lens, _k.KVQ_DT_BF16 if bf16 else _k.KVQ_DT_F32, out, out_len,
-                       stream)
+        dt_code = _k.KVQ_DT_BF16 if bf16 else _k.KVQ_DT_F32
+        if self.recent is not None:
+            _k.kvq_dequant_recent(self.desc, self.recent, which, seq_lens, dt_code, out, out_len, stream)
+        else:
+            _k.kvq_dequant(self.desc, which, seq_lens, dt_code, out, out_len, stream)
         return out
 
     def nbytes(self) -> int:

@@ -84,22 +84,41 @@ KVQ_API uint64_t kvq_cache_bytes(const kvq_cache* c) {
   return 2ull * rows * per_row;
 }
 
-KVQ_API size_t kvq_workspace_size(const kvq_cache* c, int32_t max_seq_len, int32_t n_query) {
+namespace kvq {
+namespace {
+
+kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who) {
+  if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+  if (r->window < 1) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, r->window);
+  if (r->capacity <= r->window)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: ring capacity (%d) must exceed the window (%d)", who, r->capacity,
+                r->window);
+  if (static_cast<int64_t>(r->capacity) * c.head_dim > 0x7fffffffLL)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: ring capacity too large", who);
+  if (!r->k || !r->v) return fail(KVQ_ERR_INVALID_ARG, "%s: ring pointers must be non-NULL", who);
+  return KVQ_OK;
+}
+
+bool finite(float x) { return x == x && x != INFINITY && x != -INFINITY; }
+
+size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_len, int32_t n_query,
+                      const char* who) {
   g_err[0] = '\0';
-  if (check_cache(c, "kvq_workspace_size") != KVQ_OK) return 0;
+  if (check_cache(c, who) != KVQ_OK) return 0;
+  if (r && check_recent(r, *c, who) != KVQ_OK) return 0;
   if (max_seq_len <= 0 || n_query <= 0) {
-    fail(KVQ_ERR_INVALID_ARG, "kvq_workspace_size: max_seq_len and n_query must be positive");
+    fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
   }
-  if (n_query == 1) return plan_decode(*c, max_seq_len).workspace;
+  if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r)).workspace;
   return chunk_workspace(*c, max_seq_len, n_query);
 }
 
-KVQ_API kvq_status kvq_append(const kvq_cache* c, const void* k_new, const void* v_new, int32_t in_dtype,
-                              int32_t n_new, const int32_t* start_pos, void* stream) {
-  const char* who = "kvq_append";
+kvq_status append_impl(const kvq_cache* c, const kvq_recent* r, const void* k_new, const void* v_new,
+                       int32_t in_dtype, int32_t n_new, const int32_t* start_pos, void* stream, const char* who) {
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
+  if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
   if (!k_new || !v_new || !start_pos) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new, v_new and start_pos must be non-NULL", who);
   if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
     return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
@@ -107,53 +126,117 @@ KVQ_API kvq_status kvq_append(const kvq_cache* c, const void* k_new, const void*
   if (n_new > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: n_new (%d) exceeds the per-sequence capacity (%d)", who, n_new,
                 capacity_of(*c));
-  return launch_append(*c, k_new, v_new, in_dtype, n_new, start_pos, static_cast<hipStream_t>(stream));
+  return launch_append(*c, k_new, v_new, in_dtype, n_new, start_pos, static_cast<hipStream_t>(stream), false,
+                       recent_of(r));
 }
 
-KVQ_API kvq_status kvq_attention_decode(const kvq_cache* c, const uint16_t* q, const int32_t* seq_lens,
-                                        float attn_scale, uint16_t* out, void* workspace,
-                                        size_t workspace_bytes, int32_t max_seq_len_hint, void* stream) {
-  const char* who = "kvq_attention_decode";
+// Decode, plain or fused (k_new non-NULL), with or without a recent window.
+kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, const void* k_new, const void* v_new,
+                       int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens, float attn_scale,
+                       uint16_t* out, void* workspace, size_t workspace_bytes, int32_t max_seq_len_hint,
+                       void* stream, const char* who) {
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
+  if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if (fused) {
+    if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
+    if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
+  }
   if (!q || !seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, seq_lens and out must be non-NULL", who);
-  if (!(attn_scale == attn_scale) || attn_scale == INFINITY || attn_scale == -INFINITY)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
+  if (!finite(attn_scale)) return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
   if (max_seq_len_hint < 1 || max_seq_len_hint > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
                 capacity_of(*c));
   if (!decode_supported(c->head_dim))
     return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
-  const DecodePlan plan = plan_decode(*c, max_seq_len_hint);
+  if (r && c->head_dim > 128)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: a recent window needs head_dim <= 128 (got %d)", who, c->head_dim);
+  const RecentGeom rc = recent_of(r);
+  const DecodePlan plan = plan_decode(*c, max_seq_len_hint, rc);
   st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
   if (st != KVQ_OK) return st;
   return launch_decode(*c, plan, q, seq_lens, attn_scale, out, workspace, max_seq_len_hint,
-                       static_cast<hipStream_t>(stream));
+                       static_cast<hipStream_t>(stream), fused ? k_new : nullptr, fused ? v_new : nullptr,
+                       in_dtype, rc);
+}
+
+kvq_status dequant_impl(const kvq_cache* c, const kvq_recent* r, int32_t which, const int32_t* seq_lens,
+                        int32_t out_dtype, void* out, int32_t out_len, void* stream, const char* who) {
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "%s: which must be 0 (K) or 1 (V)", who);
+  if (!seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: seq_lens and out must be non-NULL", who);
+  if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: out_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
+  if (out_len <= 0 || out_len > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: out_len (%d) must be in [1, %d]", who, out_len, capacity_of(*c));
+  return launch_dequant(*c, which, seq_lens, out_dtype, out, out_len, static_cast<hipStream_t>(stream),
+                        recent_of(r));
+}
+
+}  // namespace
+}  // namespace kvq
+
+KVQ_API size_t kvq_workspace_size(const kvq_cache* c, int32_t max_seq_len, int32_t n_query) {
+  return workspace_impl(c, nullptr, max_seq_len, n_query, "kvq_workspace_size");
+}
+
+KVQ_API size_t kvq_workspace_size_recent(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_len) {
+  if (!r) {
+    fail(KVQ_ERR_INVALID_ARG, "kvq_workspace_size_recent: recent-window descriptor is NULL");
+    return 0;
+  }
+  return workspace_impl(c, r, max_seq_len, 1, "kvq_workspace_size_recent");
+}
+
+KVQ_API kvq_status kvq_append(const kvq_cache* c, const void* k_new, const void* v_new, int32_t in_dtype,
+                              int32_t n_new, const int32_t* start_pos, void* stream) {
+  return append_impl(c, nullptr, k_new, v_new, in_dtype, n_new, start_pos, stream, "kvq_append");
+}
+
+KVQ_API kvq_status kvq_append_recent(const kvq_cache* c, const kvq_recent* r, const void* k_new, const void* v_new,
+                                     int32_t in_dtype, int32_t n_new, const int32_t* start_pos, void* stream) {
+  const char* who = "kvq_append_recent";
+  if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+  return append_impl(c, r, k_new, v_new, in_dtype, n_new, start_pos, stream, who);
+}
+
+KVQ_API kvq_status kvq_attention_decode(const kvq_cache* c, const uint16_t* q, const int32_t* seq_lens,
+                                        float attn_scale, uint16_t* out, void* workspace,
+                                        size_t workspace_bytes, int32_t max_seq_len_hint, void* stream) {
+  return decode_impl(c, nullptr, false, nullptr, nullptr, KVQ_DT_BF16, q, seq_lens, attn_scale, out, workspace,
+                     workspace_bytes, max_seq_len_hint, stream, "kvq_attention_decode");
+}
+
+KVQ_API kvq_status kvq_attention_decode_recent(const kvq_cache* c, const kvq_recent* r, const uint16_t* q,
+                                               const int32_t* seq_lens, float attn_scale, uint16_t* out,
+                                               void* workspace, size_t workspace_bytes, int32_t max_seq_len_hint,
+                                               void* stream) {
+  const char* who = "kvq_attention_decode_recent";
+  if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+  return decode_impl(c, r, false, nullptr, nullptr, KVQ_DT_BF16, q, seq_lens, attn_scale, out, workspace,
+                     workspace_bytes, max_seq_len_hint, stream, who);
 }
 
 KVQ_API kvq_status kvq_append_decode(const kvq_cache* c, const void* k_new, const void* v_new, int32_t in_dtype,
                                      const uint16_t* q, const int32_t* seq_lens, float attn_scale, uint16_t* out,
                                      void* workspace, size_t workspace_bytes, int32_t max_seq_len_hint,
                                      void* stream) {
-  const char* who = "kvq_append_decode";
-  kvq_status st = check_cache(c, who);
-  if (st != KVQ_OK) return st;
-  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
-  if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
-  if (!q || !seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, seq_lens and out must be non-NULL", who);
-  if (!(attn_scale == attn_scale) || attn_scale == INFINITY || attn_scale == -INFINITY)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
-  if (max_seq_len_hint < 1 || max_seq_len_hint > capacity_of(*c))
-    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
-                capacity_of(*c));
-  if (!decode_supported(c->head_dim))
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
-  const DecodePlan plan = plan_decode(*c, max_seq_len_hint);
-  st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
-  if (st != KVQ_OK) return st;
-  return launch_decode(*c, plan, q, seq_lens, attn_scale, out, workspace, max_seq_len_hint,
-                       static_cast<hipStream_t>(stream), k_new, v_new, in_dtype);
+  return decode_impl(c, nullptr, true, k_new, v_new, in_dtype, q, seq_lens, attn_scale, out, workspace,
+                     workspace_bytes, max_seq_len_hint, stream, "kvq_append_decode");
+}
+
+KVQ_API kvq_status kvq_append_decode_recent(const kvq_cache* c, const kvq_recent* r, const void* k_new,
+                                            const void* v_new, int32_t in_dtype, const uint16_t* q,
+                                            const int32_t* seq_lens, float attn_scale, uint16_t* out,
+                                            void* workspace, size_t workspace_bytes, int32_t max_seq_len_hint,
+                                            void* stream) {
+  const char* who = "kvq_append_decode_recent";
+  if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+  return decode_impl(c, r, true, k_new, v_new, in_dtype, q, seq_lens, attn_scale, out, workspace,
+                     workspace_bytes, max_seq_len_hint, stream, who);
 }
 
 KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens,
@@ -179,14 +262,13 @@ KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, in
 
 KVQ_API kvq_status kvq_dequant(const kvq_cache* c, int32_t which, const int32_t* seq_lens, int32_t out_dtype,
                                void* out, int32_t out_len, void* stream) {
-  const char* who = "kvq_dequant";
-  kvq_status st = check_cache(c, who);
-  if (st != KVQ_OK) return st;
-  if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "%s: which must be 0 (K) or 1 (V)", who);
-  if (!seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: seq_lens and out must be non-NULL", who);
-  if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: out_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
-  if (out_len <= 0 || out_len > capacity_of(*c))
-    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: out_len (%d) must be in [1, %d]", who, out_len, capacity_of(*c));
-  return launch_dequant(*c, which, seq_lens, out_dtype, out, out_len, static_cast<hipStream_t>(stream));
+  return dequant_impl(c, nullptr, which, seq_lens, out_dtype, out, out_len, stream, "kvq_dequant");
+}
+
+KVQ_API kvq_status kvq_dequant_recent(const kvq_cache* c, const kvq_recent* r, int32_t which,
+                                      const int32_t* seq_lens, int32_t out_dtype, void* out, int32_t out_len,
+                                      void* stream) {
+  const char* who = "kvq_dequant_recent";
+  if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+  return dequant_impl(c, r, which, seq_lens, out_dtype, out, out_len, stream, who);
 }

@@ -13,17 +13,43 @@
 namespace kvq {
 namespace {
 
+// Modes with a recent window (abaddon 0.2.0-rc.1 kv_cache_quant_cuda.rs,
+// `OptimizedQuantizedKvCache::append`): kRows places new rows (below the new
+// window: quantized from their bf16 value; inside it: bf16 in the ring);
+// kEvict quantizes the ring rows that leave the window, and runs first.
+enum AppendMode : int32_t { kPlain = 0, kRows = 1, kEvict = 2 };
+
 struct AppendParams {
-  const void* src[2];        // K, V new rows [B, KVH, n, D]
+  const void* src[2];        // K, V new rows [B, KVH, n_new, D]
   uint8_t* codes[2];
   float* scales[2];
+  uint16_t* ring[2];         // recent window: bf16 [B, KVH, rcap, D]
   const int32_t* start_pos;  // [B]; with pos_from_lens, seq_lens [B]
   CacheGeom geom;
-  int32_t batch, n, head_dim, groups;  // groups = scales per row
+  int32_t batch, n, head_dim, groups;  // n: rows per (sequence, KV head) this launch covers
+  int32_t n_new;                       // rows appended per sequence
   int32_t rows_per_side;               // B * KVH * n
   int32_t pos_from_lens;               // 1: the row goes to position seq_lens[b] - 1
   int32_t in_bf16;
+  int32_t mode;                        // AppendMode
+  int32_t rwin, rcap;                  // recent window and ring slots
 };
+
+// Stores this lane's EPL values of a row as bf16 (nearest even).
+template <int EPL>
+__device__ __forceinline__ void store_lane_bf16(uint16_t* row, int lane, const float (&x)[EPL]) {
+  uint16_t* out = row + lane * EPL;
+  if constexpr (EPL == 1) {
+    out[0] = f32_to_bf16_rne(x[0]);
+  } else if constexpr (EPL == 2) {
+    *reinterpret_cast<uint32_t*>(out) = f32_to_bf16_rne(x[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
+  } else {
+    uint2 v;
+    v.x = f32_to_bf16_rne(x[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(x[1])) << 16);
+    v.y = f32_to_bf16_rne(x[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(x[3])) << 16);
+    *reinterpret_cast<uint2*>(out) = v;
+  }
+}
 
 // One wave per row; EPL elements per lane (row_epl(D)); GROUP32: one scale
 // per 32 elements (32/EPL lanes) instead of one per row.
@@ -38,16 +64,35 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int bh = row / p.n;
   const int h = bh % p.geom.kvh;
   const int b = bh / p.geom.kvh;
-  const int pos = p.pos_from_lens ? p.start_pos[b] - 1 : p.start_pos[b] + i;
-  const int64_t dst = cache_row(p.geom, b, h, pos);
-  if (dst < 0) return;  // outside the cache: not written
-
   const int D = p.head_dim;
   const bool on = lane < D / EPL;
   float x[EPL];
-  const size_t esize = p.in_bf16 ? 2 : 4;
-  load_row_values<EPL>(static_cast<const char*>(p.src[side]) + static_cast<int64_t>(row) * D * esize, lane, on,
-                       p.in_bf16 != 0, x);
+  int pos;
+  if (p.mode == kEvict) {
+    // ring row q = start - W + i leaves the window (i < min(n_new, W))
+    pos = p.start_pos[b] - p.rwin + i;
+    if (pos < 0) return;
+    const uint16_t* src = p.ring[side] + (static_cast<int64_t>(bh) * p.rcap + pos % p.rcap) * D;
+    load_row_values<EPL>(src, lane, on, true, x);
+  } else {
+    pos = p.pos_from_lens ? p.start_pos[b] - 1 : p.start_pos[b] + i;
+    const size_t esize = p.in_bf16 ? 2 : 4;
+    load_row_values<EPL>(static_cast<const char*>(p.src[side]) + static_cast<int64_t>(row) * D * esize, lane, on,
+                         p.in_bf16 != 0, x);
+    if (p.mode == kRows) {
+      // rows enter as bf16 values; those inside the new window go to the ring
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) x[e] = bf16_to_f32(f32_to_bf16_rne(x[e]));
+      if (pos >= p.start_pos[b] + p.n_new - p.rwin) {
+        if (pos < 0) return;
+        if (on) store_lane_bf16<EPL>(p.ring[side] + (static_cast<int64_t>(bh) * p.rcap + pos % p.rcap) * D, lane, x);
+        return;
+      }
+    }
+  }
+  const int64_t dst = cache_row(p.geom, b, h, pos);
+  if (dst < 0) return;  // outside the cache: not written
+
   float s;
   const uint32_t packed = quantize_lane<EPL, GROUP32>(x, s);
   if (on) {
@@ -70,6 +115,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 struct DequantParams {
   const uint8_t* codes;
   const float* scales;
+  const uint16_t* ring;      // recent window: bf16 [B, KVH, rcap, D]
+  int32_t rwin, rcap;        // window (0: none) and ring slots
   const int32_t* seq_lens;
   void* out;
   CacheGeom geom;
@@ -91,8 +138,16 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
   int len = p.seq_lens[b];
   len = len < 0 ? 0 : (len > capacity(p.geom) ? capacity(p.geom) : len);
   float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int64_t row = t < len ? cache_row(p.geom, b, h, t) : -1;
-  if (row >= 0) {
+  // with a recent window the last rwin positions come from the ring (bf16)
+  const bool recent = t < len && t >= len - p.rwin;
+  const int64_t row = t < len && !recent ? cache_row(p.geom, b, h, t) : -1;
+  if (recent) {
+    const uint2 r = *reinterpret_cast<const uint2*>(p.ring + (bh * p.rcap + t % p.rcap) * D + d);
+    v[0] = __uint_as_float(r.x << 16);
+    v[1] = __uint_as_float(r.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.y << 16);
+    v[3] = __uint_as_float(r.y & 0xffff0000u);
+  } else if (row >= 0) {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
     const float s = p.scales[row * p.groups + (p.groups == 1 ? 0 : d / 32)];
 #pragma unroll
@@ -124,8 +179,14 @@ void dispatch_epl(int epl, dim3 grid, hipStream_t st, const AppendParams& p) {
 }  // namespace
 
 kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_new, int in_dtype,
-                         int n_new, const int32_t* start_pos, hipStream_t stream, bool pos_from_lens) {
+                         int n_new, const int32_t* start_pos, hipStream_t stream, bool pos_from_lens,
+                         const RecentGeom& rc) {
   AppendParams p;
+  p.ring[0] = rc.k;
+  p.ring[1] = rc.v;
+  p.rwin = rc.window;
+  p.rcap = rc.cap;
+  p.n_new = n_new;
   p.src[0] = k_new;
   p.src[1] = v_new;
   p.codes[0] = c.k_codes;
@@ -140,21 +201,32 @@ kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_ne
   p.groups = scales_per_row(c);
   p.pos_from_lens = pos_from_lens ? 1 : 0;
   p.in_bf16 = in_dtype == KVQ_DT_BF16 ? 1 : 0;
-  const int64_t rows = static_cast<int64_t>(c.batch) * c.num_kv_heads * n_new;
-  if (rows * 2 > 0x7fffffffLL) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_append: too many rows (%lld)", (long long)rows);
-  p.rows_per_side = static_cast<int32_t>(rows);
-  const int64_t waves = rows * 2;
-  dim3 grid(static_cast<unsigned>((waves + 3) / 4));
-  if (c.scale_mode == KVQ_SCALE_GROUP32) dispatch_epl<true>(row_epl(c.head_dim), grid, stream, p);
-  else dispatch_epl<false>(row_epl(c.head_dim), grid, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_append: launch failed: %s", hipGetErrorString(e));
+  // one launch per pass: with a recent window, first the ring rows that
+  // leave it (at most min(n_new, W) per sequence), then the new rows
+  const int passes = rc.window > 0 ? 2 : 1;
+  for (int pass = 0; pass < passes; ++pass) {
+    p.mode = rc.window == 0 ? kPlain : (pass == 0 ? kEvict : kRows);
+    p.n = p.mode == kEvict ? (n_new < rc.window ? n_new : rc.window) : n_new;
+    const int64_t rows = static_cast<int64_t>(c.batch) * c.num_kv_heads * p.n;
+    if (rows * 2 > 0x7fffffffLL)
+      return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_append: too many rows (%lld)", (long long)rows);
+    p.rows_per_side = static_cast<int32_t>(rows);
+    const int64_t waves = rows * 2;
+    dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    if (c.scale_mode == KVQ_SCALE_GROUP32) dispatch_epl<true>(row_epl(c.head_dim), grid, stream, p);
+    else dispatch_epl<false>(row_epl(c.head_dim), grid, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_append: launch failed: %s", hipGetErrorString(e));
+  }
   return KVQ_OK;
 }
 
 kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens, int out_dtype,
-                          void* out, int out_len, hipStream_t stream) {
+                          void* out, int out_len, hipStream_t stream, const RecentGeom& rc) {
   DequantParams p;
+  p.ring = which ? rc.v : rc.k;
+  p.rwin = rc.window;
+  p.rcap = rc.cap;
   p.codes = which ? c.v_codes : c.k_codes;
   p.scales = which ? c.v_scales : c.k_scales;
   p.seq_lens = seq_lens;

@@ -76,6 +76,11 @@ struct DecodeParams {
   int32_t wg_per_kvh;        // workgroups sharing one KV head (GQA group / HPW)
   int32_t longest_first;     // workgroup z takes the z-th longest sequence (batch <= kLongestFirstMax)
   float scale_log2;          // attn_scale * log2(e)
+  // recent window (hybrid cache): the last rwin positions are bf16 rows in
+  // ring slot (position % rcap); split index ring_split (-1: none) holds them
+  uint16_t* rk;              // [B, KVH, rcap, D] bf16
+  uint16_t* rv;
+  int32_t rwin, rcap, ring_split;
 };
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* x) {
@@ -352,6 +357,138 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
   }
 }
 
+// Per-wave (m, l, o) in LDS -> the workgroup's (m, l, o): o and l of each
+// wave are relative to 2^m of that wave, so they combine with 2^(m_w - M).
+template <int D, int HPW, int NW, int NT>
+__device__ __forceinline__ void combine_waves(const float (*sm_fo)[HPW][D], const float (*sm_fml)[HPW][2],
+                                              float (*sm_o)[D], float (*sm_ml)[2]) {
+  for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
+    const int j = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_fml[w][j][0]);
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_fml[w][j][0];
+      if (mw == -INFINITY) continue;
+      const float f = exp2f(mw - M);
+      acc = fmaf(sm_fo[w][j][d], f, acc);
+      lsum = fmaf(sm_fml[w][j][1], f, lsum);
+    }
+    sm_o[j][d] = acc;
+    if (d == 0) {
+      sm_ml[j][0] = M;
+      sm_ml[j][1] = lsum;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Recent-window split (abaddon 0.2.0-rc.1 kv_cache_quant_cuda.rs,
+// `OptimizedQuantizedKvCache::get_kv`: the unquantized recent rows follow
+// the dequantized old ones).  Positions [L - W, L) are bf16 rows in ring
+// slots position % rcap; this workgroup attends its HPW heads to them with
+// fp32 arithmetic and leaves one more split partial, index = the number of
+// INT8 splits.  Each lane holds two dims; each wave takes 16-token chunks
+// (loads of a chunk in flight together) with an exact running maximum.  The
+// fused step's new row (position L - 1) comes from the input, rounded to
+// bf16, and is stored in its ring slot by the wave that attends to it.
+// ---------------------------------------------------------------------------
+template <int D, int HPW, bool APPEND>
+__device__ void ring_split(const DecodeParams& p, int b, int kvh, int h0, int hg, int wave, int lane,
+                           float (*sm_fo)[HPW][D], float (*sm_fml)[HPW][2], float (*sm_o)[D],
+                           float (*sm_ml)[2]) {
+  constexpr int kChunk = 16;
+  const int L = clamp_len(p, b);
+  if (L == 0) return;  // nothing to attend to (split 0 writes the zeros); not counted
+  const int L8 = L > p.rwin ? L - p.rwin : 0;
+  const int ns8 = (L8 + p.split_len - 1) / p.split_len;
+  const int H = p.num_heads;
+  const bool on = lane < D / 2;
+  const int d0 = 2 * (on ? lane : 0);
+  float q0[HPW], q1[HPW], m[HPW], l[HPW], o0[HPW], o1[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const uint32_t w = on ? *reinterpret_cast<const uint32_t*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + d0) : 0u;
+    q0[j] = __uint_as_float(w << 16);
+    q1[j] = __uint_as_float(w & 0xffff0000u);
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+    o0[j] = 0.0f;
+    o1[j] = 0.0f;
+  }
+  const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
+  for (int c0 = L8 + wave * kChunk; c0 < L; c0 += kStreamWaves * kChunk) {
+    uint32_t kw[kChunk], vw[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int t = min(c0 + i, L - 1);
+      const int64_t off = (ring0 + t % p.rcap) * D + d0;
+      kw[i] = *reinterpret_cast<const uint32_t*>(p.rk + off);
+      vw[i] = *reinterpret_cast<const uint32_t*>(p.rv + off);
+    }
+    if constexpr (APPEND) {
+      const int i = L - 1 - c0;  // the new row, if this chunk holds it
+      if (i >= 0 && i < kChunk) {
+        const int64_t src = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D + d0;
+        uint32_t nk, nv;
+        if (p.new_bf16) {
+          nk = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_k) + src);
+          nv = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_v) + src);
+        } else {
+          const float2 fk = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_k) + src);
+          const float2 fv = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_v) + src);
+          nk = f32_to_bf16_rne(fk.x) | (static_cast<uint32_t>(f32_to_bf16_rne(fk.y)) << 16);
+          nv = f32_to_bf16_rne(fv.x) | (static_cast<uint32_t>(f32_to_bf16_rne(fv.y)) << 16);
+        }
+        if (on) {
+          const int64_t off = (ring0 + (L - 1) % p.rcap) * D + d0;
+          *reinterpret_cast<uint32_t*>(p.rk + off) = nk;
+          *reinterpret_cast<uint32_t*>(p.rv + off) = nv;
+        }
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+          kw[u] = u == i ? nk : kw[u];
+          vw[u] = u == i ? nv : vw[u];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (c0 + i >= L) continue;  // uniform
+      const float kx = __uint_as_float(kw[i] << 16), ky = __uint_as_float(kw[i] & 0xffff0000u);
+      const float vx = __uint_as_float(vw[i] << 16), vy = __uint_as_float(vw[i] & 0xffff0000u);
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const float s = uniform(wave_sum(on ? fmaf(q0[j], kx, q1[j] * ky) : 0.0f)) * p.scale_log2;
+        const float mn = fmaxf(m[j], s);
+        const float f = m[j] == -INFINITY ? 0.0f : exp2f(m[j] - mn);
+        const float w = exp2f(s - mn);
+        l[j] = fmaf(l[j], f, w);
+        o0[j] = fmaf(o0[j], f, w * vx);
+        o1[j] = fmaf(o1[j], f, w * vy);
+        m[j] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    if (on) {
+      sm_fo[wave][j][d0] = o0[j];
+      sm_fo[wave][j][d0 + 1] = o1[j];
+    }
+    if (lane == 0) {
+      sm_fml[wave][j][0] = m[j];
+      sm_fml[wave][j][1] = l[j];
+    }
+  }
+  __syncthreads();
+  combine_waves<D, HPW, kStreamWaves, kStreamThreads>(sm_fo, sm_fml, sm_o, sm_ml);
+  __syncthreads();
+  finish_split<D, HPW, kStreamThreads>(p, b, h0, hg, ns8, ns8 + 1, sm_o, sm_ml);
+}
+
 // ---------------------------------------------------------------------------
 // Streaming kernel (head_dim 32, 64, 128).
 // ---------------------------------------------------------------------------
@@ -392,6 +529,10 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
+  if (split == p.ring_split) {  // recent window: the bf16 ring is a split of its own
+    ring_split<D, HPW, APPEND>(p, b, kvh, h0, hg, wave, lane, sm_fo, sm_fml, sm_o, sm_ml);
+    return;
+  }
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
   const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
 
@@ -401,7 +542,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // memory and are masked later), overlapping the length and query loads.
   // A length already read by the ranking bounds them (an empty split loads
   // nothing).
-  int t_end = min(known_len >= 0 ? known_len : p.len_cap, t_begin + p.split_len);
+  int t_end = min(known_len >= 0 ? max(known_len - p.rwin, 0) : p.len_cap, t_begin + p.split_len);
   int pn = -1;            // fused append: position of the new row (set once the length is known)
   bool owns_new = false;  // fused append: this workgroup's split holds it
 
@@ -665,8 +806,10 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     if constexpr (G32) {
       // w_g = 2^(S + log2 sV_g - m + 7) = E * (sV_g / sV_top) with
       // E = 2^(S + log2 sV_top - m + 7) <= 2^15; the normaliser takes
-      // 2^(S - m) = E / (128 sV_top).  One exponential per head.
-      const float inv = 1.0f / sv_top;
+      // 2^(S - m) = E / (128 sV_top).  One exponential per head.  A masked
+      // token (E = 0) may come from a row never written, whose scales are
+      // 0: its factor is taken as 0, not 1/0, so no 0 * inf enters the sums.
+      const float inv = valid ? 1.0f / sv_top : 0.0f;
       float E[HPW];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
@@ -753,9 +896,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     load_block_scales(blk, pq[0]);
   }
   // fused append: waves 0 and 1 fetch the new K and V rows of this KV head
+  // (with a recent window the row to quantize is the one leaving the ring,
+  // fetched once the length is known)
   constexpr int kEpl = row_epl(D);
   float xnew[kEpl];
-  if constexpr (APPEND) {
+  if (APPEND && p.rwin == 0) {
     const size_t esz = p.new_bf16 ? 2 : 4;
     const char* src = static_cast<const char*>(wave == 0 ? p.new_k : p.new_v) +
                       (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * esz;
@@ -766,15 +911,24 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads)
       p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
   }
-  if (t_begin >= L) return;  // this split has no tokens (and is not counted)
-  t_end = min(L, t_begin + p.split_len);
+  const int L8 = L > p.rwin ? L - p.rwin : 0;  // INT8 tokens (all of them without a recent window)
+  if (t_begin >= L8) return;  // this split has no tokens (and is not counted)
+  t_end = min(L8, t_begin + p.split_len);
   const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
-  const int ns = (L + p.split_len - 1) / p.split_len;
-  // fused append: the workgroup whose split holds position L-1 quantizes the
-  // new rows (abaddon kv_cache_quant_cuda.rs `quantize_tensor` steps), stores
-  // them in the cache, and keeps a copy in LDS for its own attention
-  pn = L - 1;
+  const int ns = (L8 + p.split_len - 1) / p.split_len + (p.ring_split >= 0 ? 1 : 0);
+  // fused append: the workgroup whose split holds position L8 - 1 quantizes
+  // the row that enters the INT8 part (abaddon kv_cache_quant_cuda.rs
+  // `quantize_tensor` steps), stores it in the cache, and keeps a copy in LDS
+  // for its own attention.  Without a recent window that row is the new one;
+  // with one it is the ring row at position L - 1 - W, which this step moves
+  // out of the window.
+  pn = L8 - 1;
   owns_new = APPEND && pn >= t_begin && pn < t_end;
+  if (APPEND && p.rwin > 0 && owns_new) {
+    const uint16_t* src = (wave == 0 ? p.rk : p.rv) +
+                          ((static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap + pn % p.rcap) * D;
+    load_row_values<kEpl>(src, lane, wave < 2 && lane < D / kEpl, true, xnew);
+  }
 
   if constexpr (APPEND) {
     if (owns_new) {
@@ -858,27 +1012,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     }
   }
   __syncthreads();
-  // ---- combine the four waves -----------------------------------------------------
-  for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads) {
-    const int j = idx / D, d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) M = fmaxf(M, sm_fml[w][j][0]);
-    float acc = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kStreamWaves; ++w) {
-      const float mw = sm_fml[w][j][0];
-      if (mw == -INFINITY) continue;
-      const float f = exp2f(mw - M);
-      acc = fmaf(sm_fo[w][j][d], f, acc);
-      lsum = fmaf(sm_fml[w][j][1], f, lsum);
-    }
-    sm_o[j][d] = acc;
-    if (d == 0) {
-      sm_ml[j][0] = M;
-      sm_ml[j][1] = lsum;
-    }
-  }
+  // ---- combine the waves ------------------------------------------------------------
+  combine_waves<D, HPW, kStreamWaves, kStreamThreads>(sm_fo, sm_fml, sm_o, sm_ml);
   __syncthreads();
   finish_split<D, HPW, kStreamThreads>(p, b, h0, hg, split, ns, sm_o, sm_ml);
 }
@@ -1146,8 +1281,11 @@ bool decode_supported(int head_dim) {
   return head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
 }
 
-DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc) {
   DecodePlan pl;
+  // with a recent window the INT8 splits cover at most max_seq_len - W tokens
+  const int ring = rc.window > 0 ? 1 : 0;
+  if (ring) max_seq_len = max_seq_len > rc.window ? max_seq_len - rc.window : 1;
   const int gqa = c.num_heads / c.num_kv_heads;
   pl.heads_per_wg = heads_per_wg(gqa);
   const int step = pass_tokens(c.head_dim);
@@ -1174,6 +1312,8 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
   pl.split_len = split;
   pl.num_splits = (max_seq_len + split - 1) / split;
   if (pl.num_splits < 1) pl.num_splits = 1;
+  pl.ring_split = ring ? pl.num_splits : -1;
+  pl.num_splits += ring;
   // Longest sequence first pays when workgroups are long (several rounds of
   // splits of 4096 tokens or more): ranking the lengths costs each workgroup
   // a read of the batch's lengths and about batch compare steps up front.
@@ -1190,7 +1330,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len) {
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
                          const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
                          int max_seq_len, hipStream_t stream, const void* new_k, const void* new_v,
-                         int new_dtype) {
+                         int new_dtype, const RecentGeom& rc) {
   const bool append = new_k != nullptr;
   const bool stream_kernel = use_stream(c.head_dim);
   if (append && !stream_kernel) {
@@ -1224,6 +1364,11 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   const int gqa = c.num_heads / c.num_kv_heads;
   p.wg_per_kvh = gqa / plan.heads_per_wg;
   p.longest_first = plan.longest_first && stream_kernel ? 1 : 0;
+  p.rk = rc.k;
+  p.rv = rc.v;
+  p.rwin = rc.window;
+  p.rcap = rc.cap;
+  p.ring_split = plan.ring_split;
   p.scale_log2 = attn_scale * kLog2e;
   dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, c.batch);
   if (grid.y > 65535 || grid.z > 65535)

@@ -32,13 +32,35 @@ inline int capacity_of(const kvq_cache& c) {
   return c.layout == KVQ_LAYOUT_PAGED ? c.max_blocks_per_seq * kPageSize : c.max_len;
 }
 
+// Recent window of a hybrid cache (window 0: none).
+struct RecentGeom {
+  int32_t window = 0;
+  int32_t cap = 0;       // ring slots per (sequence, KV head)
+  uint16_t* k = nullptr; // bf16 [B, KVH, cap, D]
+  uint16_t* v = nullptr;
+};
+
+inline RecentGeom recent_of(const kvq_recent* r) {
+  RecentGeom g;
+  if (r) {
+    g.window = r->window;
+    g.cap = r->capacity;
+    g.k = r->k;
+    g.v = r->v;
+  }
+  return g;
+}
+
 // ---- append / dequant -------------------------------------------------------
 // pos_from_lens: start_pos holds seq_lens and the single new row goes to
-// position seq_lens[b] - 1.
+// position seq_lens[b] - 1.  With a recent window the rows leaving it are
+// quantized first (a launch of its own), then the new rows go to the INT8
+// cache or the ring.
 kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_new, int in_dtype,
-                         int n_new, const int32_t* start_pos, hipStream_t stream, bool pos_from_lens = false);
+                         int n_new, const int32_t* start_pos, hipStream_t stream, bool pos_from_lens = false,
+                         const RecentGeom& rc = RecentGeom());
 kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens, int out_dtype,
-                          void* out, int out_len, hipStream_t stream);
+                          void* out, int out_len, hipStream_t stream, const RecentGeom& rc = RecentGeom());
 
 // ---- decode -----------------------------------------------------------------
 struct DecodePlan {
@@ -46,17 +68,21 @@ struct DecodePlan {
   int split_len;      // tokens per split (multiple of the kernel's pass size)
   int num_splits;     // splits per sequence for the hinted length
   bool longest_first; // workgroups take sequences in order of decreasing length
+  int ring_split;     // split index of the recent window (-1: none); counted in num_splits
   size_t counter_bytes;  // leading bytes of the workspace holding split counters
   size_t workspace;   // bytes of counters + split partials
 };
 bool decode_supported(int head_dim);
-DecodePlan plan_decode(const kvq_cache& c, int max_seq_len);
+// With a recent window the INT8 splits cover at most max_seq_len - window
+// tokens and one more split holds the ring.
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc = RecentGeom());
 // new_k / new_v non-null: fused append of one row per sequence at position
 // seq_lens[b] - 1 before the attention.
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
                          const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
                          int max_seq_len, hipStream_t stream, const void* new_k = nullptr,
-                         const void* new_v = nullptr, int new_dtype = KVQ_DT_BF16);
+                         const void* new_v = nullptr, int new_dtype = KVQ_DT_BF16,
+                         const RecentGeom& rc = RecentGeom());
 
 // ---- chunked prefill --------------------------------------------------------
 bool chunk_supported(int head_dim);

@@ -31,7 +31,9 @@ KVQ_DT_BF16 = 1
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_RANGE", 3: "UNSUPPORTED", 4: "HIP", 5: "WORKSPACE"}
 
 EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_append_decode", "kvq_attention_chunk", "kvq_dequant",
-            "kvq_workspace_size", "kvq_cache_bytes", "kvq_last_error", "kvq_version")
+            "kvq_workspace_size", "kvq_cache_bytes", "kvq_last_error", "kvq_version",
+            "kvq_append_recent", "kvq_attention_decode_recent", "kvq_append_decode_recent", "kvq_dequant_recent",
+            "kvq_workspace_size_recent")
 
 
 class KvqError(RuntimeError):
@@ -59,6 +61,16 @@ class kvq_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p),
         ("k_scales", ctypes.c_void_p),
         ("v_scales", ctypes.c_void_p),
+    ]
+
+
+class kvq_recent(ctypes.Structure):
+    """Mirror of ``struct kvq_recent`` in include/kvq.h."""
+    _fields_ = [
+        ("window", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
     ]
 
 
@@ -109,6 +121,17 @@ def _load():
     lib.kvq_workspace_size.restype = ctypes.c_size_t
     lib.kvq_cache_bytes.argtypes = [CP]
     lib.kvq_cache_bytes.restype = ctypes.c_uint64
+    RP = ctypes.POINTER(kvq_recent)
+    lib.kvq_append_recent.argtypes = [CP, RP, P, P, I, I, P, P]
+    lib.kvq_append_recent.restype = I
+    lib.kvq_attention_decode_recent.argtypes = [CP, RP, P, P, ctypes.c_float, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_attention_decode_recent.restype = I
+    lib.kvq_append_decode_recent.argtypes = [CP, RP, P, P, I, P, P, ctypes.c_float, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_append_decode_recent.restype = I
+    lib.kvq_dequant_recent.argtypes = [CP, RP, I, P, I, P, I, P]
+    lib.kvq_dequant_recent.restype = I
+    lib.kvq_workspace_size_recent.argtypes = [CP, RP, I]
+    lib.kvq_workspace_size_recent.restype = ctypes.c_size_t
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
@@ -211,3 +234,45 @@ def kvq_cache_bytes(cache: kvq_cache) -> int:
     if n == 0:
         raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
     return int(n)
+
+
+def make_recent(window: int, capacity: int, k, v) -> kvq_recent:
+    """Fill a ``kvq_recent`` descriptor (bf16 rings [B, KVH, capacity, D])."""
+    return kvq_recent(window, capacity, _ptr(k), _ptr(v))
+
+
+def _rp(recent):
+    return None if recent is None else ctypes.byref(recent)
+
+
+def kvq_append_recent(cache: kvq_cache, recent, k_new, v_new, in_dtype: int, n_new: int, start_pos, stream=None):
+    _check(_lib.kvq_append_recent(ctypes.byref(cache), _rp(recent), _ptr(k_new), _ptr(v_new), in_dtype, n_new,
+                                  _ptr(start_pos), _stream(stream)))
+
+
+def kvq_attention_decode_recent(cache: kvq_cache, recent, q, seq_lens, attn_scale: float, out, workspace,
+                                workspace_bytes: int, max_seq_len_hint: int, stream=None):
+    _check(_lib.kvq_attention_decode_recent(ctypes.byref(cache), _rp(recent), _ptr(q), _ptr(seq_lens), attn_scale,
+                                            _ptr(out), _ptr(workspace), workspace_bytes, max_seq_len_hint,
+                                            _stream(stream)))
+
+
+def kvq_append_decode_recent(cache: kvq_cache, recent, k_new, v_new, in_dtype: int, q, seq_lens,
+                             attn_scale: float, out, workspace, workspace_bytes: int, max_seq_len_hint: int,
+                             stream=None):
+    _check(_lib.kvq_append_decode_recent(ctypes.byref(cache), _rp(recent), _ptr(k_new), _ptr(v_new), in_dtype,
+                                         _ptr(q), _ptr(seq_lens), attn_scale, _ptr(out), _ptr(workspace),
+                                         workspace_bytes, max_seq_len_hint, _stream(stream)))
+
+
+def kvq_dequant_recent(cache: kvq_cache, recent, which: int, seq_lens, out_dtype: int, out, out_len: int,
+                       stream=None):
+    _check(_lib.kvq_dequant_recent(ctypes.byref(cache), _rp(recent), which, _ptr(seq_lens), out_dtype, _ptr(out),
+                                   out_len, _stream(stream)))
+
+
+def kvq_workspace_size_recent(cache: kvq_cache, recent, max_seq_len: int) -> int:
+    n = _lib.kvq_workspace_size_recent(ctypes.byref(cache), _rp(recent), max_seq_len)
+    if n == 0 and kvq_last_error():
+        raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
+    return n

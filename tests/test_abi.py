@@ -35,21 +35,23 @@ def test_every_declared_symbol_is_exported():
     assert exported == set(names), exported ^ set(names)
 
 
-def test_struct_layout_matches_header(tmp_path):
-    """sizeof/offsetof of kvq_cache from the C compiler equal the ctypes mirror."""
-    fields = [f for f, _ in kvq.kvq_cache._fields_]
+@pytest.mark.parametrize("struct", ["kvq_cache", "kvq_recent"])
+def test_struct_layout_matches_header(tmp_path, struct):
+    """sizeof/offsetof of each descriptor from the C compiler equal the ctypes mirror."""
+    mirror = getattr(kvq, struct)
+    fields = [f for f, _ in mirror._fields_]
     src = tmp_path / "layout.c"
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kvq.h"\nint main(void){\n'
-                   '  printf("%zu\\n", sizeof(kvq_cache));\n' +
-                   "".join(f'  printf("%zu\\n", offsetof(kvq_cache, {f}));\n' for f in fields) +
+                   f'  printf("%zu\\n", sizeof({struct}));\n' +
+                   "".join(f'  printf("%zu\\n", offsetof({struct}, {f}));\n' for f in fields) +
                    "  return 0;\n}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
                    check=True)
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(kvq.kvq_cache)
+    assert vals[0] == ctypes.sizeof(mirror)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(kvq.kvq_cache, f).offset == off, f
+        assert getattr(mirror, f).offset == off, f
 
 
 def _desc(**kw):
@@ -189,3 +191,38 @@ def test_python_binding_raises():
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_append(_desc(head_dim=48), FAKE, FAKE, 0, 1, FAKE, stream=0)
     assert e.value.status == kvq.KVQ_ERR_INVALID_ARG
+
+
+def _recent(window=4, capacity=5, k=FAKE, v=FAKE):
+    return kvq.make_recent(window, capacity, k, v)
+
+
+def test_recent_argument_errors():
+    """A recent-window descriptor is checked before anything is enqueued."""
+    d = ctypes.byref(_desc())
+    ws = kvq.kvq_workspace_size_recent(_desc(), _recent(), 64)
+    assert ws > kvq.kvq_workspace_size(_desc(), 64, 1) - 1
+    for bad, word in ((None, "NULL"), (_recent(window=0), "window"), (_recent(capacity=4), "capacity"),
+                      (_recent(k=None), "ring"), (_recent(v=None), "ring")):
+        r = None if bad is None else ctypes.byref(bad)
+        for name, args in (("kvq_append_recent", (FAKE, FAKE, 0, 1, FAKE, None)),
+                           ("kvq_attention_decode_recent", (FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)),
+                           ("kvq_append_decode_recent", (FAKE, FAKE, 0, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64,
+                                                         None)),
+                           ("kvq_dequant_recent", (0, FAKE, 0, FAKE, 8, None))):
+            st, msg = _status(name, d, r, *args)
+            assert st == kvq.KVQ_ERR_INVALID_ARG and word in msg, (name, msg)
+    r = ctypes.byref(_recent())
+    assert _status("kvq_attention_decode_recent", d, r, FAKE, FAKE, 0.1, FAKE, FAKE, ws - 1, 64, None)[0] == \
+        kvq.KVQ_ERR_WORKSPACE
+    d256 = ctypes.byref(_desc(head_dim=256))
+    assert _status("kvq_attention_decode_recent", d256, r, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)[0] == \
+        kvq.KVQ_ERR_UNSUPPORTED
+    assert _status("kvq_append_recent", d, r, FAKE, FAKE, 0, 65, FAKE, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
+
+
+def test_recent_workspace_counts_the_ring_split():
+    """The ring adds one split partial per (sequence, head)."""
+    base = kvq.kvq_workspace_size(_desc(max_len=4096), 4096, 1)
+    with_ring = kvq.kvq_workspace_size_recent(_desc(max_len=4096), _recent(window=128, capacity=129), 4096)
+    assert with_ring > 0 and with_ring != base

@@ -217,3 +217,36 @@ def test_longest_first_order(kvq, monkeypatch, paged, fused):
     assert np.all(outs["1"][~live] == 0)
     ref = _oracle_decode(x["k"][live], x["v"][live], qv[live], lens_np[live], scale, 0)
     assert_attention_close(outs["1"][live], ref, "longest first")
+
+
+@pytest.mark.parametrize("group,paged", [(32, False), (0, False), (32, True)])
+def test_short_sequences_in_unwritten_cache(kvq, group, paged):
+    """Sequences much shorter than a zero-initialised cache: the first block's
+    loads run ahead of the length and read rows never written (zero scales),
+    which must not reach the result."""
+    import torch
+    lens = [10, 1, 63, 65]
+    B, H, KVH, D = len(lens), 32, 8, 128
+    cap = 512
+    log(f"decode: short sequences in an unwritten cache, group={group} paged={paged}")
+    rng = np.random.default_rng(51 + group + paged)
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, max(lens), D), "bf16")
+    qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, D))
+    if paged:
+        table, npages = random_block_table(rng, [cap] * B)
+        cache = kvq.Int8KVCache(B, H, KVH, D, num_pages=npages, block_table=dev_tensor(table),
+                                group32=(group == 32), fill=0)
+    else:
+        cache = kvq.Int8KVCache(B, H, KVH, D, max_len=cap, group32=(group == 32), fill=0)
+    # only each sequence's own rows are written: row i of sequence b for i < lens[b]
+    for i in range(max(lens)):
+        live = np.asarray([i < L for L in lens])
+        if not live.any():
+            break
+        pos = np.where(live, i, cap + 10).astype(np.int32)   # rows past the capacity are not written
+        cache.append(kv_dev(np.ascontiguousarray(x["k_raw"][:, :, i:i + 1])),
+                     kv_dev(np.ascontiguousarray(x["v_raw"][:, :, i:i + 1])), dev_tensor(pos))
+    out = cache.decode(bf16_dev(qb), dev_tensor(np.asarray(lens, np.int32)), 0.088, cap)
+    torch.cuda.synchronize()
+    ref = _oracle_decode(x["k"], x["v"], qv, lens, 0.088, group)
+    assert_attention_close(to_host_bits(out), ref, "short sequences")
