@@ -68,6 +68,17 @@ def step_bytes(w: wl.Workload, L: int) -> dict:
     B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
     G = 1 if w.group == 0 else D // 32
     in_bytes = 4 if w.kv_dtype == "f32" else 2
+    W = w.extra.get("window", 0)
+    if W:
+        # recent window: INT8 rows below L - W (the row leaving the window is
+        # written once, as codes and scale), W + 1 bf16 ring rows (the W - 1
+        # attended ones, the one read for eviction, the new one written), the
+        # new input row, queries and outputs
+        int8 = 2 * B * KVH * (L - W) * (D + 4 * G)
+        ring = 2 * B * KVH * (W + 1) * D * 2
+        qo = 2 * B * H * D * 2
+        app_in = 2 * B * KVH * D * in_bytes
+        return {"decode": int8 + ring + qo, "append": app_in, "step": int8 + ring + qo + app_in}
     codes = 2 * B * KVH * L * D
     scales = 2 * B * KVH * L * G * 4
     q = B * H * D * 2
@@ -123,7 +134,7 @@ def build_layers(w: wl.Workload, kvq, torch, stream, threads: int):
                 li = len(layers)
                 x = done_layers.pop(li)
                 cache = kvq.Int8KVCache(w.batch, w.num_heads, w.num_kv_heads, w.head_dim, max_len=w.max_len,
-                                        group32=(w.group == 32))
+                                        group32=(w.group == 32), recent_window=w.extra.get("window", 0))
                 k_raw, v_raw = x["k_raw"], x["v_raw"]
                 tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
 
@@ -160,6 +171,44 @@ def blas_thread_count() -> int:
         return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
         return 1
+
+
+def cpu_baseline_recent(w: wl.Workload, target_s: float = 12.0):
+    """The oracle's hybrid cache on whole sequences of layer 0: append the new
+    token (the row leaving the window is quantized) and attend over the
+    get_kv view, per sequence."""
+    import copy
+    import oracle as orc
+    blas_threads = blas_thread_count()
+    T = w.ctx + w.n_new
+    W = w.extra["window"]
+    x = wl.layer_inputs(w, 0)
+    base = []
+    for b in range(w.batch):
+        c = orc.RecentWindowCache(w.num_kv_heads, w.head_dim, W, w.group)
+        c.append(x["k"][b, :, :w.ctx], x["v"][b, :, :w.ctx])
+        base.append(c)
+
+    def one_seq(b):
+        c = copy.deepcopy(base[b])
+        c.append(x["k"][b, :, w.ctx:T], x["v"][b, :, w.ctx:T])
+        return orc.attention_decode_recent(x["q"][b:b + 1], [c], w.attn_scale)
+
+    per_seq_bytes = step_bytes(w, T)["step"] / w.batch
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        one_seq(done % w.batch)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    rate = per_seq_bytes * done / el / 1e12
+    return {"value": rate, "unit": "TB/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{done} sequences of layer 0 ({done / w.batch:.2f} layer-steps: append 1 token to the "
+                      f"hybrid cache (window {W}) + fp64 attention over {T} tokens, 32 heads), {el:.1f}s wall; "
+                      f"BLAS threads {blas_threads}; host {platform.processor() or 'x86_64'} nproc {os.cpu_count()}",
+            "seconds": el}
 
 
 def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
@@ -467,7 +516,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode"])
+    ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
+                                                            "recent_window"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -536,7 +586,8 @@ def main():
                 ly["cache"].append_decode(ly["k_new"], ly["v_new"], ly["q"], seq_lens, w.attn_scale, T,
                                           out=ly["out"], workspace=ws, stream=stream)
         kernel_pass = step
-        kernel_name, kernel_bytes = "kvq_append_decode", "step"
+        kernel_name = "kvq_append_decode_recent" if w.extra.get("window") else "kvq_append_decode"
+        kernel_bytes = "step"
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -578,7 +629,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline_recent(w) if w.extra.get("window") else cpu_baseline(w)
         cpu.pop("seconds", None)
 
     result = {
@@ -599,6 +650,8 @@ def main():
         "config": {"workload": f"{w.name}: batch {w.batch}, {w.num_heads} q / {w.num_kv_heads} kv heads, "
                                f"head_dim {w.head_dim}, context {T}, "
                                f"{'per-token' if w.group == 0 else 'group-32'} fp32 scales, {w.layers} layers, "
+                               + (f"last {w.extra['window']} tokens bf16 (recent window), " if w.extra.get("window")
+                                  else "") +
                                f"append 1 token + decode per layer "
                                f"({'two launches' if args.separate else 'one fused launch'})",
                    "batch": w.batch, "seq_len": T, "layers": w.layers, "bytes_per_step": total_bytes},

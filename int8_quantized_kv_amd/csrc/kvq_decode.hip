@@ -77,10 +77,10 @@ struct DecodeParams {
   int32_t longest_first;     // workgroup z takes the z-th longest sequence (batch <= kLongestFirstMax)
   float scale_log2;          // attn_scale * log2(e)
   // recent window (hybrid cache): the last rwin positions are bf16 rows in
-  // ring slot (position % rcap); split index ring_split (-1: none) holds them
+  // ring slot (position % rcap), attended by the workgroup of the last INT8 split
   uint16_t* rk;              // [B, KVH, rcap, D] bf16
   uint16_t* rv;
-  int32_t rwin, rcap, ring_split;
+  int32_t rwin, rcap;        // rwin 0: no recent window
 };
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* x) {
@@ -385,60 +385,76 @@ __device__ __forceinline__ void combine_waves(const float (*sm_fo)[HPW][D], cons
 }
 
 // ---------------------------------------------------------------------------
-// Recent-window split (abaddon 0.2.0-rc.1 kv_cache_quant_cuda.rs,
-// `OptimizedQuantizedKvCache::get_kv`: the unquantized recent rows follow
-// the dequantized old ones).  Positions [L - W, L) are bf16 rows in ring
-// slots position % rcap; this workgroup attends its HPW heads to them with
-// fp32 arithmetic and leaves one more split partial, index = the number of
-// INT8 splits.  Each lane holds two dims; each wave takes 16-token chunks
-// (loads of a chunk in flight together) with an exact running maximum.  The
-// fused step's new row (position L - 1) comes from the input, rounded to
-// bf16, and is stored in its ring slot by the wave that attends to it.
+// Recent window (abaddon 0.2.0-rc.1 kv_cache_quant_cuda.rs,
+// `OptimizedQuantizedKvCache::get_kv`: the unquantized recent rows follow the
+// dequantized old ones).  Positions [L - W, L) are bf16 rows in ring slots
+// position % rcap.  The workgroup of the last INT8 split attends to them too:
+// after its INT8 blocks, each wave takes 16-token chunks of the ring (loads
+// of a chunk in flight together; two dims per lane; fp32 arithmetic with an
+// exact running maximum) and merges the result into its own (m, l, o) in
+// LDS, which the wave combine then sums as usual.  The fused step's new row
+// (position L - 1) comes from the input, rounded to bf16, and is stored in
+// its ring slot by the wave that attends to it.
 // ---------------------------------------------------------------------------
 template <int D, int HPW, bool APPEND>
-__device__ void ring_split(const DecodeParams& p, int b, int kvh, int h0, int hg, int wave, int lane,
-                           float (*sm_fo)[HPW][D], float (*sm_fml)[HPW][2], float (*sm_o)[D],
-                           float (*sm_ml)[2]) {
-  constexpr int kChunk = 16;
-  const int L = clamp_len(p, b);
-  if (L == 0) return;  // nothing to attend to (split 0 writes the zeros); not counted
-  const int L8 = L > p.rwin ? L - p.rwin : 0;
-  const int ns8 = (L8 + p.split_len - 1) / p.split_len;
+__device__ void ring_into_wave(const DecodeParams& p, int b, int kvh, int h0, int wave, int lane, int L, int L8,
+                               float (*fo)[D], float (*fml)[2], float* scratch) {
+  constexpr int kChunk = 16;            // tokens per wave pass
+  constexpr int kQ = kWave / kChunk;    // lanes per token for the scores
+  constexpr int kDQ = D / kQ;           // dims per lane for the scores
   const int H = p.num_heads;
-  const bool on = lane < D / 2;
+  // this wave's LDS: fp32 queries [HPW][D], then the pass's weights [16] x 4
+  float* sq = scratch;
+  float4* sw = reinterpret_cast<float4*>(scratch + HPW * D);
+  const bool on = lane < D / 2;         // value lanes: dims (2 lane, 2 lane + 1)
   const int d0 = 2 * (on ? lane : 0);
-  float q0[HPW], q1[HPW], m[HPW], l[HPW], o0[HPW], o1[HPW];
+  const int tt = lane / kQ, qd = lane % kQ;
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    const uint32_t w = on ? *reinterpret_cast<const uint32_t*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + d0) : 0u;
-    q0[j] = __uint_as_float(w << 16);
-    q1[j] = __uint_as_float(w & 0xffff0000u);
+    if (on) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + d0);
+      sq[j * D + d0] = __uint_as_float(w << 16);
+      sq[j * D + d0 + 1] = __uint_as_float(w & 0xffff0000u);
+    }
+  }
+  float m[HPW], l[HPW], o0[HPW], o1[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
     m[j] = -INFINITY;
     l[j] = 0.0f;
     o0[j] = 0.0f;
     o1[j] = 0.0f;
   }
   const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
+  const int64_t new0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D;
   for (int c0 = L8 + wave * kChunk; c0 < L; c0 += kStreamWaves * kChunk) {
-    uint32_t kw[kChunk], vw[kChunk];
+    // scores: token c0 + tt, dims [qd kDQ, (qd + 1) kDQ)
+    const int t = c0 + tt;
+    const int tc = min(t, L - 1);
+    uint32_t kq[kDQ / 2];
+    {
+      const uint16_t* kr = p.rk + (ring0 + tc % p.rcap) * D + qd * kDQ;
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      const int t = min(c0 + i, L - 1);
-      const int64_t off = (ring0 + t % p.rcap) * D + d0;
-      kw[i] = *reinterpret_cast<const uint32_t*>(p.rk + off);
-      vw[i] = *reinterpret_cast<const uint32_t*>(p.rv + off);
+      for (int u = 0; u < kDQ / 2; u += 4)
+        *reinterpret_cast<uint4*>(&kq[u]) = *reinterpret_cast<const uint4*>(kr + 2 * u);
     }
+    // values: this lane's dim pair of the pass's 16 tokens
+    uint32_t vw[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      vw[i] = *reinterpret_cast<const uint32_t*>(p.rv + (ring0 + min(c0 + i, L - 1) % p.rcap) * D + d0);
     if constexpr (APPEND) {
-      const int i = L - 1 - c0;  // the new row, if this chunk holds it
-      if (i >= 0 && i < kChunk) {
-        const int64_t src = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D + d0;
+      // the new row (position L - 1): from the input, rounded to bf16, and
+      // stored in its ring slot
+      const int inew = L - 1 - c0;
+      if (inew >= 0 && inew < kChunk) {
         uint32_t nk, nv;
         if (p.new_bf16) {
-          nk = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_k) + src);
-          nv = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_v) + src);
+          nk = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_k) + new0 + d0);
+          nv = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_v) + new0 + d0);
         } else {
-          const float2 fk = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_k) + src);
-          const float2 fv = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_v) + src);
+          const float2 fk = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_k) + new0 + d0);
+          const float2 fv = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_v) + new0 + d0);
           nk = f32_to_bf16_rne(fk.x) | (static_cast<uint32_t>(f32_to_bf16_rne(fk.y)) << 16);
           nv = f32_to_bf16_rne(fv.x) | (static_cast<uint32_t>(f32_to_bf16_rne(fv.y)) << 16);
         }
@@ -448,45 +464,81 @@ __device__ void ring_split(const DecodeParams& p, int b, int kvh, int h0, int hg
           *reinterpret_cast<uint32_t*>(p.rv + off) = nv;
         }
 #pragma unroll
-        for (int u = 0; u < kChunk; ++u) {
-          kw[u] = u == i ? nk : kw[u];
-          vw[u] = u == i ? nv : vw[u];
+        for (int u = 0; u < kChunk; ++u) vw[u] = u == inew ? nv : vw[u];
+        if (tt == inew) {  // this token's score lanes take their K dims from the input
+#pragma unroll
+          for (int u = 0; u < kDQ / 2; ++u) {
+            const int d = qd * kDQ + 2 * u;
+            if (p.new_bf16) {
+              kq[u] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.new_k) + new0 + d);
+            } else {
+              const float2 fk = *reinterpret_cast<const float2*>(static_cast<const float*>(p.new_k) + new0 + d);
+              kq[u] = f32_to_bf16_rne(fk.x) | (static_cast<uint32_t>(f32_to_bf16_rne(fk.y)) << 16);
+            }
+          }
         }
       }
     }
+    float sc[HPW];
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kDQ / 2; ++u) {
+        const float2 qq = *reinterpret_cast<const float2*>(sq + j * D + qd * kDQ + 2 * u);
+        acc = fmaf(qq.x, __uint_as_float(kq[u] << 16), acc);
+        acc = fmaf(qq.y, __uint_as_float(kq[u] & 0xffff0000u), acc);
+      }
+      acc += __shfl_xor(acc, 1, kWave);  // sum over the token's 4 lanes
+      acc += __shfl_xor(acc, 2, kWave);
+      sc[j] = t < L ? acc * p.scale_log2 : -INFINITY;
+    }
+    // softmax over the pass, one reduction per head
+    float4 wt = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {
+      const float cm = uniform(wave_max(sc[j]));
+      const float mn = fmaxf(m[j], cm);
+      const float f = m[j] == -INFINITY ? 0.0f : exp2f(m[j] - mn);
+      const float w = t < L ? exp2f(sc[j] - mn) : 0.0f;
+      l[j] = fmaf(l[j], f, uniform(wave_sum(qd == 0 ? w : 0.0f)));
+      o0[j] *= f;
+      o1[j] *= f;
+      m[j] = mn;
+      (&wt.x)[j] = w;
+    }
+    if (qd == 0) sw[tt] = wt;
+    wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       if (c0 + i >= L) continue;  // uniform
-      const float kx = __uint_as_float(kw[i] << 16), ky = __uint_as_float(kw[i] & 0xffff0000u);
+      const float4 wi = sw[i];
       const float vx = __uint_as_float(vw[i] << 16), vy = __uint_as_float(vw[i] & 0xffff0000u);
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
-        const float s = uniform(wave_sum(on ? fmaf(q0[j], kx, q1[j] * ky) : 0.0f)) * p.scale_log2;
-        const float mn = fmaxf(m[j], s);
-        const float f = m[j] == -INFINITY ? 0.0f : exp2f(m[j] - mn);
-        const float w = exp2f(s - mn);
-        l[j] = fmaf(l[j], f, w);
-        o0[j] = fmaf(o0[j], f, w * vx);
-        o1[j] = fmaf(o1[j], f, w * vy);
-        m[j] = mn;
+        o0[j] = fmaf((&wi.x)[j], vx, o0[j]);
+        o1[j] = fmaf((&wi.x)[j], vy, o1[j]);
       }
     }
+    wave_lds_sync();  // the next pass rewrites the weights
   }
+  // merge into this wave's (m, l, o): both are relative to their own 2^m
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
+    const float m1 = fml[j][0], l1 = fml[j][1];
+    const float M = fmaxf(m1, m[j]);
+    const float f1 = m1 == -INFINITY ? 0.0f : exp2f(m1 - M);
+    const float f2 = m[j] == -INFINITY ? 0.0f : exp2f(m[j] - M);
     if (on) {
-      sm_fo[wave][j][d0] = o0[j];
-      sm_fo[wave][j][d0 + 1] = o1[j];
+      fo[j][d0] = fmaf(fo[j][d0], f1, o0[j] * f2);
+      fo[j][d0 + 1] = fmaf(fo[j][d0 + 1], f1, o1[j] * f2);
     }
+    wave_lds_sync();  // every lane has read fml[j] before lane 0 rewrites it
     if (lane == 0) {
-      sm_fml[wave][j][0] = m[j];
-      sm_fml[wave][j][1] = l[j];
+      fml[j][0] = M;
+      fml[j][1] = fmaf(l1, f1, l[j] * f2);
     }
   }
-  __syncthreads();
-  combine_waves<D, HPW, kStreamWaves, kStreamThreads>(sm_fo, sm_fml, sm_o, sm_ml);
-  __syncthreads();
-  finish_split<D, HPW, kStreamThreads>(p, b, h0, hg, ns8, ns8 + 1, sm_o, sm_ml);
 }
 
 // ---------------------------------------------------------------------------
@@ -529,10 +581,6 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  if (split == p.ring_split) {  // recent window: the bf16 ring is a split of its own
-    ring_split<D, HPW, APPEND>(p, b, kvh, h0, hg, wave, lane, sm_fo, sm_fml, sm_o, sm_ml);
-    return;
-  }
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
   const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
 
@@ -912,10 +960,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
   }
   const int L8 = L > p.rwin ? L - p.rwin : 0;  // INT8 tokens (all of them without a recent window)
-  if (t_begin >= L8) return;  // this split has no tokens (and is not counted)
+  const int ns8 = (L8 + p.split_len - 1) / p.split_len;
+  // recent window: the workgroup of the last INT8 split (split 0 if there is
+  // none) also attends to the ring
+  const bool ring_here = p.rwin > 0 && L > 0 && split == (ns8 > 0 ? ns8 - 1 : 0);
+  if (t_begin >= L8 && !ring_here) return;  // this split has no tokens (and is not counted)
   t_end = min(L8, t_begin + p.split_len);
-  const int nblk = (t_end - t_begin + kBlock - 1) / kBlock;
-  const int ns = (L8 + p.split_len - 1) / p.split_len + (p.ring_split >= 0 ? 1 : 0);
+  const int nblk = t_end > t_begin ? (t_end - t_begin + kBlock - 1) / kBlock : 0;
+  const int ns = ns8 > 0 ? ns8 : 1;
   // fused append: the workgroup whose split holds position L8 - 1 quantizes
   // the row that enters the INT8 part (abaddon kv_cache_quant_cuda.rs
   // `quantize_tensor` steps), stores it in the cache, and keeps a copy in LDS
@@ -1010,6 +1062,13 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         sm_fml[wave][j][1] = l[j];
       }
     }
+  }
+  if (ring_here) {
+    // this wave's INT8 result is in sm_fo / sm_fml; its score staging area is
+    // free (only this wave uses it)
+    wave_lds_sync();
+    ring_into_wave<D, HPW, APPEND>(p, b, kvh, h0, wave, lane, L, L8, sm_fo[wave], sm_fml[wave],
+                                   reinterpret_cast<float*>(&sm_part[wave][0]));
   }
   __syncthreads();
   // ---- combine the waves ------------------------------------------------------------
@@ -1312,8 +1371,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   pl.split_len = split;
   pl.num_splits = (max_seq_len + split - 1) / split;
   if (pl.num_splits < 1) pl.num_splits = 1;
-  pl.ring_split = ring ? pl.num_splits : -1;
-  pl.num_splits += ring;
+
   // Longest sequence first pays when workgroups are long (several rounds of
   // splits of 4096 tokens or more): ranking the lengths costs each workgroup
   // a read of the batch's lengths and about batch compare steps up front.
@@ -1368,7 +1426,6 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   p.rv = rc.v;
   p.rwin = rc.window;
   p.rcap = rc.cap;
-  p.ring_split = plan.ring_split;
   p.scale_log2 = attn_scale * kLog2e;
   dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, c.batch);
   if (grid.y > 65535 || grid.z > 65535)

@@ -68,13 +68,12 @@ struct DecodePlan {
   int split_len;      // tokens per split (multiple of the kernel's pass size)
   int num_splits;     // splits per sequence for the hinted length
   bool longest_first; // workgroups take sequences in order of decreasing length
-  int ring_split;     // split index of the recent window (-1: none); counted in num_splits
   size_t counter_bytes;  // leading bytes of the workspace holding split counters
   size_t workspace;   // bytes of counters + split partials
 };
 bool decode_supported(int head_dim);
 // With a recent window the INT8 splits cover at most max_seq_len - window
-// tokens and one more split holds the ring.
+// tokens; the last one's workgroup also attends to the ring.
 DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc = RecentGeom());
 // new_k / new_v non-null: fused append of one row per sequence at position
 // seq_lens[b] - 1 before the attention.

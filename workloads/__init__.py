@@ -81,7 +81,13 @@ PAGED = Workload("paged_decode", 64, 32, 8, 128, 0, "paged", "bf16", 0, 1, seed=
 CHUNK = Workload("chunked_prefill", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512,
                  seed=4)
 
-ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK)}
+# The 8B-shaped decode step on a recent-window hybrid cache: the last 128
+# tokens of every sequence stay bf16 (the window the hybrid cache's default
+# configuration keeps), the older ones are INT8.
+RECENT = Workload("recent_window", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
+                  layers=32, outliers=4, seed=5, extra={"window": 128})
+
+ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT)}
 
 
 # ----------------------------------------------------------------------------
