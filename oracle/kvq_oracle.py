@@ -245,29 +245,42 @@ def softmax_attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, attn_scale: floa
     return p @ v
 
 
+def window_visible(positions: np.ndarray, p: int, window: int) -> np.ndarray:
+    """Keys a query at absolute position p may see: t <= p, and with a
+    sliding window w also t > p - w ([P4] `KVCache::attention_opts` doc,
+    keys in (p - w, p]; `attend`, `too_old` = k + w - 1 < p)."""
+    vis = positions <= p
+    if window > 0:
+        vis &= positions > p - window
+    return vis
+
+
 def attention_decode(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray,
-                     seq_lens, attn_scale: float) -> np.ndarray:
+                     seq_lens, attn_scale: float, window: int = 0) -> np.ndarray:
     """Decode attention, one query token per sequence.
 
     ``q`` [B, H, D] (exact bf16 values as floats), ``k_hat``/``v_hat``
     [B, KVH, >=L, D] dequantized (fp64), ``seq_lens`` [B] attended lengths.
-    A single query at the end of the window sees every cached token, so no
-    mask applies ([P4] `attend`, the decode comment).  Returns [B, H, D] fp64.
+    The query sits at position L - 1.  Without a window it sees every cached
+    token, so no mask applies ([P4] `attend`, the decode comment); a sliding
+    window ``window`` > 0 keeps only keys in (L - 1 - window, L - 1].
+    Returns [B, H, D] fp64.
     """
     bsz, nh, d = q.shape
     nkv = k_hat.shape[1]
     out = np.zeros((bsz, nh, d), dtype=np.float64)
     for b in range(bsz):
         length = int(seq_lens[b])
+        vis = window_visible(np.arange(length), length - 1, window) if window > 0 else None
         for h in range(nh):
             g = kv_head_of(h, nh, nkv)
             out[b, h] = softmax_attend(q[b, h].astype(np.float64), k_hat[b, g, :length],
-                                       v_hat[b, g, :length], attn_scale)
+                                       v_hat[b, g, :length], attn_scale, vis)
     return out
 
 
 def attention_chunk(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, ctx_lens,
-                    causal: bool, attn_scale: float) -> np.ndarray:
+                    causal: bool, attn_scale: float, window: int = 0) -> np.ndarray:
     """Chunked-prefill attention for n new queries per sequence.
 
     ``q`` [B, H, n, D]; ``k_hat``/``v_hat`` [B, KVH, >=L0+n, D] with the chunk
@@ -275,7 +288,9 @@ def attention_chunk(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, ctx_len
     absolute position L0 + i and, when causal, sees keys t <= L0 + i
     (bottom-right alignment: [P1] `forward_attention`, cache_offset = seq_len
     - q_len; [P4] `attend`, keys > pos forbidden).  Non-causal queries see all
-    L0 + n keys.  Returns [B, H, n, D] fp64.
+    L0 + n keys.  A sliding window ``window`` > 0 implies the causal bound
+    and also hides keys t <= L0 + i - window ([P4] `attend`: the window mask
+    is OR-ed onto the causal one).  Returns [B, H, n, D] fp64.
     """
     bsz, nh, n, d = q.shape
     nkv = k_hat.shape[1]
@@ -289,7 +304,10 @@ def attention_chunk(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, ctx_len
             kk = k_hat[b, g, :total]
             vv = v_hat[b, g, :total]
             for i in range(n):
-                vis = (t <= l0 + i) if causal else None
+                if window > 0:
+                    vis = window_visible(t, l0 + i, window)
+                else:
+                    vis = (t <= l0 + i) if causal else None
                 out[b, h, i] = softmax_attend(q[b, h, i].astype(np.float64), kk, vv,
                                               attn_scale, vis)
     return out

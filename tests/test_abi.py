@@ -221,8 +221,8 @@ def test_recent_argument_errors():
     assert _status("kvq_append_recent", d, r, FAKE, FAKE, 0, 65, FAKE, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
 
 
-def test_recent_workspace_counts_the_ring_split():
-    """The ring adds one split partial per (sequence, head)."""
-    base = kvq.kvq_workspace_size(_desc(max_len=4096), 4096, 1)
+def test_recent_workspace_is_the_int8_parts():
+    """The ring adds no split of its own (the last INT8 split's workgroup
+    attends to it): the workspace is that of the INT8 part, hint - W."""
     with_ring = kvq.kvq_workspace_size_recent(_desc(max_len=4096), _recent(window=128, capacity=129), 4096)
-    assert with_ring > 0 and with_ring != base
+    assert with_ring > 0 and with_ring == kvq.kvq_workspace_size(_desc(max_len=4096), 4096 - 128, 1)

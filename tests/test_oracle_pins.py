@@ -591,3 +591,87 @@ def test_recent_memory_savings(golden):
     assert got == by_hand == 2_112_256
     full = g["tokens"] * g["kv_heads"] * g["head_dim"] * 2 * 2
     assert full / got > g["min_savings"]
+
+
+# ----------------------------------------------------------------------------
+# sliding-window attention (combs-models kv.rs, attention_opts window)
+# ----------------------------------------------------------------------------
+
+def _sliding_layer_outputs(K, V, Q, window, scale, prefill, steps):
+    """The page's sliding layer, step by step with Python floats: a store of
+    the last window - 1 (key, value) pairs; each call concatenates the store
+    with the new tokens, re-bases the query positions by the first stored
+    key's absolute position, masks keys after the query or at least window
+    positions before it, attends, then keeps the trailing window - 1 tokens.
+    K/V: [KVH, T, D]; Q: [H, T, D].  Returns {position: [H, D]}."""
+    n_kv, _, d = K.shape
+    n_q = Q.shape[0]
+    store = []   # absolute positions held by the sliding store
+    outs = {}
+    calls = [(0, prefill)] + [(p, 1) for p in range(prefill, steps)]
+    for pos, seq in calls:
+        full = store + list(range(pos, pos + seq))
+        kv_offset = pos + seq - len(full)
+        for i in range(seq):
+            qpos = pos - kv_offset + i          # query position in the concat
+            o = np.zeros((n_q, d))
+            for h in range(n_q):
+                g = h // (n_q // n_kv)
+                s = []
+                for kpos in range(len(full)):
+                    forbidden = kpos > qpos or kpos + window - 1 < qpos
+                    s.append(-math.inf if forbidden else
+                             scale * sum(float(Q[h, pos + i, e]) * float(K[g, full[kpos], e]) for e in range(d)))
+                m = max(s)
+                w = [math.exp(x - m) if x != -math.inf else 0.0 for x in s]
+                z = sum(w)
+                for e in range(d):
+                    o[h, e] = sum(w[k] * float(V[g, full[k], e]) for k in range(len(full))) / z
+            outs[pos + i] = o
+        keep = min(len(full), window - 1)
+        store = full[len(full) - keep:]
+    return outs
+
+
+def test_sliding_layer_matches_masked_global(golden):
+    """combs-models `sliding_layer_matches_masked_global`: the evicting
+    sliding layer equals attention over everything with the window applied
+    as a mask (the oracle's definition), through a prefill chunk longer than
+    the window and decode steps well past it."""
+    g = golden["sliding_vs_masked_global"]
+    n_kv, n_q, d, w = g["n_kv"], g["n_q"], g["head_dim"], g["window"]
+    scale = 0.9 / math.sqrt(d)
+    T = g["decode_to"]
+    K = np.stack([_kv_tok(i, n_kv, d, 0) for i in range(T)], axis=1)   # [KVH, T, D]
+    V = np.stack([_kv_tok(i, n_kv, d, 5) for i in range(T)], axis=1)
+    Q = np.stack([_q_tok(i, n_q, d) for i in range(T)], axis=1)        # [H, T, D]
+    sliding = _sliding_layer_outputs(K, V, Q, w, scale, g["prefill"], T)
+    P = g["prefill"]
+    chunk = orc.attention_chunk(Q[None, :, :P].astype(np.float64), K[None].astype(np.float64),
+                                V[None].astype(np.float64), [0], True, scale, window=w)
+    for i in range(P):
+        assert np.allclose(chunk[0, :, i], sliding[i], rtol=0, atol=1e-12), i
+    for pos in range(P, T):
+        dec = orc.attention_decode(Q[None, :, pos].astype(np.float64), K[None].astype(np.float64),
+                                   V[None].astype(np.float64), [pos + 1], scale, window=w)
+        assert np.allclose(dec[0], sliding[pos], rtol=0, atol=1e-12), pos
+
+
+def test_window_closed_forms():
+    """Window 1: each query sees only its own key, so the output is its V
+    row.  A window at least the length changes nothing."""
+    rng = np.random.default_rng(61)
+    k = rng.standard_normal((1, 2, 9, 8))
+    v = rng.standard_normal((1, 2, 9, 8))
+    q = rng.standard_normal((1, 4, 8))
+    one = orc.attention_decode(q, k, v, [9], 0.5, window=1)
+    for h in range(4):
+        assert np.allclose(one[0, h], v[0, h // 2, 8], rtol=0, atol=1e-15)
+    assert np.array_equal(orc.attention_decode(q, k, v, [9], 0.5, window=9), orc.attention_decode(q, k, v, [9], 0.5))
+    qc = rng.standard_normal((1, 4, 3, 8))
+    c1 = orc.attention_chunk(qc, k, v, [6], True, 0.5, window=1)
+    for i in range(3):
+        for h in range(4):
+            assert np.allclose(c1[0, h, i], v[0, h // 2, 6 + i], rtol=0, atol=1e-15)
+    assert np.array_equal(orc.attention_chunk(qc, k, v, [6], True, 0.5, window=9),
+                          orc.attention_chunk(qc, k, v, [6], True, 0.5))
