@@ -193,6 +193,36 @@ kvq_status kvq_dequant(const kvq_cache* cache, int32_t which, const int32_t* seq
                        int32_t out_dtype, void* out, int32_t out_len, void* stream);
 
 /*
+ * Sliding-window attention (combs-models 0.2.2 src/kv.rs,
+ * `KVCache::attention_opts` with `window`, and `attend`): a query at absolute
+ * position p attends only to keys in (p - window, p]; older keys stay cached
+ * but are masked out.  The window implies the causal bound.  window >= 1;
+ * a window at least the sequence length gives the plain result.
+ *
+ * kvq_attention_decode_window / kvq_append_decode_window: as
+ * kvq_attention_decode / kvq_append_decode, the query at position
+ * seq_lens[b] - 1 seeing the last min(window, seq_lens[b]) tokens.
+ * Workspace: kvq_workspace_size_window(cache, hint, 1, window).
+ * kvq_attention_chunk_window: as kvq_attention_chunk with causal = 1, query i
+ * at position ctx_lens[b] + i seeing keys in (ctx_lens[b] + i - window,
+ * ctx_lens[b] + i].  Workspace: kvq_workspace_size_window(cache, hint + n, n,
+ * window) (0 for the current kernel).
+ * Errors: those of the plain entry points, plus INVALID_ARG for window < 1.
+ */
+kvq_status kvq_attention_decode_window(const kvq_cache* cache, const uint16_t* q, const int32_t* seq_lens,
+                                       float attn_scale, int32_t window, uint16_t* out, void* workspace,
+                                       size_t workspace_bytes, int32_t max_seq_len_hint, void* stream);
+kvq_status kvq_append_decode_window(const kvq_cache* cache, const void* k_new, const void* v_new,
+                                    int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens,
+                                    float attn_scale, int32_t window, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, int32_t max_seq_len_hint, void* stream);
+kvq_status kvq_attention_chunk_window(const kvq_cache* cache, const uint16_t* q, int32_t n,
+                                      const int32_t* ctx_lens, float attn_scale, int32_t window, uint16_t* out,
+                                      void* workspace, size_t workspace_bytes, int32_t max_ctx_len_hint,
+                                      void* stream);
+size_t kvq_workspace_size_window(const kvq_cache* cache, int32_t max_seq_len, int32_t n_query, int32_t window);
+
+/*
  * Recent-window hybrid cache (abaddon 0.2.0-rc.1 src/kv_cache_quant_cuda.rs,
  * `OptimizedQuantizedKvCache` with `DynamicQuantConfig::unquantized_window`):
  * the last `window` positions of every sequence stay unquantized, as bf16,

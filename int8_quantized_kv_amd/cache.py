@@ -76,23 +76,31 @@ class Int8KVCache:
         else:
             _k.kvq_append(self.desc, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
 
-    def workspace(self, max_seq_len: int, n_query: int = 1) -> torch.Tensor:
+    def workspace(self, max_seq_len: int, n_query: int = 1, window: int = 0) -> torch.Tensor:
         """Zero-filled scratch for the attention calls (the split counters at
         its start must be zero before the first call; calls leave them zero)."""
-        if self.recent is not None and n_query == 1:
+        if window > 0:
+            n = _k.kvq_workspace_size_window(self.desc, max_seq_len, n_query, window)
+        elif self.recent is not None and n_query == 1:
             n = _k.kvq_workspace_size_recent(self.desc, self.recent, max_seq_len)
         else:
             n = _k.kvq_workspace_size(self.desc, max_seq_len, n_query)
         return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.k_codes.device)
 
     def decode(self, q: torch.Tensor, seq_lens: torch.Tensor, attn_scale: float, max_seq_len_hint: int,
-               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
-        """q: bf16 [B, H, D]; returns bf16 [B, H, D]."""
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None,
+               window: int = 0):
+        """q: bf16 [B, H, D]; returns bf16 [B, H, D].  window > 0: sliding window."""
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            workspace = self.workspace(max_seq_len_hint, 1)
-        if self.recent is not None:
+            workspace = self.workspace(max_seq_len_hint, 1, window)
+        if window > 0:
+            if self.recent is not None:
+                raise NotImplementedError("a sliding window over a recent-window cache is not provided")
+            _k.kvq_attention_decode_window(self.desc, q, seq_lens, attn_scale, window, out, workspace,
+                                           workspace.numel(), max_seq_len_hint, stream)
+        elif self.recent is not None:
             _k.kvq_attention_decode_recent(self.desc, self.recent, q, seq_lens, attn_scale, out, workspace,
                                            workspace.numel(), max_seq_len_hint, stream)
         else:
@@ -102,7 +110,7 @@ class Int8KVCache:
 
     def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, seq_lens: torch.Tensor,
                       attn_scale: float, max_seq_len_hint: int, out: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None, stream=None):
+                      workspace: torch.Tensor | None = None, stream=None, window: int = 0):
         """Append one K/V row per sequence at seq_lens - 1 and decode, in one launch."""
         if k_new.dtype not in (torch.float32, torch.bfloat16) or v_new.dtype != k_new.dtype:
             raise TypeError("k_new and v_new must both be float32 or both bfloat16")
@@ -112,8 +120,13 @@ class Int8KVCache:
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            workspace = self.workspace(max_seq_len_hint, 1)
-        if self.recent is not None:
+            workspace = self.workspace(max_seq_len_hint, 1, window)
+        if window > 0:
+            if self.recent is not None:
+                raise NotImplementedError("a sliding window over a recent-window cache is not provided")
+            _k.kvq_append_decode_window(self.desc, k_new, v_new, dt, q, seq_lens, attn_scale, window, out, workspace,
+                                        workspace.numel(), max_seq_len_hint, stream)
+        elif self.recent is not None:
             _k.kvq_append_decode_recent(self.desc, self.recent, k_new, v_new, dt, q, seq_lens, attn_scale, out,
                                         workspace, workspace.numel(), max_seq_len_hint, stream)
         else:
@@ -123,8 +136,9 @@ class Int8KVCache:
 
     def chunk(self, q: torch.Tensor, ctx_lens: torch.Tensor, causal: bool, attn_scale: float,
               max_ctx_len_hint: int, out: torch.Tensor | None = None,
-              workspace: torch.Tensor | None = None, stream=None):
-        """q: bf16 [B, H, n, D]; returns bf16 [B, H, n, D]."""
+              workspace: torch.Tensor | None = None, stream=None, window: int = 0):
+        """q: bf16 [B, H, n, D]; returns bf16 [B, H, n, D].  window > 0:
+        sliding window (implies causal)."""
         if self.recent is not None:
             raise NotImplementedError("chunked attention over a recent-window cache is not provided")
         n = q.shape[2]
@@ -132,8 +146,12 @@ class Int8KVCache:
             out = torch.empty_like(q)
         if workspace is None:
             workspace = self.workspace(max_ctx_len_hint + n, n)
-        _k.kvq_attention_chunk(self.desc, q, n, ctx_lens, causal, attn_scale, out, workspace,
-                               workspace.numel(), max_ctx_len_hint, stream)
+        if window > 0:
+            _k.kvq_attention_chunk_window(self.desc, q, n, ctx_lens, attn_scale, window, out, workspace,
+                                          workspace.numel(), max_ctx_len_hint, stream)
+        else:
+            _k.kvq_attention_chunk(self.desc, q, n, ctx_lens, causal, attn_scale, out, workspace,
+                                   workspace.numel(), max_ctx_len_hint, stream)
         return out
 
     def dequant(self, which: int, seq_lens: torch.Tensor, out_len: int, bf16: bool = False, stream=None):

@@ -102,7 +102,7 @@ kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who
 bool finite(float x) { return x == x && x != INFINITY && x != -INFINITY; }
 
 size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_len, int32_t n_query,
-                      const char* who) {
+                      const char* who, int32_t window = 0) {
   g_err[0] = '\0';
   if (check_cache(c, who) != KVQ_OK) return 0;
   if (r && check_recent(r, *c, who) != KVQ_OK) return 0;
@@ -110,7 +110,7 @@ size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_l
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
   }
-  if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r)).workspace;
+  if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r), window).workspace;
   return chunk_workspace(*c, max_seq_len, n_query);
 }
 
@@ -134,10 +134,11 @@ kvq_status append_impl(const kvq_cache* c, const kvq_recent* r, const void* k_ne
 kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, const void* k_new, const void* v_new,
                        int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens, float attn_scale,
                        uint16_t* out, void* workspace, size_t workspace_bytes, int32_t max_seq_len_hint,
-                       void* stream, const char* who) {
+                       void* stream, const char* who, int32_t window = 0) {
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
   if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
   if (fused) {
     if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
     if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
@@ -153,12 +154,12 @@ kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, cons
   if (r && c->head_dim > 128)
     return fail(KVQ_ERR_UNSUPPORTED, "%s: a recent window needs head_dim <= 128 (got %d)", who, c->head_dim);
   const RecentGeom rc = recent_of(r);
-  const DecodePlan plan = plan_decode(*c, max_seq_len_hint, rc);
+  const DecodePlan plan = plan_decode(*c, max_seq_len_hint, rc, window);
   st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
   if (st != KVQ_OK) return st;
   return launch_decode(*c, plan, q, seq_lens, attn_scale, out, workspace, max_seq_len_hint,
                        static_cast<hipStream_t>(stream), fused ? k_new : nullptr, fused ? v_new : nullptr,
-                       in_dtype, rc);
+                       in_dtype, rc, window);
 }
 
 kvq_status dequant_impl(const kvq_cache* c, const kvq_recent* r, int32_t which, const int32_t* seq_lens,
@@ -239,16 +240,18 @@ KVQ_API kvq_status kvq_append_decode_recent(const kvq_cache* c, const kvq_recent
                      workspace_bytes, max_seq_len_hint, stream, who);
 }
 
-KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens,
-                                       int32_t causal, float attn_scale, uint16_t* out, void* workspace,
-                                       size_t workspace_bytes, int32_t max_ctx_len_hint, void* stream) {
-  const char* who = "kvq_attention_chunk";
+namespace kvq {
+namespace {
+
+kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens, int32_t causal,
+                      float attn_scale, int32_t window, uint16_t* out, void* workspace, size_t workspace_bytes,
+                      int32_t max_ctx_len_hint, void* stream, const char* who) {
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
   if (!q || !ctx_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, ctx_lens and out must be non-NULL", who);
   if (n <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: n must be positive (got %d)", who, n);
-  if (!(attn_scale == attn_scale) || attn_scale == INFINITY || attn_scale == -INFINITY)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
+  if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
+  if (!finite(attn_scale)) return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
   if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
@@ -257,7 +260,54 @@ KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, in
   st = check_split_workspace(chunk_workspace(*c, max_ctx_len_hint + n, n), workspace, workspace_bytes, who);
   if (st != KVQ_OK) return st;
   return launch_chunk(*c, q, n, ctx_lens, causal, attn_scale, out, workspace, max_ctx_len_hint,
-                      static_cast<hipStream_t>(stream));
+                      static_cast<hipStream_t>(stream), window);
+}
+
+}  // namespace
+}  // namespace kvq
+
+KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens,
+                                       int32_t causal, float attn_scale, uint16_t* out, void* workspace,
+                                       size_t workspace_bytes, int32_t max_ctx_len_hint, void* stream) {
+  return chunk_impl(c, q, n, ctx_lens, causal, attn_scale, 0, out, workspace, workspace_bytes, max_ctx_len_hint,
+                    stream, "kvq_attention_chunk");
+}
+
+KVQ_API kvq_status kvq_attention_chunk_window(const kvq_cache* c, const uint16_t* q, int32_t n,
+                                              const int32_t* ctx_lens, float attn_scale, int32_t window,
+                                              uint16_t* out, void* workspace, size_t workspace_bytes,
+                                              int32_t max_ctx_len_hint, void* stream) {
+  const char* who = "kvq_attention_chunk_window";
+  if (window < 1) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
+  return chunk_impl(c, q, n, ctx_lens, 1, attn_scale, window, out, workspace, workspace_bytes, max_ctx_len_hint,
+                    stream, who);
+}
+
+KVQ_API kvq_status kvq_attention_decode_window(const kvq_cache* c, const uint16_t* q, const int32_t* seq_lens,
+                                               float attn_scale, int32_t window, uint16_t* out, void* workspace,
+                                               size_t workspace_bytes, int32_t max_seq_len_hint, void* stream) {
+  const char* who = "kvq_attention_decode_window";
+  if (window < 1) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
+  return decode_impl(c, nullptr, false, nullptr, nullptr, KVQ_DT_BF16, q, seq_lens, attn_scale, out, workspace,
+                     workspace_bytes, max_seq_len_hint, stream, who, window);
+}
+
+KVQ_API kvq_status kvq_append_decode_window(const kvq_cache* c, const void* k_new, const void* v_new,
+                                            int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens,
+                                            float attn_scale, int32_t window, uint16_t* out, void* workspace,
+                                            size_t workspace_bytes, int32_t max_seq_len_hint, void* stream) {
+  const char* who = "kvq_append_decode_window";
+  if (window < 1) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
+  return decode_impl(c, nullptr, true, k_new, v_new, in_dtype, q, seq_lens, attn_scale, out, workspace,
+                     workspace_bytes, max_seq_len_hint, stream, who, window);
+}
+
+KVQ_API size_t kvq_workspace_size_window(const kvq_cache* c, int32_t max_seq_len, int32_t n_query, int32_t window) {
+  if (window < 1) {
+    fail(KVQ_ERR_INVALID_ARG, "kvq_workspace_size_window: window must be at least 1 (got %d)", window);
+    return 0;
+  }
+  return workspace_impl(c, nullptr, max_seq_len, n_query, "kvq_workspace_size_window", window);
 }
 
 KVQ_API kvq_status kvq_dequant(const kvq_cache* c, int32_t which, const int32_t* seq_lens, int32_t out_dtype,

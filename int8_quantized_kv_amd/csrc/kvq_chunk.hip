@@ -76,6 +76,7 @@ struct ChunkParams {
   int32_t wgs_per_bg;   // workgroups per (sequence, KV head)
   int32_t total_wgs;
   int32_t causal;
+  int32_t window;       // sliding window (0: none): query p sees keys in (p - window, p]
   float scale_log2;     // attn_scale * log2(e)
 };
 
@@ -205,7 +206,21 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       wg_end = max(wg_end, p.causal ? min(L0 + pb + kQBlock, Ltot) : Ltot);
     }
   }
-  const int ntiles = (wg_end + kCkTile - 1) / kCkTile;
+  // With a sliding window the tiles start at the lowest key any of the
+  // workgroup's queries sees (combs-models kv.rs `attend`: keys at or below
+  // p - window are masked), rounded down to a tile.
+  int wg_lo = 0;
+  if (p.window > 0) {
+    wg_lo = wg_end;
+#pragma unroll
+    for (int w = 0; w < kCkWaves; ++w) {
+      const int it = wg * kCkWaves + w;
+      if (it < items) wg_lo = min(wg_lo, L0 + (it / p.hpg) * kQBlock - p.window + 1);
+    }
+    wg_lo = max(wg_lo, 0);
+  }
+  const int tbase = (wg_lo / kCkTile) * kCkTile;  // token offset of tile 0
+  const int ntiles = (wg_end - tbase + kCkTile - 1) / kCkTile;
 
   const int item = wg * kCkWaves + wave;
   const bool active = item < items;
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     }
   };
 
-  load_tile(0);
+  load_tile(tbase);
   __syncthreads();  // sm_qmax
 
   int kq = 0;
@@ -321,12 +336,12 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   }
 
   // Prologue: tiles 0 and 1 in LDS, tile 2 in flight.
-  store_tile(smem, 0, kfac);
+  store_tile(smem, tbase, kfac);
   if (ntiles > 1) {
-    load_tile(kCkTile);
-    store_tile(smem + TL::kBytes, kCkTile, kfac);
+    load_tile(tbase + kCkTile);
+    store_tile(smem + TL::kBytes, tbase + kCkTile, kfac);
   }
-  if (ntiles > 2) load_tile(2 * kCkTile);
+  if (ntiles > 2) load_tile(tbase + 2 * kCkTile);
   __syncthreads();
 
   // V transpose read: lane 16*r4 + r names token 16ks + pi(r4/2, r/2) and
@@ -406,7 +421,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     __builtin_amdgcn_s_setprio(0);
   };
   auto softmax_step = [&](int t) {
-    const int t0 = t * kCkTile;
+    const int t0 = tbase + t * kCkTile;
     const uint8_t* bc = smem + (t % kCkBufs) * TL::kBytes;
     const float* kc = reinterpret_cast<const float*>(bc + TL::kKc);
     const float* lsv = reinterpret_cast<const float*>(bc + TL::kLsv);
@@ -432,6 +447,14 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (32 * tt + 8 * (r >> 2) + 4 * half + (r & 3) > limit) z[tt][r] = -INFINITY;
+    }
+    if (p.window > 0 && t0 < L0 + pos0 + kQBlock - p.window) {  // tile reaches below a window
+      const int lower = L0 + qi - p.window + 1 - t0;               // first visible key of the tile
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * tt + 8 * (r >> 2) + 4 * half + (r & 3) < lower) z[tt][r] = -INFINITY;
     }
     float zmax = -INFINITY;
 #pragma unroll
@@ -473,8 +496,8 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     }
   };
   auto loader_step = [&](int t) {
-    if (t + 2 < ntiles) store_tile(smem + ((t + 2) % kCkBufs) * TL::kBytes, (t + 2) * kCkTile, kfac);
-    if (t + 3 < ntiles) load_tile((t + 3) * kCkTile);
+    if (t + 2 < ntiles) store_tile(smem + ((t + 2) % kCkBufs) * TL::kBytes, tbase + (t + 2) * kCkTile, kfac);
+    if (t + 3 < ntiles) load_tile(tbase + (t + 3) * kCkTile);
   };
 
   if (grp == 1) __syncthreads();
@@ -519,7 +542,7 @@ bool chunk_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
 size_t chunk_workspace(const kvq_cache&, int, int) { return 0; }
 
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens, int causal,
-                        float attn_scale, uint16_t* out, void*, int, hipStream_t stream) {
+                        float attn_scale, uint16_t* out, void*, int, hipStream_t stream, int window) {
   if (c.scale_mode != KVQ_SCALE_PER_TOKEN)
     return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: group-32 scales are not supported");
   ChunkParams p;
@@ -535,7 +558,8 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.hpg = c.num_heads / c.num_kv_heads;
   p.n = n;
   p.nblk = (n + kQBlock - 1) / kQBlock;
-  p.causal = causal ? 1 : 0;
+  p.causal = causal || window > 0 ? 1 : 0;
+  p.window = window > 0 ? window : 0;
   p.scale_log2 = attn_scale * kCkLog2e;
   const int64_t items = static_cast<int64_t>(p.hpg) * p.nblk;
   const int64_t per_bg = (items + kCkWaves - 1) / kCkWaves;

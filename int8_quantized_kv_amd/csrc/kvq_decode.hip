@@ -81,6 +81,9 @@ struct DecodeParams {
   uint16_t* rk;              // [B, KVH, rcap, D] bf16
   uint16_t* rv;
   int32_t rwin, rcap;        // rwin 0: no recent window
+  // sliding window (0: none): the query at position L - 1 sees keys in
+  // (L - 1 - window, L - 1]
+  int32_t window;
 };
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* x) {
@@ -584,7 +587,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
   const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
 
-  const int t_begin = split * p.split_len;
+  // With a sliding window the token range starts at the window's first key,
+  // rounded down to a block (blocks stay page-aligned; keys below the window
+  // are masked), so it is known only with the length.
+  int t_begin = split * p.split_len;
+  int t_min = 0;  // first visible key
   // Until seq_lens[b] arrives, t_end is only bounded by the launch: the first
   // block's loads go out against that bound (rows past the real end are valid
   // memory and are masked later), overlapping the length and query loads.
@@ -806,7 +813,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 
     // softmax: this lane owns token `lane` of the block
     const int t = t_begin + blk * kBlock + lane;
-    const bool valid = t < t_end;
+    const bool valid = t < t_end && t >= t_min;
     float4 acc4 = sm_part[wave][lane ^ 0];
     if constexpr (G32) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
 #pragma unroll
@@ -933,16 +940,19 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     qraw[j][0] = qptr[0];
     qraw[j][1] = qptr[1];
   }
-  if constexpr (PAGED) {
+  auto first_loads = [&]() {
+    if constexpr (PAGED) {
 #pragma unroll
-    for (int k = 0; k < kPidAhead; ++k)
-      if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
-  }
-  if (t_begin + blk * kBlock < t_end) {  // speculative first block
-    load_k(blk, pq[0]);
-    load_v(blk, pq[0]);
-    load_block_scales(blk, pq[0]);
-  }
+      for (int k = 0; k < kPidAhead; ++k)
+        if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
+    }
+    if (t_begin + blk * kBlock < t_end) {
+      load_k(blk, pq[0]);
+      load_v(blk, pq[0]);
+      load_block_scales(blk, pq[0]);
+    }
+  };
+  if (p.window == 0) first_loads();  // speculative first block
   // fused append: waves 0 and 1 fetch the new K and V rows of this KV head
   // (with a recent window the row to quantize is the one leaving the ring,
   // fetched once the length is known)
@@ -960,7 +970,13 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
   }
   const int L8 = L > p.rwin ? L - p.rwin : 0;  // INT8 tokens (all of them without a recent window)
-  const int ns8 = (L8 + p.split_len - 1) / p.split_len;
+  int t_base = 0;  // first token of split 0
+  if (p.window > 0) {
+    t_min = max(L - p.window, 0);
+    t_base = t_min & ~(kBlock - 1);
+    t_begin = t_base + split * p.split_len;
+  }
+  const int ns8 = (L8 - t_base + p.split_len - 1) / p.split_len;
   // recent window: the workgroup of the last INT8 split (split 0 if there is
   // none) also attends to the ring
   const bool ring_here = p.rwin > 0 && L > 0 && split == (ns8 > 0 ? ns8 - 1 : 0);
@@ -968,6 +984,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   t_end = min(L8, t_begin + p.split_len);
   const int nblk = t_end > t_begin ? (t_end - t_begin + kBlock - 1) / kBlock : 0;
   const int ns = ns8 > 0 ? ns8 : 1;
+  if (p.window > 0) first_loads();
   // fused append: the workgroup whose split holds position L8 - 1 quantizes
   // the row that enters the INT8 part (abaddon kv_cache_quant_cuda.rs
   // `quantize_tensor` steps), stores it in the cache, and keeps a copy in LDS
@@ -1105,7 +1122,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const int slot = lane / LPT;
 
   const int L = clamp_len(p, b);
-  const int t_begin = split * p.split_len;
+  const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // first visible key
+  const int t_begin = t_lo + split * p.split_len;
   if (t_begin >= L) return;
   const int t_end = min(L, t_begin + p.split_len);
   const int npass = (t_end - t_begin + TPP - 1) / TPP;
@@ -1258,7 +1276,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
   const int b = blockIdx.y;
   const int H = p.num_heads;
   const int L = clamp_len(p, b);
-  const int ns = (L + p.split_len - 1) / p.split_len;
+  const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // the splits start at the window
+  const int ns = (L - t_lo + p.split_len - 1) / p.split_len;
   const int64_t base = (static_cast<int64_t>(b) * H + h) * p.num_splits;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[(base + s) * 2]);
@@ -1340,8 +1359,11 @@ bool decode_supported(int head_dim) {
   return head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
 }
 
-DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc) {
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc, int window) {
   DecodePlan pl;
+  // a sliding window bounds each sequence's range: the window rounded out to
+  // whole blocks
+  if (window > 0 && max_seq_len > window + kBlock - 1) max_seq_len = window + kBlock - 1;
   // with a recent window the INT8 splits cover at most max_seq_len - W tokens
   const int ring = rc.window > 0 ? 1 : 0;
   if (ring) max_seq_len = max_seq_len > rc.window ? max_seq_len - rc.window : 1;
@@ -1388,7 +1410,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
                          const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
                          int max_seq_len, hipStream_t stream, const void* new_k, const void* new_v,
-                         int new_dtype, const RecentGeom& rc) {
+                         int new_dtype, const RecentGeom& rc, int window) {
   const bool append = new_k != nullptr;
   const bool stream_kernel = use_stream(c.head_dim);
   if (append && !stream_kernel) {
@@ -1426,6 +1448,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   p.rv = rc.v;
   p.rwin = rc.window;
   p.rcap = rc.cap;
+  p.window = window;
   p.scale_log2 = attn_scale * kLog2e;
   dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, c.batch);
   if (grid.y > 65535 || grid.z > 65535)

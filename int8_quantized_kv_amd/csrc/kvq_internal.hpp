@@ -74,20 +74,22 @@ struct DecodePlan {
 bool decode_supported(int head_dim);
 // With a recent window the INT8 splits cover at most max_seq_len - window
 // tokens; the last one's workgroup also attends to the ring.
-DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc = RecentGeom());
+// A sliding window (> 0) bounds each sequence's range to about the window.
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc = RecentGeom(), int window = 0);
 // new_k / new_v non-null: fused append of one row per sequence at position
 // seq_lens[b] - 1 before the attention.
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
                          const int32_t* seq_lens, float attn_scale, uint16_t* out, void* ws,
                          int max_seq_len, hipStream_t stream, const void* new_k = nullptr,
                          const void* new_v = nullptr, int new_dtype = KVQ_DT_BF16,
-                         const RecentGeom& rc = RecentGeom());
+                         const RecentGeom& rc = RecentGeom(), int window = 0);
 
 // ---- chunked prefill --------------------------------------------------------
 bool chunk_supported(int head_dim);
 size_t chunk_workspace(const kvq_cache& c, int max_total_len, int n);
+// window > 0: sliding window (implies causal).
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens,
                         int causal, float attn_scale, uint16_t* out, void* ws, int max_ctx_len,
-                        hipStream_t stream);
+                        hipStream_t stream, int window = 0);
 
 }  // namespace kvq

@@ -33,7 +33,8 @@ STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "OUT_OF_RANGE", 3: "UNSUPPORTED", 
 EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_append_decode", "kvq_attention_chunk", "kvq_dequant",
             "kvq_workspace_size", "kvq_cache_bytes", "kvq_last_error", "kvq_version",
             "kvq_append_recent", "kvq_attention_decode_recent", "kvq_append_decode_recent", "kvq_dequant_recent",
-            "kvq_workspace_size_recent")
+            "kvq_workspace_size_recent", "kvq_attention_decode_window", "kvq_append_decode_window",
+            "kvq_attention_chunk_window", "kvq_workspace_size_window")
 
 
 class KvqError(RuntimeError):
@@ -132,6 +133,15 @@ def _load():
     lib.kvq_dequant_recent.restype = I
     lib.kvq_workspace_size_recent.argtypes = [CP, RP, I]
     lib.kvq_workspace_size_recent.restype = ctypes.c_size_t
+    F = ctypes.c_float
+    lib.kvq_attention_decode_window.argtypes = [CP, P, P, F, I, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_attention_decode_window.restype = I
+    lib.kvq_append_decode_window.argtypes = [CP, P, P, I, P, P, F, I, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_append_decode_window.restype = I
+    lib.kvq_attention_chunk_window.argtypes = [CP, P, I, P, F, I, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_attention_chunk_window.restype = I
+    lib.kvq_workspace_size_window.argtypes = [CP, I, I, I]
+    lib.kvq_workspace_size_window.restype = ctypes.c_size_t
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
@@ -273,6 +283,34 @@ def kvq_dequant_recent(cache: kvq_cache, recent, which: int, seq_lens, out_dtype
 
 def kvq_workspace_size_recent(cache: kvq_cache, recent, max_seq_len: int) -> int:
     n = _lib.kvq_workspace_size_recent(ctypes.byref(cache), _rp(recent), max_seq_len)
+    if n == 0 and kvq_last_error():
+        raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
+    return n
+
+
+def kvq_attention_decode_window(cache: kvq_cache, q, seq_lens, attn_scale: float, window: int, out, workspace,
+                                workspace_bytes: int, max_seq_len_hint: int, stream=None):
+    _check(_lib.kvq_attention_decode_window(ctypes.byref(cache), _ptr(q), _ptr(seq_lens), attn_scale, window,
+                                            _ptr(out), _ptr(workspace), workspace_bytes, max_seq_len_hint,
+                                            _stream(stream)))
+
+
+def kvq_append_decode_window(cache: kvq_cache, k_new, v_new, in_dtype: int, q, seq_lens, attn_scale: float,
+                             window: int, out, workspace, workspace_bytes: int, max_seq_len_hint: int, stream=None):
+    _check(_lib.kvq_append_decode_window(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), in_dtype, _ptr(q),
+                                         _ptr(seq_lens), attn_scale, window, _ptr(out), _ptr(workspace),
+                                         workspace_bytes, max_seq_len_hint, _stream(stream)))
+
+
+def kvq_attention_chunk_window(cache: kvq_cache, q, n: int, ctx_lens, attn_scale: float, window: int, out,
+                               workspace, workspace_bytes: int, max_ctx_len_hint: int, stream=None):
+    _check(_lib.kvq_attention_chunk_window(ctypes.byref(cache), _ptr(q), n, _ptr(ctx_lens), attn_scale, window,
+                                           _ptr(out), _ptr(workspace), workspace_bytes, max_ctx_len_hint,
+                                           _stream(stream)))
+
+
+def kvq_workspace_size_window(cache: kvq_cache, max_seq_len: int, n_query: int, window: int) -> int:
+    n = _lib.kvq_workspace_size_window(ctypes.byref(cache), max_seq_len, n_query, window)
     if n == 0 and kvq_last_error():
         raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
     return n

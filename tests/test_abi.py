@@ -226,3 +226,19 @@ def test_recent_workspace_is_the_int8_parts():
     attends to it): the workspace is that of the INT8 part, hint - W."""
     with_ring = kvq.kvq_workspace_size_recent(_desc(max_len=4096), _recent(window=128, capacity=129), 4096)
     assert with_ring > 0 and with_ring == kvq.kvq_workspace_size(_desc(max_len=4096), 4096 - 128, 1)
+
+
+def test_window_argument_errors():
+    """window < 1 is rejected by every sliding-window entry point."""
+    d = ctypes.byref(_desc())
+    for w in (0, -4):
+        assert _status("kvq_attention_decode_window", d, FAKE, FAKE, 0.1, w, FAKE, FAKE, 1 << 30, 64, None)[0] == \
+            kvq.KVQ_ERR_INVALID_ARG
+        assert _status("kvq_append_decode_window", d, FAKE, FAKE, 0, FAKE, FAKE, 0.1, w, FAKE, FAKE, 1 << 30, 64,
+                       None)[0] == kvq.KVQ_ERR_INVALID_ARG
+        assert _status("kvq_attention_chunk_window", d, FAKE, 8, FAKE, 0.1, w, FAKE, FAKE, 1 << 30, 8, None)[0] == \
+            kvq.KVQ_ERR_INVALID_ARG
+        assert kvq.library().kvq_workspace_size_window(d, 64, 1, w) == 0
+    # a window shorter than the hint plans fewer splits
+    big = _desc(max_len=32768)
+    assert 0 < kvq.kvq_workspace_size_window(big, 32768, 1, 256) < kvq.kvq_workspace_size(big, 32768, 1)
