@@ -95,7 +95,11 @@ def chunk_counts(w: wl.Workload) -> dict:
     """Chunked-prefill step: MFMA flops over visible keys (QK and PV, 2 flops
     per multiply-add each) and algorithmic bytes."""
     B, H, KVH, D, n, L0 = w.batch, w.num_heads, w.num_kv_heads, w.head_dim, w.n_new, w.ctx
-    visible = n * (L0 + 1) + n * (n - 1) // 2          # sum over i < n of L0 + i + 1
+    win = w.extra.get("sliding", 0)
+    if win:   # query i sees min(window, L0 + i + 1) keys
+        visible = sum(min(win, L0 + i + 1) for i in range(n))
+    else:
+        visible = n * (L0 + 1) + n * (n - 1) // 2      # sum over i < n of L0 + i + 1
     flops = 4 * B * H * D * visible
     L = L0 + n
     codes = 2 * B * KVH * L * D
@@ -274,8 +278,10 @@ def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
             h = g * hpg + int(rng.integers(hpg))
             i = int(rng.integers(w.n_new))
             total = w.ctx + i + 1
-            orc.softmax_attend(x["q"][b, h, i].astype(np.float64), kh[:total], vh[:total], w.attn_scale, None)
-            flops += 4 * w.head_dim * total
+            first = max(0, total - w.extra.get("sliding", 0)) if w.extra.get("sliding") else 0
+            orc.softmax_attend(x["q"][b, h, i].astype(np.float64), kh[first:total], vh[first:total],
+                               w.attn_scale, None)
+            flops += 4 * w.head_dim * (total - first)
             rows += 1
     el = time.perf_counter() - t0
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
@@ -298,6 +304,7 @@ def time_calls(fn, reps: int, stream, torch) -> float:
 
 
 def run_chunk(args, w: wl.Workload, kvq, torch, stream):
+    win = w.extra.get("sliding", 0)
     x = wl.layer_inputs(w, 0)
     B, KVH, T, D = x["k"].shape
     dev = torch.device("cuda")
@@ -323,10 +330,10 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
 
     def step():  # quantize-append the chunk's rows, then attention for its queries
         cache.append(k_new, v_new, ctx, stream=stream)
-        cache.chunk(q, ctx, True, w.attn_scale, w.ctx, out=out, workspace=ws, stream=stream)
+        cache.chunk(q, ctx, True, w.attn_scale, w.ctx, out=out, workspace=ws, stream=stream, window=win)
 
     def kernel_pass():
-        cache.chunk(q, ctx, True, w.attn_scale, w.ctx, out=out, workspace=ws, stream=stream)
+        cache.chunk(q, ctx, True, w.attn_scale, w.ctx, out=out, workspace=ws, stream=stream, window=win)
 
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -350,7 +357,8 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_chunk(w, x)
     result = {
-        "metric": "INT8-KV chunked-prefill attention: MFMA TFLOP/s over visible keys",
+        "metric": "INT8-KV chunked-prefill attention: MFMA TFLOP/s over visible keys"
+                  + (" (sliding window)" if win else ""),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -363,7 +371,8 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
         "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {B}, {w.num_heads} q / {KVH} kv heads, head_dim {D}, "
-                               f"{w.ctx} cached + {w.n_new} new tokens, causal, per-token fp32 scales; "
+                               f"{w.ctx} cached + {w.n_new} new tokens, causal"
+                               + (f", sliding window {win}" if win else "") + ", per-token fp32 scales; "
                                f"append the {w.n_new} rows + chunk attention",
                    "batch": B, "seq_len": T, "flops_per_step": cnt["flops"], "bytes_per_step": cnt["step_bytes"]},
         "roofline": {"bound": "mfma", "kernel": "kvq_attention_chunk",
@@ -479,6 +488,126 @@ def run_paged(args, w: wl.Workload, kvq, torch, stream):
     print(json.dumps(result), flush=True)
 
 
+def sliding_bytes(w: wl.Workload) -> dict:
+    """Algorithmic bytes of one sliding-window layer-step: codes and scales of
+    the min(L, window) visible rows, queries, outputs, the appended row."""
+    B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    vis = min(w.ctx + w.n_new, w.extra["sliding"])
+    decode = 2 * B * KVH * vis * (D + 4) + 2 * B * H * D * 2
+    append = 2 * B * KVH * (D * 2 + D + 4)
+    return {"decode": decode, "step": decode + append}
+
+
+def run_sliding(args, w: wl.Workload, kvq, torch, stream):
+    """Sliding-window decode: every layer's cache holds 8192 tokens (drawn on
+    the device from a seeded generator); one step appends one token per
+    sequence and attends over the last `window` tokens (one fused launch per
+    layer)."""
+    B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
+    T = w.ctx + w.n_new
+    win = w.extra["sliding"]
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    t0 = time.time()
+    layers = []
+    with torch.cuda.stream(stream):
+        zero = torch.zeros(B, dtype=torch.int32, device=dev)
+        for _ in range(w.layers):
+            cache = kvq.Int8KVCache(B, H, KVH, D, max_len=T)
+            for p0 in range(0, w.ctx, 2048):
+                n = min(2048, w.ctx - p0)
+                k = torch.randn((B, KVH, n, D), generator=gen, device=dev).to(torch.bfloat16)
+                v = torch.randn((B, KVH, n, D), generator=gen, device=dev).to(torch.bfloat16)
+                cache.append(k, v, zero + p0, stream=stream)
+            layers.append({"cache": cache,
+                           "k_new": torch.randn((B, KVH, 1, D), generator=gen, device=dev).to(torch.bfloat16),
+                           "v_new": torch.randn((B, KVH, 1, D), generator=gen, device=dev).to(torch.bfloat16),
+                           "q": torch.randn((B, H, D), generator=gen, device=dev).to(torch.bfloat16)})
+            layers[-1]["out"] = torch.empty_like(layers[-1]["q"])
+        seq_lens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        ws = layers[0]["cache"].workspace(T, 1, win)
+    stream.synchronize()
+    log(f"prefilled {w.layers} layers of {T} tokens in {time.time() - t0:.1f}s")
+
+    def step():
+        for ly in layers:
+            ly["cache"].append_decode(ly["k_new"], ly["v_new"], ly["q"], seq_lens, w.attn_scale, T, out=ly["out"],
+                                      workspace=ws, stream=stream, window=win)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+        stream.synchronize()
+        step_ms = time_calls(step, args.steps, stream, torch)
+        k_ms = time_calls(step, args.kernel_reps, stream, torch)
+    nb = sliding_bytes(w)
+    tbps = nb["step"] * w.layers / (step_ms * 1e-3) / 1e12
+    us_launch = k_ms * 1e3 / w.layers
+    k_gbs = nb["step"] / (us_launch * 1e-6) / 1e9
+    log(f"{step_ms * 1e3 / w.layers:.2f} us/layer-step, {tbps:.3f} TB/s; kvq_append_decode_window "
+        f"{us_launch:.2f} us/launch = {k_gbs:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline_sliding(w)
+    result = {
+        "metric": "INT8-KV sliding-window decode attention: us/layer-step and achieved HBM TB/s (% of peak)",
+        "value": round(tbps, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "us_per_layer_step": round(step_ms * 1e3 / w.layers, 3),
+        "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {B}, {H} q / {KVH} kv heads, head_dim {D}, context {T}, "
+                               f"sliding window {win}, per-token fp32 scales, {w.layers} layers, append 1 token "
+                               f"+ decode per layer (one fused launch)",
+                   "batch": B, "seq_len": T, "layers": w.layers, "bytes_per_step": nb["step"] * w.layers},
+        "roofline": {"bound": "hbm", "kernel": "kvq_append_decode_window",
+                     "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("kvq_append_decode_window", w.name),
+                     "bytes_per_launch": nb["step"], "us_per_launch": round(us_launch, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_sliding(w: wl.Workload, target_s: float = 12.0):
+    """The oracle on whole sequences of the same shapes (drawn on the host):
+    quantize the sequence's K/V, fp64 attention of its heads with the window
+    mask applied to all of its keys."""
+    import oracle as orc
+    blas_threads = blas_thread_count()
+    T = w.ctx + w.n_new
+    win = w.extra["sliding"]
+    per_seq = sliding_bytes(w)["step"] / w.batch
+    rng = np.random.default_rng([w.seed, 7])
+    q = wl.bits_to_f32(wl.bf16_bits(wl.normal(rng, (1, w.num_heads, w.head_dim))))
+    seqs = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        x = wl.sequence_kv(w, seqs % w.batch, T)
+        kc, ks = orc.quantize(x["k"], 0)
+        vc, vs = orc.quantize(x["v"], 0)
+        orc.attention_decode(q, orc.dequantize_exact(kc, ks)[None], orc.dequantize_exact(vc, vs)[None], [T],
+                             w.attn_scale, window=win)
+        seqs += 1
+    el = time.perf_counter() - t0
+    return {"value": per_seq * seqs / el / 1e12, "unit": "TB/s", "cores": blas_threads, "kind": "oracle",
+            "sample": f"{seqs} sequences of {T} tokens drawn on the host with the workload's shapes (quantize the "
+                      f"sequence's K/V, fp64 attention of 32 heads under a {win}-token window), {el:.1f}s wall; "
+                      f"bytes counted as the step's per-sequence algorithmic bytes; BLAS threads {blas_threads}; "
+                      f"host {platform.processor() or 'x86_64'} nproc {os.cpu_count()}"}
+
+
 def cpu_baseline_paged(w: wl.Workload, lens, target_s: float = 12.0):
     """The oracle on whole sequences of the paged step (quantize the sequence's
     K/V, fp64 attention for its heads), on a bounded sample of sequences."""
@@ -517,7 +646,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
-                                                            "recent_window"])
+                                                            "recent_window", "sliding_decode", "sliding_chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -554,7 +683,10 @@ def main():
         return
 
     w = wl.ALL[args.workload]
-    if w.name == "chunked_prefill":
+    if w.name == "sliding_decode":
+        run_sliding(args, w, kvq, torch, stream)
+        return
+    if w.name in ("chunked_prefill", "sliding_chunk"):
         run_chunk(args, w, kvq, torch, stream)
         return
     if w.name == "paged_decode":

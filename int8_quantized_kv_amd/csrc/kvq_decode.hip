@@ -205,6 +205,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Splits of a token range of `len` tokens: whole splits of split_len, and a
+// remainder of at most one block joins the last one (a split of a few tokens
+// would cost a workgroup and a merge input for almost no work).
+__host__ __device__ inline int split_count(int len, int split_len) {
+  if (len <= 0) return 0;
+  const int full = len / split_len;
+  if (full == 0) return 1;
+  return full + (len - full * split_len > kBlock ? 1 : 0);
+}
+
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   int L = p.seq_lens[b];
   return L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
@@ -976,15 +986,26 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     t_base = t_min & ~(kBlock - 1);
     t_begin = t_base + split * p.split_len;
   }
-  const int ns8 = (L8 - t_base + p.split_len - 1) / p.split_len;
+  const int ns8 = split_count(L8 - t_base, p.split_len);
   // recent window: the workgroup of the last INT8 split (split 0 if there is
   // none) also attends to the ring
   const bool ring_here = p.rwin > 0 && L > 0 && split == (ns8 > 0 ? ns8 - 1 : 0);
-  if (t_begin >= L8 && !ring_here) return;  // this split has no tokens (and is not counted)
-  t_end = min(L8, t_begin + p.split_len);
+  if ((split >= ns8 || t_begin >= L8) && !ring_here) return;  // no tokens here (and not counted)
+  const int t_end_spec = t_end;
+  t_end = split == ns8 - 1 ? L8 : min(L8, t_begin + p.split_len);  // the last split takes the remainder
   const int nblk = t_end > t_begin ? (t_end - t_begin + kBlock - 1) / kBlock : 0;
   const int ns = ns8 > 0 ? ns8 : 1;
-  if (p.window > 0) first_loads();
+  if (p.window > 0) {
+    first_loads();
+  } else if constexpr (PAGED) {
+    // a remainder joined to the last split lies past the speculative bound:
+    // fetch the page ids the queue skipped
+    if (t_end > t_end_spec) {
+#pragma unroll
+      for (int k = 0; k < kPidAhead; ++k)
+        if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
+    }
+  }
   // fused append: the workgroup whose split holds position L8 - 1 quantizes
   // the row that enters the INT8 part (abaddon kv_cache_quant_cuda.rs
   // `quantize_tensor` steps), stores it in the cache, and keeps a copy in LDS
@@ -1124,8 +1145,9 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const int L = clamp_len(p, b);
   const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // first visible key
   const int t_begin = t_lo + split * p.split_len;
-  if (t_begin >= L) return;
-  const int t_end = min(L, t_begin + p.split_len);
+  const int nsg = split_count(L - t_lo, p.split_len);
+  if (split >= nsg) return;
+  const int t_end = split == nsg - 1 ? L : t_begin + p.split_len;  // the last split takes the remainder
   const int npass = (t_end - t_begin + TPP - 1) / TPP;
 
   float q[HPW][16];
@@ -1277,7 +1299,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
   const int H = p.num_heads;
   const int L = clamp_len(p, b);
   const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // the splits start at the window
-  const int ns = (L - t_lo + p.split_len - 1) / p.split_len;
+  const int ns = split_count(L - t_lo, p.split_len);
   const int64_t base = (static_cast<int64_t>(b) * H + h) * p.num_splits;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[(base + s) * 2]);
@@ -1391,7 +1413,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   split = ((split + step - 1) / step) * step;
   if (split < step) split = step;
   pl.split_len = split;
-  pl.num_splits = (max_seq_len + split - 1) / split;
+  pl.num_splits = split_count(max_seq_len, split);
   if (pl.num_splits < 1) pl.num_splits = 1;
 
   // Longest sequence first pays when workgroups are long (several rounds of

@@ -87,7 +87,15 @@ CHUNK = Workload("chunked_prefill", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192
 RECENT = Workload("recent_window", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
                   layers=32, outliers=4, seed=5, extra={"window": 128})
 
-ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT)}
+# Sliding-window (local-layer) attention: a 1024-token window over 8192-token
+# contexts, for decode (32 layers, K/V drawn on the device from a seeded
+# generator: 9 GB of cache) and for the chunked-prefill shape.
+SLIDING_DECODE = Workload("sliding_decode", 16, 32, 8, 128, 0, "contiguous", "bf16", 8191, 1,
+                          layers=32, seed=6, extra={"sliding": 1024})
+SLIDING_CHUNK = Workload("sliding_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512,
+                         seed=7, extra={"sliding": 1024})
+
+ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK)}
 
 
 # ----------------------------------------------------------------------------
