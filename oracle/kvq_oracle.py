@@ -118,6 +118,17 @@ def quantize(x: np.ndarray, group: int = 0):
     return codes, s
 
 
+def quantize_bf16_scale(x: np.ndarray):
+    """Per-token codes with the scale stored as bf16 ([P1]
+    `CudaQuantizedKvCache::quantize_tensor`): the codes come from the fp32
+    scale exactly as in :func:`quantize` (group 0), and the scale is kept as
+    its bf16 rounding (the page's `f32_to_bf16`, nearest even), which is what
+    dequantization then multiplies by.  Returns (codes uint8 [..., D],
+    scale bit patterns uint16 [..., 1])."""
+    codes, s = quantize(x, 0)
+    return codes, f32_to_bf16_bits(s)
+
+
 def _expand_scales(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     d = codes.shape[-1]
     gcount = scales.shape[-1]

@@ -675,3 +675,30 @@ def test_window_closed_forms():
             assert np.allclose(c1[0, h, i], v[0, h // 2, 6 + i], rtol=0, atol=1e-15)
     assert np.array_equal(orc.attention_chunk(qc, k, v, [6], True, 0.5, window=9),
                           orc.attention_chunk(qc, k, v, [6], True, 0.5))
+
+
+# ----------------------------------------------------------------------------
+# bf16-stored per-token scales (abaddon 0.2.0-rc.1 kv_cache_quant_cuda.rs,
+# CudaQuantizedKvCache::quantize_tensor)
+# ----------------------------------------------------------------------------
+
+def test_bf16_scale_storage():
+    """The codes come from the fp32 scale (half-step bound against it), the
+    stored scale is torch's bf16 rounding of it, and dequantizing with the
+    stored scale stays within s/2 + 127 |s - s_bf16|, a bound that can
+    exceed s/2 (the page's quantize/dequantize mismatch)."""
+    import torch
+    rng = np.random.default_rng(91)
+    x = (rng.standard_normal((4, 3, 50, 128)) * rng.uniform(0.01, 30, (4, 3, 50, 1))).astype(np.float32)
+    codes, sbits = orc.quantize_bf16_scale(x)
+    m = np.maximum(np.abs(x).max(axis=-1, keepdims=True), np.float32(1e-8))
+    s32 = (m / np.float32(127.0)).astype(np.float32)
+    want_bits = torch.from_numpy(s32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(sbits, want_bits)
+    c = codes.astype(np.float64) - 128
+    assert np.all(np.abs(x - c * s32.astype(np.float64)) <= s32.astype(np.float64) * (0.5 + 2 ** -20))
+    sb = orc.bf16_bits_to_f32(sbits).astype(np.float64)
+    err = np.abs(x - orc.dequantize_exact(codes, orc.bf16_bits_to_f32(sbits)))
+    bound = s32 * 0.5 + 127 * np.abs(s32 - sb)
+    assert np.all(err <= bound * (1 + 2 ** -20))
+    assert np.any(err > s32 * 0.5 * (1 + 2 ** -10))
