@@ -68,6 +68,7 @@ def step_bytes(w: wl.Workload, L: int) -> dict:
     B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
     G = 1 if w.group == 0 else D // 32
     in_bytes = 4 if w.kv_dtype == "f32" else 2
+    sb = 2 if w.extra.get("scale_bf16") else 4   # bytes per scale
     W = w.extra.get("window", 0)
     if W:
         # recent window: INT8 rows below L - W (the row leaving the window is
@@ -80,12 +81,12 @@ def step_bytes(w: wl.Workload, L: int) -> dict:
         app_in = 2 * B * KVH * D * in_bytes
         return {"decode": int8 + ring + qo, "append": app_in, "step": int8 + ring + qo + app_in}
     codes = 2 * B * KVH * L * D
-    scales = 2 * B * KVH * L * G * 4
+    scales = 2 * B * KVH * L * G * sb
     q = B * H * D * 2
     out = B * H * D * 2
     app_in = 2 * B * KVH * D * in_bytes
     app_codes = 2 * B * KVH * D
-    app_scales = 2 * B * KVH * G * 4
+    app_scales = 2 * B * KVH * G * sb
     decode = codes + scales + q + out
     return {"decode": decode, "append": app_in + app_codes + app_scales,
             "step": decode + app_in + app_codes + app_scales}
@@ -138,7 +139,8 @@ def build_layers(w: wl.Workload, kvq, torch, stream, threads: int):
                 li = len(layers)
                 x = done_layers.pop(li)
                 cache = kvq.Int8KVCache(w.batch, w.num_heads, w.num_kv_heads, w.head_dim, max_len=w.max_len,
-                                        group32=(w.group == 32), recent_window=w.extra.get("window", 0))
+                                        group32=(w.group == 32), recent_window=w.extra.get("window", 0),
+                                        scale_bf16=w.extra.get("scale_bf16", False))
                 k_raw, v_raw = x["k_raw"], x["v_raw"]
                 tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
 
@@ -223,16 +225,23 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     # then fp64 attention over the dequantized cache for all its heads
     x = wl.layer_inputs(w, 0)
     nb = w.batch
+
+    def quant(a):  # per-token / group-32, or per-token with the scale kept as bf16
+        if w.extra.get("scale_bf16"):
+            c, sb = orc.quantize_bf16_scale(a)
+            return c, orc.bf16_bits_to_f32(sb)
+        return orc.quantize(a, w.group)
+
     caches = []
     for b in range(nb):
-        kc, ks = orc.quantize(x["k"][b:b + 1, :, :w.ctx], w.group)
-        vc, vs = orc.quantize(x["v"][b:b + 1, :, :w.ctx], w.group)
+        kc, ks = quant(x["k"][b:b + 1, :, :w.ctx])
+        vc, vs = quant(x["v"][b:b + 1, :, :w.ctx])
         caches.append((kc, ks, vc, vs))
 
     def one_seq(b):
         kc, ks, vc, vs = caches[b]
-        nk, nks = orc.quantize(x["k"][b:b + 1, :, w.ctx:T], w.group)
-        nv, nvs = orc.quantize(x["v"][b:b + 1, :, w.ctx:T], w.group)
+        nk, nks = quant(x["k"][b:b + 1, :, w.ctx:T])
+        nv, nvs = quant(x["v"][b:b + 1, :, w.ctx:T])
         kcat = np.concatenate([kc, nk], axis=2)
         kscat = np.concatenate([ks, nks], axis=2)
         vcat = np.concatenate([vc, nv], axis=2)
@@ -646,7 +655,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
-                                                            "recent_window", "sliding_decode", "sliding_chunk"])
+                                                            "recent_window", "sliding_decode", "sliding_chunk",
+                                                            "bf16_scales"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -781,7 +791,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {w.batch}, {w.num_heads} q / {w.num_kv_heads} kv heads, "
                                f"head_dim {w.head_dim}, context {T}, "
-                               f"{'per-token' if w.group == 0 else 'group-32'} fp32 scales, {w.layers} layers, "
+                               f"{'per-token' if w.group == 0 else 'group-32'} "
+                               f"{'bf16' if w.extra.get('scale_bf16') else 'fp32'} scales, {w.layers} layers, "
                                + (f"last {w.extra['window']} tokens bf16 (recent window), " if w.extra.get("window")
                                   else "") +
                                f"append 1 token + decode per layer "

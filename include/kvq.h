@@ -57,7 +57,16 @@ typedef enum {
   KVQ_ERR_WORKSPACE = 5     /* workspace missing or smaller than required          */
 } kvq_status;
 
-enum { KVQ_SCALE_PER_TOKEN = 0, KVQ_SCALE_GROUP32 = 1 };
+/* Scale modes.  KVQ_SCALE_PER_TOKEN_BF16 (abaddon kv_cache_quant_cuda.rs,
+ * `CudaQuantizedKvCache::quantize_tensor`): the codes come from the fp32
+ * per-token scale exactly as in KVQ_SCALE_PER_TOKEN, and the scale is stored
+ * rounded to bf16 (nearest even), which every reader then multiplies by (the
+ * page's own mismatch: the dequantization error can exceed half a step).  In
+ * that mode k_scales / v_scales point to uint16 bf16 arrays of the same
+ * shape (4-byte aligned, as every scale array must be: kernels read the
+ * aligned word holding a scale).  Chunked attention supports the two
+ * per-token modes. */
+enum { KVQ_SCALE_PER_TOKEN = 0, KVQ_SCALE_GROUP32 = 1, KVQ_SCALE_PER_TOKEN_BF16 = 2 };
 enum { KVQ_LAYOUT_CONTIGUOUS = 0, KVQ_LAYOUT_PAGED = 1 };
 enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 };
 
@@ -77,7 +86,7 @@ typedef struct kvq_cache {
   const int32_t* block_table;  /* paged: device [batch, max_blocks_per_seq]       */
   uint8_t* k_codes;            /* device, layout above                            */
   uint8_t* v_codes;
-  float* k_scales;
+  float* k_scales;             /* fp32 (bf16 in KVQ_SCALE_PER_TOKEN_BF16)          */
   float* v_scales;
 } kvq_cache;
 
@@ -311,7 +320,7 @@ size_t kvq_workspace_size(const kvq_cache* cache, int32_t max_seq_len, int32_t n
 
 /* Bytes of codes plus scales the descriptor addresses, K and V together
  * (realizar kv_cache_q8_init.rs `kv_cache_q8_memory_bytes`: 2 * (values +
- * 4 * scales) per layer).  Contiguous: batch*KVH*max_len rows; paged:
+ * 4 * scales) per layer; 2 bytes per scale in KVQ_SCALE_PER_TOKEN_BF16).  Contiguous: batch*KVH*max_len rows; paged:
  * num_pages*KVH*16 rows.  0 on an invalid descriptor. */
 uint64_t kvq_cache_bytes(const kvq_cache* cache);
 

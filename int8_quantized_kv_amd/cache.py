@@ -22,7 +22,7 @@ class Int8KVCache:
     def __init__(self, batch: int, num_heads: int, num_kv_heads: int, head_dim: int, *,
                  max_len: int = 0, group32: bool = False, num_pages: int = 0,
                  block_table: torch.Tensor | None = None, device="cuda", fill: int | None = None,
-                 recent_window: int = 0, recent_capacity: int | None = None):
+                 recent_window: int = 0, recent_capacity: int | None = None, scale_bf16: bool = False):
         self.batch, self.num_heads, self.num_kv_heads, self.head_dim = batch, num_heads, num_kv_heads, head_dim
         self.groups = head_dim // 32 if group32 else 1
         self.paged = block_table is not None
@@ -44,13 +44,17 @@ class Int8KVCache:
         else:
             self.k_codes = torch.full(shape_c, fill, dtype=torch.uint8, device=device)
             self.v_codes = torch.full(shape_c, fill, dtype=torch.uint8, device=device)
-        self.k_scales = torch.zeros(shape_s, dtype=torch.float32, device=device)
-        self.v_scales = torch.zeros(shape_s, dtype=torch.float32, device=device)
+        if scale_bf16 and group32:
+            raise ValueError("bf16-stored scales are per-token only")
+        sdt = torch.bfloat16 if scale_bf16 else torch.float32
+        self.k_scales = torch.zeros(shape_s, dtype=sdt, device=device)
+        self.v_scales = torch.zeros(shape_s, dtype=sdt, device=device)
         self.desc = _k.make_cache(
             batch, num_heads, num_kv_heads, head_dim, self.k_codes, self.v_codes, self.k_scales,
             self.v_scales,
             layout=_k.KVQ_LAYOUT_PAGED if self.paged else _k.KVQ_LAYOUT_CONTIGUOUS,
-            scale_mode=_k.KVQ_SCALE_GROUP32 if group32 else _k.KVQ_SCALE_PER_TOKEN,
+            scale_mode=(_k.KVQ_SCALE_GROUP32 if group32 else
+                        _k.KVQ_SCALE_PER_TOKEN_BF16 if scale_bf16 else _k.KVQ_SCALE_PER_TOKEN),
             max_len=0 if self.paged else max_len, num_pages=num_pages,
             max_blocks_per_seq=self.max_blocks, block_table=self.block_table)
         # recent-window hybrid: the last W positions of each sequence stay bf16

@@ -36,7 +36,8 @@ kvq_status check_cache(const kvq_cache* c, const char* who) {
     return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be a multiple of 32", who, c->head_dim);
   if (c->head_dim > 256)
     return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be at most 256", who, c->head_dim);
-  if (c->scale_mode != KVQ_SCALE_PER_TOKEN && c->scale_mode != KVQ_SCALE_GROUP32)
+  if (c->scale_mode != KVQ_SCALE_PER_TOKEN && c->scale_mode != KVQ_SCALE_GROUP32 &&
+      c->scale_mode != KVQ_SCALE_PER_TOKEN_BF16)
     return fail(KVQ_ERR_INVALID_ARG, "%s: unknown scale_mode %d", who, c->scale_mode);
   if (c->layout == KVQ_LAYOUT_CONTIGUOUS) {
     if (c->max_len <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: contiguous cache needs max_len > 0", who);
@@ -53,6 +54,8 @@ kvq_status check_cache(const kvq_cache* c, const char* who) {
   }
   if (!c->k_codes || !c->v_codes || !c->k_scales || !c->v_scales)
     return fail(KVQ_ERR_INVALID_ARG, "%s: cache code and scale pointers must be non-NULL", who);
+  if (((reinterpret_cast<uintptr_t>(c->k_scales) | reinterpret_cast<uintptr_t>(c->v_scales)) & 3) != 0)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: scale arrays must be 4-byte aligned", who);
   return KVQ_OK;
 }
 
@@ -80,7 +83,7 @@ KVQ_API uint64_t kvq_cache_bytes(const kvq_cache* c) {
   const uint64_t rows = c->layout == KVQ_LAYOUT_PAGED
                             ? static_cast<uint64_t>(c->num_pages) * c->num_kv_heads * kPageSize
                             : static_cast<uint64_t>(c->batch) * c->num_kv_heads * c->max_len;
-  const uint64_t per_row = static_cast<uint64_t>(c->head_dim) + 4ull * scales_per_row(*c);
+  const uint64_t per_row = static_cast<uint64_t>(c->head_dim) + static_cast<uint64_t>(scale_bytes(*c)) * scales_per_row(*c);
   return 2ull * rows * per_row;
 }
 

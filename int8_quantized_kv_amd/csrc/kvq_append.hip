@@ -33,6 +33,7 @@ struct AppendParams {
   int32_t in_bf16;
   int32_t mode;                        // AppendMode
   int32_t rwin, rcap;                  // recent window and ring slots
+  int32_t scale_bf16;                  // per-token scales stored as bf16
 };
 
 // Stores this lane's EPL values of a row as bf16 (nearest even).
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     if (GROUP32) {
       if ((lane % kGroupLanes) == 0) sc[lane / kGroupLanes] = s;
     } else if (lane == 0) {
-      sc[0] = s;
+      store_scale(p.scales[side], dst, s, p.scale_bf16 != 0);
     }
   }
 }
@@ -117,6 +118,7 @@ struct DequantParams {
   const float* scales;
   const uint16_t* ring;      // recent window: bf16 [B, KVH, rcap, D]
   int32_t rwin, rcap;        // window (0: none) and ring slots
+  int32_t scale_bf16;        // per-token scales stored as bf16
   const int32_t* seq_lens;
   void* out;
   CacheGeom geom;
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
     v[3] = __uint_as_float(r.y & 0xffff0000u);
   } else if (row >= 0) {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
-    const float s = p.scales[row * p.groups + (p.groups == 1 ? 0 : d / 32)];
+    const float s = load_scale(p.scales, row * p.groups + (p.groups == 1 ? 0 : d / 32), p.scale_bf16 != 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       v[e] = static_cast<float>(static_cast<int>((c >> (8 * e)) & 0xffu) - 128) * s;
@@ -187,6 +189,7 @@ kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_ne
   p.rwin = rc.window;
   p.rcap = rc.cap;
   p.n_new = n_new;
+  p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
   p.src[0] = k_new;
   p.src[1] = v_new;
   p.codes[0] = c.k_codes;
@@ -227,6 +230,7 @@ kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens
   p.ring = which ? rc.v : rc.k;
   p.rwin = rc.window;
   p.rcap = rc.cap;
+  p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
   p.codes = which ? c.v_codes : c.k_codes;
   p.scales = which ? c.v_scales : c.k_scales;
   p.seq_lens = seq_lens;

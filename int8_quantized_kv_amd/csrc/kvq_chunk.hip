@@ -163,7 +163,9 @@ __device__ __forceinline__ int64_t row_of(const ChunkParams& p, int b, int g, in
   }
 }
 
-template <int D, bool PAGED>
+// SBF: per-token scales stored as bf16 (a template argument so that the fp32
+// mode keeps its registers)
+template <int D, bool PAGED, bool SBF>
 __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   using TL = Tile<D, kCkTile>;
   constexpr int kTT = kCkTile / 32;                        // 32-token S tiles per tile
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   // scales (first half K, second half V)
   const bool ld_s = tid < 2 * kCkTile;
   uint4 lreg[kLoads];
-  float sreg = 0.0f;
+  uint32_t sreg = 0u;  // scale word as loaded, decoded when the tile is stored
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       const int t = t0 + (tid & (kCkTile - 1));
       if (t < Ltot) {
         const int64_t row = row_of<PAGED>(p, b, g, t);
-        sreg = tid < kCkTile ? p.k_scales[row] : p.v_scales[row];
+        sreg = scale_word(tid < kCkTile ? p.k_scales : p.v_scales, row, SBF);
       }
     }
   };
@@ -297,11 +299,16 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     if (ld_s) {
       const int tl = tid & (kCkTile - 1);
       const bool ok = t0 + tl < Ltot;
+      // which half of the word holds a bf16 scale: the parity of the row
+      // (page rows start even, so in the paged layout the token's parity)
+      const int64_t srow = PAGED ? static_cast<int64_t>(t0 + tl)
+                                 : (static_cast<int64_t>(b) * p.geom.kvh + g) * p.geom.max_len + t0 + tl;
+      const float sv = scale_value(sreg, scale_sel(srow, SBF));
       if (tid < kCkTile) {
-        reinterpret_cast<float*>(buf + TL::kKc)[tl] = ok ? sreg * kfac : 0.0f;
+        reinterpret_cast<float*>(buf + TL::kKc)[tl] = ok ? sv * kfac : 0.0f;
       } else {
-        reinterpret_cast<float*>(buf + TL::kLsv)[tl] = ok ? __builtin_amdgcn_logf(sreg) : -INFINITY;
-        reinterpret_cast<float*>(buf + TL::kRsv)[tl] = ok ? 1.0f / sreg : 0.0f;
+        reinterpret_cast<float*>(buf + TL::kLsv)[tl] = ok ? __builtin_amdgcn_logf(sv) : -INFINITY;
+        reinterpret_cast<float*>(buf + TL::kRsv)[tl] = ok ? 1.0f / sv : 0.0f;
       }
     }
   };
@@ -535,6 +542,17 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   }
 }
 
+template <int D>
+void launch_chunk_d(bool paged, bool sbf, dim3 grid, hipStream_t stream, const ChunkParams& p) {
+  if (paged) {
+    if (sbf) hipLaunchKernelGGL((chunk_kernel<D, true, true>), grid, dim3(kCkThreads), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_kernel<D, true, false>), grid, dim3(kCkThreads), 0, stream, p);
+  } else {
+    if (sbf) hipLaunchKernelGGL((chunk_kernel<D, false, true>), grid, dim3(kCkThreads), 0, stream, p);
+    else hipLaunchKernelGGL((chunk_kernel<D, false, false>), grid, dim3(kCkThreads), 0, stream, p);
+  }
+}
+
 }  // namespace
 
 bool chunk_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
@@ -543,7 +561,7 @@ size_t chunk_workspace(const kvq_cache&, int, int) { return 0; }
 
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens, int causal,
                         float attn_scale, uint16_t* out, void*, int, hipStream_t stream, int window) {
-  if (c.scale_mode != KVQ_SCALE_PER_TOKEN)
+  if (c.scale_mode == KVQ_SCALE_GROUP32)
     return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: group-32 scales are not supported");
   ChunkParams p;
   p.q = q;
@@ -569,13 +587,9 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.total_wgs = static_cast<int32_t>(total);
   const dim3 grid(static_cast<unsigned>(total));
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  if (c.head_dim == 128) {
-    if (paged) hipLaunchKernelGGL((chunk_kernel<128, true>), grid, dim3(kCkThreads), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<128, false>), grid, dim3(kCkThreads), 0, stream, p);
-  } else {
-    if (paged) hipLaunchKernelGGL((chunk_kernel<64, true>), grid, dim3(kCkThreads), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<64, false>), grid, dim3(kCkThreads), 0, stream, p);
-  }
+  const bool sbf = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16;
+  if (c.head_dim == 128) launch_chunk_d<128>(paged, sbf, grid, stream, p);
+  else launch_chunk_d<64>(paged, sbf, grid, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;

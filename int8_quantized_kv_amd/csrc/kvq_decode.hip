@@ -48,6 +48,9 @@ constexpr int kCUs = 256;          // MI355X compute units: the split heuristic 
 constexpr int kBlock = 64;         // tokens per wave block (streaming kernel)
 constexpr int kLongestFirstMax = kStreamThreads;  // largest batch ranked by length in a workgroup
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSmToken = KVQ_SCALE_PER_TOKEN;         // scale modes, as kernel template arguments
+constexpr int kSmGroup32 = KVQ_SCALE_GROUP32;
+constexpr int kSmTokenBf16 = KVQ_SCALE_PER_TOKEN_BF16;
 constexpr float kLazy = 8.0f;      // log2 headroom before a rescale
 constexpr int kWeightShift = 7;    // weights carry 2^7 so they fill f16 range
 
@@ -84,6 +87,7 @@ struct DecodeParams {
   // sliding window (0: none): the query at position L - 1 sees keys in
   // (L - 1 - window, L - 1]
   int32_t window;
+  int32_t scale_bf16;        // per-token scales stored as bf16
 };
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* x) {
@@ -557,7 +561,9 @@ __device__ void ring_into_wave(const DecodeParams& p, int b, int kvh, int h0, in
 // ---------------------------------------------------------------------------
 // Streaming kernel (head_dim 32, 64, 128).
 // ---------------------------------------------------------------------------
-template <int D, int HPW, bool G32, bool PAGED, bool APPEND>
+// SM: scale mode (kSmToken fp32 per token, kSmGroup32, kSmTokenBf16 bf16 per
+// token), a template argument so each mode pays only for its own decoding
+template <int D, int HPW, int SM, bool PAGED, bool APPEND>
 __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(DecodeParams p) {
   // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
   // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
@@ -565,6 +571,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   constexpr int LK = D / 16, TK = kWave / LK, NPK = kBlock / TK;
   constexpr int LV = D / 8, TV = kWave / LV, NPV = kBlock / TV;
   constexpr int NPAIR = NPV / 2;             // token pairs per lane per block
+  constexpr bool G32 = SM == kSmGroup32;
+  constexpr bool SBF = SM == kSmTokenBf16;
   constexpr int NG = G32 ? D / 32 : 1;       // scales per row
   constexpr int kSwz = 16 / LK;              // partial-score swizzle
   static_assert(NPV % 2 == 0 && LV <= 16, "block shape");
@@ -633,6 +641,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   int32_t pq[kPidAhead][kBlock / kPageSize] = {};
   float s_k[NG];        // K scales of this lane's softmax token (per token or per group)
   float s_v[NG];        // V scales of this lane's softmax token
+  // per-token: the scale words as loaded (fp32, or the aligned word holding a
+  // bf16 scale), decoded only where the softmax uses them so that the
+  // prefetch is not waited for early; which half holds a bf16 scale follows
+  // from the parity of the token's row, recomputed there
+  uint32_t s_kw = 0u, s_vw = 0u;
   const int vgroup = G32 ? vsub / 4 : 0;
   const int64_t seq_row0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.geom.max_len;
   const uint32_t koff = static_cast<uint32_t>(kslot * D + ksub * 16);   // lane's byte offset in a K pass
@@ -697,12 +710,15 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       const float4 v4 = *reinterpret_cast<const float4*>(p.v_scales + srow * NG);
       s_k[0] = k4.x; s_k[1] = k4.y; s_k[2] = k4.z; s_k[3] = k4.w;
       s_v[0] = v4.x; s_v[1] = v4.y; s_v[2] = v4.z; s_v[3] = v4.w;
-    } else {
+    } else if constexpr (G32) {
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         s_k[g] = p.k_scales[srow * NG + g];
         s_v[g] = p.v_scales[srow * NG + g];
       }
+    } else {
+      s_kw = scale_word(p.k_scales, srow, SBF);
+      s_vw = scale_word(p.v_scales, srow, SBF);
     }
   };
   // scales of the softmax token (token `lane`) of block bi
@@ -786,10 +802,18 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         for (int i = 0; i < NPV; ++i)
           if (i * TV + vslot == rel) vb[i] = sm_nv[vsub];
         if (lane == rel) {
+          if constexpr (G32) {
 #pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            s_k[g] = sm_ns[0][g];
-            s_v[g] = sm_ns[1][g];
+            for (int g = 0; g < NG; ++g) {
+              s_k[g] = sm_ns[0][g];
+              s_v[g] = sm_ns[1][g];
+            }
+          } else {
+            // a stored bf16 scale has a zero low half: copied into both
+            // halves it decodes the same whichever half is selected
+            const uint32_t nk = __float_as_uint(sm_ns[0][0]), nv = __float_as_uint(sm_ns[1][0]);
+            s_kw = SBF ? nk | (nk >> 16) : nk;
+            s_vw = SBF ? nv | (nv >> 16) : nv;
           }
         }
       }
@@ -825,6 +849,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     const int t = t_begin + blk * kBlock + lane;
     const bool valid = t < t_end && t >= t_min;
     float4 acc4 = sm_part[wave][lane ^ 0];
+    if constexpr (!G32) {
+      // the row of the (clamped) token: page rows start even, so in the paged
+      // layout its parity is the token's
+      const int tc = min(t, t_end - 1);
+      const uint32_t sel = scale_sel(PAGED ? static_cast<int64_t>(tc) : seq_row0 + tc, SBF);
+      s_k[0] = scale_value(s_kw, sel);
+      s_v[0] = scale_value(s_vw, sel);
+    }
     if constexpr (G32) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
 #pragma unroll
     for (int r = 1; r < LK; ++r) {
@@ -1038,8 +1070,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
               sm_ns[wave][lane / kGroupLanes] = sc;
             }
           } else if (lane == 0) {
-            gs[0] = sc;
-            sm_ns[wave][0] = sc;
+            sm_ns[wave][0] = store_scale(wave == 0 ? p.k_scales : p.v_scales, row, sc, SBF);
           }
         }
       }
@@ -1195,8 +1226,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
       }
       kb[u] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + sub * 16);
       vb[u] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + sub * 16);
-      ks[u] = p.k_scales[row * p.groups + grp];
-      vs[u] = p.v_scales[row * p.groups + grp];
+      ks[u] = load_scale(p.k_scales, row * p.groups + grp, p.scale_bf16 != 0);
+      vs[u] = load_scale(p.v_scales, row * p.groups + grp, p.scale_bf16 != 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -1333,38 +1364,41 @@ int pass_tokens(int head_dim) {
   return use_stream(head_dim) ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
 }
 
-template <int D, int HPW, bool G32, bool PAGED>
+template <int D, int HPW, int SM, bool PAGED>
 void launch_kernel(bool stream_kernel, bool append, const DecodeParams& p, dim3 grid, hipStream_t st) {
   if (stream_kernel) {
     if constexpr (D <= 128) {
       if (append)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED, true>), grid, dim3(kStreamThreads), 0, st, p);
+        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, PAGED, true>), grid, dim3(kStreamThreads), 0, st, p);
       else
-        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, G32, PAGED, false>), grid, dim3(kStreamThreads), 0, st, p);
+        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, PAGED, false>), grid, dim3(kStreamThreads), 0, st, p);
     }
   } else {
-    hipLaunchKernelGGL((decode_generic_kernel<D, HPW, G32, PAGED>), grid, dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM == kSmGroup32, PAGED>), grid, dim3(kThreads), 0, st, p);
   }
 }
 
 template <int D, int HPW>
-void launch_modes(bool stream_kernel, bool append, bool g32, bool paged, const DecodeParams& p, dim3 grid,
+void launch_modes(bool stream_kernel, bool append, int sm, bool paged, const DecodeParams& p, dim3 grid,
                   hipStream_t st) {
-  if (g32) {
-    if (paged) launch_kernel<D, HPW, true, true>(stream_kernel, append, p, grid, st);
-    else launch_kernel<D, HPW, true, false>(stream_kernel, append, p, grid, st);
+  if (sm == kSmGroup32) {
+    if (paged) launch_kernel<D, HPW, kSmGroup32, true>(stream_kernel, append, p, grid, st);
+    else launch_kernel<D, HPW, kSmGroup32, false>(stream_kernel, append, p, grid, st);
+  } else if (sm == kSmTokenBf16) {
+    if (paged) launch_kernel<D, HPW, kSmTokenBf16, true>(stream_kernel, append, p, grid, st);
+    else launch_kernel<D, HPW, kSmTokenBf16, false>(stream_kernel, append, p, grid, st);
   } else {
-    if (paged) launch_kernel<D, HPW, false, true>(stream_kernel, append, p, grid, st);
-    else launch_kernel<D, HPW, false, false>(stream_kernel, append, p, grid, st);
+    if (paged) launch_kernel<D, HPW, kSmToken, true>(stream_kernel, append, p, grid, st);
+    else launch_kernel<D, HPW, kSmToken, false>(stream_kernel, append, p, grid, st);
   }
 }
 
 template <int D>
-void launch_d(bool stream_kernel, bool append, int hpw, bool g32, bool paged, const DecodeParams& p, dim3 grid,
+void launch_d(bool stream_kernel, bool append, int hpw, int sm, bool paged, const DecodeParams& p, dim3 grid,
               hipStream_t st) {
-  if (hpw == 4) launch_modes<D, 4>(stream_kernel, append, g32, paged, p, grid, st);
-  else if (hpw == 2) launch_modes<D, 2>(stream_kernel, append, g32, paged, p, grid, st);
-  else launch_modes<D, 1>(stream_kernel, append, g32, paged, p, grid, st);
+  if (hpw == 4) launch_modes<D, 4>(stream_kernel, append, sm, paged, p, grid, st);
+  else if (hpw == 2) launch_modes<D, 2>(stream_kernel, append, sm, paged, p, grid, st);
+  else launch_modes<D, 1>(stream_kernel, append, sm, paged, p, grid, st);
 }
 
 int env_int(const char* name, int dflt) {
@@ -1445,6 +1479,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   p.v_codes = c.v_codes;
   p.k_scales = c.k_scales;
   p.v_scales = c.v_scales;
+  p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
   p.q = q;
   p.seq_lens = seq_lens;
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * plan.num_splits;
@@ -1475,14 +1510,14 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, c.batch);
   if (grid.y > 65535 || grid.z > 65535)
     return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_decode: grid too large");
-  const bool g32 = c.scale_mode == KVQ_SCALE_GROUP32;
+  const int sm = c.scale_mode;
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
   const bool fused = append && stream_kernel;
   switch (c.head_dim) {
-    case 32: launch_d<32>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
-    case 64: launch_d<64>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
-    case 128: launch_d<128>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
-    default: launch_d<256>(stream_kernel, fused, plan.heads_per_wg, g32, paged, p, grid, stream); break;
+    case 32: launch_d<32>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
+    case 64: launch_d<64>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
+    case 128: launch_d<128>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
+    default: launch_d<256>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: launch failed: %s", hipGetErrorString(e));

@@ -26,6 +26,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Per-row scales are fp32, or bf16 in the same array's memory (bf16-stored
+// per-token scales: abaddon kv_cache_quant_cuda.rs `CudaQuantizedKvCache`
+// keeps its scales as BF16).
+__device__ __forceinline__ float load_scale(const float* scales, int64_t idx, bool bf16) {
+  return bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(scales)[idx]) : scales[idx];
+}
+
+// The same, split in two so that a pipelined load is not waited for at once:
+// scale_word loads the 32-bit word holding the scale (for bf16, the aligned
+// word containing it; the array must be 4-byte aligned, so the word never
+// crosses a page), scale_sel records which half, and scale_value decodes the
+// word where the scale is used.
+__device__ __forceinline__ uint32_t scale_word(const float* scales, int64_t idx, bool bf16) {
+  return reinterpret_cast<const uint32_t*>(scales)[idx >> (bf16 ? 1 : 0)];
+}
+__device__ __forceinline__ uint32_t scale_sel(int64_t idx, bool bf16) {
+  return bf16 ? static_cast<uint32_t>(idx & 1) : 2u;
+}
+__device__ __forceinline__ float scale_value(uint32_t w, uint32_t sel) {
+  return __uint_as_float(sel == 2u ? w : (sel ? (w & 0xffff0000u) : (w << 16)));
+}
+
+// Stores a scale and returns the value a reader will get back.
+__device__ __forceinline__ float store_scale(float* scales, int64_t idx, float s, bool bf16) {
+  if (!bf16) {
+    scales[idx] = s;
+    return s;
+  }
+  const uint16_t h = f32_to_bf16_rne(s);
+  reinterpret_cast<uint16_t*>(scales)[idx] = h;
+  return bf16_to_f32(h);
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane helpers.  DPP row controls (GFX9 encoding).
 // ---------------------------------------------------------------------------

@@ -28,6 +28,8 @@ inline int scales_per_row(const kvq_cache& c) {
   return c.scale_mode == KVQ_SCALE_GROUP32 ? c.head_dim / 32 : 1;
 }
 
+inline int scale_bytes(const kvq_cache& c) { return c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 2 : 4; }
+
 inline int capacity_of(const kvq_cache& c) {
   return c.layout == KVQ_LAYOUT_PAGED ? c.max_blocks_per_seq * kPageSize : c.max_len;
 }

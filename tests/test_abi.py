@@ -242,3 +242,11 @@ def test_window_argument_errors():
     # a window shorter than the hint plans fewer splits
     big = _desc(max_len=32768)
     assert 0 < kvq.kvq_workspace_size_window(big, 32768, 1, 256) < kvq.kvq_workspace_size(big, 32768, 1)
+
+
+def test_bf16_scale_mode_sizing():
+    """bf16-stored per-token scales take 2 bytes per row."""
+    d = _desc(scale_mode=kvq.KVQ_SCALE_PER_TOKEN_BF16, max_len=4096)
+    assert kvq.kvq_cache_bytes(d) == 2 * 2 * 2 * 4096 * (128 + 2)
+    assert kvq.kvq_cache_bytes(_desc(max_len=4096)) == 2 * 2 * 2 * 4096 * (128 + 4)
+    assert _status("kvq_cache_bytes", ctypes.byref(_desc(scale_mode=3)))[0] == 0

@@ -95,7 +95,13 @@ SLIDING_DECODE = Workload("sliding_decode", 16, 32, 8, 128, 0, "contiguous", "bf
 SLIDING_CHUNK = Workload("sliding_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512,
                          seed=7, extra={"sliding": 1024})
 
-ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK)}
+# The 8B-shaped decode step with per-token scales stored as bf16 (the GPU
+# cache of abaddon kv_cache_quant_cuda.rs keeps them so).
+BF16_SCALES = Workload("bf16_scales", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
+                       layers=32, outliers=4, seed=8, extra={"scale_bf16": True})
+
+ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
+                           BF16_SCALES)}
 
 
 # ----------------------------------------------------------------------------
