@@ -320,8 +320,9 @@ size_t kvq_workspace_size(const kvq_cache* cache, int32_t max_seq_len, int32_t n
 
 /* Bytes of codes plus scales the descriptor addresses, K and V together
  * (realizar kv_cache_q8_init.rs `kv_cache_q8_memory_bytes`: 2 * (values +
- * 4 * scales) per layer; 2 bytes per scale in KVQ_SCALE_PER_TOKEN_BF16).  Contiguous: batch*KVH*max_len rows; paged:
- * num_pages*KVH*16 rows.  0 on an invalid descriptor. */
+ * 4 * scales) per layer; 2 bytes per scale in KVQ_SCALE_PER_TOKEN_BF16).
+ * Contiguous: batch*KVH*max_len rows; paged: num_pages*KVH*16 rows.  0 on an
+ * invalid descriptor. */
 uint64_t kvq_cache_bytes(const kvq_cache* cache);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */

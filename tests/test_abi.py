@@ -112,6 +112,8 @@ INVALID_DESCRIPTORS = [
     ("paged_no_table", dict(layout=kvq.KVQ_LAYOUT_PAGED, num_pages=4, max_blocks_per_seq=2)),
     ("null_codes", dict(ptrs=(0, FAKE, FAKE, FAKE))),
     ("null_scales", dict(ptrs=(FAKE, FAKE, FAKE, 0))),
+    # kernels read the aligned 32-bit word that holds a scale
+    ("misaligned_scales", dict(scale_mode=kvq.KVQ_SCALE_PER_TOKEN_BF16, ptrs=(FAKE, FAKE, FAKE + 2, FAKE))),
 ]
 
 
