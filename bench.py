@@ -103,8 +103,9 @@ def chunk_counts(w: wl.Workload) -> dict:
         visible = n * (L0 + 1) + n * (n - 1) // 2      # sum over i < n of L0 + i + 1
     flops = 4 * B * H * D * visible
     L = L0 + n
-    codes = 2 * B * KVH * L * D
-    scales = 2 * B * KVH * L * 4
+    rows = L - max(0, L0 - win + 1) if win else L    # keys some query of the chunk sees
+    codes = 2 * B * KVH * rows * D
+    scales = 2 * B * KVH * rows * 4
     qo = 2 * B * H * n * D * 2
     append = 2 * B * KVH * n * (D * 2 + D + 4)
     return {"flops": flops, "chunk_bytes": codes + scales + qo, "step_bytes": codes + scales + qo + append}
@@ -356,10 +357,11 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
         wall = time.perf_counter() - t0
         k_ms = time_calls(kernel_pass, args.kernel_reps, stream, torch)
     cnt = chunk_counts(w)
+    kname = "kvq_attention_chunk_window" if win else "kvq_attention_chunk"
     tflops = cnt["flops"] / (step_ms * 1e-3) / 1e12
     k_tflops = cnt["flops"] / (k_ms * 1e-3) / 1e12
     log(f"step {step_ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), wall {wall * 1e3 / args.steps:.3f} ms/step; "
-        f"kvq_attention_chunk {k_ms * 1e3:.1f} us = {k_tflops:.1f} TFLOP/s "
+        f"{kname} {k_ms * 1e3:.1f} us = {k_tflops:.1f} TFLOP/s "
         f"({k_tflops / MFMA_F16_PEAK_TFLOPS * 100:.1f}% of {MFMA_F16_PEAK_TFLOPS:.0f})")
     cpu = None
     if not args.no_cpu_baseline:
@@ -384,11 +386,12 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
                                + (f", sliding window {win}" if win else "") + ", per-token fp32 scales; "
                                f"append the {w.n_new} rows + chunk attention",
                    "batch": B, "seq_len": T, "flops_per_step": cnt["flops"], "bytes_per_step": cnt["step_bytes"]},
-        "roofline": {"bound": "mfma", "kernel": "kvq_attention_chunk",
+        "roofline": {"bound": "mfma", "kernel": kname,
                      "achieved": round(k_tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(k_tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("kvq_attention_chunk", w.name),
-                     "flops_per_launch": cnt["flops"], "us_per_launch": round(k_ms * 1e3, 3)},
+                     "traffic": recorded_traffic(kname, w.name),
+                     "flops_per_launch": cnt["flops"], "bytes_per_launch": cnt["chunk_bytes"],
+                     "us_per_launch": round(k_ms * 1e3, 3)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
