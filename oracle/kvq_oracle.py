@@ -157,6 +157,97 @@ def dequantize_bf16_bits(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# FP8 codes ([P5] `KVCacheFormat::Fp8E4M3` / `Fp8E5M2`): each element is stored
+# as one FP8 byte of its own value, with no scale; the page's converters
+# `quantize_fp8_e4m3` / `quantize_fp8_e5m2` and `dequantize_fp8_*`
+# ----------------------------------------------------------------------------
+
+# (mantissa bits, exponent bias, code of a positive infinity input,
+#  code of a positive overflow)
+FP8_FORMATS = {
+    "e4m3": (3, 7, 0x7F, 0x7E),
+    "e5m2": (2, 15, 0x7C, 0x7C),
+}
+
+
+def fp8_encode(x: np.ndarray, fmt: str) -> np.ndarray:
+    """fp32 -> FP8 byte, as [P5] `quantize_fp8_e4m3` / `quantize_fp8_e5m2`
+    compute it (an encoding, so its steps are followed in order):
+      1. NaN -> 0xFF;  +/-inf -> the format's infinity code (E4M3 0x7F / 0xFF,
+         E5M2 0x7C / 0xFC);  +/-0 -> 0x00.
+      2. Split the fp32 word: sign s, unbiased exponent e (raw field - 127),
+         24-bit significand m (the implicit leading one added unless the raw
+         exponent field is 0).
+      3. Target exponent E = e + bias (7 or 15).
+      4. E above the largest field (15 or 31): s | overflow code (E4M3 0x7E,
+         the largest finite value 448; E5M2 0x7C, infinity).
+      5. -M < E <= 0 (M = mantissa bits): a subnormal; the mantissa field is
+         the top M + E bits of m, so the value is cut toward zero.
+      6. E <= -M: s | 0 (a signed zero).
+      7. Otherwise s | E << M | the top M fraction bits of m (cut toward
+         zero, no rounding).
+    Returns uint8 codes of ``x``'s shape.  Note step 7 at the largest
+    exponent field can give the format's NaN or infinity patterns
+    (E4M3 |x| in [480, 512); E5M2 |x| in [65536, 131072)), as on the page.
+    """
+    mbits, bias, inf_code, over_code = FP8_FORMATS[fmt]
+    emax = (1 << (7 - mbits)) - 1
+    xf = np.ascontiguousarray(x, dtype=np.float32)
+    u = xf.view(np.uint32).astype(np.int64)
+    sign = (u >> 31) & 1
+    raw_e = (u >> 23) & 0xFF
+    e = raw_e - 127
+    m = (u & 0x7FFFFF) | np.where(raw_e != 0, 1 << 23, 0)
+    E = e + bias
+    s7 = sign << 7
+    mask = (1 << mbits) - 1
+    out = np.empty(xf.shape, dtype=np.int64)
+    normal = (E >= 1) & (E <= emax)
+    out[normal] = s7[normal] | (E[normal] << mbits) | ((m[normal] >> (23 - mbits)) & mask)
+    sub = (E > -mbits) & (E <= 0)
+    shift = 24 - (mbits + E[sub])
+    out[sub] = s7[sub] | ((m[sub] >> shift) & (mask >> (-E[sub])))
+    out[E <= -mbits] = s7[E <= -mbits]
+    out[E > emax] = s7[E > emax] | over_code
+    out[xf == 0] = 0
+    isinf = np.isinf(xf)
+    out[isinf] = np.where(xf[isinf] > 0, inf_code, 0x80 | inf_code)
+    out[np.isnan(xf)] = 0xFF
+    return out.astype(np.uint8)
+
+
+def fp8_decode(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """FP8 byte -> value (fp64, exact), as [P5] `dequantize_fp8_e4m3` /
+    `dequantize_fp8_e5m2` define it: a zero magnitude field is +0 (for either
+    sign bit); E4M3 S.1111.111 is NaN; E5M2 S.11111.00 is +/-inf and
+    S.11111.{01,10,11} NaN; an exponent field F > 0 gives
+    (-1)^s 2^(F - bias) (1 + f / 2^M), and F = 0 the subnormal
+    (-1)^s f 2^(1 - bias - M) (the page builds the same numbers case by case)."""
+    mbits, bias, _, _ = FP8_FORMATS[fmt]
+    c = np.asarray(codes).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    F = (c >> mbits) & ((1 << (7 - mbits)) - 1)
+    f = c & ((1 << mbits) - 1)
+    mag = np.where(F > 0, np.ldexp(1.0 + f / float(1 << mbits), F - bias),
+                   np.ldexp(f.astype(np.float64), 1 - bias - mbits))
+    val = sign * mag
+    low = c & 0x7F
+    val = np.where(low == 0, 0.0, val)
+    if fmt == "e4m3":
+        val = np.where(low == 0x7F, np.nan, val)
+    else:
+        val = np.where(low == 0x7C, sign * np.inf, val)
+        val = np.where(low >= 0x7D, np.nan, val)
+    return val
+
+
+def fp8_decode_bf16_bits(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """bf16 (RNE) of the decoded value, as uint16 bit patterns (every finite
+    E4M3 / E5M2 value fits fp32 exactly)."""
+    return f32_to_bf16_bits(fp8_decode(codes, fmt).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------
 # Cache layouts
 # ----------------------------------------------------------------------------
 
@@ -454,7 +545,8 @@ def fp32_equivalent_bytes(num_kv_heads: int, max_len: int, head_dim: int,
 
 def codes_bytes(num_kv_heads: int, max_len: int, head_dim: int,
                 batch: int = 1, layers: int = 1) -> int:
-    """u8 code bytes alone for K and V."""
+    """u8 code bytes alone for K and V (also the whole of an FP8 cache, which
+    keeps no scales: [P5] `KVCacheFormat::uses_scales`)."""
     return layers * batch * 2 * num_kv_heads * max_len * head_dim
 
 

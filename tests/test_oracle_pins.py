@@ -702,3 +702,111 @@ def test_bf16_scale_storage():
     bound = s32 * 0.5 + 127 * np.abs(s32 - sb)
     assert np.all(err <= bound * (1 + 2 ** -20))
     assert np.any(err > s32 * 0.5 * (1 + 2 ** -10))
+
+
+# ----------------------------------------------------------------------------
+# FP8 codes (llama-gguf 0.14.0 kv_quantized.rs, quantize_fp8_* / dequantize_fp8_*)
+# ----------------------------------------------------------------------------
+
+FP8_TORCH = {"e4m3": "float8_e4m3fn", "e5m2": "float8_e5m2"}
+# below these magnitudes every finite input has a finite code on the page
+FP8_FINITE_LIMIT = {"e4m3": 480.0, "e5m2": 65536.0}
+
+
+def _torch_fp8_values(fmt):
+    torch = pytest.importorskip("torch")
+    c = np.arange(256, dtype=np.uint8)
+    return torch.from_numpy(c).view(getattr(torch, FP8_TORCH[fmt])).float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_decode_matches_library_cast(fmt):
+    """All 256 codes decode to torch's OCP float8 value (NaN where it is NaN,
+    +/-inf for E5M2's infinities); the page decodes negative zero as +0."""
+    lib = _torch_fp8_values(fmt)
+    ours = orc.fp8_decode(np.arange(256, dtype=np.uint8), fmt)
+    assert np.array_equal(np.isnan(ours), np.isnan(lib))
+    ok = ~np.isnan(lib)
+    assert np.array_equal(ours[ok], lib[ok])
+    assert ours[0x80] == 0.0 and not np.signbit(ours[0x80])
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_encode_cuts_toward_zero(fmt):
+    """Below the format's NaN/inf band the code decodes to the representable
+    value of largest magnitude not above |x|, with x's sign: truncation onto
+    the grid that torch's cast defines (grid points, their fp32 neighbours,
+    subnormals and random magnitudes over 10 decades)."""
+    vals = _torch_fp8_values(fmt)
+    grid = np.unique(vals[np.isfinite(vals) & (vals >= 0)])
+    rng = np.random.default_rng(71)
+    g32 = grid.astype(np.float32)
+    x = np.concatenate([rng.standard_normal(100_000) * 10.0 ** rng.uniform(-6, 5, 100_000),
+                        g32, -g32, np.nextafter(g32, np.float32(np.inf)), np.nextafter(g32, np.float32(0)),
+                        -np.nextafter(g32, np.float32(np.inf))]).astype(np.float32)
+    x = x[np.abs(x) < FP8_FINITE_LIMIT[fmt]]
+    got = orc.fp8_decode(orc.fp8_encode(x, fmt), fmt)
+    want = np.sign(x) * grid[np.searchsorted(grid, np.abs(x).astype(np.float64), side="right") - 1]
+    assert np.array_equal(got, want)
+
+
+def test_fp8_encode_special_inputs():
+    """The page's explicit cases: NaN, infinities, zeros, overflow, the
+    band just below overflow that lands on the NaN/inf patterns, and fp32
+    denormals (a signed zero)."""
+    f = np.float32
+    e4 = lambda v: int(orc.fp8_encode(np.array([v], np.float32), "e4m3")[0])  # noqa: E731
+    e5 = lambda v: int(orc.fp8_encode(np.array([v], np.float32), "e5m2")[0])  # noqa: E731
+    assert e4(np.nan) == 0xFF and e5(np.nan) == 0xFF
+    assert e4(np.inf) == 0x7F and e4(-np.inf) == 0xFF
+    assert e5(np.inf) == 0x7C and e5(-np.inf) == 0xFC
+    assert e4(0.0) == 0 and e4(-0.0) == 0 and e5(-0.0) == 0
+    # overflow: E4M3 saturates to +/-448, E5M2 to +/-inf
+    assert e4(512.0) == 0x7E and e4(-1e30) == 0xFE and e4(448.0) == 0x7E and e4(479.9) == 0x7E
+    assert e5(131072.0) == 0x7C and e5(-3e38) == 0xFC
+    # the top exponent field: E4M3 [480, 512) -> the NaN pattern; E5M2
+    # [65536, 131072) -> inf and NaN patterns
+    assert e4(480.0) == 0x7F and e4(-500.0) == 0xFF
+    assert e5(65536.0) == 0x7C and e5(98304.0) == 0x7E
+    # below the smallest subnormal: a signed zero; fp32 denormals too
+    assert e4(f(2.0 ** -10)) == 0 and e4(-f(2.0 ** -10)) == 0x80
+    assert e5(f(2.0 ** -17)) == 0 and e5(-f(1e-45)) == 0x80
+    assert np.isnan(orc.fp8_decode(np.array([0x7F]), "e4m3")[0])
+
+
+def _page_value(v):
+    return 2.0 ** int(v[2:]) if isinstance(v, str) else float(v)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_page_roundtrips(golden, fmt):
+    g = golden["fp8_roundtrip"][fmt]
+    for v in map(_page_value, g["values"]):
+        d = float(orc.fp8_decode(orc.fp8_encode(np.array([v], np.float32), fmt), fmt)[0])
+        if v == 0.0:
+            assert d == 0.0
+        elif abs(v) < 1e-5:
+            assert abs(d) < 0.01
+        else:
+            assert abs(v - d) / abs(v) < g["max_rel_err"], (v, d)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_page_cache_basic(golden, fmt):
+    g = golden["fp8_cache_basic"]
+    n = g["num_kv_heads"] * g["head_dim"]
+    i = np.arange(n, dtype=np.float32)
+    for x in (i * np.float32(0.01) - np.float32(1.0), i * np.float32(0.02) - np.float32(0.5)):
+        head0 = x[:g["head_dim"]]
+        d = orc.fp8_decode(orc.fp8_encode(head0, fmt), fmt)
+        a = head0.astype(np.float64)
+        err = np.where(np.abs(a) > 1e-6, np.abs(a - d) / np.maximum(np.abs(a), 1e-30), np.abs(a - d))
+        assert np.all(err < g["max_rel_err"])
+
+
+def test_fp8_memory_savings(golden):
+    g = golden["fp8_memory_savings"]
+    f32 = orc.fp32_equivalent_bytes(g["num_kv_heads"], g["max_seq_len"], g["head_dim"], layers=g["num_layers"])
+    fp8 = orc.codes_bytes(g["num_kv_heads"], g["max_seq_len"], g["head_dim"], layers=g["num_layers"])
+    assert fp8 < f32 // 2 + f32 // 4
+    assert fp8 * 4 == f32
