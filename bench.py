@@ -13,6 +13,10 @@ after 8192 cached ones (batch 4, 32/8 heads, head_dim 128) and run causal
 chunked-prefill attention for the 512 queries (kvq_attention_chunk); the
 figure is TFLOP/s over the visible keys only.
 
+The other workloads (recent_window, sliding_decode, sliding_chunk,
+bf16_scales, fp8_e4m3, q8_group32, paged_decode) are the same steps on the
+cache variants their names give; ``--help`` lists them.
+
 Inputs are seeded synthetic data, already resident in HBM when timing starts.
 Prints one JSON line (see --help).  ``--gpus N`` with N > 1 is refused: this
 path is measured on one GPU.
@@ -68,7 +72,7 @@ def step_bytes(w: wl.Workload, L: int) -> dict:
     B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
     G = 1 if w.group == 0 else D // 32
     in_bytes = 4 if w.kv_dtype == "f32" else 2
-    sb = 2 if w.extra.get("scale_bf16") else 4   # bytes per scale
+    sb = 2 if w.extra.get("scale_bf16") else (0 if w.extra.get("fp8") else 4)   # bytes per scale (FP8: none)
     W = w.extra.get("window", 0)
     if W:
         # recent window: INT8 rows below L - W (the row leaving the window is
@@ -141,7 +145,7 @@ def build_layers(w: wl.Workload, kvq, torch, stream, threads: int):
                 x = done_layers.pop(li)
                 cache = kvq.Int8KVCache(w.batch, w.num_heads, w.num_kv_heads, w.head_dim, max_len=w.max_len,
                                         group32=(w.group == 32), recent_window=w.extra.get("window", 0),
-                                        scale_bf16=w.extra.get("scale_bf16", False))
+                                        scale_bf16=w.extra.get("scale_bf16", False), fp8=w.extra.get("fp8"))
                 k_raw, v_raw = x["k_raw"], x["v_raw"]
                 tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
 
@@ -227,11 +231,18 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     x = wl.layer_inputs(w, 0)
     nb = w.batch
 
-    def quant(a):  # per-token / group-32, or per-token with the scale kept as bf16
+    fp8 = w.extra.get("fp8")
+
+    def quant(a):  # per-token / group-32, per-token with the scale kept as bf16, or FP8 codes
+        if fp8:
+            return orc.fp8_encode(a, fp8), np.zeros(a.shape[:-1] + (1,), np.float32)
         if w.extra.get("scale_bf16"):
             c, sb = orc.quantize_bf16_scale(a)
             return c, orc.bf16_bits_to_f32(sb)
         return orc.quantize(a, w.group)
+
+    def deq(c, s):
+        return orc.fp8_decode(c, fp8) if fp8 else orc.dequantize_exact(c, s)
 
     caches = []
     for b in range(nb):
@@ -247,8 +258,7 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
         kscat = np.concatenate([ks, nks], axis=2)
         vcat = np.concatenate([vc, nv], axis=2)
         vscat = np.concatenate([vs, nvs], axis=2)
-        return orc.attention_decode(x["q"][b:b + 1], orc.dequantize_exact(kcat, kscat),
-                                    orc.dequantize_exact(vcat, vscat), [T], w.attn_scale)
+        return orc.attention_decode(x["q"][b:b + 1], deq(kcat, kscat), deq(vcat, vscat), [T], w.attn_scale)
 
     per_seq_bytes = step_bytes(w, T)["step"] / w.batch
     done = 0
@@ -659,7 +669,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
-                                                            "bf16_scales"])
+                                                            "bf16_scales", "fp8_e4m3"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -777,8 +787,12 @@ def main():
         cpu = cpu_baseline_recent(w) if w.extra.get("window") else cpu_baseline(w)
         cpu.pop("seconds", None)
 
+    fp8 = w.extra.get("fp8")
+    codes_what = (f"FP8 {fp8.upper()} codes (no scales)" if fp8 else
+                  f"{'per-token' if w.group == 0 else 'group-32'} "
+                  f"{'bf16' if w.extra.get('scale_bf16') else 'fp32'} scales")
     result = {
-        "metric": "INT8-KV decode attention: us/layer-step and achieved HBM TB/s (% of peak)",
+        "metric": ("FP8" if fp8 else "INT8") + "-KV decode attention: us/layer-step and achieved HBM TB/s (% of peak)",
         "value": round(tbps, 4),
         "unit": "TB/s",
         "n_gpus": 1,
@@ -790,12 +804,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u8",
+        "dtype": f"fp8{fp8}" if fp8 else "u8",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {w.batch}, {w.num_heads} q / {w.num_kv_heads} kv heads, "
-                               f"head_dim {w.head_dim}, context {T}, "
-                               f"{'per-token' if w.group == 0 else 'group-32'} "
-                               f"{'bf16' if w.extra.get('scale_bf16') else 'fp32'} scales, {w.layers} layers, "
+                               f"head_dim {w.head_dim}, context {T}, {codes_what}, {w.layers} layers, "
                                + (f"last {w.extra['window']} tokens bf16 (recent window), " if w.extra.get("window")
                                   else "") +
                                f"append 1 token + decode per layer "

@@ -65,8 +65,28 @@ typedef enum {
  * that mode k_scales / v_scales point to uint16 bf16 arrays of the same
  * shape (4-byte aligned, as every scale array must be: kernels read the
  * aligned word holding a scale).  Chunked attention supports the two
- * per-token modes. */
-enum { KVQ_SCALE_PER_TOKEN = 0, KVQ_SCALE_GROUP32 = 1, KVQ_SCALE_PER_TOKEN_BF16 = 2 };
+ * per-token modes.
+ *
+ * FP8 code formats (llama-gguf 0.14.0 src/model/kv_quantized.rs,
+ * `KVCacheFormat::Fp8E4M3` / `Fp8E5M2`), set in the same field: each element
+ * is stored as one FP8 byte of its own value, with no scale (k_scales /
+ * v_scales are unused and may be NULL).  The encoder is the page's
+ * `quantize_fp8_e4m3` / `quantize_fp8_e5m2`: the value is cut toward zero
+ * onto the format's grid; E4M3 inputs of magnitude 512 and above saturate to
+ * +/-448 and E5M2 inputs of 131072 and above to +/-inf; below that, the top
+ * exponent field is kept, so E4M3 magnitudes in [480, 512) take the NaN code
+ * and E5M2 magnitudes in [65536, 131072) the inf and NaN codes, as on the
+ * page.  Readers decode as the page's `dequantize_fp8_*` (the OCP values;
+ * negative zero reads as +0).  Attention over a non-finite code is
+ * non-finite.  Decode attention and dequantization support both formats;
+ * chunked attention returns KVQ_ERR_UNSUPPORTED for them. */
+enum {
+  KVQ_SCALE_PER_TOKEN = 0,
+  KVQ_SCALE_GROUP32 = 1,
+  KVQ_SCALE_PER_TOKEN_BF16 = 2,
+  KVQ_CODES_FP8_E4M3 = 3,
+  KVQ_CODES_FP8_E5M2 = 4
+};
 enum { KVQ_LAYOUT_CONTIGUOUS = 0, KVQ_LAYOUT_PAGED = 1 };
 enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 };
 
@@ -78,7 +98,7 @@ typedef struct kvq_cache {
   int32_t num_kv_heads;        /* KV heads KVH, H % KVH == 0                      */
   int32_t head_dim;            /* D: multiple of 32, at most 256                  */
   int32_t layout;              /* KVQ_LAYOUT_*                                    */
-  int32_t scale_mode;          /* KVQ_SCALE_*                                     */
+  int32_t scale_mode;          /* KVQ_SCALE_* (INT8 codes) or KVQ_CODES_FP8_*     */
   int32_t max_len;             /* contiguous: per-sequence capacity (tokens)      */
   int32_t page_size;           /* paged: must be 16                               */
   int32_t num_pages;           /* paged: arena pages P                            */
@@ -86,7 +106,8 @@ typedef struct kvq_cache {
   const int32_t* block_table;  /* paged: device [batch, max_blocks_per_seq]       */
   uint8_t* k_codes;            /* device, layout above                            */
   uint8_t* v_codes;
-  float* k_scales;             /* fp32 (bf16 in KVQ_SCALE_PER_TOKEN_BF16)          */
+  float* k_scales;             /* fp32 (bf16 in KVQ_SCALE_PER_TOKEN_BF16; unused
+                                  for FP8 codes)                                  */
   float* v_scales;
 } kvq_cache;
 

@@ -17,12 +17,15 @@ class Int8KVCache:
     Contiguous: codes ``[B, KVH, max_len, D]``, scales ``[B, KVH, max_len, G]``.
     Paged: arena codes ``[P, KVH, 16, D]``, scales ``[P, KVH, 16, G]``, with a
     caller-provided int32 ``block_table [B, max_blocks_per_seq]``.
+    ``fp8="e4m3"`` or ``"e5m2"`` stores FP8 codes instead, with no scales
+    (``k_scales`` / ``v_scales`` are then None).
     """
 
     def __init__(self, batch: int, num_heads: int, num_kv_heads: int, head_dim: int, *,
                  max_len: int = 0, group32: bool = False, num_pages: int = 0,
                  block_table: torch.Tensor | None = None, device="cuda", fill: int | None = None,
-                 recent_window: int = 0, recent_capacity: int | None = None, scale_bf16: bool = False):
+                 recent_window: int = 0, recent_capacity: int | None = None, scale_bf16: bool = False,
+                 fp8: str | None = None):
         self.batch, self.num_heads, self.num_kv_heads, self.head_dim = batch, num_heads, num_kv_heads, head_dim
         self.groups = head_dim // 32 if group32 else 1
         self.paged = block_table is not None
@@ -46,15 +49,25 @@ class Int8KVCache:
             self.v_codes = torch.full(shape_c, fill, dtype=torch.uint8, device=device)
         if scale_bf16 and group32:
             raise ValueError("bf16-stored scales are per-token only")
-        sdt = torch.bfloat16 if scale_bf16 else torch.float32
-        self.k_scales = torch.zeros(shape_s, dtype=sdt, device=device)
-        self.v_scales = torch.zeros(shape_s, dtype=sdt, device=device)
+        if fp8 not in (None, "e4m3", "e5m2"):
+            raise ValueError("fp8 must be None, 'e4m3' or 'e5m2'")
+        if fp8 and (scale_bf16 or group32):
+            raise ValueError("FP8 codes carry no scales")
+        self.fp8 = fp8
+        if fp8:
+            self.k_scales = self.v_scales = None
+            mode = _k.KVQ_CODES_FP8_E4M3 if fp8 == "e4m3" else _k.KVQ_CODES_FP8_E5M2
+        else:
+            sdt = torch.bfloat16 if scale_bf16 else torch.float32
+            self.k_scales = torch.zeros(shape_s, dtype=sdt, device=device)
+            self.v_scales = torch.zeros(shape_s, dtype=sdt, device=device)
+            mode = (_k.KVQ_SCALE_GROUP32 if group32 else
+                    _k.KVQ_SCALE_PER_TOKEN_BF16 if scale_bf16 else _k.KVQ_SCALE_PER_TOKEN)
         self.desc = _k.make_cache(
             batch, num_heads, num_kv_heads, head_dim, self.k_codes, self.v_codes, self.k_scales,
             self.v_scales,
             layout=_k.KVQ_LAYOUT_PAGED if self.paged else _k.KVQ_LAYOUT_CONTIGUOUS,
-            scale_mode=(_k.KVQ_SCALE_GROUP32 if group32 else
-                        _k.KVQ_SCALE_PER_TOKEN_BF16 if scale_bf16 else _k.KVQ_SCALE_PER_TOKEN),
+            scale_mode=mode,
             max_len=0 if self.paged else max_len, num_pages=num_pages,
             max_blocks_per_seq=self.max_blocks, block_table=self.block_table)
         # recent-window hybrid: the last W positions of each sequence stay bf16

@@ -36,8 +36,7 @@ kvq_status check_cache(const kvq_cache* c, const char* who) {
     return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be a multiple of 32", who, c->head_dim);
   if (c->head_dim > 256)
     return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be at most 256", who, c->head_dim);
-  if (c->scale_mode != KVQ_SCALE_PER_TOKEN && c->scale_mode != KVQ_SCALE_GROUP32 &&
-      c->scale_mode != KVQ_SCALE_PER_TOKEN_BF16)
+  if (c->scale_mode < KVQ_SCALE_PER_TOKEN || c->scale_mode > KVQ_CODES_FP8_E5M2)
     return fail(KVQ_ERR_INVALID_ARG, "%s: unknown scale_mode %d", who, c->scale_mode);
   if (c->layout == KVQ_LAYOUT_CONTIGUOUS) {
     if (c->max_len <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: contiguous cache needs max_len > 0", who);
@@ -52,10 +51,13 @@ kvq_status check_cache(const kvq_cache* c, const char* who) {
   } else {
     return fail(KVQ_ERR_INVALID_ARG, "%s: unknown layout %d", who, c->layout);
   }
-  if (!c->k_codes || !c->v_codes || !c->k_scales || !c->v_scales)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: cache code and scale pointers must be non-NULL", who);
-  if (((reinterpret_cast<uintptr_t>(c->k_scales) | reinterpret_cast<uintptr_t>(c->v_scales)) & 3) != 0)
-    return fail(KVQ_ERR_INVALID_ARG, "%s: scale arrays must be 4-byte aligned", who);
+  if (!c->k_codes || !c->v_codes) return fail(KVQ_ERR_INVALID_ARG, "%s: cache code pointers must be non-NULL", who);
+  if (!is_fp8(*c)) {  // FP8 codes carry no scales
+    if (!c->k_scales || !c->v_scales)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: cache scale pointers must be non-NULL", who);
+    if (((reinterpret_cast<uintptr_t>(c->k_scales) | reinterpret_cast<uintptr_t>(c->v_scales)) & 3) != 0)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: scale arrays must be 4-byte aligned", who);
+  }
   return KVQ_OK;
 }
 
@@ -99,6 +101,7 @@ kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who
   if (static_cast<int64_t>(r->capacity) * c.head_dim > 0x7fffffffLL)
     return fail(KVQ_ERR_INVALID_ARG, "%s: ring capacity too large", who);
   if (!r->k || !r->v) return fail(KVQ_ERR_INVALID_ARG, "%s: ring pointers must be non-NULL", who);
+  if (is_fp8(c)) return fail(KVQ_ERR_UNSUPPORTED, "%s: a recent window over FP8 codes is not supported", who);
   return KVQ_OK;
 }
 

@@ -34,6 +34,7 @@ struct AppendParams {
   int32_t mode;                        // AppendMode
   int32_t rwin, rcap;                  // recent window and ring slots
   int32_t scale_bf16;                  // per-token scales stored as bf16
+  int32_t fp8;                         // FP8 codes: 1 E4M3, 2 E5M2 (no scales); 0 INT8
 };
 
 // Stores this lane's EPL values of a row as bf16 (nearest even).
@@ -94,10 +95,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int64_t dst = cache_row(p.geom, b, h, pos);
   if (dst < 0) return;  // outside the cache: not written
 
-  float s;
-  const uint32_t packed = quantize_lane<EPL, GROUP32>(x, s);
+  float s = 0.0f;
+  uint32_t packed;
+  if (p.fp8 == 2) packed = fp8_encode_lane<EPL, true>(x);
+  else if (p.fp8 == 1) packed = fp8_encode_lane<EPL, false>(x);
+  else packed = quantize_lane<EPL, GROUP32>(x, s);  // (p.fp8 is uniform: every lane joins the reduction)
   if (on) {
     store_lane_codes<EPL>(p.codes[side] + dst * D, lane, packed);
+    if (p.fp8) return;
     constexpr int kGroupLanes = 32 / EPL;
     float* sc = p.scales[side] + dst * p.groups;
     if (GROUP32) {
@@ -119,6 +124,7 @@ struct DequantParams {
   const uint16_t* ring;      // recent window: bf16 [B, KVH, rcap, D]
   int32_t rwin, rcap;        // window (0: none) and ring slots
   int32_t scale_bf16;        // per-token scales stored as bf16
+  int32_t fp8;               // FP8 codes: 1 E4M3, 2 E5M2 (no scales); 0 INT8
   const int32_t* seq_lens;
   void* out;
   CacheGeom geom;
@@ -149,6 +155,12 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
     v[1] = __uint_as_float(r.x & 0xffff0000u);
     v[2] = __uint_as_float(r.y << 16);
     v[3] = __uint_as_float(r.y & 0xffff0000u);
+  } else if (row >= 0 && p.fp8) {
+    // FP8: the page's decoder (llama-gguf kv_quantized.rs `dequantize_fp8_*`)
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = p.fp8 == 2 ? fp8_decode<true>((c >> (8 * e)) & 0xffu) : fp8_decode<false>((c >> (8 * e)) & 0xffu);
   } else if (row >= 0) {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
     const float s = load_scale(p.scales, row * p.groups + (p.groups == 1 ? 0 : d / 32), p.scale_bf16 != 0);
@@ -190,6 +202,7 @@ kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_ne
   p.rcap = rc.cap;
   p.n_new = n_new;
   p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
+  p.fp8 = fp8_kind(c);
   p.src[0] = k_new;
   p.src[1] = v_new;
   p.codes[0] = c.k_codes;
@@ -231,6 +244,7 @@ kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens
   p.rwin = rc.window;
   p.rcap = rc.cap;
   p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
+  p.fp8 = fp8_kind(c);
   p.codes = which ? c.v_codes : c.k_codes;
   p.scales = which ? c.v_scales : c.k_scales;
   p.seq_lens = seq_lens;

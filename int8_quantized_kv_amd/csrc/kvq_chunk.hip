@@ -563,6 +563,7 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
                         float attn_scale, uint16_t* out, void*, int, hipStream_t stream, int window) {
   if (c.scale_mode == KVQ_SCALE_GROUP32)
     return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: group-32 scales are not supported");
+  if (is_fp8(c)) return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: FP8 codes are not supported");
   ChunkParams p;
   p.q = q;
   p.out = out;

@@ -24,8 +24,18 @@ inline CacheGeom geom_of(const kvq_cache& c) {
   return g;
 }
 
+inline bool is_fp8(const kvq_cache& c) {
+  return c.scale_mode == KVQ_CODES_FP8_E4M3 || c.scale_mode == KVQ_CODES_FP8_E5M2;
+}
+
+// 0 for INT8 codes, 1 for FP8 E4M3, 2 for FP8 E5M2.
+inline int fp8_kind(const kvq_cache& c) {
+  return c.scale_mode == KVQ_CODES_FP8_E4M3 ? 1 : (c.scale_mode == KVQ_CODES_FP8_E5M2 ? 2 : 0);
+}
+
+// Scales per row: 1 per token, head_dim / 32 for group-32, none for FP8 codes.
 inline int scales_per_row(const kvq_cache& c) {
-  return c.scale_mode == KVQ_SCALE_GROUP32 ? c.head_dim / 32 : 1;
+  return c.scale_mode == KVQ_SCALE_GROUP32 ? c.head_dim / 32 : (is_fp8(c) ? 0 : 1);
 }
 
 inline int scale_bytes(const kvq_cache& c) { return c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 2 : 4; }

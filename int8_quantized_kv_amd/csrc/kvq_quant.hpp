@@ -98,3 +98,67 @@ __device__ __forceinline__ void store_lane_codes(uint8_t* codes, int lane, uint3
 }
 
 }  // namespace kvq
+
+namespace kvq {
+
+// ---------------------------------------------------------------------------
+// FP8 codes (llama-gguf 0.14.0 src/model/kv_quantized.rs, `quantize_fp8_e4m3`
+// / `quantize_fp8_e5m2`, `dequantize_fp8_*`): one byte per element, no scale.
+// E4M3: 3 mantissa bits, bias 7; E5M2: 2 mantissa bits, bias 15.
+// ---------------------------------------------------------------------------
+
+// The page's encoder: NaN -> 0xFF, +/-inf -> the infinity code, +/-0 -> 0;
+// otherwise the fp32 exponent is rebased, an exponent above the largest
+// field gives the overflow code (E4M3 +/-448, E5M2 +/-inf), a normal result
+// keeps the top mantissa bits, a subnormal one the top bits of the full
+// significand, and anything smaller a signed zero: the value is cut toward
+// zero, never rounded.
+template <bool E5M2>
+__device__ __forceinline__ uint32_t fp8_encode(float x) {
+  constexpr int M = E5M2 ? 2 : 3;
+  constexpr int kBias = E5M2 ? 15 : 7;
+  constexpr int kEmax = E5M2 ? 31 : 15;
+  constexpr uint32_t kMask = (1u << M) - 1;
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t s7 = (u >> 24) & 0x80u;
+  const int raw = static_cast<int>((u >> 23) & 0xFFu);
+  const uint32_t sig = (u & 0x7FFFFFu) | (raw != 0 ? 0x800000u : 0u);
+  const int E = raw - 127 + kBias;
+  if (x != x) return 0xFFu;
+  if (raw == 0xFF) return s7 | (E5M2 ? 0x7Cu : 0x7Fu);
+  if ((u & 0x7FFFFFFFu) == 0) return 0u;
+  if (E > kEmax) return s7 | (E5M2 ? 0x7Cu : 0x7Eu);
+  if (E >= 1) return s7 | (static_cast<uint32_t>(E) << M) | ((sig >> (23 - M)) & kMask);
+  if (E > -M) return s7 | ((sig >> (24 - M - E)) & (kMask >> (-E)));
+  return s7;
+}
+
+// The page's decoder, exact in fp32: a zero magnitude is +0 (either sign),
+// E4M3 S.1111.111 is NaN, E5M2 S.11111.00 is +/-inf and above it NaN; a
+// nonzero exponent field F gives 2^(F - bias) (1 + f / 2^M), F = 0 the
+// subnormal f 2^(1 - bias - M).
+template <bool E5M2>
+__device__ __forceinline__ float fp8_decode(uint32_t c) {
+  constexpr int M = E5M2 ? 2 : 3;
+  constexpr int kBias = E5M2 ? 15 : 7;
+  const uint32_t low = c & 0x7Fu;
+  const uint32_t sign = (c & 0x80u) << 24;
+  if (low == 0) return 0.0f;
+  if (!E5M2 && low == 0x7Fu) return __uint_as_float(0x7FC00000u);
+  if (E5M2 && low == 0x7Cu) return __uint_as_float(sign | 0x7F800000u);
+  if (E5M2 && low > 0x7Cu) return __uint_as_float(0x7FC00000u);
+  const uint32_t F = low >> M, f = low & ((1u << M) - 1);
+  if (F > 0) return __uint_as_float(sign | ((F + 127u - kBias) << 23) | (f << (23 - M)));
+  return __uint_as_float(sign | __float_as_uint(static_cast<float>(f) * (E5M2 ? 0x1p-16f : 0x1p-9f)));
+}
+
+// FP8 codes of this lane's EPL values, packed little-endian.
+template <int EPL, bool E5M2>
+__device__ __forceinline__ uint32_t fp8_encode_lane(const float (&x)[EPL]) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) packed |= fp8_encode<E5M2>(x[e]) << (8 * e);
+  return packed;
+}
+
+}  // namespace kvq

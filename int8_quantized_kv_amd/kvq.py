@@ -24,6 +24,8 @@ KVQ_ERR_WORKSPACE = 5
 KVQ_SCALE_PER_TOKEN = 0
 KVQ_SCALE_GROUP32 = 1
 KVQ_SCALE_PER_TOKEN_BF16 = 2
+KVQ_CODES_FP8_E4M3 = 3
+KVQ_CODES_FP8_E5M2 = 4
 KVQ_LAYOUT_CONTIGUOUS = 0
 KVQ_LAYOUT_PAGED = 1
 KVQ_DT_F32 = 0

@@ -100,8 +100,13 @@ SLIDING_CHUNK = Workload("sliding_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16"
 BF16_SCALES = Workload("bf16_scales", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
                        layers=32, outliers=4, seed=8, extra={"scale_bf16": True})
 
+# The 8B-shaped decode step on FP8 E4M3 codes with no scales (llama-gguf
+# kv_quantized.rs `KVCacheFormat::Fp8E4M3`).
+FP8_E4M3 = Workload("fp8_e4m3", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
+                    layers=32, outliers=4, seed=9, extra={"fp8": "e4m3"})
+
 ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
-                           BF16_SCALES)}
+                           BF16_SCALES, FP8_E4M3)}
 
 
 # ----------------------------------------------------------------------------
