@@ -78,8 +78,9 @@ typedef enum {
  * and E5M2 magnitudes in [65536, 131072) the inf and NaN codes, as on the
  * page.  Readers decode as the page's `dequantize_fp8_*` (the OCP values;
  * negative zero reads as +0).  Attention over a non-finite code is
- * non-finite.  Decode attention and dequantization support both formats;
- * chunked attention returns KVQ_ERR_UNSUPPORTED for them. */
+ * non-finite.  Decode attention, chunked attention and dequantization
+ * support both formats; a recent window over FP8 codes returns
+ * KVQ_ERR_UNSUPPORTED. */
 enum {
   KVQ_SCALE_PER_TOKEN = 0,
   KVQ_SCALE_GROUP32 = 1,
@@ -123,7 +124,9 @@ typedef struct kvq_cache {
  * kv_cache_q8_init.rs).  The slot write is a fixed-capacity store: contiguous
  * row (b, h, p) sits at ((b*KVH + h)*max_len + p); paged position p of
  * sequence b sits in page block_table[b][p/16], slot p%16 (combs-models kv.rs
- * `PagedKVCache::attention_opts` write loop).
+ * `PagedKVCache::attention_opts` write loop).  FP8 code formats store
+ * each element's own byte from the page's encoder instead (see the scale
+ * modes above) and write no scales.
  *
  *   k_new, v_new : device [B, KVH, n_new, D], fp32 or bf16 (in_dtype)
  *   start_pos    : device int32 [B]
@@ -141,7 +144,8 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k_new, const void* v_n
  * decode query at the end of the window needs no mask: combs-models kv.rs
  * `attend`).  out[b,h,:] = softmax_t(attn_scale * q.k_hat_t) . v_hat_t with
  * k_hat = (code - 128) * scale dequantized in registers (abaddon
- * kv_cache_quant_cuda.rs module doc, fused approach).  Computed as split-K
+ * kv_cache_quant_cuda.rs module doc, fused approach), or the decoded value
+ * of an FP8 code.  Computed as split-K
  * partials (m, l, o) per token range, merged with a log-sum-exp combine; the
  * result is rounded to bf16 (nearest even).
  *
@@ -212,7 +216,8 @@ kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_
  * kvq_dequant — materialise one cache side as values: out[b,h,t,d] =
  * fl32((code - 128) * scale) (abaddon kv_cache_quant_cuda.rs
  * `int8_dequant_bf16`; abaddon 0.2.0-rc.2 kv_cache_quant.rs `dequantize`),
- * optionally rounded to bf16 (nearest even).  Positions t >= seq_lens[b]
+ * or an FP8 code's value as the page's decoder gives it (NaN codes as the
+ * quiet NaN 0x7FC00000), optionally rounded to bf16 (nearest even).  Positions t >= seq_lens[b]
  * (clamped to capacity) are written as 0.
  *
  *   which   : 0 = K, 1 = V

@@ -38,6 +38,7 @@
 //   * the running maximum per query is lazy: accumulators are rescaled only
 //     when a score exceeds it by more than 2^8, so weights stay below 2^8.
 #include "kvq_internal.hpp"
+#include "kvq_quant.hpp"
 
 #include <type_traits>
 
@@ -116,6 +117,17 @@ __device__ __forceinline__ uint2 codes_exact_f16(uint32_t w) {
   return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
+// Eight FP8 codes -> their eight f16 values (exact).
+template <bool E5M2>
+__device__ __forceinline__ f16x8 fp8_codes_f16(uint32_t lo, uint32_t hi) {
+  uint4 w;
+  w.x = fp8_pair_k<E5M2, false>(lo);
+  w.y = fp8_pair_k<E5M2, true>(lo);
+  w.z = fp8_pair_k<E5M2, false>(hi);
+  w.w = fp8_pair_k<E5M2, true>(hi);
+  return __builtin_bit_cast(f16x8, w);
+}
+
 // Eight codes -> eight f16 values c * 2^-24 (subnormal, exact).
 __device__ __forceinline__ f16x8 codes_tiny_f16(uint32_t lo, uint32_t hi) {
   uint4 w;
@@ -163,10 +175,14 @@ __device__ __forceinline__ int64_t row_of(const ChunkParams& p, int b, int g, in
   }
 }
 
-// SBF: per-token scales stored as bf16 (a template argument so that the fp32
-// mode keeps its registers)
-template <int D, bool PAGED, bool SBF>
+// SM: KVQ_SCALE_PER_TOKEN, KVQ_SCALE_PER_TOKEN_BF16 (scales stored as bf16)
+// or an FP8 code format (values, no scales); a template argument so that each
+// mode keeps its registers
+template <int D, bool PAGED, int SM>
 __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
+  constexpr bool SBF = SM == KVQ_SCALE_PER_TOKEN_BF16;
+  constexpr bool FP8 = SM == KVQ_CODES_FP8_E4M3 || SM == KVQ_CODES_FP8_E5M2;
+  constexpr bool E5 = SM == KVQ_CODES_FP8_E5M2;
   using TL = Tile<D, kCkTile>;
   constexpr int kTT = kCkTile / 32;                        // 32-token S tiles per tile
   constexpr int kChunksPerRow = D / 16;                    // 16-code pieces per row
@@ -269,7 +285,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
         lreg[i] = *reinterpret_cast<const uint4*>((kside ? p.k_codes : p.v_codes) + row * D + 16 * (id % kChunksPerRow));
       }
     }
-    if (ld_s) {
+    if (ld_s && !FP8) {
       const int t = t0 + (tid & (kCkTile - 1));
       if (t < Ltot) {
         const int64_t row = row_of<PAGED>(p, b, g, t);
@@ -283,8 +299,18 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       const int j = tid + i * kCkThreads;
       if (j < kChunks) {  // K: 16 codes -> 16 exact f16 values = units 2c and 2c + 1
         const int r = j / kChunksPerRow, c = j % kChunksPerRow;
-        const uint2 k0 = codes_exact_f16(lreg[i].x), k1 = codes_exact_f16(lreg[i].y);
-        const uint2 k2 = codes_exact_f16(lreg[i].z), k3 = codes_exact_f16(lreg[i].w);
+        uint2 k0, k1, k2, k3;
+        if constexpr (FP8) {  // the codes' own values
+          k0 = make_uint2(fp8_pair_k<E5, false>(lreg[i].x), fp8_pair_k<E5, true>(lreg[i].x));
+          k1 = make_uint2(fp8_pair_k<E5, false>(lreg[i].y), fp8_pair_k<E5, true>(lreg[i].y));
+          k2 = make_uint2(fp8_pair_k<E5, false>(lreg[i].z), fp8_pair_k<E5, true>(lreg[i].z));
+          k3 = make_uint2(fp8_pair_k<E5, false>(lreg[i].w), fp8_pair_k<E5, true>(lreg[i].w));
+        } else {
+          k0 = codes_exact_f16(lreg[i].x);
+          k1 = codes_exact_f16(lreg[i].y);
+          k2 = codes_exact_f16(lreg[i].z);
+          k3 = codes_exact_f16(lreg[i].w);
+        }
         *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
         *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c + 1)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
       } else if (j < 2 * kChunks) {  // V: codes, 8-byte units 2c and 2c + 1 (halves swap with the low unit bit)
@@ -303,7 +329,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       // (page rows start even, so in the paged layout the token's parity)
       const int64_t srow = PAGED ? static_cast<int64_t>(t0 + tl)
                                  : (static_cast<int64_t>(b) * p.geom.kvh + g) * p.geom.max_len + t0 + tl;
-      const float sv = scale_value(sreg, scale_sel(srow, SBF));
+      const float sv = FP8 ? 1.0f : scale_value(sreg, scale_sel(srow, SBF));
       if (tid < kCkTile) {
         reinterpret_cast<float*>(buf + TL::kKc)[tl] = ok ? sv * kfac : 0.0f;
       } else {
@@ -313,8 +339,16 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     }
   };
 
+  if constexpr (FP8) {
+    // the first MFMA step takes the last buffer's values times all-zero
+    // weights before anything is staged there; FP8 bytes left in LDS could be
+    // NaN or inf codes, and 0 * NaN is NaN, so those values start as zeros
+    uint8_t* bz = smem + (kCkBufs - 1) * TL::kBytes + TL::kKBytes;
+    for (int i = tid * 16; i < TL::kVBytes; i += kCkThreads * 16)
+      *reinterpret_cast<uint4*>(bz + i) = make_uint4(0u, 0u, 0u, 0u);
+  }
   load_tile(tbase);
-  __syncthreads();  // sm_qmax
+  __syncthreads();  // sm_qmax (and the cleared values)
 
   int kq = 0;
   {
@@ -397,8 +431,9 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
           for (int dt = 0; dt < kDT; ++dt) {
             const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (v2i __attribute__((address_space(3)))*)(bv + TL::v_off(tok, 4 * dt + vunit)));
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                codes_tiny_f16(static_cast<uint32_t>(c8.x), static_cast<uint32_t>(c8.y)), pw[tt][ks], oacc[dt], 0, 0, 0);
+            const uint32_t lo = static_cast<uint32_t>(c8.x), hi = static_cast<uint32_t>(c8.y);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(FP8 ? fp8_codes_f16<E5>(lo, hi) : codes_tiny_f16(lo, hi),
+                                                             pw[tt][ks], oacc[dt], 0, 0, 0);
           }
         }
       }
@@ -525,8 +560,10 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   const float l_tot = other_half_sum(l_run);
   const float w_tot = other_half_sum(w_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const float big = 16777216.0f;  // 2^24: the V operands carry c * 2^-24
-  const float off = 128.0f * w_tot;
+  // INT8: the V operands carry c 2^-24, so the sum is 2^24 acc - 128 sum w;
+  // FP8 operands are the values themselves
+  const float big = FP8 ? 1.0f : 16777216.0f;
+  const float off = FP8 ? 0.0f : 128.0f * w_tot;
   uint16_t* orow = p.out + ((static_cast<int64_t>(b) * p.heads + head) * p.n + qi) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
@@ -542,14 +579,19 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   }
 }
 
+template <int D, int SM>
+void launch_chunk_sm(bool paged, dim3 grid, hipStream_t stream, const ChunkParams& p) {
+  if (paged) hipLaunchKernelGGL((chunk_kernel<D, true, SM>), grid, dim3(kCkThreads), 0, stream, p);
+  else hipLaunchKernelGGL((chunk_kernel<D, false, SM>), grid, dim3(kCkThreads), 0, stream, p);
+}
+
 template <int D>
-void launch_chunk_d(bool paged, bool sbf, dim3 grid, hipStream_t stream, const ChunkParams& p) {
-  if (paged) {
-    if (sbf) hipLaunchKernelGGL((chunk_kernel<D, true, true>), grid, dim3(kCkThreads), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<D, true, false>), grid, dim3(kCkThreads), 0, stream, p);
-  } else {
-    if (sbf) hipLaunchKernelGGL((chunk_kernel<D, false, true>), grid, dim3(kCkThreads), 0, stream, p);
-    else hipLaunchKernelGGL((chunk_kernel<D, false, false>), grid, dim3(kCkThreads), 0, stream, p);
+void launch_chunk_d(bool paged, int sm, dim3 grid, hipStream_t stream, const ChunkParams& p) {
+  switch (sm) {
+    case KVQ_SCALE_PER_TOKEN_BF16: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN_BF16>(paged, grid, stream, p); break;
+    case KVQ_CODES_FP8_E4M3: launch_chunk_sm<D, KVQ_CODES_FP8_E4M3>(paged, grid, stream, p); break;
+    case KVQ_CODES_FP8_E5M2: launch_chunk_sm<D, KVQ_CODES_FP8_E5M2>(paged, grid, stream, p); break;
+    default: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN>(paged, grid, stream, p); break;
   }
 }
 
@@ -563,7 +605,6 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
                         float attn_scale, uint16_t* out, void*, int, hipStream_t stream, int window) {
   if (c.scale_mode == KVQ_SCALE_GROUP32)
     return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: group-32 scales are not supported");
-  if (is_fp8(c)) return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: FP8 codes are not supported");
   ChunkParams p;
   p.q = q;
   p.out = out;
@@ -588,9 +629,8 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.total_wgs = static_cast<int32_t>(total);
   const dim3 grid(static_cast<unsigned>(total));
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  const bool sbf = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16;
-  if (c.head_dim == 128) launch_chunk_d<128>(paged, sbf, grid, stream, p);
-  else launch_chunk_d<64>(paged, sbf, grid, stream, p);
+  if (c.head_dim == 128) launch_chunk_d<128>(paged, c.scale_mode, grid, stream, p);
+  else launch_chunk_d<64>(paged, c.scale_mode, grid, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;

@@ -119,31 +119,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
-// FP8 code pairs as f16 pairs (every E4M3 and E5M2 value, infinities and
-// NaN included, is an f16 value).  E5M2 is the upper byte of an f16; E4M3
-// goes through gfx950's conversion (scale 1), which decodes every byte as
-// the OCP format does.  fp8_pair_k: bytes (0, 1) or (2, 3) of w.
-template <bool E5M2, bool HIGH>
-__device__ __forceinline__ uint32_t fp8_pair_k(uint32_t w) {
-  if constexpr (E5M2) {
-    return __builtin_amdgcn_perm(0u, w, HIGH ? 0x030C020Cu : 0x010C000Cu);
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
-  }
-}
-
-// Byte e of a and byte e of b (two tokens' codes of one dim) as an f16 pair.
-template <bool E5M2>
-__device__ __forceinline__ uint32_t fp8_pair_v(uint32_t a, uint32_t b, int e) {
-  if constexpr (E5M2) {
-    return __builtin_amdgcn_perm(b, a, 0x040C000Cu + 0x01000100u * e);
-  } else {
-    return __builtin_bit_cast(
-        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__builtin_amdgcn_perm(b, a, 0x0C0C0400u + 0x0101u * e),
-                                                           1.0f, false));
-  }
-}
-
 // f16 pair (1024 + c0, 1024 + c1) -> (c0 - 128, c1 - 128), exact.
 __device__ __forceinline__ uint32_t exact_pair(uint32_t w) {
   const half2_t off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};

@@ -257,15 +257,12 @@ def test_bf16_scale_mode_sizing():
 def test_fp8_descriptors_need_no_scales():
     """FP8 codes (llama-gguf kv_quantized.rs): scale pointers may be NULL and
     the cache holds the code bytes alone (the page's memory_usage counts
-    scales for Int8 only); chunked attention and a recent window are
-    reported as unsupported before anything is launched."""
+    scales for Int8 only); a recent window is reported as unsupported
+    before anything is launched."""
     for mode in (kvq.KVQ_CODES_FP8_E4M3, kvq.KVQ_CODES_FP8_E5M2):
         d = _desc(scale_mode=mode, max_len=4096, ptrs=(FAKE, FAKE, 0, 0))
         assert kvq.kvq_cache_bytes(d) == 2 * 2 * 2 * 4096 * 128
         assert kvq.kvq_cache_bytes(d) == orc.codes_bytes(2, 4096, 128, batch=2)
-        st, msg = _status("kvq_attention_chunk", ctypes.byref(d), FAKE, 4, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8,
-                          None)
-        assert st == kvq.KVQ_ERR_UNSUPPORTED and "FP8" in msg
         r = kvq.make_recent(4, 5, FAKE, FAKE)
         st, msg = _status("kvq_append_recent", ctypes.byref(d), ctypes.byref(r), FAKE, FAKE, 0, 1, FAKE, None)
         assert st == kvq.KVQ_ERR_UNSUPPORTED, msg

@@ -170,15 +170,39 @@ def test_fused_fp8_equals_two_launches(kvq, fmt, paged):
                            orc.attention_decode(qv, _hat(x["k"], fmt), _hat(x["v"], fmt), lens, 0.088), "fp8 fused")
 
 
-def test_fp8_chunk_and_recent_unsupported(kvq):
+CHUNK_CASES = [
+    # fmt, D, H, KVH, L0s, n, paged, window
+    ("e4m3", 128, 32, 8, [300, 17], 100, False, 0),
+    ("e5m2", 128, 32, 8, [700], 130, True, 0),
+    ("e4m3", 64, 8, 2, [200, 513], 50, False, 0),
+    ("e5m2", 64, 16, 4, [0, 90], 77, True, 0),
+    ("e4m3", 128, 32, 8, [1000], 64, False, 129),
+]
+
+
+@pytest.mark.parametrize("fmt,D,H,KVH,L0s,n,paged,window", CHUNK_CASES)
+def test_chunk_fp8(kvq, fmt, D, H, KVH, L0s, n, paged, window):
     import torch
-    cache, _ = _cache(kvq, "e4m3", 1, 8, 2, 128, 64, False, None)
-    q = torch.zeros((1, 8, 4, 128), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(kvq.KvqError) as e:
-        cache.chunk(q, dev_tensor(np.zeros(1, np.int32)), True, 0.1, 60)
-    assert e.value.status == kvq.kvq.KVQ_ERR_UNSUPPORTED
+    log(f"fp8 chunk: fmt={fmt} D={D} L0={L0s} n={n} paged={paged} window={window}")
+    B = len(L0s)
+    T = max(L0s) + n
+    rng = np.random.default_rng(D + n + paged + window)
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "bf16", scale=2.0)
+    qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, n, D))
+    cache, _ = _cache(kvq, fmt, B, H, KVH, D, T, paged, rng)
+    cache.append(kv_dev(x["k_raw"]), kv_dev(x["v_raw"]), dev_tensor(np.zeros(B, np.int32)))
+    scale = 1.0 / np.sqrt(D)
+    out = cache.chunk(bf16_dev(qb), dev_tensor(np.asarray(L0s, np.int32)), True, scale, max(L0s), window=window)
+    torch.cuda.synchronize()
+    ref = orc.attention_chunk(qv, _hat(x["k"], fmt), _hat(x["v"], fmt), L0s, True, scale, window=window)
+    assert_attention_close(to_host_bits(out), ref, f"fp8 {fmt} chunk")
+
+
+def test_fp8_recent_unsupported(kvq):
+    import torch
+    q = torch.zeros((1, 8, 128), dtype=torch.bfloat16, device="cuda")
     # (the workspace query fails first; sizes report errors as 0, which the
     # binding raises with the library's message)
     with pytest.raises(kvq.KvqError, match="recent window over FP8 codes is not supported"):
         kvq.Int8KVCache(1, 8, 2, 128, max_len=64, fp8="e5m2", recent_window=4).decode(
-            q[:, :, 0].contiguous(), dev_tensor(np.ones(1, np.int32)), 0.1, 64)
+            q, dev_tensor(np.ones(1, np.int32)), 0.1, 64)
