@@ -109,9 +109,9 @@ def chunk_counts(w: wl.Workload) -> dict:
     L = L0 + n
     rows = L - max(0, L0 - win + 1) if win else L    # keys some query of the chunk sees
     codes = 2 * B * KVH * rows * D
-    scales = 2 * B * KVH * rows * 4
+    scales = 0 if w.extra.get("fp8") else 2 * B * KVH * rows * 4
     qo = 2 * B * H * n * D * 2
-    append = 2 * B * KVH * n * (D * 2 + D + 4)
+    append = 2 * B * KVH * n * (D * 2 + D + (0 if w.extra.get("fp8") else 4))
     return {"flops": flops, "chunk_bytes": codes + scales + qo, "step_bytes": codes + scales + qo + append}
 
 
@@ -291,9 +291,14 @@ def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
     while time.perf_counter() - t0 < target_s:
         b = int(rng.integers(w.batch))
         g = int(rng.integers(w.num_kv_heads))
-        kc, ks = orc.quantize(x["k"][b, g], 0)
-        vc, vs = orc.quantize(x["v"][b, g], 0)
-        kh, vh = orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs)
+        fp8 = w.extra.get("fp8")
+        if fp8:
+            kh = orc.fp8_decode(orc.fp8_encode(x["k"][b, g], fp8), fp8)
+            vh = orc.fp8_decode(orc.fp8_encode(x["v"][b, g], fp8), fp8)
+        else:
+            kc, ks = orc.quantize(x["k"][b, g], 0)
+            vc, vs = orc.quantize(x["v"][b, g], 0)
+            kh, vh = orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs)
         for _ in range(64):
             h = g * hpg + int(rng.integers(hpg))
             i = int(rng.integers(w.n_new))
@@ -328,7 +333,8 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     x = wl.layer_inputs(w, 0)
     B, KVH, T, D = x["k"].shape
     dev = torch.device("cuda")
-    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len)
+    fp8 = w.extra.get("fp8")
+    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8)
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
@@ -377,8 +383,9 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_chunk(w, x)
+    codes_what = f"FP8 {fp8.upper()} codes" if fp8 else "per-token fp32 scales"
     result = {
-        "metric": "INT8-KV chunked-prefill attention: MFMA TFLOP/s over visible keys"
+        "metric": ("FP8" if fp8 else "INT8") + "-KV chunked-prefill attention: MFMA TFLOP/s over visible keys"
                   + (" (sliding window)" if win else ""),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
@@ -393,7 +400,7 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
         "data": "synthetic",
         "config": {"workload": f"{w.name}: batch {B}, {w.num_heads} q / {KVH} kv heads, head_dim {D}, "
                                f"{w.ctx} cached + {w.n_new} new tokens, causal"
-                               + (f", sliding window {win}" if win else "") + ", per-token fp32 scales; "
+                               + (f", sliding window {win}" if win else "") + f", {codes_what}; "
                                f"append the {w.n_new} rows + chunk attention",
                    "batch": B, "seq_len": T, "flops_per_step": cnt["flops"], "bytes_per_step": cnt["step_bytes"]},
         "roofline": {"bound": "mfma", "kernel": kname,
@@ -669,7 +676,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
-                                                            "bf16_scales", "fp8_e4m3"])
+                                                            "bf16_scales", "fp8_e4m3", "fp8_chunk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -709,7 +716,7 @@ def main():
     if w.name == "sliding_decode":
         run_sliding(args, w, kvq, torch, stream)
         return
-    if w.name in ("chunked_prefill", "sliding_chunk"):
+    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk"):
         run_chunk(args, w, kvq, torch, stream)
         return
     if w.name == "paged_decode":

@@ -105,8 +105,12 @@ BF16_SCALES = Workload("bf16_scales", 16, 32, 8, 128, 0, "contiguous", "bf16", 4
 FP8_E4M3 = Workload("fp8_e4m3", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
                     layers=32, outliers=4, seed=9, extra={"fp8": "e4m3"})
 
+# The chunked-prefill step on FP8 E4M3 codes.
+FP8_CHUNK = Workload("fp8_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512,
+                     seed=10, extra={"fp8": "e4m3"})
+
 ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
-                           BF16_SCALES, FP8_E4M3)}
+                           BF16_SCALES, FP8_E4M3, FP8_CHUNK)}
 
 
 # ----------------------------------------------------------------------------
