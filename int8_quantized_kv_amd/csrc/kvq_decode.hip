@@ -377,6 +377,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   const int gqa = c.num_heads / c.num_kv_heads;
   p.wg_per_kvh = gqa / plan.heads_per_wg;
   p.longest_first = plan.longest_first && stream_kernel ? 1 : 0;
+  p.balance = plan.split_len >= kBalanceSplit ? 1 : 0;
   p.rk = rc.k;
   p.rv = rc.v;
   p.rwin = rc.window;

@@ -69,6 +69,7 @@ struct DecodeParams {
   int32_t len_cap;           // min(hint, capacity)
   int32_t wg_per_kvh;        // workgroups sharing one KV head (GQA group / HPW)
   int32_t longest_first;     // workgroup z takes the z-th longest sequence (batch <= kLongestFirstMax)
+  int32_t balance;           // paired waves of a SIMD keep pace through their priority (long splits)
   float scale_log2;          // attn_scale * log2(e)
   // recent window (hybrid cache): the last rwin positions are bf16 rows in
   // ring slot (position % rcap), attended by the workgroup of the last INT8 split
@@ -90,6 +91,7 @@ constexpr int kStreamThreads = kStreamWaves * kWave;
 constexpr int kCUs = 256;          // MI355X compute units: the split heuristic aims at one workgroup each
 constexpr int kBlock = 64;         // tokens per wave block (streaming kernel)
 constexpr int kLongestFirstMax = kStreamThreads;  // largest batch ranked by length in a workgroup
+constexpr int kBalanceSplit = 4096;  // splits at least this long pace each SIMD's two waves
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSmToken = KVQ_SCALE_PER_TOKEN;         // scale modes, as kernel template arguments
 constexpr int kSmGroup32 = KVQ_SCALE_GROUP32;
@@ -604,6 +606,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   __shared__ uint4 sm_nk[D / 16];                    // fused append: new K codes
   __shared__ uint2 sm_nv[D / 8];                     // fused append: new V codes
   __shared__ float sm_ns[2][NG];                     // fused append: new K / V scales
+  __shared__ int sm_prog[kStreamWaves];              // blocks each wave has started
 
   // Consecutive workgroup ids go to consecutive XCDs, so the head group varies
   // fastest: each XCD then receives one head group of every (sequence, split),
@@ -801,8 +804,27 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   };
 
   // ---- one 64-token block; PREFETCH issues the next block's loads early ----------
+  // Waves w and w + 4 share a SIMD, whose issue arbitration favours the older
+  // one: left alone it finishes its blocks well ahead of the younger, which
+  // then streams by itself.  With long splits over ragged lengths (several
+  // rounds of workgroups, where the last ones stream alone and a workgroup's
+  // own rate decides) a wave that has started fewer blocks than its partner
+  // takes the higher priority, so the two keep pace (measured on the paged
+  // workload: 2-4% faster).  With one round the chip's bandwidth is the limit
+  // and the check only costs time; the contiguous kernel leaves it out, since
+  // even untaken it slows the loop's code by 3%.  (Scheduling only: which
+  // wave computes which block is unchanged.)
+  int started = 0;
+  volatile int* prog = sm_prog;
+  if (PAGED && p.balance && lane == 0) prog[wave] = 0;
   auto run_block = [&](int blk, auto prefetch) {
     constexpr bool PREFETCH = decltype(prefetch)::value;
+    if (PAGED && p.balance) {
+      ++started;
+      if (lane == 0) prog[wave] = started;
+      if (started < __builtin_amdgcn_readfirstlane(prog[wave ^ (kStreamWaves / 2)])) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
     if constexpr (APPEND) {
       // the block holding the freshly appended token uses the codes just
       // computed (its loads may have been issued before they were stored)
@@ -1141,6 +1163,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 
   for (; blk + kStreamWaves < nblk; blk += kStreamWaves) run_block(blk, std::true_type{});
   if (blk < nblk) run_block(blk, std::false_type{});
+  if constexpr (PAGED) __builtin_amdgcn_s_setprio(0);
 
   // ---- combine the wave: l and weight sums over lanes, o over token slots ------
 #pragma unroll
