@@ -336,19 +336,22 @@ kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, 
 
 /* Workspace bytes needed by kvq_attention_decode_recent and
  * kvq_append_decode_recent for lengths up to max_seq_len (0 on an invalid
- * descriptor). */
+ * descriptor).  Like every sizing call it reads only the geometry: the
+ * device pointers may still be NULL. */
 size_t kvq_workspace_size_recent(const kvq_cache* cache, const kvq_recent* recent, int32_t max_seq_len);
 
 /* Workspace bytes needed by kvq_attention_decode (n_query = 1) or
  * kvq_attention_chunk (n_query = chunk length) for lengths up to
- * max_seq_len.  0 on an invalid descriptor (see kvq_last_error). */
+ * max_seq_len.  0 on an invalid descriptor (see kvq_last_error).  Only the
+ * geometry is read: the device pointers may still be NULL. */
 size_t kvq_workspace_size(const kvq_cache* cache, int32_t max_seq_len, int32_t n_query);
 
 /* Bytes of codes plus scales the descriptor addresses, K and V together
  * (realizar kv_cache_q8_init.rs `kv_cache_q8_memory_bytes`: 2 * (values +
  * 4 * scales) per layer; 2 bytes per scale in KVQ_SCALE_PER_TOKEN_BF16).
  * Contiguous: batch*KVH*max_len rows; paged: num_pages*KVH*16 rows.  0 on an
- * invalid descriptor. */
+ * invalid descriptor.  Only the geometry is read, so a cache can be sized
+ * before it is allocated (NULL pointers are accepted). */
 uint64_t kvq_cache_bytes(const kvq_cache* cache);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */

@@ -25,7 +25,9 @@ kvq_status fail(kvq_status st, const char* fmt, ...) {
 namespace {
 
 // Descriptor checks common to every entry point.
-kvq_status check_cache(const kvq_cache* c, const char* who) {
+// The descriptor's geometry, and with need_pointers its device pointers (the
+// sizing calls take descriptors of caches not allocated yet).
+kvq_status check_cache(const kvq_cache* c, const char* who, bool need_pointers = true) {
   if (!c) return fail(KVQ_ERR_INVALID_ARG, "%s: cache descriptor is NULL", who);
   if (c->batch <= 0 || c->num_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0)
     return fail(KVQ_ERR_INVALID_ARG, "%s: batch, num_heads, num_kv_heads and head_dim must be positive", who);
@@ -45,12 +47,13 @@ kvq_status check_cache(const kvq_cache* c, const char* who) {
       return fail(KVQ_ERR_INVALID_ARG, "%s: page_size must be %d (got %d)", who, kPageSize, c->page_size);
     if (c->num_pages <= 0 || c->max_blocks_per_seq <= 0)
       return fail(KVQ_ERR_INVALID_ARG, "%s: paged cache needs num_pages > 0 and max_blocks_per_seq > 0", who);
-    if (!c->block_table) return fail(KVQ_ERR_INVALID_ARG, "%s: paged cache needs a block_table", who);
+    if (need_pointers && !c->block_table) return fail(KVQ_ERR_INVALID_ARG, "%s: paged cache needs a block_table", who);
     if (static_cast<int64_t>(c->max_blocks_per_seq) * kPageSize > 0x7fffffffLL)
       return fail(KVQ_ERR_INVALID_ARG, "%s: max_blocks_per_seq too large", who);
   } else {
     return fail(KVQ_ERR_INVALID_ARG, "%s: unknown layout %d", who, c->layout);
   }
+  if (!need_pointers) return KVQ_OK;
   if (!c->k_codes || !c->v_codes) return fail(KVQ_ERR_INVALID_ARG, "%s: cache code pointers must be non-NULL", who);
   if (!is_fp8(*c)) {  // FP8 codes carry no scales
     if (!c->k_scales || !c->v_scales)
@@ -81,7 +84,7 @@ KVQ_API const char* kvq_version(void) { return "kvq 0.1.0 (gfx950)"; }
 
 KVQ_API uint64_t kvq_cache_bytes(const kvq_cache* c) {
   g_err[0] = '\0';
-  if (check_cache(c, "kvq_cache_bytes") != KVQ_OK) return 0;
+  if (check_cache(c, "kvq_cache_bytes", false) != KVQ_OK) return 0;
   const uint64_t rows = c->layout == KVQ_LAYOUT_PAGED
                             ? static_cast<uint64_t>(c->num_pages) * c->num_kv_heads * kPageSize
                             : static_cast<uint64_t>(c->batch) * c->num_kv_heads * c->max_len;
@@ -92,7 +95,7 @@ KVQ_API uint64_t kvq_cache_bytes(const kvq_cache* c) {
 namespace kvq {
 namespace {
 
-kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who) {
+kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who, bool need_pointers = true) {
   if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
   if (r->window < 1) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, r->window);
   if (r->capacity <= r->window)
@@ -100,7 +103,7 @@ kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who
                 r->window);
   if (static_cast<int64_t>(r->capacity) * c.head_dim > 0x7fffffffLL)
     return fail(KVQ_ERR_INVALID_ARG, "%s: ring capacity too large", who);
-  if (!r->k || !r->v) return fail(KVQ_ERR_INVALID_ARG, "%s: ring pointers must be non-NULL", who);
+  if (need_pointers && (!r->k || !r->v)) return fail(KVQ_ERR_INVALID_ARG, "%s: ring pointers must be non-NULL", who);
   if (is_fp8(c)) return fail(KVQ_ERR_UNSUPPORTED, "%s: a recent window over FP8 codes is not supported", who);
   return KVQ_OK;
 }
@@ -110,8 +113,8 @@ bool finite(float x) { return x == x && x != INFINITY && x != -INFINITY; }
 size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_len, int32_t n_query,
                       const char* who, int32_t window = 0) {
   g_err[0] = '\0';
-  if (check_cache(c, who) != KVQ_OK) return 0;
-  if (r && check_recent(r, *c, who) != KVQ_OK) return 0;
+  if (check_cache(c, who, false) != KVQ_OK) return 0;
+  if (r && check_recent(r, *c, who, false) != KVQ_OK) return 0;
   if (max_seq_len <= 0 || n_query <= 0) {
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;

@@ -115,6 +115,9 @@ INVALID_DESCRIPTORS = [
     # kernels read the aligned 32-bit word that holds a scale
     ("misaligned_scales", dict(scale_mode=kvq.KVQ_SCALE_PER_TOKEN_BF16, ptrs=(FAKE, FAKE, FAKE + 2, FAKE))),
 ]
+# errors in device pointers only: the sizing calls, which read the geometry
+# alone, accept these descriptors
+POINTER_ONLY = {"paged_no_table", "null_codes", "null_scales", "misaligned_scales"}
 
 
 @pytest.mark.parametrize("name,kw", INVALID_DESCRIPTORS, ids=[n for n, _ in INVALID_DESCRIPTORS])
@@ -130,8 +133,12 @@ def test_invalid_descriptor_rejected_everywhere(name, kw):
         st, msg = _status(fn, *args)
         assert st == kvq.KVQ_ERR_INVALID_ARG, (fn, st, msg)
         assert msg
-    assert kvq.library().kvq_cache_bytes(d) == 0
-    assert kvq.library().kvq_workspace_size(d, 16, 1) == 0
+    if name in POINTER_ONLY:
+        assert kvq.library().kvq_cache_bytes(d) > 0
+        assert kvq.library().kvq_workspace_size(d, 16, 1) > 0
+    else:
+        assert kvq.library().kvq_cache_bytes(d) == 0
+        assert kvq.library().kvq_workspace_size(d, 16, 1) == 0
 
 
 def test_null_descriptor():
@@ -267,3 +274,19 @@ def test_fp8_descriptors_need_no_scales():
         st, msg = _status("kvq_append_recent", ctypes.byref(d), ctypes.byref(r), FAKE, FAKE, 0, 1, FAKE, None)
         assert st == kvq.KVQ_ERR_UNSUPPORTED, msg
     assert _status("kvq_cache_bytes", ctypes.byref(_desc(scale_mode=5)))[0] == 0
+
+
+def test_sizing_before_allocation():
+    """A descriptor with no device pointers yet sizes the cache it describes
+    (the same figures as with pointers) and its decode workspace."""
+    for mode in (kvq.KVQ_SCALE_PER_TOKEN, kvq.KVQ_SCALE_GROUP32, kvq.KVQ_CODES_FP8_E4M3):
+        bare = _desc(scale_mode=mode, max_len=512, ptrs=(0, 0, 0, 0))
+        full = _desc(scale_mode=mode, max_len=512)
+        assert kvq.kvq_cache_bytes(bare) == kvq.kvq_cache_bytes(full) > 0
+        assert kvq.library().kvq_workspace_size(ctypes.byref(bare), 512, 1) == \
+            kvq.library().kvq_workspace_size(ctypes.byref(full), 512, 1) > 0
+    paged = _desc(layout=kvq.KVQ_LAYOUT_PAGED, num_pages=10, max_blocks_per_seq=4, ptrs=(0, 0, 0, 0))
+    assert kvq.kvq_cache_bytes(paged) == 2 * 10 * 2 * 16 * (128 + 4)
+    # the entry points that touch memory still require the pointers
+    st, msg = _status("kvq_append", ctypes.byref(paged), FAKE, FAKE, 0, 1, FAKE, None)
+    assert st == kvq.KVQ_ERR_INVALID_ARG and "block_table" in msg
