@@ -109,9 +109,10 @@ def chunk_counts(w: wl.Workload) -> dict:
     L = L0 + n
     rows = L - max(0, L0 - win + 1) if win else L    # keys some query of the chunk sees
     codes = 2 * B * KVH * rows * D
-    scales = 0 if w.extra.get("fp8") else 2 * B * KVH * rows * 4
+    G = D // 32 if w.group == 32 else 1
+    scales = 0 if w.extra.get("fp8") else 2 * B * KVH * rows * 4 * G
     qo = 2 * B * H * n * D * 2
-    append = 2 * B * KVH * n * (D * 2 + D + (0 if w.extra.get("fp8") else 4))
+    append = 2 * B * KVH * n * (D * 2 + D + (0 if w.extra.get("fp8") else 4 * G))
     return {"flops": flops, "chunk_bytes": codes + scales + qo, "step_bytes": codes + scales + qo + append}
 
 
@@ -296,8 +297,8 @@ def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
             kh = orc.fp8_decode(orc.fp8_encode(x["k"][b, g], fp8), fp8)
             vh = orc.fp8_decode(orc.fp8_encode(x["v"][b, g], fp8), fp8)
         else:
-            kc, ks = orc.quantize(x["k"][b, g], 0)
-            vc, vs = orc.quantize(x["v"][b, g], 0)
+            kc, ks = orc.quantize(x["k"][b, g], w.group)
+            vc, vs = orc.quantize(x["v"][b, g], w.group)
             kh, vh = orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs)
         for _ in range(64):
             h = g * hpg + int(rng.integers(hpg))
@@ -334,7 +335,7 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     B, KVH, T, D = x["k"].shape
     dev = torch.device("cuda")
     fp8 = w.extra.get("fp8")
-    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8)
+    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8, group32=(w.group == 32))
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
@@ -383,7 +384,8 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_chunk(w, x)
-    codes_what = f"FP8 {fp8.upper()} codes" if fp8 else "per-token fp32 scales"
+    codes_what = (f"FP8 {fp8.upper()} codes" if fp8 else
+                  "group-32 fp32 scales" if w.group == 32 else "per-token fp32 scales")
     result = {
         "metric": ("FP8" if fp8 else "INT8") + "-KV chunked-prefill attention: MFMA TFLOP/s over visible keys"
                   + (" (sliding window)" if win else ""),
@@ -676,7 +678,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
-                                                            "bf16_scales", "fp8_e4m3", "fp8_chunk"])
+                                                            "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -716,7 +718,7 @@ def main():
     if w.name == "sliding_decode":
         run_sliding(args, w, kvq, torch, stream)
         return
-    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk"):
+    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk", "chunk_group32"):
         run_chunk(args, w, kvq, torch, stream)
         return
     if w.name == "paged_decode":

@@ -46,6 +46,7 @@ namespace kvq {
 namespace {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -85,12 +86,16 @@ struct ChunkParams {
 // by 16 bytes, so the 16 lanes of one K read (16 consecutive rows, one
 // 16-byte unit) fall on distinct banks.  V rows hold D codes in 8-byte units,
 // XOR-permuted so the 32 lanes of one V transpose read (8 rows x 4 units) do.
-template <int D, int TOK>
+// With group-32 scales (G32) a buffer also holds, per token, the ratios of
+// consecutive K group scales s_g / s_(g+1) (fp32, groups 0 .. G-2) and the
+// f16 ratios s_g / s_max of V.
+template <int D, int TOK, bool G32 = false>
 struct Tile {
   static constexpr int kKRow = 2 * D + 16;
   static constexpr int kKBytes = TOK * kKRow;
   static constexpr int kVBytes = TOK * D;
-  static constexpr int kBytes = kKBytes + kVBytes + 3 * TOK * 4;
+  static constexpr int kNG = D / 32;
+  static constexpr int kBytes = kKBytes + kVBytes + 3 * TOK * 4 + (G32 ? (kNG - 1) * TOK * 4 + kNG * TOK * 2 : 0);
   static __device__ __forceinline__ int vswz(int t) {
     if constexpr (D == 128) {
       const int s = (t >> 1) & 15;
@@ -106,6 +111,8 @@ struct Tile {
   static constexpr int kKc = kKBytes + kVBytes;
   static constexpr int kLsv = kKc + TOK * 4;
   static constexpr int kRsv = kLsv + TOK * 4;
+  static constexpr int kRk = kRsv + TOK * 4;            // G32: fp32 [group][token], K s_g / s_(g+1)
+  static constexpr int kRv = kRk + (kNG - 1) * TOK * 4; // G32: f16 [group][token], V s_g / s_max
 };
 
 // Four codes -> two f16 pairs holding the exact values c - 128.
@@ -183,7 +190,14 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   constexpr bool SBF = SM == KVQ_SCALE_PER_TOKEN_BF16;
   constexpr bool FP8 = SM == KVQ_CODES_FP8_E4M3 || SM == KVQ_CODES_FP8_E5M2;
   constexpr bool E5 = SM == KVQ_CODES_FP8_E5M2;
-  using TL = Tile<D, kCkTile>;
+  // group-32: K stays exact f16 c - 128; the score accumulator takes the
+  // group scales in Horner form, multiplied per token by s_g / s_(g+1) after
+  // group g's k-steps, with the last group's scale in the token's score
+  // factor (all fp32).  V is exact c - 128, and each 32-dim output tile (one
+  // group) weights its tokens by s_g / s_max
+  constexpr bool G32 = SM == KVQ_SCALE_GROUP32;
+  constexpr int NG = D / 32;
+  using TL = Tile<D, kCkTile, G32>;
   constexpr int kTT = kCkTile / 32;                        // 32-token S tiles per tile
   constexpr int kChunksPerRow = D / 16;                    // 16-code pieces per row
   constexpr int kChunks = kCkTile * kChunksPerRow;         // per side per tile
@@ -272,6 +286,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   const bool ld_s = tid < 2 * kCkTile;
   uint4 lreg[kLoads];
   uint32_t sreg = 0u;  // scale word as loaded, decoded when the tile is stored
+  float greg[G32 ? NG : 1];  // group-32: the token's group scales as loaded
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -289,7 +304,18 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       const int t = t0 + (tid & (kCkTile - 1));
       if (t < Ltot) {
         const int64_t row = row_of<PAGED>(p, b, g, t);
-        sreg = scale_word(tid < kCkTile ? p.k_scales : p.v_scales, row, SBF);
+        if constexpr (G32) {
+          const float* gs = (tid < kCkTile ? p.k_scales : p.v_scales) + row * NG;
+          if constexpr (NG == 4) {
+            const float4 v = *reinterpret_cast<const float4*>(gs);
+            greg[0] = v.x; greg[1] = v.y; greg[2] = v.z; greg[3] = v.w;
+          } else {
+#pragma unroll
+            for (int k = 0; k < NG; ++k) greg[k] = gs[k];
+          }
+        } else {
+          sreg = scale_word(tid < kCkTile ? p.k_scales : p.v_scales, row, SBF);
+        }
       }
     }
   };
@@ -329,7 +355,24 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       // (page rows start even, so in the paged layout the token's parity)
       const int64_t srow = PAGED ? static_cast<int64_t>(t0 + tl)
                                  : (static_cast<int64_t>(b) * p.geom.kvh + g) * p.geom.max_len + t0 + tl;
-      const float sv = FP8 ? 1.0f : scale_value(sreg, scale_sel(srow, SBF));
+      float sv = FP8 ? 1.0f : scale_value(sreg, scale_sel(srow, SBF));
+      if constexpr (G32) {
+        if (tid < kCkTile) {
+          // K: consecutive group ratios; the last group's scale is the factor
+          float* rk = reinterpret_cast<float*>(buf + TL::kRk);
+#pragma unroll
+          for (int k = 0; k + 1 < NG; ++k) rk[k * kCkTile + tl] = ok ? greg[k] / greg[k + 1] : 1.0f;
+          sv = greg[NG - 1];
+        } else {
+          // V: the token's largest group scale, and each group's ratio to it
+          sv = greg[0];
+#pragma unroll
+          for (int k = 1; k < NG; ++k) sv = fmaxf(sv, greg[k]);
+          _Float16* rv = reinterpret_cast<_Float16*>(buf + TL::kRv);
+#pragma unroll
+          for (int k = 0; k < NG; ++k) rv[k * kCkTile + tl] = static_cast<_Float16>(ok ? greg[k] / sv : 0.0f);
+        }
+      }
       if (tid < kCkTile) {
         reinterpret_cast<float*>(buf + TL::kKc)[tl] = ok ? sv * kfac : 0.0f;
       } else {
@@ -339,12 +382,14 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     }
   };
 
-  if constexpr (FP8) {
+  if constexpr (FP8 || G32) {
     // the first MFMA step takes the last buffer's values times all-zero
     // weights before anything is staged there; FP8 bytes left in LDS could be
-    // NaN or inf codes, and 0 * NaN is NaN, so those values start as zeros
-    uint8_t* bz = smem + (kCkBufs - 1) * TL::kBytes + TL::kKBytes;
-    for (int i = tid * 16; i < TL::kVBytes; i += kCkThreads * 16)
+    // NaN or inf codes (group-32: the V group ratios, f16, could be), and
+    // 0 * NaN is NaN, so those values start as zeros
+    uint8_t* bz = smem + (kCkBufs - 1) * TL::kBytes + (FP8 ? TL::kKBytes : TL::kRv);
+    constexpr int kZero = FP8 ? TL::kVBytes : TL::kNG * kCkTile * 2;
+    for (int i = tid * 16; i < kZero; i += kCkThreads * 16)
       *reinterpret_cast<uint4*>(bz + i) = make_uint4(0u, 0u, 0u, 0u);
   }
   load_tile(tbase);
@@ -432,8 +477,20 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
             const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                 (v2i __attribute__((address_space(3)))*)(bv + TL::v_off(tok, 4 * dt + vunit)));
             const uint32_t lo = static_cast<uint32_t>(c8.x), hi = static_cast<uint32_t>(c8.y);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(FP8 ? fp8_codes_f16<E5>(lo, hi) : codes_tiny_f16(lo, hi),
-                                                             pw[tt][ks], oacc[dt], 0, 0, 0);
+            if constexpr (G32) {
+              // tile dt is group dt: the weights of its tokens times s_g / s_max
+              const _Float16* rv = reinterpret_cast<const _Float16*>(bv + TL::kRv) + dt * kCkTile + 32 * tt + 16 * ks +
+                                   4 * half;
+              const f16x4 r0 = *reinterpret_cast<const f16x4*>(rv);
+              const f16x4 r1 = *reinterpret_cast<const f16x4*>(rv + 8);
+              const f16x8 r8 = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+              const uint2 a0 = codes_exact_f16(lo), a1 = codes_exact_f16(hi);
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(f16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)), pw[tt][ks] * r8, oacc[dt], 0, 0, 0);
+            } else {
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  FP8 ? fp8_codes_f16<E5>(lo, hi) : codes_tiny_f16(lo, hi), pw[tt][ks], oacc[dt], 0, 0, 0);
+            }
           }
         }
       }
@@ -457,6 +514,22 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
         for (int tt = 0; tt < kTT; ++tt) {
           s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[tt], qop[kk], s[tt], 0, 0, 0);
           ka[tt] = na[tt];
+        }
+        if constexpr (G32) {
+          if (kk % 2 == 1 && kk + 1 < kKK) {  // group kk / 2 complete: Horner step
+            const float* rk = reinterpret_cast<const float*>(bk + TL::kRk) + (kk / 2) * kCkTile;
+#pragma unroll
+            for (int tt = 0; tt < kTT; ++tt) {
+#pragma unroll
+              for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 f = *reinterpret_cast<const float4*>(rk + 32 * tt + 8 * q4 + 4 * half);
+                s[tt][4 * q4 + 0] *= f.x;
+                s[tt][4 * q4 + 1] *= f.y;
+                s[tt][4 * q4 + 2] *= f.z;
+                s[tt][4 * q4 + 3] *= f.w;
+              }
+            }
+          }
         }
       }
     }
@@ -530,7 +603,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f16x2 h2 = pack2(w[2 * e], w[2 * e + 1]);
-          w_run = dot2(h2, ones, w_run);
+          if constexpr (!G32) w_run = dot2(h2, ones, w_run);
           pw[tt][ks][2 * e] = h2[0];
           pw[tt][ks][2 * e + 1] = h2[1];
         }
@@ -562,8 +635,8 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   // INT8: the V operands carry c 2^-24, so the sum is 2^24 acc - 128 sum w;
   // FP8 operands are the values themselves
-  const float big = FP8 ? 1.0f : 16777216.0f;
-  const float off = FP8 ? 0.0f : 128.0f * w_tot;
+  const float big = FP8 || G32 ? 1.0f : 16777216.0f;
+  const float off = FP8 || G32 ? 0.0f : 128.0f * w_tot;
   uint16_t* orow = p.out + ((static_cast<int64_t>(b) * p.heads + head) * p.n + qi) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
@@ -591,6 +664,7 @@ void launch_chunk_d(bool paged, int sm, dim3 grid, hipStream_t stream, const Chu
     case KVQ_SCALE_PER_TOKEN_BF16: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN_BF16>(paged, grid, stream, p); break;
     case KVQ_CODES_FP8_E4M3: launch_chunk_sm<D, KVQ_CODES_FP8_E4M3>(paged, grid, stream, p); break;
     case KVQ_CODES_FP8_E5M2: launch_chunk_sm<D, KVQ_CODES_FP8_E5M2>(paged, grid, stream, p); break;
+    case KVQ_SCALE_GROUP32: launch_chunk_sm<D, KVQ_SCALE_GROUP32>(paged, grid, stream, p); break;
     default: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN>(paged, grid, stream, p); break;
   }
 }
@@ -603,8 +677,6 @@ size_t chunk_workspace(const kvq_cache&, int, int) { return 0; }
 
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens, int causal,
                         float attn_scale, uint16_t* out, void*, int, hipStream_t stream, int window) {
-  if (c.scale_mode == KVQ_SCALE_GROUP32)
-    return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk: group-32 scales are not supported");
   ChunkParams p;
   p.q = q;
   p.out = out;

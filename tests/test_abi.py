@@ -183,10 +183,7 @@ def test_chunk_and_dequant_argument_errors():
         kvq.KVQ_ERR_INVALID_ARG
     assert _status("kvq_attention_chunk", d, FAKE, 8, FAKE, 1, float("nan"), FAKE, FAKE, 1 << 30, 8, None)[0] == \
         kvq.KVQ_ERR_INVALID_ARG
-    # group-32 scales and head sizes other than 64 / 128 have no chunk kernel
-    g32 = ctypes.byref(_desc(scale_mode=kvq.KVQ_SCALE_GROUP32))
-    assert _status("kvq_attention_chunk", g32, FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
-        kvq.KVQ_ERR_UNSUPPORTED
+    # head sizes other than 64 / 128 have no chunk kernel
     d256 = ctypes.byref(_desc(head_dim=256))
     assert _status("kvq_attention_chunk", d256, FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
         kvq.KVQ_ERR_UNSUPPORTED

@@ -140,3 +140,43 @@ def test_chunk_full_size_sampled(kvq):
         ref[j] = orc.softmax_attend(x["q"][b, h, i].astype(np.float64), kh, vh, w.attn_scale, None)
         gsel[j] = got[b, h, i]
     assert_attention_close(gsel, ref, "full-size chunk")
+
+
+G32_CASES = [
+    # D, H, KVH, ctx_lens, n, causal, paged, window
+    (128, 32, 8, [0, 100], 37, True, False, 0),
+    (128, 32, 8, [513, 64], 96, True, True, 0),
+    (64, 8, 2, [17, 300], 70, False, False, 0),
+    (64, 16, 4, [200], 33, True, True, 0),
+    (128, 32, 8, [700], 130, True, False, 129),
+]
+
+
+@pytest.mark.parametrize("D,H,KVH,ctx,n,causal,paged,window", G32_CASES)
+def test_chunk_group32(kvq, D, H, KVH, ctx, n, causal, paged, window):
+    """Group-32 scales (realizar kv_cache_q8_init.rs layout): the oracle
+    dequantizes each 32-element group with its own scale.  Inputs carry a
+    different magnitude per group, so the group scales differ widely."""
+    import torch
+    log(f"chunk group-32: D={D} H={H} KVH={KVH} ctx={ctx} n={n} causal={causal} paged={paged} w={window}")
+    B = len(ctx)
+    T = max(ctx) + n
+    rng = np.random.default_rng(D + n + paged + window)
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "f32")
+    gain = np.repeat(np.float32(2.0) ** rng.integers(-4, 5, size=(1, KVH, 1, D // 32)).astype(np.float32), 32, -1)
+    k, v = (x["k"] * gain).astype(np.float32), (x["v"] * gain[..., ::-1]).astype(np.float32)
+    qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, n, D))
+    if paged:
+        table, npages = random_block_table(rng, [T] * B)
+        cache = kvq.Int8KVCache(B, H, KVH, D, num_pages=npages, block_table=dev_tensor(table), fill=0, group32=True)
+    else:
+        cache = kvq.Int8KVCache(B, H, KVH, D, max_len=T, fill=0, group32=True)
+    cache.append(kv_dev(k), kv_dev(v), dev_tensor(np.zeros(B, np.int32)))
+    scale = 1.0 / np.sqrt(D)
+    out = cache.chunk(bf16_dev(qb), dev_tensor(np.asarray(ctx, np.int32)), causal, scale, max(ctx), window=window)
+    torch.cuda.synchronize()
+    kc, ks = orc.quantize(k, 32)
+    vc, vs = orc.quantize(v, 32)
+    ref = orc.attention_chunk(qv, orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs), ctx, causal, scale,
+                              window=window)
+    assert_attention_close(to_host_bits(out), ref, "chunk group-32")

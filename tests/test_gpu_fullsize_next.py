@@ -143,10 +143,10 @@ def test_sliding_decode_full_size(kvq):
     del hat
 
 
-@pytest.mark.parametrize("name", ["sliding_chunk", "fp8_chunk"])
+@pytest.mark.parametrize("name", ["sliding_chunk", "fp8_chunk", "chunk_group32"])
 def test_chunk_variant_full_size(kvq, name):
-    """512 new queries after 8192 cached tokens: with a window of 1024, or on
-    FP8 E4M3 codes."""
+    """512 new queries after 8192 cached tokens: with a window of 1024, on
+    FP8 E4M3 codes, or with group-32 scales."""
     import torch
     w = wl.ALL[name]
     win = w.extra.get("sliding", 0)
@@ -154,7 +154,7 @@ def test_chunk_variant_full_size(kvq, name):
     x = wl.layer_inputs(w, 0)
     B, KVH, T, D = x["k"].shape
     log(f"full size {name}: B={B} ctx={w.ctx} n={w.n_new} window={win} fp8={fp8}")
-    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8)
+    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8, group32=(w.group == 32))
     _prefill(cache, x, w.ctx)
     cache.append(kv_dev(np.ascontiguousarray(x["k_raw"][:, :, w.ctx:])),
                  kv_dev(np.ascontiguousarray(x["v_raw"][:, :, w.ctx:])), dev_tensor(np.full(B, w.ctx, np.int32)))
@@ -177,8 +177,8 @@ def test_chunk_variant_full_size(kvq, name):
                 kc, vc = orc.fp8_encode(x["k"][b, g], fp8), orc.fp8_encode(x["v"][b, g], fp8)
                 hat[(b, g)] = (orc.fp8_decode(kc, fp8), orc.fp8_decode(vc, fp8))
             else:
-                kc, ks = orc.quantize(x["k"][b, g], 0)
-                vc, vs = orc.quantize(x["v"][b, g], 0)
+                kc, ks = orc.quantize(x["k"][b, g], w.group)
+                vc, vs = orc.quantize(x["v"][b, g], w.group)
                 hat[(b, g)] = (orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs))
             assert np.array_equal(dk[b, g], kc), f"codes of sequence {b}, KV head {g}"
         kh, vh = hat[(b, g)]

@@ -109,8 +109,12 @@ FP8_E4M3 = Workload("fp8_e4m3", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1
 FP8_CHUNK = Workload("fp8_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512,
                      seed=10, extra={"fp8": "e4m3"})
 
+# The chunked-prefill step on group-32 scales (the Q8 layout of the decode
+# workload above).
+CHUNK_G32 = Workload("chunk_group32", 4, 32, 8, 128, 32, "contiguous", "bf16", 8192, 512, seed=11)
+
 ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
-                           BF16_SCALES, FP8_E4M3, FP8_CHUNK)}
+                           BF16_SCALES, FP8_E4M3, FP8_CHUNK, CHUNK_G32)}
 
 
 # ----------------------------------------------------------------------------
