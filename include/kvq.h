@@ -64,8 +64,7 @@ typedef enum {
  * page's own mismatch: the dequantization error can exceed half a step).  In
  * that mode k_scales / v_scales point to uint16 bf16 arrays of the same
  * shape (4-byte aligned, as every scale array must be: kernels read the
- * aligned word holding a scale).  Chunked attention supports the two
- * per-token modes.
+ * aligned word holding a scale).  Every entry point supports every mode.
  *
  * FP8 code formats (llama-gguf 0.14.0 src/model/kv_quantized.rs,
  * `KVCacheFormat::Fp8E4M3` / `Fp8E5M2`), set in the same field: each element
@@ -194,7 +193,9 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const vo
  * `forward_attention`, cache_offset = seq_len - q_len; combs-models kv.rs
  * `attend`); otherwise all ctx_lens[b] + n keys.  Both products run on
  * f16 MFMA with the codes as exact f16 values and the scales applied to the
- * fp32 scores and weights; bf16 output.
+ * fp32 scores and weights (group-32 K scales to the fp32 score accumulator
+ * group by group; group-32 V ratios to the f16 weights of each 32-dim output
+ * tile); bf16 output.
  *
  *   q        : device bf16 [B, H, n, D];  out : device bf16 [B, H, n, D]
  *   ctx_lens : device int32 [B], tokens cached before the chunk
@@ -205,7 +206,7 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const vo
  * Keys beyond the cache capacity do not exist: a query sees at most
  * min(ctx_lens[b] + n, capacity) keys.
  * Errors: INVALID_ARG, OUT_OF_RANGE, WORKSPACE, UNSUPPORTED (head_dim other
- * than 64 or 128, or group-32 scales), HIP.
+ * than 64 or 128), HIP.
  */
 kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_t n,
                                const int32_t* ctx_lens, int32_t causal, float attn_scale,
