@@ -64,7 +64,7 @@ typedef enum {
  * page's own mismatch: the dequantization error can exceed half a step).  In
  * that mode k_scales / v_scales point to uint16 bf16 arrays of the same
  * shape (4-byte aligned, as every scale array must be: kernels read the
- * aligned word holding a scale).  Every entry point supports every mode.
+ * aligned word holding a scale).  Every entry point accepts this mode.
  *
  * FP8 code formats (llama-gguf 0.14.0 src/model/kv_quantized.rs,
  * `KVCacheFormat::Fp8E4M3` / `Fp8E5M2`), set in the same field: each element
