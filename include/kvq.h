@@ -195,18 +195,22 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const vo
  * f16 MFMA with the codes as exact f16 values and the scales applied to the
  * fp32 scores and weights (group-32 K scales to the fp32 score accumulator
  * group by group; group-32 V ratios to the f16 weights of each 32-dim output
- * tile); bf16 output.
+ * tile); bf16 output.  Head dims 32 and 256 run instead as one decode per
+ * (sequence, query) over the keys that query sees (fp32 arithmetic, split
+ * partials in the workspace; batch * n at most 65535).
  *
  *   q        : device bf16 [B, H, n, D];  out : device bf16 [B, H, n, D]
  *   ctx_lens : device int32 [B], tokens cached before the chunk
  *   max_ctx_len_hint : host upper bound on ctx_lens; hint + n must fit the
  *              capacity
- *   workspace: kvq_workspace_size(cache, max_ctx_len_hint + n, n) bytes (the
- *              current kernel needs none: the size is 0 and NULL is accepted)
+ *   workspace: kvq_workspace_size(cache, max_ctx_len_hint + n, n) bytes
+ *              (kvq_workspace_size_window with the window): 0 for head dims
+ *              64 and 128, where NULL is accepted
  * Keys beyond the cache capacity do not exist: a query sees at most
  * min(ctx_lens[b] + n, capacity) keys.
- * Errors: INVALID_ARG, OUT_OF_RANGE, WORKSPACE, UNSUPPORTED (head_dim other
- * than 64 or 128), HIP.
+ * Errors: INVALID_ARG, OUT_OF_RANGE (batch * n above 65535 for head dims 32
+ * and 256), WORKSPACE, UNSUPPORTED (head_dim other than 32, 64, 128, 256),
+ * HIP.
  */
 kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_t n,
                                const int32_t* ctx_lens, int32_t causal, float attn_scale,

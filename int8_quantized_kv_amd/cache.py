@@ -162,7 +162,7 @@ class Int8KVCache:
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            workspace = self.workspace(max_ctx_len_hint + n, n)
+            workspace = self.workspace(max_ctx_len_hint + n, n, window)
         if window > 0:
             _k.kvq_attention_chunk_window(self.desc, q, n, ctx_lens, attn_scale, window, out, workspace,
                                           workspace.numel(), max_ctx_len_hint, stream)

@@ -120,6 +120,8 @@ size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_l
     return 0;
   }
   if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r), window).workspace;
+  if (!chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim))
+    return plan_chunk_generic(*c, max_seq_len, n_query, window).workspace;
   return chunk_workspace(*c, max_seq_len, n_query);
 }
 
@@ -264,8 +266,15 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
   if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
-  if (!chunk_supported(c->head_dim))
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported", who, c->head_dim);
+  if (!chunk_supported(c->head_dim)) {
+    if (!chunk_generic_supported(c->head_dim))
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported", who, c->head_dim);
+    const DecodePlan plan = plan_chunk_generic(*c, max_ctx_len_hint + n, n, window);
+    st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
+    if (st != KVQ_OK) return st;
+    return launch_chunk_generic(*c, plan, q, n, ctx_lens, causal, attn_scale, out, workspace, max_ctx_len_hint + n,
+                                static_cast<hipStream_t>(stream), window);
+  }
   st = check_split_workspace(chunk_workspace(*c, max_ctx_len_hint + n, n), workspace, workspace_bytes, who);
   if (st != KVQ_OK) return st;
   return launch_chunk(*c, q, n, ctx_lens, causal, attn_scale, out, workspace, max_ctx_len_hint,

@@ -27,7 +27,10 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
 
   const int hg = blockIdx.x;
   const int split = blockIdx.y;
-  const int b = blockIdx.z;  // the launch never sets longest_first for this kernel
+  const int v = blockIdx.z;  // the launch never sets longest_first for this kernel
+  int b, qi;
+  const int L = row_len(p, v, b, qi);
+  const int nq = p.chunk_n > 0 ? p.chunk_n : 1;
   const int kvh = hg / p.wg_per_kvh;
   const int H = p.num_heads;
   const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
@@ -36,7 +39,6 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const int sub = lane % LPT;
   const int slot = lane / LPT;
 
-  const int L = clamp_len(p, b);
   const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // first visible key
   const int t_begin = t_lo + split * p.split_len;
   const int nsg = split_count(L - t_lo, p.split_len);
@@ -48,7 +50,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   float qsum[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
-    const uint4* qp = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + sub * 16);
+    const uint4* qp =
+        reinterpret_cast<const uint4*>(p.q + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16);
     bf16x8_to_f32(qp[0], &q[j][0]);
     bf16x8_to_f32(qp[1], &q[j][8]);
     float s = 0.0f;
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
       acc = fmaf(sm_o[w][j][d], f, acc);
       lsum = fmaf(sm_l[w][j], f, lsum);
     }
-    const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + split;
+    const int64_t pidx = (static_cast<int64_t>(v) * H + h0 + j) * p.num_splits + split;
     p.part_o[pidx * D + d] = acc;
     if (d == 0) {
       p.part_ml[pidx * 2] = M;
@@ -189,12 +192,14 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
 // Log-sum-exp merge of the split partials of one (sequence, head); bf16 out.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D) {
   const int h = blockIdx.x;
-  const int b = blockIdx.y;
+  const int v = blockIdx.y;
+  int b, qi;
+  const int L = row_len(p, v, b, qi);
+  const int nq = p.chunk_n > 0 ? p.chunk_n : 1;
   const int H = p.num_heads;
-  const int L = clamp_len(p, b);
   const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // the splits start at the window
   const int ns = split_count(L - t_lo, p.split_len);
-  const int64_t base = (static_cast<int64_t>(b) * H + h) * p.num_splits;
+  const int64_t base = (static_cast<int64_t>(v) * H + h) * p.num_splits;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, p.part_ml[(base + s) * 2]);
   float den = 0.0f;
@@ -208,8 +213,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
       const float ms = p.part_ml[(base + s) * 2];
       if (ms != -INFINITY) num = fmaf(p.part_o[(base + s) * D + d], exp2f(ms - M), num);
     }
-    const float v = den > 0.0f ? num / den : 0.0f;
-    p.out[(static_cast<int64_t>(b) * H + h) * D + d] = f32_to_bf16_rne(v);
+    const float val = den > 0.0f ? num / den : 0.0f;
+    p.out[((static_cast<int64_t>(b) * H + h) * nq + qi) * D + d] = f32_to_bf16_rne(val);
   }
 }
 
@@ -350,7 +355,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
     kvq_status st = launch_append(c, new_k, new_v, new_dtype, 1, seq_lens, stream, true);
     if (st != KVQ_OK) return st;
   }
-  DecodeParams p;
+  DecodeParams p{};  // (chunk mode off)
   p.k_codes = c.k_codes;
   p.v_codes = c.v_codes;
   p.k_scales = c.k_scales;
@@ -405,6 +410,97 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
     if (e != hipSuccess)
       return fail(KVQ_ERR_HIP, "kvq_attention_decode: merge launch failed: %s", hipGetErrorString(e));
   }
+  return KVQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Chunked prefill through the generic kernel, for head sizes the MFMA chunk
+// kernel does not take: each (sequence, query) pair is one grid row, a decode
+// over the keys that query sees (bottom-right causal, optionally a sliding
+// window), with its own split partials and merge.
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int D, int HPW>
+void launch_generic_modes(int sm, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
+  auto go = [&](auto smc) {
+    constexpr int SM = decltype(smc)::value;
+    if (paged) hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, true>), grid, dim3(kThreads), 0, st, p);
+    else hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, false>), grid, dim3(kThreads), 0, st, p);
+  };
+  switch (sm) {
+    case kSmGroup32: go(std::integral_constant<int, kSmGroup32>{}); break;
+    case kSmTokenBf16: go(std::integral_constant<int, kSmTokenBf16>{}); break;
+    case kSmFp8E4M3: go(std::integral_constant<int, kSmFp8E4M3>{}); break;
+    case kSmFp8E5M2: go(std::integral_constant<int, kSmFp8E5M2>{}); break;
+    default: go(std::integral_constant<int, kSmToken>{}); break;
+  }
+}
+
+template <int D>
+void launch_generic_hpw(int hpw, int sm, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
+  if (hpw == 4) launch_generic_modes<D, 4>(sm, paged, p, grid, st);
+  else if (hpw == 2) launch_generic_modes<D, 2>(sm, paged, p, grid, st);
+  else launch_generic_modes<D, 1>(sm, paged, p, grid, st);
+}
+
+kvq_cache rows_as_batch(const kvq_cache& c, int n) {
+  kvq_cache cv = c;
+  cv.batch = c.batch * n;
+  return cv;
+}
+
+}  // namespace
+
+bool chunk_generic_supported(int head_dim) { return head_dim == 32 || head_dim == 256; }
+
+DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int window) {
+  return plan_decode(rows_as_batch(c, n), max_total_len, RecentGeom(), window);
+}
+
+kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q, int n,
+                                const int32_t* ctx_lens, int causal, float attn_scale, uint16_t* out, void* ws,
+                                int max_total_len, hipStream_t stream, int window) {
+  const int64_t rows = static_cast<int64_t>(c.batch) * n;
+  if (rows > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: batch * n too large (%lld)",
+                                static_cast<long long>(rows));
+  DecodeParams p{};
+  p.k_codes = c.k_codes;
+  p.v_codes = c.v_codes;
+  p.k_scales = c.k_scales;
+  p.v_scales = c.v_scales;
+  p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
+  p.q = q;
+  const size_t partials = static_cast<size_t>(rows) * c.num_heads * plan.num_splits;
+  char* w = static_cast<char*>(ws);
+  p.counters = reinterpret_cast<int32_t*>(w);
+  p.part_ml = reinterpret_cast<float*>(w + plan.counter_bytes);
+  p.part_o = reinterpret_cast<float*>(w + plan.counter_bytes + align_up(partials * 2 * sizeof(float), 256));
+  p.out = out;
+  p.geom = geom_of(c);
+  p.num_heads = c.num_heads;
+  p.groups = scales_per_row(c);
+  p.split_len = plan.split_len;
+  p.num_splits = plan.num_splits;
+  const int cap = capacity_of(c);
+  p.len_cap = max_total_len < cap ? max_total_len : cap;
+  p.wg_per_kvh = (c.num_heads / c.num_kv_heads) / plan.heads_per_wg;
+  p.window = window;
+  p.scale_log2 = attn_scale * kLog2e;
+  p.chunk_n = n;
+  p.chunk_causal = causal || window > 0 ? 1 : 0;
+  p.ctx_lens = ctx_lens;
+  const dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, static_cast<unsigned>(rows));
+  if (grid.y > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: grid too large");
+  const bool paged = c.layout == KVQ_LAYOUT_PAGED;
+  if (c.head_dim == 32) launch_generic_hpw<32>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream);
+  else launch_generic_hpw<256>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(c.num_heads, static_cast<unsigned>(rows)),
+                     dim3(c.head_dim < 256 ? c.head_dim : 256), 0, stream, p, c.head_dim);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: merge launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;
 }
 

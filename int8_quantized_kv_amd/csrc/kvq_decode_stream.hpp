@@ -80,6 +80,12 @@ struct DecodeParams {
   // (L - 1 - window, L - 1]
   int32_t window;
   int32_t scale_bf16;        // per-token scales stored as bf16
+  // chunked prefill through the generic kernel (chunk_n > 0): grid z runs over
+  // (sequence b, query i) pairs, b * chunk_n + i, each a decode over the keys
+  // query i sees; q and out are [B, H, chunk_n, D]
+  int32_t chunk_n;
+  int32_t chunk_causal;      // query i sees keys t <= ctx_lens[b] + i (else all ctx + n)
+  const int32_t* ctx_lens;   // [B], tokens cached before the chunk
 };
 
 namespace {
@@ -236,6 +242,22 @@ __host__ __device__ inline int split_count(int len, int split_len) {
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   int L = p.seq_lens[b];
   return L < 0 ? 0 : (L > p.len_cap ? p.len_cap : L);
+}
+
+// The sequence b and query qi of grid row v, and the keys that query sees:
+// decode, v = b; chunk mode, v = b * chunk_n + qi.
+__device__ __forceinline__ int row_len(const DecodeParams& p, int v, int& b, int& qi) {
+  if (p.chunk_n == 0) {
+    b = v;
+    qi = 0;
+    return clamp_len(p, b);
+  }
+  b = v / p.chunk_n;
+  qi = v % p.chunk_n;
+  int L0 = p.ctx_lens[b];
+  L0 = L0 < 0 ? 0 : (L0 > p.len_cap ? p.len_cap : L0);
+  const int L = p.chunk_causal ? L0 + qi + 1 : L0 + p.chunk_n;
+  return L > p.len_cap ? p.len_cap : L;
 }
 
 // The sequence a workgroup serves.  With longest_first set (batch at most NT),

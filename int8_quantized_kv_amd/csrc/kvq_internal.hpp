@@ -99,6 +99,14 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
 // ---- chunked prefill --------------------------------------------------------
 bool chunk_supported(int head_dim);
 size_t chunk_workspace(const kvq_cache& c, int max_total_len, int n);
+// Head sizes the MFMA chunk kernel does not take (32, 256) go through the
+// decode path's generic kernel, one grid row per (sequence, query), with
+// split partials in the workspace.
+bool chunk_generic_supported(int head_dim);
+DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int window);
+kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q, int n,
+                                const int32_t* ctx_lens, int causal, float attn_scale, uint16_t* out, void* ws,
+                                int max_total_len, hipStream_t stream, int window);
 // window > 0: sliding window (implies causal).
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens,
                         int causal, float attn_scale, uint16_t* out, void* ws, int max_ctx_len,

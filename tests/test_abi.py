@@ -183,9 +183,9 @@ def test_chunk_and_dequant_argument_errors():
         kvq.KVQ_ERR_INVALID_ARG
     assert _status("kvq_attention_chunk", d, FAKE, 8, FAKE, 1, float("nan"), FAKE, FAKE, 1 << 30, 8, None)[0] == \
         kvq.KVQ_ERR_INVALID_ARG
-    # head sizes other than 64 / 128 have no chunk kernel
-    d256 = ctypes.byref(_desc(head_dim=256))
-    assert _status("kvq_attention_chunk", d256, FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
+    # head sizes other than 32, 64, 128 and 256 have no chunk kernel
+    d96 = ctypes.byref(_desc(head_dim=96))
+    assert _status("kvq_attention_chunk", d96, FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
         kvq.KVQ_ERR_UNSUPPORTED
     assert _status("kvq_dequant", d, 2, FAKE, 0, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG
     assert _status("kvq_dequant", d, 0, FAKE, 3, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG

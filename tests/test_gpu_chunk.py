@@ -180,3 +180,54 @@ def test_chunk_group32(kvq, D, H, KVH, ctx, n, causal, paged, window):
     ref = orc.attention_chunk(qv, orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs), ctx, causal, scale,
                               window=window)
     assert_attention_close(to_host_bits(out), ref, "chunk group-32")
+
+
+GENERIC_CASES = [
+    # D, H, KVH, ctx_lens, n, causal, paged, window, mode
+    (256, 16, 4, [0, 100], 37, True, False, 0, "token"),
+    (256, 8, 2, [300], 20, False, True, 0, "token"),
+    (32, 8, 2, [513, 64], 45, True, False, 0, "token"),
+    (32, 4, 4, [90], 33, True, True, 17, "token"),
+    (256, 16, 4, [200], 30, True, False, 0, "group32"),
+    (32, 8, 2, [130, 7], 25, True, False, 0, "bf16"),
+    (256, 8, 2, [150], 40, True, True, 64, "e4m3"),
+    (32, 8, 2, [70], 19, False, False, 0, "e5m2"),
+]
+
+
+@pytest.mark.parametrize("D,H,KVH,ctx,n,causal,paged,window,mode", GENERIC_CASES)
+def test_chunk_generic_head_dims(kvq, D, H, KVH, ctx, n, causal, paged, window, mode):
+    """head_dim 32 and 256 have no MFMA chunk kernel: each (sequence, query)
+    pair runs as a decode over the keys it sees, with the same masks."""
+    import torch
+    log(f"chunk generic: D={D} H={H} KVH={KVH} ctx={ctx} n={n} causal={causal} paged={paged} w={window} {mode}")
+    B = len(ctx)
+    T = max(ctx) + n
+    rng = np.random.default_rng(D + n + paged + window + len(mode))
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "bf16", scale=1.5)
+    qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, n, D))
+    kw = dict(group32=mode == "group32", scale_bf16=mode == "bf16", fp8=mode if mode in ("e4m3", "e5m2") else None)
+    if paged:
+        table, npages = random_block_table(rng, [T] * B)
+        cache = kvq.Int8KVCache(B, H, KVH, D, num_pages=npages, block_table=dev_tensor(table), fill=0, **kw)
+    else:
+        cache = kvq.Int8KVCache(B, H, KVH, D, max_len=T, fill=0, **kw)
+    cache.append(kv_dev(x["k_raw"]), kv_dev(x["v_raw"]), dev_tensor(np.zeros(B, np.int32)))
+    scale = 1.0 / np.sqrt(D)
+    out = cache.chunk(bf16_dev(qb), dev_tensor(np.asarray(ctx, np.int32)), causal, scale, max(ctx), window=window)
+    torch.cuda.synchronize()
+    if mode in ("e4m3", "e5m2"):
+        kh = orc.fp8_decode(orc.fp8_encode(x["k"], mode), mode)
+        vh = orc.fp8_decode(orc.fp8_encode(x["v"], mode), mode)
+    elif mode == "bf16":
+        kc, ksb = orc.quantize_bf16_scale(x["k"])
+        vc, vsb = orc.quantize_bf16_scale(x["v"])
+        kh = orc.dequantize_exact(kc, orc.bf16_bits_to_f32(ksb))
+        vh = orc.dequantize_exact(vc, orc.bf16_bits_to_f32(vsb))
+    else:
+        grp = 32 if mode == "group32" else 0
+        kc, ks = orc.quantize(x["k"], grp)
+        vc, vs = orc.quantize(x["v"], grp)
+        kh, vh = orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs)
+    ref = orc.attention_chunk(qv, kh, vh, ctx, causal, scale, window=window)
+    assert_attention_close(to_host_bits(out), ref, f"chunk generic D={D} {mode}")
