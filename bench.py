@@ -678,7 +678,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
-                                                            "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32"])
+                                                            "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32",
+                                                            "tiny_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
