@@ -307,7 +307,9 @@ kvq_status kvq_append_recent(const kvq_cache* cache, const kvq_recent* recent, c
  * dequantized, then the recent rows).  The ring is one more split of the
  * split-K launch.  seq_lens[b] is clamped to [0, min(hint, capacity of the
  * INT8 cache)].  Workspace: kvq_workspace_size_recent(cache, recent, hint).
- * Errors: those of kvq_attention_decode; UNSUPPORTED for head_dim 256.
+ * Head dims 64 and 128 run on the streaming kernel; 32 and 256 on the
+ * generic one, whose ring is a second loop after the INT8 rows.
+ * Errors: those of kvq_attention_decode.
  */
 kvq_status kvq_attention_decode_recent(const kvq_cache* cache, const kvq_recent* recent,
                                        const uint16_t* q, const int32_t* seq_lens, float attn_scale,
@@ -338,6 +340,31 @@ kvq_status kvq_append_decode_recent(const kvq_cache* cache, const kvq_recent* re
 kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, int32_t which,
                               const int32_t* seq_lens, int32_t out_dtype, void* out, int32_t out_len,
                               void* stream);
+
+/*
+ * kvq_attention_chunk_recent — chunked prefill over a hybrid cache: the n
+ * chunk rows are already appended (kvq_append_recent), so the cache holds
+ * L_b = ctx_lens[b] + n positions, INT8 below L_b - window and bf16 in the
+ * ring from there.  Query i at position ctx_lens[b] + i sees keys
+ * t <= ctx_lens[b] + i (bottom-right causal) of that `get_kv` view
+ * (abaddon kv_cache_quant_cuda.rs `OptimizedQuantizedKvCache::get_kv`).
+ * Runs as one decode per (sequence, query) through the generic kernel, any
+ * supported head_dim (32, 64, 128, 256); batch * n at most 65535.
+ *   q, out, ctx_lens, max_ctx_len_hint: as kvq_attention_chunk
+ *   workspace: kvq_workspace_size_chunk_recent(cache, recent,
+ *              max_ctx_len_hint + n, n) bytes
+ * Errors: those of kvq_attention_chunk, plus the recent descriptor's.
+ */
+kvq_status kvq_attention_chunk_recent(const kvq_cache* cache, const kvq_recent* recent, const uint16_t* q,
+                                      int32_t n, const int32_t* ctx_lens, float attn_scale, uint16_t* out,
+                                      void* workspace, size_t workspace_bytes, int32_t max_ctx_len_hint,
+                                      void* stream);
+
+/* Workspace bytes needed by kvq_attention_chunk_recent for n_query queries
+ * per sequence and max_seq_len = hint + n (0 on an invalid descriptor or
+ * argument). */
+size_t kvq_workspace_size_chunk_recent(const kvq_cache* cache, const kvq_recent* recent, int32_t max_seq_len,
+                                       int32_t n_query);
 
 /* Workspace bytes needed by kvq_attention_decode_recent and
  * kvq_append_decode_recent for lengths up to max_seq_len (0 on an invalid

@@ -156,11 +156,20 @@ class Int8KVCache:
               workspace: torch.Tensor | None = None, stream=None, window: int = 0):
         """q: bf16 [B, H, n, D]; returns bf16 [B, H, n, D].  window > 0:
         sliding window (implies causal)."""
-        if self.recent is not None:
-            raise NotImplementedError("chunked attention over a recent-window cache is not provided")
         n = q.shape[2]
         if out is None:
             out = torch.empty_like(q)
+        if self.recent is not None:
+            if window > 0:
+                raise NotImplementedError("a sliding window over a recent-window cache is not provided")
+            if not causal:
+                raise ValueError("chunked attention over a recent-window cache is causal")
+            if workspace is None:
+                nb = _k.kvq_workspace_size_chunk_recent(self.desc, self.recent, max_ctx_len_hint + n, n)
+                workspace = torch.zeros(max(nb, 1), dtype=torch.uint8, device=self.k_codes.device)
+            _k.kvq_attention_chunk_recent(self.desc, self.recent, q, n, ctx_lens, attn_scale, out, workspace,
+                                          workspace.numel(), max_ctx_len_hint, stream)
+            return out
         if workspace is None:
             workspace = self.workspace(max_ctx_len_hint + n, n, window)
         if window > 0:

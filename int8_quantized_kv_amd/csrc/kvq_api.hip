@@ -120,7 +120,7 @@ size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_l
     return 0;
   }
   if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r), window).workspace;
-  if (!chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim))
+  if (r || (!chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim)))
     return plan_chunk_generic(*c, max_seq_len, n_query, window).workspace;
   return chunk_workspace(*c, max_seq_len, n_query);
 }
@@ -162,8 +162,6 @@ kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, cons
                 capacity_of(*c));
   if (!decode_supported(c->head_dim))
     return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
-  if (r && c->head_dim > 128)
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: a recent window needs head_dim <= 128 (got %d)", who, c->head_dim);
   const RecentGeom rc = recent_of(r);
   const DecodePlan plan = plan_decode(*c, max_seq_len_hint, rc, window);
   st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
@@ -256,9 +254,10 @@ namespace {
 
 kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const int32_t* ctx_lens, int32_t causal,
                       float attn_scale, int32_t window, uint16_t* out, void* workspace, size_t workspace_bytes,
-                      int32_t max_ctx_len_hint, void* stream, const char* who) {
+                      int32_t max_ctx_len_hint, void* stream, const char* who, const kvq_recent* r = nullptr) {
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
+  if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
   if (!q || !ctx_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, ctx_lens and out must be non-NULL", who);
   if (n <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: n must be positive (got %d)", who, n);
   if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
@@ -266,14 +265,16 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
   if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
-  if (!chunk_supported(c->head_dim)) {
-    if (!chunk_generic_supported(c->head_dim))
+  // head dims without an MFMA chunk kernel, and every chunk over a hybrid
+  // cache, go through the generic kernel
+  if (r || !chunk_supported(c->head_dim)) {
+    if (!chunk_supported(c->head_dim) && !chunk_generic_supported(c->head_dim))
       return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported", who, c->head_dim);
     const DecodePlan plan = plan_chunk_generic(*c, max_ctx_len_hint + n, n, window);
     st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
     if (st != KVQ_OK) return st;
     return launch_chunk_generic(*c, plan, q, n, ctx_lens, causal, attn_scale, out, workspace, max_ctx_len_hint + n,
-                                static_cast<hipStream_t>(stream), window);
+                                static_cast<hipStream_t>(stream), window, recent_of(r));
   }
   st = check_split_workspace(chunk_workspace(*c, max_ctx_len_hint + n, n), workspace, workspace_bytes, who);
   if (st != KVQ_OK) return st;
@@ -289,6 +290,32 @@ KVQ_API kvq_status kvq_attention_chunk(const kvq_cache* c, const uint16_t* q, in
                                        size_t workspace_bytes, int32_t max_ctx_len_hint, void* stream) {
   return chunk_impl(c, q, n, ctx_lens, causal, attn_scale, 0, out, workspace, workspace_bytes, max_ctx_len_hint,
                     stream, "kvq_attention_chunk");
+}
+
+KVQ_API kvq_status kvq_attention_chunk_recent(const kvq_cache* c, const kvq_recent* r, const uint16_t* q, int32_t n,
+                                              const int32_t* ctx_lens, float attn_scale, uint16_t* out,
+                                              void* workspace, size_t workspace_bytes, int32_t max_ctx_len_hint,
+                                              void* stream) {
+  const char* who = "kvq_attention_chunk_recent";
+  if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+  return chunk_impl(c, q, n, ctx_lens, 1, attn_scale, 0, out, workspace, workspace_bytes, max_ctx_len_hint, stream,
+                    who, r);
+}
+
+KVQ_API size_t kvq_workspace_size_chunk_recent(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_len,
+                                               int32_t n_query) {
+  const char* who = "kvq_workspace_size_chunk_recent";
+  g_err[0] = '\0';
+  if (!r) {
+    fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
+    return 0;
+  }
+  if (check_cache(c, who, false) != KVQ_OK || check_recent(r, *c, who, false) != KVQ_OK) return 0;
+  if (max_seq_len <= 0 || n_query <= 0) {
+    fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
+    return 0;
+  }
+  return plan_chunk_generic(*c, max_seq_len, n_query, 0).workspace;
 }
 
 KVQ_API kvq_status kvq_attention_chunk_window(const kvq_cache* c, const uint16_t* q, int32_t n,

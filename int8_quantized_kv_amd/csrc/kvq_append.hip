@@ -70,14 +70,17 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const bool on = lane < D / EPL;
   float x[EPL];
   int pos;
+  // first position this call appends (with pos_from_lens the array holds
+  // lengths, and the one new row sits at length - 1)
+  const int start = p.pos_from_lens ? p.start_pos[b] - 1 : p.start_pos[b];
   if (p.mode == kEvict) {
     // ring row q = start - W + i leaves the window (i < min(n_new, W))
-    pos = p.start_pos[b] - p.rwin + i;
+    pos = start - p.rwin + i;
     if (pos < 0) return;
     const uint16_t* src = p.ring[side] + (static_cast<int64_t>(bh) * p.rcap + pos % p.rcap) * D;
     load_row_values<EPL>(src, lane, on, true, x);
   } else {
-    pos = p.pos_from_lens ? p.start_pos[b] - 1 : p.start_pos[b] + i;
+    pos = start + i;
     const size_t esize = p.in_bf16 ? 2 : 4;
     load_row_values<EPL>(static_cast<const char*>(p.src[side]) + static_cast<int64_t>(row) * D * esize, lane, on,
                          p.in_bf16 != 0, x);
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       // rows enter as bf16 values; those inside the new window go to the ring
 #pragma unroll
       for (int e = 0; e < EPL; ++e) x[e] = bf16_to_f32(f32_to_bf16_rne(x[e]));
-      if (pos >= p.start_pos[b] + p.n_new - p.rwin) {
+      if (pos >= start + p.n_new - p.rwin) {
         if (pos < 0) return;
         if (on) store_lane_bf16<EPL>(p.ring[side] + (static_cast<int64_t>(bh) * p.rcap + pos % p.rcap) * D, lane, x);
         return;

@@ -1,15 +1,16 @@
-// Decode attention: the generic kernel (head_dim 256) and its merge, the
-// split planner, and the launch of both kernels.  The streaming kernel
-// lives in kvq_decode_stream.hpp.
+// Decode attention: the generic kernel (decode at head_dim 256, chunk rows
+// the MFMA chunk kernel does not take) and its merge, the split planner, and
+// the launch of both kernels.  The streaming kernel lives in
+// kvq_decode_stream.hpp.
 #include "kvq_decode_stream.hpp"
 
 namespace kvq {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Generic kernel (any supported head_dim, used for 256): fp32 FMAs on codes
-// widened in registers, per-lane online softmax, partials merged by
-// decode_merge_kernel.
+// Generic kernel (any supported head_dim): fp32 FMAs on codes widened in
+// registers, per-lane online softmax, partials merged by decode_merge_kernel.
+// On a hybrid cache a second loop takes the bf16 ring rows of the split.
 // ---------------------------------------------------------------------------
 template <int D, int HPW, int SM, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p) {
@@ -44,7 +45,19 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const int nsg = split_count(L - t_lo, p.split_len);
   if (split >= nsg) return;
   const int t_end = split == nsg - 1 ? L : t_begin + p.split_len;  // the last split takes the remainder
-  const int npass = (t_end - t_begin + TPP - 1) / TPP;
+  // recent window: positions from L8 on are bf16 rows in the ring (decode:
+  // the last rwin of the sequence; chunk: of the ctx + n rows the cache holds)
+  int L8 = L;
+  if (p.rwin > 0) {
+    int Lc = L;
+    if (p.chunk_n > 0) {
+      const int c0 = min(max(p.ctx_lens[b], 0), p.len_cap);
+      Lc = min(c0 + p.chunk_n, p.len_cap);
+    }
+    L8 = max(Lc - p.rwin, 0);
+  }
+  const int t8_end = min(t_end, L8);  // INT8 tokens of this split end here
+  const int npass = t8_end > t_begin ? (t8_end - t_begin + TPP - 1) / TPP : 0;
 
   float q[HPW][16];
   float qsum[HPW];
@@ -80,8 +93,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
       // unconditional loads from a clamped row; out-of-range tokens are
       // discarded through their -inf score
       const int t = t_begin + (ip + u) * TPP + wave * TPW + slot;
-      ok[u] = t < t_end;
-      const int tc = min(t, t_end - 1);
+      ok[u] = t < t8_end;
+      const int tc = min(t, t8_end - 1);
       int64_t row;
       if constexpr (PAGED) {
         int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (tc >> 4)];
@@ -134,6 +147,44 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
         ws[j] += w;
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[j][e] = fmaf(w, cv[e], o[j][e]);
+      }
+    }
+  }
+
+  // ring rows (bf16 values, no scale and no offset): one token per lane slot
+  // and pass, the same online softmax
+  if (p.rwin > 0) {
+    const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
+    for (int tb = max(t_begin, L8); tb < t_end; tb += TPP) {
+      const int t = tb + wave * TPW + slot;
+      const bool okr = t < t_end;
+      const int64_t slot_row = ring0 + min(t, t_end - 1) % p.rcap;
+      const uint4* kr = reinterpret_cast<const uint4*>(p.rk + slot_row * D + sub * 16);
+      const uint4* vr = reinterpret_cast<const uint4*>(p.rv + slot_row * D + sub * 16);
+      float kx[16], vx[16];
+      bf16x8_to_f32(kr[0], &kx[0]);
+      bf16x8_to_f32(kr[1], &kx[8]);
+      bf16x8_to_f32(vr[0], &vx[0]);
+      bf16x8_to_f32(vr[1], &vx[8]);
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part = fmaf(q[j][e], kx[e], part);
+        const float sc = group_sum<LPT>(part) * p.scale_log2;
+        const float sj = okr ? sc : -INFINITY;
+        if (sj > m[j] + kLazy) {
+          const float alpha = exp2f(m[j] - sj);
+          l[j] *= alpha;
+          ws[j] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
+          m[j] = sj;
+        }
+        const float pj = okr ? exp2f(sj - m[j]) : 0.0f;
+        l[j] += pj;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[j][e] = fmaf(pj, vx[e], o[j][e]);
       }
     }
   }
@@ -226,10 +277,10 @@ int heads_per_wg(int gqa) {
 
 bool use_stream(int head_dim) { return head_dim <= 128; }
 
-int pass_tokens(int head_dim) {
+int pass_tokens(int head_dim, bool stream_kernel) {
   // tokens a workgroup consumes per step: whole 64-token wave blocks for the
   // streaming kernel, one pass of all waves for the generic kernel
-  return use_stream(head_dim) ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
+  return stream_kernel ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
 }
 
 template <int D, int HPW, int SM, bool PAGED>
@@ -296,17 +347,20 @@ bool decode_supported(int head_dim) {
   return head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
 }
 
-DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc, int window) {
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc, int window, bool generic) {
   DecodePlan pl;
+  const bool stream_kernel = !generic && use_stream(c.head_dim);
   // a sliding window bounds each sequence's range: the window rounded out to
   // whole blocks
   if (window > 0 && max_seq_len > window + kBlock - 1) max_seq_len = window + kBlock - 1;
-  // with a recent window the INT8 splits cover at most max_seq_len - W tokens
-  const int ring = rc.window > 0 ? 1 : 0;
+  // with a recent window the streaming kernel's INT8 splits cover at most
+  // max_seq_len - W tokens (the ring goes to the last split's workgroup); the
+  // generic kernel's splits cover ring rows too
+  const int ring = rc.window > 0 && stream_kernel ? 1 : 0;
   if (ring) max_seq_len = max_seq_len > rc.window ? max_seq_len - rc.window : 1;
   const int gqa = c.num_heads / c.num_kv_heads;
   pl.heads_per_wg = heads_per_wg(gqa);
-  const int step = pass_tokens(c.head_dim);
+  const int step = pass_tokens(c.head_dim, stream_kernel);
   // Aim at about one workgroup per compute unit (one round), in whole
   // workgroup passes.  When one round would need splits longer than 2048
   // tokens (large batches of long windows), take about four rounds instead,
@@ -334,9 +388,9 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   // Longest sequence first pays when workgroups are long (several rounds of
   // splits of 4096 tokens or more): ranking the lengths costs each workgroup
   // a read of the batch's lengths and about batch compare steps up front.
-  pl.longest_first = use_stream(c.head_dim) && c.batch > 1 && c.batch <= kLongestFirstMax && split >= 4096;
+  pl.longest_first = stream_kernel && c.batch > 1 && c.batch <= kLongestFirstMax && split >= 4096;
   const int forced_lf = env_int("KVQ_LONGEST_FIRST", -1);
-  if (forced_lf >= 0) pl.longest_first = forced_lf != 0 && use_stream(c.head_dim) && c.batch <= kLongestFirstMax;
+  if (forced_lf >= 0) pl.longest_first = forced_lf != 0 && stream_kernel && c.batch <= kLongestFirstMax;
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
   pl.counter_bytes = align_up(static_cast<size_t>(groups) * sizeof(int32_t), 256);
   pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
@@ -352,7 +406,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   const bool stream_kernel = use_stream(c.head_dim);
   if (append && !stream_kernel) {
     // the generic kernel has no fused path: append the row first
-    kvq_status st = launch_append(c, new_k, new_v, new_dtype, 1, seq_lens, stream, true);
+    kvq_status st = launch_append(c, new_k, new_v, new_dtype, 1, seq_lens, stream, true, rc);
     if (st != KVQ_OK) return st;
   }
   DecodeParams p{};  // (chunk mode off)
@@ -455,12 +509,12 @@ kvq_cache rows_as_batch(const kvq_cache& c, int n) {
 bool chunk_generic_supported(int head_dim) { return head_dim == 32 || head_dim == 256; }
 
 DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int window) {
-  return plan_decode(rows_as_batch(c, n), max_total_len, RecentGeom(), window);
+  return plan_decode(rows_as_batch(c, n), max_total_len, RecentGeom(), window, true);
 }
 
 kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q, int n,
                                 const int32_t* ctx_lens, int causal, float attn_scale, uint16_t* out, void* ws,
-                                int max_total_len, hipStream_t stream, int window) {
+                                int max_total_len, hipStream_t stream, int window, const RecentGeom& rc) {
   const int64_t rows = static_cast<int64_t>(c.batch) * n;
   if (rows > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: batch * n too large (%lld)",
                                 static_cast<long long>(rows));
@@ -490,11 +544,19 @@ kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, cons
   p.chunk_n = n;
   p.chunk_causal = causal || window > 0 ? 1 : 0;
   p.ctx_lens = ctx_lens;
+  p.rk = rc.k;
+  p.rv = rc.v;
+  p.rwin = rc.window;
+  p.rcap = rc.cap;
   const dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, static_cast<unsigned>(rows));
   if (grid.y > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: grid too large");
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  if (c.head_dim == 32) launch_generic_hpw<32>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream);
-  else launch_generic_hpw<256>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream);
+  switch (c.head_dim) {
+    case 32: launch_generic_hpw<32>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
+    case 64: launch_generic_hpw<64>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
+    case 128: launch_generic_hpw<128>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
+    default: launch_generic_hpw<256>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   hipLaunchKernelGGL(decode_merge_kernel, dim3(c.num_heads, static_cast<unsigned>(rows)),

@@ -87,7 +87,9 @@ bool decode_supported(int head_dim);
 // With a recent window the INT8 splits cover at most max_seq_len - window
 // tokens; the last one's workgroup also attends to the ring.
 // A sliding window (> 0) bounds each sequence's range to about the window.
-DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc = RecentGeom(), int window = 0);
+// generic: plan for the generic kernel at any head size (chunk rows).
+DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc = RecentGeom(), int window = 0,
+                       bool generic = false);
 // new_k / new_v non-null: fused append of one row per sequence at position
 // seq_lens[b] - 1 before the attention.
 kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q,
@@ -99,14 +101,16 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
 // ---- chunked prefill --------------------------------------------------------
 bool chunk_supported(int head_dim);
 size_t chunk_workspace(const kvq_cache& c, int max_total_len, int n);
-// Head sizes the MFMA chunk kernel does not take (32, 256) go through the
-// decode path's generic kernel, one grid row per (sequence, query), with
-// split partials in the workspace.
+// Head sizes the MFMA chunk kernel does not take (32, 256), and chunks over a
+// recent-window cache (any head size), go through the decode path's generic
+// kernel, one grid row per (sequence, query), with split partials in the
+// workspace.
 bool chunk_generic_supported(int head_dim);
 DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int window);
 kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q, int n,
                                 const int32_t* ctx_lens, int causal, float attn_scale, uint16_t* out, void* ws,
-                                int max_total_len, hipStream_t stream, int window);
+                                int max_total_len, hipStream_t stream, int window,
+                                const RecentGeom& rc = RecentGeom());
 // window > 0: sliding window (implies causal).
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens,
                         int causal, float attn_scale, uint16_t* out, void* ws, int max_ctx_len,

@@ -37,7 +37,8 @@ EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_append_decode", "kvq_atte
             "kvq_workspace_size", "kvq_cache_bytes", "kvq_last_error", "kvq_version",
             "kvq_append_recent", "kvq_attention_decode_recent", "kvq_append_decode_recent", "kvq_dequant_recent",
             "kvq_workspace_size_recent", "kvq_attention_decode_window", "kvq_append_decode_window",
-            "kvq_attention_chunk_window", "kvq_workspace_size_window")
+            "kvq_attention_chunk_window", "kvq_workspace_size_window", "kvq_attention_chunk_recent",
+            "kvq_workspace_size_chunk_recent")
 
 
 class KvqError(RuntimeError):
@@ -136,6 +137,10 @@ def _load():
     lib.kvq_dequant_recent.restype = I
     lib.kvq_workspace_size_recent.argtypes = [CP, RP, I]
     lib.kvq_workspace_size_recent.restype = ctypes.c_size_t
+    lib.kvq_attention_chunk_recent.argtypes = [CP, RP, P, I, P, ctypes.c_float, P, P, ctypes.c_size_t, I, P]
+    lib.kvq_attention_chunk_recent.restype = I
+    lib.kvq_workspace_size_chunk_recent.argtypes = [CP, RP, I, I]
+    lib.kvq_workspace_size_chunk_recent.restype = ctypes.c_size_t
     F = ctypes.c_float
     lib.kvq_attention_decode_window.argtypes = [CP, P, P, F, I, P, P, ctypes.c_size_t, I, P]
     lib.kvq_attention_decode_window.restype = I
@@ -286,6 +291,20 @@ def kvq_dequant_recent(cache: kvq_cache, recent, which: int, seq_lens, out_dtype
 
 def kvq_workspace_size_recent(cache: kvq_cache, recent, max_seq_len: int) -> int:
     n = _lib.kvq_workspace_size_recent(ctypes.byref(cache), _rp(recent), max_seq_len)
+    if n == 0 and kvq_last_error():
+        raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
+    return n
+
+
+def kvq_attention_chunk_recent(cache: kvq_cache, recent, q, n: int, ctx_lens, attn_scale: float, out, workspace,
+                               workspace_bytes: int, max_ctx_len_hint: int, stream=None):
+    _check(_lib.kvq_attention_chunk_recent(ctypes.byref(cache), _rp(recent), _ptr(q), n, _ptr(ctx_lens), attn_scale,
+                                           _ptr(out), _ptr(workspace), workspace_bytes, max_ctx_len_hint,
+                                           _stream(stream)))
+
+
+def kvq_workspace_size_chunk_recent(cache: kvq_cache, recent, max_seq_len: int, n_query: int) -> int:
+    n = _lib.kvq_workspace_size_chunk_recent(ctypes.byref(cache), _rp(recent), max_seq_len, n_query)
     if n == 0 and kvq_last_error():
         raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
     return n

@@ -215,16 +215,35 @@ def test_recent_argument_errors():
                            ("kvq_attention_decode_recent", (FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)),
                            ("kvq_append_decode_recent", (FAKE, FAKE, 0, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64,
                                                          None)),
-                           ("kvq_dequant_recent", (0, FAKE, 0, FAKE, 8, None))):
+                           ("kvq_dequant_recent", (0, FAKE, 0, FAKE, 8, None)),
+                           ("kvq_attention_chunk_recent", (FAKE, 8, FAKE, 0.1, FAKE, FAKE, 1 << 30, 8, None))):
             st, msg = _status(name, d, r, *args)
             assert st == kvq.KVQ_ERR_INVALID_ARG and word in msg, (name, msg)
     r = ctypes.byref(_recent())
     assert _status("kvq_attention_decode_recent", d, r, FAKE, FAKE, 0.1, FAKE, FAKE, ws - 1, 64, None)[0] == \
         kvq.KVQ_ERR_WORKSPACE
-    d256 = ctypes.byref(_desc(head_dim=256))
-    assert _status("kvq_attention_decode_recent", d256, r, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)[0] == \
+    d96 = ctypes.byref(_desc(head_dim=96))
+    assert _status("kvq_attention_decode_recent", d96, r, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)[0] == \
+        kvq.KVQ_ERR_UNSUPPORTED
+    assert _status("kvq_attention_chunk_recent", d96, r, FAKE, 8, FAKE, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
         kvq.KVQ_ERR_UNSUPPORTED
     assert _status("kvq_append_recent", d, r, FAKE, FAKE, 0, 65, FAKE, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
+
+
+def test_chunk_recent_workspace():
+    """Chunks over a hybrid cache run one decode per (sequence, query): the
+    workspace holds partials for batch * n rows, any n including 1, and the
+    descriptor is checked first."""
+    r = _recent(window=16, capacity=17)
+    one = kvq.kvq_workspace_size_chunk_recent(_desc(), r, 64, 1)
+    eight = kvq.kvq_workspace_size_chunk_recent(_desc(), r, 64, 8)
+    assert 0 < one < eight
+    for d in (32, 256):
+        assert kvq.kvq_workspace_size_chunk_recent(_desc(head_dim=d), r, 64, 8) > 0
+    with pytest.raises(kvq.KvqError, match="window"):
+        kvq.kvq_workspace_size_chunk_recent(_desc(), _recent(window=0), 64, 8)
+    with pytest.raises(kvq.KvqError, match="positive"):
+        kvq.kvq_workspace_size_chunk_recent(_desc(), r, 64, 0)
 
 
 def test_recent_workspace_is_the_int8_parts():

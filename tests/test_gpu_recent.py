@@ -141,6 +141,8 @@ DECODE_CASES = [
     (32, 4, 4, 0, 5, [5, 6, 90], False),
     (128, 24, 8, 0, 32, [40, 517], False),        # one head per workgroup
     (128, 64, 8, 0, 32, [77, 600], False),        # two workgroups per KV head
+    (256, 16, 4, 0, 16, [1, 17, 300, 1100], False),  # generic kernel: the ring is its second loop
+    (256, 8, 2, 32, 8, [9, 64, 600], True),
 ]
 
 
@@ -163,18 +165,19 @@ def test_decode_recent(kvq, D, H, KVH, group, W, lens, paged):
     assert_attention_close(to_host_bits(out), ref, "decode recent")
 
 
-@pytest.mark.parametrize("paged,group,dtype", [(False, 0, "bf16"), (True, 0, "f32"), (False, 32, "f32"),
-                                               (True, 32, "bf16")])
-def test_fused_recent_equals_two_steps(kvq, paged, group, dtype):
+@pytest.mark.parametrize("paged,group,dtype,D", [(False, 0, "bf16", 128), (True, 0, "f32", 128),
+                                                 (False, 32, "f32", 128), (True, 32, "bf16", 128),
+                                                 (False, 0, "bf16", 256), (True, 32, "f32", 256)])
+def test_fused_recent_equals_two_steps(kvq, paged, group, dtype, D):
     """kvq_append_decode_recent == kvq_append_recent (one row at L - 1) then
     kvq_attention_decode_recent, bit for bit (outputs, codes, scales, rings),
     and both match the oracle's state after the step."""
     import torch
     lens = [1, 2, 16, 17, 18, 100, 1500, 2049]
     W = 16
-    B, H, KVH, D = len(lens), 32, 8, 128
+    B, H, KVH = len(lens), 32, 8
     T = max(lens)
-    log(f"fused recent: paged={paged} group={group} dtype={dtype} lens={lens}")
+    log(f"fused recent: paged={paged} group={group} dtype={dtype} D={D} lens={lens}")
     rng = np.random.default_rng(7 + paged + group)
     x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), dtype)
     qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, D))
@@ -254,3 +257,57 @@ def test_recent_longest_first_and_splits(kvq, monkeypatch):
     ref = orc.attention_decode_recent(qv[live], [r for r, L in zip(refs, lens) if L > 0], 0.088)
     for env, o in outs.items():
         assert_attention_close(o[live], ref, f"splits {env}")
+
+
+CHUNK_CASES = [
+    # D, H, KVH, group, W, ctx_lens, n, paged
+    (32, 4, 4, 0, 8, [0, 5, 40], 13, False),
+    (64, 8, 2, 0, 16, [3, 100, 0], 37, False),
+    (128, 32, 8, 32, 64, [0, 200, 1000], 70, True),
+    (128, 16, 8, 0, 128, [10, 300], 5, False),       # chunk shorter than the window
+    (256, 16, 4, 0, 32, [7, 500], 45, False),
+    (256, 8, 2, 32, 16, [0, 90], 16, True),
+]
+
+
+@pytest.mark.parametrize("D,H,KVH,group,W,ctx,n,paged", CHUNK_CASES)
+def test_chunk_recent(kvq, D, H, KVH, group, W, ctx, n, paged, monkeypatch):
+    """Chunked prefill on a hybrid cache: the chunk goes in through
+    kvq_append_recent (state checked against the oracle), then
+    kvq_attention_chunk_recent against the oracle's causal chunk attention
+    over each sequence's get_kv view, with the planner's splits and with
+    short forced ones (splits holding INT8 and ring rows, and splits of ring
+    rows only)."""
+    import torch
+    B = len(ctx)
+    lens = [c + n for c in ctx]
+    T = max(lens)
+    log(f"chunk recent: D={D} H={H} KVH={KVH} group={group} W={W} ctx={ctx} n={n} paged={paged}")
+    rng = np.random.default_rng(D * 7 + W + n + group + paged)
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "bf16")
+    qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, n, D))
+    refs = _oracle_states(x, ctx, W, group)
+    cache, table = _new_cache(kvq, B, H, KVH, D, group, W, W + 5, paged, T, rng, lens)
+    _write_state(cache, table, refs)
+    rows = lambda a: np.ascontiguousarray(np.stack([a[b, :, c:c + n] for b, c in enumerate(ctx)]))
+    ctx_dev = dev_tensor(np.asarray(ctx, np.int32))
+    cache.append(kv_dev(rows(x["k_raw"])), kv_dev(rows(x["v_raw"])), ctx_dev)
+    for b, ref in enumerate(refs):
+        ref.append(x["k"][b, :, ctx[b]:lens[b]], x["v"][b, :, ctx[b]:lens[b]])
+    _check_state(cache, table, refs, "chunk append")
+    scale = 1.0 / np.sqrt(D)
+    outs = []
+    for split in ("0", "64"):
+        monkeypatch.setenv("KVQ_SPLIT_LEN", split)
+        out = cache.chunk(bf16_dev(qb), ctx_dev, True, scale, max(ctx))
+        torch.cuda.synchronize()
+        outs.append(to_host_bits(out))
+    kh = np.zeros((B, KVH, T, D))
+    vh = np.zeros((B, KVH, T, D))
+    for b, ref in enumerate(refs):
+        k, v = ref.kv()
+        kh[b, :, :lens[b]], vh[b, :, :lens[b]] = k, v
+    want = orc.attention_chunk(qv, kh, vh, ctx, True, scale)
+    for o, split in zip(outs, ("default", "64")):
+        assert np.all(np.isfinite(orc.bf16_bits_to_f32(o)))
+        assert_attention_close(o, want, f"chunk recent, splits {split}")
