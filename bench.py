@@ -14,8 +14,9 @@ chunked-prefill attention for the 512 queries (kvq_attention_chunk); the
 figure is TFLOP/s over the visible keys only.
 
 The other workloads (recent_window, sliding_decode, sliding_chunk,
-bf16_scales, fp8_e4m3, q8_group32, paged_decode) are the same steps on the
-cache variants their names give; ``--help`` lists them.
+bf16_scales, fp8_e4m3, fp8_chunk, chunk_group32, recent_chunk, q8_group32,
+paged_decode, tiny_decode) are the same steps on the cache variants their
+names give; ``--help`` lists them.
 
 Inputs are seeded synthetic data, already resident in HBM when timing starts.
 Prints one JSON line (see --help).  ``--gpus N`` with N > 1 is refused: this
@@ -108,12 +109,20 @@ def chunk_counts(w: wl.Workload) -> dict:
     flops = 4 * B * H * D * visible
     L = L0 + n
     rows = L - max(0, L0 - win + 1) if win else L    # keys some query of the chunk sees
-    codes = 2 * B * KVH * rows * D
     G = D // 32 if w.group == 32 else 1
-    scales = 0 if w.extra.get("fp8") else 2 * B * KVH * rows * 4 * G
+    scale_b = 0 if w.extra.get("fp8") else 4 * G
     qo = 2 * B * H * n * D * 2
-    append = 2 * B * KVH * n * (D * 2 + D + (0 if w.extra.get("fp8") else 4 * G))
-    return {"flops": flops, "chunk_bytes": codes + scales + qo, "step_bytes": codes + scales + qo + append}
+    rw = w.extra.get("window", 0)
+    if rw:
+        # hybrid cache: INT8 rows below L - W, bf16 ring rows above
+        kv = 2 * B * KVH * ((L - rw) * (D + scale_b) + rw * D * 2)
+        # append: the input rows; the n rows leaving the window quantized
+        # (ring rows read, codes and scales written); the last W stored in the ring
+        append = 2 * B * KVH * (n * D * 2 + min(n, rw) * D * 2 + n * (D + scale_b) + rw * D * 2)
+        return {"flops": flops, "chunk_bytes": kv + qo, "step_bytes": kv + qo + append}
+    kv = 2 * B * KVH * rows * (D + scale_b)
+    append = 2 * B * KVH * n * (D * 2 + D + scale_b)
+    return {"flops": flops, "chunk_bytes": kv + qo, "step_bytes": kv + qo + append}
 
 
 # ----------------------------------------------------------------------------
@@ -296,6 +305,10 @@ def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
         if fp8:
             kh = orc.fp8_decode(orc.fp8_encode(x["k"][b, g], fp8), fp8)
             vh = orc.fp8_decode(orc.fp8_encode(x["v"][b, g], fp8), fp8)
+        elif w.extra.get("window"):  # the hybrid cache's get_kv view
+            rc = orc.RecentWindowCache(1, w.head_dim, w.extra["window"], w.group)
+            rc.append(x["k"][b, g:g + 1], x["v"][b, g:g + 1])
+            kh, vh = (a[0] for a in rc.kv())
         else:
             kc, ks = orc.quantize(x["k"][b, g], w.group)
             vc, vs = orc.quantize(x["v"][b, g], w.group)
@@ -335,7 +348,9 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     B, KVH, T, D = x["k"].shape
     dev = torch.device("cuda")
     fp8 = w.extra.get("fp8")
-    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8, group32=(w.group == 32))
+    rw = w.extra.get("window", 0)
+    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8, group32=(w.group == 32),
+                            recent_window=rw)
 
     def up(a):
         t = torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a))
@@ -374,7 +389,7 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
         wall = time.perf_counter() - t0
         k_ms = time_calls(kernel_pass, args.kernel_reps, stream, torch)
     cnt = chunk_counts(w)
-    kname = "kvq_attention_chunk_window" if win else "kvq_attention_chunk"
+    kname = "kvq_attention_chunk_window" if win else ("kvq_attention_chunk_recent" if rw else "kvq_attention_chunk")
     tflops = cnt["flops"] / (step_ms * 1e-3) / 1e12
     k_tflops = cnt["flops"] / (k_ms * 1e-3) / 1e12
     log(f"step {step_ms * 1e3:.1f} us ({tflops:.1f} TFLOP/s), wall {wall * 1e3 / args.steps:.3f} ms/step; "
@@ -386,9 +401,11 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
         cpu = cpu_baseline_chunk(w, x)
     codes_what = (f"FP8 {fp8.upper()} codes" if fp8 else
                   "group-32 fp32 scales" if w.group == 32 else "per-token fp32 scales")
+    if rw:
+        codes_what += f", last {rw} tokens bf16 (recent window)"
     result = {
         "metric": ("FP8" if fp8 else "INT8") + "-KV chunked-prefill attention: MFMA TFLOP/s over visible keys"
-                  + (" (sliding window)" if win else ""),
+                  + (" (sliding window)" if win else "") + (" (recent window)" if rw else ""),
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -679,7 +696,7 @@ def main():
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
                                                             "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32",
-                                                            "tiny_decode"])
+                                                            "recent_chunk", "tiny_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -719,7 +736,7 @@ def main():
     if w.name == "sliding_decode":
         run_sliding(args, w, kvq, torch, stream)
         return
-    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk", "chunk_group32"):
+    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk", "chunk_group32", "recent_chunk"):
         run_chunk(args, w, kvq, torch, stream)
         return
     if w.name == "paged_decode":

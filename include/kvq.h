@@ -348,9 +348,13 @@ kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, 
  * ring from there.  Query i at position ctx_lens[b] + i sees keys
  * t <= ctx_lens[b] + i (bottom-right causal) of that `get_kv` view
  * (abaddon kv_cache_quant_cuda.rs `OptimizedQuantizedKvCache::get_kv`).
- * Runs as one decode per (sequence, query) through the generic kernel, any
- * supported head_dim (32, 64, 128, 256); batch * n at most 65535.
- *   q, out, ctx_lens, max_ctx_len_hint: as kvq_attention_chunk
+ * head_dim 64 and 128: the MFMA chunk kernel attends to the INT8 keys, a
+ * second launch to the ring rows, and a third merges the two partial
+ * softmaxes; head_dim 32 and 256: one decode per (sequence, query) through
+ * the generic kernel.  batch * n at most 65535.
+ *   q, out, ctx_lens, max_ctx_len_hint: as kvq_attention_chunk; ctx_lens[b]
+ *              must not exceed the hint (at head_dim 64 and 128 a larger
+ *              length is taken as the hint)
  *   workspace: kvq_workspace_size_chunk_recent(cache, recent,
  *              max_ctx_len_hint + n, n) bytes
  * Errors: those of kvq_attention_chunk, plus the recent descriptor's.

@@ -100,6 +100,8 @@ class Int8KVCache:
             n = _k.kvq_workspace_size_window(self.desc, max_seq_len, n_query, window)
         elif self.recent is not None and n_query == 1:
             n = _k.kvq_workspace_size_recent(self.desc, self.recent, max_seq_len)
+        elif self.recent is not None:  # a chunk of n_query queries
+            n = _k.kvq_workspace_size_chunk_recent(self.desc, self.recent, max_seq_len, n_query)
         else:
             n = _k.kvq_workspace_size(self.desc, max_seq_len, n_query)
         return torch.zeros(max(n, 1), dtype=torch.uint8, device=self.k_codes.device)

@@ -120,7 +120,7 @@ size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_l
     return 0;
   }
   if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r), window).workspace;
-  if (r || (!chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim)))
+  if (!chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim))
     return plan_chunk_generic(*c, max_seq_len, n_query, window).workspace;
   return chunk_workspace(*c, max_seq_len, n_query);
 }
@@ -265,8 +265,16 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
   if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
-  // head dims without an MFMA chunk kernel, and every chunk over a hybrid
-  // cache, go through the generic kernel
+  // a hybrid cache at an MFMA head size: the MFMA kernel takes the INT8
+  // keys and the generic kernel the ring rows
+  if (r && chunk_supported(c->head_dim)) {
+    const DecodePlan plan = plan_chunk_hybrid(*c, n, r->window);
+    st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
+    if (st != KVQ_OK) return st;
+    return launch_chunk_generic(*c, plan, q, n, ctx_lens, 1, attn_scale, out, workspace, max_ctx_len_hint + n,
+                                static_cast<hipStream_t>(stream), 0, recent_of(r), true);
+  }
+  // head dims without an MFMA chunk kernel go through the generic kernel
   if (r || !chunk_supported(c->head_dim)) {
     if (!chunk_supported(c->head_dim) && !chunk_generic_supported(c->head_dim))
       return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported", who, c->head_dim);
@@ -315,6 +323,7 @@ KVQ_API size_t kvq_workspace_size_chunk_recent(const kvq_cache* c, const kvq_rec
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
   }
+  if (chunk_supported(c->head_dim)) return plan_chunk_hybrid(*c, n_query, r->window).workspace;
   return plan_chunk_generic(*c, max_seq_len, n_query, 0).workspace;
 }
 

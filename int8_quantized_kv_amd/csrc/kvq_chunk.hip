@@ -80,6 +80,15 @@ struct ChunkParams {
   int32_t causal;
   int32_t window;       // sliding window (0: none): query p sees keys in (p - window, p]
   float scale_log2;     // attn_scale * log2(e)
+  // recent-window cache (rwin > 0): only the INT8 keys, below L - rwin, are
+  // attended here; a query that also sees ring rows leaves an unnormalised
+  // split partial (m, l, o) at slot part_slot of part_stride per (sequence,
+  // query, head) instead of its output
+  int32_t rwin;
+  int32_t len_cap;      // hint + n when rwin > 0 (ctx_lens clamp to the hint)
+  int32_t part_stride, part_slot;
+  float* part_o;
+  float* part_ml;
 };
 
 // LDS tile geometry for TOK tokens.  K rows hold D f16 values and are padded
@@ -224,9 +233,10 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   const int g = bg % p.geom.kvh;
   const int b = bg / p.geom.kvh;
 
-  const int cap = capacity(p.geom);
-  const int L0 = min(max(p.ctx_lens[b], 0), cap);
-  const int Ltot = min(L0 + p.n, cap);   // keys that exist
+  const int cap = p.rwin > 0 ? min(capacity(p.geom), p.len_cap) : capacity(p.geom);
+  const int L0 = min(max(p.ctx_lens[b], 0), p.rwin > 0 ? cap - p.n : cap);
+  // keys attended here: all that exist, or the INT8 ones of a hybrid cache
+  const int Ltot = p.rwin > 0 ? max(min(L0 + p.n, cap) - p.rwin, 0) : min(L0 + p.n, cap);
   const int items = p.hpg * p.nblk;
 
   int wg_end = 0;
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     wg_lo = max(wg_lo, 0);
   }
   const int tbase = (wg_lo / kCkTile) * kCkTile;  // token offset of tile 0
-  const int ntiles = (wg_end - tbase + kCkTile - 1) / kCkTile;
+  const int ntiles = max((wg_end - tbase + kCkTile - 1) / kCkTile, 0);
 
   const int item = wg * kCkWaves + wave;
   const bool active = item < items;
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
         const bool kside = j < kChunks;
         const int id = kside ? j : j - kChunks;
         int t = t0 + id / kChunksPerRow;
-        t = t < Ltot ? t : Ltot - 1;
+        t = max(t < Ltot ? t : Ltot - 1, 0);  // (row 0 stands in when no key exists)
         const int64_t row = row_of<PAGED>(p, b, g, t);
         lreg[i] = *reinterpret_cast<const uint4*>((kside ? p.k_codes : p.v_codes) + row * D + 16 * (id % kChunksPerRow));
       }
@@ -637,6 +647,27 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   // FP8 operands are the values themselves
   const float big = FP8 || G32 ? 1.0f : 16777216.0f;
   const float off = FP8 || G32 ? 0.0f : 128.0f * w_tot;
+  const int q0 = max(p.n - p.rwin, 0);  // the last rwin queries see ring rows (L0 <= hint)
+  if (p.rwin > 0 && qi >= q0) {
+    // the query also sees ring rows: a split partial in log2 units
+    // (w / sV = 2^(score - m_run), so l_tot and the weighted value sum are
+    // relative to m_run), rows (b, qi - q0)
+    const int64_t prow = static_cast<int64_t>(b) * (p.n - q0) + qi - q0;
+    const int64_t pidx = (prow * p.heads + head) * p.part_stride + p.part_slot;
+    float* po = p.part_o + pidx * D;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<float4*>(po + 32 * dt + 8 * q4 + 4 * half) =
+            make_float4(fmaf(oacc[dt][4 * q4 + 0], big, -off), fmaf(oacc[dt][4 * q4 + 1], big, -off),
+                        fmaf(oacc[dt][4 * q4 + 2], big, -off), fmaf(oacc[dt][4 * q4 + 3], big, -off));
+    if (half == 0) {
+      p.part_ml[pidx * 2] = l_tot > 0.0f ? m_run : -INFINITY;
+      p.part_ml[pidx * 2 + 1] = l_tot;
+    }
+    return;
+  }
   uint16_t* orow = p.out + ((static_cast<int64_t>(b) * p.heads + head) * p.n + qi) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
@@ -676,8 +707,9 @@ bool chunk_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
 size_t chunk_workspace(const kvq_cache&, int, int) { return 0; }
 
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens, int causal,
-                        float attn_scale, uint16_t* out, void*, int, hipStream_t stream, int window) {
-  ChunkParams p;
+                        float attn_scale, uint16_t* out, void*, int max_ctx_len, hipStream_t stream, int window,
+                        const ChunkPartials* partials) {
+  ChunkParams p{};
   p.q = q;
   p.out = out;
   p.k_codes = c.k_codes;
@@ -693,6 +725,14 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.causal = causal || window > 0 ? 1 : 0;
   p.window = window > 0 ? window : 0;
   p.scale_log2 = attn_scale * kCkLog2e;
+  if (partials) {
+    p.rwin = partials->rwin;
+    p.len_cap = max_ctx_len + n;
+    p.part_stride = partials->stride;
+    p.part_slot = partials->slot;
+    p.part_o = partials->o;
+    p.part_ml = partials->ml;
+  }
   const int64_t items = static_cast<int64_t>(p.hpg) * p.nblk;
   const int64_t per_bg = (items + kCkWaves - 1) / kCkWaves;
   const int64_t total = per_bg * c.batch * c.num_kv_heads;

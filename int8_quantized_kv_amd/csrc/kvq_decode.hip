@@ -40,22 +40,13 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   const int sub = lane % LPT;
   const int slot = lane / LPT;
 
+  // recent window: positions from L8 on are bf16 rows in the ring
+  const int L8 = ring_start(p, b, L);
   const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // first visible key
   const int t_begin = t_lo + split * p.split_len;
   const int nsg = split_count(L - t_lo, p.split_len);
   if (split >= nsg) return;
   const int t_end = split == nsg - 1 ? L : t_begin + p.split_len;  // the last split takes the remainder
-  // recent window: positions from L8 on are bf16 rows in the ring (decode:
-  // the last rwin of the sequence; chunk: of the ctx + n rows the cache holds)
-  int L8 = L;
-  if (p.rwin > 0) {
-    int Lc = L;
-    if (p.chunk_n > 0) {
-      const int c0 = min(max(p.ctx_lens[b], 0), p.len_cap);
-      Lc = min(c0 + p.chunk_n, p.len_cap);
-    }
-    L8 = max(Lc - p.rwin, 0);
-  }
   const int t8_end = min(t_end, L8);  // INT8 tokens of this split end here
   const int npass = t8_end > t_begin ? (t8_end - t_begin + TPP - 1) / TPP : 0;
 
@@ -266,6 +257,140 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
     }
     const float val = den > 0.0f ? num / den : 0.0f;
     p.out[((static_cast<int64_t>(b) * H + h) * nq + qi) * D + d] = f32_to_bf16_rne(val);
+  }
+}
+
+// Ring rows of a chunk on a hybrid cache, after the MFMA chunk kernel has
+// attended to the INT8 keys: one wave per (sequence, query, group of HPW
+// query heads) for the queries that see ring rows, the last min(n, W) of
+// each sequence with ctx_lens clamped to the hint (the others already have
+// their output).  LPT lanes per ring row, the same per-lane online softmax as
+// the generic kernel, then the MFMA kernel's partial (m, l, o) for the query
+// is folded in and the normalised row written as bf16.
+template <int D, int HPW>
+__global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
+  constexpr int LPT = D / 16;
+  constexpr int TPW = kWave / LPT;
+  const int lane = threadIdx.x % kWave;
+  const int groups = p.geom.kvh * p.wg_per_kvh;
+  const int nq = p.chunk_n;
+  const int nt = nq - p.chunk_q0;  // ring-seeing queries per sequence
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
+  if (item >= static_cast<int64_t>(p.batch_rows) * nt * groups) return;
+  const int hg = static_cast<int>(item % groups);
+  const int v = static_cast<int>(item / groups);  // partial row
+  const int b = v / nt;
+  const int qi = p.chunk_q0 + v % nt;
+  const int L0 = min(max(p.ctx_lens[b], 0), p.len_cap - nq);
+  const int L = L0 + qi + 1;                  // keys this query sees
+  const int L8 = max(L0 + nq - p.rwin, 0);    // first ring row (L > L8 for these queries)
+  const int kvh = hg / p.wg_per_kvh;
+  const int H = p.num_heads;
+  const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
+  const int sub = lane % LPT;
+  const int slot = lane / LPT;
+
+  float q[HPW][16];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const uint4* qp =
+        reinterpret_cast<const uint4*>(p.q + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16);
+    bf16x8_to_f32(qp[0], &q[j][0]);
+    bf16x8_to_f32(qp[1], &q[j][8]);
+  }
+  float m[HPW], l[HPW], o[HPW][16];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
+  }
+  // the INT8 keys' partial, read while the ring rows stream
+  float pm[HPW], pl[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int64_t pidx = static_cast<int64_t>(v) * H + h0 + j;
+    pm[j] = p.part_ml[pidx * 2];
+    pl[j] = p.part_ml[pidx * 2 + 1];
+  }
+  constexpr int U = 4;  // passes whose loads are issued together
+  const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
+  for (int tb = L8; tb < L; tb += U * TPW) {  // (t >= L8 >= 0)
+    uint4 kb[U][2], vb[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = ring0 + min(tb + u * TPW + slot, L - 1) % p.rcap;
+      const uint4* kr = reinterpret_cast<const uint4*>(p.rk + row * D + sub * 16);
+      const uint4* vr = reinterpret_cast<const uint4*>(p.rv + row * D + sub * 16);
+      kb[u][0] = kr[0];
+      kb[u][1] = kr[1];
+      vb[u][0] = vr[0];
+      vb[u][1] = vr[1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool ok = tb + u * TPW + slot < L;
+      float kx[16], vx[16];
+      bf16x8_to_f32(kb[u][0], &kx[0]);
+      bf16x8_to_f32(kb[u][1], &kx[8]);
+      bf16x8_to_f32(vb[u][0], &vx[0]);
+      bf16x8_to_f32(vb[u][1], &vx[8]);
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part = fmaf(q[j][e], kx[e], part);
+        const float sc = group_sum<LPT>(part) * p.scale_log2;
+        const float sj = ok ? sc : -INFINITY;
+        if (sj > m[j]) {  // exact running maximum (exp2(-inf) = 0 on the first key)
+          const float alpha = exp2f(m[j] - sj);
+          l[j] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
+          m[j] = sj;
+        }
+        const float pj = ok ? exp2f(sj - m[j]) : 0.0f;
+        l[j] += pj;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[j][e] = fmaf(pj, vx[e], o[j][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    // combine the lane slots (every query here sees a ring row, so M is finite)
+    float M = m[j];
+    for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+    const float f = m[j] == -INFINITY ? 0.0f : exp2f(m[j] - M);
+    float lj = l[j] * f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[j][e] *= f;
+    for (int off = LPT; off < kWave; off <<= 1) {
+      lj += __shfl_xor(lj, off, kWave);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[j][e] += __shfl_xor(o[j][e], off, kWave);
+    }
+    // fold in the INT8 keys' partial
+    const int64_t pidx = static_cast<int64_t>(v) * H + h0 + j;
+    const float M2 = fmaxf(M, pm[j]);
+    const float fa = exp2f(M - M2);
+    const float fb = pm[j] == -INFINITY ? 0.0f : exp2f(pm[j] - M2);
+    const float inv = 1.0f / fmaf(lj, fa, pl[j] * fb);
+    if (slot == 0) {
+      const float* po = p.part_o + pidx * D + sub * 16;
+      uint16_t* orow = p.out + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16;
+#pragma unroll
+      for (int e = 0; e < 16; e += 4) {
+        const float4 pv = *reinterpret_cast<const float4*>(po + e);
+        ushort4 w;
+        w.x = f32_to_bf16_rne(fmaf(o[j][e + 0], fa, pv.x * fb) * inv);
+        w.y = f32_to_bf16_rne(fmaf(o[j][e + 1], fa, pv.y * fb) * inv);
+        w.z = f32_to_bf16_rne(fmaf(o[j][e + 2], fa, pv.z * fb) * inv);
+        w.w = f32_to_bf16_rne(fmaf(o[j][e + 3], fa, pv.w * fb) * inv);
+        *reinterpret_cast<ushort4*>(orow + e) = w;
+      }
+    }
   }
 }
 
@@ -512,9 +637,21 @@ DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int 
   return plan_decode(rows_as_batch(c, n), max_total_len, RecentGeom(), window, true);
 }
 
+DecodePlan plan_chunk_hybrid(const kvq_cache& c, int n, int recent_window) {
+  // one partial (the INT8 keys') per (sequence, ring-seeing query, head)
+  DecodePlan pl{};
+  pl.heads_per_wg = heads_per_wg(c.num_heads / c.num_kv_heads);
+  pl.num_splits = 1;
+  pl.counter_bytes = 0;
+  const size_t partials = static_cast<size_t>(c.batch) * (n < recent_window ? n : recent_window) * c.num_heads;
+  pl.workspace = align_up(partials * 2 * sizeof(float), 256) + partials * static_cast<size_t>(c.head_dim) * sizeof(float);
+  return pl;
+}
+
 kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q, int n,
                                 const int32_t* ctx_lens, int causal, float attn_scale, uint16_t* out, void* ws,
-                                int max_total_len, hipStream_t stream, int window, const RecentGeom& rc) {
+                                int max_total_len, hipStream_t stream, int window, const RecentGeom& rc,
+                                bool int8_on_mfma) {
   const int64_t rows = static_cast<int64_t>(c.batch) * n;
   if (rows > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: batch * n too large (%lld)",
                                 static_cast<long long>(rows));
@@ -525,7 +662,8 @@ kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, cons
   p.v_scales = c.v_scales;
   p.scale_bf16 = c.scale_mode == KVQ_SCALE_PER_TOKEN_BF16 ? 1 : 0;
   p.q = q;
-  const size_t partials = static_cast<size_t>(rows) * c.num_heads * plan.num_splits;
+  const int nt = int8_on_mfma ? (n < rc.window ? n : rc.window) : n;  // hybrid: partial rows per sequence
+  const size_t partials = static_cast<size_t>(c.batch) * nt * c.num_heads * plan.num_splits;
   char* w = static_cast<char*>(ws);
   p.counters = reinterpret_cast<int32_t*>(w);
   p.part_ml = reinterpret_cast<float*>(w + plan.counter_bytes);
@@ -548,6 +686,37 @@ kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, cons
   p.rv = rc.v;
   p.rwin = rc.window;
   p.rcap = rc.cap;
+  if (int8_on_mfma) {
+    // the MFMA chunk kernel attends to the INT8 keys (partials for the
+    // queries that also see ring rows), then one wave per (row, head group)
+    // takes the ring rows and writes those queries' outputs
+    ChunkPartials cp;
+    cp.rwin = rc.window;
+    cp.stride = 1;
+    cp.slot = 0;
+    cp.o = p.part_o;
+    cp.ml = p.part_ml;
+    const kvq_status st = launch_chunk(c, q, n, ctx_lens, 1, attn_scale, out, ws, max_total_len - n, stream, 0, &cp);
+    if (st != KVQ_OK) return st;
+    p.chunk_q0 = n - nt;
+    p.batch_rows = c.batch;
+    const int64_t items = static_cast<int64_t>(c.batch) * nt * c.num_kv_heads * p.wg_per_kvh;
+    const dim3 rgrid(static_cast<unsigned>((items + 3) / 4));
+    const int hpw = plan.heads_per_wg;
+    if (c.head_dim == 128) {
+      if (hpw == 4) hipLaunchKernelGGL((chunk_ring_kernel<128, 4>), rgrid, dim3(256), 0, stream, p);
+      else if (hpw == 2) hipLaunchKernelGGL((chunk_ring_kernel<128, 2>), rgrid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((chunk_ring_kernel<128, 1>), rgrid, dim3(256), 0, stream, p);
+    } else {
+      if (hpw == 4) hipLaunchKernelGGL((chunk_ring_kernel<64, 4>), rgrid, dim3(256), 0, stream, p);
+      else if (hpw == 2) hipLaunchKernelGGL((chunk_ring_kernel<64, 2>), rgrid, dim3(256), 0, stream, p);
+      else hipLaunchKernelGGL((chunk_ring_kernel<64, 1>), rgrid, dim3(256), 0, stream, p);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+      return fail(KVQ_ERR_HIP, "kvq_attention_chunk_recent: ring launch failed: %s", hipGetErrorString(e));
+    return KVQ_OK;
+  }
   const dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, static_cast<unsigned>(rows));
   if (grid.y > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: grid too large");
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;

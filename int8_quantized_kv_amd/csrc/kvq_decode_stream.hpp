@@ -86,6 +86,9 @@ struct DecodeParams {
   int32_t chunk_n;
   int32_t chunk_causal;      // query i sees keys t <= ctx_lens[b] + i (else all ctx + n)
   const int32_t* ctx_lens;   // [B], tokens cached before the chunk
+  // chunk_ring_kernel: queries chunk_q0 .. chunk_n - 1 of batch_rows sequences
+  int32_t chunk_q0;
+  int32_t batch_rows;
 };
 
 namespace {
@@ -258,6 +261,19 @@ __device__ __forceinline__ int row_len(const DecodeParams& p, int v, int& b, int
   L0 = L0 < 0 ? 0 : (L0 > p.len_cap ? p.len_cap : L0);
   const int L = p.chunk_causal ? L0 + qi + 1 : L0 + p.chunk_n;
   return L > p.len_cap ? p.len_cap : L;
+}
+
+// First ring position of a hybrid cache for grid row (b, L) (L itself
+// without a recent window): the last rwin of the L decode tokens, or of the
+// ctx + chunk_n rows the cache holds in chunk mode.
+__device__ __forceinline__ int ring_start(const DecodeParams& p, int b, int L) {
+  if (p.rwin <= 0) return L;
+  int Lc = L;
+  if (p.chunk_n > 0) {
+    const int c0 = min(max(p.ctx_lens[b], 0), p.len_cap);
+    Lc = min(c0 + p.chunk_n, p.len_cap);
+  }
+  return max(Lc - p.rwin, 0);
 }
 
 // The sequence a workgroup serves.  With longest_first set (batch at most NT),

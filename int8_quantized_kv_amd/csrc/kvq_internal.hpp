@@ -107,13 +107,29 @@ size_t chunk_workspace(const kvq_cache& c, int max_total_len, int n);
 // workspace.
 bool chunk_generic_supported(int head_dim);
 DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int window);
+// A causal chunk over a hybrid cache at an MFMA head size (64, 128), with
+// int8_on_mfma: the MFMA chunk kernel attends to the INT8 keys, writing the
+// outputs of the queries that see no ring row and an unnormalised partial
+// for the others, which a ring kernel completes.
+DecodePlan plan_chunk_hybrid(const kvq_cache& c, int n, int recent_window);
 kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, const uint16_t* q, int n,
                                 const int32_t* ctx_lens, int causal, float attn_scale, uint16_t* out, void* ws,
                                 int max_total_len, hipStream_t stream, int window,
-                                const RecentGeom& rc = RecentGeom());
+                                const RecentGeom& rc = RecentGeom(), bool int8_on_mfma = false);
+// Where the MFMA chunk kernel puts its result on a hybrid cache: keys below
+// L - rwin only (ctx_lens clamped to the hint); the last min(n, rwin) queries
+// of each sequence, which see ring rows, leave split partials (m, l in log2
+// units; o unnormalised) at slot `slot` of `stride` per (sequence, one of
+// those queries, head), the others their output.
+struct ChunkPartials {
+  int rwin = 0;
+  int stride = 0, slot = 0;
+  float* o = nullptr;   // [B, min(n, rwin), H, stride, D]
+  float* ml = nullptr;  // [B, min(n, rwin), H, stride, 2]
+};
 // window > 0: sliding window (implies causal).
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens,
                         int causal, float attn_scale, uint16_t* out, void* ws, int max_ctx_len,
-                        hipStream_t stream, int window = 0);
+                        hipStream_t stream, int window = 0, const ChunkPartials* partials = nullptr);
 
 }  // namespace kvq

@@ -143,18 +143,21 @@ def test_sliding_decode_full_size(kvq):
     del hat
 
 
-@pytest.mark.parametrize("name", ["sliding_chunk", "fp8_chunk", "chunk_group32"])
+@pytest.mark.parametrize("name", ["sliding_chunk", "fp8_chunk", "chunk_group32", "recent_chunk"])
 def test_chunk_variant_full_size(kvq, name):
     """512 new queries after 8192 cached tokens: with a window of 1024, on
-    FP8 E4M3 codes, or with group-32 scales."""
+    FP8 E4M3 codes, with group-32 scales, or on a hybrid cache whose last 128
+    rows are bf16."""
     import torch
     w = wl.ALL[name]
     win = w.extra.get("sliding", 0)
+    rw = w.extra.get("window", 0)
     fp8 = w.extra.get("fp8")
     x = wl.layer_inputs(w, 0)
     B, KVH, T, D = x["k"].shape
-    log(f"full size {name}: B={B} ctx={w.ctx} n={w.n_new} window={win} fp8={fp8}")
-    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8, group32=(w.group == 32))
+    log(f"full size {name}: B={B} ctx={w.ctx} n={w.n_new} window={win} fp8={fp8} recent={rw}")
+    cache = kvq.Int8KVCache(B, w.num_heads, KVH, D, max_len=w.max_len, fp8=fp8, group32=(w.group == 32),
+                            recent_window=rw)
     _prefill(cache, x, w.ctx)
     cache.append(kv_dev(np.ascontiguousarray(x["k_raw"][:, :, w.ctx:])),
                  kv_dev(np.ascontiguousarray(x["v_raw"][:, :, w.ctx:])), dev_tensor(np.full(B, w.ctx, np.int32)))
@@ -173,14 +176,20 @@ def test_chunk_variant_full_size(kvq, name):
     for b, h, i in picks:
         g = h // hpg
         if (b, g) not in hat:
-            if fp8:
+            if rw:  # the oracle's hybrid cache holding the same rows
+                rc = orc.RecentWindowCache(1, D, rw, w.group)
+                rc.append(x["k"][b, g:g + 1], x["v"][b, g:g + 1])
+                assert np.array_equal(dk[b, g, :T - rw], rc.k_codes[0]), f"INT8 rows of sequence {b}, KV head {g}"
+                hat[(b, g)] = tuple(a[0] for a in rc.kv())
+            elif fp8:
                 kc, vc = orc.fp8_encode(x["k"][b, g], fp8), orc.fp8_encode(x["v"][b, g], fp8)
                 hat[(b, g)] = (orc.fp8_decode(kc, fp8), orc.fp8_decode(vc, fp8))
             else:
                 kc, ks = orc.quantize(x["k"][b, g], w.group)
                 vc, vs = orc.quantize(x["v"][b, g], w.group)
                 hat[(b, g)] = (orc.dequantize_exact(kc, ks), orc.dequantize_exact(vc, vs))
-            assert np.array_equal(dk[b, g], kc), f"codes of sequence {b}, KV head {g}"
+            if not rw:
+                assert np.array_equal(dk[b, g], kc), f"codes of sequence {b}, KV head {g}"
         kh, vh = hat[(b, g)]
         total = w.ctx + i + 1
         lo = max(total - win, 0) if win else 0

@@ -265,6 +265,8 @@ CHUNK_CASES = [
     (64, 8, 2, 0, 16, [3, 100, 0], 37, False),
     (128, 32, 8, 32, 64, [0, 200, 1000], 70, True),
     (128, 16, 8, 0, 128, [10, 300], 5, False),       # chunk shorter than the window
+    (128, 32, 8, 0, 128, [0, 700, 2000], 300, False),  # several query blocks, ring inside the chunk
+    (64, 16, 4, 32, 32, [1, 90, 500], 100, True),
     (256, 16, 4, 0, 32, [7, 500], 45, False),
     (256, 8, 2, 32, 16, [0, 90], 16, True),
 ]

@@ -113,8 +113,14 @@ FP8_CHUNK = Workload("fp8_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 
 # workload above).
 CHUNK_G32 = Workload("chunk_group32", 4, 32, 8, 128, 32, "contiguous", "bf16", 8192, 512, seed=11)
 
+# The chunked-prefill step on a recent-window hybrid cache (W = 128): the
+# chunk's rows enter through the hybrid append, and its queries attend to the
+# INT8 rows and the ring.
+RECENT_CHUNK = Workload("recent_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512, seed=12,
+                        extra={"window": 128})
+
 ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
-                           BF16_SCALES, FP8_E4M3, FP8_CHUNK, CHUNK_G32)}
+                           BF16_SCALES, FP8_E4M3, FP8_CHUNK, CHUNK_G32, RECENT_CHUNK)}
 
 
 # ----------------------------------------------------------------------------
