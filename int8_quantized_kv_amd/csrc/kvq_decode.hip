@@ -261,42 +261,57 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
 }
 
 // Ring rows of a chunk on a hybrid cache, after the MFMA chunk kernel has
-// attended to the INT8 keys: one wave per (sequence, query, group of HPW
-// query heads) for the queries that see ring rows, the last min(n, W) of
-// each sequence with ctx_lens clamped to the hint (the others already have
-// their output).  LPT lanes per ring row, the same per-lane online softmax as
-// the generic kernel, then the MFMA kernel's partial (m, l, o) for the query
-// is folded in and the normalised row written as bf16.
+// attended to the INT8 keys.  The queries that see ring rows are the last
+// min(n, W) of each sequence (ctx_lens clamped to the hint); the others
+// already have their output.  One workgroup per (sequence, group of HPW
+// query heads, four of those queries), one wave per query: the ring rows the
+// four see are staged in LDS 64 at a time, then each wave runs LPT lanes per
+// row with the same per-lane online softmax as the generic kernel, folds in
+// the MFMA kernel's partial (m, l, o) for its query and writes the
+// normalised row as bf16.
 template <int D, int HPW>
 __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
   constexpr int LPT = D / 16;
   constexpr int TPW = kWave / LPT;
+  constexpr int kQPB = 256 / kWave;       // queries per workgroup
+  constexpr int kTile = 64;               // ring rows staged per step
+  constexpr int kRow = 2 * D + 16;        // LDS row bytes (padded)
+  constexpr int kPer = kTile * (D / 8) / 256;  // 16-byte pieces per thread and side
+  __shared__ __attribute__((aligned(16))) uint8_t sk[kTile * kRow];
+  __shared__ __attribute__((aligned(16))) uint8_t sv[kTile * kRow];
+
   const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
   const int groups = p.geom.kvh * p.wg_per_kvh;
   const int nq = p.chunk_n;
   const int nt = nq - p.chunk_q0;  // ring-seeing queries per sequence
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * (256 / kWave) + threadIdx.x / kWave;
-  if (item >= static_cast<int64_t>(p.batch_rows) * nt * groups) return;
-  const int hg = static_cast<int>(item % groups);
-  const int v = static_cast<int>(item / groups);  // partial row
-  const int b = v / nt;
-  const int qi = p.chunk_q0 + v % nt;
+  const int qblocks = (nt + kQPB - 1) / kQPB;
+  const int hg = blockIdx.x % groups;
+  const int qb = (blockIdx.x / groups) % qblocks;
+  const int b = blockIdx.x / groups / qblocks;
+  const int r = qb * kQPB + wave;         // this wave's partial row in the sequence
+  const bool active = r < nt;
+  const int qi = p.chunk_q0 + min(r, nt - 1);
   const int L0 = min(max(p.ctx_lens[b], 0), p.len_cap - nq);
   const int L = L0 + qi + 1;                  // keys this query sees
-  const int L8 = max(L0 + nq - p.rwin, 0);    // first ring row (L > L8 for these queries)
+  const int L8 = max(L0 + nq - p.rwin, 0);    // first ring row (L > L8)
+  const int Lblk = L0 + p.chunk_q0 + min(qb * kQPB + kQPB, nt);  // keys the workgroup's last query sees
   const int kvh = hg / p.wg_per_kvh;
   const int H = p.num_heads;
   const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
   const int sub = lane % LPT;
   const int slot = lane / LPT;
+  const int64_t v = static_cast<int64_t>(b) * nt + min(r, nt - 1);  // partial row
 
-  float q[HPW][16];
+  float q[HPW][16], pm[HPW], pl[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const uint4* qp =
         reinterpret_cast<const uint4*>(p.q + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16);
     bf16x8_to_f32(qp[0], &q[j][0]);
     bf16x8_to_f32(qp[1], &q[j][8]);
+    pm[j] = p.part_ml[(v * H + h0 + j) * 2];
+    pl[j] = p.part_ml[(v * H + h0 + j) * 2 + 1];
   }
   float m[HPW], l[HPW], o[HPW][16];
 #pragma unroll
@@ -306,36 +321,37 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
   }
-  // the INT8 keys' partial, read while the ring rows stream
-  float pm[HPW], pl[HPW];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int64_t pidx = static_cast<int64_t>(v) * H + h0 + j;
-    pm[j] = p.part_ml[pidx * 2];
-    pl[j] = p.part_ml[pidx * 2 + 1];
-  }
-  constexpr int U = 4;  // passes whose loads are issued together
+
   const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
-  for (int tb = L8; tb < L; tb += U * TPW) {  // (t >= L8 >= 0)
-    uint4 kb[U][2], vb[U][2];
+  for (int t0 = L8; t0 < Lblk; t0 += kTile) {  // (block-uniform bounds: every wave meets the barriers)
+    const int nrows = min(kTile, Lblk - t0);
+    uint4 kr[kPer], vr[kPer];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t row = ring0 + min(tb + u * TPW + slot, L - 1) % p.rcap;
-      const uint4* kr = reinterpret_cast<const uint4*>(p.rk + row * D + sub * 16);
-      const uint4* vr = reinterpret_cast<const uint4*>(p.rv + row * D + sub * 16);
-      kb[u][0] = kr[0];
-      kb[u][1] = kr[1];
-      vb[u][0] = vr[0];
-      vb[u][1] = vr[1];
+    for (int i = 0; i < kPer; ++i) {
+      const int id = threadIdx.x + i * 256;
+      const int64_t row = ring0 + (t0 + min(id / (D / 8), nrows - 1)) % p.rcap;
+      kr[i] = *reinterpret_cast<const uint4*>(p.rk + row * D + (id % (D / 8)) * 8);
+      vr[i] = *reinterpret_cast<const uint4*>(p.rv + row * D + (id % (D / 8)) * 8);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = tb + u * TPW + slot < L;
+    for (int i = 0; i < kPer; ++i) {
+      const int id = threadIdx.x + i * 256;
+      *reinterpret_cast<uint4*>(sk + (id / (D / 8)) * kRow + (id % (D / 8)) * 16) = kr[i];
+      *reinterpret_cast<uint4*>(sv + (id / (D / 8)) * kRow + (id % (D / 8)) * 16) = vr[i];
+    }
+    __syncthreads();
+    const int tend = active ? min(t0 + kTile, L) : t0;
+    for (int tb = t0; tb < tend; tb += TPW) {
+      const int t = tb + slot;
+      const bool ok = t < tend;
+      const int rr = min(t, tend - 1) - t0;
+      const uint4* kp = reinterpret_cast<const uint4*>(sk + rr * kRow + sub * 32);
+      const uint4* vp = reinterpret_cast<const uint4*>(sv + rr * kRow + sub * 32);
       float kx[16], vx[16];
-      bf16x8_to_f32(kb[u][0], &kx[0]);
-      bf16x8_to_f32(kb[u][1], &kx[8]);
-      bf16x8_to_f32(vb[u][0], &vx[0]);
-      bf16x8_to_f32(vb[u][1], &vx[8]);
+      bf16x8_to_f32(kp[0], &kx[0]);
+      bf16x8_to_f32(kp[1], &kx[8]);
+      bf16x8_to_f32(vp[0], &vx[0]);
+      bf16x8_to_f32(vp[1], &vx[8]);
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         float part = 0.0f;
@@ -356,7 +372,9 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
         for (int e = 0; e < 16; ++e) o[j][e] = fmaf(pj, vx[e], o[j][e]);
       }
     }
+    __syncthreads();
   }
+  if (!active) return;
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     // combine the lane slots (every query here sees a ring row, so M is finite)
@@ -372,13 +390,12 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
       for (int e = 0; e < 16; ++e) o[j][e] += __shfl_xor(o[j][e], off, kWave);
     }
     // fold in the INT8 keys' partial
-    const int64_t pidx = static_cast<int64_t>(v) * H + h0 + j;
     const float M2 = fmaxf(M, pm[j]);
     const float fa = exp2f(M - M2);
     const float fb = pm[j] == -INFINITY ? 0.0f : exp2f(pm[j] - M2);
     const float inv = 1.0f / fmaf(lj, fa, pl[j] * fb);
     if (slot == 0) {
-      const float* po = p.part_o + pidx * D + sub * 16;
+      const float* po = p.part_o + (v * H + h0 + j) * D + sub * 16;
       uint16_t* orow = p.out + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16;
 #pragma unroll
       for (int e = 0; e < 16; e += 4) {
@@ -700,8 +717,10 @@ kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, cons
     if (st != KVQ_OK) return st;
     p.chunk_q0 = n - nt;
     p.batch_rows = c.batch;
-    const int64_t items = static_cast<int64_t>(c.batch) * nt * c.num_kv_heads * p.wg_per_kvh;
-    const dim3 rgrid(static_cast<unsigned>((items + 3) / 4));
+    // one workgroup per (sequence, four ring-seeing queries, head group)
+    const int64_t blocks = static_cast<int64_t>(c.batch) * ((nt + 3) / 4) * c.num_kv_heads * p.wg_per_kvh;
+    if (blocks > 0x7fffffffLL) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk_recent: grid too large");
+    const dim3 rgrid(static_cast<unsigned>(blocks));
     const int hpw = plan.heads_per_wg;
     if (c.head_dim == 128) {
       if (hpw == 4) hipLaunchKernelGGL((chunk_ring_kernel<128, 4>), rgrid, dim3(256), 0, stream, p);
