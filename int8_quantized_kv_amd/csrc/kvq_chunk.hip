@@ -11,15 +11,13 @@
 //     lane's 16 token rows are exactly the k-slots the B operand of the
 //     second product O^T = V^T P^T needs, so the weights never leave their
 //     lanes.
-//   * K codes are widened once per workgroup, while staging the tile in LDS,
-//     to exact f16 values c - 128 (v_perm_b32 puts a code under the f16
-//     exponent of 1024, v_pk_add_f16 subtracts 1152).  V stays as codes in
-//     LDS; V^T comes out through ds_read_b64_tr_b8 (each lane of a 16-lane
-//     group names one 8-byte row piece; lane j gets byte j % 8 of the pieces
-//     named by lanes 2b + j / 8, b = 0..7) and v_perm_b32 makes each code the
-//     f16 value c * 2^-24 (exact), so sum_t w_t (c_t - 128) =
-//     2^24 sum_t w_t c_t 2^-24 - 128 sum_t w_t, the last sum taken from the
-//     same f16 weights with v_dot2.
+//   * K and V codes are widened once per workgroup, while staging the tile
+//     in LDS, to exact f16 values c - 128 (v_perm_b32 puts a code under the
+//     f16 exponent of 1024, v_pk_add_f16 subtracts 1152).  V^T comes out of
+//     LDS through ds_read_b64_tr_b16: each lane of a 16-lane group names one
+//     8-byte row piece (four f16), and lane j gets element j % 4 of the
+//     pieces named by lanes j / 4 + 4b, b = 0..3; two such reads give a
+//     lane its eight k-slots.
 //   * queries are scaled by one power of two per workgroup into f16 range
 //     (exact for bf16 inputs); the per-token K scale, the attention scale,
 //     log2 e and that power of two form one staged factor per token, so a
@@ -50,7 +48,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int kCkWaves = 8;      // two groups of four, one wave of each per SIMD
 constexpr int kGroupWaves = 4;
@@ -102,21 +100,15 @@ template <int D, int TOK, bool G32 = false>
 struct Tile {
   static constexpr int kKRow = 2 * D + 16;
   static constexpr int kKBytes = TOK * kKRow;
-  static constexpr int kVBytes = TOK * D;
+  // V rows hold D f16 values, padded to a stride of 32 mod 128 bytes so the
+  // four rows x 32 bytes of one 16-lane transposed read cover every bank once
+  static constexpr int kVRow = 2 * D + 32;
+  static constexpr int kVBytes = TOK * kVRow;
   static constexpr int kNG = D / 32;
   static constexpr int kBytes = kKBytes + kVBytes + 3 * TOK * 4 + (G32 ? (kNG - 1) * TOK * 4 + kNG * TOK * 2 : 0);
-  static __device__ __forceinline__ int vswz(int t) {
-    if constexpr (D == 128) {
-      const int s = (t >> 1) & 15;
-      return ((s & 1) << 2) | (((s >> 2) & 1) << 3) | ((s >> 1) & 1) | (((s >> 3) & 1) << 1);
-    } else {
-      const int s = (t >> 2) & 7;
-      return (((s >> 1) & 1) << 2) | ((s & 1) << 1) | ((s >> 2) & 1);
-    }
-  }
   // byte offsets inside one buffer
   static __device__ __forceinline__ int k_off(int t, int u16) { return t * kKRow + 16 * u16; }
-  static __device__ __forceinline__ int v_off(int t, int u8) { return kKBytes + t * D + 8 * (u8 ^ vswz(t)); }
+  static __device__ __forceinline__ int v_off(int t, int u16) { return kKBytes + t * kVRow + 16 * u16; }
   static constexpr int kKc = kKBytes + kVBytes;
   static constexpr int kLsv = kKc + TOK * 4;
   static constexpr int kRsv = kLsv + TOK * 4;
@@ -133,33 +125,10 @@ __device__ __forceinline__ uint2 codes_exact_f16(uint32_t w) {
   return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
-// Eight FP8 codes -> their eight f16 values (exact).
-template <bool E5M2>
-__device__ __forceinline__ f16x8 fp8_codes_f16(uint32_t lo, uint32_t hi) {
-  uint4 w;
-  w.x = fp8_pair_k<E5M2, false>(lo);
-  w.y = fp8_pair_k<E5M2, true>(lo);
-  w.z = fp8_pair_k<E5M2, false>(hi);
-  w.w = fp8_pair_k<E5M2, true>(hi);
-  return __builtin_bit_cast(f16x8, w);
-}
-
-// Eight codes -> eight f16 values c * 2^-24 (subnormal, exact).
-__device__ __forceinline__ f16x8 codes_tiny_f16(uint32_t lo, uint32_t hi) {
-  uint4 w;
-  w.x = __builtin_amdgcn_perm(0u, lo, 0x0C010C00u);
-  w.y = __builtin_amdgcn_perm(0u, lo, 0x0C030C02u);
-  w.z = __builtin_amdgcn_perm(0u, hi, 0x0C010C00u);
-  w.w = __builtin_amdgcn_perm(0u, hi, 0x0C030C02u);
-  return __builtin_bit_cast(f16x8, w);
-}
-
 __device__ __forceinline__ f16x2 pack2(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_convertvector(v, f16x2);
 }
-
-__device__ __forceinline__ float dot2(f16x2 a, f16x2 b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
 
 __device__ __forceinline__ float other_half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -333,8 +302,10 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int j = tid + i * kCkThreads;
-      if (j < kChunks) {  // K: 16 codes -> 16 exact f16 values = units 2c and 2c + 1
-        const int r = j / kChunksPerRow, c = j % kChunksPerRow;
+      if (j < 2 * kChunks) {  // K or V: 16 codes -> 16 exact f16 values = units 2c and 2c + 1
+        const bool kside = j < kChunks;
+        const int id = kside ? j : j - kChunks;
+        const int r = id / kChunksPerRow, c = id % kChunksPerRow;
         uint2 k0, k1, k2, k3;
         if constexpr (FP8) {  // the codes' own values
           k0 = make_uint2(fp8_pair_k<E5, false>(lreg[i].x), fp8_pair_k<E5, true>(lreg[i].x));
@@ -347,15 +318,9 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
           k2 = codes_exact_f16(lreg[i].z);
           k3 = codes_exact_f16(lreg[i].w);
         }
-        *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c)) = make_uint4(k0.x, k0.y, k1.x, k1.y);
-        *reinterpret_cast<uint4*>(buf + TL::k_off(r, 2 * c + 1)) = make_uint4(k2.x, k2.y, k3.x, k3.y);
-      } else if (j < 2 * kChunks) {  // V: codes, 8-byte units 2c and 2c + 1 (halves swap with the low unit bit)
-        const int id = j - kChunks;
-        const int r = id / kChunksPerRow, c = id % kChunksPerRow;
-        const int f = TL::vswz(r);
-        uint4 vv = lreg[i];
-        if (f & 1) vv = make_uint4(vv.z, vv.w, vv.x, vv.y);
-        *reinterpret_cast<uint4*>(buf + TL::kKBytes + r * D + 8 * ((2 * c) ^ (f & ~1))) = vv;
+        uint8_t* dst = buf + (kside ? TL::k_off(r, 2 * c) : TL::v_off(r, 2 * c));
+        *reinterpret_cast<uint4*>(dst) = make_uint4(k0.x, k0.y, k1.x, k1.y);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(k2.x, k2.y, k3.x, k3.y);
       }
     }
     if (ld_s) {
@@ -392,15 +357,19 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     }
   };
 
-  if constexpr (FP8 || G32) {
+  {
     // the first MFMA step takes the last buffer's values times all-zero
-    // weights before anything is staged there; FP8 bytes left in LDS could be
-    // NaN or inf codes (group-32: the V group ratios, f16, could be), and
-    // 0 * NaN is NaN, so those values start as zeros
-    uint8_t* bz = smem + (kCkBufs - 1) * TL::kBytes + (FP8 ? TL::kKBytes : TL::kRv);
-    constexpr int kZero = FP8 ? TL::kVBytes : TL::kNG * kCkTile * 2;
-    for (int i = tid * 16; i < kZero; i += kCkThreads * 16)
+    // weights before anything is staged there; f16 bits left in LDS could be
+    // NaN or inf (group-32: the V group ratios too), and 0 * NaN is NaN, so
+    // those values start as zeros
+    uint8_t* bz = smem + (kCkBufs - 1) * TL::kBytes + TL::kKBytes;
+    for (int i = tid * 16; i < TL::kVBytes; i += kCkThreads * 16)
       *reinterpret_cast<uint4*>(bz + i) = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (G32) {
+      uint8_t* br = smem + (kCkBufs - 1) * TL::kBytes + TL::kRv;
+      for (int i = tid * 16; i < TL::kNG * kCkTile * 2; i += kCkThreads * 16)
+        *reinterpret_cast<uint4*>(br + i) = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   load_tile(tbase);
   __syncthreads();  // sm_qmax (and the cleared values)
@@ -440,21 +409,18 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   if (ntiles > 2) load_tile(tbase + 2 * kCkTile);
   __syncthreads();
 
-  // V transpose read: lane 16*r4 + r names token 16ks + pi(r4/2, r/2) and
-  // unit 4dt + 2(r4%2) + r%2, where pi(h, e) = 8(e/4) + 4h + e%4 is the
-  // token of k-slot 8h + e in the S^T C layout.
-  const int r4 = lane >> 4;
-  const int r16 = lane & 15;
-  const int vtok = 8 * ((r16 >> 1) >> 2) + 4 * (r4 >> 1) + ((r16 >> 1) & 3);
-  const int vunit = 2 * (r4 & 1) + (r16 & 1);
-  const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+  // V transpose reads: lane 16G + n names token 16ks + 4(G/2) + n/4 (the
+  // second read 8 further) and f16 column 16(G%2) + 4(n%4) of the d tile, so
+  // it receives column d = lane % 32 at k-slots 8h + e, h = lane / 32, whose
+  // tokens pi(h, e) = 8(e/4) + 4h + e%4 are those of the S^T C layout.
+  const int vtok = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   f32x16 oacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x16{};
   float m_run = kMinusBig;
   float l_run = 0.0f;   // sum of w / sV over this lane's tokens
-  float w_run = 0.0f;   // sum of the f16 weights over this lane's tokens
   f32x16 s[kTT];        // S^T of the tile whose softmax comes next
   f16x8 pw[kTT][2];     // weights of the tile whose values come next
 #pragma unroll
@@ -484,9 +450,12 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
           const int tok = 32 * tt + 16 * ks + vtok;
 #pragma unroll
           for (int dt = 0; dt < kDT; ++dt) {
-            const v2i c8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (v2i __attribute__((address_space(3)))*)(bv + TL::v_off(tok, 4 * dt + vunit)));
-            const uint32_t lo = static_cast<uint32_t>(c8.x), hi = static_cast<uint32_t>(c8.y);
+            const uint8_t* va = bv + TL::kKBytes + tok * TL::kVRow + 2 * (32 * dt + vcol);
+            const f16x4 a0 = __builtin_bit_cast(
+                f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)va));
+            const f16x4 a1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                           (v4s __attribute__((address_space(3)))*)(va + 8 * TL::kVRow)));
+            const f16x8 a8 = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
             if constexpr (G32) {
               // tile dt is group dt: the weights of its tokens times s_g / s_max
               const _Float16* rv = reinterpret_cast<const _Float16*>(bv + TL::kRv) + dt * kCkTile + 32 * tt + 16 * ks +
@@ -494,12 +463,9 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
               const f16x4 r0 = *reinterpret_cast<const f16x4*>(rv);
               const f16x4 r1 = *reinterpret_cast<const f16x4*>(rv + 8);
               const f16x8 r8 = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-              const uint2 a0 = codes_exact_f16(lo), a1 = codes_exact_f16(hi);
-              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  __builtin_bit_cast(f16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)), pw[tt][ks] * r8, oacc[dt], 0, 0, 0);
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, pw[tt][ks] * r8, oacc[dt], 0, 0, 0);
             } else {
-              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  FP8 ? fp8_codes_f16<E5>(lo, hi) : codes_tiny_f16(lo, hi), pw[tt][ks], oacc[dt], 0, 0, 0);
+              oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a8, pw[tt][ks], oacc[dt], 0, 0, 0);
             }
           }
         }
@@ -593,7 +559,6 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
-      w_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
     }
@@ -613,7 +578,6 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const f16x2 h2 = pack2(w[2 * e], w[2 * e + 1]);
-          if constexpr (!G32) w_run = dot2(h2, ones, w_run);
           pw[tt][ks][2 * e] = h2[0];
           pw[tt][ks][2 * e + 1] = h2[1];
         }
@@ -641,12 +605,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   // ---- normalise and store: lane holds query qi, d = 32dt + 8(r/4) + 4*half + r%4
   if (!q_ok) return;
   const float l_tot = other_half_sum(l_run);
-  const float w_tot = other_half_sum(w_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  // INT8: the V operands carry c 2^-24, so the sum is 2^24 acc - 128 sum w;
-  // FP8 operands are the values themselves
-  const float big = FP8 || G32 ? 1.0f : 16777216.0f;
-  const float off = FP8 || G32 ? 0.0f : 128.0f * w_tot;
   const int q0 = max(p.n - p.rwin, 0);  // the last rwin queries see ring rows (L0 <= hint)
   if (p.rwin > 0 && qi >= q0) {
     // the query also sees ring rows: a split partial in log2 units
@@ -660,8 +619,8 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<float4*>(po + 32 * dt + 8 * q4 + 4 * half) =
-            make_float4(fmaf(oacc[dt][4 * q4 + 0], big, -off), fmaf(oacc[dt][4 * q4 + 1], big, -off),
-                        fmaf(oacc[dt][4 * q4 + 2], big, -off), fmaf(oacc[dt][4 * q4 + 3], big, -off));
+            make_float4(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1],
+                        oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]);
     if (half == 0) {
       p.part_ml[pidx * 2] = l_tot > 0.0f ? m_run : -INFINITY;
       p.part_ml[pidx * 2 + 1] = l_tot;
@@ -674,10 +633,10 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       ushort4 o;
-      o.x = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 0], big, -off) * inv);
-      o.y = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 1], big, -off) * inv);
-      o.z = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 2], big, -off) * inv);
-      o.w = f32_to_bf16_rne(fmaf(oacc[dt][4 * q4 + 3], big, -off) * inv);
+      o.x = f32_to_bf16_rne(oacc[dt][4 * q4 + 0] * inv);
+      o.y = f32_to_bf16_rne(oacc[dt][4 * q4 + 1] * inv);
+      o.z = f32_to_bf16_rne(oacc[dt][4 * q4 + 2] * inv);
+      o.w = f32_to_bf16_rne(oacc[dt][4 * q4 + 3] * inv);
       *reinterpret_cast<ushort4*>(orow + 32 * dt + 8 * q4 + 4 * half) = o;
     }
   }
