@@ -1,8 +1,10 @@
 """GPU parity of the recent-window hybrid cache (the last W positions of a
 sequence in bf16, older ones INT8) against the oracle's RecentWindowCache:
 append state bit-exact after every call, decode within the attention bar,
-the fused step equal to append-then-decode bit for bit, and the get_kv view
-exact."""
+the fused step equal to append-then-decode bit for bit, the get_kv view
+exact, and chunked prefill over the view within the attention bar at every
+head size (MFMA kernel plus ring kernel at 64 and 128, the generic kernel's
+ring loop at 32 and 256)."""
 
 import numpy as np
 import pytest
