@@ -35,7 +35,7 @@
 //     KV head) to finish merges them with the log-sum-exp identity and writes
 //     bf16 (a counter in the workspace elects it and is reset for the next
 //     call).
-// head_dim 256 uses the generic kernel below (fp32 FMAs, separate merge).
+// head_dim 256 uses the generic kernel of kvq_decode.hip (fp32 FMAs, separate merge).
 #pragma once
 
 #include "kvq_internal.hpp"
