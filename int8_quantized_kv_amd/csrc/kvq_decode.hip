@@ -260,6 +260,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
   }
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // Ring rows of a chunk on a hybrid cache, after the MFMA chunk kernel has
 // attended to the INT8 keys.  The queries that see ring rows are the last
 // min(n, W) of each sequence (ctx_lens clamped to the hint); the others
@@ -287,7 +289,8 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
   const int nt = nq - p.chunk_q0;  // ring-seeing queries per sequence
   const int qblocks = (nt + kQPB - 1) / kQPB;
   const int hg = blockIdx.x % groups;
-  const int qb = (blockIdx.x / groups) % qblocks;
+  // the last queries see the most ring rows: their workgroups go first
+  const int qb = qblocks - 1 - (blockIdx.x / groups) % qblocks;
   const int b = blockIdx.x / groups / qblocks;
   const int r = qb * kQPB + wave;         // this wave's partial row in the sequence
   const bool active = r < nt;
@@ -303,13 +306,17 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
   const int slot = lane / LPT;
   const int64_t v = static_cast<int64_t>(b) * nt + min(r, nt - 1);  // partial row
 
-  float q[HPW][16], pm[HPW], pl[HPW];
+  // queries and ring K stay bf16 pairs: scores use v_dot2_f32_bf16 (exact
+  // products, fp32 sums)
+  uint32_t q[HPW][8];
+  float pm[HPW], pl[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     const uint4* qp =
         reinterpret_cast<const uint4*>(p.q + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16);
-    bf16x8_to_f32(qp[0], &q[j][0]);
-    bf16x8_to_f32(qp[1], &q[j][8]);
+    const uint4 q0 = qp[0], q1 = qp[1];
+    q[j][0] = q0.x; q[j][1] = q0.y; q[j][2] = q0.z; q[j][3] = q0.w;
+    q[j][4] = q1.x; q[j][5] = q1.y; q[j][6] = q1.z; q[j][7] = q1.w;
     pm[j] = p.part_ml[(v * H + h0 + j) * 2];
     pl[j] = p.part_ml[(v * H + h0 + j) * 2 + 1];
   }
@@ -347,26 +354,31 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
       const int rr = min(t, tend - 1) - t0;
       const uint4* kp = reinterpret_cast<const uint4*>(sk + rr * kRow + sub * 32);
       const uint4* vp = reinterpret_cast<const uint4*>(sv + rr * kRow + sub * 32);
-      float kx[16], vx[16];
-      bf16x8_to_f32(kp[0], &kx[0]);
-      bf16x8_to_f32(kp[1], &kx[8]);
+      const uint4 k0 = kp[0], k1 = kp[1];
+      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      float vx[16];
       bf16x8_to_f32(vp[0], &vx[0]);
       bf16x8_to_f32(vp[1], &vx[8]);
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
-        float part = 0.0f;
+        float pa = 0.0f, pb = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part = fmaf(q[j][e], kx[e], part);
-        const float sc = group_sum<LPT>(part) * p.scale_log2;
+        for (int e = 0; e < 8; e += 2) {
+          pa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[j][e]), __builtin_bit_cast(bf16x2, kw[e]), pa,
+                                               false);
+          pb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[j][e + 1]),
+                                               __builtin_bit_cast(bf16x2, kw[e + 1]), pb, false);
+        }
+        const float sc = group_sum<LPT>(pa + pb) * p.scale_log2;
         const float sj = ok ? sc : -INFINITY;
-        if (sj > m[j]) {  // exact running maximum (exp2(-inf) = 0 on the first key)
-          const float alpha = exp2f(m[j] - sj);
+        if (sj > m[j] + kLazy) {  // lazy running maximum: weights stay below 2^8
+          const float alpha = __builtin_amdgcn_exp2f(m[j] - sj);  // 0 on the first key (m = -inf)
           l[j] *= alpha;
 #pragma unroll
           for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
           m[j] = sj;
         }
-        const float pj = ok ? exp2f(sj - m[j]) : 0.0f;
+        const float pj = ok ? __builtin_amdgcn_exp2f(sj - m[j]) : 0.0f;
         l[j] += pj;
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[j][e] = fmaf(pj, vx[e], o[j][e]);
@@ -378,17 +390,11 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
     // combine the lane slots (every query here sees a ring row, so M is finite)
-    float M = m[j];
-    for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+    const float M = slot_max<LPT>(m[j]);
     const float f = m[j] == -INFINITY ? 0.0f : exp2f(m[j] - M);
-    float lj = l[j] * f;
+    const float lj = slot_sum<LPT>(l[j] * f);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[j][e] *= f;
-    for (int off = LPT; off < kWave; off <<= 1) {
-      lj += __shfl_xor(lj, off, kWave);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[j][e] += __shfl_xor(o[j][e], off, kWave);
-    }
+    for (int e = 0; e < 16; ++e) o[j][e] = slot_sum<LPT>(o[j][e] * f);
     // fold in the INT8 keys' partial
     const float M2 = fmaxf(M, pm[j]);
     const float fa = exp2f(M - M2);

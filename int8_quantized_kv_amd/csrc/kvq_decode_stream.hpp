@@ -201,6 +201,22 @@ __device__ __forceinline__ float slot_sum(float x) {
   return a + b;
 }
 
+// Maximum over the lanes that share (lane % LPT).
+template <int LPT>
+__device__ __forceinline__ float slot_max(float x) {
+  float a, b;
+  if constexpr (LPT <= 1) x = fmaxf(x, dpp_f32<0x121>(x));  // row_ror:1
+  if constexpr (LPT <= 2) x = fmaxf(x, dpp_f32<0x122>(x));  // row_ror:2
+  if constexpr (LPT <= 4) x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+  if constexpr (LPT <= 8) x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+  if constexpr (LPT <= 16) {
+    swap16(x, a, b);
+    x = fmaxf(a, b);
+  }
+  swap32(x, a, b);
+  return fmaxf(a, b);
+}
+
 // Value of lane (i + N) for lanes whose partner lies in the same 32-lane half.
 template <int N>
 __device__ __forceinline__ uint32_t lane_up(uint32_t x) {
