@@ -269,6 +269,8 @@ CHUNK_CASES = [
     (128, 16, 8, 0, 128, [10, 300], 5, False),       # chunk shorter than the window
     (128, 32, 8, 0, 128, [0, 700, 2000], 300, False),  # several query blocks, ring inside the chunk
     (64, 16, 4, 32, 32, [1, 90, 500], 100, True),
+    (128, 32, 8, 0, 16, [0, 33, 300], 1, False),       # one query per sequence
+    (64, 8, 2, 0, 16, [5, 40], 16, False),              # chunk exactly one window long
     (256, 16, 4, 0, 32, [7, 500], 45, False),
     (256, 8, 2, 32, 16, [0, 90], 16, True),
 ]
