@@ -348,10 +348,11 @@ kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, 
  * ring from there.  Query i at position ctx_lens[b] + i sees keys
  * t <= ctx_lens[b] + i (bottom-right causal) of that `get_kv` view
  * (abaddon kv_cache_quant_cuda.rs `OptimizedQuantizedKvCache::get_kv`).
- * head_dim 64 and 128: the MFMA chunk kernel attends to the INT8 keys, a
- * second launch to the ring rows, and a third merges the two partial
- * softmaxes; head_dim 32 and 256: one decode per (sequence, query) through
- * the generic kernel.  batch * n at most 65535.
+ * head_dim 64 and 128: the MFMA chunk kernel attends to the INT8 keys and
+ * writes the queries that see no ring row; a second launch attends the last
+ * min(n, window) queries of each sequence to the ring rows and merges the
+ * two partial softmaxes.  head_dim 32 and 256: one decode per (sequence,
+ * query) through the generic kernel.  batch * n at most 65535.
  *   q, out, ctx_lens, max_ctx_len_hint: as kvq_attention_chunk; ctx_lens[b]
  *              must not exceed the hint (at head_dim 64 and 128 a larger
  *              length is taken as the hint)
