@@ -100,9 +100,10 @@ template <int D, int TOK, bool G32 = false>
 struct Tile {
   static constexpr int kKRow = 2 * D + 16;
   static constexpr int kKBytes = TOK * kKRow;
-  // V rows hold D f16 values, padded to a stride of 32 mod 128 bytes so the
-  // four rows x 32 bytes of one 16-lane transposed read cover every bank once
-  static constexpr int kVRow = 2 * D + 32;
+  // V rows hold D f16 values, padded to a stride of 64 mod 256 bytes: the
+  // LDS serves a transposed read 32 lanes (four rows x 64 bytes) at a time,
+  // and those then cover every bank once
+  static constexpr int kVRow = 2 * D + 64;
   static constexpr int kVBytes = TOK * kVRow;
   static constexpr int kNG = D / 32;
   static constexpr int kBytes = kKBytes + kVBytes + 3 * TOK * 4 + (G32 ? (kNG - 1) * TOK * 4 + kNG * TOK * 2 : 0);
