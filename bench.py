@@ -685,6 +685,71 @@ def cpu_baseline_paged(w: wl.Workload, lens, target_s: float = 12.0):
 
 
 # ----------------------------------------------------------------------------
+# Read-bandwidth ceiling: a plain read stream of the same bytes per launch
+# ----------------------------------------------------------------------------
+
+STREAM_SHAPES = [  # (workgroups, waves per workgroup, KB in flight per wave (x1..x2), interleaved)
+    (256, 8, 2, True), (256, 8, 4, True), (512, 8, 2, True), (512, 8, 4, True),
+    (1024, 8, 2, True), (1024, 4, 4, True), (2048, 4, 2, True), (256, 16, 2, True),
+    (512, 8, 4, False), (1024, 8, 2, False),
+]
+
+
+def stream_ceiling(kvq, torch, stream, nbytes: int, launches: int, reps: int = 5, shapes=STREAM_SHAPES):
+    """Best rate of the read-only stream kernel over `launches` buffers of
+    `nbytes` each (one launch per buffer, visited in turn as the decode step
+    visits its layers, so nothing is re-read from the Infinity Cache), over a
+    sweep of launch shapes.  Returns (best record, every record)."""
+    nbytes = nbytes // 16 * 16
+    buf = torch.empty(launches * nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    recs = []
+    with torch.cuda.stream(stream):
+        for wg, wv, dep, il in shapes:
+            def one():
+                for i in range(launches):
+                    kvq.kvq.kvq_stream_read(buf.data_ptr() + i * nbytes, nbytes, sink, wg, wv, dep, il, stream=stream)
+            one()
+            ms = time_calls(one, reps, stream, torch)
+            us = ms * 1e3 / launches
+            recs.append({"workgroups": wg, "waves": wv, "kb_in_flight_per_wave": dep, "interleaved": il,
+                         "us_per_launch": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    del buf
+    best = max(recs, key=lambda r: r["gbs"])
+    return best, recs
+
+
+def run_stream(args, kvq, torch, stream):
+    """The read-only stream kernel alone: the 8B-shaped decode's bytes per
+    layer-step (one launch per layer, 32 layers), and one 4 GiB launch."""
+    w = wl.ALL["decode_8b"]
+    per_layer = step_bytes(w, w.ctx + w.n_new)["step"]
+    best, recs = stream_ceiling(kvq, torch, stream, per_layer, w.layers, reps=args.steps)
+    for r in recs:
+        log(f"stream {r}")
+    big, big_recs = stream_ceiling(kvq, torch, stream, 1 << 32, 1, reps=3,
+                                   shapes=[(1024, 8, 4, True), (2048, 8, 4, False), (4096, 4, 4, True)])
+    for r in big_recs:
+        log(f"stream 4 GiB {r}")
+    result = {
+        "metric": "read-only stream kernel: achieved HBM GB/s (ceiling for the decode kernels)",
+        "value": best["gbs"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 1,
+        "ms_per_step": round(best["us_per_launch"] * w.layers * 1e-3, 4),
+        "pct_of_hbm_peak": round(best["gbs"] / HBM_PEAK_GBS * 100, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"stream_read: {per_layer} B per launch (the 8B-shaped decode's bytes per "
+                               f"layer-step), {w.layers} buffers read in turn; best of {len(recs)} launch shapes",
+                   "best_shape": best, "asymptote_4gib": big},
+        "roofline": {"bound": "hbm", "kernel": "kvq_stream_read", "achieved": best["gbs"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(best["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": per_layer, "us_per_launch": best["us_per_launch"]},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------------------------------
 # main
 # ----------------------------------------------------------------------------
 
@@ -696,7 +761,7 @@ def main():
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
                                                             "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32",
-                                                            "recent_chunk", "tiny_decode"])
+                                                            "recent_chunk", "tiny_decode", "stream_read"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -732,6 +797,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return
 
+    if args.workload == "stream_read":
+        run_stream(args, kvq, torch, stream)
+        return
     w = wl.ALL[args.workload]
     if w.name == "sliding_decode":
         run_sliding(args, w, kvq, torch, stream)

@@ -391,6 +391,23 @@ size_t kvq_workspace_size(const kvq_cache* cache, int32_t max_seq_len, int32_t n
  * before it is allocated (NULL pointers are accepted). */
 uint64_t kvq_cache_bytes(const kvq_cache* cache);
 
+/*
+ * kvq_stream_read — measurement aid, not a step of the method: reads `bytes`
+ * bytes of the device buffer `src` with 16-byte vector loads and does nothing
+ * else with them (their xor is written to sink[0] only if it equals a fixed
+ * constant, so the loads cannot be dropped).  Its rate is the read-bandwidth
+ * ceiling that the attention kernels' achieved HBM bandwidth is compared
+ * with.  `workgroups` workgroups of `waves_per_wg` (1..16) waves; each wave
+ * keeps `depth` (1, 2, 4 or 8) to 2*depth 1-KB loads in flight; interleave != 0:
+ * the waves of a workgroup take turns over its contiguous range, else each
+ * wave reads a contiguous range of its own.
+ *   src  : device, 16-byte aligned, bytes a positive multiple of 16
+ *   sink : device uint32 [1]
+ * Errors: INVALID_ARG, HIP.
+ */
+kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                           int32_t waves_per_wg, int32_t depth, int32_t interleave, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* kvq_last_error(void);
 

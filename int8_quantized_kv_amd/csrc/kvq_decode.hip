@@ -432,53 +432,41 @@ int pass_tokens(int head_dim, bool stream_kernel) {
 }
 
 template <int D, int HPW, int SM, bool PAGED>
-void launch_kernel(bool stream_kernel, bool append, const DecodeParams& p, dim3 grid, hipStream_t st) {
-  if (stream_kernel) {
-    if constexpr (D <= 128) {
-      if (append)
-        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, PAGED, true>), grid, dim3(kStreamThreads), 0, st, p);
-      else
-        hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, PAGED, false>), grid, dim3(kStreamThreads), 0, st, p);
-    }
-  } else if constexpr (D == 256) {  // (the planner picks the generic kernel for head_dim 256 only)
+void launch_generic(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  if constexpr (D == 256) {  // (the planner picks the generic kernel for head_dim 256 only)
     hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, PAGED>), grid, dim3(kThreads), 0, st, p);
   }
 }
 
-template <int D, int HPW, int SM>
-void launch_generic_fp8(bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
-  if constexpr (D == 256) {
-    if (paged) hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, true>), grid, dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, false>), grid, dim3(kThreads), 0, st, p);
-  }
-}
-
 template <int D, int HPW>
-void launch_modes(bool stream_kernel, bool append, int sm, bool paged, const DecodeParams& p, dim3 grid,
-                  hipStream_t st) {
-  if (sm == kSmGroup32) {
-    if (paged) launch_kernel<D, HPW, kSmGroup32, true>(stream_kernel, append, p, grid, st);
-    else launch_kernel<D, HPW, kSmGroup32, false>(stream_kernel, append, p, grid, st);
-  } else if (sm == kSmTokenBf16) {
-    if (paged) launch_kernel<D, HPW, kSmTokenBf16, true>(stream_kernel, append, p, grid, st);
-    else launch_kernel<D, HPW, kSmTokenBf16, false>(stream_kernel, append, p, grid, st);
-  } else if (sm == kSmFp8E4M3 || sm == kSmFp8E5M2) {
-    // the streaming kernel's FP8 instantiations live in their own translation unit
-    if (stream_kernel) launch_stream_fp8(D, HPW, sm, paged, append, p, grid, st);
-    else if (sm == kSmFp8E4M3) launch_generic_fp8<D, HPW, kSmFp8E4M3>(paged, p, grid, st);
-    else launch_generic_fp8<D, HPW, kSmFp8E5M2>(paged, p, grid, st);
-  } else {
-    if (paged) launch_kernel<D, HPW, kSmToken, true>(stream_kernel, append, p, grid, st);
-    else launch_kernel<D, HPW, kSmToken, false>(stream_kernel, append, p, grid, st);
+void launch_generic_modes_d(int sm, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
+  auto go = [&](auto smc) {
+    constexpr int SM = decltype(smc)::value;
+    if (paged) launch_generic<D, HPW, SM, true>(p, grid, st);
+    else launch_generic<D, HPW, SM, false>(p, grid, st);
+  };
+  switch (sm) {
+    case kSmGroup32: go(std::integral_constant<int, kSmGroup32>{}); break;
+    case kSmTokenBf16: go(std::integral_constant<int, kSmTokenBf16>{}); break;
+    case kSmFp8E4M3: go(std::integral_constant<int, kSmFp8E4M3>{}); break;
+    case kSmFp8E5M2: go(std::integral_constant<int, kSmFp8E5M2>{}); break;
+    default: go(std::integral_constant<int, kSmToken>{}); break;
   }
 }
 
 template <int D>
 void launch_d(bool stream_kernel, bool append, int hpw, int sm, bool paged, const DecodeParams& p, dim3 grid,
               hipStream_t st) {
-  if (hpw == 4) launch_modes<D, 4>(stream_kernel, append, sm, paged, p, grid, st);
-  else if (hpw == 2) launch_modes<D, 2>(stream_kernel, append, sm, paged, p, grid, st);
-  else launch_modes<D, 1>(stream_kernel, append, sm, paged, p, grid, st);
+  if (stream_kernel) {
+    if (sm == kSmGroup32) launch_stream_group32(D, hpw, paged, append, p, grid, st);
+    else if (sm == kSmTokenBf16) launch_stream_bf16(D, hpw, paged, append, p, grid, st);
+    else if (sm == kSmFp8E4M3 || sm == kSmFp8E5M2) launch_stream_fp8(D, hpw, sm, paged, append, p, grid, st);
+    else launch_stream_token(D, hpw, paged, append, p, grid, st);
+    return;
+  }
+  if (hpw == 4) launch_generic_modes_d<D, 4>(sm, paged, p, grid, st);
+  else if (hpw == 2) launch_generic_modes_d<D, 2>(sm, paged, p, grid, st);
+  else launch_generic_modes_d<D, 1>(sm, paged, p, grid, st);
 }
 
 int env_int(const char* name, int dflt) {

@@ -1263,9 +1263,46 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   finish_split<D, HPW, kStreamThreads>(p, b, h0, hg, split, ns, sm_o, sm_ml);
 }
 
+// Launch of one scale mode's streaming-kernel instantiations (head_dim 32, 64,
+// 128; 1, 2 or 4 heads per workgroup; contiguous or paged; plain or fused
+// append).  Each mode's instantiations live in a translation unit of their
+// own (kvq_decode_<mode>.hip), so the library's kernels compile in parallel.
+template <int SM>
+void launch_stream_impl(int head_dim, int hpw, bool paged, bool append, const DecodeParams& p, dim3 grid,
+                        hipStream_t st) {
+  auto go = [&](auto dc, auto hc) {
+    constexpr int D = decltype(dc)::value;
+    constexpr int HPW = decltype(hc)::value;
+    if (paged) {
+      if (append) hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, true, true>), grid, dim3(kStreamThreads), 0, st, p);
+      else hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, true, false>), grid, dim3(kStreamThreads), 0, st, p);
+    } else {
+      if (append) hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, false, true>), grid, dim3(kStreamThreads), 0, st, p);
+      else hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, false, false>), grid, dim3(kStreamThreads), 0, st, p);
+    }
+  };
+  auto by_hpw = [&](auto dc) {
+    if (hpw == 4) go(dc, std::integral_constant<int, 4>{});
+    else if (hpw == 2) go(dc, std::integral_constant<int, 2>{});
+    else go(dc, std::integral_constant<int, 1>{});
+  };
+  switch (head_dim) {
+    case 32: by_hpw(std::integral_constant<int, 32>{}); break;
+    case 64: by_hpw(std::integral_constant<int, 64>{}); break;
+    default: by_hpw(std::integral_constant<int, 128>{}); break;
+  }
+}
+
 }  // namespace
 
-// Launches the streaming kernel for the FP8 code formats (kvq_decode_fp8.hip).
+// The streaming kernel for each scale mode (kvq_decode_token.hip,
+// kvq_decode_group32.hip, kvq_decode_bf16.hip, kvq_decode_fp8.hip).
+void launch_stream_token(int head_dim, int hpw, bool paged, bool append, const DecodeParams& p, dim3 grid,
+                         hipStream_t st);
+void launch_stream_group32(int head_dim, int hpw, bool paged, bool append, const DecodeParams& p, dim3 grid,
+                           hipStream_t st);
+void launch_stream_bf16(int head_dim, int hpw, bool paged, bool append, const DecodeParams& p, dim3 grid,
+                        hipStream_t st);
 void launch_stream_fp8(int head_dim, int hpw, int sm, bool paged, bool append, const DecodeParams& p, dim3 grid,
                        hipStream_t st);
 

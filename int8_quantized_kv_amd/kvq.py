@@ -38,7 +38,7 @@ EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_append_decode", "kvq_atte
             "kvq_append_recent", "kvq_attention_decode_recent", "kvq_append_decode_recent", "kvq_dequant_recent",
             "kvq_workspace_size_recent", "kvq_attention_decode_window", "kvq_append_decode_window",
             "kvq_attention_chunk_window", "kvq_workspace_size_window", "kvq_attention_chunk_recent",
-            "kvq_workspace_size_chunk_recent")
+            "kvq_workspace_size_chunk_recent", "kvq_stream_read")
 
 
 class KvqError(RuntimeError):
@@ -150,6 +150,8 @@ def _load():
     lib.kvq_attention_chunk_window.restype = I
     lib.kvq_workspace_size_window.argtypes = [CP, I, I, I]
     lib.kvq_workspace_size_window.restype = ctypes.c_size_t
+    lib.kvq_stream_read.argtypes = [P, ctypes.c_size_t, P, I, I, I, I, P]
+    lib.kvq_stream_read.restype = I
     lib.kvq_last_error.argtypes = []
     lib.kvq_last_error.restype = ctypes.c_char_p
     lib.kvq_version.argtypes = []
@@ -336,3 +338,9 @@ def kvq_workspace_size_window(cache: kvq_cache, max_seq_len: int, n_query: int, 
     if n == 0 and kvq_last_error():
         raise KvqError(KVQ_ERR_INVALID_ARG, kvq_last_error())
     return n
+
+
+def kvq_stream_read(src, nbytes: int, sink, workgroups: int, waves_per_wg: int = 8, depth: int = 4,
+                    interleave: bool = True, stream=None):
+    _check(_lib.kvq_stream_read(_ptr(src), nbytes, _ptr(sink), workgroups, waves_per_wg, depth,
+                                1 if interleave else 0, _stream(stream)))
