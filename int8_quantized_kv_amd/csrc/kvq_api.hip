@@ -119,7 +119,16 @@ size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_l
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
   }
-  if (n_query == 1) return plan_decode(*c, max_seq_len, recent_of(r), window).workspace;
+  if (n_query == 1) {
+    // one query: a decode, or a one-row chunk, which at head dims without an
+    // MFMA chunk kernel runs on the generic kernel's (shorter) splits
+    size_t w = plan_decode(*c, max_seq_len, recent_of(r), window).workspace;
+    if (!r && !chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim)) {
+      const size_t wc = plan_chunk_generic(*c, max_seq_len, 1, window).workspace;
+      w = wc > w ? wc : w;
+    }
+    return w;
+  }
   if (!chunk_supported(c->head_dim) && chunk_generic_supported(c->head_dim))
     return plan_chunk_generic(*c, max_seq_len, n_query, window).workspace;
   return chunk_workspace(*c, max_seq_len, n_query);

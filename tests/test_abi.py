@@ -306,3 +306,15 @@ def test_sizing_before_allocation():
     # the entry points that touch memory still require the pointers
     st, msg = _status("kvq_append", ctypes.byref(paged), FAKE, FAKE, 0, 1, FAKE, None)
     assert st == kvq.KVQ_ERR_INVALID_ARG and "block_table" in msg
+
+
+@pytest.mark.parametrize("head_dim", [32, 256])
+def test_one_query_chunk_workspace_is_enough(head_dim):
+    """kvq_workspace_size(cache, hint + 1, 1) covers a one-query chunk at head
+    dims that run chunks on the generic kernel (whose splits are shorter than
+    decode's): one byte less is refused as exactly that many bytes short."""
+    c = kvq.make_cache(4, 32, 8, head_dim, FAKE, FAKE, FAKE, FAKE, max_len=8192)
+    ws = kvq.kvq_workspace_size(c, 4096 + 1, 1)
+    st, msg = _status("kvq_attention_chunk", ctypes.byref(c), FAKE, 1, FAKE, 1, ctypes.c_float(0.1), FAKE, FAKE,
+                      ws - 1, 4096, None)
+    assert st == kvq.KVQ_ERR_WORKSPACE and f"the {ws} bytes needed" in msg
