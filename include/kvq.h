@@ -392,6 +392,29 @@ size_t kvq_workspace_size(const kvq_cache* cache, int32_t max_seq_len, int32_t n
 uint64_t kvq_cache_bytes(const kvq_cache* cache);
 
 /*
+ * kvq_append_decode_noalloc — kvq_append_decode for callers that cannot
+ * allocate or own device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same launch and kernels, with
+ * the split counters and partials in a static device array of 8 MiB that the
+ * library holds on each GPU it runs on until the process ends.  The caller
+ * passes inputs and outputs only; no workspace argument, and the call
+ * allocates nothing.  The array's address on a device is looked up at the
+ * first call on that device, which also clears its counter region on
+ * `stream` ahead of its own kernel; every completed call leaves the counters
+ * zero again.  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must not be made.
+ *
+ *   arguments : as kvq_append_decode, without workspace / workspace_bytes
+ * Errors: those of kvq_append_decode; WORKSPACE when the call's split
+ * partials would exceed the array (batch * num_heads * splits * (head_dim + 2)
+ * * 4 bytes above 8 MiB less the 64 KiB counter region), HIP if the array's
+ * address cannot be obtained.
+ */
+kvq_status kvq_append_decode_noalloc(const kvq_cache* cache, const void* k_new, const void* v_new,
+                                     int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens,
+                                     float attn_scale, uint16_t* out, int32_t max_seq_len_hint, void* stream);
+
+/*
  * kvq_stream_read — measurement aid, not a step of the method: reads `bytes`
  * bytes of the device buffer `src` with 16-byte vector loads and does nothing
  * else with them (their xor is written to sink[0] only if it equals a fixed

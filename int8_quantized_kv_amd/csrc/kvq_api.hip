@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <cmath>
+#include <mutex>
 
 #include "kvq_internal.hpp"
 
@@ -256,6 +257,100 @@ KVQ_API kvq_status kvq_append_decode_recent(const kvq_cache* c, const kvq_recent
   if (!r) return fail(KVQ_ERR_INVALID_ARG, "%s: recent-window descriptor is NULL", who);
   return decode_impl(c, r, true, k_new, v_new, in_dtype, q, seq_lens, attn_scale, out, workspace,
                      workspace_bytes, max_seq_len_hint, stream, who);
+}
+
+// ---------------------------------------------------------------------------
+// The fused decode step without a caller workspace: split counters and
+// partials live in a static device array of kScratchBytes, one per GPU, held
+// until the process ends.  Its address on each device comes from
+// hipGetSymbolAddress at the first call on that device; host code never
+// passes the array's own name to a kernel or a copy (on the host that name is
+// a stand-in, not a device address).
+// ---------------------------------------------------------------------------
+namespace kvq {
+namespace {
+
+constexpr size_t kScratchBytes = 8u << 20;      // 8 MiB per GPU
+constexpr size_t kScratchCounters = 64u << 10;  // fixed counter region at the front
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The device address of this device's scratch array, looked up once per
+// device (with that device current); the counter region is cleared on
+// `stream` at that first call, ahead of the call's own kernel.
+kvq_status scratch_of(int dev, hipStream_t stream, void** out, const char* who) {
+  ScratchSlot& s = g_scratch[dev];
+  bool first = false;
+  std::call_once(s.once, [&] {
+    first = true;
+    s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+  });
+  if (s.err != hipSuccess || !s.ptr)
+    return fail(KVQ_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", who, dev,
+                hipGetErrorString(s.err));
+  if (first) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t*>(s.ptr),
+                       static_cast<int>(kScratchCounters / 4));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: scratch clear failed: %s", who, hipGetErrorString(e));
+  }
+  *out = s.ptr;
+  return KVQ_OK;
+}
+
+}  // namespace
+}  // namespace kvq
+
+KVQ_API kvq_status kvq_append_decode_noalloc(const kvq_cache* c, const void* k_new, const void* v_new,
+                                             int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens,
+                                             float attn_scale, uint16_t* out, int32_t max_seq_len_hint,
+                                             void* stream) {
+  const char* who = "kvq_append_decode_noalloc";
+  kvq_status st = check_cache(c, who);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
+  if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
+  if (!q || !seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, seq_lens and out must be non-NULL", who);
+  if (!finite(attn_scale)) return fail(KVQ_ERR_INVALID_ARG, "%s: attn_scale must be finite", who);
+  if (max_seq_len_hint < 1 || max_seq_len_hint > capacity_of(*c))
+    return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
+                capacity_of(*c));
+  if (!decode_supported(c->head_dim))
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
+  // the caller's plan, with the split counters moved to the fixed region at
+  // the front of the array and the partials after it
+  DecodePlan plan = plan_decode(*c, max_seq_len_hint);
+  if (plan.counter_bytes > kScratchCounters)
+    return fail(KVQ_ERR_WORKSPACE, "%s: %zu bytes of split counters exceed the %zu-byte counter region", who,
+                plan.counter_bytes, kScratchCounters);
+  const size_t need = plan.workspace - plan.counter_bytes + kScratchCounters;
+  if (need > kScratchBytes)
+    return fail(KVQ_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch, above the %zu-byte maximum "
+                "(use kvq_append_decode with a workspace)", who, need, kScratchBytes);
+  plan.counter_bytes = kScratchCounters;
+  plan.workspace = need;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: hipGetDevice failed: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "%s: device %d beyond %d", who, dev, kMaxDevices);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  st = scratch_of(dev, hs, &ws, who);
+  if (st != KVQ_OK) return st;
+  return launch_decode(*c, plan, q, seq_lens, attn_scale, out, ws, max_seq_len_hint, hs, k_new, v_new, in_dtype);
 }
 
 namespace kvq {

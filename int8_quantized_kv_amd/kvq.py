@@ -38,7 +38,7 @@ EXPORTED = ("kvq_append", "kvq_attention_decode", "kvq_append_decode", "kvq_atte
             "kvq_append_recent", "kvq_attention_decode_recent", "kvq_append_decode_recent", "kvq_dequant_recent",
             "kvq_workspace_size_recent", "kvq_attention_decode_window", "kvq_append_decode_window",
             "kvq_attention_chunk_window", "kvq_workspace_size_window", "kvq_attention_chunk_recent",
-            "kvq_workspace_size_chunk_recent", "kvq_stream_read")
+            "kvq_workspace_size_chunk_recent", "kvq_stream_read", "kvq_append_decode_noalloc")
 
 
 class KvqError(RuntimeError):
@@ -150,6 +150,8 @@ def _load():
     lib.kvq_attention_chunk_window.restype = I
     lib.kvq_workspace_size_window.argtypes = [CP, I, I, I]
     lib.kvq_workspace_size_window.restype = ctypes.c_size_t
+    lib.kvq_append_decode_noalloc.argtypes = [CP, P, P, I, P, P, F, P, I, P]
+    lib.kvq_append_decode_noalloc.restype = I
     lib.kvq_stream_read.argtypes = [P, ctypes.c_size_t, P, I, I, I, I, P]
     lib.kvq_stream_read.restype = I
     lib.kvq_last_error.argtypes = []
@@ -344,3 +346,10 @@ def kvq_stream_read(src, nbytes: int, sink, workgroups: int, waves_per_wg: int =
                     interleave: bool = True, stream=None):
     _check(_lib.kvq_stream_read(_ptr(src), nbytes, _ptr(sink), workgroups, waves_per_wg, depth,
                                 1 if interleave else 0, _stream(stream)))
+
+
+def kvq_append_decode_noalloc(cache: kvq_cache, k_new, v_new, in_dtype: int, q, seq_lens, attn_scale: float, out,
+                              max_seq_len_hint: int, stream=None):
+    _check(_lib.kvq_append_decode_noalloc(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), in_dtype, _ptr(q),
+                                          _ptr(seq_lens), attn_scale, _ptr(out), max_seq_len_hint,
+                                          _stream(stream)))

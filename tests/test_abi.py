@@ -308,6 +308,23 @@ def test_sizing_before_allocation():
     assert st == kvq.KVQ_ERR_INVALID_ARG and "block_table" in msg
 
 
+def test_noalloc_host_errors():
+    """kvq_append_decode_noalloc checks its arguments and the scratch size on
+    the host, before any launch."""
+    d = ctypes.byref(_desc())
+    F = ctypes.c_float
+    assert _status("kvq_append_decode_noalloc", d, None, FAKE, 1, FAKE, FAKE, F(0.1), FAKE, 64, None)[0] == \
+        kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_append_decode_noalloc", d, FAKE, FAKE, 7, FAKE, FAKE, F(0.1), FAKE, 64, None)[0] == \
+        kvq.KVQ_ERR_INVALID_ARG
+    assert _status("kvq_append_decode_noalloc", d, FAKE, FAKE, 1, FAKE, FAKE, F(0.1), FAKE, 65, None)[0] == \
+        kvq.KVQ_ERR_OUT_OF_RANGE
+    # 512 sequences x 64 heads x 2 splits x 130 floats of partials: above the 8 MiB array
+    big = ctypes.byref(kvq.make_cache(512, 64, 8, 128, FAKE, FAKE, FAKE, FAKE, max_len=4096))
+    st, msg = _status("kvq_append_decode_noalloc", big, FAKE, FAKE, 1, FAKE, FAKE, F(0.1), FAKE, 4096, None)
+    assert st == kvq.KVQ_ERR_WORKSPACE and "maximum" in msg
+
+
 @pytest.mark.parametrize("head_dim", [32, 256])
 def test_one_query_chunk_workspace_is_enough(head_dim):
     """kvq_workspace_size(cache, hint + 1, 1) covers a one-query chunk at head
