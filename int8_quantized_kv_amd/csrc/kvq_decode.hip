@@ -528,7 +528,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   const int forced_lf = env_int("KVQ_LONGEST_FIRST", -1);
   if (forced_lf >= 0) pl.longest_first = forced_lf != 0 && stream_kernel && c.batch <= kLongestFirstMax;
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
-  pl.counter_bytes = align_up(static_cast<size_t>(groups) * sizeof(int32_t), 256);
+  pl.counter_bytes = align_up(static_cast<size_t>(groups) * (1 + pl.num_splits) * sizeof(int32_t), 256);
   pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
                  partials * static_cast<size_t>(c.head_dim) * sizeof(float);
   return pl;

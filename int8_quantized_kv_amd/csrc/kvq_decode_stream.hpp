@@ -344,38 +344,53 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
     }
     return;
   }
-  // Partials go out as agent-scope stores, which bypass the per-XCD L2, so the
-  // workgroup that merges them (possibly on another XCD) reads them back with
-  // agent-scope loads; no L2 write-back or invalidate is needed.
-  for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
-    const int j = idx / D, d = idx % D;
-    const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + split;
-    __hip_atomic_store(&p.part_o[pidx * D + d], sm_o[j][d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (d == 0) {
-      __hip_atomic_store(&p.part_ml[pidx * 2], sm_ml[j][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.part_ml[pidx * 2 + 1], sm_ml[j][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Split merge.  Each split first takes a ticket from the (sequence, head
+  // group) counter.  The last to arrive merges: it keeps its own (m, l, o) in
+  // LDS and reads the others' from the workspace.  Every other split writes
+  // its partial, waits until those stores are acknowledged, then raises its
+  // ready flag; the last one waits for each flag before reading that partial
+  // (the flag's split has taken its ticket, so it is running and gets there).
+  // Partials and flags go through agent-scope (L2-bypassing) stores and
+  // loads, so a merge on another XCD sees them without any L2 write-back or
+  // invalidate.  The merger leaves the counter and flags zero for the next call.
+  const int64_t grp = static_cast<int64_t>(b) * gridDim.x + hg;   // grid x = head groups
+  int32_t* cnt = p.counters + grp;
+  int32_t* flags = p.counters + static_cast<int64_t>(gridDim.x) * gridDim.z + grp * p.num_splits;
+  if (threadIdx.x == 0) sm_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+  __syncthreads();
+  if (!sm_last) {
+    for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
+      const int j = idx / D, d = idx % D;
+      const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + split;
+      __hip_atomic_store(&p.part_o[pidx * D + d], sm_o[j][d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(&p.part_ml[pidx * 2], sm_ml[j][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.part_ml[pidx * 2 + 1], sm_ml[j][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+    // every wave's partial stores are acknowledged before the flag goes up:
+    // a workgroup-scope release emits no wait for global stores (and an
+    // agent-scope one a write-back of the whole L2), so wait for them
+    // explicitly (vmcnt 0; expcnt and lgkmcnt left at their maxima)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
-  // Every wave's partial stores have completed before the split is counted.
-  // A workgroup-scope release emits no wait for global stores, and an
-  // agent-scope one adds a write-back of the whole L2; the partials are
-  // agent-scope (write-through) stores, so waiting for their acknowledgement
-  // (vmcnt 0; expcnt and lgkmcnt left at their maxima) is what is needed.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t* cnt = p.counters + static_cast<int64_t>(b) * gridDim.x + hg;  // grid x = head groups
-    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == ns - 1;
-    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // all splits counted
-    sm_last = last;
+  // the merger: wait for every other split's flag (one lane each), and reset
+  for (int s2 = threadIdx.x; s2 < ns; s2 += NT) {
+    if (s2 == split) continue;
+    while (__hip_atomic_load(flags + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) __builtin_amdgcn_s_sleep(1);
+    __hip_atomic_store(flags + s2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (!sm_last) return;
 
-  // Merge.  All loads of one round are independent and unconditional
-  // (indices clamped, surplus entries masked), so they are in flight together.
+  // Merge in split order (the same order whichever split arrives last), this
+  // split's (m, l, o) from LDS.  All loads of one round are independent and
+  // unconditional (indices clamped, surplus entries masked), so they are in
+  // flight together.
   constexpr int kChunk = NT / HPW;   // splits whose (m, l) one round stages in LDS
   constexpr int kItems = (HPW * D + NT - 1) / NT;
   __shared__ float sm_sm[HPW][kChunk];
@@ -388,15 +403,21 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
     den[it] = 0.0f;
   }
   for (int c0 = 0; c0 < ns; c0 += kChunk) {
-    const int cnt = min(kChunk, ns - c0);
+    const int cnt_c = min(kChunk, ns - c0);
     {
       const int j = threadIdx.x / kChunk, u = threadIdx.x % kChunk;
       const int sidx = min(c0 + u, ns - 1);
       const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + sidx;
-      const float mv = __hip_atomic_load(&p.part_ml[pidx * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const float lv = __hip_atomic_load(&p.part_ml[pidx * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      sm_sm[j][u] = u < cnt ? mv : -INFINITY;
-      sm_sl[j][u] = u < cnt ? lv : 0.0f;
+      float mv, lv;
+      if (sidx == split) {
+        mv = sm_ml[j][0];
+        lv = sm_ml[j][1];
+      } else {
+        mv = __hip_atomic_load(&p.part_ml[pidx * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lv = __hip_atomic_load(&p.part_ml[pidx * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      sm_sm[j][u] = u < cnt_c ? mv : -INFINITY;
+      sm_sl[j][u] = u < cnt_c ? lv : 0.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -405,7 +426,7 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
       if (idx >= HPW * D) break;
       const int j = idx / D, d = idx % D;
       float cm = -INFINITY;
-      for (int u = 0; u < cnt; ++u) cm = fmaxf(cm, sm_sm[j][u]);
+      for (int u = 0; u < cnt_c; ++u) cm = fmaxf(cm, sm_sm[j][u]);
       const float newm = fmaxf(run_m[it], cm);
       if (newm == -INFINITY) continue;
       const float f_old = run_m[it] == -INFINITY ? 0.0f : exp2f(run_m[it] - newm);
@@ -413,20 +434,22 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
       den[it] *= f_old;
       run_m[it] = newm;
       const int64_t base = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + c0;
-      for (int u0 = 0; u0 < cnt; u0 += 8) {
+      for (int u0 = 0; u0 < cnt_c; u0 += 8) {
         float ov[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int uu = min(u0 + u, cnt - 1);
-          ov[u] = __hip_atomic_load(&p.part_o[(base + uu) * D + d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int uu = min(u0 + u, cnt_c - 1);
+          ov[u] = c0 + uu == split ? sm_o[j][d]
+                                   : __hip_atomic_load(&p.part_o[(base + uu) * D + d], __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int uu = u0 + u;
-          const float ms = uu < cnt ? sm_sm[j][uu] : -INFINITY;
+          const float ms = uu < cnt_c ? sm_sm[j][uu] : -INFINITY;
           const float f = ms == -INFINITY ? 0.0f : exp2f(ms - newm);
           num[it] = fmaf(ov[u], f, num[it]);
-          den[it] = fmaf(uu < cnt ? sm_sl[j][uu] : 0.0f, f, den[it]);
+          den[it] = fmaf(uu < cnt_c ? sm_sl[j][uu] : 0.0f, f, den[it]);
         }
       }
     }
@@ -631,7 +654,10 @@ __device__ void ring_into_wave(const DecodeParams& p, int b, int kvh, int h0, in
 // ---------------------------------------------------------------------------
 // SM: scale mode (kSmToken fp32 per token, kSmGroup32, kSmTokenBf16 bf16 per
 // token), a template argument so each mode pays only for its own decoding
-template <int D, int HPW, int SM, bool PAGED, bool APPEND>
+// WIN: a sliding window (p.window > 0), a template argument so that the
+// plain kernel's code holds no path where the first block's loads wait for
+// the length (the compiler's wait counts after such a join are conservative)
+template <int D, int HPW, int SM, bool PAGED, bool APPEND, bool WIN>
 __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(DecodeParams p) {
   // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
   // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
@@ -752,7 +778,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // clamped per-lane row of token t of the block starting at s0 (whose page ids
   // are pid): the clamp keeps t inside the block, so no table read is needed
   auto block_row = [&](int s0, int t, const int32_t (&pid)[kPages]) -> int64_t {
-    t = min(t, t_end - 1);
+    t = max(min(t, t_end - 1), 0);  // (row 0 stands in when the range is empty)
     if constexpr (PAGED) {
       // the ids are uniform: reading them through readfirstlane makes the
       // per-lane choice a select of values, which the optimiser would otherwise
@@ -767,7 +793,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     }
   };
   auto row_of = [&](int t) -> int64_t {                  // clamped per-lane row (table read)
-    t = min(t, t_end - 1);
+    t = max(min(t, t_end - 1), 0);  // (row 0 stands in when the range is empty)
     if constexpr (PAGED) {
       int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (t >> 4)];
       phys = min(max(phys, 0), p.geom.num_pages - 1);
@@ -1082,9 +1108,25 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 
   // the wave index is uniform, so every block condition below is a scalar branch
   int blk = wave;
-  // the length and the queries go out before the first block's K/V loads, so
-  // they do not queue behind the bulk traffic every workgroup starts with
+  // The length, the fused append's new row and the queries go out before the
+  // first block's K/V loads, so they do not queue behind the bulk traffic
+  // every workgroup starts with.  The code between these loads and the
+  // queries' use holds no loop of memory operations, so the wait for the
+  // queries covers the queries alone, not the first block as well (the
+  // compiler's wait counts are exact only through straight-line code).
   const int len_raw = p.seq_lens[b];
+  // fused append: waves 0 and 1 fetch the new K and V rows of this KV head
+  // (with a recent window the row to quantize is the one leaving the ring,
+  // fetched once the length is known)
+  constexpr int kEpl = row_epl(D);
+  uint4 xraw = make_uint4(0u, 0u, 0u, 0u);  // the row's raw bytes, converted where they are quantized
+  const bool xbf16 = p.new_bf16 != 0;
+  if (APPEND && p.rwin == 0) {
+    const size_t esz = xbf16 ? 2 : 4;
+    const char* src = static_cast<const char*>(wave == 0 ? p.new_k : p.new_v) +
+                      (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * esz;
+    xraw = load_row_raw<kEpl>(src, lane, wave < 2 && lane < D / kEpl, xbf16);
+  }
   uint4 qraw[HPW][2];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
@@ -1098,32 +1140,17 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       for (int k = 0; k < kPidAhead; ++k)
         if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
     }
-    if (t_begin + blk * kBlock < t_end) {
-      load_k(blk, pq[0]);
-      load_v(blk, pq[0]);
-      load_block_scales(blk, pq[0]);
-    }
+    // unconditional (rows clamped into the range, row 0 if it is empty), so
+    // that every path issues the same loads and the waits after them stay exact
+    load_k(blk, pq[0]);
+    load_v(blk, pq[0]);
+    load_block_scales(blk, pq[0]);
   };
-  if (p.window == 0) first_loads();  // speculative first block
-  // fused append: waves 0 and 1 fetch the new K and V rows of this KV head
-  // (with a recent window the row to quantize is the one leaving the ring,
-  // fetched once the length is known)
-  constexpr int kEpl = row_epl(D);
-  float xnew[kEpl];
-  if (APPEND && p.rwin == 0) {
-    const size_t esz = p.new_bf16 ? 2 : 4;
-    const char* src = static_cast<const char*>(wave == 0 ? p.new_k : p.new_v) +
-                      (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * esz;
-    load_row_values<kEpl>(src, lane, wave < 2 && lane < D / kEpl, p.new_bf16 != 0, xnew);
-  }
+  if constexpr (!WIN) first_loads();  // speculative first block
   const int L = len_raw < 0 ? 0 : (len_raw > p.len_cap ? p.len_cap : len_raw);
-  if (L == 0 && split == 0) {  // empty window: the output is zero
-    for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads)
-      p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
-  }
   const int L8 = L > p.rwin ? L - p.rwin : 0;  // INT8 tokens (all of them without a recent window)
   int t_base = 0;  // first token of split 0
-  if (p.window > 0) {
+  if constexpr (WIN) {
     t_min = max(L - p.window, 0);
     t_base = t_min & ~(kBlock - 1);
     t_begin = t_base + split * p.split_len;
@@ -1132,13 +1159,19 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // recent window: the workgroup of the last INT8 split (split 0 if there is
   // none) also attends to the ring
   const bool ring_here = p.rwin > 0 && L > 0 && split == (ns8 > 0 ? ns8 - 1 : 0);
-  if ((split >= ns8 || t_begin >= L8) && !ring_here) return;  // no tokens here (and not counted)
+  if ((split >= ns8 || t_begin >= L8) && !ring_here) {  // no tokens here (and not counted)
+    if (L == 0 && split == 0) {  // empty window: the output is zero
+      for (int idx = threadIdx.x; idx < HPW * D; idx += kStreamThreads)
+        p.out[(static_cast<int64_t>(b) * H + h0 + idx / D) * D + idx % D] = 0;
+    }
+    return;
+  }
   const int t_end_spec = t_end;
   t_end = split == ns8 - 1 ? L8 : min(L8, t_begin + p.split_len);  // the last split takes the remainder
   const int nblk = t_end > t_begin ? (t_end - t_begin + kBlock - 1) / kBlock : 0;
   const int ns = ns8 > 0 ? ns8 : 1;
-  if (p.window > 0) {
-    first_loads();
+  if constexpr (WIN) {
+    // (the first block's loads go out after the queries' prescale, below)
   } else if constexpr (PAGED) {
     // a remainder joined to the last split lies past the speculative bound:
     // fetch the page ids the queue skipped
@@ -1156,15 +1189,45 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // out of the window.
   pn = L8 - 1;
   owns_new = APPEND && pn >= t_begin && pn < t_end;
-  if (APPEND && p.rwin > 0 && owns_new) {
-    const uint16_t* src = (wave == 0 ? p.rk : p.rv) +
-                          ((static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap + pn % p.rcap) * D;
-    load_row_values<kEpl>(src, lane, wave < 2 && lane < D / kEpl, true, xnew);
+
+  // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    float qf[16];
+    bf16x8_to_f32(qraw[j][0], &qf[0]);
+    bf16x8_to_f32(qraw[j][1], &qf[8]);
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(qf[e]));
+    a = group_max<LK>(a);
+    const int kq = a > 0.0f ? 14 - ilogbf(a) : 0;
+    float qs = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b0 = f16_bits(ldexpf(qf[2 * k], kq)), b1 = f16_bits(ldexpf(qf[2 * k + 1], kq));
+      qs += f16_value(b0) + f16_value(b1);
+      qp[j][k] = b0 | (b1 << 16);
+    }
+    fold_row[j] = FP8 ? 0.0f : uniform(group_sum<LK>(qs * (128.0f * 0x1p-24f)));
+    // INT8 per-token codes enter as c 2^-24; group-32 and FP8 as exact values
+    cst[j] = uniform(ldexpf(p.scale_log2, (G32 || FP8 ? 0 : 24) - kq));
   }
 
+  // a sliding window's first block, whose range needed the length
+  if constexpr (WIN) first_loads();
+  // fused append, after the queries' prescale (its stores would otherwise
+  // make the wait for the queries cover the first block too)
   if constexpr (APPEND) {
     if (owns_new) {
       if (wave < 2) {
+        float xnew[kEpl];
+        if (p.rwin > 0) {  // the ring row leaving the window (its own branch: this load is waited for at once)
+          const uint16_t* src = (wave == 0 ? p.rk : p.rv) +
+                                ((static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap + pn % p.rcap) * D;
+          row_raw_values<kEpl>(load_row_raw<kEpl>(src, lane, lane < D / kEpl, true), true, xnew);
+        } else {
+          row_raw_values<kEpl>(xraw, xbf16, xnew);
+        }
         float sc = 0.0f;
         uint32_t packed;
         if constexpr (FP8) packed = fp8_encode_lane<kEpl, E5>(xnew);
@@ -1190,29 +1253,6 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       }
       __syncthreads();
     }
-  }
-
-  // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    float qf[16];
-    bf16x8_to_f32(qraw[j][0], &qf[0]);
-    bf16x8_to_f32(qraw[j][1], &qf[8]);
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(qf[e]));
-    a = group_max<LK>(a);
-    const int kq = a > 0.0f ? 14 - ilogbf(a) : 0;
-    float qs = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t b0 = f16_bits(ldexpf(qf[2 * k], kq)), b1 = f16_bits(ldexpf(qf[2 * k + 1], kq));
-      qs += f16_value(b0) + f16_value(b1);
-      qp[j][k] = b0 | (b1 << 16);
-    }
-    fold_row[j] = FP8 ? 0.0f : uniform(group_sum<LK>(qs * (128.0f * 0x1p-24f)));
-    // INT8 per-token codes enter as c 2^-24; group-32 and FP8 as exact values
-    cst[j] = uniform(ldexpf(p.scale_log2, (G32 || FP8 ? 0 : 24) - kq));
   }
 
   for (; blk + kStreamWaves < nblk; blk += kStreamWaves) run_block(blk, std::true_type{});
@@ -1270,16 +1310,21 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 template <int SM>
 void launch_stream_impl(int head_dim, int hpw, bool paged, bool append, const DecodeParams& p, dim3 grid,
                         hipStream_t st) {
-  auto go = [&](auto dc, auto hc) {
+  auto go2 = [&](auto dc, auto hc, auto wc) {
     constexpr int D = decltype(dc)::value;
     constexpr int HPW = decltype(hc)::value;
+    constexpr bool WIN = decltype(wc)::value;
     if (paged) {
-      if (append) hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, true, true>), grid, dim3(kStreamThreads), 0, st, p);
-      else hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, true, false>), grid, dim3(kStreamThreads), 0, st, p);
+      if (append) hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, true, true, WIN>), grid, dim3(kStreamThreads), 0, st, p);
+      else hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, true, false, WIN>), grid, dim3(kStreamThreads), 0, st, p);
     } else {
-      if (append) hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, false, true>), grid, dim3(kStreamThreads), 0, st, p);
-      else hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, false, false>), grid, dim3(kStreamThreads), 0, st, p);
+      if (append) hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, false, true, WIN>), grid, dim3(kStreamThreads), 0, st, p);
+      else hipLaunchKernelGGL((decode_stream_kernel<D, HPW, SM, false, false, WIN>), grid, dim3(kStreamThreads), 0, st, p);
     }
+  };
+  auto go = [&](auto dc, auto hc) {
+    if (p.window > 0) go2(dc, hc, std::true_type{});
+    else go2(dc, hc, std::false_type{});
   };
   auto by_hpw = [&](auto dc) {
     if (hpw == 4) go(dc, std::integral_constant<int, 4>{});

@@ -85,6 +85,49 @@ __device__ __forceinline__ uint32_t quantize_lane(const float (&x)[EPL], float& 
 }
 
 // Stores this lane's EPL codes of a row that starts at `codes`.
+// The same values in two steps: the raw bytes of this lane's EPL elements
+// (fp32 or bf16, up to 16 bytes), and their fp32 values.  Splitting them
+// lets a load go out early while its conversion waits for the use, so the
+// load is not waited for on the spot.
+template <int EPL>
+__device__ __forceinline__ uint4 load_row_raw(const void* row, int lane, bool active, bool bf16) {
+  uint4 r = make_uint4(0u, 0u, 0u, 0u);
+  if (!active) return r;
+  if (bf16) {
+    const uint16_t* p = static_cast<const uint16_t*>(row) + lane * EPL;
+    if constexpr (EPL == 1) r.x = p[0];
+    else if constexpr (EPL == 2) r.x = *reinterpret_cast<const uint32_t*>(p);
+    else {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      r.x = v.x;
+      r.y = v.y;
+    }
+  } else {
+    const float* p = static_cast<const float*>(row) + lane * EPL;
+    if constexpr (EPL == 1) r.x = __float_as_uint(p[0]);
+    else if constexpr (EPL == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      r.x = v.x;
+      r.y = v.y;
+    } else {
+      r = *reinterpret_cast<const uint4*>(p);
+    }
+  }
+  return r;
+}
+
+template <int EPL>
+__device__ __forceinline__ void row_raw_values(uint4 r, bool bf16, float (&x)[EPL]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if (bf16) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) x[e] = __uint_as_float(w[e]);
+  }
+}
+
 template <int EPL>
 __device__ __forceinline__ void store_lane_codes(uint8_t* codes, int lane, uint32_t packed) {
   uint8_t* out = codes + lane * EPL;
