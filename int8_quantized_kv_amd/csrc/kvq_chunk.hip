@@ -18,10 +18,12 @@
 //     8-byte row piece (four f16), and lane j gets element j % 4 of the
 //     pieces named by lanes j / 4 + 4b, b = 0..3; two such reads give a
 //     lane its eight k-slots.
-//   * queries are scaled by one power of two per workgroup into f16 range
-//     (exact for bf16 inputs); the per-token K scale, the attention scale,
-//     log2 e and that power of two form one staged factor per token, so a
-//     score is one FMA: z_t = acc * kc_t + log2 sV_t.  The V scale rides in
+//   * queries are scaled by powers of two into f16 range (exact for bf16
+//     inputs): the per-token K scale, the attention scale, log2 e and the
+//     workgroup's power of two (set by its largest query) form one staged
+//     factor per token, so a score is one FMA: z_t = acc * kc_t + log2 sV_t;
+//     a wave whose own queries are much smaller scales them by a larger power
+//     of two and brings its scores back to the workgroup's before the FMA.  The V scale rides in
 //     the exponent of the weight, w_t = 2^(z_t - m), and the normaliser sums
 //     w_t / sV_t.
 //   * one workgroup = 8 waves = 8 (query head, 32-position block) items of
@@ -91,8 +93,8 @@ struct ChunkParams {
 
 // LDS tile geometry for TOK tokens.  K rows hold D f16 values and are padded
 // by 16 bytes, so the 16 lanes of one K read (16 consecutive rows, one
-// 16-byte unit) fall on distinct banks.  V rows hold D codes in 8-byte units,
-// XOR-permuted so the 32 lanes of one V transpose read (8 rows x 4 units) do.
+// 16-byte unit) fall on distinct banks.  V rows also hold D f16 values (the
+// codes are widened while staging), with the padding described below.
 // With group-32 scales (G32) a buffer also holds, per token, the ratios of
 // consecutive K group scales s_g / s_(g+1) (fp32, groups 0 .. G-2) and the
 // f16 ratios s_g / s_max of V.
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   const int qi = pos0 + col;
   const bool q_ok = active && qi < p.n;
 
-  // ---- queries: one power-of-two scale for the workgroup
+  // ---- queries: each wave's largest magnitude (the powers of two are set below)
   uint4 qraw[kKK];
   {
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(b) * p.heads + head) * p.n + (q_ok ? qi : 0)) * D;
@@ -375,17 +377,27 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   load_tile(tbase);
   __syncthreads();  // sm_qmax (and the cleared values)
 
+  // The staged K factor carries the workgroup's power of two 2^-kq (set by
+  // its largest query); each wave scales its own queries by 2^kqw (set by
+  // its own largest), so a head much smaller than another head of the
+  // workgroup keeps its bits instead of falling into f16 subnormals, and
+  // multiplies its scores by 2^(kq - kqw) <= 1 before the K factor (a
+  // uniform branch, not taken when the two agree).
+  auto pow2_for = [](float amax, int dflt) {
+    if (!(amax > 0.0f && amax <= 3.0e38f)) return dflt;
+    int ex;
+    (void)frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+    return min(max(15 - ex, -120), 120);
+  };
   int kq = 0;
   {
     float amax = 0.0f;
 #pragma unroll
     for (int w = 0; w < kCkWaves; ++w) amax = fmaxf(amax, sm_qmax[w]);
-    if (amax > 0.0f && amax <= 3.0e38f) {
-      int ex;
-      (void)frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
-      kq = min(max(15 - ex, -120), 120);
-    }
+    kq = pow2_for(amax, 0);
   }
+  const int kqw = __builtin_amdgcn_readfirstlane(pow2_for(sm_qmax[wave], kq));
+  const float qcorr = ldexpf(1.0f, kq - kqw);
   const float kfac = ldexpf(p.scale_log2, -kq);
   f16x8 qop[kKK];  // B of S^T = K Q^T: k-slot 8*half + e <-> d = 16kk + 8*half + e
 #pragma unroll
@@ -394,7 +406,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     f16x8 v;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const f16x2 h2 = pack2(ldexpf(__uint_as_float(w[e] << 16), kq), ldexpf(__uint_as_float(w[e] & 0xffff0000u), kq));
+      const f16x2 h2 = pack2(ldexpf(__uint_as_float(w[e] << 16), kqw), ldexpf(__uint_as_float(w[e] & 0xffff0000u), kqw));
       v[2 * e] = h2[0];
       v[2 * e + 1] = h2[1];
     }
@@ -518,6 +530,10 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     const float* kc = reinterpret_cast<const float*>(bc + TL::kKc);
     const float* lsv = reinterpret_cast<const float*>(bc + TL::kLsv);
     const float* rsv = reinterpret_cast<const float*>(bc + TL::kRsv);
+    if (kqw != kq) {  // this wave's queries carry a larger power of two than the K factor expects
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) s[tt] *= qcorr;
+    }
     float z[kTT][16];
 #pragma unroll
     for (int tt = 0; tt < kTT; ++tt) {
