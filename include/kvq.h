@@ -52,7 +52,7 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID_ARG = 1,  /* bad descriptor or argument (host-checkable)        */
   KVQ_ERR_OUT_OF_RANGE = 2, /* host-known size beyond the cache capacity          */
-  KVQ_ERR_UNSUPPORTED = 3,  /* valid but not implemented (e.g. head_dim 96 decode) */
+  KVQ_ERR_UNSUPPORTED = 3,  /* valid but not implemented (e.g. FP8 recent window) */
   KVQ_ERR_HIP = 4,          /* kernel launch failed (hipGetLastError)             */
   KVQ_ERR_WORKSPACE = 5     /* workspace missing or smaller than required          */
 } kvq_status;
@@ -153,13 +153,16 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k_new, const void* v_n
  *               clamped to [0, min(hint, capacity)]; a length of 0 gives zeros)
  *   out       : device bf16 [B, H, D]
  *   workspace : device scratch of at least kvq_workspace_size(cache,
- *               max_seq_len_hint, 1) bytes: split counters followed by split
- *               partials.  Zero-fill it once after allocation; every call
- *               returns the counters to zero, so it can be reused by later
- *               calls on the same stream.  Calls that overlap in time (other
- *               streams) must not share a workspace.
+ *               max_seq_len_hint, 1) bytes: split arrival counters and
+ *               ready flags, then split partials.  Zero-fill it once after
+ *               allocation; every call returns the counters and flags to zero,
+ *               so it can be reused by later calls on the same stream.  Calls
+ *               that overlap in time (other streams) must not share a
+ *               workspace.
  * Errors: INVALID_ARG, OUT_OF_RANGE (hint beyond capacity or < 1),
- * WORKSPACE, UNSUPPORTED (head_dim not in {32, 64, 128, 256}), HIP.
+ * WORKSPACE, HIP.  Head dims 32, 64 and 128 run on the streaming kernel; the
+ * other multiples of 32 up to 256 on a generic kernel (fp32 arithmetic,
+ * a separate merge launch).
  */
 kvq_status kvq_attention_decode(const kvq_cache* cache, const uint16_t* q,
                                 const int32_t* seq_lens, float attn_scale, uint16_t* out,
@@ -195,9 +198,9 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const vo
  * f16 MFMA with the codes as exact f16 values and the scales applied to the
  * fp32 scores and weights (group-32 K scales to the fp32 score accumulator
  * group by group; group-32 V ratios to the f16 weights of each 32-dim output
- * tile); bf16 output.  Head dims 32 and 256 run instead as one decode per
- * (sequence, query) over the keys that query sees (fp32 arithmetic, split
- * partials in the workspace; batch * n at most 65535).
+ * tile); bf16 output.  Head dims other than 64 and 128 run instead as one
+ * decode per (sequence, query) over the keys that query sees (fp32
+ * arithmetic, split partials in the workspace; batch * n at most 65535).
  *
  *   q        : device bf16 [B, H, n, D];  out : device bf16 [B, H, n, D]
  *   ctx_lens : device int32 [B], tokens cached before the chunk
@@ -208,9 +211,8 @@ kvq_status kvq_append_decode(const kvq_cache* cache, const void* k_new, const vo
  *              64 and 128, where NULL is accepted
  * Keys beyond the cache capacity do not exist: a query sees at most
  * min(ctx_lens[b] + n, capacity) keys.
- * Errors: INVALID_ARG, OUT_OF_RANGE (batch * n above 65535 for head dims 32
- * and 256), WORKSPACE, UNSUPPORTED (head_dim other than 32, 64, 128, 256),
- * HIP.
+ * Errors: INVALID_ARG, OUT_OF_RANGE (batch * n above 65535 for head dims
+ * other than 64 and 128), WORKSPACE, HIP.
  */
 kvq_status kvq_attention_chunk(const kvq_cache* cache, const uint16_t* q, int32_t n,
                                const int32_t* ctx_lens, int32_t causal, float attn_scale,
@@ -307,7 +309,7 @@ kvq_status kvq_append_recent(const kvq_cache* cache, const kvq_recent* recent, c
  * dequantized, then the recent rows).  The ring is one more split of the
  * split-K launch.  seq_lens[b] is clamped to [0, min(hint, capacity of the
  * INT8 cache)].  Workspace: kvq_workspace_size_recent(cache, recent, hint).
- * Head dims 64 and 128 run on the streaming kernel; 32 and 256 on the
+ * Head dims 64 and 128 run on the streaming kernel; the others on the
  * generic one, whose ring is a second loop after the INT8 rows.
  * Errors: those of kvq_attention_decode.
  */
@@ -351,7 +353,7 @@ kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, 
  * head_dim 64 and 128: the MFMA chunk kernel attends to the INT8 keys and
  * writes the queries that see no ring row; a second launch attends the last
  * min(n, window) queries of each sequence to the ring rows and merges the
- * two partial softmaxes.  head_dim 32 and 256: one decode per (sequence,
+ * two partial softmaxes.  Other head dims: one decode per (sequence,
  * query) through the generic kernel.  batch * n at most 65535.
  *   q, out, ctx_lens, max_ctx_len_hint: as kvq_attention_chunk; ctx_lens[b]
  *              must not exceed the hint (at head_dim 64 and 128 a larger
@@ -395,20 +397,22 @@ uint64_t kvq_cache_bytes(const kvq_cache* cache);
  * kvq_append_decode_noalloc — kvq_append_decode for callers that cannot
  * allocate or own device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the same launch and kernels, with
- * the split counters and partials in a static device array of 8 MiB that the
- * library holds on each GPU it runs on until the process ends.  The caller
- * passes inputs and outputs only; no workspace argument, and the call
- * allocates nothing.  The array's address on a device is looked up at the
- * first call on that device, which also clears its counter region on
- * `stream` ahead of its own kernel; every completed call leaves the counters
- * zero again.  All calls on one GPU share the array: calls that overlap in
- * time on one GPU (other streams, other threads) race and must not be made.
+ * the split counters, ready flags and partials in a static device array of
+ * 8 MiB that the library holds on each GPU it runs on until the process
+ * ends.  The caller passes inputs and outputs only; no workspace argument,
+ * and the call allocates nothing.  The array's address on a device is
+ * looked up at the first call on that device, which also clears its 64 KiB
+ * counter region on `stream` ahead of its own kernel; every completed call
+ * leaves the counters and flags zero again.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must not be made.
  *
  *   arguments : as kvq_append_decode, without workspace / workspace_bytes
- * Errors: those of kvq_append_decode; WORKSPACE when the call's split
- * partials would exceed the array (batch * num_heads * splits * (head_dim + 2)
- * * 4 bytes above 8 MiB less the 64 KiB counter region), HIP if the array's
- * address cannot be obtained.
+ * Errors: those of kvq_append_decode; WORKSPACE when the call's counters and
+ * flags (4 * batch * head groups * (1 + splits) bytes) exceed 64 KiB or its
+ * split partials (batch * num_heads * splits * (head_dim + 2) * 4 bytes)
+ * exceed the rest of the array; HIP if the array's address cannot be
+ * obtained.
  */
 kvq_status kvq_append_decode_noalloc(const kvq_cache* cache, const void* k_new, const void* v_new,
                                      int32_t in_dtype, const uint16_t* q, const int32_t* seq_lens,

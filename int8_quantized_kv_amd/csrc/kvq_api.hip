@@ -171,7 +171,7 @@ kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, cons
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
                 capacity_of(*c));
   if (!decode_supported(c->head_dim))
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (multiples of 32 up to 256)", who, c->head_dim);
   const RecentGeom rc = recent_of(r);
   const DecodePlan plan = plan_decode(*c, max_seq_len_hint, rc, window);
   st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
@@ -329,7 +329,7 @@ KVQ_API kvq_status kvq_append_decode_noalloc(const kvq_cache* c, const void* k_n
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_seq_len_hint (%d) must be in [1, %d]", who, max_seq_len_hint,
                 capacity_of(*c));
   if (!decode_supported(c->head_dim))
-    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (32, 64, 128, 256)", who, c->head_dim);
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d not supported (multiples of 32 up to 256)", who, c->head_dim);
   // the caller's plan, with the split counters moved to the fixed region at
   // the front of the array and the partials after it
   DecodePlan plan = plan_decode(*c, max_seq_len_hint);

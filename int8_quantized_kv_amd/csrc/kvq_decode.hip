@@ -2,234 +2,10 @@
 // the MFMA chunk kernel does not take) and its merge, the split planner, and
 // the launch of both kernels.  The streaming kernel lives in
 // kvq_decode_stream.hpp.
-#include "kvq_decode_stream.hpp"
+#include "kvq_decode_generic.hpp"
 
 namespace kvq {
 namespace {
-
-// ---------------------------------------------------------------------------
-// Generic kernel (any supported head_dim): fp32 FMAs on codes widened in
-// registers, per-lane online softmax, partials merged by decode_merge_kernel.
-// On a hybrid cache a second loop takes the bf16 ring rows of the split.
-// ---------------------------------------------------------------------------
-template <int D, int HPW, int SM, bool PAGED>
-__global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p) {
-  constexpr bool G32 = SM == kSmGroup32;
-  constexpr bool FP8 = SM == kSmFp8E4M3 || SM == kSmFp8E5M2;  // values, no scales
-  constexpr bool E5 = SM == kSmFp8E5M2;
-  constexpr int LPT = D / 16;          // lanes per token row (16 bytes each)
-  constexpr int TPW = kWave / LPT;     // token rows per wave pass
-  constexpr int TPP = TPW * kWaves;    // token rows per workgroup pass
-  constexpr int U = 4;                 // passes issued together
-
-  __shared__ float sm_o[kWaves][HPW][D];
-  __shared__ float sm_m[kWaves][HPW];
-  __shared__ float sm_l[kWaves][HPW];
-
-  const int hg = blockIdx.x;
-  const int split = blockIdx.y;
-  const int v = blockIdx.z;  // the launch never sets longest_first for this kernel
-  int b, qi;
-  const int L = row_len(p, v, b, qi);
-  const int nq = p.chunk_n > 0 ? p.chunk_n : 1;
-  const int kvh = hg / p.wg_per_kvh;
-  const int H = p.num_heads;
-  const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int sub = lane % LPT;
-  const int slot = lane / LPT;
-
-  // recent window: positions from L8 on are bf16 rows in the ring
-  const int L8 = ring_start(p, b, L);
-  const int t_lo = p.window > 0 ? max(L - p.window, 0) : 0;  // first visible key
-  const int t_begin = t_lo + split * p.split_len;
-  const int nsg = split_count(L - t_lo, p.split_len);
-  if (split >= nsg) return;
-  const int t_end = split == nsg - 1 ? L : t_begin + p.split_len;  // the last split takes the remainder
-  const int t8_end = min(t_end, L8);  // INT8 tokens of this split end here
-  const int npass = t8_end > t_begin ? (t8_end - t_begin + TPP - 1) / TPP : 0;
-
-  float q[HPW][16];
-  float qsum[HPW];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const uint4* qp =
-        reinterpret_cast<const uint4*>(p.q + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16);
-    bf16x8_to_f32(qp[0], &q[j][0]);
-    bf16x8_to_f32(qp[1], &q[j][8]);
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s += q[j][e];
-    qsum[j] = s;
-  }
-  const int grp = G32 ? (sub * 16) / 32 : 0;
-
-  float m[HPW], l[HPW], ws[HPW], o[HPW][16];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    m[j] = -INFINITY;
-    l[j] = 0.0f;
-    ws[j] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[j][e] = 0.0f;
-  }
-
-  for (int ip = 0; ip < npass; ip += U) {
-    uint4 kb[U], vb[U];
-    float ks[U], vs[U];
-    bool ok[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // unconditional loads from a clamped row; out-of-range tokens are
-      // discarded through their -inf score
-      const int t = t_begin + (ip + u) * TPP + wave * TPW + slot;
-      ok[u] = t < t8_end;
-      const int tc = min(t, t8_end - 1);
-      int64_t row;
-      if constexpr (PAGED) {
-        int phys = p.geom.block_table[static_cast<int64_t>(b) * p.geom.max_blocks + (tc >> 4)];
-        phys = min(max(phys, 0), p.geom.num_pages - 1);
-        row = (static_cast<int64_t>(phys) * p.geom.kvh + kvh) * kPageSize + (tc & (kPageSize - 1));
-      } else {
-        row = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.geom.max_len + tc;
-      }
-      kb[u] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + sub * 16);
-      vb[u] = *reinterpret_cast<const uint4*>(p.v_codes + row * D + sub * 16);
-      ks[u] = FP8 ? 1.0f : load_scale(p.k_scales, row * p.groups + grp, p.scale_bf16 != 0);
-      vs[u] = FP8 ? 1.0f : load_scale(p.v_scales, row * p.groups + grp, p.scale_bf16 != 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t kw[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
-      const uint32_t vw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
-      float part[HPW];
-#pragma unroll
-      for (int j = 0; j < HPW; ++j) part[j] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float c = FP8 ? fp8_decode<E5>((kw[i] >> (8 * e)) & 0xffu) : byte_f32(kw[i], e);
-#pragma unroll
-          for (int j = 0; j < HPW; ++j) part[j] = fmaf(q[j][4 * i + e], c, part[j]);
-        }
-      float cv[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) cv[4 * i + e] = FP8 ? fp8_decode<E5>((vw[i] >> (8 * e)) & 0xffu) : byte_f32(vw[i], e);
-#pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        float sc = FP8 ? part[j] : (part[j] - 128.0f * qsum[j]) * ks[u];
-        sc = group_sum<LPT>(sc) * p.scale_log2;
-        const float sj = ok[u] ? sc : -INFINITY;
-        if (sj > m[j] + kLazy) {
-          const float alpha = exp2f(m[j] - sj);
-          l[j] *= alpha;
-          ws[j] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
-          m[j] = sj;
-        }
-        const float pj = ok[u] ? exp2f(sj - m[j]) : 0.0f;
-        l[j] += pj;
-        const float w = ok[u] ? pj * vs[u] : 0.0f;
-        ws[j] += w;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[j][e] = fmaf(w, cv[e], o[j][e]);
-      }
-    }
-  }
-
-  // ring rows (bf16 values, no scale and no offset): one token per lane slot
-  // and pass, the same online softmax
-  if (p.rwin > 0) {
-    const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
-    for (int tb = max(t_begin, L8); tb < t_end; tb += TPP) {
-      const int t = tb + wave * TPW + slot;
-      const bool okr = t < t_end;
-      const int64_t slot_row = ring0 + min(t, t_end - 1) % p.rcap;
-      const uint4* kr = reinterpret_cast<const uint4*>(p.rk + slot_row * D + sub * 16);
-      const uint4* vr = reinterpret_cast<const uint4*>(p.rv + slot_row * D + sub * 16);
-      float kx[16], vx[16];
-      bf16x8_to_f32(kr[0], &kx[0]);
-      bf16x8_to_f32(kr[1], &kx[8]);
-      bf16x8_to_f32(vr[0], &vx[0]);
-      bf16x8_to_f32(vr[1], &vx[8]);
-#pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        float part = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) part = fmaf(q[j][e], kx[e], part);
-        const float sc = group_sum<LPT>(part) * p.scale_log2;
-        const float sj = okr ? sc : -INFINITY;
-        if (sj > m[j] + kLazy) {
-          const float alpha = exp2f(m[j] - sj);
-          l[j] *= alpha;
-          ws[j] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) o[j][e] *= alpha;
-          m[j] = sj;
-        }
-        const float pj = okr ? exp2f(sj - m[j]) : 0.0f;
-        l[j] += pj;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[j][e] = fmaf(pj, vx[e], o[j][e]);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[j][e] = FP8 ? o[j][e] : fmaf(-128.0f, ws[j], o[j][e]);
-    float M = m[j];
-    for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
-    const float f = (m[j] == -INFINITY) ? 0.0f : exp2f(m[j] - M);
-    l[j] *= f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[j][e] *= f;
-    for (int off = LPT; off < kWave; off <<= 1) {
-      l[j] += __shfl_xor(l[j], off, kWave);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[j][e] += __shfl_xor(o[j][e], off, kWave);
-    }
-    m[j] = M;
-  }
-  if (slot == 0) {
-#pragma unroll
-    for (int j = 0; j < HPW; ++j) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sm_o[wave][j][sub * 16 + e] = o[j][e];
-      if (sub == 0) {
-        sm_m[wave][j] = m[j];
-        sm_l[wave][j] = l[j];
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < HPW * D; idx += kThreads) {
-    const int j = idx / D;
-    const int d = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][j]);
-    float acc = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = sm_m[w][j] == -INFINITY ? 0.0f : exp2f(sm_m[w][j] - M);
-      acc = fmaf(sm_o[w][j][d], f, acc);
-      lsum = fmaf(sm_l[w][j], f, lsum);
-    }
-    const int64_t pidx = (static_cast<int64_t>(v) * H + h0 + j) * p.num_splits + split;
-    p.part_o[pidx * D + d] = acc;
-    if (d == 0) {
-      p.part_ml[pidx * 2] = M;
-      p.part_ml[pidx * 2 + 1] = lsum;
-    }
-  }
-}
 
 // Log-sum-exp merge of the split partials of one (sequence, head); bf16 out.
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D) {
@@ -423,7 +199,7 @@ int heads_per_wg(int gqa) {
   return 1;
 }
 
-bool use_stream(int head_dim) { return head_dim <= 128; }
+bool use_stream(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
 
 int pass_tokens(int head_dim, bool stream_kernel) {
   // tokens a workgroup consumes per step: whole 64-token wave blocks for the
@@ -431,42 +207,28 @@ int pass_tokens(int head_dim, bool stream_kernel) {
   return stream_kernel ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
 }
 
-template <int D, int HPW, int SM, bool PAGED>
-void launch_generic(const DecodeParams& p, dim3 grid, hipStream_t st) {
-  if constexpr (D == 256) {  // (the planner picks the generic kernel for head_dim 256 only)
-    hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, PAGED>), grid, dim3(kThreads), 0, st, p);
+// The generic kernel at any supported head dim.
+void launch_generic_any(int head_dim, int hpw, int sm, bool paged, const DecodeParams& p, dim3 grid,
+                        hipStream_t st) {
+  switch (head_dim) {
+    case 32: launch_generic_all<32>(hpw, sm, paged, p, grid, st); break;
+    case 64: launch_generic_all<64>(hpw, sm, paged, p, grid, st); break;
+    case 128: launch_generic_all<128>(hpw, sm, paged, p, grid, st); break;
+    case 256: launch_generic_all<256>(hpw, sm, paged, p, grid, st); break;
+    default: launch_generic_wide(head_dim, hpw, sm, paged, p, grid, st); break;
   }
 }
 
-template <int D, int HPW>
-void launch_generic_modes_d(int sm, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
-  auto go = [&](auto smc) {
-    constexpr int SM = decltype(smc)::value;
-    if (paged) launch_generic<D, HPW, SM, true>(p, grid, st);
-    else launch_generic<D, HPW, SM, false>(p, grid, st);
-  };
-  switch (sm) {
-    case kSmGroup32: go(std::integral_constant<int, kSmGroup32>{}); break;
-    case kSmTokenBf16: go(std::integral_constant<int, kSmTokenBf16>{}); break;
-    case kSmFp8E4M3: go(std::integral_constant<int, kSmFp8E4M3>{}); break;
-    case kSmFp8E5M2: go(std::integral_constant<int, kSmFp8E5M2>{}); break;
-    default: go(std::integral_constant<int, kSmToken>{}); break;
-  }
-}
-
-template <int D>
-void launch_d(bool stream_kernel, bool append, int hpw, int sm, bool paged, const DecodeParams& p, dim3 grid,
-              hipStream_t st) {
+void launch_decode_kernel(int head_dim, bool stream_kernel, bool append, int hpw, int sm, bool paged,
+                          const DecodeParams& p, dim3 grid, hipStream_t st) {
   if (stream_kernel) {
-    if (sm == kSmGroup32) launch_stream_group32(D, hpw, paged, append, p, grid, st);
-    else if (sm == kSmTokenBf16) launch_stream_bf16(D, hpw, paged, append, p, grid, st);
-    else if (sm == kSmFp8E4M3 || sm == kSmFp8E5M2) launch_stream_fp8(D, hpw, sm, paged, append, p, grid, st);
-    else launch_stream_token(D, hpw, paged, append, p, grid, st);
+    if (sm == kSmGroup32) launch_stream_group32(head_dim, hpw, paged, append, p, grid, st);
+    else if (sm == kSmTokenBf16) launch_stream_bf16(head_dim, hpw, paged, append, p, grid, st);
+    else if (sm == kSmFp8E4M3 || sm == kSmFp8E5M2) launch_stream_fp8(head_dim, hpw, sm, paged, append, p, grid, st);
+    else launch_stream_token(head_dim, hpw, paged, append, p, grid, st);
     return;
   }
-  if (hpw == 4) launch_generic_modes_d<D, 4>(sm, paged, p, grid, st);
-  else if (hpw == 2) launch_generic_modes_d<D, 2>(sm, paged, p, grid, st);
-  else launch_generic_modes_d<D, 1>(sm, paged, p, grid, st);
+  launch_generic_any(head_dim, hpw, sm, paged, p, grid, st);
 }
 
 int env_int(const char* name, int dflt) {
@@ -479,9 +241,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
 
-bool decode_supported(int head_dim) {
-  return head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256;
-}
+bool decode_supported(int head_dim) { return head_dim % 32 == 0 && head_dim >= 32 && head_dim <= 256; }
 
 DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc, int window, bool generic) {
   DecodePlan pl;
@@ -528,6 +288,7 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   const int forced_lf = env_int("KVQ_LONGEST_FIRST", -1);
   if (forced_lf >= 0) pl.longest_first = forced_lf != 0 && stream_kernel && c.batch <= kLongestFirstMax;
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
+  // per (sequence, head group): an arrival counter, then one ready flag per split
   pl.counter_bytes = align_up(static_cast<size_t>(groups) * (1 + pl.num_splits) * sizeof(int32_t), 256);
   pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
                  partials * static_cast<size_t>(c.head_dim) * sizeof(float);
@@ -585,12 +346,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   const int sm = c.scale_mode;
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
   const bool fused = append && stream_kernel;
-  switch (c.head_dim) {
-    case 32: launch_d<32>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
-    case 64: launch_d<64>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
-    case 128: launch_d<128>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
-    default: launch_d<256>(stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream); break;
-  }
+  launch_decode_kernel(c.head_dim, stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: launch failed: %s", hipGetErrorString(e));
   if (!stream_kernel) {
@@ -611,29 +367,6 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
 // ---------------------------------------------------------------------------
 namespace {
 
-template <int D, int HPW>
-void launch_generic_modes(int sm, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
-  auto go = [&](auto smc) {
-    constexpr int SM = decltype(smc)::value;
-    if (paged) hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, true>), grid, dim3(kThreads), 0, st, p);
-    else hipLaunchKernelGGL((decode_generic_kernel<D, HPW, SM, false>), grid, dim3(kThreads), 0, st, p);
-  };
-  switch (sm) {
-    case kSmGroup32: go(std::integral_constant<int, kSmGroup32>{}); break;
-    case kSmTokenBf16: go(std::integral_constant<int, kSmTokenBf16>{}); break;
-    case kSmFp8E4M3: go(std::integral_constant<int, kSmFp8E4M3>{}); break;
-    case kSmFp8E5M2: go(std::integral_constant<int, kSmFp8E5M2>{}); break;
-    default: go(std::integral_constant<int, kSmToken>{}); break;
-  }
-}
-
-template <int D>
-void launch_generic_hpw(int hpw, int sm, bool paged, const DecodeParams& p, dim3 grid, hipStream_t st) {
-  if (hpw == 4) launch_generic_modes<D, 4>(sm, paged, p, grid, st);
-  else if (hpw == 2) launch_generic_modes<D, 2>(sm, paged, p, grid, st);
-  else launch_generic_modes<D, 1>(sm, paged, p, grid, st);
-}
-
 kvq_cache rows_as_batch(const kvq_cache& c, int n) {
   kvq_cache cv = c;
   cv.batch = c.batch * n;
@@ -642,7 +375,8 @@ kvq_cache rows_as_batch(const kvq_cache& c, int n) {
 
 }  // namespace
 
-bool chunk_generic_supported(int head_dim) { return head_dim == 32 || head_dim == 256; }
+// every supported head dim without an MFMA chunk kernel
+bool chunk_generic_supported(int head_dim) { return decode_supported(head_dim) && !chunk_supported(head_dim); }
 
 DecodePlan plan_chunk_generic(const kvq_cache& c, int max_total_len, int n, int window) {
   return plan_decode(rows_as_batch(c, n), max_total_len, RecentGeom(), window, true);
@@ -733,12 +467,7 @@ kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, cons
   const dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, static_cast<unsigned>(rows));
   if (grid.y > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: grid too large");
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  switch (c.head_dim) {
-    case 32: launch_generic_hpw<32>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
-    case 64: launch_generic_hpw<64>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
-    case 128: launch_generic_hpw<128>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
-    default: launch_generic_hpw<256>(plan.heads_per_wg, c.scale_mode, paged, p, grid, stream); break;
-  }
+  launch_generic_any(c.head_dim, plan.heads_per_wg, c.scale_mode, paged, p, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   hipLaunchKernelGGL(decode_merge_kernel, dim3(c.num_heads, static_cast<unsigned>(rows)),

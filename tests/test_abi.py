@@ -168,9 +168,14 @@ def test_decode_argument_errors():
     st, msg = _status("kvq_attention_decode", d, FAKE, FAKE, 0.1, FAKE, FAKE, ws - 1, 64, None)
     assert st == kvq.KVQ_ERR_WORKSPACE and "workspace" in msg
     assert _status("kvq_attention_decode", d, FAKE, FAKE, 0.1, FAKE, None, ws, 64, None)[0] == kvq.KVQ_ERR_WORKSPACE
-    d96 = ctypes.byref(_desc(head_dim=96))
-    assert _status("kvq_attention_decode", d96, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)[0] == \
-        kvq.KVQ_ERR_UNSUPPORTED
+    # head dims whose lane count is not a power of two run on the generic
+    # kernel: sized like the others, refused only for a short workspace
+    for d in (96, 160, 192, 224):
+        dd = _desc(head_dim=d)
+        need = kvq.kvq_workspace_size(dd, 64, 1)
+        assert need > 0
+        st, msg = _status("kvq_attention_decode", ctypes.byref(dd), FAKE, FAKE, 0.1, FAKE, FAKE, need - 1, 64, None)
+        assert st == kvq.KVQ_ERR_WORKSPACE and f"the {need} bytes needed" in msg
 
 
 def test_chunk_and_dequant_argument_errors():
@@ -183,10 +188,12 @@ def test_chunk_and_dequant_argument_errors():
         kvq.KVQ_ERR_INVALID_ARG
     assert _status("kvq_attention_chunk", d, FAKE, 8, FAKE, 1, float("nan"), FAKE, FAKE, 1 << 30, 8, None)[0] == \
         kvq.KVQ_ERR_INVALID_ARG
-    # head sizes other than 32, 64, 128 and 256 have no chunk kernel
-    d96 = ctypes.byref(_desc(head_dim=96))
-    assert _status("kvq_attention_chunk", d96, FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
-        kvq.KVQ_ERR_UNSUPPORTED
+    # head sizes without an MFMA chunk kernel take chunks on the generic kernel
+    d96 = _desc(head_dim=96)
+    need = kvq.kvq_workspace_size(d96, 8 + 8, 8)
+    assert need > 0
+    st, msg = _status("kvq_attention_chunk", ctypes.byref(d96), FAKE, 8, FAKE, 1, 0.1, FAKE, FAKE, need - 1, 8, None)
+    assert st == kvq.KVQ_ERR_WORKSPACE and f"the {need} bytes needed" in msg
     assert _status("kvq_dequant", d, 2, FAKE, 0, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG
     assert _status("kvq_dequant", d, 0, FAKE, 3, FAKE, 8, None)[0] == kvq.KVQ_ERR_INVALID_ARG
     assert _status("kvq_dequant", d, 0, FAKE, 0, FAKE, 65, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
@@ -222,11 +229,17 @@ def test_recent_argument_errors():
     r = ctypes.byref(_recent())
     assert _status("kvq_attention_decode_recent", d, r, FAKE, FAKE, 0.1, FAKE, FAKE, ws - 1, 64, None)[0] == \
         kvq.KVQ_ERR_WORKSPACE
-    d96 = ctypes.byref(_desc(head_dim=96))
-    assert _status("kvq_attention_decode_recent", d96, r, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, 64, None)[0] == \
-        kvq.KVQ_ERR_UNSUPPORTED
-    assert _status("kvq_attention_chunk_recent", d96, r, FAKE, 8, FAKE, 0.1, FAKE, FAKE, 1 << 30, 8, None)[0] == \
-        kvq.KVQ_ERR_UNSUPPORTED
+    # head dim 96 runs on the generic kernel: sized like the others (the
+    # calls are refused for a workspace one byte short, before any launch)
+    d96 = _desc(head_dim=96)
+    need = kvq.kvq_workspace_size_recent(d96, _recent(), 64)
+    st, msg = _status("kvq_attention_decode_recent", ctypes.byref(d96), r, FAKE, FAKE, 0.1, FAKE, FAKE, need - 1, 64,
+                      None)
+    assert st == kvq.KVQ_ERR_WORKSPACE and f"the {need} bytes needed" in msg
+    need = kvq.kvq_workspace_size_chunk_recent(d96, _recent(), 16, 8)
+    st, msg = _status("kvq_attention_chunk_recent", ctypes.byref(d96), r, FAKE, 8, FAKE, 0.1, FAKE, FAKE, need - 1, 8,
+                      None)
+    assert st == kvq.KVQ_ERR_WORKSPACE and f"the {need} bytes needed" in msg
     assert _status("kvq_append_recent", d, r, FAKE, FAKE, 0, 65, FAKE, None)[0] == kvq.KVQ_ERR_OUT_OF_RANGE
 
 
