@@ -227,7 +227,7 @@ def cpu_baseline_recent(w: wl.Workload, target_s: float = 12.0):
     rate = per_seq_bytes * done / el / 1e12
     return {"value": rate, "unit": "TB/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{done} sequences of layer 0 ({done / w.batch:.2f} layer-steps: append 1 token to the "
-                      f"hybrid cache (window {W}) + fp64 attention over {T} tokens, 32 heads), {el:.1f}s wall; "
+                      f"hybrid cache (window {W}) + fp64 attention over {T} tokens, {w.num_heads} heads), {el:.1f}s wall; "
                       f"BLAS threads {blas_threads}; host {platform.processor() or 'x86_64'} nproc {os.cpu_count()}",
             "seconds": el}
 
@@ -282,7 +282,7 @@ def cpu_baseline(w: wl.Workload, target_s: float = 12.0):
     rate = per_seq_bytes * done / el / 1e12
     return {"value": rate, "unit": "TB/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"{done} sequences of layer 0 ({done / w.batch:.2f} layer-steps: quantize 1 new token "
-                      f"+ fp64 attention over {T} tokens, 32 heads), {el:.1f}s wall; numpy elementwise "
+                      f"+ fp64 attention over {T} tokens, {w.num_heads} heads), {el:.1f}s wall; numpy elementwise "
                       f"single-threaded, BLAS threads {blas_threads}; host {platform.processor() or 'x86_64'} "
                       f"nproc {os.cpu_count()}",
             "seconds": el}
@@ -328,6 +328,15 @@ def cpu_baseline_chunk(w: wl.Workload, x: dict, target_s: float = 12.0):
                       f"attention over its visible keys, plus the oracle quantization of the K/V of their "
                       f"(sequence, KV head); {el:.1f}s wall; numpy, BLAS threads {blas_threads}; host "
                       f"{platform.processor() or 'x86_64'} nproc {os.cpu_count()}"}
+
+
+def with_one_thread(baseline, *args, target_s: float = 6.0):
+    """The same oracle sample with numpy's BLAS held to one thread: the
+    single-thread figure beside the all-cores one."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        r = baseline(*args, target_s=target_s)
+    return {"value": r["value"], "unit": r["unit"], "cores": 1, "seconds": round(r.get("seconds", target_s), 1)}
 
 
 def time_calls(fn, reps: int, stream, torch) -> float:
@@ -399,6 +408,7 @@ def run_chunk(args, w: wl.Workload, kvq, torch, stream):
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_chunk(w, x)
+        cpu["single_thread"] = with_one_thread(cpu_baseline_chunk, w, x)
     codes_what = (f"FP8 {fp8.upper()} codes" if fp8 else
                   "group-32 fp32 scales" if w.group == 32 else "per-token fp32 scales")
     if rw:
@@ -439,7 +449,7 @@ def paged_bytes(w: wl.Workload, lens) -> dict:
     H, KVH, D = w.num_heads, w.num_kv_heads, w.head_dim
     total = int(np.sum(lens))
     B = len(lens)
-    decode = 2 * total * KVH * (D + 4) + 2 * B * H * D * 2 + B * w.max_blocks_read * 4
+    decode = 2 * total * KVH * (D + 4) + 2 * B * H * D * 2 + w.max_blocks_read * 4
     append = 2 * B * KVH * (D * 2 + D + 4)
     return {"decode": decode, "step": decode + append}
 
@@ -500,12 +510,14 @@ def run_paged(args, w: wl.Workload, kvq, torch, stream):
     nb = paged_bytes(w, lens)
     tbps = nb["step"] / (step_ms * 1e-3) / 1e12
     k_gbs = nb["step"] / (step_ms * 1e-3) / 1e9
+    ceil, _ = stream_ceiling(kvq, torch, stream, nb["step"], 1, reps=5, shapes=STREAM_QUICK)
     log(f"step {step_ms * 1e3:.1f} us, {tbps:.3f} TB/s ({tbps * 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s), "
         f"wall {wall * 1e3 / args.steps:.3f} ms/step")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_paged(w, lens)
+        cpu["single_thread"] = with_one_thread(cpu_baseline_paged, w, lens)
     result = {
         "metric": "INT8-KV paged decode attention: achieved HBM TB/s (% of peak)",
         "value": round(tbps, 4),
@@ -515,6 +527,8 @@ def run_paged(args, w: wl.Workload, kvq, torch, stream):
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
         "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
+        "pct_of_stream": round(k_gbs / ceil["gbs"] * 100, 2),
+        "stream": {"kernel": "kvq_stream_read", "gbs": ceil["gbs"], "us_per_launch": ceil["us_per_launch"]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -593,12 +607,14 @@ def run_sliding(args, w: wl.Workload, kvq, torch, stream):
     tbps = nb["step"] * w.layers / (step_ms * 1e-3) / 1e12
     us_launch = k_ms * 1e3 / w.layers
     k_gbs = nb["step"] / (us_launch * 1e-6) / 1e9
+    ceil, _ = stream_ceiling(kvq, torch, stream, nb["step"], w.layers, reps=5, shapes=STREAM_QUICK)
     log(f"{step_ms * 1e3 / w.layers:.2f} us/layer-step, {tbps:.3f} TB/s; kvq_append_decode_window "
         f"{us_launch:.2f} us/launch = {k_gbs:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline_sliding(w)
+        cpu["single_thread"] = with_one_thread(cpu_baseline_sliding, w)
     result = {
         "metric": "INT8-KV sliding-window decode attention: us/layer-step and achieved HBM TB/s (% of peak)",
         "value": round(tbps, 4),
@@ -609,6 +625,8 @@ def run_sliding(args, w: wl.Workload, kvq, torch, stream):
         "ms_per_step": round(step_ms, 4),
         "us_per_layer_step": round(step_ms * 1e3 / w.layers, 3),
         "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
+        "pct_of_stream": round(k_gbs / ceil["gbs"] * 100, 2),
+        "stream": {"kernel": "kvq_stream_read", "gbs": ceil["gbs"], "us_per_launch": ceil["us_per_launch"]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -651,7 +669,7 @@ def cpu_baseline_sliding(w: wl.Workload, target_s: float = 12.0):
     el = time.perf_counter() - t0
     return {"value": per_seq * seqs / el / 1e12, "unit": "TB/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"{seqs} sequences of {T} tokens drawn on the host with the workload's shapes (quantize the "
-                      f"sequence's K/V, fp64 attention of 32 heads under a {win}-token window), {el:.1f}s wall; "
+                      f"sequence's K/V, fp64 attention of {w.num_heads} heads under a {win}-token window), {el:.1f}s wall; "
                       f"bytes counted as the step's per-sequence algorithmic bytes; BLAS threads {blas_threads}; "
                       f"host {platform.processor() or 'x86_64'} nproc {os.cpu_count()}"}
 
@@ -679,7 +697,7 @@ def cpu_baseline_paged(w: wl.Workload, lens, target_s: float = 12.0):
     el = time.perf_counter() - t0
     return {"value": done_bytes / el / 1e12, "unit": "TB/s", "cores": blas_threads, "kind": "oracle",
             "sample": f"{seqs} sequences of the paged step in order (quantize the sequence's K/V, fp64 attention "
-                      f"for its 32 heads), {el:.1f}s wall; bytes counted as the cache codes and scales those "
+                      f"for its {w.num_heads} heads), {el:.1f}s wall; bytes counted as the cache codes and scales those "
                       f"sequences occupy; numpy elementwise single-threaded, BLAS threads {blas_threads}; host "
                       f"{platform.processor() or 'x86_64'} nproc {os.cpu_count()}"}
 
@@ -693,6 +711,11 @@ STREAM_SHAPES = [  # (workgroups, waves per workgroup, KB in flight per wave (x1
     (1024, 8, 2, True), (1024, 4, 4, True), (2048, 4, 2, True), (256, 16, 2, True),
     (512, 8, 4, False), (1024, 8, 2, False),
 ]
+
+
+# the best shapes of the sweep above (bench.py --workload stream_read), timed
+# beside every decode line for its percent-of-stream figure
+STREAM_QUICK = [(256, 8, 2, True), (512, 8, 8, True), (1024, 8, 2, True), (256, 8, 4, False)]
 
 
 def stream_ceiling(kvq, torch, stream, nbytes: int, launches: int, reps: int = 5, shapes=STREAM_SHAPES):
@@ -870,17 +893,21 @@ def main():
 
     nbytes = step_bytes(w, T)
     total_bytes = nbytes["step"] * w.layers
+    ceil, _ = stream_ceiling(kvq, torch, stream, nbytes[kernel_bytes], w.layers, reps=5, shapes=STREAM_QUICK)
     tbps = total_bytes / (step_ms * 1e-3) / 1e12
     us_layer = step_ms * 1e3 / w.layers
     dec_gbs = nbytes[kernel_bytes] / (dec_us * 1e-6) / 1e9
     log(f"{us_layer:.2f} us/layer-step, {tbps:.3f} TB/s ({tbps * 1e3 / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s); "
-        f"{kernel_name} {dec_us:.2f} us/launch = {dec_gbs:.0f} GB/s")
+        f"{kernel_name} {dec_us:.2f} us/launch = {dec_gbs:.0f} GB/s; read stream of the same bytes "
+        f"{ceil['us_per_launch']:.2f} us = {ceil['gbs']:.0f} GB/s ({dec_gbs / ceil['gbs'] * 100:.1f}% of it)")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline_recent(w) if w.extra.get("window") else cpu_baseline(w)
+        base = cpu_baseline_recent if w.extra.get("window") else cpu_baseline
+        cpu = base(w)
         cpu.pop("seconds", None)
+        cpu["single_thread"] = with_one_thread(base, w)
 
     fp8 = w.extra.get("fp8")
     codes_what = (f"FP8 {fp8.upper()} codes (no scales)" if fp8 else
@@ -896,6 +923,11 @@ def main():
         "ms_per_step": round(step_ms, 4),
         "us_per_layer_step": round(us_layer, 3),
         "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
+        "pct_of_stream": round(dec_gbs / ceil["gbs"] * 100, 2),
+        "stream": {"kernel": "kvq_stream_read", "gbs": ceil["gbs"], "us_per_launch": ceil["us_per_launch"],
+                   "shape": {k: ceil[k] for k in ("workgroups", "waves", "kb_in_flight_per_wave", "interleaved")},
+                   "what": f"read-only stream of the same {nbytes[kernel_bytes]} B per launch, {w.layers} buffers "
+                           f"in turn; pct_of_stream compares the kernel's algorithmic GB/s with it"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
