@@ -485,6 +485,107 @@ class RecentWindowCache:
         return k, v
 
 
+# ----------------------------------------------------------------------------
+# Per-head and per-channel granularity ([P1] `QuantGranularity`,
+# `quantize_with_granularity`): the page takes one scale per head (the maximum
+# over sequence and head_dim) or per (head, channel) (the maximum over the
+# sequence) of whatever tensor one `append` hands over, so a row's codes
+# depend on which rows were appended with it.  Reading used here (the design doc
+# reading 20): the "sequence" is a fixed, position-aligned block of B rows
+# (B = 16 in the kernels).  Block j (rows jB .. jB+B-1) is quantized, from its
+# rows' bf16 values, at the append after which its first row has left the
+# window (L > jB + W); W >= B - 1 guarantees that all B rows exist then.  Row
+# p is read as INT8 when p < L - W, as on the page, so the quantized and
+# recent counts are the page's; rows of a quantized block still inside the
+# window are read from the recent part until they leave it.
+# ----------------------------------------------------------------------------
+
+def quantize_block(x: np.ndarray, granularity: str):
+    """One block ``x`` [KVH, B, D] (fp32 values) with the per-token
+    quantizer's steps (:func:`quantize`) applied over the page's reduction
+    sets: ``"head"``, the maximum over the block's B rows and all D elements;
+    ``"channel"``, the maximum over the B rows of each element index d.
+    Returns (codes uint8 [KVH, B, D], scales float32: [KVH, 1] per head,
+    [KVH, D] per channel)."""
+    x = np.asarray(x, dtype=np.float32)
+    kvh, nb, d = x.shape
+    if granularity == "head":
+        codes, s = quantize(x.reshape(kvh, nb * d), 0)        # one scale over B x D
+        return codes.reshape(kvh, nb, d), s
+    if granularity == "channel":
+        codes, s = quantize(np.swapaxes(x, 1, 2), 0)          # [KVH, D, B]: one scale per d
+        return np.ascontiguousarray(np.swapaxes(codes, 1, 2)), s[..., 0]
+    raise ValueError("granularity is 'head' or 'channel'")
+
+
+class BlockRecentCache:
+    """One sequence's hybrid cache with per-head or per-channel block scales
+    (reading above).  Rows enter as bf16 values, as in
+    :class:`RecentWindowCache`; the quantized state is kept per block.
+
+    ``codes``: [KVH, nq_blocks * B, D] for every quantized block (rows inside
+    the window included).  ``scales``: per head [KVH, nq_blocks], per channel
+    [KVH, nq_blocks, D].
+    """
+
+    def __init__(self, num_kv_heads: int, head_dim: int, window: int, granularity: str, block: int = 16):
+        if granularity not in ("head", "channel"):
+            raise ValueError("granularity is 'head' or 'channel'")
+        if block < 1 or window < block - 1:
+            raise ValueError("the window must be at least block - 1 rows")
+        self.window, self.granularity, self.block = int(window), granularity, int(block)
+        self.kvh, self.d = int(num_kv_heads), int(head_dim)
+        self.rows = [np.zeros((num_kv_heads, 0, head_dim), np.float32) for _ in range(2)]  # every row, bf16 values
+        self.codes = [np.zeros((num_kv_heads, 0, head_dim), np.uint8) for _ in range(2)]
+        sshape = (num_kv_heads, 0) if granularity == "head" else (num_kv_heads, 0, head_dim)
+        self.scales = [np.zeros(sshape, np.float32) for _ in range(2)]
+
+    def append(self, k_new: np.ndarray, v_new: np.ndarray) -> None:
+        for side, x in enumerate((k_new, v_new)):
+            self.rows[side] = np.concatenate([self.rows[side], to_bf16_values(x)], axis=1)
+        length = self.seq_len()
+        for side in range(2):
+            # every block whose first row has left the window is quantized
+            while self.codes[side].shape[1] < length - self.window:
+                j0 = self.codes[side].shape[1]
+                blk = self.rows[side][:, j0:j0 + self.block]
+                assert blk.shape[1] == self.block  # guaranteed by window >= block - 1
+                c, sc = quantize_block(blk, self.granularity)
+                self.codes[side] = np.concatenate([self.codes[side], c], axis=1)
+                sc = sc[:, None] if self.granularity == "channel" else sc
+                self.scales[side] = np.concatenate([self.scales[side], sc], axis=1)
+
+    def seq_len(self) -> int:
+        return self.rows[0].shape[1]
+
+    def quantized_len(self) -> int:
+        """Rows read as INT8 (the page's count)."""
+        return recent_split(self.seq_len(), self.window)
+
+    def recent_len(self) -> int:
+        return self.seq_len() - self.quantized_len()
+
+    def row_scales(self, side: int) -> np.ndarray:
+        """Scales expanded to one entry per quantized row: [KVH, rows, 1] per
+        head, [KVH, rows, D] per channel."""
+        s = np.repeat(self.scales[side], self.block, axis=1)
+        return s[..., None] if self.granularity == "head" else s
+
+    def dequant(self, side: int) -> np.ndarray:
+        """Exact fp64 (code - 128) * scale of every quantized row."""
+        c = self.codes[side].astype(np.float64) - CODE_OFFSET
+        return c * self.row_scales(side).astype(np.float64)
+
+    def kv(self):
+        """[P1] `get_kv`: dequantized rows below L - W, then the recent rows."""
+        nq = self.quantized_len()
+        out = []
+        for side in range(2):
+            old = self.dequant(side)[:, :nq]
+            out.append(np.concatenate([old, self.rows[side][:, nq:].astype(np.float64)], axis=1))
+        return out[0], out[1]
+
+
 def attention_decode_recent(q: np.ndarray, caches, attn_scale: float) -> np.ndarray:
     """Decode attention over hybrid caches: ``q`` [B, H, D], ``caches`` one
     :class:`RecentWindowCache` per sequence; each query sees its sequence's

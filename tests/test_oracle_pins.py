@@ -594,6 +594,127 @@ def test_recent_memory_savings(golden):
 
 
 # ----------------------------------------------------------------------------
+# per-head and per-channel block scales (abaddon kv_cache_quant_cuda.rs,
+# QuantGranularity / quantize_with_granularity)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gran", ["head", "channel"])
+def test_block_modes_page_counts(golden, gran):
+    """The page's test_per_head_quantization (W = 4, 10 tokens, 4 KV heads,
+    head_dim 64: 6 quantized, 4 recent, a [4, 10, 64] get_kv view) and the
+    other printed counts, with blocks of 4 rows (the reading needs B <= W + 1)."""
+    for case in golden["recent_window_counts"]["cases"]:
+        c = orc.BlockRecentCache(case["kv_heads"], case["head_dim"], case["window"], gran, block=4)
+        rng = np.random.default_rng(0)
+        for n in case["appends"]:
+            x = rng.standard_normal((case["kv_heads"], n, case["head_dim"])).astype(np.float32)
+            c.append(x, x)
+        assert (c.seq_len(), c.quantized_len(), c.recent_len()) == (case["seq_len"], case["quantized"],
+                                                                     case["recent"])
+        k, v = c.kv()
+        assert k.shape == v.shape == (case["kv_heads"], case["seq_len"], case["head_dim"])
+
+
+def test_block_modes_need_a_window_of_block_minus_one():
+    with pytest.raises(ValueError):
+        orc.BlockRecentCache(1, 32, 14, "head", block=16)
+    orc.BlockRecentCache(1, 32, 15, "head", block=16)
+
+
+@pytest.mark.parametrize("gran", ["head", "channel"])
+def test_block_scales_half_step_bound(gran):
+    """Every dequantized element lies within (s/2)(1 + 2^-15) of its bf16
+    input, s its own block (per head) or block-channel scale; per head that
+    s is max over the block / 127, per channel max over the block's column."""
+    rng = np.random.default_rng(11)
+    KVH, D, B, W, T = 2, 64, 16, 20, 100
+    x = (rng.standard_normal((KVH, T, D)) * np.exp(rng.uniform(-3, 3, (1, T, D)))).astype(np.float32)
+    c = orc.BlockRecentCache(KVH, D, W, gran, block=B)
+    c.append(x[:, :37], x[:, :37])
+    c.append(x[:, 37:], x[:, 37:])
+    xb = _bf16_values_torch(x).astype(np.float64)
+    nrow = c.codes[0].shape[1]
+    # the blocks are quantized from the rows' bf16 values (library cast),
+    # with the per-token quantizer's steps over the block's reduction set
+    blocks = xb[:, :nrow].astype(np.float32).reshape(KVH, nrow // B, B, D)
+    if gran == "head":
+        want_codes = orc.quantize(blocks.reshape(KVH, nrow // B, B * D), 0)[0].reshape(KVH, nrow, D)
+    else:
+        want_codes = np.swapaxes(orc.quantize(np.swapaxes(blocks, 2, 3), 0)[0], 2, 3).reshape(KVH, nrow, D)
+    assert np.array_equal(c.codes[0], want_codes)
+    err = np.abs(c.dequant(0) - xb[:, :nrow])
+    s = c.row_scales(0).astype(np.float64)
+    assert np.all(err <= s / 2 * (1 + 2.0 ** -15))
+    for j in range(nrow // B):
+        blk = np.abs(xb[:, j * B:(j + 1) * B])
+        want = blk.max(axis=(1, 2)) if gran == "head" else blk.max(axis=1)
+        got = c.scales[0][:, j]
+        # s = fl32(max / 127): within half an fp32 ulp of the exact quotient
+        assert np.all(np.abs(got.astype(np.float64) - want / 127) <= np.spacing(got) / 2 + 1e-300)
+
+
+def test_block_head_with_one_row_blocks_is_per_token():
+    """B = 1: the per-head block maximum is the row maximum, so codes and
+    scales are those of the per-token quantizer."""
+    rng = np.random.default_rng(12)
+    x = _bf16_values_torch(rng.standard_normal((3, 20, 32)))
+    c = orc.BlockRecentCache(3, 32, 0, "head", block=1)
+    c.append(x, x)
+    kc, ks = orc.quantize(x, 0)
+    assert np.array_equal(c.codes[0], kc) and np.array_equal(c.scales[0], ks[..., 0])
+
+
+def test_block_channel_constant_rows_closed_form():
+    """A block of B equal rows u: per channel each scale is |u_d| / 127 and
+    every code is 128 + 127 sign(u_d); per head the scale is max|u| / 127."""
+    rng = np.random.default_rng(13)
+    D, B = 32, 16
+    u = _bf16_values_torch(rng.standard_normal(D))
+    u[3] = 0.0
+    x = np.repeat(u[None, None, :], 2 * B - 1, axis=1).astype(np.float32)
+    c = orc.BlockRecentCache(1, D, B - 1, "channel", block=B)
+    c.append(x, x)
+    assert c.codes[0].shape[1] == B  # L - W = B: block 0 alone has started to leave
+    want = np.where(u > 0, 255, np.where(u < 0, 1, 128))
+    assert np.all(c.codes[0][0] == want[None, :])
+    mag = np.maximum(np.abs(u), np.float32(1e-8))
+    assert np.array_equal(c.scales[0][0, 0], (mag / np.float32(127)).astype(np.float32))
+    h = orc.BlockRecentCache(1, D, B - 1, "head", block=B)
+    h.append(x, x)
+    assert h.scales[0][0, 0] == np.float32(np.max(np.abs(u)) / np.float32(127))
+
+
+@pytest.mark.parametrize("gran", ["head", "channel"])
+def test_block_state_is_history_independent(gran):
+    """The state depends on the rows alone: any chunking of the appends gives
+    the same codes, scales and get_kv view; and changing a row changes no
+    code outside its block."""
+    rng = np.random.default_rng(14)
+    KVH, D, W, B, T = 2, 32, 17, 16, 90
+    k = rng.standard_normal((KVH, T, D)).astype(np.float32)
+    v = rng.standard_normal((KVH, T, D)).astype(np.float32)
+    ref = orc.BlockRecentCache(KVH, D, W, gran, block=B)
+    ref.append(k, v)
+    for trial in range(6):
+        c = orc.BlockRecentCache(KVH, D, W, gran, block=B)
+        L = 0
+        while L < T:
+            n = min(int(rng.integers(1, 25)), T - L)
+            c.append(k[:, L:L + n], v[:, L:L + n])
+            L += n
+        for side in range(2):
+            assert np.array_equal(c.codes[side], ref.codes[side])
+            assert np.array_equal(c.scales[side], ref.scales[side])
+        assert all(np.array_equal(a, b) for a, b in zip(c.kv(), ref.kv()))
+    k2 = k.copy()
+    k2[:, 20] *= 8.0  # row 20: block 1
+    c = orc.BlockRecentCache(KVH, D, W, gran, block=B)
+    c.append(k2, v)
+    diff = np.any(c.codes[0] != ref.codes[0], axis=(0, 2))
+    assert diff[16:32].any() and not diff[:16].any() and not diff[32:].any()
+
+
+# ----------------------------------------------------------------------------
 # sliding-window attention (combs-models kv.rs, attention_opts window)
 # ----------------------------------------------------------------------------
 
