@@ -74,5 +74,70 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side sanitizer build (a CPU check of the host validation layer, not a
+# product library): every translation unit at -O0 with AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host pass only; the device pass is left
+# alone.  Loaded with the compiler's ASan runtime preloaded (see san_env).
+SAN_DIR = os.path.join(PKG, "_san")
+SAN_LIB = os.path.join(SAN_DIR, "libkvq.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def san_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (it carries UBSan's handlers)."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isfile(path):
+        hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+        if not hits:
+            raise RuntimeError("no libclang_rt.asan-x86_64.so found")
+        path = hits[-1]
+    return path
+
+
+def san_env() -> dict:
+    """Environment that loads the sanitized library under the ASan runtime."""
+    env = dict(os.environ)
+    env["KVQ_LIBRARY"] = SAN_LIB
+    env["LD_PRELOAD"] = san_runtime()
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1"
+    env["UBSAN_OPTIONS"] = "print_stacktrace=1:halt_on_error=1"
+    return env
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """Compile and link the sanitizer build into _san/libkvq.so (skipped when
+    it is newer than every source and header)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(SRC, "*.hip")))
+    deps = sources + glob.glob(os.path.join(SRC, "*.hpp")) + glob.glob(os.path.join(INCLUDE, "*.h")) + [__file__]
+    if os.path.exists(SAN_LIB) and os.path.getmtime(SAN_LIB) > max(os.path.getmtime(d) for d in deps):
+        return SAN_LIB
+    common = [a for a in COMMON if a != "-O3"] + ["-O0", "-g"] + SAN_FLAGS
+
+    def one(src: str) -> str:
+        obj = os.path.join(SAN_DIR, os.path.basename(src) + ".o")
+        r = subprocess.run([HIPCC, *common, "-c", src, "-o", obj], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
+        objs = list(ex.map(one, sources))
+    tmp = SAN_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *SAN_FLAGS, "-shared-libsan", "-o", tmp,
+                        *objs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"sanitizer link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, SAN_LIB)
+    if verbose:
+        print(f"built {SAN_LIB}")
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build()
+    if len(sys.argv) > 1 and sys.argv[1] == "--sanitize":
+        build_sanitized()
+    else:
+        build()
