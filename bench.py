@@ -15,8 +15,10 @@ figure is TFLOP/s over the visible keys only.
 
 The other workloads (recent_window, sliding_decode, sliding_chunk,
 bf16_scales, fp8_e4m3, fp8_chunk, chunk_group32, recent_chunk, q8_group32,
-paged_decode, tiny_decode) are the same steps on the cache variants their
-names give; ``--help`` lists them.
+paged_decode, tiny_decode, recent_block_head, recent_block_channel,
+chunk_d256) are the same steps on the cache variants their names give;
+stream_read times a plain read of the decode step's bytes; ``--help`` lists
+them.
 
 Inputs are seeded synthetic data, already resident in HBM when timing starts.
 Prints one JSON line (see --help).  ``--gpus N`` with N > 1 is refused: this
@@ -71,7 +73,8 @@ def recorded_traffic(kernel: str, workload: str):
 def step_bytes(w: wl.Workload, L: int) -> dict:
     """Algorithmic bytes of one layer-step (each byte the step must move once)."""
     B, H, KVH, D = w.batch, w.num_heads, w.num_kv_heads, w.head_dim
-    G = 1 if w.group == 0 else D // 32
+    # scales per row (per-channel block scales: D per 16 rows)
+    G = D // 16 if w.extra.get("block") == "channel" else (1 if w.group == 0 else D // 32)
     in_bytes = 4 if w.kv_dtype == "f32" else 2
     sb = 2 if w.extra.get("scale_bf16") else (0 if w.extra.get("fp8") else 4)   # bytes per scale (FP8: none)
     W = w.extra.get("window", 0)
@@ -155,7 +158,8 @@ def build_layers(w: wl.Workload, kvq, torch, stream, threads: int):
                 x = done_layers.pop(li)
                 cache = kvq.Int8KVCache(w.batch, w.num_heads, w.num_kv_heads, w.head_dim, max_len=w.max_len,
                                         group32=(w.group == 32), recent_window=w.extra.get("window", 0),
-                                        scale_bf16=w.extra.get("scale_bf16", False), fp8=w.extra.get("fp8"))
+                                        scale_bf16=w.extra.get("scale_bf16", False), fp8=w.extra.get("fp8"),
+                                        block_scales=w.extra.get("block"))
                 k_raw, v_raw = x["k_raw"], x["v_raw"]
                 tdt = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
 
@@ -206,7 +210,10 @@ def cpu_baseline_recent(w: wl.Workload, target_s: float = 12.0):
     x = wl.layer_inputs(w, 0)
     base = []
     for b in range(w.batch):
-        c = orc.RecentWindowCache(w.num_kv_heads, w.head_dim, W, w.group)
+        if w.extra.get("block"):
+            c = orc.BlockRecentCache(w.num_kv_heads, w.head_dim, W, w.extra["block"])
+        else:
+            c = orc.RecentWindowCache(w.num_kv_heads, w.head_dim, W, w.group)
         c.append(x["k"][b, :, :w.ctx], x["v"][b, :, :w.ctx])
         base.append(c)
 
@@ -784,7 +791,8 @@ def main():
     ap.add_argument("--workload", default="decode_8b", choices=["decode_8b", "q8_group32", "chunked_prefill", "paged_decode",
                                                             "recent_window", "sliding_decode", "sliding_chunk",
                                                             "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32",
-                                                            "recent_chunk", "tiny_decode", "stream_read"])
+                                                            "recent_chunk", "tiny_decode", "stream_read",
+                                                            "recent_block_head", "recent_block_channel", "chunk_d256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -827,7 +835,7 @@ def main():
     if w.name == "sliding_decode":
         run_sliding(args, w, kvq, torch, stream)
         return
-    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk", "chunk_group32", "recent_chunk"):
+    if w.name in ("chunked_prefill", "sliding_chunk", "fp8_chunk", "chunk_group32", "recent_chunk", "chunk_d256"):
         run_chunk(args, w, kvq, torch, stream)
         return
     if w.name == "paged_decode":

@@ -79,13 +79,36 @@ typedef enum {
  * negative zero reads as +0).  Attention over a non-finite code is
  * non-finite.  Decode attention, chunked attention and dequantization
  * support both formats; a recent window over FP8 codes returns
+ * KVQ_ERR_UNSUPPORTED.
+ *
+ * Block scales (abaddon kv_cache_quant_cuda.rs, `QuantGranularity::PerHead` /
+ * `PerChannel`, `quantize_with_granularity`), for hybrid caches only: the
+ * page's per-head scale (maximum over the sequence and head_dim) and
+ * per-channel scale (maximum over the sequence, one per element index) are
+ * taken over fixed, position-aligned blocks of 16 rows of one (sequence, KV
+ * head), so that the codes depend on the token history alone.  Block j
+ * (positions 16j .. 16j+15) is quantized from its rows' bf16 values when its
+ * first row leaves the recent window; the window must be at least 15 so that
+ * all 16 rows exist then.  Positions below L - window read as INT8, as in the
+ * per-token hybrid cache.
+ *   KVQ_SCALE_BLOCK_HEAD    : one scale per (block, KV head), stored once
+ *                             per row, like per-token scales (G = 1), so the
+ *                             per-token kernels read it unchanged.
+ *   KVQ_SCALE_BLOCK_CHANNEL : head_dim scales per (block, KV head): contiguous
+ *                             [batch, num_kv_heads, max_len/16, head_dim],
+ *                             paged [num_pages, num_kv_heads, head_dim] (a
+ *                             page is one block).
+ * Contiguous caches in these modes need max_len % 16 == 0.  Only the
+ * recent-window entry points (kvq_*_recent) take them; the others return
  * KVQ_ERR_UNSUPPORTED. */
 enum {
   KVQ_SCALE_PER_TOKEN = 0,
   KVQ_SCALE_GROUP32 = 1,
   KVQ_SCALE_PER_TOKEN_BF16 = 2,
   KVQ_CODES_FP8_E4M3 = 3,
-  KVQ_CODES_FP8_E5M2 = 4
+  KVQ_CODES_FP8_E5M2 = 4,
+  KVQ_SCALE_BLOCK_HEAD = 5,
+  KVQ_SCALE_BLOCK_CHANNEL = 6
 };
 enum { KVQ_LAYOUT_CONTIGUOUS = 0, KVQ_LAYOUT_PAGED = 1 };
 enum { KVQ_DT_F32 = 0, KVQ_DT_BF16 = 1 };
@@ -153,12 +176,13 @@ kvq_status kvq_append(const kvq_cache* cache, const void* k_new, const void* v_n
  *               clamped to [0, min(hint, capacity)]; a length of 0 gives zeros)
  *   out       : device bf16 [B, H, D]
  *   workspace : device scratch of at least kvq_workspace_size(cache,
- *               max_seq_len_hint, 1) bytes: split arrival counters and
- *               ready flags, then split partials.  Zero-fill it once after
- *               allocation; every call returns the counters and flags to zero,
- *               so it can be reused by later calls on the same stream.  Calls
- *               that overlap in time (other streams) must not share a
- *               workspace.
+ *               max_seq_len_hint, 1) bytes: split merge counters, then
+ *               split partials (a partial word reads zero until its split
+ *               has written it).  Zero-fill it once after allocation; every
+ *               call of this library returns the whole workspace to zero,
+ *               so it can be reused by later calls on the same stream, of
+ *               any entry point.  Calls that overlap in time (other streams)
+ *               must not share a workspace.
  * Errors: INVALID_ARG, OUT_OF_RANGE (hint beyond capacity or < 1),
  * WORKSPACE, HIP.  Head dims 32, 64 and 128 run on the streaming kernel; the
  * other multiples of 32 up to 256 on a generic kernel (fp32 arithmetic,
@@ -397,19 +421,18 @@ uint64_t kvq_cache_bytes(const kvq_cache* cache);
  * kvq_append_decode_noalloc — kvq_append_decode for callers that cannot
  * allocate or own device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): the same launch and kernels, with
- * the split counters, ready flags and partials in a static device array of
- * 8 MiB that the library holds on each GPU it runs on until the process
- * ends.  The caller passes inputs and outputs only; no workspace argument,
- * and the call allocates nothing.  The array's address on a device is
- * looked up at the first call on that device, which also clears its 64 KiB
- * counter region on `stream` ahead of its own kernel; every completed call
- * leaves the counters and flags zero again.  All calls on one GPU share the
- * array: calls that overlap in time on one GPU (other streams, other
- * threads) race and must not be made.
+ * the split counters and partials in a static device array of 8 MiB that
+ * the library holds on each GPU it runs on until the process ends.  The
+ * caller passes inputs and outputs only; no workspace argument, and the
+ * call allocates nothing.  The array's address on a device is looked up at
+ * the first call on that device, which also clears the array on `stream`
+ * ahead of its own kernel; every completed call leaves it zero again.  All
+ * calls on one GPU share the array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and must not be made.
  *
  *   arguments : as kvq_append_decode, without workspace / workspace_bytes
- * Errors: those of kvq_append_decode; WORKSPACE when the call's counters and
- * flags (4 * batch * head groups * (1 + splits) bytes) exceed 64 KiB or its
+ * Errors: those of kvq_append_decode; WORKSPACE when the call's counters
+ * (4 * batch * head groups bytes) exceed the 64 KiB counter region or its
  * split partials (batch * num_heads * splits * (head_dim + 2) * 4 bytes)
  * exceed the rest of the array; HIP if the array's address cannot be
  * obtained.

@@ -18,14 +18,18 @@ class Int8KVCache:
     Paged: arena codes ``[P, KVH, 16, D]``, scales ``[P, KVH, 16, G]``, with a
     caller-provided int32 ``block_table [B, max_blocks_per_seq]``.
     ``fp8="e4m3"`` or ``"e5m2"`` stores FP8 codes instead, with no scales
-    (``k_scales`` / ``v_scales`` are then None).
+    (``k_scales`` / ``v_scales`` are then None).  ``block_scales="head"`` or
+    ``"channel"`` (with a recent window of at least 15) takes one scale per
+    16-row block and KV head, or per block, KV head and element index:
+    per-head scales are stored on every row (G = 1); per-channel scales are
+    ``[B, KVH, max_len / 16, D]`` (paged: ``[P, KVH, D]``).
     """
 
     def __init__(self, batch: int, num_heads: int, num_kv_heads: int, head_dim: int, *,
                  max_len: int = 0, group32: bool = False, num_pages: int = 0,
                  block_table: torch.Tensor | None = None, device="cuda", fill: int | None = None,
                  recent_window: int = 0, recent_capacity: int | None = None, scale_bf16: bool = False,
-                 fp8: str | None = None):
+                 fp8: str | None = None, block_scales: str | None = None):
         self.batch, self.num_heads, self.num_kv_heads, self.head_dim = batch, num_heads, num_kv_heads, head_dim
         self.groups = head_dim // 32 if group32 else 1
         self.paged = block_table is not None
@@ -41,6 +45,12 @@ class Int8KVCache:
             self.capacity = max_len
         shape_c = rows + (head_dim,)
         shape_s = rows + (self.groups,)
+        if block_scales not in (None, "head", "channel"):
+            raise ValueError("block_scales must be None, 'head' or 'channel'")
+        if block_scales and (group32 or scale_bf16 or fp8):
+            raise ValueError("block scales are fp32 INT8 scales of their own layout")
+        if block_scales == "channel":
+            shape_s = (num_pages, num_kv_heads, head_dim) if self.paged else (batch, num_kv_heads, max_len // 16, head_dim)
         if fill is None:
             self.k_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
             self.v_codes = torch.empty(shape_c, dtype=torch.uint8, device=device)
@@ -62,7 +72,10 @@ class Int8KVCache:
             self.k_scales = torch.zeros(shape_s, dtype=sdt, device=device)
             self.v_scales = torch.zeros(shape_s, dtype=sdt, device=device)
             mode = (_k.KVQ_SCALE_GROUP32 if group32 else
-                    _k.KVQ_SCALE_PER_TOKEN_BF16 if scale_bf16 else _k.KVQ_SCALE_PER_TOKEN)
+                    _k.KVQ_SCALE_PER_TOKEN_BF16 if scale_bf16 else
+                    _k.KVQ_SCALE_BLOCK_HEAD if block_scales == "head" else
+                    _k.KVQ_SCALE_BLOCK_CHANNEL if block_scales == "channel" else _k.KVQ_SCALE_PER_TOKEN)
+        self.block_scales = block_scales
         self.desc = _k.make_cache(
             batch, num_heads, num_kv_heads, head_dim, self.k_codes, self.v_codes, self.k_scales,
             self.v_scales,
@@ -94,8 +107,8 @@ class Int8KVCache:
             _k.kvq_append(self.desc, k_new, v_new, dt, k_new.shape[2], start_pos, stream)
 
     def workspace(self, max_seq_len: int, n_query: int = 1, window: int = 0) -> torch.Tensor:
-        """Zero-filled scratch for the attention calls (the split counters at
-        its start must be zero before the first call; calls leave them zero)."""
+        """Zero-filled scratch for the attention calls (it must be zero before
+        the first call; every call leaves it zero again)."""
         if window > 0:
             n = _k.kvq_workspace_size_window(self.desc, max_seq_len, n_query, window)
         elif self.recent is not None and n_query == 1:

@@ -39,10 +39,13 @@ kvq_status check_cache(const kvq_cache* c, const char* who, bool need_pointers =
     return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be a multiple of 32", who, c->head_dim);
   if (c->head_dim > 256)
     return fail(KVQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be at most 256", who, c->head_dim);
-  if (c->scale_mode < KVQ_SCALE_PER_TOKEN || c->scale_mode > KVQ_CODES_FP8_E5M2)
+  if (c->scale_mode < KVQ_SCALE_PER_TOKEN || c->scale_mode > KVQ_SCALE_BLOCK_CHANNEL)
     return fail(KVQ_ERR_INVALID_ARG, "%s: unknown scale_mode %d", who, c->scale_mode);
   if (c->layout == KVQ_LAYOUT_CONTIGUOUS) {
     if (c->max_len <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: contiguous cache needs max_len > 0", who);
+    if (is_block_mode(*c) && c->max_len % kBlockRows != 0)
+      return fail(KVQ_ERR_INVALID_ARG, "%s: block scales need max_len %% %d == 0 (got %d)", who, kBlockRows,
+                  c->max_len);
   } else if (c->layout == KVQ_LAYOUT_PAGED) {
     if (c->page_size != kPageSize)
       return fail(KVQ_ERR_INVALID_ARG, "%s: page_size must be %d (got %d)", who, kPageSize, c->page_size);
@@ -106,16 +109,36 @@ kvq_status check_recent(const kvq_recent* r, const kvq_cache& c, const char* who
     return fail(KVQ_ERR_INVALID_ARG, "%s: ring capacity too large", who);
   if (need_pointers && (!r->k || !r->v)) return fail(KVQ_ERR_INVALID_ARG, "%s: ring pointers must be non-NULL", who);
   if (is_fp8(c)) return fail(KVQ_ERR_UNSUPPORTED, "%s: a recent window over FP8 codes is not supported", who);
+  if (is_block_mode(c) && r->window < kBlockRows - 1)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: block scales need a window of at least %d (got %d)", who, kBlockRows - 1,
+                r->window);
+  return KVQ_OK;
+}
+
+// Block scales exist only on hybrid caches (a block is quantized when its
+// first row leaves the recent window).
+kvq_status check_block_needs_recent(const kvq_cache& c, const kvq_recent* r, const char* who) {
+  if (is_block_mode(c) && !r)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: block scale modes need a recent-window cache (the kvq_*_recent calls)",
+                who);
   return KVQ_OK;
 }
 
 bool finite(float x) { return x == x && x != INFINITY && x != -INFINITY; }
+
+// On a hybrid cache the MFMA chunk kernel (with the ring kernel) takes head
+// dims 64 and 128 in every per-row scale mode; other head dims and
+// per-channel block scales go through the generic kernel.
+bool mfma_hybrid_ok(const kvq_cache& c) {
+  return (c.head_dim == 64 || c.head_dim == 128) && c.scale_mode != KVQ_SCALE_BLOCK_CHANNEL;
+}
 
 size_t workspace_impl(const kvq_cache* c, const kvq_recent* r, int32_t max_seq_len, int32_t n_query,
                       const char* who, int32_t window = 0) {
   g_err[0] = '\0';
   if (check_cache(c, who, false) != KVQ_OK) return 0;
   if (r && check_recent(r, *c, who, false) != KVQ_OK) return 0;
+  if (check_block_needs_recent(*c, r, who) != KVQ_OK) return 0;
   if (max_seq_len <= 0 || n_query <= 0) {
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
@@ -140,6 +163,7 @@ kvq_status append_impl(const kvq_cache* c, const kvq_recent* r, const void* k_ne
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
   if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if ((st = check_block_needs_recent(*c, r, who)) != KVQ_OK) return st;
   if (!k_new || !v_new || !start_pos) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new, v_new and start_pos must be non-NULL", who);
   if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
     return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
@@ -159,6 +183,7 @@ kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, cons
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
   if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if ((st = check_block_needs_recent(*c, r, who)) != KVQ_OK) return st;
   if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
   if (fused) {
     if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
@@ -186,6 +211,7 @@ kvq_status dequant_impl(const kvq_cache* c, const kvq_recent* r, int32_t which, 
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
   if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if ((st = check_block_needs_recent(*c, r, who)) != KVQ_OK) return st;
   if (which != 0 && which != 1) return fail(KVQ_ERR_INVALID_ARG, "%s: which must be 0 (K) or 1 (V)", who);
   if (!seq_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: seq_lens and out must be non-NULL", who);
   if (out_dtype != KVQ_DT_F32 && out_dtype != KVQ_DT_BF16)
@@ -288,8 +314,9 @@ struct ScratchSlot {
 ScratchSlot g_scratch[kMaxDevices];
 
 // The device address of this device's scratch array, looked up once per
-// device (with that device current); the counter region is cleared on
-// `stream` at that first call, ahead of the call's own kernel.
+// device (with that device current); the whole array is cleared on `stream`
+// at that first call, ahead of the call's own kernel (every call leaves the
+// counters and the partial words it used zero again).
 kvq_status scratch_of(int dev, hipStream_t stream, void** out, const char* who) {
   ScratchSlot& s = g_scratch[dev];
   bool first = false;
@@ -301,8 +328,8 @@ kvq_status scratch_of(int dev, hipStream_t stream, void** out, const char* who) 
     return fail(KVQ_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", who, dev,
                 hipGetErrorString(s.err));
   if (first) {
-    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, static_cast<uint32_t*>(s.ptr),
-                       static_cast<int>(kScratchCounters / 4));
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream, static_cast<uint32_t*>(s.ptr),
+                       static_cast<int>(kScratchBytes / 4));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: scratch clear failed: %s", who, hipGetErrorString(e));
   }
@@ -320,6 +347,7 @@ KVQ_API kvq_status kvq_append_decode_noalloc(const kvq_cache* c, const void* k_n
   const char* who = "kvq_append_decode_noalloc";
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
+  if ((st = check_block_needs_recent(*c, nullptr, who)) != KVQ_OK) return st;
   if (!k_new || !v_new) return fail(KVQ_ERR_INVALID_ARG, "%s: k_new and v_new must be non-NULL", who);
   if (in_dtype != KVQ_DT_F32 && in_dtype != KVQ_DT_BF16)
     return fail(KVQ_ERR_INVALID_ARG, "%s: in_dtype must be KVQ_DT_F32 or KVQ_DT_BF16", who);
@@ -362,6 +390,7 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
   kvq_status st = check_cache(c, who);
   if (st != KVQ_OK) return st;
   if (r && (st = check_recent(r, *c, who)) != KVQ_OK) return st;
+  if ((st = check_block_needs_recent(*c, r, who)) != KVQ_OK) return st;
   if (!q || !ctx_lens || !out) return fail(KVQ_ERR_INVALID_ARG, "%s: q, ctx_lens and out must be non-NULL", who);
   if (n <= 0) return fail(KVQ_ERR_INVALID_ARG, "%s: n must be positive (got %d)", who, n);
   if (window < 0) return fail(KVQ_ERR_INVALID_ARG, "%s: window must be at least 1 (got %d)", who, window);
@@ -371,7 +400,7 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
   // a hybrid cache at an MFMA head size: the MFMA kernel takes the INT8
   // keys and the generic kernel the ring rows
-  if (r && chunk_supported(c->head_dim)) {
+  if (r && mfma_hybrid_ok(*c)) {
     const DecodePlan plan = plan_chunk_hybrid(*c, n, r->window);
     st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
     if (st != KVQ_OK) return st;
@@ -427,7 +456,7 @@ KVQ_API size_t kvq_workspace_size_chunk_recent(const kvq_cache* c, const kvq_rec
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
   }
-  if (chunk_supported(c->head_dim)) return plan_chunk_hybrid(*c, n_query, r->window).workspace;
+  if (mfma_hybrid_ok(*c)) return plan_chunk_hybrid(*c, n_query, r->window).workspace;
   return plan_chunk_generic(*c, max_seq_len, n_query, 0).workspace;
 }
 

@@ -35,6 +35,9 @@ struct AppendParams {
   int32_t rwin, rcap;                  // recent window and ring slots
   int32_t scale_bf16;                  // per-token scales stored as bf16
   int32_t fp8;                         // FP8 codes: 1 E4M3, 2 E5M2 (no scales); 0 INT8
+  int32_t block;                       // block scales: 1 per head, 2 per channel (the block pass
+                                       // writes every row below the window); 0 per row
+  int32_t nblk;                        // block pass: blocks per (sequence, KV head) this launch covers
 };
 
 // Stores this lane's EPL values of a row as bf16 (nearest even).
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         if (on) store_lane_bf16<EPL>(p.ring[side] + (static_cast<int64_t>(bh) * p.rcap + pos % p.rcap) * D, lane, x);
         return;
       }
+      if (p.block) return;  // below the window: written by the block pass
     }
   }
   const int64_t dst = cache_row(p.geom, b, h, pos);
@@ -117,6 +121,124 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Block scales on a hybrid cache (abaddon kv_cache_quant_cuda.rs,
+// `quantize_with_granularity`, PerHead / PerChannel, over position-aligned
+// blocks of kBlockRows rows): block j of a sequence and KV head is quantized
+// by the append after which its first row has left the window, i.e. when
+// 16j lies in [start - W, L' - W) for this append's first position `start`
+// and new length L'.  Its rows are then all present (W >= 15): rows below
+// `start` in their ring slots, the others in this append's input (rounded
+// to bf16, as every row entering a hybrid cache is).  One wave per (side,
+// sequence, KV head, block); lane l holds element indices l, l + 64, ... of
+// all 16 rows.  The maximum is exact, so the codes follow the per-token
+// quantizer's steps over the block's reduction set: every element of the
+// block (per head) or each element index across the 16 rows (per channel).
+// Runs before the row pass, which overwrites ring slots.
+// ---------------------------------------------------------------------------
+template <int D, bool CHANNEL>
+__global__ __launch_bounds__(256) void block_quant_kernel(AppendParams p) {
+  constexpr int K = (D + kWave - 1) / kWave;  // element indices per lane
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int per_side = p.batch * p.geom.kvh * p.nblk;
+  if (w >= 2 * per_side) return;
+  const int side = w >= per_side ? 1 : 0;
+  const int r = w - side * per_side;
+  const int jrel = r % p.nblk;
+  const int bh = r / p.nblk;
+  const int h = bh % p.geom.kvh;
+  const int b = bh / p.geom.kvh;
+  const int start = p.pos_from_lens ? p.start_pos[b] - 1 : p.start_pos[b];
+  const int lo = start - p.rwin;                   // blocks whose first row is in [lo, hi) trigger
+  const int hi = start + p.n_new - p.rwin;
+  const int j0 = lo <= 0 ? 0 : (lo + kBlockRows - 1) / kBlockRows;
+  const int j = j0 + jrel;
+  if (start < 0 || kBlockRows * j >= hi) return;
+  const int p0 = kBlockRows * j;
+  float x[kBlockRows][K];
+#pragma unroll
+  for (int i = 0; i < kBlockRows; ++i) {
+    const int pos = p0 + i;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int d = lane + kWave * k;
+      float v = 0.0f;
+      if (d < D) {
+        if (pos < start) {  // an older row, in its ring slot
+          v = bf16_to_f32(p.ring[side][(static_cast<int64_t>(bh) * p.rcap + pos % p.rcap) * D + d]);
+        } else {            // this append's row pos - start, entering as bf16
+          const int64_t src = (static_cast<int64_t>(bh) * p.n_new + (pos - start)) * D + d;
+          const float raw = p.in_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p.src[side])[src])
+                                      : static_cast<const float*>(p.src[side])[src];
+          v = bf16_to_f32(f32_to_bf16_rne(raw));
+        }
+      }
+      x[i][k] = v;
+    }
+  }
+  float s[K];
+  if constexpr (CHANNEL) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kBlockRows; ++i) a = fmaxf(a, fabsf(x[i][k]));
+      s[k] = fmaxf(a, 1e-8f) / 127.0f;  // IEEE division (correctly rounded)
+    }
+  } else {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kBlockRows; ++i)
+#pragma unroll
+      for (int k = 0; k < K; ++k) a = fmaxf(a, fabsf(x[i][k]));
+#pragma unroll
+    for (int off = kWave / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
+    const float sh = fmaxf(a, 1e-8f) / 127.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) s[k] = sh;
+  }
+  int64_t row0 = -1;
+#pragma unroll
+  for (int i = 0; i < kBlockRows; ++i) {
+    const int64_t row = cache_row(p.geom, b, h, p0 + i);
+    if (i == 0) row0 = row;
+    if (row < 0) continue;  // outside the cache: not written
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int d = lane + kWave * k;
+      if (d >= D) continue;
+      const float y = x[i][k] / s[k];  // IEEE division, not a reciprocal multiply
+      float q = roundf(y);             // half away from zero
+      q = fminf(fmaxf(q, -127.0f), 127.0f);
+      p.codes[side][row * D + d] = static_cast<uint8_t>(static_cast<int>(q) + 128);
+    }
+    if (!CHANNEL && lane == 0) p.scales[side][row] = s[0];  // the block's scale on each of its rows
+  }
+  if (CHANNEL && row0 >= 0) {
+    // [row / 16] is the block's slot: contiguous (b, h, j), paged (page, h)
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int d = lane + kWave * k;
+      if (d < D) p.scales[side][(row0 / kBlockRows) * D + d] = s[k];
+    }
+  }
+}
+
+template <bool CHANNEL>
+void launch_block_quant(int head_dim, dim3 grid, hipStream_t st, const AppendParams& p) {
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL((block_quant_kernel<32, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((block_quant_kernel<64, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    case 96: hipLaunchKernelGGL((block_quant_kernel<96, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((block_quant_kernel<128, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    case 160: hipLaunchKernelGGL((block_quant_kernel<160, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    case 192: hipLaunchKernelGGL((block_quant_kernel<192, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    case 224: hipLaunchKernelGGL((block_quant_kernel<224, CHANNEL>), grid, dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL((block_quant_kernel<256, CHANNEL>), grid, dim3(256), 0, st, p); break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Dequantization: out = fl32((code - 128) * s) (abaddon kv_cache_quant_cuda.rs
 // `int8_dequant_bf16`; abaddon 0.2.0-rc.2 src/kv_cache_quant.rs
 // `dequantize`), optionally rounded to bf16.  One thread per 4 elements.
@@ -132,6 +254,7 @@ struct DequantParams {
   void* out;
   CacheGeom geom;
   int32_t batch, head_dim, groups, out_len, out_bf16;
+  int32_t channel;  // per-channel block scales: [row / 16][d]
   int64_t quads;  // B * KVH * out_len * D / 4
 };
 
@@ -164,6 +287,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       v[e] = p.fp8 == 2 ? fp8_decode<true>((c >> (8 * e)) & 0xffu) : fp8_decode<false>((c >> (8 * e)) & 0xffu);
+  } else if (row >= 0 && p.channel) {
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
+    const float4 s = *reinterpret_cast<const float4*>(p.scales + (row / kBlockRows) * D + d);
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = static_cast<float>(static_cast<int>((c >> (8 * e)) & 0xffu) - 128) * sv[e];
   } else if (row >= 0) {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(p.codes + row * D + d);
     const float s = load_scale(p.scales, row * p.groups + (p.groups == 1 ? 0 : d / 32), p.scale_bf16 != 0);
@@ -220,10 +350,25 @@ kvq_status launch_append(const kvq_cache& c, const void* k_new, const void* v_ne
   p.groups = scales_per_row(c);
   p.pos_from_lens = pos_from_lens ? 1 : 0;
   p.in_bf16 = in_dtype == KVQ_DT_BF16 ? 1 : 0;
+  p.block = c.scale_mode == KVQ_SCALE_BLOCK_HEAD ? 1 : (c.scale_mode == KVQ_SCALE_BLOCK_CHANNEL ? 2 : 0);
+  p.nblk = 0;
+  if (p.block) {
+    // block scales: first the blocks whose first row leaves the window (at
+    // most n_new / 16 + 2 per sequence), then the new rows of the window
+    p.nblk = n_new / kBlockRows + 2;
+    const int64_t waves = 2ll * c.batch * c.num_kv_heads * p.nblk;
+    if (waves > 0x7fffffffLL) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_append_recent: too many blocks");
+    const dim3 grid(static_cast<unsigned>((waves + 3) / 4));
+    if (p.block == 2) launch_block_quant<true>(c.head_dim, grid, stream, p);
+    else launch_block_quant<false>(c.head_dim, grid, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_append_recent: block launch failed: %s", hipGetErrorString(e));
+  }
   // one launch per pass: with a recent window, first the ring rows that
-  // leave it (at most min(n_new, W) per sequence), then the new rows
+  // leave it (at most min(n_new, W) per sequence; the block pass has done
+  // that with block scales), then the new rows
   const int passes = rc.window > 0 ? 2 : 1;
-  for (int pass = 0; pass < passes; ++pass) {
+  for (int pass = p.block ? 1 : 0; pass < passes; ++pass) {
     p.mode = rc.window == 0 ? kPlain : (pass == 0 ? kEvict : kRows);
     p.n = p.mode == kEvict ? (n_new < rc.window ? n_new : rc.window) : n_new;
     const int64_t rows = static_cast<int64_t>(c.batch) * c.num_kv_heads * p.n;
@@ -255,7 +400,8 @@ kvq_status launch_dequant(const kvq_cache& c, int which, const int32_t* seq_lens
   p.geom = geom_of(c);
   p.batch = c.batch;
   p.head_dim = c.head_dim;
-  p.groups = scales_per_row(c);
+  p.groups = c.scale_mode == KVQ_SCALE_BLOCK_HEAD ? 1 : scales_per_row(c);
+  p.channel = c.scale_mode == KVQ_SCALE_BLOCK_CHANNEL ? 1 : 0;
   p.out_len = out_len;
   p.out_bf16 = out_dtype == KVQ_DT_BF16 ? 1 : 0;
   p.quads = static_cast<int64_t>(c.batch) * c.num_kv_heads * out_len * c.head_dim / 4;

@@ -55,7 +55,10 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 constexpr int kCkWaves = 8;      // two groups of four, one wave of each per SIMD
 constexpr int kGroupWaves = 4;
 constexpr int kCkThreads = kCkWaves * kWave;
-constexpr int kCkTile = 64;     // tokens per tile
+// tokens per tile: 64, or 32 at head dim 256 (four buffers of 64-token
+// tiles would not fit the LDS; a 32-token tile at D = 256 carries the MFMA
+// work of a 64-token one at D = 128)
+constexpr int tile_tokens(int D) { return D > 128 ? 32 : 64; }
 constexpr int kCkBufs = 4;      // LDS tile buffers in rotation
 constexpr int kQBlock = 32;     // query positions per wave
 constexpr float kCkLog2e = 1.4426950408889634f;
@@ -178,6 +181,7 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   // group) weights its tokens by s_g / s_max
   constexpr bool G32 = SM == KVQ_SCALE_GROUP32;
   constexpr int NG = D / 32;
+  constexpr int kCkTile = tile_tokens(D);
   using TL = Tile<D, kCkTile, G32>;
   constexpr int kTT = kCkTile / 32;                        // 32-token S tiles per tile
   constexpr int kChunksPerRow = D / 16;                    // 16-code pieces per row
@@ -678,7 +682,7 @@ void launch_chunk_d(bool paged, int sm, dim3 grid, hipStream_t stream, const Chu
 
 }  // namespace
 
-bool chunk_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
+bool chunk_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
 
 size_t chunk_workspace(const kvq_cache&, int, int) { return 0; }
 
@@ -717,8 +721,9 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.total_wgs = static_cast<int32_t>(total);
   const dim3 grid(static_cast<unsigned>(total));
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  if (c.head_dim == 128) launch_chunk_d<128>(paged, c.scale_mode, grid, stream, p);
-  else launch_chunk_d<64>(paged, c.scale_mode, grid, stream, p);
+  if (c.head_dim == 128) launch_chunk_d<128>(paged, kernel_scale_mode(c), grid, stream, p);
+  else if (c.head_dim == 256) launch_chunk_d<256>(paged, kernel_scale_mode(c), grid, stream, p);
+  else launch_chunk_d<64>(paged, kernel_scale_mode(c), grid, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;

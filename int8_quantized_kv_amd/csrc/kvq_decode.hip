@@ -30,9 +30,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p, int D
     for (int s = 0; s < ns; ++s) {
       const float ms = p.part_ml[(base + s) * 2];
       if (ms != -INFINITY) num = fmaf(p.part_o[(base + s) * D + d], exp2f(ms - M), num);
+      p.part_o[(base + s) * D + d] = 0.0f;  // the workspace goes back to zero
     }
     const float val = den > 0.0f ? num / den : 0.0f;
     p.out[((static_cast<int64_t>(b) * H + h) * nq + qi) * D + d] = f32_to_bf16_rne(val);
+  }
+  __syncthreads();  // every thread has read the (m, l) pairs
+  for (int s = threadIdx.x; s < ns; s += blockDim.x) {
+    p.part_ml[(base + s) * 2] = 0.0f;
+    p.part_ml[(base + s) * 2 + 1] = 0.0f;
   }
 }
 
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
     const float fb = pm[j] == -INFINITY ? 0.0f : exp2f(pm[j] - M2);
     const float inv = 1.0f / fmaf(lj, fa, pl[j] * fb);
     if (slot == 0) {
-      const float* po = p.part_o + (v * H + h0 + j) * D + sub * 16;
+      float* po = p.part_o + (v * H + h0 + j) * D + sub * 16;
       uint16_t* orow = p.out + ((static_cast<int64_t>(b) * H + h0 + j) * nq + qi) * D + sub * 16;
 #pragma unroll
       for (int e = 0; e < 16; e += 4) {
@@ -188,6 +194,12 @@ __global__ __launch_bounds__(256) void chunk_ring_kernel(DecodeParams p) {
         w.z = f32_to_bf16_rne(fmaf(o[j][e + 2], fa, pv.z * fb) * inv);
         w.w = f32_to_bf16_rne(fmaf(o[j][e + 3], fa, pv.w * fb) * inv);
         *reinterpret_cast<ushort4*>(orow + e) = w;
+        // the workspace goes back to zero (this wave alone reads the row)
+        *reinterpret_cast<float4*>(po + e) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+      if (sub == 0) {
+        p.part_ml[(v * H + h0 + j) * 2] = 0.0f;
+        p.part_ml[(v * H + h0 + j) * 2 + 1] = 0.0f;
       }
     }
   }
@@ -200,6 +212,10 @@ int heads_per_wg(int gqa) {
 }
 
 bool use_stream(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
+
+// The streaming kernel takes head dims 32, 64 and 128 in every per-row scale
+// mode; per-channel block scales run on the generic kernel.
+bool stream_ok(const kvq_cache& c) { return use_stream(c.head_dim) && c.scale_mode != KVQ_SCALE_BLOCK_CHANNEL; }
 
 int pass_tokens(int head_dim, bool stream_kernel) {
   // tokens a workgroup consumes per step: whole 64-token wave blocks for the
@@ -245,7 +261,7 @@ bool decode_supported(int head_dim) { return head_dim % 32 == 0 && head_dim >= 3
 
 DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc, int window, bool generic) {
   DecodePlan pl;
-  const bool stream_kernel = !generic && use_stream(c.head_dim);
+  const bool stream_kernel = !generic && stream_ok(c);
   // a sliding window bounds each sequence's range: the window rounded out to
   // whole blocks
   if (window > 0 && max_seq_len > window + kBlock - 1) max_seq_len = window + kBlock - 1;
@@ -256,6 +272,9 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   if (ring) max_seq_len = max_seq_len > rc.window ? max_seq_len - rc.window : 1;
   const int gqa = c.num_heads / c.num_kv_heads;
   pl.heads_per_wg = heads_per_wg(gqa);
+  const int forced_hpw = env_int("KVQ_HEADS_PER_WG", 0);  // (tests and sweeps)
+  if (forced_hpw == 1 || forced_hpw == 2 || forced_hpw == 4)
+    if (gqa % forced_hpw == 0) pl.heads_per_wg = forced_hpw;
   const int step = pass_tokens(c.head_dim, stream_kernel);
   // Aim at about one workgroup per compute unit (one round), in whole
   // workgroup passes.  When one round would need splits longer than 2048
@@ -288,8 +307,8 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   const int forced_lf = env_int("KVQ_LONGEST_FIRST", -1);
   if (forced_lf >= 0) pl.longest_first = forced_lf != 0 && stream_kernel && c.batch <= kLongestFirstMax;
   const size_t partials = static_cast<size_t>(c.batch) * c.num_heads * pl.num_splits;
-  // per (sequence, head group): an arrival counter, then one ready flag per split
-  pl.counter_bytes = align_up(static_cast<size_t>(groups) * (1 + pl.num_splits) * sizeof(int32_t), 256);
+  // per (sequence, head group): the splits' merge-ticket counter
+  pl.counter_bytes = align_up(static_cast<size_t>(groups) * sizeof(int32_t), 256);
   pl.workspace = pl.counter_bytes + align_up(partials * 2 * sizeof(float), 256) +
                  partials * static_cast<size_t>(c.head_dim) * sizeof(float);
   return pl;
@@ -300,9 +319,10 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
                          int max_seq_len, hipStream_t stream, const void* new_k, const void* new_v,
                          int new_dtype, const RecentGeom& rc, int window) {
   const bool append = new_k != nullptr;
-  const bool stream_kernel = use_stream(c.head_dim);
-  if (append && !stream_kernel) {
-    // the generic kernel has no fused path: append the row first
+  const bool stream_kernel = stream_ok(c);
+  if (append && (!stream_kernel || is_block_mode(c))) {
+    // the generic kernel has no fused path, and a block-scale step may
+    // quantize a whole block: append the row first
     kvq_status st = launch_append(c, new_k, new_v, new_dtype, 1, seq_lens, stream, true, rc);
     if (st != KVQ_OK) return st;
   }
@@ -343,9 +363,9 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
   dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, c.batch);
   if (grid.y > 65535 || grid.z > 65535)
     return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_decode: grid too large");
-  const int sm = c.scale_mode;
+  const int sm = kernel_scale_mode(c);
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  const bool fused = append && stream_kernel;
+  const bool fused = append && stream_kernel && !is_block_mode(c);
   launch_decode_kernel(c.head_dim, stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: launch failed: %s", hipGetErrorString(e));
@@ -467,7 +487,7 @@ kvq_status launch_chunk_generic(const kvq_cache& c, const DecodePlan& plan, cons
   const dim3 grid(c.num_kv_heads * p.wg_per_kvh, plan.num_splits, static_cast<unsigned>(rows));
   if (grid.y > 65535) return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_chunk: grid too large");
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  launch_generic_any(c.head_dim, plan.heads_per_wg, c.scale_mode, paged, p, grid, stream);
+  launch_generic_any(c.head_dim, plan.heads_per_wg, kernel_scale_mode(c), paged, p, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   hipLaunchKernelGGL(decode_merge_kernel, dim3(c.num_heads, static_cast<unsigned>(rows)),

@@ -20,6 +20,9 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   constexpr bool G32 = SM == kSmGroup32;
   constexpr bool FP8 = SM == kSmFp8E4M3 || SM == kSmFp8E5M2;  // values, no scales
   constexpr bool E5 = SM == kSmFp8E5M2;
+  // per-channel block scales: each element dequantized with its block's
+  // scale for its index, (c - 128) s_d, before the dot products
+  constexpr bool CH = SM == kSmBlockChannel;
   // A token row is read by NSUB lanes, 16 bytes each, in a group of LPT
   // lanes (the power of two at or above NSUB; at head dims 96, 160, 192 and
   // 224 the group's last lanes hold zeros)
@@ -88,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
   for (int ip = 0; ip < npass; ip += U) {
     uint4 kb[U], vb[U];
     float ks[U], vs[U];
+    int64_t rowu[U];
     bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -104,15 +108,27 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
       } else {
         row = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.geom.max_len + tc;
       }
+      rowu[u] = row;
       kb[u] = zero_if_off(*reinterpret_cast<const uint4*>(p.k_codes + row * D + subc * 16));
       vb[u] = zero_if_off(*reinterpret_cast<const uint4*>(p.v_codes + row * D + subc * 16));
-      ks[u] = FP8 ? 1.0f : load_scale(p.k_scales, row * p.groups + grp, p.scale_bf16 != 0);
-      vs[u] = FP8 ? 1.0f : load_scale(p.v_scales, row * p.groups + grp, p.scale_bf16 != 0);
+      ks[u] = FP8 || CH ? 1.0f : load_scale(p.k_scales, row * p.groups + grp, p.scale_bf16 != 0);
+      vs[u] = FP8 || CH ? 1.0f : load_scale(p.v_scales, row * p.groups + grp, p.scale_bf16 != 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t kw[4] = {kb[u].x, kb[u].y, kb[u].z, kb[u].w};
       const uint32_t vw[4] = {vb[u].x, vb[u].y, vb[u].z, vb[u].w};
+      float kscl[CH ? 16 : 1], vscl[CH ? 16 : 1];  // this lane's 16 channel scales of the token's block
+      if constexpr (CH) {
+        const int64_t sidx = (rowu[u] / kBlockRows) * D + subc * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 a = *reinterpret_cast<const float4*>(p.k_scales + sidx + 4 * i);
+          const float4 c = *reinterpret_cast<const float4*>(p.v_scales + sidx + 4 * i);
+          kscl[4 * i] = a.x; kscl[4 * i + 1] = a.y; kscl[4 * i + 2] = a.z; kscl[4 * i + 3] = a.w;
+          vscl[4 * i] = c.x; vscl[4 * i + 1] = c.y; vscl[4 * i + 2] = c.z; vscl[4 * i + 3] = c.w;
+        }
+      }
       float part[HPW];
 #pragma unroll
       for (int j = 0; j < HPW; ++j) part[j] = 0.0f;
@@ -120,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float c = FP8 ? fp8_decode<E5>((kw[i] >> (8 * e)) & 0xffu) : byte_f32(kw[i], e);
+          float c = FP8 ? fp8_decode<E5>((kw[i] >> (8 * e)) & 0xffu) : byte_f32(kw[i], e);
+          if constexpr (CH) c = fmaf(c, kscl[4 * i + e], -128.0f * kscl[4 * i + e]);  // fl32((c - 128) s)
 #pragma unroll
           for (int j = 0; j < HPW; ++j) part[j] = fmaf(q[j][4 * i + e], c, part[j]);
         }
@@ -128,10 +145,13 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cv[4 * i + e] = FP8 ? fp8_decode<E5>((vw[i] >> (8 * e)) & 0xffu) : byte_f32(vw[i], e);
+        for (int e = 0; e < 4; ++e) {
+          cv[4 * i + e] = FP8 ? fp8_decode<E5>((vw[i] >> (8 * e)) & 0xffu) : byte_f32(vw[i], e);
+          if constexpr (CH) cv[4 * i + e] = fmaf(cv[4 * i + e], vscl[4 * i + e], -128.0f * vscl[4 * i + e]);
+        }
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
-        float sc = FP8 ? part[j] : (part[j] - 128.0f * qsum[j]) * ks[u];
+        float sc = FP8 || CH ? part[j] : (part[j] - 128.0f * qsum[j]) * ks[u];
         sc = group_sum<LPT>(sc) * p.scale_log2;
         const float sj = ok[u] ? sc : -INFINITY;
         if (sj > m[j] + kLazy) {
@@ -193,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(DecodeParams p
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[j][e] = FP8 ? o[j][e] : fmaf(-128.0f, ws[j], o[j][e]);
+    for (int e = 0; e < 16; ++e) o[j][e] = FP8 || CH ? o[j][e] : fmaf(-128.0f, ws[j], o[j][e]);
     float M = m[j];
     for (int off = LPT; off < kWave; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
     const float f = (m[j] == -INFINITY) ? 0.0f : exp2f(m[j] - M);
@@ -257,6 +277,7 @@ void launch_generic_all(int hpw, int sm, bool paged, const DecodeParams& p, dim3
       case kSmTokenBf16: go(hc, std::integral_constant<int, kSmTokenBf16>{}); break;
       case kSmFp8E4M3: go(hc, std::integral_constant<int, kSmFp8E4M3>{}); break;
       case kSmFp8E5M2: go(hc, std::integral_constant<int, kSmFp8E5M2>{}); break;
+      case kSmBlockChannel: go(hc, std::integral_constant<int, kSmBlockChannel>{}); break;
       default: go(hc, std::integral_constant<int, kSmToken>{}); break;
     }
   };

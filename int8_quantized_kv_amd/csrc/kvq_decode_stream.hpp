@@ -107,6 +107,7 @@ constexpr int kSmGroup32 = KVQ_SCALE_GROUP32;
 constexpr int kSmTokenBf16 = KVQ_SCALE_PER_TOKEN_BF16;
 constexpr int kSmFp8E4M3 = KVQ_CODES_FP8_E4M3;          // FP8 codes, no scales
 constexpr int kSmFp8E5M2 = KVQ_CODES_FP8_E5M2;
+constexpr int kSmBlockChannel = KVQ_SCALE_BLOCK_CHANNEL;  // per-channel block scales (generic kernel)
 constexpr float kLazy = 8.0f;      // log2 headroom before a rescale
 constexpr int kWeightShift = 7;    // weights carry 2^7 so they fill f16 range
 
@@ -325,16 +326,78 @@ __device__ __forceinline__ int sequence_of(const DecodeParams& p, int* scratch, 
 }
 
 // ---------------------------------------------------------------------------
-// Final output of HPW heads from the workgroup's own combined partial, or,
-// when several splits exist, by the last workgroup to arrive.  `acc` / `msum`
-// hold, for this thread's (head j, dim d) pairs, the workgroup's combined
-// unnormalised output and (m, l).
+// Split partials between workgroups.  A word of the partial area reads zero
+// until its split has written it, so the data is its own ready flag: a value
+// whose bits are zero (+0.0) is stored as -0.0, which every use treats alike,
+// and the merging workgroup returns each word it consumed to zero for the
+// next call.  Stores and loads are agent-scope atomics (they bypass the
+// per-XCD L2), so a merger on another XCD sees them without an L2 write-back
+// or invalidate.
+// ---------------------------------------------------------------------------
+constexpr int kPollBudget = 1 << 20;  // polling rounds per thread before a missing partial reads as zero
+
+__device__ __forceinline__ void put_partial(float* dst, float x) {
+  const uint32_t u = __float_as_uint(x);
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), u == 0u ? 0x80000000u : u, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t peek_partial(const float* src) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Words w1[k], w2[k] are first readings of a1[k], a2[k] (a slot not taken
+// part in holds a nonzero dummy and is never read).  Every word still reading
+// zero (not written yet) is read again, all of them together, until none is,
+// within
+// the thread's poll budget (which bounds the wait should a writer never
+// come; such a word then stays +0.0).
+template <int N, int M>
+__device__ __forceinline__ void await_partials(float* const (&a1)[N], uint32_t (&w1)[N], float* const (&a2)[M],
+                                               uint32_t (&w2)[M], int& budget) {
+  for (;;) {
+    bool missing = false;
+#pragma unroll
+    for (int k = 0; k < N; ++k) missing |= w1[k] == 0u;
+#pragma unroll
+    for (int k = 0; k < M; ++k) missing |= w2[k] == 0u;
+    if (!missing || budget <= 0) return;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (w1[k] == 0u) w1[k] = peek_partial(a1[k]);
+#pragma unroll
+    for (int k = 0; k < M; ++k)
+      if (w2[k] == 0u) w2[k] = peek_partial(a2[k]);
+    --budget;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void await_partials(float* const (&a)[N], uint32_t (&w)[N], int& budget) {
+  float* const none[1] = {nullptr};
+  uint32_t one[1] = {1u};  // (a dummy slot, never read)
+  await_partials(a, w, none, one, budget);
+}
+
+__device__ __forceinline__ void clear_partial(float* dst) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(dst), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Final output of HPW heads, from the workgroup's own combined partial
+// (sm_o, sm_ml) when the sequence has one split, else by the merging
+// workgroup.  Every split of a (sequence, head group) takes a ticket from its
+// counter once its first wave is through its tokens; the one that draws the
+// last ticket merges, and `last` says whether this is it.  Since
+// the others drew theirs first they are running and write their partials
+// without waiting on anything, so the merger's wait for them always ends.
+// The merger keeps its own partial in LDS.
 // ---------------------------------------------------------------------------
 template <int D, int HPW, int NT>
-__device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int split, int ns,
+__device__ void finish_split(const DecodeParams& p, int b, int h0, int split, int ns, bool last,
                              const float (*sm_o)[D], const float (*sm_ml)[2]) {
   const int H = p.num_heads;
-  __shared__ int sm_last;
   if (ns == 1) {
     for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
       const int j = idx / D, d = idx % D;
@@ -344,55 +407,27 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
     }
     return;
   }
-  // Split merge.  Each split first takes a ticket from the (sequence, head
-  // group) counter.  The last to arrive merges: it keeps its own (m, l, o) in
-  // LDS and reads the others' from the workspace.  Every other split writes
-  // its partial, waits until those stores are acknowledged, then raises its
-  // ready flag; the last one waits for each flag before reading that partial
-  // (the flag's split has taken its ticket, so it is running and gets there).
-  // Partials and flags go through agent-scope (L2-bypassing) stores and
-  // loads, so a merge on another XCD sees them without any L2 write-back or
-  // invalidate.  The merger leaves the counter and flags zero for the next call.
-  const int64_t grp = static_cast<int64_t>(b) * gridDim.x + hg;   // grid x = head groups
-  int32_t* cnt = p.counters + grp;
-  int32_t* flags = p.counters + static_cast<int64_t>(gridDim.x) * gridDim.z + grp * p.num_splits;
-  if (threadIdx.x == 0) sm_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
-  __syncthreads();
-  if (!sm_last) {
+  if (!last) {
     for (int idx = threadIdx.x; idx < HPW * D; idx += NT) {
       const int j = idx / D, d = idx % D;
       const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + split;
-      __hip_atomic_store(&p.part_o[pidx * D + d], sm_o[j][d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      put_partial(&p.part_o[pidx * D + d], sm_o[j][d]);
       if (d == 0) {
-        __hip_atomic_store(&p.part_ml[pidx * 2], sm_ml[j][0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.part_ml[pidx * 2 + 1], sm_ml[j][1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        put_partial(&p.part_ml[pidx * 2], sm_ml[j][0]);
+        put_partial(&p.part_ml[pidx * 2 + 1], sm_ml[j][1]);
       }
     }
-    // every wave's partial stores are acknowledged before the flag goes up:
-    // a workgroup-scope release emits no wait for global stores (and an
-    // agent-scope one a write-back of the whole L2), so wait for them
-    // explicitly (vmcnt 0; expcnt and lgkmcnt left at their maxima)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flags + split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  // the merger: wait for every other split's flag (one lane each), and reset
-  for (int s2 = threadIdx.x; s2 < ns; s2 += NT) {
-    if (s2 == split) continue;
-    while (__hip_atomic_load(flags + s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) __builtin_amdgcn_s_sleep(1);
-    __hip_atomic_store(flags + s2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  int budget = kPollBudget;
 
-  // Merge in split order (the same order whichever split arrives last), this
-  // split's (m, l, o) from LDS.  All loads of one round are independent and
-  // unconditional (indices clamped, surplus entries masked), so they are in
-  // flight together.
+  // Merge in split order (the same order whichever split merges), this
+  // split's (m, l, o) from LDS.  A round stages the (m, l) of up to kChunk
+  // splits in LDS; the first readings of those and of this thread's o words
+  // of the round's first kU splits all go out before anything is waited for.
   constexpr int kChunk = NT / HPW;   // splits whose (m, l) one round stages in LDS
   constexpr int kItems = (HPW * D + NT - 1) / NT;
+  constexpr int kU = 8;              // splits whose o words one pass reads
   __shared__ float sm_sm[HPW][kChunk];
   __shared__ float sm_sl[HPW][kChunk];
   float run_m[kItems], num[kItems], den[kItems];
@@ -404,52 +439,72 @@ __device__ void finish_split(const DecodeParams& p, int b, int h0, int hg, int s
   }
   for (int c0 = 0; c0 < ns; c0 += kChunk) {
     const int cnt_c = min(kChunk, ns - c0);
-    {
-      const int j = threadIdx.x / kChunk, u = threadIdx.x % kChunk;
-      const int sidx = min(c0 + u, ns - 1);
-      const int64_t pidx = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + sidx;
-      float mv, lv;
-      if (sidx == split) {
-        mv = sm_ml[j][0];
-        lv = sm_ml[j][1];
-      } else {
-        mv = __hip_atomic_load(&p.part_ml[pidx * 2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lv = __hip_atomic_load(&p.part_ml[pidx * 2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int jm = threadIdx.x / kChunk, um = threadIdx.x % kChunk;
+    const bool own_ml = um < cnt_c && c0 + um != split;
+    float* mlp = &p.part_ml[((static_cast<int64_t>(b) * H + h0 + jm) * p.num_splits + c0 + min(um, cnt_c - 1)) * 2];
+    float* const ma[2] = {mlp, mlp + 1};
+    uint32_t mw[2] = {own_ml ? peek_partial(ma[0]) : 1u, own_ml ? peek_partial(ma[1]) : 1u};
+    float* oa[kItems][kU];
+    uint32_t ow[kItems][kU];
+    auto read_o = [&](int u0) {
+#pragma unroll
+      for (int it = 0; it < kItems; ++it) {
+        const int idx = min(threadIdx.x + it * NT, HPW * D - 1);
+        const bool item = threadIdx.x + it * NT < HPW * D;
+        const int j = idx / D, d = idx % D;
+        const int64_t base = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + c0;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int uu = u0 + u;
+          oa[it][u] = &p.part_o[(base + min(uu, cnt_c - 1)) * D + d];
+          ow[it][u] = item && uu < cnt_c && c0 + uu != split ? peek_partial(oa[it][u]) : 1u;
+        }
       }
-      sm_sm[j][u] = u < cnt_c ? mv : -INFINITY;
-      sm_sl[j][u] = u < cnt_c ? lv : 0.0f;
+    };
+    read_o(0);
+    await_partials(ma, mw, oa[0], ow[0], budget);  // (the (m, l) pair and the first o words together)
+    if (own_ml) {
+      clear_partial(ma[0]);
+      clear_partial(ma[1]);
     }
+    const bool mine = um < cnt_c && c0 + um == split;
+    sm_sm[jm][um] = um < cnt_c ? (mine ? sm_ml[jm][0] : __uint_as_float(mw[0])) : -INFINITY;
+    sm_sl[jm][um] = um < cnt_c ? (mine ? sm_ml[jm][1] : __uint_as_float(mw[1])) : 0.0f;
     __syncthreads();
+    float newm[kItems];
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
-      const int idx = threadIdx.x + it * NT;
-      if (idx >= HPW * D) break;
-      const int j = idx / D, d = idx % D;
+      const int j = min(threadIdx.x + it * NT, HPW * D - 1) / D;
       float cm = -INFINITY;
       for (int u = 0; u < cnt_c; ++u) cm = fmaxf(cm, sm_sm[j][u]);
-      const float newm = fmaxf(run_m[it], cm);
-      if (newm == -INFINITY) continue;
-      const float f_old = run_m[it] == -INFINITY ? 0.0f : exp2f(run_m[it] - newm);
-      num[it] *= f_old;
-      den[it] *= f_old;
-      run_m[it] = newm;
-      const int64_t base = (static_cast<int64_t>(b) * H + h0 + j) * p.num_splits + c0;
-      for (int u0 = 0; u0 < cnt_c; u0 += 8) {
-        float ov[8];
+      newm[it] = fmaxf(run_m[it], cm);
+      if (newm[it] != -INFINITY) {
+        const float f_old = run_m[it] == -INFINITY ? 0.0f : exp2f(run_m[it] - newm[it]);
+        num[it] *= f_old;
+        den[it] *= f_old;
+        run_m[it] = newm[it];
+      }
+    }
+    for (int u0 = 0; u0 < cnt_c; u0 += kU) {
+      if (u0 > 0) read_o(u0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int uu = min(u0 + u, cnt_c - 1);
-          ov[u] = c0 + uu == split ? sm_o[j][d]
-                                   : __hip_atomic_load(&p.part_o[(base + uu) * D + d], __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-        }
+      for (int it = 0; it < kItems; ++it) await_partials(oa[it], ow[it], budget);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+      for (int it = 0; it < kItems; ++it) {
+        const int idx = threadIdx.x + it * NT;
+        if (idx >= HPW * D) break;
+        const int j = idx / D, d = idx % D;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
           const int uu = u0 + u;
-          const float ms = uu < cnt_c ? sm_sm[j][uu] : -INFINITY;
-          const float f = ms == -INFINITY ? 0.0f : exp2f(ms - newm);
-          num[it] = fmaf(ov[u], f, num[it]);
-          den[it] = fmaf(uu < cnt_c ? sm_sl[j][uu] : 0.0f, f, den[it]);
+          if (uu >= cnt_c) break;
+          const bool own = c0 + uu == split;
+          if (!own) clear_partial(oa[it][u]);
+          if (newm[it] == -INFINITY) continue;
+          const float ms = sm_sm[j][uu];
+          const float f = ms == -INFINITY ? 0.0f : exp2f(ms - newm[it]);
+          num[it] = fmaf(own ? sm_o[j][d] : __uint_as_float(ow[it][u]), f, num[it]);
+          den[it] = fmaf(sm_sl[j][uu], f, den[it]);
         }
       }
     }
@@ -687,17 +742,21 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   __shared__ uint2 sm_nv[D / 8];                     // fused append: new V codes
   __shared__ float sm_ns[2][NG];                     // fused append: new K / V scales
   __shared__ int sm_prog[kStreamWaves];              // blocks each wave has started
+  __shared__ int sm_last;                            // this split merges the sequence's splits
 
   // Consecutive workgroup ids go to consecutive XCDs, so the head group varies
   // fastest: each XCD then receives one head group of every (sequence, split),
-  // the same token count whatever the mix of lengths.
+  // the same token count whatever the mix of lengths.  Head group hg is KV
+  // head hg % KVH, query heads (hg / KVH) * HPW onwards of its GQA group:
+  // when KVH is a multiple of 8 the workgroups that share a KV head's rows
+  // then share an XCD and its L2.
   const int hg = blockIdx.x;
   const int split = blockIdx.y;
   int known_len;  // (the ranking's scratch lies in wave 0's score staging)
   const int b = sequence_of<kStreamThreads>(p, reinterpret_cast<int*>(&sm_part[0][0]), known_len);
   const int H = p.num_heads;
-  const int kvh = hg / p.wg_per_kvh;
-  const int h0 = kvh * (H / p.geom.kvh) + (hg % p.wg_per_kvh) * HPW;
+  const int kvh = hg % p.geom.kvh;
+  const int h0 = kvh * (H / p.geom.kvh) + (hg / p.geom.kvh) * HPW;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
@@ -1259,6 +1318,16 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   if (blk < nblk) run_block(blk, std::false_type{});
   if constexpr (PAGED) __builtin_amdgcn_s_setprio(0);
 
+  // the split's merge ticket, drawn by wave 0 as soon as its blocks are done,
+  // so that the round trip overlaps the other waves' last blocks.  The
+  // increment wraps: the last of the ns tickets returns the counter to zero
+  // for the next call.
+  uint32_t ticket = 0u;
+  if (ns > 1 && threadIdx.x == 0)
+    ticket = __builtin_amdgcn_atomic_inc32(reinterpret_cast<uint32_t*>(p.counters) +
+                                               static_cast<int64_t>(b) * gridDim.x + hg,
+                                           static_cast<uint32_t>(ns - 1), __ATOMIC_RELAXED, "agent");
+
   // ---- combine the wave: l and weight sums over lanes, o over token slots ------
 #pragma unroll
   for (int j = 0; j < HPW; ++j) {
@@ -1296,11 +1365,12 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     ring_into_wave<D, HPW, APPEND>(p, b, kvh, h0, wave, lane, L, L8, sm_fo[wave], sm_fml[wave],
                                    reinterpret_cast<float*>(&sm_part[wave][0]));
   }
+  if (threadIdx.x == 0) sm_last = ticket == static_cast<uint32_t>(ns - 1);
   __syncthreads();
   // ---- combine the waves ------------------------------------------------------------
   combine_waves<D, HPW, kStreamWaves, kStreamThreads>(sm_fo, sm_fml, sm_o, sm_ml);
   __syncthreads();
-  finish_split<D, HPW, kStreamThreads>(p, b, h0, hg, split, ns, sm_o, sm_ml);
+  finish_split<D, HPW, kStreamThreads>(p, b, h0, split, ns, sm_last != 0, sm_o, sm_ml);
 }
 
 // Launch of one scale mode's streaming-kernel instantiations (head_dim 32, 64,

@@ -33,8 +33,25 @@ inline int fp8_kind(const kvq_cache& c) {
   return c.scale_mode == KVQ_CODES_FP8_E4M3 ? 1 : (c.scale_mode == KVQ_CODES_FP8_E5M2 ? 2 : 0);
 }
 
-// Scales per row: 1 per token, head_dim / 32 for group-32, none for FP8 codes.
+// Block scales (per head or per channel over position-aligned blocks of
+// kBlockRows rows of one sequence and KV head; hybrid caches only).
+constexpr int kBlockRows = 16;
+inline bool is_block_mode(const kvq_cache& c) {
+  return c.scale_mode == KVQ_SCALE_BLOCK_HEAD || c.scale_mode == KVQ_SCALE_BLOCK_CHANNEL;
+}
+
+// The scale mode the attention and dequant kernels see: per-head block
+// scales are stored once per row, so they read as per-token scales.
+inline int kernel_scale_mode(const kvq_cache& c) {
+  return c.scale_mode == KVQ_SCALE_BLOCK_HEAD ? KVQ_SCALE_PER_TOKEN : c.scale_mode;
+}
+
+// Scales per row: 1 per token (per-head blocks store theirs on every row),
+// head_dim / 32 for group-32, none for FP8 codes; per-channel blocks hold
+// head_dim scales per 16 rows, head_dim / 16 per row on average (their
+// kernels index them per block, not through this count).
 inline int scales_per_row(const kvq_cache& c) {
+  if (c.scale_mode == KVQ_SCALE_BLOCK_CHANNEL) return c.head_dim / kBlockRows;
   return c.scale_mode == KVQ_SCALE_GROUP32 ? c.head_dim / 32 : (is_fp8(c) ? 0 : 1);
 }
 

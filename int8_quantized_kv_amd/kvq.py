@@ -26,6 +26,8 @@ KVQ_SCALE_GROUP32 = 1
 KVQ_SCALE_PER_TOKEN_BF16 = 2
 KVQ_CODES_FP8_E4M3 = 3
 KVQ_CODES_FP8_E5M2 = 4
+KVQ_SCALE_BLOCK_HEAD = 5
+KVQ_SCALE_BLOCK_CHANNEL = 6
 KVQ_LAYOUT_CONTIGUOUS = 0
 KVQ_LAYOUT_PAGED = 1
 KVQ_DT_F32 = 0

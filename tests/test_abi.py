@@ -302,7 +302,7 @@ def test_fp8_descriptors_need_no_scales():
         r = kvq.make_recent(4, 5, FAKE, FAKE)
         st, msg = _status("kvq_append_recent", ctypes.byref(d), ctypes.byref(r), FAKE, FAKE, 0, 1, FAKE, None)
         assert st == kvq.KVQ_ERR_UNSUPPORTED, msg
-    assert _status("kvq_cache_bytes", ctypes.byref(_desc(scale_mode=5)))[0] == 0
+    assert _status("kvq_cache_bytes", ctypes.byref(_desc(scale_mode=7)))[0] == 0
 
 
 def test_sizing_before_allocation():
@@ -348,3 +348,40 @@ def test_one_query_chunk_workspace_is_enough(head_dim):
     st, msg = _status("kvq_attention_chunk", ctypes.byref(c), FAKE, 1, FAKE, 1, ctypes.c_float(0.1), FAKE, FAKE,
                       ws - 1, 4096, None)
     assert st == kvq.KVQ_ERR_WORKSPACE and f"the {ws} bytes needed" in msg
+
+
+def test_block_scale_descriptors():
+    """Per-head and per-channel block scales (abaddon QuantGranularity over
+    16-row blocks): the byte count (per head: one fp32 scale per row; per
+    channel: head_dim scales per 16 rows), max_len a multiple of 16, a window
+    of at least 15, and the entry points without a recent window refusing
+    the modes before anything is launched."""
+    head = _desc(scale_mode=kvq.KVQ_SCALE_BLOCK_HEAD, max_len=4096)
+    chan = _desc(scale_mode=kvq.KVQ_SCALE_BLOCK_CHANNEL, max_len=4096)
+    rows = 2 * 2 * 4096
+    assert kvq.kvq_cache_bytes(head) == 2 * rows * (128 + 4)
+    assert kvq.kvq_cache_bytes(chan) == 2 * (rows * 128 + (rows // 16) * 128 * 4)
+    for mode in (kvq.KVQ_SCALE_BLOCK_HEAD, kvq.KVQ_SCALE_BLOCK_CHANNEL):
+        bad = _desc(scale_mode=mode, max_len=100)
+        with pytest.raises(kvq.KvqError, match="16"):
+            kvq.kvq_cache_bytes(bad)
+        d = _desc(scale_mode=mode, max_len=4096)
+        st, msg = _status("kvq_append", ctypes.byref(d), FAKE, FAKE, 0, 1, FAKE, None)
+        assert st == kvq.KVQ_ERR_UNSUPPORTED and "recent" in msg, msg
+        st, msg = _status("kvq_attention_decode", ctypes.byref(d), FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                          ctypes.c_size_t(1 << 20), 64, None)
+        assert st == kvq.KVQ_ERR_UNSUPPORTED, msg
+        st, msg = _status("kvq_attention_chunk", ctypes.byref(d), FAKE, 4, FAKE, 1, ctypes.c_float(0.1), FAKE,
+                          FAKE, ctypes.c_size_t(1 << 20), 64, None)
+        assert st == kvq.KVQ_ERR_UNSUPPORTED, msg
+        st, msg = _status("kvq_append_decode_noalloc", ctypes.byref(d), FAKE, FAKE, 0, FAKE, FAKE,
+                          ctypes.c_float(0.1), FAKE, 64, None)
+        assert st == kvq.KVQ_ERR_UNSUPPORTED, msg
+        with pytest.raises(kvq.KvqError, match="recent"):
+            kvq.kvq_workspace_size(d, 64, 1)
+        short = kvq.make_recent(14, 20, FAKE, FAKE)
+        st, msg = _status("kvq_append_recent", ctypes.byref(d), ctypes.byref(short), FAKE, FAKE, 0, 1, FAKE, None)
+        assert st == kvq.KVQ_ERR_INVALID_ARG and "15" in msg, msg
+        ok = kvq.make_recent(15, 16, FAKE, FAKE)
+        assert kvq.kvq_workspace_size_recent(d, ok, 4096) > 0
+        assert kvq.kvq_workspace_size_chunk_recent(d, ok, 4096, 64) > 0

@@ -23,6 +23,8 @@ CASES = [
     (128, 32, 8, [40, 500], 45, True, True),      # paged
     (64, 8, 2, [17, 130], 100, False, True),      # paged, non-causal
     (128, 8, 2, [1000], 1, True, False),          # n = 1
+    (256, 16, 4, [513, 64], 96, True, False),     # head dim 256: 32-token tiles
+    (256, 8, 2, [40, 300], 70, False, True),      # head dim 256, paged, non-causal
 ]
 
 
@@ -197,8 +199,9 @@ GENERIC_CASES = [
 
 @pytest.mark.parametrize("D,H,KVH,ctx,n,causal,paged,window,mode", GENERIC_CASES)
 def test_chunk_generic_head_dims(kvq, D, H, KVH, ctx, n, causal, paged, window, mode):
-    """head_dim 32 and 256 have no MFMA chunk kernel: each (sequence, query)
-    pair runs as a decode over the keys it sees, with the same masks."""
+    """Every scale mode at head dims 32 (no MFMA chunk kernel: each
+    (sequence, query) pair runs as a decode over the keys it sees, with the
+    same masks) and 256 (the MFMA kernel with 32-token tiles)."""
     import torch
     log(f"chunk generic: D={D} H={H} KVH={KVH} ctx={ctx} n={n} causal={causal} paged={paged} w={window} {mode}")
     B = len(ctx)

@@ -119,8 +119,21 @@ CHUNK_G32 = Workload("chunk_group32", 4, 32, 8, 128, 32, "contiguous", "bf16", 8
 RECENT_CHUNK = Workload("recent_chunk", 4, 32, 8, 128, 0, "contiguous", "bf16", 8192, 512, seed=12,
                         extra={"window": 128})
 
+# The recent-window decode step with per-head and per-channel block scales
+# (abaddon kv_cache_quant_cuda.rs `QuantGranularity`, over 16-row blocks).
+RECENT_BLOCK_HEAD = Workload("recent_block_head", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
+                             layers=32, outliers=4, seed=13, extra={"window": 128, "block": "head"})
+RECENT_BLOCK_CHANNEL = Workload("recent_block_channel", 16, 32, 8, 128, 0, "contiguous", "bf16", 4095, 1,
+                                layers=32, outliers=4, seed=14, extra={"window": 128, "block": "channel"})
+
+# Chunked prefill at head dim 256 (local-attention layers of the Gemma
+# family, which combs-models' sliding-window cache serves): 16 query heads on
+# 8 KV heads, the chunked-prefill shape otherwise.
+CHUNK_D256 = Workload("chunk_d256", 4, 16, 8, 256, 0, "contiguous", "bf16", 8192, 512, seed=15)
+
 ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
-                           BF16_SCALES, FP8_E4M3, FP8_CHUNK, CHUNK_G32, RECENT_CHUNK)}
+                           BF16_SCALES, FP8_E4M3, FP8_CHUNK, CHUNK_G32, RECENT_CHUNK, RECENT_BLOCK_HEAD,
+                           RECENT_BLOCK_CHANNEL, CHUNK_D256)}
 
 
 # ----------------------------------------------------------------------------
