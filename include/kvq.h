@@ -374,16 +374,18 @@ kvq_status kvq_dequant_recent(const kvq_cache* cache, const kvq_recent* recent, 
  * ring from there.  Query i at position ctx_lens[b] + i sees keys
  * t <= ctx_lens[b] + i (bottom-right causal) of that `get_kv` view
  * (abaddon kv_cache_quant_cuda.rs `OptimizedQuantizedKvCache::get_kv`).
- * head_dim 64 and 128: the MFMA chunk kernel attends to the INT8 keys and
- * writes the queries that see no ring row; a second launch attends the last
- * min(n, window) queries of each sequence to the ring rows and merges the
- * two partial softmaxes.  Other head dims: one decode per (sequence,
- * query) through the generic kernel.  batch * n at most 65535.
+ * head_dim 64 and 128 (per-row scales, per-head block scales): one launch
+ * of the MFMA chunk kernel, whose tiles hold both kinds of rows: INT8 rows
+ * widened to exact f16 values as in kvq_attention_chunk, ring rows converted
+ * to f16 with one power of two per row (exact for every element within
+ * 2^28 of its row's largest), their own per-token factors beside them; no
+ * workspace.  Other head dims and per-channel block scales: one decode per
+ * (sequence, query) through the generic kernel, batch * n at most 65535.
  *   q, out, ctx_lens, max_ctx_len_hint: as kvq_attention_chunk; ctx_lens[b]
  *              must not exceed the hint (at head_dim 64 and 128 a larger
  *              length is taken as the hint)
  *   workspace: kvq_workspace_size_chunk_recent(cache, recent,
- *              max_ctx_len_hint + n, n) bytes
+ *              max_ctx_len_hint + n, n) bytes (0 on the MFMA path)
  * Errors: those of kvq_attention_chunk, plus the recent descriptor's.
  */
 kvq_status kvq_attention_chunk_recent(const kvq_cache* cache, const kvq_recent* recent, const uint16_t* q,

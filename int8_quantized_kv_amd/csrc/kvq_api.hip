@@ -398,14 +398,12 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
   if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
-  // a hybrid cache at an MFMA head size: the MFMA kernel takes the INT8
-  // keys and the generic kernel the ring rows
+  // a hybrid cache at an MFMA head size: the MFMA kernel stages INT8 rows and
+  // bf16 ring rows in the same tiles (no workspace)
   if (r && mfma_hybrid_ok(*c)) {
-    const DecodePlan plan = plan_chunk_hybrid(*c, n, r->window);
-    st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
-    if (st != KVQ_OK) return st;
-    return launch_chunk_generic(*c, plan, q, n, ctx_lens, 1, attn_scale, out, workspace, max_ctx_len_hint + n,
-                                static_cast<hipStream_t>(stream), 0, recent_of(r), true);
+    const RecentGeom rc = recent_of(r);
+    return launch_chunk(*c, q, n, ctx_lens, 1, attn_scale, out, workspace, max_ctx_len_hint,
+                        static_cast<hipStream_t>(stream), 0, &rc);
   }
   // head dims without an MFMA chunk kernel go through the generic kernel
   if (r || !chunk_supported(c->head_dim)) {
@@ -456,7 +454,7 @@ KVQ_API size_t kvq_workspace_size_chunk_recent(const kvq_cache* c, const kvq_rec
     fail(KVQ_ERR_INVALID_ARG, "%s: max_seq_len and n_query must be positive", who);
     return 0;
   }
-  if (mfma_hybrid_ok(*c)) return plan_chunk_hybrid(*c, n_query, r->window).workspace;
+  if (mfma_hybrid_ok(*c)) return 0;  // the MFMA kernel needs none
   return plan_chunk_generic(*c, max_seq_len, n_query, 0).workspace;
 }
 

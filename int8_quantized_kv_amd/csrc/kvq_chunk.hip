@@ -83,15 +83,14 @@ struct ChunkParams {
   int32_t causal;
   int32_t window;       // sliding window (0: none): query p sees keys in (p - window, p]
   float scale_log2;     // attn_scale * log2(e)
-  // recent-window cache (rwin > 0): only the INT8 keys, below L - rwin, are
-  // attended here; a query that also sees ring rows leaves an unnormalised
-  // split partial (m, l, o) at slot part_slot of part_stride per (sequence,
-  // query, head) instead of its output
+  // recent-window cache (rwin > 0): the last rwin of each sequence's L0 + n
+  // rows are bf16 rows in ring slot position % rcap, staged in the same
+  // tiles as the INT8 rows below them
   int32_t rwin;
   int32_t len_cap;      // hint + n when rwin > 0 (ctx_lens clamp to the hint)
-  int32_t part_stride, part_slot;
-  float* part_o;
-  float* part_ml;
+  int32_t rcap;
+  const uint16_t* rk;   // [B, KVH, rcap, D] bf16
+  const uint16_t* rv;
 };
 
 // LDS tile geometry for TOK tokens.  K rows hold D f16 values and are padded
@@ -168,8 +167,9 @@ __device__ __forceinline__ int64_t row_of(const ChunkParams& p, int b, int g, in
 
 // SM: KVQ_SCALE_PER_TOKEN, KVQ_SCALE_PER_TOKEN_BF16 (scales stored as bf16)
 // or an FP8 code format (values, no scales); a template argument so that each
-// mode keeps its registers
-template <int D, bool PAGED, int SM>
+// mode keeps its registers.  RING: a hybrid cache whose ring rows join the
+// tiles (below).
+template <int D, bool PAGED, int SM, bool RING>
 __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   constexpr bool SBF = SM == KVQ_SCALE_PER_TOKEN_BF16;
   constexpr bool FP8 = SM == KVQ_CODES_FP8_E4M3 || SM == KVQ_CODES_FP8_E5M2;
@@ -209,10 +209,11 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   const int g = bg % p.geom.kvh;
   const int b = bg / p.geom.kvh;
 
-  const int cap = p.rwin > 0 ? min(capacity(p.geom), p.len_cap) : capacity(p.geom);
-  const int L0 = min(max(p.ctx_lens[b], 0), p.rwin > 0 ? cap - p.n : cap);
-  // keys attended here: all that exist, or the INT8 ones of a hybrid cache
-  const int Ltot = p.rwin > 0 ? max(min(L0 + p.n, cap) - p.rwin, 0) : min(L0 + p.n, cap);
+  const int cap = RING ? min(capacity(p.geom), p.len_cap) : capacity(p.geom);
+  const int L0 = min(max(p.ctx_lens[b], 0), RING ? cap - p.n : cap);
+  const int Ltot = min(L0 + p.n, cap);         // keys that exist
+  const int L8 = RING ? max(Ltot - p.rwin, 0) : Ltot;  // a hybrid cache's ring rows start here
+  const int64_t ring0 = (static_cast<int64_t>(b) * p.geom.kvh + g) * p.rcap;
   const int items = p.hpg * p.nblk;
 
   int wg_end = 0;
@@ -273,6 +274,12 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   uint4 lreg[kLoads];
   uint32_t sreg = 0u;  // scale word as loaded, decoded when the tile is stored
   float greg[G32 ? NG : 1];  // group-32: the token's group scales as loaded
+  static_assert(!RING || 2 * kChunks == kLoads * kCkThreads, "ring pieces: every thread holds whole pieces");
+  // the clamped key of piece id of the tile at t0 (row 0 stands in when no key exists)
+  auto piece_key = [&](int t0, int id) {
+    const int t = t0 + id / kChunksPerRow;
+    return max(t < Ltot ? t : Ltot - 1, 0);
+  };
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
@@ -280,15 +287,13 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
       if (j < 2 * kChunks) {
         const bool kside = j < kChunks;
         const int id = kside ? j : j - kChunks;
-        int t = t0 + id / kChunksPerRow;
-        t = max(t < Ltot ? t : Ltot - 1, 0);  // (row 0 stands in when no key exists)
-        const int64_t row = row_of<PAGED>(p, b, g, t);
+        const int64_t row = row_of<PAGED>(p, b, g, piece_key(t0, id));
         lreg[i] = *reinterpret_cast<const uint4*>((kside ? p.k_codes : p.v_codes) + row * D + 16 * (id % kChunksPerRow));
       }
     }
     if (ld_s && !FP8) {
       const int t = t0 + (tid & (kCkTile - 1));
-      if (t < Ltot) {
+      if (t < (RING ? L8 : Ltot)) {
         const int64_t row = row_of<PAGED>(p, b, g, t);
         if constexpr (G32) {
           const float* gs = (tid < kCkTile ? p.k_scales : p.v_scales) + row * NG;
@@ -330,7 +335,8 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
         *reinterpret_cast<uint4*>(dst + 16) = make_uint4(k2.x, k2.y, k3.x, k3.y);
       }
     }
-    if (ld_s) {
+    if (ld_s && !(RING && t0 + (tid & (kCkTile - 1)) >= L8 && t0 + (tid & (kCkTile - 1)) < Ltot)) {
+      // (a ring row's factors are written by its first piece's thread above)
       const int tl = tid & (kCkTile - 1);
       const bool ok = t0 + tl < Ltot;
       // which half of the word holds a bf16 scale: the parity of the row
@@ -361,6 +367,76 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
         reinterpret_cast<float*>(buf + TL::kLsv)[tl] = ok ? __builtin_amdgcn_logf(sv) : -INFINITY;
         reinterpret_cast<float*>(buf + TL::kRsv)[tl] = ok ? 1.0f / sv : 0.0f;
       }
+    }
+  };
+  // A hybrid cache's ring rows, in the tiles that hold any: store_tile has
+  // staged the INT8 storage at their positions; each thread overwrites the
+  // pieces it stored there (so its own later writes win) with the ring row
+  // converted to f16 values x 2^sh, sh set by the row's largest |x| (a
+  // reduction over the row's pieces, which consecutive threads hold) so
+  // that it lands in [2^14, 2^15): exact for every element within 2^28 of
+  // that largest.  The row's per-token factors carry 2^-sh, as an INT8
+  // row's carry its scale (store_tile leaves them to this step).  Kept out
+  // of the loader so that the tiles without ring rows run the plain code.
+  auto ring_fixup = [&](uint8_t* buf, int t0, float kfac) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int j = tid + i * kCkThreads;
+      const bool kside = j < kChunks;
+      const int id = kside ? j : j - kChunks;
+      const int r = id / kChunksPerRow, c = id % kChunksPerRow;
+      const int t = piece_key(t0, id);
+      const bool ring = t >= L8;
+      const uint4* src =
+          reinterpret_cast<const uint4*>((kside ? p.rk : p.rv) + (ring0 + t % p.rcap) * D + 16 * c);
+      const uint4 a0 = src[0], a1 = src[1];
+      const uint32_t wv[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      float x[16];
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[2 * e] = __uint_as_float(wv[e] << 16);
+        x[2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
+        m = fmaxf(m, fmaxf(fabsf(x[2 * e]), fabsf(x[2 * e + 1])));
+      }
+      if (!ring) m = 0.0f;
+#pragma unroll
+      for (int off = 1; off < kChunksPerRow; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+      const int sh = m > 0.0f && m <= 3.4e38f ? min(max(14 - ilogbf(m), -120), 120) : 0;
+      if (ring) {
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          h[e] = __builtin_bit_cast(uint32_t, pack2(ldexpf(x[2 * e], sh), ldexpf(x[2 * e + 1], sh)));
+        uint8_t* dst = buf + (kside ? TL::k_off(r, 2 * c) : TL::v_off(r, 2 * c));
+        *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(h[4], h[5], h[6], h[7]);
+        if (c == 0 && t0 + r < Ltot) {
+          if (kside) {
+            reinterpret_cast<float*>(buf + TL::kKc)[r] = ldexpf(kfac, -sh);
+            if constexpr (G32) {
+              float* rk = reinterpret_cast<float*>(buf + TL::kRk);
+#pragma unroll
+              for (int k = 0; k + 1 < NG; ++k) rk[k * kCkTile + r] = 1.0f;
+            }
+          } else {
+            reinterpret_cast<float*>(buf + TL::kLsv)[r] = static_cast<float>(-sh);
+            reinterpret_cast<float*>(buf + TL::kRsv)[r] = ldexpf(1.0f, sh);
+            if constexpr (G32) {
+              _Float16* rv = reinterpret_cast<_Float16*>(buf + TL::kRv);
+#pragma unroll
+              for (int k = 0; k < NG; ++k) rv[k * kCkTile + r] = static_cast<_Float16>(1.0f);
+            }
+          }
+        }
+      }
+    }
+  };
+  // stage tile t0 into buf: the loaded pieces, then (hybrid caches) its ring rows
+  auto stage_tile = [&](uint8_t* buf, int t0, float kfac) {
+    store_tile(buf, t0, kfac);
+    if constexpr (RING) {
+      if (t0 + kCkTile > L8) ring_fixup(buf, t0, kfac);
     }
   };
 
@@ -418,10 +494,10 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   }
 
   // Prologue: tiles 0 and 1 in LDS, tile 2 in flight.
-  store_tile(smem, tbase, kfac);
+  stage_tile(smem, tbase, kfac);
   if (ntiles > 1) {
     load_tile(tbase + kCkTile);
-    store_tile(smem + TL::kBytes, tbase + kCkTile, kfac);
+    stage_tile(smem + TL::kBytes, tbase + kCkTile, kfac);
   }
   if (ntiles > 2) load_tile(tbase + 2 * kCkTile);
   __syncthreads();
@@ -606,17 +682,24 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
     }
   };
   auto loader_step = [&](int t) {
-    if (t + 2 < ntiles) store_tile(smem + ((t + 2) % kCkBufs) * TL::kBytes, tbase + (t + 2) * kCkTile, kfac);
+    if (t + 2 < ntiles) stage_tile(smem + ((t + 2) % kCkBufs) * TL::kBytes, tbase + (t + 2) * kCkTile, kfac);
     if (t + 3 < ntiles) load_tile(tbase + (t + 3) * kCkTile);
   };
 
+  // Where each group's share of the loader work goes.  Both groups may store
+  // tile t + 2 in their own MFMA phase (group 0 in phase 2t, group 1 in
+  // 2t + 1): its buffer last held tile t - 2, whose last reader, group 1's
+  // values of tile t - 2, ran in phase 2t - 1.  Doing so frees registers the
+  // ring fix-up and head dim 256 need; elsewhere group 0 stores in its vector
+  // phase, which measured no different.
+  constexpr bool kLoadInMfma = RING || D == 256;
   if (grp == 1) __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     mfma_step(t);
-    if (grp == 1) loader_step(t);
+    if (kLoadInMfma || grp == 1) loader_step(t);
     __syncthreads();
     softmax_step(t);
-    if (grp == 0) loader_step(t);
+    if (!kLoadInMfma && grp == 0) loader_step(t);
     __syncthreads();
   }
   mfma_step(ntiles);  // values of the last tile (its S product is unused)
@@ -627,27 +710,6 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
   if (!q_ok) return;
   const float l_tot = other_half_sum(l_run);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-  const int q0 = max(p.n - p.rwin, 0);  // the last rwin queries see ring rows (L0 <= hint)
-  if (p.rwin > 0 && qi >= q0) {
-    // the query also sees ring rows: a split partial in log2 units
-    // (w / sV = 2^(score - m_run), so l_tot and the weighted value sum are
-    // relative to m_run), rows (b, qi - q0)
-    const int64_t prow = static_cast<int64_t>(b) * (p.n - q0) + qi - q0;
-    const int64_t pidx = (prow * p.heads + head) * p.part_stride + p.part_slot;
-    float* po = p.part_o + pidx * D;
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        *reinterpret_cast<float4*>(po + 32 * dt + 8 * q4 + 4 * half) =
-            make_float4(oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1],
-                        oacc[dt][4 * q4 + 2], oacc[dt][4 * q4 + 3]);
-    if (half == 0) {
-      p.part_ml[pidx * 2] = l_tot > 0.0f ? m_run : -INFINITY;
-      p.part_ml[pidx * 2 + 1] = l_tot;
-    }
-    return;
-  }
   uint16_t* orow = p.out + ((static_cast<int64_t>(b) * p.heads + head) * p.n + qi) * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) {
@@ -664,19 +726,27 @@ __global__ __launch_bounds__(kCkThreads, 1) void chunk_kernel(ChunkParams p) {
 }
 
 template <int D, int SM>
-void launch_chunk_sm(bool paged, dim3 grid, hipStream_t stream, const ChunkParams& p) {
-  if (paged) hipLaunchKernelGGL((chunk_kernel<D, true, SM>), grid, dim3(kCkThreads), 0, stream, p);
-  else hipLaunchKernelGGL((chunk_kernel<D, false, SM>), grid, dim3(kCkThreads), 0, stream, p);
+void launch_chunk_sm(bool paged, bool ring, dim3 grid, hipStream_t stream, const ChunkParams& p) {
+  constexpr bool FP8 = SM == KVQ_CODES_FP8_E4M3 || SM == KVQ_CODES_FP8_E5M2;
+  if constexpr (!FP8 && D != 256) {  // hybrid caches: INT8 codes, head dims 64 and 128
+    if (ring) {
+      if (paged) hipLaunchKernelGGL((chunk_kernel<D, true, SM, true>), grid, dim3(kCkThreads), 0, stream, p);
+      else hipLaunchKernelGGL((chunk_kernel<D, false, SM, true>), grid, dim3(kCkThreads), 0, stream, p);
+      return;
+    }
+  }
+  if (paged) hipLaunchKernelGGL((chunk_kernel<D, true, SM, false>), grid, dim3(kCkThreads), 0, stream, p);
+  else hipLaunchKernelGGL((chunk_kernel<D, false, SM, false>), grid, dim3(kCkThreads), 0, stream, p);
 }
 
 template <int D>
-void launch_chunk_d(bool paged, int sm, dim3 grid, hipStream_t stream, const ChunkParams& p) {
+void launch_chunk_d(bool paged, bool ring, int sm, dim3 grid, hipStream_t stream, const ChunkParams& p) {
   switch (sm) {
-    case KVQ_SCALE_PER_TOKEN_BF16: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN_BF16>(paged, grid, stream, p); break;
-    case KVQ_CODES_FP8_E4M3: launch_chunk_sm<D, KVQ_CODES_FP8_E4M3>(paged, grid, stream, p); break;
-    case KVQ_CODES_FP8_E5M2: launch_chunk_sm<D, KVQ_CODES_FP8_E5M2>(paged, grid, stream, p); break;
-    case KVQ_SCALE_GROUP32: launch_chunk_sm<D, KVQ_SCALE_GROUP32>(paged, grid, stream, p); break;
-    default: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN>(paged, grid, stream, p); break;
+    case KVQ_SCALE_PER_TOKEN_BF16: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN_BF16>(paged, ring, grid, stream, p); break;
+    case KVQ_CODES_FP8_E4M3: launch_chunk_sm<D, KVQ_CODES_FP8_E4M3>(paged, ring, grid, stream, p); break;
+    case KVQ_CODES_FP8_E5M2: launch_chunk_sm<D, KVQ_CODES_FP8_E5M2>(paged, ring, grid, stream, p); break;
+    case KVQ_SCALE_GROUP32: launch_chunk_sm<D, KVQ_SCALE_GROUP32>(paged, ring, grid, stream, p); break;
+    default: launch_chunk_sm<D, KVQ_SCALE_PER_TOKEN>(paged, ring, grid, stream, p); break;
   }
 }
 
@@ -688,7 +758,7 @@ size_t chunk_workspace(const kvq_cache&, int, int) { return 0; }
 
 kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int32_t* ctx_lens, int causal,
                         float attn_scale, uint16_t* out, void*, int max_ctx_len, hipStream_t stream, int window,
-                        const ChunkPartials* partials) {
+                        const RecentGeom* ring) {
   ChunkParams p{};
   p.q = q;
   p.out = out;
@@ -705,13 +775,15 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.causal = causal || window > 0 ? 1 : 0;
   p.window = window > 0 ? window : 0;
   p.scale_log2 = attn_scale * kCkLog2e;
-  if (partials) {
-    p.rwin = partials->rwin;
+  const bool hybrid = ring != nullptr && ring->window > 0;
+  if (hybrid) {
+    if (c.head_dim != 64 && c.head_dim != 128)
+      return fail(KVQ_ERR_UNSUPPORTED, "kvq_attention_chunk_recent: the MFMA path takes head dims 64 and 128");
+    p.rwin = ring->window;
     p.len_cap = max_ctx_len + n;
-    p.part_stride = partials->stride;
-    p.part_slot = partials->slot;
-    p.part_o = partials->o;
-    p.part_ml = partials->ml;
+    p.rcap = ring->cap;
+    p.rk = ring->k;
+    p.rv = ring->v;
   }
   const int64_t items = static_cast<int64_t>(p.hpg) * p.nblk;
   const int64_t per_bg = (items + kCkWaves - 1) / kCkWaves;
@@ -721,9 +793,9 @@ kvq_status launch_chunk(const kvq_cache& c, const uint16_t* q, int n, const int3
   p.total_wgs = static_cast<int32_t>(total);
   const dim3 grid(static_cast<unsigned>(total));
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  if (c.head_dim == 128) launch_chunk_d<128>(paged, kernel_scale_mode(c), grid, stream, p);
-  else if (c.head_dim == 256) launch_chunk_d<256>(paged, kernel_scale_mode(c), grid, stream, p);
-  else launch_chunk_d<64>(paged, kernel_scale_mode(c), grid, stream, p);
+  if (c.head_dim == 128) launch_chunk_d<128>(paged, hybrid, kernel_scale_mode(c), grid, stream, p);
+  else if (c.head_dim == 256) launch_chunk_d<256>(paged, hybrid, kernel_scale_mode(c), grid, stream, p);
+  else launch_chunk_d<64>(paged, hybrid, kernel_scale_mode(c), grid, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_chunk: launch failed: %s", hipGetErrorString(e));
   return KVQ_OK;

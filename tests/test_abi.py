@@ -244,15 +244,19 @@ def test_recent_argument_errors():
 
 
 def test_chunk_recent_workspace():
-    """Chunks over a hybrid cache run one decode per (sequence, query): the
-    workspace holds partials for batch * n rows, any n including 1, and the
-    descriptor is checked first."""
+    """Chunks over a hybrid cache: at head dims 64 and 128 one MFMA launch
+    with no workspace; elsewhere (and with per-channel block scales) one
+    decode per (sequence, query), whose workspace holds partials for
+    batch * n rows, any n including 1.  The descriptor is checked first."""
     r = _recent(window=16, capacity=17)
-    one = kvq.kvq_workspace_size_chunk_recent(_desc(), r, 64, 1)
-    eight = kvq.kvq_workspace_size_chunk_recent(_desc(), r, 64, 8)
-    assert 0 < one < eight
-    for d in (32, 256):
-        assert kvq.kvq_workspace_size_chunk_recent(_desc(head_dim=d), r, 64, 8) > 0
+    for d in (64, 128):
+        assert kvq.kvq_workspace_size_chunk_recent(_desc(head_dim=d), r, 64, 8) == 0
+    for d in (32, 96, 256):
+        one = kvq.kvq_workspace_size_chunk_recent(_desc(head_dim=d), r, 64, 1)
+        eight = kvq.kvq_workspace_size_chunk_recent(_desc(head_dim=d), r, 64, 8)
+        assert 0 < one < eight
+    chan = _desc(scale_mode=kvq.KVQ_SCALE_BLOCK_CHANNEL, max_len=64)
+    assert kvq.kvq_workspace_size_chunk_recent(chan, r, 64, 8) > 0
     with pytest.raises(kvq.KvqError, match="window"):
         kvq.kvq_workspace_size_chunk_recent(_desc(), _recent(window=0), 64, 8)
     with pytest.raises(kvq.KvqError, match="positive"):
@@ -338,7 +342,7 @@ def test_noalloc_host_errors():
     assert st == kvq.KVQ_ERR_WORKSPACE and "maximum" in msg
 
 
-@pytest.mark.parametrize("head_dim", [32, 256])
+@pytest.mark.parametrize("head_dim", [32, 96])
 def test_one_query_chunk_workspace_is_enough(head_dim):
     """kvq_workspace_size(cache, hint + 1, 1) covers a one-query chunk at head
     dims that run chunks on the generic kernel (whose splits are shorter than
@@ -384,4 +388,6 @@ def test_block_scale_descriptors():
         assert st == kvq.KVQ_ERR_INVALID_ARG and "15" in msg, msg
         ok = kvq.make_recent(15, 16, FAKE, FAKE)
         assert kvq.kvq_workspace_size_recent(d, ok, 4096) > 0
-        assert kvq.kvq_workspace_size_chunk_recent(d, ok, 4096, 64) > 0
+        # per-head blocks chunk on the MFMA kernel (no workspace), per-channel on the generic one
+        got = kvq.kvq_workspace_size_chunk_recent(d, ok, 4096, 64)
+        assert got == 0 if mode == kvq.KVQ_SCALE_BLOCK_HEAD else got > 0

@@ -142,3 +142,41 @@ def test_value_rows_of_very_different_size(kvq, group, focus):
         qb_d, qv_d = wl.random_q(12, (B, H, D))
     x = {"k": k.astype(np.float32), "v": v.astype(np.float32)}
     _run(kvq, x, qb_c, qv_c, qb_d, qv_d, group, f"V 1e-6/1e4 {focus}")
+
+
+@pytest.mark.parametrize("group", [0, 32])
+def test_ring_rows_of_very_different_size(kvq, group):
+    """Chunked prefill over a hybrid cache stages its ring rows (bf16) in the
+    MFMA tiles as f16 with one power of two per row.  Ring rows alternate
+    between V absmax about 1e-6 and 1e4, with unit-normal keys spreading
+    attention over both; each row keeps its own power of two, so neither
+    kind loses its bits.  Against the oracle's get_kv view, with the scaled bar."""
+    import torch
+    W, L0, n = 32, 150, 40
+    T = L0 + n
+    log(f"range: ring rows 1e-6 / 1e4, group={group}")
+    x = wl.random_kv(400 + group, (B, KVH, T, D), "f32")
+    odd = (np.arange(T) % 2 == 1)[None, None, :, None]
+    mag = np.where(odd, 1e-6 / 4, 1e4 / 4).astype(np.float32)
+    x = {"k": x["k"], "v": (x["v"] * mag).astype(np.float32)}
+    cache = kvq.Int8KVCache(B, H, KVH, D, max_len=T, group32=(group == 32), fill=0, recent_window=W)
+    cache.append(kv_dev(np.ascontiguousarray(x["k"][:, :, :L0])), kv_dev(np.ascontiguousarray(x["v"][:, :, :L0])),
+                 dev_tensor(np.zeros(B, np.int32)))
+    cache.append(kv_dev(np.ascontiguousarray(x["k"][:, :, L0:])), kv_dev(np.ascontiguousarray(x["v"][:, :, L0:])),
+                 dev_tensor(np.full(B, L0, np.int32)))
+    refs = []
+    for b in range(B):
+        r = orc.RecentWindowCache(KVH, D, W, group)
+        r.append(x["k"][b, :, :L0], x["v"][b, :, :L0])
+        r.append(x["k"][b, :, L0:], x["v"][b, :, L0:])
+        refs.append(r)
+    qb, qv = wl.random_q(13, (B, H, n, D))
+    scale = 1.0 / np.sqrt(D)
+    ctx = [L0] * B
+    out = cache.chunk(bf16_dev(qb), dev_tensor(np.asarray(ctx, np.int32)), True, scale, L0)
+    torch.cuda.synchronize()
+    kh = np.stack([r.kv()[0] for r in refs])
+    vh = np.stack([r.kv()[1] for r in refs])
+    ref = orc.attention_chunk(qv, kh, vh, ctx, True, scale)
+    mag_ref = orc.attention_chunk(qv, kh, np.abs(vh), ctx, True, scale)
+    _assert_scaled(to_host_bits(out), ref, mag_ref, f"ring rows 1e-6/1e4 group={group}")

@@ -95,11 +95,11 @@ def test_sliding_window_calls_leave_workspace_zero(kvq, monkeypatch):
 
 
 def test_recent_chunk_then_decode_share_a_workspace(kvq):
-    """A recent-window cache: chunked prefill (MFMA chunk kernel, then the
-    ring kernel folding its partials) and then a fused decode step, both on
-    one workspace sized for the larger of the two."""
+    """A recent-window cache: chunked prefill (at head dim 96 through the
+    generic kernel, whose split partials use the workspace) and then a fused
+    decode step, both on one workspace sized for the larger of the two."""
     import torch
-    B, H, KVH, D, W = 2, 8, 2, 128, 16
+    B, H, KVH, D, W = 2, 8, 2, 96, 16
     L0, n = 200, 24
     T = L0 + n + 1
     log("workspace: recent chunk then decode")
