@@ -157,9 +157,11 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
                          int new_dtype, const RecentGeom& rc, int window) {
   const bool append = new_k != nullptr;
   const bool stream_kernel = stream_ok(c);
-  if (append && (!stream_kernel || is_block_mode(c))) {
-    // the generic kernel has no fused path, and a block-scale step may
-    // quantize a whole block: append the row first
+  // per-head block scales run the streaming kernel, whose fused step
+  // quantizes a whole block when its first row leaves the window
+  const bool fuse = append && stream_kernel;
+  if (append && !fuse) {
+    // the generic kernel has no fused path: append the row first
     kvq_status st = launch_append(c, new_k, new_v, new_dtype, 1, seq_lens, stream, true, rc);
     if (st != KVQ_OK) return st;
   }
@@ -202,8 +204,8 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
     return fail(KVQ_ERR_OUT_OF_RANGE, "kvq_attention_decode: grid too large");
   const int sm = kernel_scale_mode(c);
   const bool paged = c.layout == KVQ_LAYOUT_PAGED;
-  const bool fused = append && stream_kernel && !is_block_mode(c);
-  launch_decode_kernel(c.head_dim, stream_kernel, fused, plan.heads_per_wg, sm, paged, p, grid, stream);
+  p.block_head = fuse && c.scale_mode == KVQ_SCALE_BLOCK_HEAD ? 1 : 0;
+  launch_decode_kernel(c.head_dim, stream_kernel, fuse, plan.heads_per_wg, sm, paged, p, grid, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "kvq_attention_decode: launch failed: %s", hipGetErrorString(e));
   if (!stream_kernel) {

@@ -86,9 +86,9 @@ struct DecodeParams {
   int32_t chunk_n;
   int32_t chunk_causal;      // query i sees keys t <= ctx_lens[b] + i (else all ctx + n)
   const int32_t* ctx_lens;   // [B], tokens cached before the chunk
-  // chunk_ring_kernel: queries chunk_q0 .. chunk_n - 1 of batch_rows sequences
-  int32_t chunk_q0;
-  int32_t batch_rows;
+  // fused append on a hybrid cache with per-head block scales: the step
+  // whose leaving row starts a 16-row block quantizes the whole block
+  int32_t block_head;
 };
 
 namespace {
@@ -1247,7 +1247,9 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // with one it is the ring row at position L - 1 - W, which this step moves
   // out of the window.
   pn = L8 - 1;
-  owns_new = APPEND && pn >= t_begin && pn < t_end;
+  // (per-head block scales: only a row that starts a block has codes to
+  // make, its block's; the others were made with their block's first row)
+  owns_new = APPEND && pn >= t_begin && pn < t_end && (!p.block_head || pn % kBlockRows == 0);
 
   // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
 #pragma unroll
@@ -1278,7 +1280,53 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // make the wait for the queries cover the first block too)
   if constexpr (APPEND) {
     if (owns_new) {
-      if (wave < 2) {
+      // (a sliding window never has a recent window, so WIN kernels leave it out)
+      if (SM == kSmToken && !WIN && p.block_head && wave < 2) {
+        // Per-head block scales (the leaving row pn starts block pn / 16):
+        // one scale over the block's 16 rows, all of them ring rows (with a
+        // 15-row window the last is this step's new row, taken from the
+        // input as bf16), and each row's codes under it.  Two passes over
+        // the rows keep few registers live: the maximum, then the codes.
+        // The block lies in one page, so its rows follow row pn.
+        const int64_t rbase = (static_cast<int64_t>(b) * p.geom.kvh + kvh) * p.rcap;
+        const char* nsrc = static_cast<const char*>(wave == 0 ? p.new_k : p.new_v) +
+                           (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * (xbf16 ? 2 : 4);
+        auto block_row_values = [&](int i, float (&x)[kEpl]) {
+          const int pos = pn + i;
+          if (pos == L - 1) {
+            row_raw_values<kEpl>(load_row_raw<kEpl>(nsrc, lane, lane < D / kEpl, xbf16), xbf16, x);
+#pragma unroll
+            for (int e = 0; e < kEpl; ++e) x[e] = bf16_to_f32(f32_to_bf16_rne(x[e]));
+          } else {
+            const uint16_t* src = (wave == 0 ? p.rk : p.rv) + (rbase + pos % p.rcap) * D;
+            row_raw_values<kEpl>(load_row_raw<kEpl>(src, lane, lane < D / kEpl, true), true, x);
+          }
+        };
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kBlockRows; ++i) {
+          float x[kEpl];
+          block_row_values(i, x);
+#pragma unroll
+          for (int e = 0; e < kEpl; ++e) a = fmaxf(a, fabsf(x[e]));
+        }
+        a = wave_max(a);
+        const float sb = fmaxf(a, 1e-8f) / 127.0f;  // IEEE division (correctly rounded)
+        const int64_t row0 = row_of(pn);
+        uint8_t* codes = wave == 0 ? p.k_codes : p.v_codes;
+#pragma unroll 4
+        for (int i = 0; i < kBlockRows; ++i) {
+          float x[kEpl];
+          block_row_values(i, x);
+          const uint32_t packed = codes_with_scale<kEpl>(x, sb);
+          if (lane < D / kEpl) store_lane_codes<kEpl>(codes + (row0 + i) * D, lane, packed);
+          if (lane == 0) store_scale(wave == 0 ? p.k_scales : p.v_scales, row0 + i, sb, false);
+          if (i == 0 && lane < D / kEpl)
+            store_lane_codes<kEpl>(wave == 0 ? reinterpret_cast<uint8_t*>(sm_nk) : reinterpret_cast<uint8_t*>(sm_nv),
+                                   lane, packed);
+        }
+        if (lane == 0) sm_ns[wave][0] = sb;
+      } else if (wave < 2) {
         float xnew[kEpl];
         if (p.rwin > 0) {  // the ring row leaving the window (its own branch: this load is waited for at once)
           const uint16_t* src = (wave == 0 ? p.rk : p.rv) +

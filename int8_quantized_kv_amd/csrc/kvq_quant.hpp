@@ -58,6 +58,20 @@ __device__ __forceinline__ void load_row_values(const void* row, int lane, bool 
   }
 }
 
+// Codes of this lane's EPL values under a given scale s, packed little-endian.
+template <int EPL>
+__device__ __forceinline__ uint32_t codes_with_scale(const float (&x)[EPL], float s) {
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const float y = x[e] / s;  // IEEE division, not a reciprocal multiply
+    float q = roundf(y);       // half away from zero
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    packed |= static_cast<uint32_t>(static_cast<int>(q) + 128) << (8 * e);
+  }
+  return packed;
+}
+
 // Codes of this lane's EPL values, packed little-endian, and the scale of
 // the row (per-token) or of this lane's 32-element group (GROUP32).  Every
 // lane of the wave must call it; lanes without values pass zeros.
@@ -72,16 +86,8 @@ __device__ __forceinline__ uint32_t quantize_lane(const float (&x)[EPL], float& 
   for (int off = kSpan / 2; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, kWave));
   const float m = fmaxf(a, 1e-8f);
   const float s = m / 127.0f;  // IEEE division (correctly rounded)
-  uint32_t packed = 0;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const float y = x[e] / s;  // IEEE division, not a reciprocal multiply
-    float q = roundf(y);       // half away from zero
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    packed |= static_cast<uint32_t>(static_cast<int>(q) + 128) << (8 * e);
-  }
   scale = s;
-  return packed;
+  return codes_with_scale(x, s);
 }
 
 // Stores this lane's EPL codes of a row that starts at `codes`.

@@ -179,23 +179,30 @@ def test_decode_block(kvq, gran, D, H, KVH, W, lens, paged):
     assert_attention_close(to_host_bits(out), orc.attention_decode_recent(qv, refs, scale), "block decode")
 
 
-@pytest.mark.parametrize("gran,D,paged", [("head", 128, False), ("channel", 128, True), ("head", 64, True),
-                                          ("channel", 96, False)])
-def test_fused_step_block(kvq, gran, D, paged):
+@pytest.mark.parametrize("gran,D,paged,W", [("head", 128, False, 15), ("channel", 128, True, 15), ("head", 64, True, 15),
+                                            ("channel", 96, False, 15), ("head", 128, True, 20), ("head", 128, False, 33)])
+def test_fused_step_block(kvq, gran, D, paged, W):
     """kvq_append_decode_recent on block scales: the step that moves a
-    block's first row out of the window quantizes the whole block; state
-    and attention against the oracle, over steps that cross block edges."""
+    block's first row out of the window quantizes the whole block (per-head
+    scales: inside the fused decode kernel, which with W = 15 takes the
+    block's last row from the step's input); state and attention against the
+    oracle over steps that cross block edges, and the same state and output,
+    bit for bit, as kvq_append_recent followed by kvq_attention_decode_recent."""
     import torch
-    B, H, KVH, W = 3, 8, 2, 15
+    B, H, KVH = 3, 8, 2
     lens0 = [14, 16, 40]
-    steps = 20
+    steps = 20 + W
     T = max(lens0) + steps
-    log(f"block fused: {gran} D={D} paged={paged}")
-    rng = np.random.default_rng(D + paged + len(gran))
+    log(f"block fused: {gran} D={D} paged={paged} W={W}")
+    rng = np.random.default_rng(D + paged + len(gran) + W)
     x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "f32")
     refs = _oracle_states(x, lens0, W, gran)
-    cache, table = _new_cache(kvq, B, H, KVH, D, gran, W, W + 1, paged, T, rng, [T] * B)
-    _write_state(cache, table, refs, gran)
+    caches = []
+    for _ in range(2):
+        c, table = _new_cache(kvq, B, H, KVH, D, gran, W, W + 1, paged, T, np.random.default_rng(9), [T] * B)
+        _write_state(c, table, refs, gran)
+        caches.append(c)
+    cache, two = caches
     lens = np.asarray(lens0, np.int32)
     scale = 1.0 / np.sqrt(D)
     for s in range(steps):
@@ -207,8 +214,13 @@ def test_fused_step_block(kvq, gran, D, paged):
             refs[b].append(k_new[b], v_new[b])
         qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, D))
         out = cache.append_decode(kv_dev(k_new), kv_dev(v_new), bf16_dev(qb), dev_tensor(lens), scale, T)
+        two.append(kv_dev(k_new), kv_dev(v_new), dev_tensor(idx.astype(np.int32)))
+        out2 = two.decode(bf16_dev(qb), dev_tensor(lens), scale, T)
         torch.cuda.synchronize()
         _check_state(cache, table, refs, gran, f"step {s}")
+        for name in ("k_codes", "v_codes", "k_scales", "v_scales", "k_recent", "v_recent"):
+            assert torch.equal(getattr(cache, name), getattr(two, name)), f"step {s}: {name}"
+        assert np.array_equal(to_host_bits(out), to_host_bits(out2)), f"step {s}: fused and two-step outputs"
         assert_attention_close(to_host_bits(out), orc.attention_decode_recent(qv, refs, scale), f"step {s}")
 
 
