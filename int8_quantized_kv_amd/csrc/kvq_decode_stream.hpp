@@ -112,6 +112,8 @@ constexpr float kLazy = 8.0f;      // log2 headroom before a rescale
 constexpr int kWeightShift = 7;    // weights carry 2^7 so they fill f16 range
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
 
 __device__ __forceinline__ void bf16x8_to_f32(uint4 v, float* x) {
@@ -727,6 +729,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   constexpr bool E5 = SM == kSmFp8E5M2;
   constexpr int NG = G32 ? D / 32 : 1;       // scales per row
   constexpr int kSwz = 16 / LK;              // partial-score swizzle
+  // MQK: the scores on the matrix cores (v_mfma_f32_16x16x32_f16; head dims
+  // 64 and 128, all but group-32 scales): KST k-steps of 32 dims, NU
+  // 16-byte K pieces per lane and 16-token group
+  constexpr bool MQK = (D == 128 || D == 64) && !G32;
+  constexpr int KST = D / 32, NU = D / 64;
   static_assert(NPV % 2 == 0 && LV <= 16, "block shape");
   static_assert(HPW >= 1 && HPW <= 4, "at most four heads per workgroup");
 
@@ -760,6 +767,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
+  const int mtok = lane % 16, mgrp = lane / 16;      // MQK lanes: token of a 16-token group, quarter of the dims
   const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
 
   // With a sliding window the token range starts at the window's first key,
@@ -777,6 +785,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   bool owns_new = false;  // fused append: this workgroup's split holds it
 
   uint32_t qp[HPW][8];
+  half8_t qa[MQK ? KST : 1];  // MQK: the queries as the score product's A operand, per k-step
+  int kq_of[HPW];             // each head's prescale exponent
   float fold_row[HPW];  // per-token: 128 * 2^-24 * (sum of the scaled queries), wave-uniform
   float cst[HPW];       // scale_log2 * 2^24 * 2^-kq (wave-uniform)
 
@@ -888,6 +898,27 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   };
   auto load_k = [&](int bi, const int32_t (&pid)[kPages]) {
     const int s0 = t_begin + bi * kBlock;
+    if constexpr (MQK) {
+      // lane l: token 16g + l % 16 of each 16-token group g (one page), the
+      // D/4 bytes at (l / 16) D/4
+      const int moff = mgrp * (D / 4);
+      if (PAGED || s0 + kBlock <= t_end) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t r = PAGED ? page_row0(pid[g]) + mtok : seq_row0 + s0 + 16 * g + mtok;
+#pragma unroll
+          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(p.k_codes + r * D + moff + 16 * u);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t r = row_of(s0 + 16 * g + mtok);
+#pragma unroll
+          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(p.k_codes + r * D + moff + 16 * u);
+        }
+      }
+      return;
+    }
     if (PAGED ? kPassInPage : s0 + kBlock <= t_end) {
       if constexpr (PAGED) {
         int64_t r0[kPages];
@@ -970,10 +1001,19 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       const int s0 = t_begin + blk * kBlock;
       if (owns_new && pn >= s0 && pn < s0 + kBlock) {
         const int rel = pn - s0;
+        if constexpr (MQK) {
 #pragma unroll
-        for (int i = 0; i < NPK; ++i) {
-          if (i * TK + kslot == rel) {
-            kb[i] = sm_nk[ksub];
+          for (int g = 0; g < 4; ++g)
+            if (16 * g + mtok == rel) {
+#pragma unroll
+              for (int u = 0; u < NU; ++u) kb[g * NU + u] = sm_nk[mgrp * NU + u];
+            }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NPK; ++i) {
+            if (i * TK + kslot == rel) {
+              kb[i] = sm_nk[ksub];
+            }
           }
         }
 #pragma unroll
@@ -996,9 +1036,52 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         }
       }
     }
+    float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (MQK) {
+      // S = Q K^T per 16-token group: A = the queries (rows: heads, HPW of
+      // 16 used), B = K^T (lane l: token l % 16, k-slots 8(l/16) + e, which
+      // are dims (l/16) D/4 + 8s + e at k-step s, as for the queries).  The
+      // result's row 4(l/16) + i, column l % 16 puts heads 0..3 of the
+      // group's tokens in lanes 0..15.
+      float4_t sg[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KST; ++st) {
+          const uint4 w = kb[g * NU + st / 2];
+          const uint32_t w0 = (st & 1) ? w.z : w.x, w1 = (st & 1) ? w.w : w.y;
+          uint32_t c4[4];
+          if constexpr (FP8) {
+            c4[0] = fp8_pair_k<E5, false>(w0);
+            c4[1] = fp8_pair_k<E5, true>(w0);
+            c4[2] = fp8_pair_k<E5, false>(w1);
+            c4[3] = fp8_pair_k<E5, true>(w1);
+          } else {
+            c4[0] = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u);
+            c4[1] = __builtin_amdgcn_perm(0u, w0, 0x0C030C02u);
+            c4[2] = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
+            c4[3] = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
+          }
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], __builtin_bit_cast(half8_t, c4), c, 0, 0, 0);
+        }
+        sg[g] = c;
+      }
+      // group g's scores to lanes 16g .. 16g + 15: rows of 16 lanes swap
+      // pairwise (row 1 of the first operand with row 0 of the second),
+      // then halves
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        const uint32_t y01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[0][j]), __float_as_uint(sg[1][j]),
+                                                               false, false)[0];
+        const uint32_t y23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[2][j]), __float_as_uint(sg[3][j]),
+                                                               false, false)[0];
+        S[j] = __uint_as_float(__builtin_amdgcn_permlane32_swap(y01, y23, false, false)[0]);
+      }
+    }
     // QK: partial dots of this lane's 16 dims, all heads
 #pragma unroll
-    for (int i = 0; i < NPK; ++i) {
+    for (int i = 0; i < (MQK ? 0 : NPK); ++i) {
       const uint32_t kw[4] = {kb[i].x, kb[i].y, kb[i].z, kb[i].w};
       float P[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -1024,12 +1107,12 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       sm_part[wave][ksub * kBlock + ((i * TK + kslot) ^ (ksub * kSwz))] = make_float4(P[0], P[1], P[2], P[3]);
     }
     if constexpr (PREFETCH) load_k(blk + kStreamWaves, pq[1]);
-    wave_lds_sync();
+    if constexpr (!MQK) wave_lds_sync();
 
     // softmax: this lane owns token `lane` of the block
     const int t = t_begin + blk * kBlock + lane;
     const bool valid = t < t_end && t >= t_min;
-    float4 acc4 = sm_part[wave][lane ^ 0];
+    float4 acc4 = MQK ? make_float4(S[0], S[1], S[2], S[3]) : sm_part[wave][lane ^ 0];
     if constexpr (!G32 && !FP8) {
       // the row of the (clamped) token: page rows start even, so in the paged
       // layout its parity is the token's
@@ -1040,7 +1123,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     }
     if constexpr (G32) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
 #pragma unroll
-    for (int r = 1; r < LK; ++r) {
+    for (int r = 1; r < (MQK ? 1 : LK); ++r) {
       const float4 v = sm_part[wave][r * kBlock + (lane ^ (r * kSwz))];
       if constexpr (G32) {
         const float sg = s_k[r >> 1];  // k-lane r holds dims 16r..16r+15: group r / 2
@@ -1050,7 +1133,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         acc4.x += v.x; acc4.y += v.y; acc4.z += v.z; acc4.w += v.w;
       }
     }
-    const float S[4] = {acc4.x, acc4.y, acc4.z, acc4.w};
+    S[0] = acc4.x; S[1] = acc4.y; S[2] = acc4.z; S[3] = acc4.w;
     // V scale of the token: per-token, or the largest of its groups (group-32)
     float sv_top = FP8 ? 1.0f : s_v[0];
 #pragma unroll
@@ -1193,6 +1276,16 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     qraw[j][0] = qptr[0];
     qraw[j][1] = qptr[1];
   }
+  // MQK: this lane's operand rows of the score product: head l % 16 (lanes
+  // past the HPW heads read head HPW - 1 and later hold zeros), dims
+  // (l / 16) D/4 + 8s .. + 7 for k-step s
+  uint4 qmr[MQK ? KST : 1];
+  if constexpr (MQK) {
+    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + min(mtok, HPW - 1)) * D +
+                                                       mgrp * (D / 4));
+#pragma unroll
+    for (int st = 0; st < KST; ++st) qmr[st] = qptr[st];
+  }
   auto first_loads = [&]() {
     if constexpr (PAGED) {
 #pragma unroll
@@ -1272,6 +1365,24 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     fold_row[j] = FP8 ? 0.0f : uniform(group_sum<LK>(qs * (128.0f * 0x1p-24f)));
     // INT8 per-token codes enter as c 2^-24; group-32 and FP8 as exact values
     cst[j] = uniform(ldexpf(p.scale_log2, (G32 || FP8 ? 0 : 24) - kq));
+    kq_of[j] = kq;
+  }
+  if constexpr (MQK) {  // the same prescale, in the score product's lane layout
+    int kqm = kq_of[0];
+#pragma unroll
+    for (int j = 1; j < HPW; ++j) kqm = mtok == j ? kq_of[j] : kqm;
+#pragma unroll
+    for (int st = 0; st < KST; ++st) {
+      float qf[8];
+      bf16x8_to_f32(qmr[st], qf);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t b0 = f16_bits(ldexpf(qf[2 * e], kqm)), b1 = f16_bits(ldexpf(qf[2 * e + 1], kqm));
+        w[e] = mtok < HPW ? b0 | (b1 << 16) : 0u;
+      }
+      qa[st] = __builtin_bit_cast(half8_t, w);
+    }
   }
 
   // a sliding window's first block, whose range needed the length
