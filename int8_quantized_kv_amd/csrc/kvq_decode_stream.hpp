@@ -730,9 +730,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   constexpr int NG = G32 ? D / 32 : 1;       // scales per row
   constexpr int kSwz = 16 / LK;              // partial-score swizzle
   // MQK: the scores on the matrix cores (v_mfma_f32_16x16x32_f16; head dims
-  // 64 and 128, all but group-32 scales): KST k-steps of 32 dims, NU
-  // 16-byte K pieces per lane and 16-token group
-  constexpr bool MQK = (D == 128 || D == 64) && !G32;
+  // 64 and 128): KST k-steps of 32 dims, NU 16-byte K pieces per lane and
+  // 16-token group.  A lane's k-slots 8(l/16) + e of k-step s are dims
+  // (l/16) D/4 + 8s + e (16 contiguous bytes per load); with group-32
+  // scales they are dims 32s + 8(l/16) + e, so that k-step s is group s.
+  constexpr bool MQK = D == 128 || D == 64;
   constexpr int KST = D / 32, NU = D / 64;
   static_assert(NPV % 2 == 0 && LV <= 16, "block shape");
   static_assert(HPW >= 1 && HPW <= 4, "at most four heads per workgroup");
@@ -767,7 +769,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int ksub = lane % LK, kslot = lane / LK;     // K lanes: 16 dims of token slot
-  const int mtok = lane % 16, mgrp = lane / 16;      // MQK lanes: token of a 16-token group, quarter of the dims
+  const int mtok = lane % 16, mgrp = lane / 16;      // MQK lanes: token of a 16-token group, a quarter of the k-slots
   const int vsub = lane % LV, vslot = lane / LV;     // V lanes: 8 dims of token slot
 
   // With a sliding window the token range starts at the window's first key,
@@ -900,22 +902,27 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     const int s0 = t_begin + bi * kBlock;
     if constexpr (MQK) {
       // lane l: token 16g + l % 16 of each 16-token group g (one page), the
-      // D/4 bytes at (l / 16) D/4
-      const int moff = mgrp * (D / 4);
+      // D/4 bytes at (l / 16) D/4, or (group-32) 8 bytes of each group
+      auto piece = [&](int64_t r, int g) {
+        const uint8_t* row = p.k_codes + r * D;
+        if constexpr (G32) {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const uint2 a = *reinterpret_cast<const uint2*>(row + 64 * u + 8 * mgrp);
+            const uint2 c = *reinterpret_cast<const uint2*>(row + 64 * u + 32 + 8 * mgrp);
+            kb[g * NU + u] = make_uint4(a.x, a.y, c.x, c.y);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(row + mgrp * (D / 4) + 16 * u);
+        }
+      };
       if (PAGED || s0 + kBlock <= t_end) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t r = PAGED ? page_row0(pid[g]) + mtok : seq_row0 + s0 + 16 * g + mtok;
-#pragma unroll
-          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(p.k_codes + r * D + moff + 16 * u);
-        }
+        for (int g = 0; g < 4; ++g) piece(PAGED ? page_row0(pid[g]) + mtok : seq_row0 + s0 + 16 * g + mtok, g);
       } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t r = row_of(s0 + 16 * g + mtok);
-#pragma unroll
-          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(p.k_codes + r * D + moff + 16 * u);
-        }
+        for (int g = 0; g < 4; ++g) piece(row_of(s0 + 16 * g + mtok), g);
       }
       return;
     }
@@ -1002,11 +1009,19 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       if (owns_new && pn >= s0 && pn < s0 + kBlock) {
         const int rel = pn - s0;
         if constexpr (MQK) {
+          const uint2* nk2 = reinterpret_cast<const uint2*>(sm_nk);
 #pragma unroll
           for (int g = 0; g < 4; ++g)
             if (16 * g + mtok == rel) {
 #pragma unroll
-              for (int u = 0; u < NU; ++u) kb[g * NU + u] = sm_nk[mgrp * NU + u];
+              for (int u = 0; u < NU; ++u) {
+                if constexpr (G32) {
+                  const uint2 a = nk2[8 * u + mgrp], c = nk2[8 * u + 4 + mgrp];
+                  kb[g * NU + u] = make_uint4(a.x, a.y, c.x, c.y);
+                } else {
+                  kb[g * NU + u] = sm_nk[mgrp * NU + u];
+                }
+              }
             }
         } else {
 #pragma unroll
@@ -1043,40 +1058,65 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       // are dims (l/16) D/4 + 8s + e at k-step s, as for the queries).  The
       // result's row 4(l/16) + i, column l % 16 puts heads 0..3 of the
       // group's tokens in lanes 0..15.
-      float4_t sg[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int st = 0; st < KST; ++st) {
-          const uint4 w = kb[g * NU + st / 2];
-          const uint32_t w0 = (st & 1) ? w.z : w.x, w1 = (st & 1) ? w.w : w.y;
-          uint32_t c4[4];
-          if constexpr (FP8) {
-            c4[0] = fp8_pair_k<E5, false>(w0);
-            c4[1] = fp8_pair_k<E5, true>(w0);
-            c4[2] = fp8_pair_k<E5, false>(w1);
-            c4[3] = fp8_pair_k<E5, true>(w1);
-          } else {
-            c4[0] = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u);
-            c4[1] = __builtin_amdgcn_perm(0u, w0, 0x0C030C02u);
-            c4[2] = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
-            c4[3] = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
-          }
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], __builtin_bit_cast(half8_t, c4), c, 0, 0, 0);
+      auto k_operand = [&](int g, int st) {
+        const uint4 w = kb[g * NU + st / 2];
+        const uint32_t w0 = (st & 1) ? w.z : w.x, w1 = (st & 1) ? w.w : w.y;
+        uint32_t c4[4];
+        if constexpr (G32) {  // exact f16 c - 128: the group scale multiplies later
+          c4[0] = exact_pair(__builtin_amdgcn_perm(0x64646464u, w0, 0x04010400u));
+          c4[1] = exact_pair(__builtin_amdgcn_perm(0x64646464u, w0, 0x04030402u));
+          c4[2] = exact_pair(__builtin_amdgcn_perm(0x64646464u, w1, 0x04010400u));
+          c4[3] = exact_pair(__builtin_amdgcn_perm(0x64646464u, w1, 0x04030402u));
+        } else if constexpr (FP8) {
+          c4[0] = fp8_pair_k<E5, false>(w0);
+          c4[1] = fp8_pair_k<E5, true>(w0);
+          c4[2] = fp8_pair_k<E5, false>(w1);
+          c4[3] = fp8_pair_k<E5, true>(w1);
+        } else {
+          c4[0] = __builtin_amdgcn_perm(0u, w0, 0x0C010C00u);
+          c4[1] = __builtin_amdgcn_perm(0u, w0, 0x0C030C02u);
+          c4[2] = __builtin_amdgcn_perm(0u, w1, 0x0C010C00u);
+          c4[3] = __builtin_amdgcn_perm(0u, w1, 0x0C030C02u);
         }
-        sg[g] = c;
-      }
+        return __builtin_bit_cast(half8_t, c4);
+      };
       // group g's scores to lanes 16g .. 16g + 15: rows of 16 lanes swap
       // pairwise (row 1 of the first operand with row 0 of the second),
       // then halves
-#pragma unroll
-      for (int j = 0; j < HPW; ++j) {
+      auto gather = [&](const float4_t (&sg)[4], int j) {
         const uint32_t y01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[0][j]), __float_as_uint(sg[1][j]),
                                                                false, false)[0];
         const uint32_t y23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[2][j]), __float_as_uint(sg[3][j]),
                                                                false, false)[0];
-        S[j] = __uint_as_float(__builtin_amdgcn_permlane32_swap(y01, y23, false, false)[0]);
+        return __uint_as_float(__builtin_amdgcn_permlane32_swap(y01, y23, false, false)[0]);
+      };
+      if constexpr (G32) {
+        // one k-step per group: its partial scores, gathered, times the
+        // token's group scale
+#pragma unroll
+        for (int st = 0; st < KST; ++st) {
+          float4_t sg[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            sg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], k_operand(g, st), float4_t{0.0f, 0.0f, 0.0f, 0.0f},
+                                                            0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < HPW; ++j) S[j] = fmaf(gather(sg, j), s_k[st], S[j]);
+        }
+      }
+      float4_t sg[4];
+#pragma unroll
+      for (int g = 0; g < (G32 ? 0 : 4); ++g) {
+        float4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < KST; ++st) {
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], k_operand(g, st), c, 0, 0, 0);
+        }
+        sg[g] = c;
+      }
+      if constexpr (!G32) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) S[j] = gather(sg, j);
       }
     }
     // QK: partial dots of this lane's 16 dims, all heads
@@ -1121,7 +1161,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       s_k[0] = scale_value(s_kw, sel);
       s_v[0] = scale_value(s_vw, sel);
     }
-    if constexpr (G32) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
+    if constexpr (G32 && !MQK) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
 #pragma unroll
     for (int r = 1; r < (MQK ? 1 : LK); ++r) {
       const float4 v = sm_part[wave][r * kBlock + (lane ^ (r * kSwz))];
@@ -1281,10 +1321,10 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // (l / 16) D/4 + 8s .. + 7 for k-step s
   uint4 qmr[MQK ? KST : 1];
   if constexpr (MQK) {
-    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + min(mtok, HPW - 1)) * D +
-                                                       mgrp * (D / 4));
+    const uint16_t* qrow = p.q + (static_cast<int64_t>(b) * H + h0 + min(mtok, HPW - 1)) * D;
 #pragma unroll
-    for (int st = 0; st < KST; ++st) qmr[st] = qptr[st];
+    for (int st = 0; st < KST; ++st)
+      qmr[st] = *reinterpret_cast<const uint4*>(qrow + (G32 ? 32 * st + 8 * mgrp : mgrp * (D / 4) + 8 * st));
   }
   auto first_loads = [&]() {
     if constexpr (PAGED) {
