@@ -16,7 +16,7 @@ figure is TFLOP/s over the visible keys only.
 The other workloads (recent_window, sliding_decode, sliding_chunk,
 bf16_scales, fp8_e4m3, fp8_chunk, chunk_group32, recent_chunk, q8_group32,
 paged_decode, tiny_decode, recent_block_head, recent_block_channel,
-chunk_d256) are the same steps on the cache variants their names give;
+chunk_d256, decode_d256) are the same steps on the cache variants their names give;
 stream_read times a plain read of the decode step's bytes; ``--help`` lists
 them.
 
@@ -792,7 +792,8 @@ def main():
                                                             "recent_window", "sliding_decode", "sliding_chunk",
                                                             "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32",
                                                             "recent_chunk", "tiny_decode", "stream_read",
-                                                            "recent_block_head", "recent_block_channel", "chunk_d256"])
+                                                            "recent_block_head", "recent_block_channel", "chunk_d256",
+                                                            "decode_d256"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")

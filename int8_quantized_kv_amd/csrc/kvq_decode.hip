@@ -48,15 +48,19 @@ int heads_per_wg(int gqa) {
   return 1;
 }
 
-bool use_stream(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128; }
+bool use_stream(int head_dim) { return head_dim == 32 || head_dim == 64 || head_dim == 128 || head_dim == 256; }
 
-// The streaming kernel takes head dims 32, 64 and 128 in every per-row scale
-// mode; per-channel block scales run on the generic kernel.
-bool stream_ok(const kvq_cache& c) { return use_stream(c.head_dim) && c.scale_mode != KVQ_SCALE_BLOCK_CHANNEL; }
+// The streaming kernel takes head dims 32, 64, 128 and 256 in every per-row
+// scale mode; per-channel block scales, and head dim 256 with a recent window
+// (whose ring pass holds two dims per lane), run on the generic kernel.
+bool stream_ok(const kvq_cache& c, const RecentGeom& rc) {
+  return use_stream(c.head_dim) && c.scale_mode != KVQ_SCALE_BLOCK_CHANNEL && !(c.head_dim == 256 && rc.window > 0);
+}
 
 int pass_tokens(int head_dim, bool stream_kernel) {
-  // tokens a workgroup consumes per step: whole 64-token wave blocks for the
-  // streaming kernel, one pass of all waves for the generic kernel
+  // tokens a workgroup consumes per step: one 64-token block per wave for
+  // the streaming kernel (two 32-token ones at head dim 256), one pass of
+  // all waves for the generic kernel
   return stream_kernel ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
 }
 
@@ -98,7 +102,7 @@ bool decode_supported(int head_dim) { return head_dim % 32 == 0 && head_dim >= 3
 
 DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc, int window, bool generic) {
   DecodePlan pl;
-  const bool stream_kernel = !generic && stream_ok(c);
+  const bool stream_kernel = !generic && stream_ok(c, rc);
   // a sliding window bounds each sequence's range: the window rounded out to
   // whole blocks
   if (window > 0 && max_seq_len > window + kBlock - 1) max_seq_len = window + kBlock - 1;
@@ -156,7 +160,7 @@ kvq_status launch_decode(const kvq_cache& c, const DecodePlan& plan, const uint1
                          int max_seq_len, hipStream_t stream, const void* new_k, const void* new_v,
                          int new_dtype, const RecentGeom& rc, int window) {
   const bool append = new_k != nullptr;
-  const bool stream_kernel = stream_ok(c);
+  const bool stream_kernel = stream_ok(c, rc);
   // per-head block scales run the streaming kernel, whose fused step
   // quantizes a whole block when its first row leaves the window
   const bool fuse = append && stream_kernel;

@@ -12,30 +12,32 @@
 //     S_t = scale * sum_d q_d (cK_td - 128) sK_t(d)
 //     o   = sum_t softmax(S)_t (cV_td - 128) sV_t(d)
 //
-// gfx950 design of the streaming kernel (head_dim 32, 64, 128):
-//   * one workgroup = (sequence, KV head, token split); its 4 waves take
-//     64-token blocks in turn.  A token row of D code bytes is read by D/16
-//     lanes with one 16-byte load each, and every loaded byte serves all the
-//     query heads of the GQA group (one K/V read per group).
+// gfx950 design of the streaming kernel (head_dim 32, 64, 128, 256):
+//   * one workgroup = (sequence, KV head (and a share of its query heads),
+//     token split); its 8 waves take blocks of 64 tokens (32 at head dim
+//     256: 16 KB of K and V either way) in turn.  Every loaded byte serves
+//     all the query heads of the workgroup (one K/V read per GQA group).
 //   * codes are never widened to fp32: v_perm_b32 places two code bytes into
-//     the low bytes of two f16 halves (the f16 values c * 2^-24, exact) and
-//     v_dot2_f32_f16 multiplies them with f16 queries (QK: pairs along D) or
-//     f16 softmax weights (PV: pairs of tokens), accumulating in fp32.  The
-//     -128 offset is folded out: sum x (c - 128) = sum x c - 128 sum x.
-//     Queries are scaled by a power of two into [2^14, 2^15) first, which is
-//     exact for bf16 inputs.
-//   * the softmax of each token is computed once, by one lane, from partial
-//     dot products exchanged through LDS; per-token V scales are folded into
-//     the exponent (w = 2^(S + log2 sV - m)), so the weights stay in f16
-//     range; the running maximum is wave-uniform and only rescales the
-//     accumulators when a score exceeds it by more than 2^8.
+//     the low bytes of two f16 halves (the f16 values c * 2^-24, exact).  The
+//     scores are matrix-core products S = Q K^T of 16-token groups
+//     (v_mfma_f32_16x16x32_f16; head dim 32: v_dot2_f32_f16 partial dots
+//     summed through LDS), and PV multiplies f16 softmax weights with pairs
+//     of tokens' codes in v_dot2_f32_f16, accumulating in fp32.  The -128
+//     offset is folded out: sum x (c - 128) = sum x c - 128 sum x.  Queries
+//     are scaled by a power of two into [2^14, 2^15) first, which is exact
+//     for bf16 inputs.
+//   * the softmax of each token is computed once, by one lane; per-token V
+//     scales are folded into the exponent (w = 2^(S + log2 sV - m)), so the
+//     weights stay in f16 range; the running maximum is wave-uniform and
+//     only rescales the accumulators when a score exceeds it by more than
+//     2^8.
 //   * the next block's K (and V) rows are loaded while the current block is
 //     computed;
-//   * each split leaves (m, l, o) partials; the last workgroup of a (sequence,
-//     KV head) to finish merges them with the log-sum-exp identity and writes
-//     bf16 (a counter in the workspace elects it and is reset for the next
-//     call).
-// head_dim 256 uses the generic kernel of kvq_decode.hip (fp32 FMAs, separate merge).
+//   * each split leaves (m, l, o) partials; the split that draws the last
+//     ticket of its (sequence, head group) merges them with the log-sum-exp
+//     identity and writes bf16.
+// Head dim 256 with a recent window, per-channel block scales and head dims
+// 96-224 use the generic kernel of kvq_decode.hip (fp32 FMAs, separate merge).
 #pragma once
 
 #include "kvq_internal.hpp"
@@ -707,7 +709,7 @@ __device__ void ring_into_wave(const DecodeParams& p, int b, int kvh, int h0, in
 }
 
 // ---------------------------------------------------------------------------
-// Streaming kernel (head_dim 32, 64, 128).
+// Streaming kernel (head_dim 32, 64, 128, 256).
 // ---------------------------------------------------------------------------
 // SM: scale mode (kSmToken fp32 per token, kSmGroup32, kSmTokenBf16 bf16 per
 // token), a template argument so each mode pays only for its own decoding
@@ -716,11 +718,13 @@ __device__ void ring_into_wave(const DecodeParams& p, int b, int kvh, int h0, in
 // the length (the compiler's wait counts after such a join are conservative)
 template <int D, int HPW, int SM, bool PAGED, bool APPEND, bool WIN>
 __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(DecodeParams p) {
+  // BLK: tokens per wave block, 16 KB of K and V (32 at head dim 256)
+  constexpr int BLK = D == 256 ? 32 : kBlock;
   // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
   // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
   // so a lane accumulates 8 output dims per head.
-  constexpr int LK = D / 16, TK = kWave / LK, NPK = kBlock / TK;
-  constexpr int LV = D / 8, TV = kWave / LV, NPV = kBlock / TV;
+  constexpr int LK = D / 16, TK = kWave / LK, NPK = BLK / TK;
+  constexpr int LV = D / 8, TV = kWave / LV, NPV = BLK / TV;
   constexpr int NPAIR = NPV / 2;             // token pairs per lane per block
   constexpr bool G32 = SM == kSmGroup32;
   constexpr bool SBF = SM == kSmTokenBf16;
@@ -734,14 +738,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // 16-token group.  A lane's k-slots 8(l/16) + e of k-step s are dims
   // (l/16) D/4 + 8s + e (16 contiguous bytes per load); with group-32
   // scales they are dims 32s + 8(l/16) + e, so that k-step s is group s.
-  constexpr bool MQK = D == 128 || D == 64;
-  constexpr int KST = D / 32, NU = D / 64;
-  static_assert(NPV % 2 == 0 && LV <= 16, "block shape");
+  constexpr bool MQK = D == 128 || D == 64 || D == 256;
+  constexpr int KST = D / 32, NU = D / 64, NGRP = BLK / 16;  // NGRP: 16-token groups per block
+  static_assert(NPV % 2 == 0 && LV <= 32, "block shape");
   static_assert(HPW >= 1 && HPW <= 4, "at most four heads per workgroup");
 
   // partial scores, [k-lane][token ^ (k-lane * 16/LK)] x 4 heads: the writes of
   // one pass and the reads of one k-lane both touch distinct banks
-  __shared__ float4 sm_part[kStreamWaves][kBlock * LK];
+  __shared__ float4 sm_part[kStreamWaves][BLK * LK];
   __shared__ uint4 sm_w[kStreamWaves][NPAIR * TV * NG];    // f16 weight pairs [pair][slot][group] x 4 heads
   __shared__ float sm_fo[kStreamWaves][HPW][D];            // per-wave outputs
   __shared__ float sm_fml[kStreamWaves][HPW][2];           // per-wave (m, l)
@@ -807,7 +811,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   uint4 kb[NPK];
   uint2 vb[NPV];
   constexpr int kPidAhead = 4;  // paged: blocks of page ids held ahead (covers a 2048-token split)
-  int32_t pq[kPidAhead][kBlock / kPageSize] = {};
+  int32_t pq[kPidAhead][BLK / kPageSize] = {};
   float s_k[NG];        // K scales of this lane's softmax token (per token or per group)
   float s_v[NG];        // V scales of this lane's softmax token
   // per-token: the scale words as loaded (fp32, or the aligned word holding a
@@ -832,12 +836,12 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // through their -inf score and zero weight.  No load sits under a per-lane
   // branch.
   constexpr bool kPassInPage = TK <= kPageSize && TV <= kPageSize;
-  constexpr int kPages = kBlock / kPageSize;          // pages per block
+  constexpr int kPages = BLK / kPageSize;          // pages per block
   typedef const int32_t __attribute__((address_space(4))) const_i32;
   const const_i32* bt_s = (const const_i32*)(p.geom.block_table);  // scalar loads
   // page ids of block bi (uniform; ids past the table read as 0)
   auto fetch_pids = [&](int bi, int32_t (&pid)[kPages]) {
-    const int blk0 = (t_begin + bi * kBlock) >> 4;
+    const int blk0 = (t_begin + bi * BLK) >> 4;
 #pragma unroll
     for (int pg = 0; pg < kPages; ++pg)
       pid[pg] = blk0 + pg < p.geom.max_blocks ? bt_s[static_cast<int64_t>(b) * p.geom.max_blocks + blk0 + pg] : 0;
@@ -895,11 +899,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   // scales of the softmax token (token `lane`) of block bi
   // (scales of rows past the end could be any bits, so their rows are clamped)
   auto load_block_scales = [&](int bi, const int32_t (&pid)[kPages]) {
-    const int s0 = t_begin + bi * kBlock;
+    const int s0 = t_begin + bi * BLK;
     load_scales(block_row(s0, s0 + lane, pid));
   };
   auto load_k = [&](int bi, const int32_t (&pid)[kPages]) {
-    const int s0 = t_begin + bi * kBlock;
+    const int s0 = t_begin + bi * BLK;
     if constexpr (MQK) {
       // lane l: token 16g + l % 16 of each 16-token group g (one page), the
       // D/4 bytes at (l / 16) D/4, or (group-32) 8 bytes of each group
@@ -917,16 +921,16 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
           for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(row + mgrp * (D / 4) + 16 * u);
         }
       };
-      if (PAGED || s0 + kBlock <= t_end) {
+      if (PAGED || s0 + BLK <= t_end) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) piece(PAGED ? page_row0(pid[g]) + mtok : seq_row0 + s0 + 16 * g + mtok, g);
+        for (int g = 0; g < NGRP; ++g) piece(PAGED ? page_row0(pid[g]) + mtok : seq_row0 + s0 + 16 * g + mtok, g);
       } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) piece(row_of(s0 + 16 * g + mtok), g);
+        for (int g = 0; g < NGRP; ++g) piece(row_of(s0 + 16 * g + mtok), g);
       }
       return;
     }
-    if (PAGED ? kPassInPage : s0 + kBlock <= t_end) {
+    if (PAGED ? kPassInPage : s0 + BLK <= t_end) {
       if constexpr (PAGED) {
         int64_t r0[kPages];
 #pragma unroll
@@ -954,8 +958,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     }
   };
   auto load_v = [&](int bi, const int32_t (&pid)[kPages]) {
-    const int s0 = t_begin + bi * kBlock;
-    if (PAGED ? kPassInPage : s0 + kBlock <= t_end) {
+    const int s0 = t_begin + bi * BLK;
+    if (PAGED ? kPassInPage : s0 + BLK <= t_end) {
       if constexpr (PAGED) {
         int64_t r0[kPages];
 #pragma unroll
@@ -1005,13 +1009,13 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     if constexpr (APPEND) {
       // the block holding the freshly appended token uses the codes just
       // computed (its loads may have been issued before they were stored)
-      const int s0 = t_begin + blk * kBlock;
-      if (owns_new && pn >= s0 && pn < s0 + kBlock) {
+      const int s0 = t_begin + blk * BLK;
+      if (owns_new && pn >= s0 && pn < s0 + BLK) {
         const int rel = pn - s0;
         if constexpr (MQK) {
           const uint2* nk2 = reinterpret_cast<const uint2*>(sm_nk);
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+          for (int g = 0; g < NGRP; ++g)
             if (16 * g + mtok == rel) {
 #pragma unroll
               for (int u = 0; u < NU; ++u) {
@@ -1082,31 +1086,35 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       };
       // group g's scores to lanes 16g .. 16g + 15: rows of 16 lanes swap
       // pairwise (row 1 of the first operand with row 0 of the second),
-      // then halves
-      auto gather = [&](const float4_t (&sg)[4], int j) {
+      // then halves (two groups: the first swap alone)
+      auto gather = [&](const float4_t (&sg)[NGRP], int j) {
         const uint32_t y01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[0][j]), __float_as_uint(sg[1][j]),
                                                                false, false)[0];
-        const uint32_t y23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[2][j]), __float_as_uint(sg[3][j]),
-                                                               false, false)[0];
-        return __uint_as_float(__builtin_amdgcn_permlane32_swap(y01, y23, false, false)[0]);
+        if constexpr (NGRP == 2) {
+          return __uint_as_float(y01);
+        } else {
+          const uint32_t y23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(sg[2][j]), __float_as_uint(sg[3][j]),
+                                                                 false, false)[0];
+          return __uint_as_float(__builtin_amdgcn_permlane32_swap(y01, y23, false, false)[0]);
+        }
       };
       if constexpr (G32) {
         // one k-step per group: its partial scores, gathered, times the
         // token's group scale
 #pragma unroll
         for (int st = 0; st < KST; ++st) {
-          float4_t sg[4];
+          float4_t sg[NGRP];
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
+          for (int g = 0; g < NGRP; ++g)
             sg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], k_operand(g, st), float4_t{0.0f, 0.0f, 0.0f, 0.0f},
                                                             0, 0, 0);
 #pragma unroll
           for (int j = 0; j < HPW; ++j) S[j] = fmaf(gather(sg, j), s_k[st], S[j]);
         }
       }
-      float4_t sg[4];
+      float4_t sg[NGRP];
 #pragma unroll
-      for (int g = 0; g < (G32 ? 0 : 4); ++g) {
+      for (int g = 0; g < (G32 ? 0 : NGRP); ++g) {
         float4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int st = 0; st < KST; ++st) {
@@ -1144,14 +1152,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
           P[j] = dot2(qp[j][2 * w4 + 1], c23, P[j]);
         }
       }
-      sm_part[wave][ksub * kBlock + ((i * TK + kslot) ^ (ksub * kSwz))] = make_float4(P[0], P[1], P[2], P[3]);
+      sm_part[wave][ksub * BLK + ((i * TK + kslot) ^ (ksub * kSwz))] = make_float4(P[0], P[1], P[2], P[3]);
     }
     if constexpr (PREFETCH) load_k(blk + kStreamWaves, pq[1]);
     if constexpr (!MQK) wave_lds_sync();
 
     // softmax: this lane owns token `lane` of the block
-    const int t = t_begin + blk * kBlock + lane;
-    const bool valid = t < t_end && t >= t_min;
+    const int t = t_begin + blk * BLK + lane;
+    const bool valid = t < t_end && t >= t_min && lane < BLK;
     float4 acc4 = MQK ? make_float4(S[0], S[1], S[2], S[3]) : sm_part[wave][lane ^ 0];
     if constexpr (!G32 && !FP8) {
       // the row of the (clamped) token: page rows start even, so in the paged
@@ -1164,7 +1172,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     if constexpr (G32 && !MQK) acc4 = make_float4(acc4.x * s_k[0], acc4.y * s_k[0], acc4.z * s_k[0], acc4.w * s_k[0]);
 #pragma unroll
     for (int r = 1; r < (MQK ? 1 : LK); ++r) {
-      const float4 v = sm_part[wave][r * kBlock + (lane ^ (r * kSwz))];
+      const float4 v = sm_part[wave][r * BLK + (lane ^ (r * kSwz))];
       if constexpr (G32) {
         const float sg = s_k[r >> 1];  // k-lane r holds dims 16r..16r+15: group r / 2
         acc4.x = fmaf(v.x, sg, acc4.x); acc4.y = fmaf(v.y, sg, acc4.y);
@@ -1226,7 +1234,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
           const uint32_t wb = f16_bits(E[j] * r);
           word[j] = wb | (lane_up<TV>(wb) << 16);
         }
-        if (even_pass) sm_w[wave][wslot * NG + g] = make_uint4(word[0], word[1], word[2], word[3]);
+        if (even_pass && lane < BLK) sm_w[wave][wslot * NG + g] = make_uint4(word[0], word[1], word[2], word[3]);
       }
     } else {
       uint32_t word[4] = {0u, 0u, 0u, 0u};
@@ -1237,7 +1245,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         if constexpr (!FP8) ws[j][0] += f16_value(wb);
         word[j] = wb | (lane_up<TV>(wb) << 16);
       }
-      if (even_pass) sm_w[wave][wslot] = make_uint4(word[0], word[1], word[2], word[3]);
+      if (even_pass && lane < BLK) sm_w[wave][wslot] = make_uint4(word[0], word[1], word[2], word[3]);
     }
     // the scales of this block are used up: fetch the next block's
     if constexpr (PREFETCH) load_block_scales(blk + kStreamWaves, pq[1]);
@@ -1247,8 +1255,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     // be NaN or inf codes; its weight is 0, but 0 * NaN is not, so such rows
     // read as zero codes (blocks wholly inside [t_min, t_end) skip this)
     if constexpr (FP8) {
-      const int s0 = t_begin + blk * kBlock;
-      if (s0 < t_min || s0 + kBlock > t_end) {
+      const int s0 = t_begin + blk * BLK;
+      if (s0 < t_min || s0 + BLK > t_end) {
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
           const int tv = s0 + i * TV + vslot;
@@ -1284,7 +1292,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       for (int k = 0; k + 1 < kPidAhead; ++k)
 #pragma unroll
         for (int pg = 0; pg < kPages; ++pg) pq[k][pg] = pq[k + 1][pg];
-      if (t_begin + (blk + kPidAhead * kStreamWaves) * kBlock < t_end) fetch_pids(blk + kPidAhead * kStreamWaves, pq[kPidAhead - 1]);
+      if (t_begin + (blk + kPidAhead * kStreamWaves) * BLK < t_end) fetch_pids(blk + kPidAhead * kStreamWaves, pq[kPidAhead - 1]);
     }
   };
 
@@ -1330,7 +1338,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     if constexpr (PAGED) {
 #pragma unroll
       for (int k = 0; k < kPidAhead; ++k)
-        if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
+        if (t_begin + (blk + k * kStreamWaves) * BLK < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
     }
     // unconditional (rows clamped into the range, row 0 if it is empty), so
     // that every path issues the same loads and the waits after them stay exact
@@ -1344,7 +1352,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   int t_base = 0;  // first token of split 0
   if constexpr (WIN) {
     t_min = max(L - p.window, 0);
-    t_base = t_min & ~(kBlock - 1);
+    t_base = t_min & ~(BLK - 1);
     t_begin = t_base + split * p.split_len;
   }
   const int ns8 = split_count(L8 - t_base, p.split_len);
@@ -1360,7 +1368,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   }
   const int t_end_spec = t_end;
   t_end = split == ns8 - 1 ? L8 : min(L8, t_begin + p.split_len);  // the last split takes the remainder
-  const int nblk = t_end > t_begin ? (t_end - t_begin + kBlock - 1) / kBlock : 0;
+  const int nblk = t_end > t_begin ? (t_end - t_begin + BLK - 1) / BLK : 0;
   const int ns = ns8 > 0 ? ns8 : 1;
   if constexpr (WIN) {
     // (the first block's loads go out after the queries' prescale, below)
@@ -1370,7 +1378,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     if (t_end > t_end_spec) {
 #pragma unroll
       for (int k = 0; k < kPidAhead; ++k)
-        if (t_begin + (blk + k * kStreamWaves) * kBlock < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
+        if (t_begin + (blk + k * kStreamWaves) * BLK < t_end) fetch_pids(blk + k * kStreamWaves, pq[k]);
     }
   }
   // fused append: the workgroup whose split holds position L8 - 1 quantizes
@@ -1573,7 +1581,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 }
 
 // Launch of one scale mode's streaming-kernel instantiations (head_dim 32, 64,
-// 128; 1, 2 or 4 heads per workgroup; contiguous or paged; plain or fused
+// 128, 256; 1, 2 or 4 heads per workgroup; contiguous or paged; plain or fused
 // append).  Each mode's instantiations live in a translation unit of their
 // own (kvq_decode_<mode>.hip), so the library's kernels compile in parallel.
 template <int SM>
@@ -1603,6 +1611,7 @@ void launch_stream_impl(int head_dim, int hpw, bool paged, bool append, const De
   switch (head_dim) {
     case 32: by_hpw(std::integral_constant<int, 32>{}); break;
     case 64: by_hpw(std::integral_constant<int, 64>{}); break;
+    case 256: by_hpw(std::integral_constant<int, 256>{}); break;
     default: by_hpw(std::integral_constant<int, 128>{}); break;
   }
 }

@@ -68,7 +68,7 @@ DECODE_CASES = [
     (128, 32, 8, [1, 17, 300, 511, 512, 513, 2000], False),
     (128, 32, 8, [5, 600, 1025], True),
     (64, 8, 2, [3, 129, 257], False),
-    (256, 16, 4, [9, 300], False),   # generic kernel
+    (256, 16, 4, [9, 300], False),
 ]
 
 

@@ -62,7 +62,10 @@ CASES = [
     (128, 32, 8, 32, [7, 64, 700, 1025], False),
     (64, 8, 2, 0, [3, 129, 257, 1], False),
     (32, 4, 4, 0, [5, 90, 333], False),
-    (256, 16, 2, 32, [9, 200, 513], False),
+    (256, 16, 2, 32, [9, 200, 513], False),     # head dim 256: 32-token blocks
+    (256, 16, 4, 0, [1, 31, 32, 33, 600, 1025], False),
+    (256, 8, 4, 0, [17, 256, 257, 700], True),  # GQA 2: two heads per workgroup, paged
+    (256, 12, 4, 32, [64, 300], True),          # GQA 3: one head per workgroup
     (128, 24, 8, 0, [100, 517], False),        # GQA 3: one head per workgroup
     (128, 64, 8, 0, [77, 600], False),         # GQA 8: two workgroups per KV head
     (128, 16, 16, 0, [40, 41], False),         # MHA

@@ -99,8 +99,8 @@ DECODE_CASES = [
     ("e5m2", 128, 32, 8, [70, 333], True, 0),
     ("e4m3", 64, 8, 2, [3, 129, 257], False, 0),
     ("e5m2", 32, 4, 4, [16, 200], False, 0),
-    ("e4m3", 256, 16, 4, [9, 300], False, 0),    # generic kernel
-    ("e5m2", 256, 16, 4, [40, 77], True, 0),     # generic kernel, paged
+    ("e4m3", 256, 16, 4, [9, 300], False, 0),
+    ("e5m2", 256, 16, 4, [40, 77], True, 0),     # paged
     ("e4m3", 128, 32, 8, [50, 700, 2500], False, 100),
     ("e5m2", 128, 64, 8, [76, 600], True, 77),
 ]

@@ -19,7 +19,8 @@ CASES = [
     (64, 8, 2, 0, "f32", [1, 255, 256, 257], False),
     (64, 8, 2, 32, "bf16", [33, 700], True),
     (32, 4, 4, 0, "bf16", [3, 100], False),
-    (256, 16, 4, 0, "bf16", [9, 600], False),   # generic kernel: append launch + decode
+    (256, 16, 4, 0, "bf16", [9, 600, 33, 32], False),
+    (256, 8, 4, 32, "f32", [31, 1000], True),
     (128, 64, 8, 0, "bf16", [77, 1500], False),  # two workgroups per KV head
 ]
 

@@ -39,7 +39,7 @@ DECODE_CASES = [
     (128, 32, 8, 0, 1000, [5, 999, 1000, 1001, 3000], True),
     (64, 8, 2, 0, 5, [3, 5, 6, 90], False),
     (32, 4, 4, 0, 17, [16, 17, 18, 200], False),
-    (256, 16, 4, 0, 40, [20, 41, 300], False),   # generic kernel
+    (256, 16, 4, 0, 40, [20, 41, 300], False),
     (128, 64, 8, 0, 77, [76, 600], False),        # two workgroups per KV head
 ]
 

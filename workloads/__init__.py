@@ -130,10 +130,14 @@ RECENT_BLOCK_CHANNEL = Workload("recent_block_channel", 16, 32, 8, 128, 0, "cont
 # family, which combs-models' sliding-window cache serves): 16 query heads on
 # 8 KV heads, the chunked-prefill shape otherwise.
 CHUNK_D256 = Workload("chunk_d256", 4, 16, 8, 256, 0, "contiguous", "bf16", 8192, 512, seed=15)
+# Decode at head dim 256: the 8B-shaped decode's bytes per token (4 KV heads
+# of 256 dims), 16 query heads.
+DECODE_D256 = Workload("decode_d256", 16, 16, 4, 256, 0, "contiguous", "bf16", 4095, 1,
+                       layers=32, outliers=4, seed=16)
 
 ALL = {w.name: w for w in (TINY, DECODE_8B, Q8_GROUP32, PAGED, CHUNK, RECENT, SLIDING_DECODE, SLIDING_CHUNK,
                            BF16_SCALES, FP8_E4M3, FP8_CHUNK, CHUNK_G32, RECENT_CHUNK, RECENT_BLOCK_HEAD,
-                           RECENT_BLOCK_CHANNEL, CHUNK_D256)}
+                           RECENT_BLOCK_CHANNEL, CHUNK_D256, DECODE_D256)}
 
 
 # ----------------------------------------------------------------------------
