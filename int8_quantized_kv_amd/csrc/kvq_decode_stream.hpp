@@ -734,10 +734,11 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   constexpr int NG = G32 ? D / 32 : 1;       // scales per row
   constexpr int kSwz = 16 / LK;              // partial-score swizzle
   // MQK: the scores on the matrix cores (v_mfma_f32_16x16x32_f16; head dims
-  // 64 and 128): KST k-steps of 32 dims, NU 16-byte K pieces per lane and
-  // 16-token group.  A lane's k-slots 8(l/16) + e of k-step s are dims
-  // (l/16) D/4 + 8s + e (16 contiguous bytes per load); with group-32
-  // scales they are dims 32s + 8(l/16) + e, so that k-step s is group s.
+  // 64, 128 and 256): KST k-steps of 32 dims, NU 16-byte K pieces per lane
+  // and 16-token group.  A lane's k-slots 8(l/16) + e of k-step s are dims
+  // 64(s/2) + 16(l/16) + 8(s%2) + e, so that the four lane groups of one
+  // load read a row's 64 contiguous bytes; with group-32 scales they are
+  // dims 32s + 8(l/16) + e, so that k-step s is group s.
   constexpr bool MQK = D == 128 || D == 64 || D == 256;
   constexpr int KST = D / 32, NU = D / 64, NGRP = BLK / 16;  // NGRP: 16-token groups per block
   static_assert(NPV % 2 == 0 && LV <= 32, "block shape");
@@ -791,7 +792,16 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   bool owns_new = false;  // fused append: this workgroup's split holds it
 
   uint32_t qp[HPW][8];
-  half8_t qa[MQK ? KST : 1];  // MQK: the queries as the score product's A operand, per k-step
+  // MQK: the queries as the score product's A operand, per k-step; at head
+  // dim 256 (where registers are short) they wait in LDS, one copy per
+  // workgroup, read once per k-step and block
+  constexpr bool kQaLds = D == 256;
+  __shared__ half8_t sm_qa[kQaLds ? KST : 1][kQaLds ? kWave : 1];
+  half8_t qa[MQK && !kQaLds ? KST : 1];
+  auto q_operand = [&](int st) -> half8_t {
+    if constexpr (kQaLds) return sm_qa[st][lane];
+    else return qa[MQK ? st : 0];
+  };
   int kq_of[HPW];             // each head's prescale exponent
   float fold_row[HPW];  // per-token: 128 * 2^-24 * (sum of the scaled queries), wave-uniform
   float cst[HPW];       // scale_log2 * 2^24 * 2^-kq (wave-uniform)
@@ -905,8 +915,9 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   auto load_k = [&](int bi, const int32_t (&pid)[kPages]) {
     const int s0 = t_begin + bi * BLK;
     if constexpr (MQK) {
-      // lane l: token 16g + l % 16 of each 16-token group g (one page), the
-      // D/4 bytes at (l / 16) D/4, or (group-32) 8 bytes of each group
+      // lane l: token 16g + l % 16 of each 16-token group g (one page), 16
+      // bytes at 64u + 16(l / 16) for each u, or (group-32) 8 bytes of each
+      // group
       auto piece = [&](int64_t r, int g) {
         const uint8_t* row = p.k_codes + r * D;
         if constexpr (G32) {
@@ -918,7 +929,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(row + mgrp * (D / 4) + 16 * u);
+          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(row + 64 * u + 16 * mgrp);
         }
       };
       if (PAGED || s0 + BLK <= t_end) {
@@ -1023,7 +1034,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
                   const uint2 a = nk2[8 * u + mgrp], c = nk2[8 * u + 4 + mgrp];
                   kb[g * NU + u] = make_uint4(a.x, a.y, c.x, c.y);
                 } else {
-                  kb[g * NU + u] = sm_nk[mgrp * NU + u];
+                  kb[g * NU + u] = sm_nk[4 * u + mgrp];
                 }
               }
             }
@@ -1058,8 +1069,8 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     float S[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (MQK) {
       // S = Q K^T per 16-token group: A = the queries (rows: heads, HPW of
-      // 16 used), B = K^T (lane l: token l % 16, k-slots 8(l/16) + e, which
-      // are dims (l/16) D/4 + 8s + e at k-step s, as for the queries).  The
+      // 16 used), B = K^T (lane l: token l % 16, k-slots 8(l/16) + e, the
+      // same dims of k-step s as for the queries).  The
       // result's row 4(l/16) + i, column l % 16 puts heads 0..3 of the
       // group's tokens in lanes 0..15.
       auto k_operand = [&](int g, int st) {
@@ -1104,23 +1115,24 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 #pragma unroll
         for (int st = 0; st < KST; ++st) {
           float4_t sg[NGRP];
+          const half8_t a = q_operand(st);
 #pragma unroll
           for (int g = 0; g < NGRP; ++g)
-            sg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], k_operand(g, st), float4_t{0.0f, 0.0f, 0.0f, 0.0f},
+            sg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, k_operand(g, st), float4_t{0.0f, 0.0f, 0.0f, 0.0f},
                                                             0, 0, 0);
 #pragma unroll
           for (int j = 0; j < HPW; ++j) S[j] = fmaf(gather(sg, j), s_k[st], S[j]);
         }
       }
+      // (the groups' products interleave: NGRP independent accumulators)
       float4_t sg[NGRP];
 #pragma unroll
-      for (int g = 0; g < (G32 ? 0 : NGRP); ++g) {
-        float4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int g = 0; g < NGRP; ++g) sg[g] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int st = 0; st < KST; ++st) {
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[st], k_operand(g, st), c, 0, 0, 0);
-        }
-        sg[g] = c;
+      for (int st = 0; st < (G32 ? 0 : KST); ++st) {
+        const half8_t a = q_operand(st);
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) sg[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, k_operand(g, st), sg[g], 0, 0, 0);
       }
       if constexpr (!G32) {
 #pragma unroll
@@ -1325,14 +1337,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     qraw[j][1] = qptr[1];
   }
   // MQK: this lane's operand rows of the score product: head l % 16 (lanes
-  // past the HPW heads read head HPW - 1 and later hold zeros), dims
-  // (l / 16) D/4 + 8s .. + 7 for k-step s
+  // past the HPW heads read head HPW - 1 and later hold zeros), the 8 dims
+  // of its k-slots at each k-step s
   uint4 qmr[MQK ? KST : 1];
   if constexpr (MQK) {
     const uint16_t* qrow = p.q + (static_cast<int64_t>(b) * H + h0 + min(mtok, HPW - 1)) * D;
 #pragma unroll
     for (int st = 0; st < KST; ++st)
-      qmr[st] = *reinterpret_cast<const uint4*>(qrow + (G32 ? 32 * st + 8 * mgrp : mgrp * (D / 4) + 8 * st));
+      qmr[st] = *reinterpret_cast<const uint4*>(qrow + (G32 ? 32 * st + 8 * mgrp : 64 * (st / 2) + 16 * mgrp + 8 * (st % 2)));
   }
   auto first_loads = [&]() {
     if constexpr (PAGED) {
@@ -1429,8 +1441,13 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         const uint32_t b0 = f16_bits(ldexpf(qf[2 * e], kqm)), b1 = f16_bits(ldexpf(qf[2 * e + 1], kqm));
         w[e] = mtok < HPW ? b0 | (b1 << 16) : 0u;
       }
-      qa[st] = __builtin_bit_cast(half8_t, w);
+      if constexpr (kQaLds) {
+        if (wave == 0) sm_qa[st][lane] = __builtin_bit_cast(half8_t, w);
+      } else {
+        qa[st] = __builtin_bit_cast(half8_t, w);
+      }
     }
+    if constexpr (kQaLds) __syncthreads();
   }
 
   // a sliding window's first block, whose range needed the length
