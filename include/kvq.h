@@ -274,6 +274,11 @@ kvq_status kvq_dequant(const kvq_cache* cache, int32_t which, const int32_t* seq
  * ctx_lens[b] + i].  Workspace: kvq_workspace_size_window(cache, hint + n, n,
  * window) (0 for the current kernel).
  * Errors: those of the plain entry points, plus INVALID_ARG for window < 1.
+ * A sliding-window layer may keep only its window: give it a paged cache whose
+ * block table maps each sequence's logical pages j onto P physical pages in
+ * turn (j mod P), with 16 P >= window + n - 1 for appends of at most n rows.
+ * Rows then overwrite rows that no later query sees; the loads of keys below
+ * the window that the kernels still issue read finite, zero-weighted rows.
  */
 kvq_status kvq_attention_decode_window(const kvq_cache* cache, const uint16_t* q, const int32_t* seq_lens,
                                        float attn_scale, int32_t window, uint16_t* out, void* workspace,

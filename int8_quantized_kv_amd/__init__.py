@@ -7,6 +7,6 @@ library has not been built.
 """
 from . import kvq  # noqa: F401  (loads libkvq.so or raises ImportError)
 from .kvq import KvqError  # noqa: F401
-from .cache import Int8KVCache  # noqa: F401
+from .cache import Int8KVCache, rolling_block_table  # noqa: F401
 
-__all__ = ["kvq", "KvqError", "Int8KVCache"]
+__all__ = ["kvq", "KvqError", "Int8KVCache", "rolling_block_table"]

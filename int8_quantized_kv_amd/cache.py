@@ -11,6 +11,25 @@ import torch
 from . import kvq as _k
 
 
+def rolling_block_table(batch: int, max_len: int, window: int, chunk: int = 1):
+    """Block table of a sliding-window layer's rolling store: a paged cache
+    in which each sequence owns P = ceil((window + chunk - 1) / 16) pages and
+    its logical page j is its physical page j mod P.  The row of position p
+    then takes the slot of position p - 16 P, which no query of that append
+    or any later one sees, so the store holds 16 P rows per sequence however
+    long it grows (combs-models' sliding layers keep only the last w - 1).
+    ``chunk`` is the most rows one append adds before attention; the
+    attention calls take the window as usual.  Returns (int32 table
+    [batch, ceil(max_len / 16)] on the host, pages)."""
+    if window < 1 or chunk < 1 or max_len < 1:
+        raise ValueError("window, chunk and max_len must be at least 1")
+    per = -(-(window + chunk - 1) // 16)
+    blocks = -(-max_len // 16)
+    j = torch.arange(blocks, dtype=torch.int32)
+    table = torch.stack([b * per + j % per for b in range(batch)])
+    return table, batch * per
+
+
 class Int8KVCache:
     """One layer's cache: u8 codes + fp32 scales, contiguous or paged.
 

@@ -134,3 +134,54 @@ def test_chunk_window(kvq, D, H, KVH, L0s, n, window, paged):
     k_hat, v_hat = _oracle_hat(x, 0)
     ref = orc.attention_chunk(qv, k_hat, v_hat, L0s, True, scale, window=window)
     assert_attention_close(to_host_bits(out), ref, "chunk window")
+
+
+@pytest.mark.parametrize("group,fused,D", [(0, False, 128), (32, True, 128), (0, True, 64)])
+def test_rolling_store(kvq, group, fused, D):
+    """A sliding-window layer on a rolling store: a paged cache whose block
+    table maps each sequence's logical pages onto ceil((w + n - 1) / 16)
+    physical ones in turn, so rows overwrite rows that left the window.  The
+    sequences grow to 700 tokens through appends of 1 to n rows; after each
+    append the decode (fused for single rows when ``fused``) and, after a
+    chunk, chunked prefill over the chunk's queries match the oracle's
+    sliding attention over the whole history."""
+    import torch
+    B, H, KVH, w, n = 2, 8, 2, 100, 29
+    T = 700
+    log(f"rolling store: group={group} fused={fused} D={D}")
+    table, npages = kvq.rolling_block_table(B, T, w, n)
+    assert npages * 16 < T // 2
+    rng = np.random.default_rng(91 + group + D)
+    x = wl.random_kv(int(rng.integers(1 << 30)), (B, KVH, T, D), "bf16")
+    k_hat, v_hat = _oracle_hat(x, group)
+    cache = kvq.Int8KVCache(B, H, KVH, D, num_pages=npages, block_table=table.cuda(), group32=(group == 32), fill=0)
+    scale = 1.0 / np.sqrt(D)
+    ws = cache.workspace(T, 1, w)      # decode
+    wsc = cache.workspace(T, n, w)     # chunks of up to n rows
+    sizes = [1, 29, 7, 1, 1, 13, 29, 2, 1]
+    L, i, checked = 0, 0, 0
+    while L < T:
+        m = min(sizes[i % len(sizes)], T - L)
+        i += 1
+        rows = lambda a: np.ascontiguousarray(a[:, :, L:L + m])
+        start = dev_tensor(np.full(B, L, np.int32))
+        lens = dev_tensor(np.full(B, L + m, np.int32))
+        qb, qv = wl.random_q(int(rng.integers(1 << 30)), (B, H, D))
+        if m == 1 and fused:
+            out = cache.append_decode(kv_dev(rows(x["k_raw"])), kv_dev(rows(x["v_raw"])), bf16_dev(qb), lens, scale, T,
+                                      workspace=ws, window=w)
+        else:
+            cache.append(kv_dev(rows(x["k_raw"])), kv_dev(rows(x["v_raw"])), start)
+            out = cache.decode(bf16_dev(qb), lens, scale, T, workspace=ws, window=w)
+        torch.cuda.synchronize()
+        L += m
+        ref = orc.attention_decode(qv, k_hat, v_hat, [L] * B, scale, window=w)
+        assert_attention_close(to_host_bits(out), ref, f"rolling decode at L={L}")
+        if m > 1:
+            cb, cv = wl.random_q(int(rng.integers(1 << 30)), (B, H, m, D))
+            out = cache.chunk(bf16_dev(cb), start, True, scale, L - m, workspace=wsc, window=w)
+            torch.cuda.synchronize()
+            ref = orc.attention_chunk(cv, k_hat, v_hat, [L - m] * B, True, scale, window=w)
+            assert_attention_close(to_host_bits(out), ref, f"rolling chunk at L={L}")
+        checked += 1
+    assert checked > 50
