@@ -39,7 +39,7 @@ def _sampled_decode_check(got, x, lens, kc, ks, vc, vs, num_heads, scale, picks,
     return assert_attention_close(sel, ref, what)
 
 
-@pytest.mark.parametrize("name", ["decode_8b", "q8_group32"])
+@pytest.mark.parametrize("name", ["decode_8b", "q8_group32", "decode_d256"])
 def test_contiguous_decode_full_size(kvq, name):
     import torch
     w = wl.ALL[name]

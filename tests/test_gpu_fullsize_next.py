@@ -143,11 +143,11 @@ def test_sliding_decode_full_size(kvq):
     del hat
 
 
-@pytest.mark.parametrize("name", ["sliding_chunk", "fp8_chunk", "chunk_group32", "recent_chunk"])
+@pytest.mark.parametrize("name", ["sliding_chunk", "fp8_chunk", "chunk_group32", "recent_chunk", "chunk_d256"])
 def test_chunk_variant_full_size(kvq, name):
     """512 new queries after 8192 cached tokens: with a window of 1024, on
-    FP8 E4M3 codes, with group-32 scales, or on a hybrid cache whose last 128
-    rows are bf16."""
+    FP8 E4M3 codes, with group-32 scales, on a hybrid cache whose last 128
+    rows are bf16, or at head dim 256."""
     import torch
     w = wl.ALL[name]
     win = w.extra.get("sliding", 0)
