@@ -59,8 +59,8 @@ bool stream_ok(const kvq_cache& c, const RecentGeom& rc) {
 
 int pass_tokens(int head_dim, bool stream_kernel) {
   // tokens a workgroup consumes per step: one 64-token block per wave for
-  // the streaming kernel (two 32-token ones at head dim 256), one pass of
-  // all waves for the generic kernel
+  // the streaming kernel (two 32-token ones at head dims 128 and 256), one
+  // pass of all waves for the generic kernel
   return stream_kernel ? kBlock * kStreamWaves : (kWave / (head_dim / 16)) * kWaves;
 }
 

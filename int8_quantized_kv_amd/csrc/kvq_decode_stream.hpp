@@ -718,8 +718,12 @@ __device__ void ring_into_wave(const DecodeParams& p, int b, int kvh, int h0, in
 // the length (the compiler's wait counts after such a join are conservative)
 template <int D, int HPW, int SM, bool PAGED, bool APPEND, bool WIN>
 __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(DecodeParams p) {
-  // BLK: tokens per wave block, 16 KB of K and V (32 at head dim 256)
-  constexpr int BLK = D == 256 ? 32 : kBlock;
+  // BLK: tokens per wave block, 8-16 KB of K and V: 64 at head dims 32 and
+  // 64, 32 at 128 and 256.  At head dim 128 the 32-token block (8 KB) beats
+  // the 64-token one: the block the wave computes after its last loads land
+  // is shorter, and the registers fall from about 220 to 160.  (16 tokens
+  // was slower again: the per-block softmax and exchange steps dominate.)
+  constexpr int BLK = D >= 128 ? 32 : kBlock;
   // K side: a token row is read by LK lanes, 16 bytes each (TK rows per pass).
   // V side: a token row is read by LV lanes, 8 bytes each (TV rows per pass),
   // so a lane accumulates 8 output dims per head.
@@ -835,7 +839,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
   const uint32_t voff = static_cast<uint32_t>(vslot * D + vsub * 8);    // lane's byte offset in a V pass
 
   // ---- loads --------------------------------------------------------------------
-  // A block whose 64 tokens all lie before t_end takes the fast path: the rows of
+  // A block whose BLK tokens all lie before t_end takes the fast path: the rows of
   // one pass are consecutive (contiguous layout) or lie in one 16-token page
   // (paged layout), so a load is a uniform base plus a per-lane constant.
   // Page ids come from a queue of scalar registers filled kPidAhead blocks
@@ -995,7 +999,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     }
   };
 
-  // ---- one 64-token block; PREFETCH issues the next block's loads early ----------
+  // ---- one block of BLK tokens; PREFETCH issues the next block's loads early ------
   // Waves w and w + 4 share a SIMD, whose issue arbitration favours the older
   // one: left alone it finishes its blocks well ahead of the younger, which
   // then streams by itself.  With long splits over ragged lengths (several
