@@ -806,7 +806,6 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     if constexpr (kQaLds) return sm_qa[st][lane];
     else return qa[MQK ? st : 0];
   };
-  int kq_of[HPW];             // each head's prescale exponent
   float fold_row[HPW];  // per-token: 128 * 2^-24 * (sum of the scaled queries), wave-uniform
   float cst[HPW];       // scale_log2 * 2^24 * 2^-kq (wave-uniform)
 
@@ -1333,12 +1332,15 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
                       (static_cast<int64_t>(b) * p.geom.kvh + kvh) * D * esz;
     xraw = load_row_raw<kEpl>(src, lane, wave < 2 && lane < D / kEpl, xbf16);
   }
-  uint4 qraw[HPW][2];
+  // (without the matrix cores: LK lanes per query row, 16 dims each)
+  uint4 qraw[MQK ? 1 : HPW][2];
+  if constexpr (!MQK) {
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
-    qraw[j][0] = qptr[0];
-    qraw[j][1] = qptr[1];
+    for (int j = 0; j < HPW; ++j) {
+      const uint4* qptr = reinterpret_cast<const uint4*>(p.q + (static_cast<int64_t>(b) * H + h0 + j) * D + ksub * 16);
+      qraw[j][0] = qptr[0];
+      qraw[j][1] = qptr[1];
+    }
   }
   // MQK: this lane's operand rows of the score product: head l % 16 (lanes
   // past the HPW heads read head HPW - 1 and later hold zeros), the 8 dims
@@ -1410,7 +1412,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 
   // ---- queries: power-of-two prescale into [2^14, 2^15), f16 pairs -----------
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
+  for (int j = 0; j < (MQK ? 0 : HPW); ++j) {
     float qf[16];
     bf16x8_to_f32(qraw[j][0], &qf[0]);
     bf16x8_to_f32(qraw[j][1], &qf[8]);
@@ -1429,12 +1431,25 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
     fold_row[j] = FP8 ? 0.0f : uniform(group_sum<LK>(qs * (128.0f * 0x1p-24f)));
     // INT8 per-token codes enter as c 2^-24; group-32 and FP8 as exact values
     cst[j] = uniform(ldexpf(p.scale_log2, (G32 || FP8 ? 0 : 24) - kq));
-    kq_of[j] = kq;
   }
-  if constexpr (MQK) {  // the same prescale, in the score product's lane layout
-    int kqm = kq_of[0];
+  if constexpr (MQK) {
+    // The prescale worked out in the score product's lane layout alone: the
+    // four lanes l % 16 = j together hold every dim of head j, so one pass
+    // over this lane's KST * 8 values gives the head's absmax, its operand
+    // and its sum (each wave of the workgroup does it once, instead of once
+    // per head in the row layout as well).  The same exponent as from the
+    // head's row; the sum of the same f16 values.
+    float a = 0.0f;
 #pragma unroll
-    for (int j = 1; j < HPW; ++j) kqm = mtok == j ? kq_of[j] : kqm;
+    for (int st = 0; st < KST; ++st) {
+      float qf[8];
+      bf16x8_to_f32(qmr[st], qf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(qf[e]));
+    }
+    a = slot_max<16>(a);
+    const int kqm = a > 0.0f ? 14 - ilogbf(a) : 0;
+    float qs = 0.0f;
 #pragma unroll
     for (int st = 0; st < KST; ++st) {
       float qf[8];
@@ -1443,6 +1458,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t b0 = f16_bits(ldexpf(qf[2 * e], kqm)), b1 = f16_bits(ldexpf(qf[2 * e + 1], kqm));
+        qs += f16_value(b0) + f16_value(b1);
         w[e] = mtok < HPW ? b0 | (b1 << 16) : 0u;
       }
       if constexpr (kQaLds) {
@@ -1450,6 +1466,14 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       } else {
         qa[st] = __builtin_bit_cast(half8_t, w);
       }
+    }
+    qs = slot_sum<16>(qs);
+#pragma unroll
+    for (int j = 0; j < HPW; ++j) {  // head j's figures, from lane j
+      const int kq = __builtin_amdgcn_readlane(kqm, j);
+      fold_row[j] = FP8 ? 0.0f : __int_as_float(__builtin_amdgcn_readlane(__float_as_int(qs), j)) * (128.0f * 0x1p-24f);
+      // INT8 per-token codes enter as c 2^-24; group-32 and FP8 as exact values
+      cst[j] = uniform(ldexpf(p.scale_log2, (G32 || FP8 ? 0 : 24) - kq));
     }
     if constexpr (kQaLds) __syncthreads();
   }
