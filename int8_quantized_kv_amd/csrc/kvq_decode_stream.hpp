@@ -149,6 +149,20 @@ __device__ __forceinline__ float f16_value(uint32_t bits) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
 }
 
+// Loads of K and V codes, which each launch reads once: non-temporal, so
+// that the stream does not push out of L2 what is read again (the kernel's
+// own code among it: an instruction fetch that misses L2 waits for HBM).
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* ptr) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream8(const uint8_t* ptr) {
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(ptr));
+  return make_uint2(v.x, v.y);
+}
+
 // Maximum over aligned groups of N consecutive lanes (N in {1,2,4,8,16}).
 template <int N>
 __device__ __forceinline__ float group_max(float x) {
@@ -926,13 +940,15 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         if constexpr (G32) {
 #pragma unroll
           for (int u = 0; u < NU; ++u) {
+            // (plain loads: two instructions read each 64-byte segment, and a
+            // non-temporal first read lets the line go before the second)
             const uint2 a = *reinterpret_cast<const uint2*>(row + 64 * u + 8 * mgrp);
             const uint2 c = *reinterpret_cast<const uint2*>(row + 64 * u + 32 + 8 * mgrp);
             kb[g * NU + u] = make_uint4(a.x, a.y, c.x, c.y);
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < NU; ++u) kb[g * NU + u] = *reinterpret_cast<const uint4*>(row + 64 * u + 16 * mgrp);
+          for (int u = 0; u < NU; ++u) kb[g * NU + u] = load_stream16(row + 64 * u + 16 * mgrp);
         }
       };
       if (PAGED || s0 + BLK <= t_end) {
@@ -953,21 +969,21 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         for (int i = 0; i < NPK; ++i) {
           const int tok = i * TK;                          // first token of the pass
           const uint8_t* base = p.k_codes + (r0[tok >> 4] + (tok & 15)) * D;
-          kb[i] = *reinterpret_cast<const uint4*>(base + koff);
+          kb[i] = load_stream16(base + koff);
         }
       } else {
         const int64_t r = seq_row0 + s0;
         const uint8_t* base = p.k_codes + r * D;
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
-          kb[i] = *reinterpret_cast<const uint4*>(base + i * TK * D + koff);
+          kb[i] = load_stream16(base + i * TK * D + koff);
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NPK; ++i) {
         const int64_t row = row_of(s0 + i * TK + kslot);
-        kb[i] = *reinterpret_cast<const uint4*>(p.k_codes + row * D + ksub * 16);
+        kb[i] = load_stream16(p.k_codes + row * D + ksub * 16);
       }
     }
   };
@@ -982,18 +998,18 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         for (int i = 0; i < NPV; ++i) {
           const int tok = i * TV;
           const uint8_t* base = p.v_codes + (r0[tok >> 4] + (tok & 15)) * D;
-          vb[i] = *reinterpret_cast<const uint2*>(base + voff);
+          vb[i] = load_stream8(base + voff);
         }
       } else {
         const uint8_t* base = p.v_codes + (seq_row0 + s0) * D;
 #pragma unroll
-        for (int i = 0; i < NPV; ++i) vb[i] = *reinterpret_cast<const uint2*>(base + i * TV * D + voff);
+        for (int i = 0; i < NPV; ++i) vb[i] = load_stream8(base + i * TV * D + voff);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const int64_t row = row_of(s0 + i * TV + vslot);
-        vb[i] = *reinterpret_cast<const uint2*>(p.v_codes + row * D + vsub * 8);
+        vb[i] = load_stream8(p.v_codes + row * D + vsub * 8);
       }
     }
   };
