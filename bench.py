@@ -713,16 +713,18 @@ def cpu_baseline_paged(w: wl.Workload, lens, target_s: float = 12.0):
 # Read-bandwidth ceiling: a plain read stream of the same bytes per launch
 # ----------------------------------------------------------------------------
 
-STREAM_SHAPES = [  # (workgroups, waves per workgroup, KB in flight per wave (x1..x2), interleaved)
+STREAM_SHAPES = [  # (workgroups, waves per workgroup, KB in flight per wave (x1..x2), interleaved[, non-temporal])
     (256, 8, 2, True), (256, 8, 4, True), (512, 8, 2, True), (512, 8, 4, True),
     (1024, 8, 2, True), (1024, 4, 4, True), (2048, 4, 2, True), (256, 16, 2, True),
     (512, 8, 4, False), (1024, 8, 2, False),
+    (256, 8, 2, True, True), (512, 8, 8, True, True), (1024, 8, 2, True, True), (256, 8, 4, False, True),
 ]
 
 
 # the best shapes of the sweep above (bench.py --workload stream_read), timed
 # beside every decode line for its percent-of-stream figure
-STREAM_QUICK = [(256, 8, 2, True), (512, 8, 8, True), (1024, 8, 2, True), (256, 8, 4, False)]
+STREAM_QUICK = [(256, 8, 2, True), (512, 8, 8, True), (1024, 8, 2, True), (256, 8, 4, False),
+                (256, 8, 2, True, True), (1024, 8, 2, True, True)]
 
 
 def stream_ceiling(kvq, torch, stream, nbytes: int, launches: int, reps: int = 5, shapes=STREAM_SHAPES):
@@ -736,15 +738,19 @@ def stream_ceiling(kvq, torch, stream, nbytes: int, launches: int, reps: int = 5
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     recs = []
     with torch.cuda.stream(stream):
-        for wg, wv, dep, il in shapes:
+        for shape in shapes:
+            wg, wv, dep, il = shape[:4]
+            nt = len(shape) > 4 and shape[4]
+
             def one():
                 for i in range(launches):
-                    kvq.kvq.kvq_stream_read(buf.data_ptr() + i * nbytes, nbytes, sink, wg, wv, dep, il, stream=stream)
+                    kvq.kvq.kvq_stream_read(buf.data_ptr() + i * nbytes, nbytes, sink, wg, wv, dep, il, stream=stream,
+                                            nontemporal=nt)
             one()
             ms = time_calls(one, reps, stream, torch)
             us = ms * 1e3 / launches
             recs.append({"workgroups": wg, "waves": wv, "kb_in_flight_per_wave": dep, "interleaved": il,
-                         "us_per_launch": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
+                         "nontemporal": nt, "us_per_launch": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1)})
     del buf
     best = max(recs, key=lambda r: r["gbs"])
     return best, recs
@@ -934,7 +940,7 @@ def main():
         "pct_of_hbm_peak": round(tbps * 1e3 / HBM_PEAK_GBS * 100, 2),
         "pct_of_stream": round(dec_gbs / ceil["gbs"] * 100, 2),
         "stream": {"kernel": "kvq_stream_read", "gbs": ceil["gbs"], "us_per_launch": ceil["us_per_launch"],
-                   "shape": {k: ceil[k] for k in ("workgroups", "waves", "kb_in_flight_per_wave", "interleaved")},
+                   "shape": {k: ceil[k] for k in ("workgroups", "waves", "kb_in_flight_per_wave", "interleaved", "nontemporal")},
                    "what": f"read-only stream of the same {nbytes[kernel_bytes]} B per launch, {w.layers} buffers "
                            f"in turn; pct_of_stream compares the kernel's algorithmic GB/s with it"},
         "higher_is_better": True,

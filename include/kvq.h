@@ -455,9 +455,11 @@ kvq_status kvq_append_decode_noalloc(const kvq_cache* cache, const void* k_new, 
  * constant, so the loads cannot be dropped).  Its rate is the read-bandwidth
  * ceiling that the attention kernels' achieved HBM bandwidth is compared
  * with.  `workgroups` workgroups of `waves_per_wg` (1..16) waves; each wave
- * keeps `depth` (1, 2, 4 or 8) to 2*depth 1-KB loads in flight; interleave != 0:
- * the waves of a workgroup take turns over its contiguous range, else each
- * wave reads a contiguous range of its own.
+ * keeps `depth` (1, 2, 4 or 8) to 2*depth 1-KB loads in flight.  interleave
+ * is a set of flags: bit 0 set, the waves of a workgroup take turns over its
+ * contiguous range, else each wave reads a contiguous range of its own; bit
+ * 1 set, the loads are non-temporal (as the decode kernels' loads of K and V
+ * codes); other bits set is INVALID_ARG.
  *   src  : device, 16-byte aligned, bytes a positive multiple of 16
  *   sink : device uint32 [1]
  * Errors: INVALID_ARG, HIP.

@@ -15,8 +15,9 @@ constexpr uint32_t kNever = 0x9E3779B9u;  // xor of everything read; written out
 // one is consumed while the other's loads are outstanding).  INTERLEAVE: the
 // waves of a workgroup take turns over 64*U-word steps of the workgroup's
 // contiguous range (as the decode kernel's waves take turns over blocks);
-// otherwise each wave reads a contiguous range of its own.
-template <int U, bool INTERLEAVE>
+// otherwise each wave reads a contiguous range of its own.  NT: non-temporal
+// loads (as the decode kernels read K and V codes).
+template <int U, bool INTERLEAVE, bool NT>
 __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
                                                            uint32_t* sink) {
   const int waves = blockDim.x / kWave;
@@ -43,7 +44,13 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4* __restri
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = i0 + u * kWave + lane;
-      r[u] = i < end ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (NT) {
+        typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+        const v4u v = i < end ? __builtin_nontemporal_load(reinterpret_cast<const v4u*>(src + i)) : v4u{0u, 0u, 0u, 0u};
+        r[u] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        r[u] = i < end ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+      }
     }
   };
   auto eat = [&](const uint4 (&r)[U]) {
@@ -62,13 +69,13 @@ __global__ __launch_bounds__(1024) void stream_read_kernel(const uint4* __restri
   if (acc == kNever) sink[0] = acc;
 }
 
-template <bool IL>
+template <bool IL, bool NT>
 void launch_stream(int depth, const uint4* src, int64_t n16, uint32_t* sink, dim3 grid, dim3 block, hipStream_t st) {
   switch (depth) {
-    case 1: hipLaunchKernelGGL((stream_read_kernel<1, IL>), grid, block, 0, st, src, n16, sink); break;
-    case 2: hipLaunchKernelGGL((stream_read_kernel<2, IL>), grid, block, 0, st, src, n16, sink); break;
-    case 4: hipLaunchKernelGGL((stream_read_kernel<4, IL>), grid, block, 0, st, src, n16, sink); break;
-    default: hipLaunchKernelGGL((stream_read_kernel<8, IL>), grid, block, 0, st, src, n16, sink); break;
+    case 1: hipLaunchKernelGGL((stream_read_kernel<1, IL, NT>), grid, block, 0, st, src, n16, sink); break;
+    case 2: hipLaunchKernelGGL((stream_read_kernel<2, IL, NT>), grid, block, 0, st, src, n16, sink); break;
+    case 4: hipLaunchKernelGGL((stream_read_kernel<4, IL, NT>), grid, block, 0, st, src, n16, sink); break;
+    default: hipLaunchKernelGGL((stream_read_kernel<8, IL, NT>), grid, block, 0, st, src, n16, sink); break;
   }
 }
 
@@ -93,8 +100,13 @@ KVQ_API kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink
   const auto* s = static_cast<const uint4*>(src);
   const dim3 grid(workgroups), block(waves_per_wg * kWave);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (interleave) launch_stream<true>(depth, s, n16, sink, grid, block, st);
-  else launch_stream<false>(depth, s, n16, sink, grid, block, st);
+  if (interleave & ~3)
+    return fail(KVQ_ERR_INVALID_ARG, "%s: interleave takes bits 0 and 1 only (got %d)", who, interleave);
+  const bool il = (interleave & 1) != 0, nt = (interleave & 2) != 0;
+  if (il && nt) launch_stream<true, true>(depth, s, n16, sink, grid, block, st);
+  else if (il) launch_stream<true, false>(depth, s, n16, sink, grid, block, st);
+  else if (nt) launch_stream<false, true>(depth, s, n16, sink, grid, block, st);
+  else launch_stream<false, false>(depth, s, n16, sink, grid, block, st);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return KVQ_OK;

@@ -345,9 +345,9 @@ def kvq_workspace_size_window(cache: kvq_cache, max_seq_len: int, n_query: int, 
 
 
 def kvq_stream_read(src, nbytes: int, sink, workgroups: int, waves_per_wg: int = 8, depth: int = 4,
-                    interleave: bool = True, stream=None):
+                    interleave: bool = True, stream=None, nontemporal: bool = False):
     _check(_lib.kvq_stream_read(_ptr(src), nbytes, _ptr(sink), workgroups, waves_per_wg, depth,
-                                1 if interleave else 0, _stream(stream)))
+                                (1 if interleave else 0) | (2 if nontemporal else 0), _stream(stream)))
 
 
 def kvq_append_decode_noalloc(cache: kvq_cache, k_new, v_new, in_dtype: int, q, seq_lens, attn_scale: float, out,

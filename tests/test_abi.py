@@ -391,3 +391,12 @@ def test_block_scale_descriptors():
         # per-head blocks chunk on the MFMA kernel (no workspace), per-channel on the generic one
         got = kvq.kvq_workspace_size_chunk_recent(d, ok, 4096, 64)
         assert got == 0 if mode == kvq.KVQ_SCALE_BLOCK_HEAD else got > 0
+
+
+def test_stream_read_flag_errors():
+    # bits 0 (interleave) and 1 (non-temporal) are the only flags; the rest is
+    # refused before anything reaches the device
+    for flags in (4, 8, -1):
+        st, msg = _status("kvq_stream_read", FAKE, 1 << 20, FAKE, 256, 8, 2, flags, None)
+        assert st == kvq.KVQ_ERR_INVALID_ARG and "interleave" in msg, (flags, st, msg)
+    assert _status("kvq_stream_read", FAKE, 1 << 20, FAKE, 256, 8, 3, 1, None)[0] == kvq.KVQ_ERR_INVALID_ARG
