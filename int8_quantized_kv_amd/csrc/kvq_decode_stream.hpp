@@ -904,6 +904,16 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
       return seq_row0 + t;
     }
   };
+  // K and V code loads: non-temporal, except in the paged layout (where, on
+  // the paged workload, they made the step slower)
+  auto ld_kv16 = [&](const uint8_t* ptr) -> uint4 {
+    if constexpr (PAGED) return *reinterpret_cast<const uint4*>(ptr);
+    else return load_stream16(ptr);
+  };
+  auto ld_kv8 = [&](const uint8_t* ptr) -> uint2 {
+    if constexpr (PAGED) return *reinterpret_cast<const uint2*>(ptr);
+    else return load_stream8(ptr);
+  };
   auto load_scales = [&](int64_t srow) {
     if constexpr (FP8) {
       (void)srow;
@@ -948,7 +958,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
           }
         } else {
 #pragma unroll
-          for (int u = 0; u < NU; ++u) kb[g * NU + u] = load_stream16(row + 64 * u + 16 * mgrp);
+          for (int u = 0; u < NU; ++u) kb[g * NU + u] = ld_kv16(row + 64 * u + 16 * mgrp);
         }
       };
       if (PAGED || s0 + BLK <= t_end) {
@@ -969,21 +979,21 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         for (int i = 0; i < NPK; ++i) {
           const int tok = i * TK;                          // first token of the pass
           const uint8_t* base = p.k_codes + (r0[tok >> 4] + (tok & 15)) * D;
-          kb[i] = load_stream16(base + koff);
+          kb[i] = ld_kv16(base + koff);
         }
       } else {
         const int64_t r = seq_row0 + s0;
         const uint8_t* base = p.k_codes + r * D;
 #pragma unroll
         for (int i = 0; i < NPK; ++i) {
-          kb[i] = load_stream16(base + i * TK * D + koff);
+          kb[i] = ld_kv16(base + i * TK * D + koff);
         }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NPK; ++i) {
         const int64_t row = row_of(s0 + i * TK + kslot);
-        kb[i] = load_stream16(p.k_codes + row * D + ksub * 16);
+        kb[i] = ld_kv16(p.k_codes + row * D + ksub * 16);
       }
     }
   };
@@ -998,18 +1008,18 @@ __global__ __launch_bounds__(kStreamThreads, 2) void decode_stream_kernel(Decode
         for (int i = 0; i < NPV; ++i) {
           const int tok = i * TV;
           const uint8_t* base = p.v_codes + (r0[tok >> 4] + (tok & 15)) * D;
-          vb[i] = load_stream8(base + voff);
+          vb[i] = ld_kv8(base + voff);
         }
       } else {
         const uint8_t* base = p.v_codes + (seq_row0 + s0) * D;
 #pragma unroll
-        for (int i = 0; i < NPV; ++i) vb[i] = load_stream8(base + i * TV * D + voff);
+        for (int i = 0; i < NPV; ++i) vb[i] = ld_kv8(base + i * TV * D + voff);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const int64_t row = row_of(s0 + i * TV + vslot);
-        vb[i] = load_stream8(p.v_codes + row * D + vsub * 8);
+        vb[i] = ld_kv8(p.v_codes + row * D + vsub * 8);
       }
     }
   };
