@@ -756,6 +756,61 @@ def stream_ceiling(kvq, torch, stream, nbytes: int, launches: int, reps: int = 5
     return best, recs
 
 
+def run_ctx_sweep(args, kvq, torch, stream):
+    """The fused decode step of the 8B-shaped workload's shape (B16, 32/8
+    heads, D128, per-token scales) at contexts 1024..16384 on a fixed grid
+    (two splits per head group: one round of 256 workgroups at every
+    context), eight layers of synthetic codes, beside the read stream of the
+    same bytes.  A straight-line fit of time against bytes separates the
+    per-launch fixed cost from the streaming rate."""
+    import numpy as np
+    os.environ["KVQ_NUM_SPLITS"] = "2"
+    B, H, KVH, D, NL = 16, 32, 8, 128, 8
+    pts = []
+    for ctx in (1024, 2048, 4096, 8192, 16384):
+        g = torch.Generator(device="cuda").manual_seed(ctx)
+        caches = []
+        for _ in range(NL):
+            c = kvq.Int8KVCache(B, H, KVH, D, max_len=ctx)
+            c.k_codes.random_(0, 256, generator=g)
+            c.v_codes.random_(0, 256, generator=g)
+            c.k_scales.uniform_(0.001, 0.01, generator=g)
+            c.v_scales.uniform_(0.001, 0.01, generator=g)
+            caches.append(c)
+        q = torch.randn(B, H, D, device="cuda", generator=g).to(torch.bfloat16)
+        kn = torch.randn(B, KVH, D, device="cuda", generator=g).to(torch.bfloat16)
+        vn = torch.randn(B, KVH, D, device="cuda", generator=g).to(torch.bfloat16)
+        sl = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+        ws = caches[0].workspace(ctx, 1)
+        out = torch.empty_like(q)
+        torch.cuda.synchronize()  # the fills above ran on the default stream
+
+        def one():
+            for c in caches:
+                c.append_decode(kn, vn, q, sl, 0.088, ctx, out=out, workspace=ws, stream=stream)
+        with torch.cuda.stream(stream):
+            for _ in range(max(args.warmup, 1)):
+                one()
+            us = time_calls(one, args.steps, stream, torch) * 1e3 / NL
+        nbytes = 2 * B * KVH * ctx * (D + 4) + 2 * B * H * D * 2 + 2 * B * KVH * D * 2
+        best, _ = stream_ceiling(kvq, torch, stream, nbytes, NL, reps=5, shapes=STREAM_QUICK)
+        pts.append({"ctx": ctx, "bytes": nbytes, "us": round(us, 3), "stream_us": best["us_per_launch"]})
+        log(f"ctx {ctx}: {us:.2f} us per launch, read stream {best['us_per_launch']:.2f} us")
+        del caches
+        torch.cuda.empty_cache()
+    x = np.array([p["bytes"] for p in pts], dtype=np.float64)
+    fit = {}
+    for key in ("us", "stream_us"):
+        y = np.array([p[key] for p in pts])
+        slope, icpt = np.polyfit(x, y, 1)
+        fit[key] = {"fixed_us": round(float(icpt), 2), "rate_gbs": round(float(1e-3 / slope), 1)}
+    log(f"fit: decode {fit['us']}, read stream {fit['stream_us']}")
+    print(json.dumps({"metric": "fused decode time vs context (fixed grid)", "unit": "us", "points": pts, "fit": fit,
+                      "data": "synthetic", "config": {"workload": "decode_ctx_sweep: batch 16, 32 q / 8 kv heads, "
+                                                      "head_dim 128, per-token fp32 scales, 8 layers, 2 splits"}}),
+          flush=True)
+
+
 def run_stream(args, kvq, torch, stream):
     """The read-only stream kernel alone: the 8B-shaped decode's bytes per
     layer-step (one launch per layer, 32 layers), and one 4 GiB launch."""
@@ -799,7 +854,7 @@ def main():
                                                             "bf16_scales", "fp8_e4m3", "fp8_chunk", "chunk_group32",
                                                             "recent_chunk", "tiny_decode", "stream_read",
                                                             "recent_block_head", "recent_block_channel", "chunk_d256",
-                                                            "decode_d256"])
+                                                            "decode_d256", "decode_ctx_sweep"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="time kvq_append + kvq_attention_decode as two launches instead of kvq_append_decode")
@@ -837,6 +892,9 @@ def main():
 
     if args.workload == "stream_read":
         run_stream(args, kvq, torch, stream)
+        return
+    if args.workload == "decode_ctx_sweep":
+        run_ctx_sweep(args, kvq, torch, stream)
         return
     w = wl.ALL[args.workload]
     if w.name == "sliding_decode":
