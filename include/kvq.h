@@ -36,7 +36,13 @@
  *     above 256, paged page_size != 16, n_new <= 0, ...).  Device-side values
  *     (positions, lengths, page ids) are the caller's contract; kernels clamp
  *     or skip out-of-range ones so that no access leaves the buffers described
- *     by the descriptor.
+ *     by the descriptor.  A library built with -DKVQ_DEBUG (build.py --debug,
+ *     int8_quantized_kv_amd/_dbg/libkvq.so) checks them on the host before
+ *     each attention launch: it waits for the stream, copies the lengths and
+ *     the block table, and returns KVQ_ERR_OUT_OF_RANGE, launching nothing,
+ *     when a length passes its bound or a page the call reads lies outside
+ *     [0, num_pages).  For testing; the release build never reads device
+ *     memory on the host.
  */
 #ifndef KVQ_H
 #define KVQ_H

@@ -136,8 +136,41 @@ def build_sanitized(verbose: bool = True) -> str:
     return SAN_LIB
 
 
+# Debug build: the C ABI translation unit compiled with -DKVQ_DEBUG (host-side
+# checks of lengths and page ids before each attention launch), linked with
+# the release build's other objects.  Run build() first.
+DBG_DIR = os.path.join(PKG, "_dbg")
+DBG_LIB = os.path.join(DBG_DIR, "libkvq.so")
+
+
+def build_debug(verbose: bool = True) -> str:
+    os.makedirs(DBG_DIR, exist_ok=True)
+    api = os.path.join(SRC, "kvq_api.hip")
+    obj = os.path.join(DBG_DIR, "kvq_api.hip.o")
+    r = subprocess.run([HIPCC, *COMMON, "-DKVQ_DEBUG", "-c", api, "-o", obj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"debug build failed:\n{r.stdout}\n{r.stderr}")
+    others = [os.path.join(OUT_DIR, os.path.basename(src) + ".o") for src in sorted(glob.glob(os.path.join(SRC, "*.hip")))
+              if os.path.basename(src) != "kvq_api.hip"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"debug build needs the release objects first (missing {missing[0]})")
+    tmp = DBG_LIB + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, obj, *others],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"debug link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, DBG_LIB)
+    if verbose:
+        print(f"built {DBG_LIB}")
+    return DBG_LIB
+
+
 if __name__ == "__main__":
     if len(sys.argv) > 1 and sys.argv[1] == "--sanitize":
         build_sanitized()
+    elif len(sys.argv) > 1 and sys.argv[1] == "--debug":
+        build_debug()
     else:
         build()
+        build_debug()

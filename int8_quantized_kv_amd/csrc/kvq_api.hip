@@ -1,11 +1,12 @@
 // C ABI entry points of libkvq: argument validation, launch planning and the
 // thread-local error message.  No allocation, no synchronisation, no device
-// reads on the host.
+// reads on the host (except in a KVQ_DEBUG build, below).
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "kvq_internal.hpp"
 
@@ -24,6 +25,50 @@ kvq_status fail(kvq_status st, const char* fmt, ...) {
 }
 
 namespace {
+
+#ifdef KVQ_DEBUG
+// Debug builds (-DKVQ_DEBUG) check the device-side values that the kernels
+// take on trust and would otherwise clamp: every length within its bound
+// and, in the paged layout, every page the call reads mapped to an arena
+// page.  The check waits for the stream and copies the lengths and the block
+// table to the host, so it is a testing aid, not for production.
+//   lens  : device [batch]; total length of sequence b = lens[b] + add
+//   bound : largest total length allowed (the hint, within the capacity)
+//   rwin  : recent-window rows at the end of each sequence (not in pages)
+//   first : tokens the earliest query sees before its own position under a
+//           sliding window (window - 1), or -1 for every earlier token
+kvq_status debug_check(const kvq_cache& c, const int32_t* lens, int32_t add, int64_t bound, int32_t rwin,
+                       int32_t nq, int32_t first, hipStream_t stream, const char* who) {
+  std::vector<int32_t> L(c.batch);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e == hipSuccess) e = hipMemcpy(L.data(), lens, sizeof(int32_t) * c.batch, hipMemcpyDeviceToHost);
+  std::vector<int32_t> bt;
+  const bool paged = c.layout == KVQ_LAYOUT_PAGED;
+  if (e == hipSuccess && paged) {
+    bt.resize(static_cast<size_t>(c.batch) * c.max_blocks_per_seq);
+    e = hipMemcpy(bt.data(), c.block_table, sizeof(int32_t) * bt.size(), hipMemcpyDeviceToHost);
+  }
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: debug check: copy failed: %s", who, hipGetErrorString(e));
+  for (int b = 0; b < c.batch; ++b) {
+    const int64_t total = static_cast<int64_t>(L[b]) + add;
+    if (L[b] < 0 || total > bound)
+      return fail(KVQ_ERR_OUT_OF_RANGE, "%s: debug check: sequence %d has length %lld, outside [0, %lld]", who, b,
+                  static_cast<long long>(total), static_cast<long long>(bound));
+    if (!paged) continue;
+    const int64_t hi = total - rwin > 0 ? total - rwin : 0;  // INT8 positions [lo, hi) are read
+    int64_t lo = first >= 0 ? total - nq - first : 0;
+    if (lo < 0) lo = 0;
+    for (int64_t pos = lo & ~static_cast<int64_t>(kPageSize - 1); pos < hi; pos += kPageSize) {
+      const int64_t blk = pos / kPageSize;
+      const int32_t id = blk < c.max_blocks_per_seq ? bt[static_cast<size_t>(b) * c.max_blocks_per_seq + blk] : -1;
+      if (id < 0 || id >= c.num_pages)
+        return fail(KVQ_ERR_OUT_OF_RANGE, "%s: debug check: sequence %d position %lld is in page %d, outside [0, %d)",
+                    who, b, static_cast<long long>(pos), id, c.num_pages);
+    }
+  }
+  return KVQ_OK;
+}
+#endif
 
 // Descriptor checks common to every entry point.
 // The descriptor's geometry, and with need_pointers its device pointers (the
@@ -201,6 +246,11 @@ kvq_status decode_impl(const kvq_cache* c, const kvq_recent* r, bool fused, cons
   const DecodePlan plan = plan_decode(*c, max_seq_len_hint, rc, window);
   st = check_split_workspace(plan.workspace, workspace, workspace_bytes, who);
   if (st != KVQ_OK) return st;
+#ifdef KVQ_DEBUG
+  st = debug_check(*c, seq_lens, 0, max_seq_len_hint, rc.window, 1, window > 0 ? window - 1 : -1,
+                   static_cast<hipStream_t>(stream), who);
+  if (st != KVQ_OK) return st;
+#endif
   return launch_decode(*c, plan, q, seq_lens, attn_scale, out, workspace, max_seq_len_hint,
                        static_cast<hipStream_t>(stream), fused ? k_new : nullptr, fused ? v_new : nullptr,
                        in_dtype, rc, window);
@@ -378,6 +428,10 @@ KVQ_API kvq_status kvq_append_decode_noalloc(const kvq_cache* c, const void* k_n
   void* ws = nullptr;
   st = scratch_of(dev, hs, &ws, who);
   if (st != KVQ_OK) return st;
+#ifdef KVQ_DEBUG
+  st = debug_check(*c, seq_lens, 0, max_seq_len_hint, 0, 1, -1, hs, who);
+  if (st != KVQ_OK) return st;
+#endif
   return launch_decode(*c, plan, q, seq_lens, attn_scale, out, ws, max_seq_len_hint, hs, k_new, v_new, in_dtype);
 }
 
@@ -398,6 +452,11 @@ kvq_status chunk_impl(const kvq_cache* c, const uint16_t* q, int32_t n, const in
   if (max_ctx_len_hint < 0 || static_cast<int64_t>(max_ctx_len_hint) + n > capacity_of(*c))
     return fail(KVQ_ERR_OUT_OF_RANGE, "%s: max_ctx_len_hint + n (%lld) exceeds the capacity (%d)", who,
                 static_cast<long long>(max_ctx_len_hint) + n, capacity_of(*c));
+#ifdef KVQ_DEBUG
+  st = debug_check(*c, ctx_lens, n, static_cast<int64_t>(max_ctx_len_hint) + n, r ? recent_of(r).window : 0, n,
+                   window > 0 ? window - 1 : -1, static_cast<hipStream_t>(stream), who);
+  if (st != KVQ_OK) return st;
+#endif
   // a hybrid cache at an MFMA head size: the MFMA kernel stages INT8 rows and
   // bf16 ring rows in the same tiles (no workspace)
   if (r && mfma_hybrid_ok(*c)) {

@@ -94,7 +94,7 @@ def _hip_runtimes():
     return paths
 
 
-def _load():
+def _load(path: str = LIB_PATH):
     # torch ships its own HIP runtime with the same soname as the system one.
     # Loading torch first makes libkvq bind to that already-loaded runtime, so
     # one process never holds two HIP runtimes (the second one would not see
@@ -103,10 +103,10 @@ def _load():
         import torch  # noqa: F401
     except ImportError:
         pass
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libkvq.so not found at {LIB_PATH}; build it with "
+    if not os.path.exists(path):
+        raise ImportError(f"libkvq.so not found at {path}; build it with "
                           "`python int8_quantized_kv_amd/build.py`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     runtimes = _hip_runtimes()
     if len(runtimes) > 1:
         raise ImportError("two HIP runtimes are loaded (" + ", ".join(sorted(runtimes)) +
@@ -168,6 +168,12 @@ _lib = _load()
 
 def library():
     return _lib
+
+
+def load_library(path: str):
+    """Another build of libkvq (the KVQ_DEBUG one, say) with the same
+    prototypes; its calls report errors through its own kvq_last_error."""
+    return _load(path)
 
 
 def _ptr(x):
