@@ -127,23 +127,34 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
   // ones fill the end of the launch.  (On the paged workload, 64 sequences
   // of U[512, 32768] tokens: splits of 32768 tokens 386 us, of 16384 from
   // aiming at four rounds 457 us, of 4096 506 us.)
-  const int64_t groups = static_cast<int64_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
-  int64_t want = (static_cast<int64_t>(max_seq_len) * groups + kCUs - 1) / kCUs;
-  if (want > 2048) {  // several rounds
-    want = (static_cast<int64_t>(max_seq_len) * groups + 2 * kCUs - 1) / (2 * kCUs);
-    want = want < 2048 ? 2048 : (want > 32768 ? 32768 : want);
-  }
-  want = want < 512 ? 512 : want;
-  int split = static_cast<int>(want);
   const int forced_splits = env_int("KVQ_NUM_SPLITS", 0);
   const int forced_len = env_int("KVQ_SPLIT_LEN", 0);
-  if (forced_splits > 0) split = (max_seq_len + forced_splits - 1) / forced_splits;
-  else if (forced_len > 0) split = forced_len;
-  split = ((split + step - 1) / step) * step;
-  if (split < step) split = step;
-  pl.split_len = split;
-  pl.num_splits = split_count(max_seq_len, split);
-  if (pl.num_splits < 1) pl.num_splits = 1;
+  int64_t groups = 0;
+  int split = 0;
+  for (;;) {
+    groups = static_cast<int64_t>(c.batch) * c.num_kv_heads * (gqa / pl.heads_per_wg);
+    int64_t want = (static_cast<int64_t>(max_seq_len) * groups + kCUs - 1) / kCUs;
+    if (want > 2048) {  // several rounds
+      want = (static_cast<int64_t>(max_seq_len) * groups + 2 * kCUs - 1) / (2 * kCUs);
+      want = want < 2048 ? 2048 : (want > 32768 ? 32768 : want);
+    }
+    want = want < 512 ? 512 : want;
+    split = static_cast<int>(want);
+    if (forced_splits > 0) split = (max_seq_len + forced_splits - 1) / forced_splits;
+    else if (forced_len > 0) split = forced_len;
+    split = ((split + step - 1) / step) * step;
+    if (split < step) split = step;
+    pl.split_len = split;
+    pl.num_splits = split_count(max_seq_len, split);
+    if (pl.num_splits < 1) pl.num_splits = 1;
+    // A one-round plan that leaves half the compute units idle or more
+    // (short contexts, sliding windows) takes fewer heads per workgroup: a
+    // KV head's rows are then read by two workgroups, which share its XCD and
+    // L2 (sliding decode, 16 sequences x 8 KV heads over a 1024-token window:
+    // 15.7 -> 13.5 us).
+    if (forced_hpw != 0 || pl.heads_per_wg == 1 || groups * pl.num_splits > kCUs / 2) break;
+    pl.heads_per_wg /= 2;
+  }
 
   // Longest sequence first pays when workgroups are long (several rounds of
   // splits of 4096 tokens or more): ranking the lengths costs each workgroup
