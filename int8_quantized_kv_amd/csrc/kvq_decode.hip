@@ -150,9 +150,12 @@ DecodePlan plan_decode(const kvq_cache& c, int max_seq_len, const RecentGeom& rc
     // A one-round plan that leaves half the compute units idle or more
     // (short contexts, sliding windows) takes fewer heads per workgroup: a
     // KV head's rows are then read by two workgroups, which share its XCD and
-    // L2 (sliding decode, 16 sequences x 8 KV heads over a 1024-token window:
-    // 15.7 -> 13.5 us).
-    if (forced_hpw != 0 || pl.heads_per_wg == 1 || groups * pl.num_splits > kCUs / 2) break;
+    // L2 when the KV heads are a multiple of 8 (consecutive workgroup ids go
+    // to consecutive XCDs; otherwise each L2 would fetch the rows again).
+    // Sliding decode, 16 sequences x 8 KV heads over a 1024-token window:
+    // 15.7 -> 13.5 us.
+    if (forced_hpw != 0 || pl.heads_per_wg == 1 || c.num_kv_heads % 8 != 0 || groups * pl.num_splits > kCUs / 2)
+      break;
     pl.heads_per_wg /= 2;
   }
 
