@@ -400,3 +400,38 @@ def test_stream_read_flag_errors():
         st, msg = _status("kvq_stream_read", FAKE, 1 << 20, FAKE, 256, 8, 2, flags, None)
         assert st == kvq.KVQ_ERR_INVALID_ARG and "interleave" in msg, (flags, st, msg)
     assert _status("kvq_stream_read", FAKE, 1 << 20, FAKE, 256, 8, 3, 1, None)[0] == kvq.KVQ_ERR_INVALID_ARG
+
+
+def _plan_bytes(batch, heads, groups, splits, head_dim):
+    """Workspace of a decode plan: the splits' ticket counters (one per
+    (sequence, head group), 256-byte aligned), then (m, l) and D outputs per
+    (sequence, head, split)."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    partials = batch * heads * splits
+    return up(groups * 4) + up(partials * 2 * 4) + partials * head_dim * 4
+
+
+def test_split_planner_rules():
+    # one round: the 8B-shaped decode, four heads per workgroup, two splits of
+    # 2048 tokens (128 head groups x 2 = 256 workgroups)
+    d = _desc(batch=16, num_heads=32, num_kv_heads=8, head_dim=128, max_len=4096)
+    assert kvq.kvq_workspace_size(d, 4096, 1) == _plan_bytes(16, 32, 128, 2, 128)
+    # several rounds: about two rounds of the longest length, at most 32768
+    # tokens a split -- the paged workload's 64 sequences up to 31912 tokens
+    # take one split each (512 workgroups), a uniform 16 x 32768 batch four
+    # splits of 8192
+    dp = _desc(batch=64, num_heads=32, num_kv_heads=8, head_dim=128, max_len=0, layout=kvq.KVQ_LAYOUT_PAGED,
+               num_pages=70000, max_blocks_per_seq=2048, block_table=FAKE)
+    assert kvq.kvq_workspace_size(dp, 31912, 1) == _plan_bytes(64, 32, 512, 1, 128)
+    dl = _desc(batch=16, num_heads=32, num_kv_heads=8, head_dim=128, max_len=32768)
+    assert kvq.kvq_workspace_size(dl, 32768, 1) == _plan_bytes(16, 32, 128, 4, 128)
+    # a one-round plan that would leave half the compute units idle halves the
+    # heads per workgroup when the KV heads are a multiple of 8: the sliding
+    # decode (16 x 8 KV heads, 1024-token window) runs 256 workgroups of two
+    # heads, one split each
+    dw = _desc(batch=16, num_heads=32, num_kv_heads=8, head_dim=128, max_len=8192)
+    assert kvq.kvq_workspace_size_window(dw, 8192, 1, 1024) == _plan_bytes(16, 32, 256, 1, 128)
+    # ... but not with 2 KV heads (the tiny decode keeps four heads, one split)
+    dt = _desc(batch=1, num_heads=8, num_kv_heads=2, head_dim=64, max_len=256)
+    assert kvq.kvq_workspace_size(dt, 256, 1) == _plan_bytes(1, 8, 2, 1, 64)
